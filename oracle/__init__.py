@@ -1,0 +1,25 @@
+"""CPU oracle for the GPT-2 training step (test infrastructure only).
+
+Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import anything from this package.  The HIP product path
+never calls it and shares no code with it.
+"""
+
+from .gpt2_oracle import (  # noqa: F401
+    OracleConfig,
+    param_shapes,
+    layernorm_forward,
+    layernorm_backward,
+    gelu_tanh,
+    gelu_tanh_backward,
+    causal_attention_forward,
+    causal_attention_backward,
+    softmax_cross_entropy,
+    encoder_forward,
+    encoder_backward,
+    adamw_update,
+    gpt2_forward,
+    gpt2_backward,
+    gpt2_step,
+)
+from .init_rng import splitmix64_stream, gpt2_init_params  # noqa: F401
