@@ -1,0 +1,186 @@
+"""Training-throughput benchmark: GPT-2 training steps (forward + backward +
+AdamW) through the HIP C-ABI library on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 124m|350m|1.6b]
+
+Prints one JSON line.  value = tokens/s of whole training steps (inputs
+already resident in HBM), MFU against the bf16 dense MFMA peak, the roofline
+position of the step's dominant kernel (its average launch duration measured
+with HIP events on the library stream during the timed steps), and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "train tokens/sec + MFU, GPT-2 124M B=24 T=1024 bf16, 1 MI355X"
+PEAK_BF16 = 2.5e15        # MI355X dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12         # MI355X HBM3E, bytes/s
+
+CONFIGS = {
+    "124m": dict(V=50257, Vp=50304, maxT=1024, L=12, H=12, C=768, B=24, T=1024, lr=6e-4, wd=0.1),
+    "350m": dict(V=50257, Vp=50304, maxT=1024, L=24, H=16, C=1024, B=16, T=1024, lr=6e-4, wd=0.1),
+    "1.6b": dict(V=50257, Vp=50304, maxT=1024, L=48, H=25, C=1600, B=8, T=1024, lr=2e-4, wd=0.1),
+}
+
+# sites whose launch durations can be timed by the library (include/gpt2.h)
+GEMM_SITES = ["qkv", "attproj", "fc", "fcproj", "logits", "fcproj_dx", "fcproj_dw", "fc_dx", "fc_dw",
+              "attproj_dx", "attproj_dw", "qkv_dx", "qkv_dw", "cls_dx", "cls_dw"]
+MFMA_SITES = set(GEMM_SITES)
+ALL_SITES = GEMM_SITES + ["attn_fwd", "attn_bwd", "softmax_xent", "adamw"]
+
+
+def flops_per_token(c) -> float:
+    """6 N + 12 L C T with N the unpadded parameter count (model FLOPs)."""
+    V, T, L, C = c["V"], c["maxT"], c["L"], c["C"]
+    N = V * C + T * C + L * (12 * C * C + 13 * C) + 2 * C
+    return 6.0 * N + 12.0 * L * C * c["T"]
+
+
+def cpu_baseline(c, seed):
+    """The CPU oracle (float32 numpy), as it stands, on one sequence of the
+    same workload: one forward + backward + AdamW step at B=1, T=1024."""
+    import oracle as O
+    from gpt_transformer_lm_amd import synthetic as S
+    cores = len(os.sched_getaffinity(0))
+    oc = O.OracleConfig(vocab_size=c["V"], max_seq_len=c["maxT"], num_layers=c["L"], num_heads=c["H"],
+                        channels=c["C"])
+    params = S.random_params(c["V"], c["V"], c["maxT"], c["L"], c["C"], seed=seed, perturbed=False)
+    tok, tgt = S.zipf_batch(1, c["T"], seed=seed + 1)
+    t0 = time.perf_counter()
+    O.gpt2_step(params, tok, tgt, oc, None, c["lr"], 0.9, 0.999, 1e-8, c["wd"], 1)
+    dt = time.perf_counter() - t0
+    return {"value": c["T"] / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"1 sequence x {c['T']} tokens (1 of the {c['B']} rows of a batch): one float32 numpy "
+                      f"forward+backward+AdamW step of the same model, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="124m", choices=sorted(CONFIGS))
+    ap.add_argument("--seed", type=int, default=1234)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--site", default=None, help="kernel site to report in roofline (default: the slowest)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gpt_transformer_lm_amd import lib
+    from gpt_transformer_lm_amd import synthetic as S
+
+    c = CONFIGS[args.config]
+    B, T = c["B"], c["T"]
+    cfg = lib.make_config(c["V"], c["Vp"], c["maxT"], c["L"], c["H"], c["C"], B, T, lib.GPT2_BF16)
+    torch.cuda.init()
+    stream = torch.cuda.current_stream()
+    model = lib.Model(cfg, seed=args.seed, stream=stream)
+    nsteps = args.warmup + args.steps
+    batches = []
+    for s in range(nsteps + 1):
+        x, y = S.zipf_batch(B, T, seed=args.seed * 1000 + s)
+        batches.append((torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda()))
+    torch.cuda.synchronize()
+
+    def step(i, t):
+        x, y = batches[i]
+        loss = model.forward(x, y)
+        model.backward()
+        model.adamw_step(c["lr"], 0.9, 0.999, 1e-8, c["wd"], t)
+        return loss
+
+    # warmup; the last warmup step also times every kernel site once to find the dominant kernel
+    t = 0
+    for i in range(args.warmup):
+        if i == args.warmup - 1:
+            for s in ALL_SITES:
+                model.timing_enable(s, True)
+        t += 1
+        step(i, t)
+    site_ms = {}
+    if args.warmup > 0:
+        for s in ALL_SITES:
+            r = model.timing_read(s)
+            site_ms[s] = r["total_ms"]
+            model.timing_enable(s, False)
+    dom = args.site or (max(site_ms, key=site_ms.get) if site_ms else "fc")
+    model.timing_enable(dom, True)
+
+    torch.cuda.synchronize()
+    losses = []
+    t0 = time.perf_counter()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        t += 1
+        losses.append(step(args.warmup + i, t))
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    elapsed = wall
+    dom_t = model.timing_read(dom)
+    model.close()
+
+    tok_s = B * T * args.steps / elapsed
+    ftok = flops_per_token(c)
+    mfu = tok_s * ftok / PEAK_BF16
+    avg_ms = dom_t["total_ms"] / max(dom_t["launches"], 1)
+    if dom in MFMA_SITES or dom.startswith("attn"):
+        achieved = dom_t["flops_per_launch"] / (avg_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                "frac": achieved / (PEAK_BF16 / 1e12), "traffic": None}
+    else:
+        achieved = dom_t["bytes_per_launch"] / (avg_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                "frac": achieved / (PEAK_HBM / 1e9), "traffic": None}
+    roof.update({"kernel_site": dom, "avg_launch_ms": avg_ms, "launches": dom_t["launches"],
+                 "algorithmic_per_launch": dom_t["flops_per_launch"] if roof["bound"] == "mfma"
+                 else dom_t["bytes_per_launch"]})
+
+    out = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic Zipf(1.1)/EoT token ids, seeded random GPT-2 init",
+        "config": {"workload": f"GPT-2 {args.config} training step (fwd+bwd+AdamW, fp32 master), "
+                               f"B={B}, T={T}, vocab 50257 padded to 50304",
+                   "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+        "mfu": mfu,
+        "model_flops_per_token": ftok,
+        "loss_first_last": [losses[0], losses[-1]] if losses else None,
+        "site_ms_one_step": site_ms,
+        "gpu_event_ms_per_step": gpu_ms / args.steps,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(c, args.seed)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

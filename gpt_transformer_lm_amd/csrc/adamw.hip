@@ -1,0 +1,158 @@
+// Parameter update and parameter-state kernels.
+//
+// AdamW (the adamw_kernel3 row of the kernel table in "State of the Union
+// [May 3, 2024]", section "Runtime, DRAM traffic, instructions"; the opening
+// bullet list keeps the master copy of the parameters in fp32), one pass over
+// the flat parameter array:
+//   m = b1 m + (1 - b1) g;  v = b2 v + (1 - b2) g^2;
+//   theta -= lr * ((m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps) + wd * theta)
+// and, in the same pass, the bf16 copy that the forward reads (the page's
+// separate copy_and_cast kernel is folded in).  16-byte vector accesses;
+// 30 bytes of HBM traffic per parameter (read theta, g, m, v; write theta,
+// m, v and the bf16 copy).
+//
+// Seeded initialisation: counter-based SplitMix64 (Steele, Lea & Flood 2014)
+// and the Box-Muller transform, evaluated in double precision, one element
+// per thread (the pages list random init in C as pending work, paragraph
+// "Functional").
+
+#include "kernels.h"
+
+namespace gpt2k {
+namespace {
+
+__global__ void adamw_kernel(int64_t n, float* __restrict__ master, const float* __restrict__ grad,
+                             float* __restrict__ mom1, float* __restrict__ mom2, bf16* __restrict__ pbf,
+                             float lr, float b1, float b2, float eps, float wd, float c1, float c2) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+    if (i + 4 <= n) {
+      float4 th = *reinterpret_cast<const float4*>(master + i);
+      float4 g = *reinterpret_cast<const float4*>(grad + i);
+      float4 m = *reinterpret_cast<const float4*>(mom1 + i);
+      float4 v = *reinterpret_cast<const float4*>(mom2 + i);
+      float tv[4] = {th.x, th.y, th.z, th.w}, gv[4] = {g.x, g.y, g.z, g.w};
+      float mv[4] = {m.x, m.y, m.z, m.w}, vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        mv[e] = b1 * mv[e] + (1.0f - b1) * gv[e];
+        vv[e] = b2 * vv[e] + (1.0f - b2) * gv[e] * gv[e];
+        const float mh = mv[e] * c1, vh = vv[e] * c2;
+        tv[e] -= lr * (mh / (sqrtf(vh) + eps) + wd * tv[e]);
+      }
+      *reinterpret_cast<float4*>(master + i) = make_float4(tv[0], tv[1], tv[2], tv[3]);
+      *reinterpret_cast<float4*>(mom1 + i) = make_float4(mv[0], mv[1], mv[2], mv[3]);
+      *reinterpret_cast<float4*>(mom2 + i) = make_float4(vv[0], vv[1], vv[2], vv[3]);
+      if (pbf) {
+        typedef bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+        bf16x4_t o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (bf16)tv[e];
+        *reinterpret_cast<bf16x4_t*>(pbf + i) = o;
+      }
+    } else {
+      for (int64_t j = i; j < n; ++j) {
+        float mv = b1 * mom1[j] + (1.0f - b1) * grad[j];
+        float vv = b2 * mom2[j] + (1.0f - b2) * grad[j] * grad[j];
+        float th = master[j];
+        th -= lr * ((mv * c1) / (sqrtf(vv * c2) + eps) + wd * th);
+        master[j] = th;
+        mom1[j] = mv;
+        mom2[j] = vv;
+        if (pbf) pbf[j] = (bf16)th;
+      }
+    }
+  }
+}
+
+__global__ void cast_kernel(int64_t n, const float* __restrict__ src, bf16* __restrict__ dst) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = (bf16)src[i];
+}
+
+__global__ void fill_kernel(int64_t n, float* __restrict__ dst, float value) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = value;
+}
+
+__global__ void bf16_to_f32_kernel(int64_t n, const bf16* __restrict__ src, float* __restrict__ dst) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = (float)src[i];
+}
+
+__device__ __forceinline__ uint64_t splitmix64_out(uint64_t seed, uint64_t n) {
+  uint64_t z = seed + (n + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+__global__ void init_normal_kernel(int64_t n, float* __restrict__ dst, uint64_t seed, uint64_t tensor_index,
+                                   double stddev) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  const uint64_t c = (tensor_index << 40) | (uint64_t)e;
+  const uint64_t r0 = splitmix64_out(seed, 2 * c);
+  const uint64_t r1 = splitmix64_out(seed, 2 * c + 1);
+  const double u1 = ((double)(r0 >> 11) + 1.0) * 0x1.0p-53;
+  const double u2 = (double)(r1 >> 11) * 0x1.0p-53;
+  const double z = sqrt(-2.0 * log(u1)) * cos(2.0 * 3.14159265358979323846 * u2);
+  dst[e] = (float)(stddev * z);
+}
+
+unsigned blocks_for(int64_t n, int per_thread = 1) {
+  return (unsigned)ceil_div64(ceil_div64(n, per_thread), 256);
+}
+
+}  // namespace
+
+int adamw(int64_t n, float* master, const float* grad, float* m, float* v, bf16* param_bf16, float lr,
+          float beta1, float beta2, float eps, float wd, int t, hipStream_t stream) {
+  if (n < 0 || !master || !grad || !m || !v || t < 1) return gpt2_internal_fail(1, "adamw: bad arguments");
+  if (n == 0) return 0;
+  if (((uintptr_t)master | (uintptr_t)grad | (uintptr_t)m | (uintptr_t)v) % 16 ||
+      (param_bf16 && (uintptr_t)param_bf16 % 8))
+    return gpt2_internal_fail(1, "adamw: buffers must be 16-byte aligned");
+  const double c1 = 1.0 / (1.0 - pow((double)beta1, (double)t));
+  const double c2 = 1.0 / (1.0 - pow((double)beta2, (double)t));
+  unsigned grid = (unsigned)std::min<int64_t>(ceil_div64(n, 4 * 256), 8192);
+  hipLaunchKernelGGL(adamw_kernel, dim3(grid), dim3(256), 0, stream, n, master, grad, m, v, param_bf16, lr, beta1,
+                     beta2, eps, wd, (float)c1, (float)c2);
+  GPT2_LAUNCH_CHECK();
+  return 0;
+}
+
+int cast_f32_to_bf16(int64_t n, const float* src, bf16* dst, hipStream_t stream) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(cast_kernel, dim3(blocks_for(n)), dim3(256), 0, stream, n, src, dst);
+  GPT2_LAUNCH_CHECK();
+  return 0;
+}
+
+int init_normal(int64_t n, float* dst, uint64_t seed, int tensor_index, double stddev, hipStream_t stream) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(init_normal_kernel, dim3(blocks_for(n)), dim3(256), 0, stream, n, dst, seed,
+                     (uint64_t)tensor_index, stddev);
+  GPT2_LAUNCH_CHECK();
+  return 0;
+}
+
+int fill_f32(int64_t n, float* dst, float value, hipStream_t stream) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(fill_kernel, dim3(blocks_for(n)), dim3(256), 0, stream, n, dst, value);
+  GPT2_LAUNCH_CHECK();
+  return 0;
+}
+
+int convert_to_f32(int dtype, int64_t n, const void* src, float* dst, hipStream_t stream) {
+  if (n <= 0) return 0;
+  if (dtype == BF16) {
+    hipLaunchKernelGGL(bf16_to_f32_kernel, dim3(blocks_for(n)), dim3(256), 0, stream, n, (const bf16*)src, dst);
+    GPT2_LAUNCH_CHECK();
+    return 0;
+  }
+  GPT2_HIP_CHECK(hipMemcpyAsync(dst, src, n * sizeof(float), hipMemcpyDeviceToDevice, stream));
+  return 0;
+}
+
+}  // namespace gpt2k

@@ -1,0 +1,115 @@
+// Device and host helpers shared by the GPT-2 HIP kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include <algorithm>
+
+typedef __bf16 bf16;
+
+// ---------------------------------------------------------------- conversions
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+// Round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// ---------------------------------------------------------------- 8-wide vectors
+// One "chunk" is 8 consecutive elements: 16 bytes of bf16 or 32 bytes of fp32.
+
+template <typename T> struct Chunk8;
+
+template <> struct Chunk8<float> {
+  __device__ __forceinline__ static void load(const float* p, float v[8]) {
+    float4 a = *reinterpret_cast<const float4*>(p);
+    float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  __device__ __forceinline__ static void store(float* p, const float v[8]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+};
+
+template <> struct Chunk8<bf16> {
+  __device__ __forceinline__ static void load(const bf16* p, float v[8]) {
+    uint4 u = *reinterpret_cast<const uint4*>(p);
+    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ __forceinline__ static void store(bf16* p, const float v[8]) {
+    typedef bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+    bf16x8_t o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (bf16)v[i];
+    *reinterpret_cast<bf16x8_t*>(p) = o;
+  }
+};
+
+// ---------------------------------------------------------------- reductions
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// ---------------------------------------------------------------- math
+
+// exp(x) through the hardware base-2 exponential.
+__device__ __forceinline__ float fast_exp(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+// GELU, tanh form: 0.5 u (1 + tanh(k0 (u + k1 u^3))), with
+// tanh(z) = 1 - 2 / (1 + e^{2z}) (saturates correctly for |z| large).
+__device__ __forceinline__ float gelu_tanh_f(float u) {
+  const float k0 = 0.7978845608028654f, k1 = 0.044715f;
+  float z = k0 * (u + k1 * u * u * u);
+  float th = 1.0f - 2.0f / (1.0f + __expf(2.0f * z));
+  return 0.5f * u * (1.0f + th);
+}
+
+// d/du of gelu_tanh_f.
+__device__ __forceinline__ float gelu_tanh_grad_f(float u) {
+  const float k0 = 0.7978845608028654f, k1 = 0.044715f;
+  float z = k0 * (u + k1 * u * u * u);
+  float th = 1.0f - 2.0f / (1.0f + __expf(2.0f * z));
+  float dz = k0 * (1.0f + 3.0f * k1 * u * u);
+  return 0.5f * (1.0f + th) + 0.5f * u * (1.0f - th * th) * dz;
+}
+
+// ---------------------------------------------------------------- host side
+
+#define GPT2_HIP_CHECK(expr)                                  \
+  do {                                                        \
+    hipError_t _e = (expr);                                   \
+    if (_e != hipSuccess) return gpt2_internal_hip_fail(_e, #expr, __FILE__, __LINE__); \
+  } while (0)
+
+#define GPT2_LAUNCH_CHECK() GPT2_HIP_CHECK(hipGetLastError())
+
+int gpt2_internal_hip_fail(hipError_t e, const char* expr, const char* file, int line);
+int gpt2_internal_fail(int status, const char* fmt, ...);
+
+static inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }

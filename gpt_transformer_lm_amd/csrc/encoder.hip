@@ -1,0 +1,234 @@
+// Token + position encoder, forward and backward (the encoder_forward /
+// encoder_backward rows of the kernel table in "State of the Union
+// [May 3, 2024]", section "Runtime, DRAM traffic, instructions").
+//
+// Forward:  x0[b, t, :] = wte[tok[b, t], :] + wpe[t, :]  (16-byte chunks).
+// Backward: dwpe[t] = sum_b dx0[b, t];  dwte[k] += sum_{positions p, tok[p] = k} dx0[p].
+// Token ids are heavily skewed (Zipf-like text statistics: the most frequent
+// id can own >10% of all positions), so the scatter is done without atomics
+// and in a fixed order:
+//   1. sort the keys (token << S) | position in one workgroup (bitonic, LDS);
+//   2. cut the sorted list into pieces of 64 entries; each piece sums its runs
+//      of equal tokens; a run that lies wholly inside the piece is added to
+//      its dwte row directly (only this piece touches that row); a run that
+//      crosses a piece boundary leaves a partial row;
+//   3. the piece where a boundary-crossing run starts adds its partial and the
+//      continuation partials of the following pieces, in order.
+// The result is deterministic (independent of scheduling).
+
+#include "kernels.h"
+
+namespace gpt2k {
+namespace {
+
+constexpr int kSortMax = 32768;   // B*T limit of the one-workgroup sort
+constexpr int kPiece = 64;
+
+template <typename T>
+__global__ void encoder_fwd_kernel(int BT, int T_, int C, const int32_t* __restrict__ tokens,
+                                   const T* __restrict__ wte, const T* __restrict__ wpe, T* __restrict__ out,
+                                   int Vrows) {
+  const int nch = C / 8;
+  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)BT * nch) return;
+  int p = idx / nch, ch = idx % nch;
+  int t = p % T_;
+  int tok = tokens[p];
+  tok = tok < 0 ? 0 : (tok >= Vrows ? Vrows - 1 : tok);   // memory safety only
+  float a[8], b[8];
+  Chunk8<T>::load(wte + (size_t)tok * C + ch * 8, a);
+  Chunk8<T>::load(wpe + (size_t)t * C + ch * 8, b);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] += b[e];
+  Chunk8<T>::store(out + (size_t)p * C + ch * 8, a);
+}
+
+// dwpe[t, c] (+)= sum_b dx0[b, t, c]
+__global__ void encoder_bwd_wpe_kernel(int B, int T_, int C, const float* __restrict__ dx0,
+                                       float* __restrict__ dwpe, bool accumulate) {
+  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)T_ * C) return;
+  float s = 0.f;
+  for (int b = 0; b < B; ++b) s += dx0[(size_t)b * T_ * C + idx];
+  dwpe[idx] = accumulate ? dwpe[idx] + s : s;
+}
+
+// One workgroup: sorts keys[i] = (tok[i] << shift) | i, i < n, ascending.
+__global__ __launch_bounds__(1024) void sort_keys_kernel(int n, int shift, const int32_t* __restrict__ tokens,
+                                                         int Vrows, uint32_t* __restrict__ sorted) {
+  extern __shared__ uint32_t keys[];
+  int np = 1;
+  while (np < n) np <<= 1;
+  for (int i = threadIdx.x; i < np; i += 1024) {
+    if (i < n) {
+      int tok = tokens[i];
+      tok = tok < 0 ? 0 : (tok >= Vrows ? Vrows - 1 : tok);
+      keys[i] = ((uint32_t)tok << shift) | (uint32_t)i;
+    } else {
+      keys[i] = 0xffffffffu;
+    }
+  }
+  __syncthreads();
+  for (int k = 2; k <= np; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < np; i += 1024) {
+        int ixj = i ^ j;
+        if (ixj > i) {
+          uint32_t a = keys[i], b = keys[ixj];
+          bool up = (i & k) == 0;
+          if ((a > b) == up) {
+            keys[i] = b;
+            keys[ixj] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < n; i += 1024) sorted[i] = keys[i];
+}
+
+__device__ __forceinline__ int key_tok(uint32_t k, int shift) { return (int)(k >> shift); }
+__device__ __forceinline__ int key_pos(uint32_t k, int shift) { return (int)(k & ((1u << shift) - 1)); }
+
+// Step 2: one block per piece; threads stride over channels.
+__global__ __launch_bounds__(256) void encoder_bwd_pieces_kernel(int n, int C, int shift,
+                                                                 const uint32_t* __restrict__ sorted,
+                                                                 const float* __restrict__ dx0,
+                                                                 float* __restrict__ dwte,
+                                                                 float* __restrict__ pcont,
+                                                                 float* __restrict__ pown) {
+  const int piece = blockIdx.x;
+  const int start = piece * kPiece;
+  const int end = min(n, start + kPiece);
+  __shared__ int stok[kPiece], spos[kPiece];
+  for (int e = threadIdx.x; e < end - start; e += blockDim.x) {
+    uint32_t k = sorted[start + e];
+    stok[e] = key_tok(k, shift);
+    spos[e] = key_pos(k, shift);
+  }
+  __syncthreads();
+  const int prev_tok = start > 0 ? key_tok(sorted[start - 1], shift) : -1;
+  const int next_tok = end < n ? key_tok(sorted[end], shift) : -1;
+  for (int c = threadIdx.x; c < C; c += blockDim.x) {
+    int rs = 0;   // run start (index within piece)
+    float acc = 0.f;
+    for (int e = 0; e < end - start; ++e) {
+      acc += dx0[(size_t)spos[e] * C + c];
+      const bool last = (e == end - start - 1) || (stok[e + 1] != stok[e]);
+      if (last) {
+        const int tok = stok[e];
+        const bool from_prev = (rs == 0) && (prev_tok == tok);
+        const bool to_next = (e == end - start - 1) && (next_tok == tok);
+        if (from_prev)
+          pcont[(size_t)piece * C + c] = acc;
+        else if (to_next)
+          pown[(size_t)piece * C + c] = acc;
+        else
+          dwte[(size_t)tok * C + c] += acc;
+        acc = 0.f;
+        rs = e + 1;
+      }
+    }
+  }
+}
+
+// Step 3: one block per piece whose last run starts a boundary-crossing run.
+__global__ __launch_bounds__(256) void encoder_bwd_spans_kernel(int n, int C, int shift, int npieces,
+                                                                const uint32_t* __restrict__ sorted,
+                                                                const float* __restrict__ pcont,
+                                                                const float* __restrict__ pown,
+                                                                float* __restrict__ dwte) {
+  const int piece = blockIdx.x;
+  const int start = piece * kPiece;
+  const int end = min(n, start + kPiece);
+  if (end >= n) return;
+  const int tok = key_tok(sorted[end - 1], shift);
+  if (key_tok(sorted[end], shift) != tok) return;    // last run does not continue
+  // find where the last run starts; if it started in an earlier piece this
+  // piece holds a continuation, not the owner partial
+  int rs = end - 1;
+  while (rs > start && key_tok(sorted[rs - 1], shift) == tok) --rs;
+  if (rs == start && start > 0 && key_tok(sorted[start - 1], shift) == tok) return;
+  for (int c = threadIdx.x; c < C; c += blockDim.x) {
+    float acc = pown[(size_t)piece * C + c];
+    for (int q = piece + 1; q < npieces && key_tok(sorted[q * kPiece], shift) == tok; ++q)
+      acc += pcont[(size_t)q * C + c];
+    dwte[(size_t)tok * C + c] += acc;
+  }
+}
+
+int pos_bits(int n) {
+  int s = 0;
+  while ((1 << s) < n) ++s;
+  return s;
+}
+
+}  // namespace
+
+int encoder_forward(int dtype, int B, int T_, int C, int vocab_rows, const int32_t* tokens, const void* wte,
+                    const void* wpe, void* out, hipStream_t stream) {
+  if (B < 0 || T_ < 0 || C <= 0 || C % 8 || vocab_rows <= 0 || !tokens || !wte || !wpe || !out)
+    return gpt2_internal_fail(1, "encoder_forward: bad arguments");
+  const int BT = B * T_;
+  if (BT == 0) return 0;
+  int64_t total = (int64_t)BT * (C / 8);
+  dim3 grid((unsigned)ceil_div64(total, 256));
+  if (dtype == BF16)
+    hipLaunchKernelGGL(encoder_fwd_kernel<bf16>, grid, dim3(256), 0, stream, BT, T_, C, tokens,
+                       (const bf16*)wte, (const bf16*)wpe, (bf16*)out, vocab_rows);
+  else
+    hipLaunchKernelGGL(encoder_fwd_kernel<float>, grid, dim3(256), 0, stream, BT, T_, C, tokens,
+                       (const float*)wte, (const float*)wpe, (float*)out, vocab_rows);
+  GPT2_LAUNCH_CHECK();
+  return 0;
+}
+
+size_t encoder_backward_workspace_bytes(int B, int T_, int C) {
+  const int n = B * T_;
+  const int np = (int)ceil_div64(n, kPiece);
+  return (size_t)n * sizeof(uint32_t) + 2 * (size_t)np * C * sizeof(float) + 512;
+}
+
+int encoder_backward(int B, int T_, int C, int vocab_rows, const int32_t* tokens, const float* dx0,
+                     float* dwte, float* dwpe, bool accumulate_wpe, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  if (B < 0 || T_ < 0 || C <= 0 || vocab_rows <= 0 || vocab_rows > 65536 || !tokens || !dx0 || !dwte || !dwpe)
+    return gpt2_internal_fail(1, "encoder_backward: bad arguments");
+  const int n = B * T_;
+  if (n == 0) return 0;
+  if (n > kSortMax) return gpt2_internal_fail(1, "encoder_backward: B*T=%d exceeds %d", n, kSortMax);
+  if (!workspace || workspace_bytes < encoder_backward_workspace_bytes(B, T_, C))
+    return gpt2_internal_fail(3, "encoder_backward: workspace too small");
+  const int shift = pos_bits(n);
+  if (shift + 16 > 32) return gpt2_internal_fail(1, "encoder_backward: key overflow");
+  const int npieces = (int)ceil_div64(n, kPiece);
+  uint32_t* sorted = (uint32_t*)workspace;
+  float* pcont = (float*)((char*)workspace + (((size_t)n * 4 + 255) / 256) * 256);
+  float* pown = pcont + (size_t)npieces * C;
+
+  hipLaunchKernelGGL(encoder_bwd_wpe_kernel, dim3((unsigned)ceil_div64((int64_t)T_ * C, 256)), dim3(256), 0,
+                     stream, B, T_, C, dx0, dwpe, accumulate_wpe);
+  GPT2_LAUNCH_CHECK();
+  int np2 = 1;
+  while (np2 < n) np2 <<= 1;
+  static bool lds_attr_set = false;
+  if (!lds_attr_set) {
+    GPT2_HIP_CHECK(hipFuncSetAttribute((const void*)sort_keys_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       kSortMax * (int)sizeof(uint32_t)));
+    lds_attr_set = true;
+  }
+  hipLaunchKernelGGL(sort_keys_kernel, dim3(1), dim3(1024), (size_t)np2 * sizeof(uint32_t), stream, n, shift,
+                     tokens, vocab_rows, sorted);
+  GPT2_LAUNCH_CHECK();
+  hipLaunchKernelGGL(encoder_bwd_pieces_kernel, dim3(npieces), dim3(256), 0, stream, n, C, shift, sorted, dx0,
+                     dwte, pcont, pown);
+  GPT2_LAUNCH_CHECK();
+  hipLaunchKernelGGL(encoder_bwd_spans_kernel, dim3(npieces), dim3(256), 0, stream, n, C, shift, npieces, sorted,
+                     pcont, pown, dwte);
+  GPT2_LAUNCH_CHECK();
+  return 0;
+}
+
+}  // namespace gpt2k

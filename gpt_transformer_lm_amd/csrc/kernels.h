@@ -1,0 +1,106 @@
+// Launchers of the GPT-2 step kernels (internal C++ interface of the library).
+// Every launcher enqueues on `stream` and returns a gpt2 status code.
+#pragma once
+
+#include "common.h"
+
+namespace gpt2k {
+
+enum DType { F32 = 0, BF16 = 1 };
+
+// ------------------------------------------------------------------ GEMM
+//
+// C[M, N] = sum_k A(m, k) * B(n, k)
+//   A(m, k) = A[m * lda + k]  (a_kmajor)   or  A[k * lda + m]  (!a_kmajor)
+//   B(n, k) = B[n * ldb + k]  (b_kmajor)   or  B[k * ldb + n]  (!b_kmajor)
+// Epilogues (element (m, n), v = the fp32 sum):
+//   STORE      C = v
+//   BIAS       C = v + bias[n]
+//   BIAS_RES   C = v + bias[n] + R[m * ld_aux + n]
+//   BIAS_GELU  U[m * ldc + n] = v + bias[n];  C = gelu_tanh(v + bias[n])
+//   GELU_BWD   C = v * gelu_tanh'(U[m * ld_aux + n])
+//   WGRAD      fp32 result into out32[m * N + n] (overwrite, or add if
+//              accumulate), and if bias_grad32 != null also
+//              bias_grad32[m] = sum_k A(m, k) (A must be !a_kmajor).
+//              Split over K into partial sums that a second kernel reduces
+//              in a fixed order (deterministic).
+enum Epi { EPI_STORE = 0, EPI_BIAS = 1, EPI_BIAS_RES = 2, EPI_BIAS_GELU = 3, EPI_GELU_BWD = 4,
+           EPI_WGRAD = 5 };
+
+struct GemmDesc {
+  int dtype;            // F32 or BF16 (type of A, B, C, bias, R, U)
+  bool a_kmajor, b_kmajor;
+  int M, N, K;
+  const void* A; int64_t lda;
+  const void* B; int64_t ldb;
+  int epi;
+  void* C; int64_t ldc;
+  const void* bias;
+  const void* aux_in; int64_t ld_aux;   // R (BIAS_RES) or U (GELU_BWD)
+  void* aux_out;                        // U (BIAS_GELU)
+  float* out32;                         // WGRAD result [M, N]
+  float* bias_grad32;                   // WGRAD bias gradient [M] (optional)
+  bool accumulate;                      // WGRAD: add into out32 / bias_grad32
+  void* workspace; size_t workspace_bytes;
+};
+
+// Device bytes of scratch a GEMM with this descriptor needs (WGRAD only).
+size_t gemm_workspace_bytes(int dtype, int epi, int M, int N, int K);
+int gemm(const GemmDesc& d, hipStream_t stream);
+
+// ------------------------------------------------------------------ LayerNorm
+// y = (x - mean) * rstd * w + b per row of C; mean, rstd fp32 [N].
+int layernorm_forward(int dtype, int N, int C, const void* x, const void* w, const void* b,
+                      void* y, float* mean, float* rstd, hipStream_t stream);
+// dres[N, C] (fp32) += dx; dres_copy (dtype, optional) = new dres;
+// dw, db (fp32 [C]) = (or +=, if accumulate) column sums.  If dres_overwrite,
+// dres is written (= dx) instead of accumulated.
+size_t layernorm_backward_workspace_bytes(int N, int C);
+int layernorm_backward(int dtype, int N, int C, const void* dy, const void* x, const void* w,
+                       const float* mean, const float* rstd, float* dres, bool dres_overwrite,
+                       void* dres_copy, float* dw, float* db, bool accumulate, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+// ------------------------------------------------------------------ attention
+// qkv [B, T, 3C] -> out [B, T, C], lse [B, H, T] fp32.
+int attention_forward(int dtype, int B, int T, int H, int hd, const void* qkv, void* out,
+                      float* lse, hipStream_t stream);
+size_t attention_backward_workspace_bytes(int B, int T, int H, int hd);
+int attention_backward(int dtype, int B, int T, int H, int hd, const void* qkv, const void* out,
+                       const void* dout, const float* lse, void* dqkv, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+// ------------------------------------------------------------------ classifier
+// In place over logits [N, Vp] (row stride Vp): columns >= V are masked.
+// losses[i] = logsumexp_{j<V} z_ij - z_i,y_i;  z_ij <- (softmax_ij - [j==y_i]) * dscale
+// for j < V and 0 for j >= V.
+int softmax_xent(int dtype, int N, int V, int Vp, void* logits, const int32_t* labels,
+                 float* losses, float dscale, hipStream_t stream);
+// out[0] = sum_i x[i] * scale  (fixed order; single block).
+int sum_scaled(int n, const float* x, float scale, float* out, hipStream_t stream);
+
+// ------------------------------------------------------------------ encoder
+// Token ids are clamped to [0, vocab_rows) for memory safety only (ids outside
+// [0, V) are undefined behaviour of the step).
+int encoder_forward(int dtype, int B, int T, int C, int vocab_rows, const int32_t* tokens,
+                    const void* wte, const void* wpe, void* out, hipStream_t stream);
+size_t encoder_backward_workspace_bytes(int B, int T, int C);
+// dwte[tok] += dx0 rows (fp32, deterministic order); dwpe[0:T] = (or +=) sum over b.
+// B*T <= 32768 and vocab_rows <= 65536 (one-workgroup key sort).
+int encoder_backward(int B, int T, int C, int vocab_rows, const int32_t* tokens, const float* dx0,
+                     float* dwte, float* dwpe, bool accumulate_wpe, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+// ------------------------------------------------------------------ optimizer
+// AdamW over n fp32 parameters; writes the bf16 copy if param_bf16 != null.
+int adamw(int64_t n, float* master, const float* grad, float* m, float* v, bf16* param_bf16,
+          float lr, float beta1, float beta2, float eps, float wd, int t, hipStream_t stream);
+// dst = RNE bf16 of src.
+int cast_f32_to_bf16(int64_t n, const float* src, bf16* dst, hipStream_t stream);
+// Seeded GPT-2-style normal init of one tensor (see gpt2.h).
+int init_normal(int64_t n, float* dst, uint64_t seed, int tensor_index, double stddev,
+                hipStream_t stream);
+int fill_f32(int64_t n, float* dst, float value, hipStream_t stream);
+int convert_to_f32(int dtype, int64_t n, const void* src, float* dst, hipStream_t stream);
+
+}  // namespace gpt2k

@@ -1,0 +1,258 @@
+// LayerNorm forward and backward (the layernorm_forward / layernorm_backward
+// rows of the kernel table in "State of the Union [May 3, 2024]", section
+// "Runtime, DRAM traffic, instructions": 25 launches each per GPT-2 124M step,
+// two per block plus the final one).
+//
+// One wavefront per row; each lane holds up to NCH 16-byte chunks of the row
+// in registers, so a row is read once.  Statistics are fp32:
+//   mean = sum(x) / C,  var = sum((x - mean)^2) / C (biased),  rstd = 1/sqrt(var + 1e-5).
+// Backward, with xhat = (x - mean) * rstd and g = dy * w:
+//   dx = rstd * (g - sum(g)/C - xhat * sum(g * xhat)/C)
+// accumulated into the fp32 residual-stream gradient (the residual add of the
+// block is the identity, so its gradient is this running sum), with a
+// storage-type copy for the next GEMM.  dw = sum_rows dy * xhat and
+// db = sum_rows dy are accumulated per wave in registers, written as per-wave
+// partial rows and summed by a second kernel in a fixed order.
+
+#include "kernels.h"
+
+namespace gpt2k {
+namespace {
+
+constexpr float kLnEps = 1e-5f;
+
+template <typename T, int NCH>
+__global__ __launch_bounds__(256) void ln_fwd_kernel(int N, int C, const T* __restrict__ x,
+                                                     const T* __restrict__ w, const T* __restrict__ b,
+                                                     T* __restrict__ y, float* __restrict__ mean,
+                                                     float* __restrict__ rstd) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= N) return;
+  const int nch = C / 8;
+  const T* xr = x + (size_t)row * C;
+  float v[NCH][8];
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    int ch = lane + 64 * c;
+    if (ch < nch) {
+      Chunk8<T>::load(xr + ch * 8, v[c]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += v[c][e];
+    }
+  }
+  const float mu = wave_sum(s) / (float)C;
+  float s2 = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    int ch = lane + 64 * c;
+    if (ch < nch) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float d = v[c][e] - mu;
+        s2 += d * d;
+      }
+    }
+  }
+  const float var = wave_sum(s2) / (float)C;
+  const float rs = 1.0f / sqrtf(var + kLnEps);
+  T* yr = y + (size_t)row * C;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    int ch = lane + 64 * c;
+    if (ch < nch) {
+      float wv[8], bv[8], o[8];
+      Chunk8<T>::load(w + ch * 8, wv);
+      Chunk8<T>::load(b + ch * 8, bv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (v[c][e] - mu) * rs * wv[e] + bv[e];
+      Chunk8<T>::store(yr + ch * 8, o);
+    }
+  }
+  if (lane == 0) {
+    mean[row] = mu;
+    rstd[row] = rs;
+  }
+}
+
+template <typename T, int NCH>
+__global__ __launch_bounds__(256) void ln_bwd_kernel(int N, int C, const T* __restrict__ dy,
+                                                     const T* __restrict__ x, const T* __restrict__ w,
+                                                     const float* __restrict__ mean,
+                                                     const float* __restrict__ rstd,
+                                                     float* __restrict__ dres, bool dres_overwrite,
+                                                     T* __restrict__ dres_copy,
+                                                     float* __restrict__ part_dw,
+                                                     float* __restrict__ part_db) {
+  const int wave_id = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nwaves = gridDim.x * 4;
+  const int lane = threadIdx.x & 63;
+  const int nch = C / 8;
+  const float invC = 1.0f / (float)C;
+  float wv[NCH][8], dwa[NCH][8], dba[NCH][8];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    int ch = lane + 64 * c;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { dwa[c][e] = 0.f; dba[c][e] = 0.f; wv[c][e] = 0.f; }
+    if (ch < nch) Chunk8<T>::load(w + ch * 8, wv[c]);
+  }
+  for (int row = wave_id; row < N; row += nwaves) {
+    const float mu = mean[row], rs = rstd[row];
+    const T* dyr = dy + (size_t)row * C;
+    const T* xr = x + (size_t)row * C;
+    float dyv[NCH][8], xh[NCH][8];
+    float sg = 0.f, sgx = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      int ch = lane + 64 * c;
+      if (ch < nch) {
+        float xv[8];
+        Chunk8<T>::load(dyr + ch * 8, dyv[c]);
+        Chunk8<T>::load(xr + ch * 8, xv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          xh[c][e] = (xv[e] - mu) * rs;
+          float g = dyv[c][e] * wv[c][e];
+          sg += g;
+          sgx += g * xh[c][e];
+          dwa[c][e] += dyv[c][e] * xh[c][e];
+          dba[c][e] += dyv[c][e];
+        }
+      }
+    }
+    const float mg = wave_sum(sg) * invC;
+    const float mgx = wave_sum(sgx) * invC;
+    float* dr = dres + (size_t)row * C;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      int ch = lane + 64 * c;
+      if (ch < nch) {
+        float o[8];
+        if (dres_overwrite) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = 0.f;
+        } else {
+          Chunk8<float>::load(dr + ch * 8, o);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          o[e] += rs * (dyv[c][e] * wv[c][e] - mg - xh[c][e] * mgx);
+        Chunk8<float>::store(dr + ch * 8, o);
+        if (dres_copy) Chunk8<T>::store(dres_copy + (size_t)row * C + ch * 8, o);
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    int ch = lane + 64 * c;
+    if (ch < nch) {
+      Chunk8<float>::store(part_dw + (size_t)wave_id * C + ch * 8, dwa[c]);
+      Chunk8<float>::store(part_db + (size_t)wave_id * C + ch * 8, dba[c]);
+    }
+  }
+}
+
+// out[c] (+)= sum_p part[p * C + c], p in order.
+__global__ void column_reduce_kernel(const float* __restrict__ part, int P, int C,
+                                     float* __restrict__ out, bool accumulate) {
+  int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= C) return;
+  float s = 0.f;
+  for (int p = 0; p < P; ++p) s += part[(size_t)p * C + c];
+  out[c] = accumulate ? out[c] + s : s;
+}
+
+int nch_for(int C) {
+  int nch = C / 8;
+  if (nch <= 64) return 1;
+  if (nch <= 128) return 2;
+  if (nch <= 256) return 4;
+  if (nch <= 512) return 8;
+  return -1;
+}
+
+int bwd_waves(int N) { return (int)std::min<int64_t>(1024, ((int64_t)N + 3) / 4 * 4); }
+
+template <typename T>
+int fwd_t(int N, int C, const void* x, const void* w, const void* b, void* y, float* mean, float* rstd,
+          hipStream_t s) {
+  dim3 grid((unsigned)ceil_div64(N, 4)), block(256);
+  const T* X = (const T*)x;
+  const T* W = (const T*)w;
+  const T* Bb = (const T*)b;
+  T* Y = (T*)y;
+  switch (nch_for(C)) {
+    case 1: hipLaunchKernelGGL((ln_fwd_kernel<T, 1>), grid, block, 0, s, N, C, X, W, Bb, Y, mean, rstd); break;
+    case 2: hipLaunchKernelGGL((ln_fwd_kernel<T, 2>), grid, block, 0, s, N, C, X, W, Bb, Y, mean, rstd); break;
+    case 4: hipLaunchKernelGGL((ln_fwd_kernel<T, 4>), grid, block, 0, s, N, C, X, W, Bb, Y, mean, rstd); break;
+    case 8: hipLaunchKernelGGL((ln_fwd_kernel<T, 8>), grid, block, 0, s, N, C, X, W, Bb, Y, mean, rstd); break;
+    default: return gpt2_internal_fail(1, "layernorm: C=%d unsupported", C);
+  }
+  GPT2_LAUNCH_CHECK();
+  return 0;
+}
+
+template <typename T>
+int bwd_t(int N, int C, const void* dy, const void* x, const void* w, const float* mean,
+          const float* rstd, float* dres, bool ovw, void* dres_copy, float* pdw, float* pdb,
+          hipStream_t s) {
+  int waves = bwd_waves(N);
+  dim3 grid((unsigned)(waves / 4)), block(256);
+  const T* DY = (const T*)dy;
+  const T* X = (const T*)x;
+  const T* W = (const T*)w;
+  T* DC = (T*)dres_copy;
+  switch (nch_for(C)) {
+    case 1: hipLaunchKernelGGL((ln_bwd_kernel<T, 1>), grid, block, 0, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
+    case 2: hipLaunchKernelGGL((ln_bwd_kernel<T, 2>), grid, block, 0, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
+    case 4: hipLaunchKernelGGL((ln_bwd_kernel<T, 4>), grid, block, 0, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
+    case 8: hipLaunchKernelGGL((ln_bwd_kernel<T, 8>), grid, block, 0, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
+    default: return gpt2_internal_fail(1, "layernorm: C=%d unsupported", C);
+  }
+  GPT2_LAUNCH_CHECK();
+  return 0;
+}
+
+}  // namespace
+
+int layernorm_forward(int dtype, int N, int C, const void* x, const void* w, const void* b, void* y,
+                      float* mean, float* rstd, hipStream_t stream) {
+  if (N < 0 || C <= 0 || C % 8 || !x || !w || !b || !y || !mean || !rstd)
+    return gpt2_internal_fail(1, "layernorm_forward: bad arguments");
+  if (N == 0) return 0;
+  return dtype == BF16 ? fwd_t<bf16>(N, C, x, w, b, y, mean, rstd, stream)
+                       : fwd_t<float>(N, C, x, w, b, y, mean, rstd, stream);
+}
+
+size_t layernorm_backward_workspace_bytes(int N, int C) {
+  return 2 * (size_t)bwd_waves(N) * C * sizeof(float) + 256;
+}
+
+int layernorm_backward(int dtype, int N, int C, const void* dy, const void* x, const void* w,
+                       const float* mean, const float* rstd, float* dres, bool dres_overwrite,
+                       void* dres_copy, float* dw, float* db, bool accumulate, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  if (N < 0 || C <= 0 || C % 8 || !dy || !x || !w || !mean || !rstd || !dres || !dw || !db)
+    return gpt2_internal_fail(1, "layernorm_backward: bad arguments");
+  if (N == 0) return 0;
+  size_t need = layernorm_backward_workspace_bytes(N, C);
+  if (!workspace || workspace_bytes < need)
+    return gpt2_internal_fail(3, "layernorm_backward: workspace too small");
+  const int P = bwd_waves(N);
+  float* pdw = (float*)workspace;
+  float* pdb = pdw + (size_t)P * C;
+  int rc = dtype == BF16 ? bwd_t<bf16>(N, C, dy, x, w, mean, rstd, dres, dres_overwrite, dres_copy, pdw, pdb, stream)
+                         : bwd_t<float>(N, C, dy, x, w, mean, rstd, dres, dres_overwrite, dres_copy, pdw, pdb, stream);
+  if (rc) return rc;
+  hipLaunchKernelGGL(column_reduce_kernel, dim3((unsigned)ceil_div64(C, 256)), dim3(256), 0, stream, pdw, P,
+                     C, dw, accumulate);
+  GPT2_LAUNCH_CHECK();
+  hipLaunchKernelGGL(column_reduce_kernel, dim3((unsigned)ceil_div64(C, 256)), dim3(256), 0, stream, pdb, P,
+                     C, db, accumulate);
+  GPT2_LAUNCH_CHECK();
+  return 0;
+}
+
+}  // namespace gpt2k

@@ -1,0 +1,834 @@
+// Host runtime of the GPT-2 step library: configuration checks, the one-arena
+// memory plan, parameter table, seeded initialisation, orchestration of the
+// forward / backward / AdamW kernels on one HIP stream, state access, timing
+// hooks, and the C ABI of gpt2.h and gpt2_ops.h.
+//
+// The step follows the pre-LayerNorm GPT-2 block of the pages' kernel table
+// ("State of the Union [May 3, 2024]", section "Runtime, DRAM traffic,
+// instructions"): encoder -> L x [LN1 -> QKV -> attention -> projection +
+// residual -> LN2 -> fc + GELU -> fc-projection + residual] -> LNf -> tied
+// logits -> fused softmax cross-entropy, then the reverse pass and AdamW.
+// Memory: one arena holds parameters (fp32 master, bf16 copy), gradients,
+// AdamW moments, every saved activation and one scratch region shared by the
+// backward kernels (they run in order on one stream).  The opening bullet list
+// of that page notes the memory saved by not keeping per-layer backward
+// gradient buffers; likewise here the activation gradients live in four
+// buffers reused by every layer.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/gpt2.h"
+#include "../../include/gpt2_ops.h"
+#include "kernels.h"
+
+using namespace gpt2k;
+
+// ---------------------------------------------------------------- errors
+
+static thread_local char g_last_error[1024] = "";
+
+int gpt2_internal_fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int gpt2_internal_hip_fail(hipError_t e, const char* expr, const char* file, int line) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s failed: %s (%s:%d)", expr, hipGetErrorString(e), file, line);
+  return GPT2_E_HIP;
+}
+
+#define RC(x)                \
+  do {                       \
+    int _rc = (x);           \
+    if (_rc) return _rc;     \
+  } while (0)
+
+// ---------------------------------------------------------------- config
+
+namespace {
+
+const char* kParamNames[16] = {"wte",  "wpe",      "ln1w",     "ln1b", "qkvw", "qkvb",    "attprojw", "attprojb",
+                               "ln2w", "ln2b",     "fcw",      "fcb",  "fcprojw", "fcprojb", "lnfw", "lnfb"};
+
+struct ParamTable {
+  int64_t off[16];
+  int64_t shape[16][3];
+  int ndim[16];
+  int64_t total;
+};
+
+void param_table(const gpt2_config& c, bool padded, ParamTable* t) {
+  const int64_t V = padded ? c.padded_vocab_size : c.vocab_size;
+  const int64_t T = c.max_seq_len, L = c.num_layers, C = c.channels;
+  const int64_t sh[16][3] = {{V, C, 1},     {T, C, 1},     {L, C, 1},     {L, C, 1},
+                             {L, 3 * C, C}, {L, 3 * C, 1}, {L, C, C},     {L, C, 1},
+                             {L, C, 1},     {L, C, 1},     {L, 4 * C, C}, {L, 4 * C, 1},
+                             {L, C, 4 * C}, {L, C, 1},     {C, 1, 1},     {C, 1, 1}};
+  const int nd[16] = {2, 2, 2, 2, 3, 2, 3, 2, 2, 2, 3, 2, 3, 2, 1, 1};
+  int64_t o = 0;
+  for (int i = 0; i < 16; ++i) {
+    t->off[i] = o;
+    t->ndim[i] = nd[i];
+    for (int d = 0; d < 3; ++d) t->shape[i][d] = sh[i][d];
+    o += sh[i][0] * sh[i][1] * sh[i][2];
+  }
+  t->total = o;
+}
+
+int validate(const gpt2_config* c) {
+  if (!c) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "config is NULL");
+  if (c->dtype != GPT2_FP32 && c->dtype != GPT2_BF16)
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "dtype %d is neither GPT2_FP32 nor GPT2_BF16", c->dtype);
+  if (c->vocab_size <= 0 || c->vocab_size > 65536)
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "vocab_size %d outside (0, 65536]", c->vocab_size);
+  if (c->padded_vocab_size < c->vocab_size || c->padded_vocab_size % 64 || c->padded_vocab_size > 65536)
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "padded_vocab_size %d must be >= vocab_size, <= 65536 and a multiple of 64",
+                              c->padded_vocab_size);
+  if (c->num_layers < 0 || c->num_layers > 1024)
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "num_layers %d", c->num_layers);
+  if (c->channels <= 0 || c->channels % 64 || c->channels > 4096)
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "channels %d must be a positive multiple of 64, <= 4096", c->channels);
+  if (c->num_heads <= 0 || c->channels % c->num_heads)
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "num_heads %d must divide channels %d", c->num_heads, c->channels);
+  const int hd = c->channels / c->num_heads;
+  if (hd != 16 && hd != 32 && hd != 64 && hd != 128)
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "head dim %d unsupported (16, 32, 64, 128)", hd);
+  if (c->max_seq_len <= 0 || c->seq_len <= 0 || c->seq_len > c->max_seq_len)
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "seq_len %d / max_seq_len %d", c->seq_len, c->max_seq_len);
+  if (c->batch_size <= 0) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "batch_size %d", c->batch_size);
+  const int64_t BT = (int64_t)c->batch_size * c->seq_len;
+  if (BT % 64 || BT > 32768)
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "batch_size*seq_len = %lld must be a multiple of 64 and <= 32768",
+                              (long long)BT);
+  return GPT2_OK;
+}
+
+// ---------------------------------------------------------------- arena plan
+
+struct Plan {
+  size_t total = 0;
+  size_t alloc(size_t bytes) {
+    size_t o = total;
+    total += (bytes + 255) / 256 * 256;
+    return o;
+  }
+};
+
+struct LayerOffsets {
+  size_t ln1, ln1_mean, ln1_rstd, qkv, atty, lse, h, ln2, ln2_mean, ln2_rstd, u, g;
+};
+
+struct Layout {
+  ParamTable pt;
+  int64_t P;
+  size_t master, grad, adam_m, adam_v, params_bf16;
+  std::vector<size_t> resid;             // L + 1 buffers [BT, C]
+  std::vector<LayerOffsets> layer;
+  size_t tokens, lnf, lnf_mean, lnf_rstd, logits, losses, mean_loss;
+  size_t dres, dres_t, d_ln, d_big, d_qkv, scratch;
+  size_t scratch_bytes;
+  size_t total;
+};
+
+size_t scratch_need(const gpt2_config& c) {
+  const int dt = c.dtype;
+  const int BT = c.batch_size * c.seq_len, C = c.channels, Vp = c.padded_vocab_size;
+  size_t s = 0;
+  auto upd = [&](size_t x) { s = std::max(s, x); };
+  upd(gemm_workspace_bytes(dt, EPI_WGRAD, Vp, C, BT));
+  upd(gemm_workspace_bytes(dt, EPI_WGRAD, C, 4 * C, BT));
+  upd(gemm_workspace_bytes(dt, EPI_WGRAD, 4 * C, C, BT));
+  upd(gemm_workspace_bytes(dt, EPI_WGRAD, C, C, BT));
+  upd(gemm_workspace_bytes(dt, EPI_WGRAD, 3 * C, C, BT));
+  upd(layernorm_backward_workspace_bytes(BT, C));
+  upd(attention_backward_workspace_bytes(c.batch_size, c.seq_len, c.num_heads, C / c.num_heads));
+  upd(encoder_backward_workspace_bytes(c.batch_size, c.seq_len, C));
+  return s;
+}
+
+void make_layout(const gpt2_config& c, Layout* lo) {
+  param_table(c, true, &lo->pt);
+  lo->P = lo->pt.total;
+  const size_t es = c.dtype == GPT2_BF16 ? 2 : 4;
+  const size_t BT = (size_t)c.batch_size * c.seq_len, C = c.channels, L = c.num_layers;
+  const size_t BHT = (size_t)c.batch_size * c.num_heads * c.seq_len;
+  Plan p;
+  lo->master = p.alloc(lo->P * 4);
+  lo->grad = p.alloc(lo->P * 4);
+  lo->adam_m = p.alloc(lo->P * 4);
+  lo->adam_v = p.alloc(lo->P * 4);
+  lo->params_bf16 = c.dtype == GPT2_BF16 ? p.alloc(lo->P * 2) : 0;
+  lo->tokens = p.alloc(BT * 4);
+  lo->resid.resize(L + 1);
+  for (size_t l = 0; l <= L; ++l) lo->resid[l] = p.alloc(BT * C * es);
+  lo->layer.resize(L);
+  for (size_t l = 0; l < L; ++l) {
+    LayerOffsets& o = lo->layer[l];
+    o.ln1 = p.alloc(BT * C * es);
+    o.ln1_mean = p.alloc(BT * 4);
+    o.ln1_rstd = p.alloc(BT * 4);
+    o.qkv = p.alloc(BT * 3 * C * es);
+    o.atty = p.alloc(BT * C * es);
+    o.lse = p.alloc(BHT * 4);
+    o.h = p.alloc(BT * C * es);
+    o.ln2 = p.alloc(BT * C * es);
+    o.ln2_mean = p.alloc(BT * 4);
+    o.ln2_rstd = p.alloc(BT * 4);
+    o.u = p.alloc(BT * 4 * C * es);
+    o.g = p.alloc(BT * 4 * C * es);
+  }
+  lo->lnf = p.alloc(BT * C * es);
+  lo->lnf_mean = p.alloc(BT * 4);
+  lo->lnf_rstd = p.alloc(BT * 4);
+  lo->logits = p.alloc(BT * (size_t)c.padded_vocab_size * es);
+  lo->losses = p.alloc(BT * 4);
+  lo->mean_loss = p.alloc(4);
+  lo->dres = p.alloc(BT * C * 4);
+  lo->dres_t = c.dtype == GPT2_BF16 ? p.alloc(BT * C * es) : lo->dres;
+  lo->d_ln = p.alloc(BT * C * es);
+  lo->d_big = p.alloc(BT * 4 * C * es);
+  lo->d_qkv = p.alloc(BT * 3 * C * es);
+  lo->scratch_bytes = scratch_need(c);
+  lo->scratch = p.alloc(lo->scratch_bytes);
+  lo->total = p.total;
+}
+
+// ---------------------------------------------------------------- timing sites
+
+enum Site {
+  S_QKV = 0, S_ATTPROJ, S_FC, S_FCPROJ, S_LOGITS, S_FCPROJ_DX, S_FCPROJ_DW, S_FC_DX, S_FC_DW,
+  S_ATTPROJ_DX, S_ATTPROJ_DW, S_QKV_DX, S_QKV_DW, S_CLS_DX, S_CLS_DW, S_ATTN_FWD, S_ATTN_BWD, S_XENT,
+  S_ADAMW, S_COUNT
+};
+
+struct SiteTimer {
+  bool on = false;
+  std::vector<hipEvent_t> ev;   // pairs
+  size_t used = 0;              // events used (2 per launch)
+  int64_t launches = 0;
+  double flops = 0, bytes = 0;  // per launch
+};
+
+}  // namespace
+
+struct gpt2_model {
+  gpt2_config cfg;
+  Layout lo;
+  hipStream_t stream;
+  char* base;
+  bool owns;
+  bool have_dlogits = false;
+  bool have_grads = false;
+  int device = 0;
+  SiteTimer timers[S_COUNT];
+
+  template <typename P> P* at(size_t off) { return reinterpret_cast<P*>(base + off); }
+  float* master() { return at<float>(lo.master); }
+  float* grad() { return at<float>(lo.grad); }
+  // parameter tensor i as read by the forward (bf16 copy or fp32 master)
+  void* param(int i) {
+    if (cfg.dtype == GPT2_BF16) return at<bf16>(lo.params_bf16) + lo.pt.off[i];
+    return master() + lo.pt.off[i];
+  }
+  // layer slice of a per-layer parameter tensor (storage type)
+  void* lparam(int i, int l) {
+    int64_t per = lo.pt.shape[i][1] * lo.pt.shape[i][2];
+    if (cfg.dtype == GPT2_BF16) return at<bf16>(lo.params_bf16) + lo.pt.off[i] + (int64_t)l * per;
+    return master() + lo.pt.off[i] + (int64_t)l * per;
+  }
+  float* lgrad(int i, int l) {
+    int64_t per = lo.pt.shape[i][1] * lo.pt.shape[i][2];
+    return grad() + lo.pt.off[i] + (int64_t)l * per;
+  }
+  int dt() const { return cfg.dtype; }
+  size_t es() const { return cfg.dtype == GPT2_BF16 ? 2 : 4; }
+  void* scratch() { return base + lo.scratch; }
+};
+
+namespace {
+
+int timer_begin(gpt2_model* m, int site) {
+  SiteTimer& t = m->timers[site];
+  if (!t.on || t.used + 2 > t.ev.size()) return 0;
+  GPT2_HIP_CHECK(hipEventRecord(t.ev[t.used], m->stream));
+  return 0;
+}
+
+int timer_end(gpt2_model* m, int site, double flops, double bytes) {
+  SiteTimer& t = m->timers[site];
+  if (!t.on || t.used + 2 > t.ev.size()) return 0;
+  GPT2_HIP_CHECK(hipEventRecord(t.ev[t.used + 1], m->stream));
+  t.used += 2;
+  t.launches++;
+  t.flops = flops;
+  t.bytes = bytes;
+  return 0;
+}
+
+// GEMM wrapper that records the timing site.
+int run_gemm(gpt2_model* m, int site, const GemmDesc& d) {
+  RC(timer_begin(m, site));
+  RC(gemm(d, m->stream));
+  const double es = (double)m->es();
+  double bytes = ((double)d.M * d.K + (double)d.N * d.K) * es +
+                 (d.epi == EPI_WGRAD ? (double)d.M * d.N * 4.0 : (double)d.M * d.N * es);
+  return timer_end(m, site, 2.0 * d.M * d.N * d.K, bytes);
+}
+
+GemmDesc gdesc(int dtype) {
+  GemmDesc d;
+  memset(&d, 0, sizeof(d));
+  d.dtype = dtype;
+  return d;
+}
+
+// y[M,N] = x[M,K] W[N,K]^T (+ epilogue)
+GemmDesc fwd_desc(gpt2_model* m, int M, int N, int K, const void* x, const void* W, int epi, void* C,
+                  const void* bias, const void* aux_in, void* aux_out) {
+  GemmDesc d = gdesc(m->dt());
+  d.a_kmajor = true; d.b_kmajor = true;
+  d.M = M; d.N = N; d.K = K;
+  d.A = x; d.lda = K; d.B = W; d.ldb = K;
+  d.epi = epi; d.C = C; d.ldc = N; d.bias = bias; d.aux_in = aux_in; d.ld_aux = N; d.aux_out = aux_out;
+  return d;
+}
+
+// dx[M,K] = dy[M,N] W[N,K]
+GemmDesc dx_desc(gpt2_model* m, int M, int N, int K, const void* dy, const void* W, void* dx, int epi,
+                 const void* gelu_u) {
+  GemmDesc d = gdesc(m->dt());
+  d.a_kmajor = true; d.b_kmajor = false;
+  d.M = M; d.N = K; d.K = N;
+  d.A = dy; d.lda = N; d.B = W; d.ldb = K;
+  d.epi = epi; d.C = dx; d.ldc = K; d.aux_in = gelu_u; d.ld_aux = K;
+  return d;
+}
+
+// dW[N,K] (+)= dy[M,N]^T x[M,K];  db[N] = sum_rows dy
+GemmDesc dw_desc(gpt2_model* m, int M, int N, int K, const void* dy, const void* x, float* dW, float* db,
+                 bool acc) {
+  GemmDesc d = gdesc(m->dt());
+  d.a_kmajor = false; d.b_kmajor = false;
+  d.M = N; d.N = K; d.K = M;
+  d.A = dy; d.lda = N; d.B = x; d.ldb = K;
+  d.epi = EPI_WGRAD; d.out32 = dW; d.bias_grad32 = db; d.accumulate = acc;
+  d.workspace = m->scratch(); d.workspace_bytes = m->lo.scratch_bytes;
+  return d;
+}
+
+int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets) {
+  const gpt2_config& c = m->cfg;
+  const int B = c.batch_size, T = c.seq_len, C = c.channels, H = c.num_heads, hd = C / H;
+  const int BT = B * T, Vp = c.padded_vocab_size, V = c.vocab_size;
+  const int dt = m->dt();
+  hipStream_t s = m->stream;
+  Layout& lo = m->lo;
+  m->have_dlogits = false;
+  m->have_grads = false;
+  // keep a copy of the ids for the encoder backward (the caller may reuse its buffer)
+  int32_t* tok = m->at<int32_t>(lo.tokens);
+  GPT2_HIP_CHECK(hipMemcpyAsync(tok, tokens, (size_t)BT * sizeof(int32_t), hipMemcpyDeviceToDevice, s));
+  RC(encoder_forward(dt, B, T, C, V, tok, m->param(0), m->param(1), m->at<char>(lo.resid[0]), s));
+  for (int l = 0; l < c.num_layers; ++l) {
+    LayerOffsets& o = lo.layer[l];
+    void* x = m->at<char>(lo.resid[l]);
+    RC(layernorm_forward(dt, BT, C, x, m->lparam(2, l), m->lparam(3, l), m->at<char>(o.ln1),
+                         m->at<float>(o.ln1_mean), m->at<float>(o.ln1_rstd), s));
+    RC(run_gemm(m, S_QKV, fwd_desc(m, BT, 3 * C, C, m->at<char>(o.ln1), m->lparam(4, l), EPI_BIAS,
+                                   m->at<char>(o.qkv), m->lparam(5, l), nullptr, nullptr)));
+    RC(timer_begin(m, S_ATTN_FWD));
+    RC(attention_forward(dt, B, T, H, hd, m->at<char>(o.qkv), m->at<char>(o.atty), m->at<float>(o.lse), s));
+    RC(timer_end(m, S_ATTN_FWD, 4.0 * B * H * hd * (double)T * (T + 1) / 2.0,
+                 (double)BT * 4 * C * m->es() + (double)B * H * T * 4));
+    RC(run_gemm(m, S_ATTPROJ, fwd_desc(m, BT, C, C, m->at<char>(o.atty), m->lparam(6, l), EPI_BIAS_RES,
+                                       m->at<char>(o.h), m->lparam(7, l), x, nullptr)));
+    RC(layernorm_forward(dt, BT, C, m->at<char>(o.h), m->lparam(8, l), m->lparam(9, l), m->at<char>(o.ln2),
+                         m->at<float>(o.ln2_mean), m->at<float>(o.ln2_rstd), s));
+    RC(run_gemm(m, S_FC, fwd_desc(m, BT, 4 * C, C, m->at<char>(o.ln2), m->lparam(10, l), EPI_BIAS_GELU,
+                                  m->at<char>(o.g), m->lparam(11, l), nullptr, m->at<char>(o.u))));
+    RC(run_gemm(m, S_FCPROJ, fwd_desc(m, BT, C, 4 * C, m->at<char>(o.g), m->lparam(12, l), EPI_BIAS_RES,
+                                      m->at<char>(lo.resid[l + 1]), m->lparam(13, l), m->at<char>(o.h),
+                                      nullptr)));
+  }
+  RC(layernorm_forward(dt, BT, C, m->at<char>(lo.resid[c.num_layers]), m->param(14), m->param(15),
+                       m->at<char>(lo.lnf), m->at<float>(lo.lnf_mean), m->at<float>(lo.lnf_rstd), s));
+  RC(run_gemm(m, S_LOGITS, fwd_desc(m, BT, Vp, C, m->at<char>(lo.lnf), m->param(0), EPI_STORE,
+                                    m->at<char>(lo.logits), nullptr, nullptr, nullptr)));
+  if (targets) {
+    RC(timer_begin(m, S_XENT));
+    RC(softmax_xent(dt, BT, V, Vp, m->at<char>(lo.logits), targets, m->at<float>(lo.losses), 1.0f / BT, s));
+    RC(timer_end(m, S_XENT, 0.0, 2.0 * BT * (double)Vp * m->es() + BT * 8.0));
+    RC(sum_scaled(BT, m->at<float>(lo.losses), 1.0f / BT, m->at<float>(lo.mean_loss), s));
+    m->have_dlogits = true;
+  }
+  return 0;
+}
+
+int backward_impl(gpt2_model* m) {
+  const gpt2_config& c = m->cfg;
+  const int B = c.batch_size, T = c.seq_len, C = c.channels, H = c.num_heads, hd = C / H;
+  const int BT = B * T, Vp = c.padded_vocab_size, V = c.vocab_size, L = c.num_layers;
+  const int dt = m->dt();
+  hipStream_t s = m->stream;
+  Layout& lo = m->lo;
+  void* d_ln = m->at<char>(lo.d_ln);
+  void* d_big = m->at<char>(lo.d_big);
+  void* d_qkv = m->at<char>(lo.d_qkv);
+  float* dres = m->at<float>(lo.dres);
+  void* dres_t = m->at<char>(lo.dres_t);
+  void* dres_copy = dt == GPT2_BF16 ? dres_t : nullptr;
+  void* logits = m->at<char>(lo.logits);
+  const size_t sb = lo.scratch_bytes;
+
+  // classifier: d_lnf = dz wte;  d_wte = dz^T lnf (overwrite; padded rows get exactly 0)
+  RC(run_gemm(m, S_CLS_DX, dx_desc(m, BT, Vp, C, logits, m->param(0), d_ln, EPI_STORE, nullptr)));
+  RC(run_gemm(m, S_CLS_DW, dw_desc(m, BT, Vp, C, logits, m->at<char>(lo.lnf), m->lgrad(0, 0), nullptr, false)));
+  RC(layernorm_backward(dt, BT, C, d_ln, m->at<char>(lo.resid[L]), m->param(14), m->at<float>(lo.lnf_mean),
+                        m->at<float>(lo.lnf_rstd), dres, true, dres_copy, m->lgrad(14, 0), m->lgrad(15, 0), false,
+                        m->scratch(), sb, s));
+  for (int l = L - 1; l >= 0; --l) {
+    LayerOffsets& o = lo.layer[l];
+    // x_{l+1} = h + g Wp^T + bp
+    RC(run_gemm(m, S_FCPROJ_DW, dw_desc(m, BT, C, 4 * C, dres_t, m->at<char>(o.g), m->lgrad(12, l),
+                                        m->lgrad(13, l), false)));
+    RC(run_gemm(m, S_FCPROJ_DX, dx_desc(m, BT, C, 4 * C, dres_t, m->lparam(12, l), d_big, EPI_GELU_BWD,
+                                        m->at<char>(o.u))));
+    // u = ln2 Wfc^T + bfc   (d_big now holds du)
+    RC(run_gemm(m, S_FC_DW, dw_desc(m, BT, 4 * C, C, d_big, m->at<char>(o.ln2), m->lgrad(10, l),
+                                    m->lgrad(11, l), false)));
+    RC(run_gemm(m, S_FC_DX, dx_desc(m, BT, 4 * C, C, d_big, m->lparam(10, l), d_ln, EPI_STORE, nullptr)));
+    RC(layernorm_backward(dt, BT, C, d_ln, m->at<char>(o.h), m->lparam(8, l), m->at<float>(o.ln2_mean),
+                          m->at<float>(o.ln2_rstd), dres, false, dres_copy, m->lgrad(8, l), m->lgrad(9, l), false,
+                          m->scratch(), sb, s));
+    // h = x + atty Wo^T + bo
+    RC(run_gemm(m, S_ATTPROJ_DW, dw_desc(m, BT, C, C, dres_t, m->at<char>(o.atty), m->lgrad(6, l),
+                                         m->lgrad(7, l), false)));
+    RC(run_gemm(m, S_ATTPROJ_DX, dx_desc(m, BT, C, C, dres_t, m->lparam(6, l), d_ln, EPI_STORE, nullptr)));
+    RC(timer_begin(m, S_ATTN_BWD));
+    RC(attention_backward(dt, B, T, H, hd, m->at<char>(o.qkv), m->at<char>(o.atty), d_ln, m->at<float>(o.lse),
+                          d_qkv, m->scratch(), sb, s));
+    RC(timer_end(m, S_ATTN_BWD, 2.5 * 4.0 * B * H * hd * (double)T * (T + 1) / 2.0,
+                 (double)BT * 8 * C * m->es()));
+    // qkv = ln1 Wqkv^T + bqkv
+    RC(run_gemm(m, S_QKV_DW, dw_desc(m, BT, 3 * C, C, d_qkv, m->at<char>(o.ln1), m->lgrad(4, l),
+                                     m->lgrad(5, l), false)));
+    RC(run_gemm(m, S_QKV_DX, dx_desc(m, BT, 3 * C, C, d_qkv, m->lparam(4, l), d_ln, EPI_STORE, nullptr)));
+    RC(layernorm_backward(dt, BT, C, d_ln, m->at<char>(lo.resid[l]), m->lparam(2, l), m->at<float>(o.ln1_mean),
+                          m->at<float>(o.ln1_rstd), dres, false, dres_copy, m->lgrad(2, l), m->lgrad(3, l), false,
+                          m->scratch(), sb, s));
+  }
+  // encoder: wpe rows >= T get no gradient
+  float* dwpe = m->lgrad(1, 0);
+  RC(fill_f32((int64_t)(c.max_seq_len - T) * C, dwpe + (size_t)T * C, 0.f, s));
+  RC(encoder_backward(B, T, C, V, m->at<int32_t>(lo.tokens), dres, m->lgrad(0, 0), dwpe, false, m->scratch(), sb,
+                      s));
+  (void)Vp;
+  return 0;
+}
+
+int init_params(gpt2_model* m, uint64_t seed) {
+  const gpt2_config& c = m->cfg;
+  hipStream_t s = m->stream;
+  const double resid_std = 0.02 / sqrt(2.0 * (c.num_layers > 0 ? c.num_layers : 1));
+  for (int i = 0; i < 16; ++i) {
+    const int64_t n = m->lo.pt.shape[i][0] * m->lo.pt.shape[i][1] * m->lo.pt.shape[i][2];
+    float* dst = m->master() + m->lo.pt.off[i];
+    const std::string name = kParamNames[i];
+    if (name == "ln1w" || name == "ln2w" || name == "lnfw") {
+      RC(fill_f32(n, dst, 1.0f, s));
+    } else if (name == "wte" || name == "wpe" || name == "qkvw" || name == "fcw" || name == "attprojw" ||
+               name == "fcprojw") {
+      const double sd = (name == "attprojw" || name == "fcprojw") ? resid_std : 0.02;
+      RC(init_normal(n, dst, seed, i, sd, s));
+      if (i == 0)
+        RC(fill_f32((int64_t)(c.padded_vocab_size - c.vocab_size) * c.channels,
+                    dst + (size_t)c.vocab_size * c.channels, 0.f, s));
+    } else {
+      RC(fill_f32(n, dst, 0.f, s));
+    }
+  }
+  return 0;
+}
+
+int refresh_bf16(gpt2_model* m) {
+  if (m->cfg.dtype != GPT2_BF16) return 0;
+  return cast_f32_to_bf16(m->lo.P, m->master(), m->at<bf16>(m->lo.params_bf16), m->stream);
+}
+
+}  // namespace
+
+// ================================================================ C ABI
+
+extern "C" {
+
+const char* gpt2_status_string(int st) {
+  switch (st) {
+    case GPT2_OK: return "ok";
+    case GPT2_E_INVALID_ARG: return "invalid argument";
+    case GPT2_E_STATE: return "invalid call order";
+    case GPT2_E_OOM: return "out of device memory / workspace too small";
+    case GPT2_E_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* gpt2_last_error(void) { return g_last_error; }
+
+int gpt2_validate_config(const gpt2_config* cfg) {
+  g_last_error[0] = 0;
+  return validate(cfg);
+}
+
+int64_t gpt2_num_parameters(const gpt2_config* cfg, int padded) {
+  if (validate(cfg)) return -1;
+  ParamTable t;
+  param_table(*cfg, padded != 0, &t);
+  return t.total;
+}
+
+int gpt2_num_param_tensors(void) { return 16; }
+
+int gpt2_param_info(const gpt2_config* cfg, int i, const char** name, int64_t* offset, int64_t shape[3],
+                    int32_t* ndim) {
+  RC(validate(cfg));
+  if (i < 0 || i >= 16) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "tensor index %d out of range", i);
+  ParamTable t;
+  param_table(*cfg, true, &t);
+  if (name) *name = kParamNames[i];
+  if (offset) *offset = t.off[i];
+  if (shape)
+    for (int d = 0; d < 3; ++d) shape[d] = t.shape[i][d];
+  if (ndim) *ndim = t.ndim[i];
+  return GPT2_OK;
+}
+
+size_t gpt2_workspace_bytes(const gpt2_config* cfg) {
+  if (validate(cfg)) return 0;
+  Layout lo;
+  make_layout(*cfg, &lo);
+  return lo.total;
+}
+
+int gpt2_create(const gpt2_config* cfg, uint64_t seed, void* stream, void* workspace, size_t workspace_bytes,
+                gpt2_model** out) {
+  g_last_error[0] = 0;
+  if (!out) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  RC(validate(cfg));
+  gpt2_model* m = new (std::nothrow) gpt2_model();
+  if (!m) return gpt2_internal_fail(GPT2_E_OOM, "host allocation failed");
+  m->cfg = *cfg;
+  make_layout(*cfg, &m->lo);
+  m->stream = (hipStream_t)stream;
+  if (hipGetDevice(&m->device) != hipSuccess) {
+    delete m;
+    return gpt2_internal_fail(GPT2_E_HIP, "hipGetDevice failed");
+  }
+  if (workspace) {
+    if (workspace_bytes < m->lo.total || (uintptr_t)workspace % 256) {
+      size_t need = m->lo.total;
+      delete m;
+      return gpt2_internal_fail(GPT2_E_OOM, "workspace of %zu bytes (need %zu, 256-byte aligned)", workspace_bytes,
+                                need);
+    }
+    m->base = (char*)workspace;
+    m->owns = false;
+  } else {
+    void* p = nullptr;
+    if (hipMalloc(&p, m->lo.total) != hipSuccess) {
+      (void)hipGetLastError();
+      size_t need = m->lo.total;
+      delete m;
+      return gpt2_internal_fail(GPT2_E_OOM, "hipMalloc(%zu) failed", need);
+    }
+    m->base = (char*)p;
+    m->owns = true;
+  }
+  int rc = init_params(m, seed);
+  if (!rc) rc = fill_f32(m->lo.P, m->at<float>(m->lo.adam_m), 0.f, m->stream);
+  if (!rc) rc = fill_f32(m->lo.P, m->at<float>(m->lo.adam_v), 0.f, m->stream);
+  if (!rc) rc = fill_f32(m->lo.P, m->grad(), 0.f, m->stream);
+  if (!rc) rc = refresh_bf16(m);
+  if (!rc && hipStreamSynchronize(m->stream) != hipSuccess) rc = gpt2_internal_fail(GPT2_E_HIP, "sync failed");
+  if (rc) {
+    if (m->owns) (void)hipFree(m->base);
+    delete m;
+    return rc;
+  }
+  *out = m;
+  return GPT2_OK;
+}
+
+void gpt2_destroy(gpt2_model* m) {
+  if (!m) return;
+  (void)hipStreamSynchronize(m->stream);
+  for (auto& t : m->timers)
+    for (auto e : t.ev) (void)hipEventDestroy(e);
+  if (m->owns) (void)hipFree(m->base);
+  delete m;
+}
+
+int gpt2_forward(gpt2_model* m, const int32_t* d_tokens, const int32_t* d_targets, float* mean_loss) {
+  if (!m || !d_tokens) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "forward: NULL model or tokens");
+  if (d_targets && !mean_loss) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "forward: mean_loss is NULL");
+  RC(forward_impl(m, d_tokens, d_targets));
+  if (d_targets) {
+    GPT2_HIP_CHECK(hipMemcpyAsync(mean_loss, m->at<float>(m->lo.mean_loss), sizeof(float), hipMemcpyDeviceToHost,
+                                  m->stream));
+    GPT2_HIP_CHECK(hipStreamSynchronize(m->stream));
+  }
+  return GPT2_OK;
+}
+
+int gpt2_backward(gpt2_model* m) {
+  if (!m) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "backward: NULL model");
+  if (!m->have_dlogits) return gpt2_internal_fail(GPT2_E_STATE, "backward needs a forward with targets first");
+  RC(backward_impl(m));
+  m->have_dlogits = false;
+  m->have_grads = true;
+  return GPT2_OK;
+}
+
+int gpt2_adamw_step(gpt2_model* m, float lr, float beta1, float beta2, float eps, float weight_decay, int32_t t) {
+  if (!m) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "adamw: NULL model");
+  if (t < 1) return gpt2_internal_fail(GPT2_E_STATE, "adamw: t must be >= 1");
+  if (!m->have_grads) return gpt2_internal_fail(GPT2_E_STATE, "adamw needs a completed backward first");
+  RC(timer_begin(m, S_ADAMW));
+  RC(adamw(m->lo.P, m->master(), m->grad(), m->at<float>(m->lo.adam_m), m->at<float>(m->lo.adam_v),
+           m->cfg.dtype == GPT2_BF16 ? m->at<bf16>(m->lo.params_bf16) : nullptr, lr, beta1, beta2, eps, weight_decay,
+           t, m->stream));
+  RC(timer_end(m, S_ADAMW, 0.0, (double)m->lo.P * (m->cfg.dtype == GPT2_BF16 ? 30.0 : 28.0)));
+  m->have_grads = false;
+  return GPT2_OK;
+}
+
+static int copy_out(gpt2_model* m, const void* src, void* dst, size_t bytes) {
+  GPT2_HIP_CHECK(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, m->stream));
+  GPT2_HIP_CHECK(hipStreamSynchronize(m->stream));
+  return GPT2_OK;
+}
+
+int gpt2_get_params(gpt2_model* m, float* host_out) {
+  if (!m || !host_out) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "get_params: NULL");
+  return copy_out(m, m->master(), host_out, m->lo.P * sizeof(float));
+}
+
+int gpt2_set_params(gpt2_model* m, const float* host_in) {
+  if (!m || !host_in) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "set_params: NULL");
+  GPT2_HIP_CHECK(hipMemcpyAsync(m->master(), host_in, m->lo.P * sizeof(float), hipMemcpyHostToDevice, m->stream));
+  RC(fill_f32(m->lo.P, m->at<float>(m->lo.adam_m), 0.f, m->stream));
+  RC(fill_f32(m->lo.P, m->at<float>(m->lo.adam_v), 0.f, m->stream));
+  RC(refresh_bf16(m));
+  GPT2_HIP_CHECK(hipStreamSynchronize(m->stream));
+  m->have_dlogits = m->have_grads = false;
+  return GPT2_OK;
+}
+
+int gpt2_get_grads(gpt2_model* m, float* host_out) {
+  if (!m || !host_out) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "get_grads: NULL");
+  return copy_out(m, m->grad(), host_out, m->lo.P * sizeof(float));
+}
+
+int gpt2_get_adam_state(gpt2_model* m, float* host_m, float* host_v) {
+  if (!m) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "get_adam_state: NULL");
+  if (host_m) RC(copy_out(m, m->at<float>(m->lo.adam_m), host_m, m->lo.P * sizeof(float)));
+  if (host_v) RC(copy_out(m, m->at<float>(m->lo.adam_v), host_v, m->lo.P * sizeof(float)));
+  return GPT2_OK;
+}
+
+int gpt2_get_token_losses(gpt2_model* m, float* host_out) {
+  if (!m || !host_out) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "get_token_losses: NULL");
+  return copy_out(m, m->at<float>(m->lo.losses), host_out,
+                  (size_t)m->cfg.batch_size * m->cfg.seq_len * sizeof(float));
+}
+
+int gpt2_get_logits(gpt2_model* m, float* host_out) {
+  if (!m || !host_out) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "get_logits: NULL");
+  const int64_t n = (int64_t)m->cfg.batch_size * m->cfg.seq_len * m->cfg.padded_vocab_size;
+  if (m->cfg.dtype == GPT2_FP32) return copy_out(m, m->at<float>(m->lo.logits), host_out, n * sizeof(float));
+  // convert through the d_big scratch region chunk by chunk
+  float* tmp = m->at<float>(m->lo.scratch);
+  const int64_t chunk = (int64_t)(m->lo.scratch_bytes / sizeof(float)) / 4096 * 4096;
+  if (chunk <= 0) return gpt2_internal_fail(GPT2_E_OOM, "get_logits: scratch too small");
+  for (int64_t i = 0; i < n; i += chunk) {
+    const int64_t k = std::min(chunk, n - i);
+    RC(convert_to_f32(GPT2_BF16, k, m->at<bf16>(m->lo.logits) + i, tmp, m->stream));
+    RC(copy_out(m, tmp, host_out + i, k * sizeof(float)));
+  }
+  return GPT2_OK;
+}
+
+int gpt2_timing_enable(gpt2_model* m, int site, int enable) {
+  if (!m || site < 0 || site >= S_COUNT) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "timing_enable: bad site");
+  SiteTimer& t = m->timers[site];
+  if (enable && t.ev.empty()) {
+    t.ev.resize(2 * 4096);
+    for (auto& e : t.ev) GPT2_HIP_CHECK(hipEventCreate(&e));
+  }
+  t.on = enable != 0;
+  t.used = 0;
+  t.launches = 0;
+  return GPT2_OK;
+}
+
+int gpt2_timing_read(gpt2_model* m, int site, double* total_ms, int64_t* launches, double* flops_per_launch,
+                     double* bytes_per_launch) {
+  if (!m || site < 0 || site >= S_COUNT) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "timing_read: bad site");
+  SiteTimer& t = m->timers[site];
+  GPT2_HIP_CHECK(hipStreamSynchronize(m->stream));
+  double tot = 0;
+  for (size_t i = 0; i + 1 < t.used; i += 2) {
+    float ms = 0;
+    GPT2_HIP_CHECK(hipEventElapsedTime(&ms, t.ev[i], t.ev[i + 1]));
+    tot += ms;
+  }
+  if (total_ms) *total_ms = tot;
+  if (launches) *launches = t.launches;
+  if (flops_per_launch) *flops_per_launch = t.flops;
+  if (bytes_per_launch) *bytes_per_launch = t.bytes;
+  t.used = 0;
+  t.launches = 0;
+  return GPT2_OK;
+}
+
+// ================================================================ op-level ABI
+
+int gpt2_op_linear_forward(int dtype, int M, int N, int K, const void* x, const void* W, const void* b,
+                           const void* residual, void* y, void* gelu_out, void* stream) {
+  if (residual && gelu_out) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "residual and gelu_out are exclusive");
+  GemmDesc d;
+  memset(&d, 0, sizeof(d));
+  d.dtype = dtype;
+  d.a_kmajor = d.b_kmajor = true;
+  d.M = M; d.N = N; d.K = K;
+  d.A = x; d.lda = K; d.B = W; d.ldb = K;
+  d.ldc = N; d.ld_aux = N; d.bias = b;
+  if (gelu_out) {
+    if (!b) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "gelu epilogue needs a bias");
+    d.epi = EPI_BIAS_GELU; d.C = gelu_out; d.aux_out = y;
+  } else if (residual) {
+    if (!b) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "residual epilogue needs a bias");
+    d.epi = EPI_BIAS_RES; d.C = y; d.aux_in = residual;
+  } else {
+    d.epi = b ? EPI_BIAS : EPI_STORE; d.C = y;
+  }
+  return gemm(d, (hipStream_t)stream);
+}
+
+size_t gpt2_op_linear_backward_workspace_bytes(int dtype, int M, int N, int K) {
+  return gemm_workspace_bytes(dtype, EPI_WGRAD, N, K, M);
+}
+
+int gpt2_op_linear_backward(int dtype, int M, int N, int K, const void* dy, const void* x, const void* W,
+                            const void* gelu_u, void* dx, float* dW, float* db, int accumulate, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (dW) {
+    GemmDesc d;
+    memset(&d, 0, sizeof(d));
+    d.dtype = dtype; d.a_kmajor = false; d.b_kmajor = false;
+    d.M = N; d.N = K; d.K = M;
+    d.A = dy; d.lda = N; d.B = x; d.ldb = K;
+    d.epi = EPI_WGRAD; d.out32 = dW; d.bias_grad32 = db; d.accumulate = accumulate != 0;
+    d.workspace = workspace; d.workspace_bytes = workspace_bytes;
+    RC(gemm(d, s));
+  } else if (db) {
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "db is computed in the dW pass; pass dW too");
+  }
+  if (dx) {
+    GemmDesc d;
+    memset(&d, 0, sizeof(d));
+    d.dtype = dtype; d.a_kmajor = true; d.b_kmajor = false;
+    d.M = M; d.N = K; d.K = N;
+    d.A = dy; d.lda = N; d.B = W; d.ldb = K;
+    d.epi = gelu_u ? EPI_GELU_BWD : EPI_STORE; d.C = dx; d.ldc = K; d.aux_in = gelu_u; d.ld_aux = K;
+    RC(gemm(d, s));
+  }
+  return GPT2_OK;
+}
+
+int gpt2_op_layernorm_forward(int dtype, int N, int C, const void* x, const void* w, const void* b, void* y,
+                              float* mean, float* rstd, void* stream) {
+  return layernorm_forward(dtype, N, C, x, w, b, y, mean, rstd, (hipStream_t)stream);
+}
+
+size_t gpt2_op_layernorm_backward_workspace_bytes(int N, int C) { return layernorm_backward_workspace_bytes(N, C); }
+
+int gpt2_op_layernorm_backward(int dtype, int N, int C, const void* dy, const void* x, const void* w,
+                               const float* mean, const float* rstd, float* dres, int dres_overwrite,
+                               void* dres_copy, float* dw, float* db, int accumulate, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return layernorm_backward(dtype, N, C, dy, x, w, mean, rstd, dres, dres_overwrite != 0, dres_copy, dw, db,
+                            accumulate != 0, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+int gpt2_op_attention_forward(int dtype, int B, int T, int H, int hd, const void* qkv, void* out, float* lse,
+                              void* stream) {
+  return attention_forward(dtype, B, T, H, hd, qkv, out, lse, (hipStream_t)stream);
+}
+
+size_t gpt2_op_attention_backward_workspace_bytes(int B, int T, int H, int hd) {
+  return attention_backward_workspace_bytes(B, T, H, hd);
+}
+
+int gpt2_op_attention_backward(int dtype, int B, int T, int H, int hd, const void* qkv, const void* out,
+                               const void* dout, const float* lse, void* dqkv, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return attention_backward(dtype, B, T, H, hd, qkv, out, dout, lse, dqkv, workspace, workspace_bytes,
+                            (hipStream_t)stream);
+}
+
+int gpt2_op_softmax_xent(int dtype, int N, int V, int Vp, void* logits, const int32_t* labels, float* losses,
+                         float dscale, void* stream) {
+  return softmax_xent(dtype, N, V, Vp, logits, labels, losses, dscale, (hipStream_t)stream);
+}
+
+size_t gpt2_op_classifier_workspace_bytes(int dtype, int N, int C, int Vp) {
+  return gemm_workspace_bytes(dtype, EPI_WGRAD, Vp, C, N);
+}
+
+int gpt2_op_classifier_fwd_bwd(int dtype, int N, int C, int V, int Vp, const void* hidden, const void* wte,
+                               const int32_t* labels, float* losses, void* logits, void* d_hidden, float* d_wte,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (N <= 0 || C <= 0 || V <= 0 || Vp < V || !hidden || !wte || !labels || !losses || !logits || !d_hidden || !d_wte)
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "classifier: bad arguments");
+  hipStream_t s = (hipStream_t)stream;
+  RC(gpt2_op_linear_forward(dtype, N, Vp, C, hidden, wte, nullptr, nullptr, logits, nullptr, stream));
+  RC(softmax_xent(dtype, N, V, Vp, logits, labels, losses, 1.0f / N, s));
+  // d_hidden = dlogits wte  (a linear backward with W = wte [Vp, C])
+  return gpt2_op_linear_backward(dtype, N, Vp, C, logits, hidden, wte, nullptr, d_hidden, d_wte, nullptr, 0,
+                                 workspace, workspace_bytes, stream);
+}
+
+int gpt2_op_encoder_forward(int dtype, int B, int T, int C, int V, const int32_t* tokens, const void* wte,
+                            const void* wpe, void* out, void* stream) {
+  return encoder_forward(dtype, B, T, C, V, tokens, wte, wpe, out, (hipStream_t)stream);
+}
+
+size_t gpt2_op_encoder_backward_workspace_bytes(int B, int T, int C) {
+  return encoder_backward_workspace_bytes(B, T, C);
+}
+
+int gpt2_op_encoder_backward(int B, int T, int C, int V, const int32_t* tokens, const float* dx0, float* dwte,
+                             float* dwpe, int accumulate_wpe, void* workspace, size_t workspace_bytes, void* stream) {
+  return encoder_backward(B, T, C, V, tokens, dx0, dwte, dwpe, accumulate_wpe != 0, workspace, workspace_bytes,
+                          (hipStream_t)stream);
+}
+
+int gpt2_op_adamw(int64_t n, float* master, const float* grad, float* m, float* v, void* param_bf16, float lr,
+                  float beta1, float beta2, float eps, float weight_decay, int32_t t, void* stream) {
+  return adamw(n, master, grad, m, v, (bf16*)param_bf16, lr, beta1, beta2, eps, weight_decay, t,
+               (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,184 @@
+/*
+ * gpt2.h -- C ABI of the GPT-2 training-step library for MI355X (gfx950).
+ *
+ * One training step is: token + position encoder, L pre-LayerNorm blocks
+ * (causal multi-head attention, GELU-tanh MLP, residual adds), final
+ * LayerNorm, a classifier tied to the token table with softmax
+ * cross-entropy, the full backward pass, and AdamW.  The page
+ * "State of the Union [May 3, 2024]" (karpathy/llm.c discussion #344)
+ * describes this step: its opening bullet list names bf16 mixed precision
+ * with an fp32 master copy of the parameters, a fused classifier that never
+ * materialises normalised logits and evaluates the loss only at the label's
+ * index, and flash attention; its kernel table (section "Runtime, DRAM
+ * traffic, instructions") lists the kernels of the step; its "Fine print"
+ * section pads the vocabulary 50257 -> 50304 (a multiple of 64) and requires
+ * the padded logits to be masked to -inf.
+ *
+ * Conventions
+ *   - Every function is extern "C"; no C++ type or exception crosses it.
+ *   - Pointers named d_* are device pointers (HIP global memory of the
+ *     current device); pointers named host_* are host memory.
+ *   - Every function returns a status: GPT2_OK (0) or one of GPT2_E_*.
+ *     gpt2_last_error() returns a thread-local text for the last failure.
+ *   - "stream" arguments are hipStream_t values passed as void*; NULL means
+ *     the null stream.  Work is enqueued on that stream; only the calls that
+ *     say so synchronise.
+ *
+ * Parameter layout (one flat array, this order, weights stored [out, in]
+ * row-major so that y = x W^T + b; QKV output columns ordered [q | k | v],
+ * head h owning columns h*hd .. h*hd + hd - 1 inside each):
+ *   wte[Vp,C] wpe[maxT,C] ln1w[L,C] ln1b[L,C] qkvw[L,3C,C] qkvb[L,3C]
+ *   attprojw[L,C,C] attprojb[L,C] ln2w[L,C] ln2b[L,C] fcw[L,4C,C] fcb[L,4C]
+ *   fcprojw[L,C,4C] fcprojb[L,C] lnfw[C] lnfb[C]
+ * Rows V..Vp-1 of wte are padding: initialised to zero, their logits are
+ * masked to -inf, so their gradient is exactly zero and AdamW keeps them 0.
+ */
+#ifndef GPT2_H
+#define GPT2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  GPT2_OK = 0,
+  GPT2_E_INVALID_ARG = 1, /* null pointer, bad config, unsupported shape */
+  GPT2_E_STATE = 2,       /* calls out of order (e.g. backward before forward with targets) */
+  GPT2_E_OOM = 3,         /* device allocation failed or workspace too small */
+  GPT2_E_HIP = 4          /* a HIP runtime call failed; text in gpt2_last_error() */
+};
+
+enum {
+  GPT2_FP32 = 0, /* every tensor fp32 (parity mode) */
+  GPT2_BF16 = 1  /* bf16 weights copy, activations and activation gradients;
+                    fp32 master weights, parameter gradients, AdamW moments,
+                    LayerNorm statistics, softmax statistics, residual-stream
+                    gradient and every accumulator */
+};
+
+typedef struct gpt2_config {
+  int32_t vocab_size;        /* V, e.g. 50257                                  */
+  int32_t padded_vocab_size; /* Vp >= V, multiple of 64, e.g. 50304            */
+  int32_t max_seq_len;       /* maxT, rows of wpe                              */
+  int32_t num_layers;        /* L >= 0                                         */
+  int32_t num_heads;         /* H, C % H == 0                                  */
+  int32_t channels;          /* C, multiple of 64                              */
+  int32_t batch_size;        /* B: activation buffers are sized for B x T      */
+  int32_t seq_len;           /* T <= maxT; B*T multiple of 64, B*T <= 32768    */
+  int32_t dtype;             /* GPT2_FP32 or GPT2_BF16                         */
+} gpt2_config;
+
+typedef struct gpt2_model gpt2_model; /* opaque */
+
+/* ---- host-only queries (no HIP call; usable without a GPU) -------------- */
+
+/* Checks every field; returns GPT2_OK or GPT2_E_INVALID_ARG with a reason in
+ * gpt2_last_error().  Head dimension C/H must be 16, 32, 64 or 128 and a
+ * multiple of 16. */
+int gpt2_validate_config(const gpt2_config* cfg);
+
+/* Number of parameters; padded != 0 counts the Vp-row token table,
+ * padded == 0 the V-row one.  Returns -1 for an invalid config. */
+int64_t gpt2_num_parameters(const gpt2_config* cfg, int padded);
+
+/* Number of parameter tensors (16). */
+int gpt2_num_param_tensors(void);
+
+/* Tensor i of the flat layout: *name (static string), *offset (elements from
+ * the start of the flat array), shape[0..2] (unused trailing dims are 1) and
+ * *ndim.  Returns GPT2_E_INVALID_ARG for i out of range or a bad config. */
+int gpt2_param_info(const gpt2_config* cfg, int i, const char** name, int64_t* offset,
+                    int64_t shape[3], int32_t* ndim);
+
+/* Device bytes gpt2_create needs for all model state (parameters, master,
+ * gradients, AdamW moments, activations, scratch).  0 for a bad config. */
+size_t gpt2_workspace_bytes(const gpt2_config* cfg);
+
+/* Status code -> static text. */
+const char* gpt2_status_string(int status);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char* gpt2_last_error(void);
+
+/* ---- model lifecycle and the training step ------------------------------ */
+
+/* Creates a model on the current HIP device and initialises the parameters
+ * from seed (GPT-2 scheme: N(0, 0.02); the two residual projections
+ * N(0, 0.02/sqrt(2L)); biases 0; LayerNorm gains 1; padded wte rows 0),
+ * drawn with the counter-based SplitMix64 + Box-Muller generator
+ * (element e of tensor i uses stream outputs 2c and 2c+1, c = (i << 40) | e).
+ * workspace: NULL -> the library allocates gpt2_workspace_bytes(cfg) bytes
+ * and frees them in gpt2_destroy; otherwise a caller-owned device buffer of
+ * at least that many bytes, 256-byte aligned, that outlives the model.
+ * stream: the stream every later call of this model enqueues on.
+ * Synchronises the stream before returning. */
+int gpt2_create(const gpt2_config* cfg, uint64_t seed, void* stream, void* workspace,
+                size_t workspace_bytes, gpt2_model** out);
+
+/* Forward pass over d_tokens [B, T] int32 (ids in [0, V)).  With d_targets
+ * (int32 [B, T], ids in [0, V)) it also evaluates softmax cross-entropy,
+ * writes the per-position losses, stores dlogits in place of the logits
+ * (ready for gpt2_backward) and writes the mean loss to *mean_loss (host),
+ * synchronising the stream.  With d_targets == NULL it stops at the logits
+ * and does not touch *mean_loss or synchronise.  Token ids outside [0, V)
+ * are undefined behaviour. */
+int gpt2_forward(gpt2_model* m, const int32_t* d_tokens, const int32_t* d_targets,
+                 float* mean_loss);
+
+/* Backward pass of the mean loss of the last forward-with-targets.  Parameter
+ * gradients (fp32) are overwritten.  GPT2_E_STATE if the last forward had no
+ * targets. */
+int gpt2_backward(gpt2_model* m);
+
+/* One AdamW update of every parameter (fp32 master), then refreshes the bf16
+ * copy used by the forward:  m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
+ * theta -= lr (m/(1-b1^t) / (sqrt(v/(1-b2^t)) + eps) + wd theta).
+ * Requires t >= 1 and a completed backward (GPT2_E_STATE otherwise). */
+int gpt2_adamw_step(gpt2_model* m, float lr, float beta1, float beta2, float eps,
+                    float weight_decay, int32_t t);
+
+/* Releases the model (and the workspace if the library allocated it).
+ * Synchronises the model's stream first.  NULL is a no-op. */
+void gpt2_destroy(gpt2_model* m);
+
+/* ---- state access (synchronous copies through host memory) -------------- */
+
+/* fp32 master parameters in the flat layout, num_parameters(cfg, 1) floats. */
+int gpt2_get_params(gpt2_model* m, float* host_out);
+/* Sets the fp32 master parameters (flat layout), refreshes the bf16 copy and
+ * clears the AdamW moments. */
+int gpt2_set_params(gpt2_model* m, const float* host_in);
+/* fp32 parameter gradients of the last backward, flat layout. */
+int gpt2_get_grads(gpt2_model* m, float* host_out);
+/* AdamW first and second moments, flat layout (either pointer may be NULL). */
+int gpt2_get_adam_state(gpt2_model* m, float* host_m, float* host_v);
+/* Per-position losses [B*T] of the last forward with targets. */
+int gpt2_get_token_losses(gpt2_model* m, float* host_out);
+/* Logits [B*T, Vp] of the last forward WITHOUT targets, converted to fp32
+ * (after a forward with targets the buffer holds dlogits instead; this call
+ * returns whichever is there). */
+int gpt2_get_logits(gpt2_model* m, float* host_out);
+
+/* ---- timing hooks ------------------------------------------------------- */
+
+/* Enables (1) or disables (0) HIP-event timing of the launches of one GEMM
+ * site inside the step.  site: 0 QKV fwd, 1 attn-proj fwd, 2 fc fwd,
+ * 3 fc-proj fwd, 4 logits fwd, 5 fc-proj dX, 6 fc-proj dW, 7 fc dX, 8 fc dW,
+ * 9 attn-proj dX, 10 attn-proj dW, 11 QKV dX, 12 QKV dW, 13 classifier dX,
+ * 14 classifier dW, 15 attention fwd, 16 attention bwd, 17 softmax-CE,
+ * 18 AdamW.  Events are recorded on the model's stream around every launch
+ * of that site. */
+int gpt2_timing_enable(gpt2_model* m, int site, int enable);
+/* Total elapsed milliseconds and launch count recorded for a site since it
+ * was enabled (synchronises the stream). */
+int gpt2_timing_read(gpt2_model* m, int site, double* total_ms, int64_t* launches,
+                     double* flops_per_launch, double* bytes_per_launch);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPT2_H */

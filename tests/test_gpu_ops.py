@@ -1,0 +1,359 @@
+"""Op-level parity of the HIP kernels against the CPU oracle, through the
+C ABI (include/gpt2_ops.h).  Same seeded inputs on both sides; bf16 inputs
+are the bf16-rounded values on both sides.
+
+Tolerances (relative L2, oracle as reference), from the arithmetic:
+  * fp32 storage, fp32 arithmetic: 1e-5 (reassociation only);
+  * bf16 outputs: each element is rounded to nearest bf16 (relative error
+    <= 2^-9 = 1.95e-3), so 3e-3, and 6e-3 where a bf16-rounded intermediate
+    feeds a second product (attention);
+  * fp32 outputs of bf16 inputs (weight / bias gradients): products are exact
+    in fp32, only the fp32 summation order differs: 1e-5.
+Integer and layout results (encoder gather, padded columns) are bit-exact.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+from gpt_transformer_lm_amd import lib
+from gpt_transformer_lm_amd import synthetic as S
+from gpu_util import BF16, FP32, as_input, dev, dev_i32, empty, empty32, host, rel, say
+
+pytestmark = pytest.mark.gpu
+
+TOL_OUT = {FP32: 1e-5, BF16: 3e-3}
+TOL_F32 = 1e-5
+DT = [FP32, BF16]
+DTN = {FP32: "fp32", BF16: "bf16"}
+
+
+def rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+# ---------------------------------------------------------------- GEMM / linear
+
+SHAPES = [(256, 192, 64), (200, 136, 128), (64, 64, 64), (320, 200, 192)]
+
+
+@pytest.mark.parametrize("dtype", DT, ids=DTN.get)
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("epi", ["store", "bias", "bias_res", "bias_gelu"])
+def test_linear_forward(dtype, M, N, K, epi):
+    say("linear_forward", DTN[dtype], M, N, K, epi)
+    r = rng(M * 7 + N + K)
+    x, W = r.standard_normal((M, K)), r.standard_normal((N, K)) * 0.1
+    b, res = r.standard_normal(N) * 0.5, r.standard_normal((M, N))
+    xi, Wi, bi, ri = (as_input(a, dtype).astype(np.float64) for a in (x, W, b, res))
+    y = empty((M, N), dtype)
+    g = empty((M, N), dtype) if epi == "bias_gelu" else None
+    lib.linear_forward(dtype, dev(x, dtype), dev(W, dtype), b=None if epi == "store" else dev(b, dtype),
+                       residual=dev(res, dtype) if epi == "bias_res" else None, gelu_out=g, y=y)
+    ref = O.linear_forward(xi, Wi, None if epi == "store" else bi)
+    if epi == "bias_res":
+        ref = ref + ri
+    assert rel(host(y), ref) < TOL_OUT[dtype]
+    if g is not None:
+        assert rel(host(g), O.gelu_tanh(ref)) < TOL_OUT[dtype]
+
+
+@pytest.mark.parametrize("dtype", DT, ids=DTN.get)
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("gelu", [False, True])
+def test_linear_backward(dtype, M, N, K, gelu):
+    say("linear_backward", DTN[dtype], M, N, K, "gelu" if gelu else "")
+    r = rng(M + 3 * N + 5 * K + gelu)
+    dy, x, W, u = r.standard_normal((M, N)), r.standard_normal((M, K)), r.standard_normal((N, K)) * 0.1, \
+        r.standard_normal((M, K))
+    dyi, xi, Wi, ui = (as_input(a, dtype).astype(np.float64) for a in (dy, x, W, u))
+    dx = empty((M, K), dtype)
+    dW = empty32((N, K))
+    db = empty32((N,))
+    lib.linear_backward(dtype, dev(dy, dtype), dev(x, dtype), dev(W, dtype), dx=dx, dW=dW, db=db,
+                        gelu_u=dev(u, dtype) if gelu else None)
+    rdx, rdW, rdb = O.linear_backward(dyi, xi, Wi)
+    if gelu:
+        rdx = O.gelu_tanh_backward(ui, rdx)
+    assert rel(host(dx), rdx) < TOL_OUT[dtype]
+    assert rel(host(dW), rdW) < TOL_F32
+    assert rel(host(db), rdb) < TOL_F32
+
+
+@pytest.mark.parametrize("dtype", DT, ids=DTN.get)
+def test_linear_backward_accumulates(dtype):
+    say("linear_backward accumulate", DTN[dtype])
+    r = rng(5)
+    M, N, K = 128, 64, 192
+    dy, x, W = r.standard_normal((M, N)), r.standard_normal((M, K)), r.standard_normal((N, K))
+    base_w, base_b = r.standard_normal((N, K)), r.standard_normal(N)
+    dW, db = dev(base_w, FP32), dev(base_b, FP32)
+    lib.linear_backward(dtype, dev(dy, dtype), dev(x, dtype), dev(W, dtype), dW=dW, db=db, accumulate=True)
+    _, rdW, rdb = O.linear_backward(as_input(dy, dtype).astype(np.float64), as_input(x, dtype).astype(np.float64),
+                                    W)
+    assert rel(host(dW), base_w.astype(np.float32) + rdW) < TOL_F32
+    assert rel(host(db), base_b.astype(np.float32) + rdb) < TOL_F32
+
+
+# The GEMMs of the GPT-2 124M step (B*T = 24576, C = 768, Vp = 50304) at full
+# size, in the launch configuration the step uses; 512 sampled outputs each are
+# recomputed as float64 dot products.
+FULL = [("qkv", 24576, 2304, 768), ("attproj", 24576, 768, 768), ("fc", 24576, 3072, 768),
+        ("fcproj", 24576, 768, 3072), ("logits", 24576, 50304, 768)]
+
+
+@pytest.mark.parametrize("name,M,N,K", FULL)
+def test_linear_full_size_sampled(name, M, N, K):
+    say("full-size linear", name, M, N, K)
+    torch = __import__("torch")
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    x = torch.randn((M, K), generator=gen, device="cuda").to(torch.bfloat16)
+    W = (torch.randn((N, K), generator=gen, device="cuda") * 0.05).to(torch.bfloat16)
+    dy = (torch.randn((M, N), generator=gen, device="cuda") * 0.1).to(torch.bfloat16)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    lib.linear_forward(BF16, x, W, y=y)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    dW = torch.empty((N, K), dtype=torch.float32, device="cuda")
+    db = torch.empty((N,), dtype=torch.float32, device="cuda")
+    lib.linear_backward(BF16, dy, x, W, dx=dx, dW=dW, db=db)
+    torch.cuda.synchronize()
+    r = rng(M + N)
+    im, in_, ik = r.integers(0, M, 512), r.integers(0, N, 512), r.integers(0, K, 512)
+    xs = x.float().cpu().numpy().astype(np.float64)
+    Ws = W.float().cpu().numpy().astype(np.float64)
+    dys = dy.float().cpu().numpy().astype(np.float64)
+    ref_y = np.einsum("ik,ik->i", xs[im], Ws[in_])
+    assert rel(y.float().cpu().numpy()[im, in_], ref_y) < 3e-3
+    ref_dx = np.einsum("in,in->i", dys[im], Ws[:, ik].T)
+    assert rel(dx.float().cpu().numpy()[im, ik], ref_dx) < 3e-3
+    ref_dw = np.einsum("mi,mi->i", dys[:, in_], xs[:, ik])
+    assert rel(dW.cpu().numpy()[in_, ik], ref_dw) < 1e-4
+    assert rel(db.cpu().numpy(), dys.sum(0)) < 1e-4
+
+
+# ---------------------------------------------------------------- LayerNorm
+
+@pytest.mark.parametrize("dtype", DT, ids=DTN.get)
+@pytest.mark.parametrize("N,C", [(200, 64), (77, 768), (130, 1600), (24576, 768)])
+def test_layernorm_forward_backward(dtype, N, C):
+    say("layernorm", DTN[dtype], N, C)
+    r = rng(N + C)
+    x = r.standard_normal((N, C)) * 2 + 0.5
+    w, b = 1 + r.standard_normal(C) * 0.2, r.standard_normal(C) * 0.2
+    dy, dres0 = r.standard_normal((N, C)), r.standard_normal((N, C))
+    xi, wi, bi, dyi = (as_input(a, dtype).astype(np.float64) for a in (x, w, b, dy))
+    y, mean, rstd = empty((N, C), dtype), empty32((N,)), empty32((N,))
+    lib.layernorm_forward(dtype, dev(x, dtype), dev(w, dtype), dev(b, dtype), y, mean, rstd)
+    ry, cache = O.layernorm_forward(xi, wi, bi)
+    assert rel(host(y), ry) < TOL_OUT[dtype]
+    assert rel(host(rstd), cache[1][:, 0]) < 1e-5
+    assert rel(host(mean), xi.mean(-1)) < 1e-5
+    dres = dev(dres0, FP32)
+    copy = empty((N, C), dtype) if dtype == BF16 else None
+    dw, db = empty32((C,)), empty32((C,))
+    lib.layernorm_backward(dtype, dev(dy, dtype), dev(x, dtype), dev(w, dtype), mean, rstd, dres, False, copy,
+                           dw, db)
+    rdx, rdw, rdb = O.layernorm_backward(dyi, cache)
+    expect = dres0.astype(np.float32).astype(np.float64) + rdx
+    assert rel(host(dres), expect) < 1e-5
+    if copy is not None:
+        assert rel(host(copy), expect) < 3e-3
+    assert rel(host(dw), rdw) < 1e-5
+    assert rel(host(db), rdb) < 1e-5
+    # overwrite mode
+    lib.layernorm_backward(dtype, dev(dy, dtype), dev(x, dtype), dev(w, dtype), mean, rstd, dres, True, None, dw, db)
+    assert rel(host(dres), rdx) < 1e-5
+
+
+# ---------------------------------------------------------------- attention
+
+def qkv_heads(qkv, B, T, H, hd):
+    C = H * hd
+    q = qkv[:, :, :C].reshape(B, T, H, hd).transpose(0, 2, 1, 3)
+    k = qkv[:, :, C:2 * C].reshape(B, T, H, hd).transpose(0, 2, 1, 3)
+    v = qkv[:, :, 2 * C:].reshape(B, T, H, hd).transpose(0, 2, 1, 3)
+    return q, k, v
+
+
+ATT = [(2, 64, 4, 16), (2, 200, 3, 64), (1, 1, 2, 64), (3, 130, 2, 32), (1, 96, 1, 128), (2, 256, 2, 64)]
+
+
+@pytest.mark.parametrize("dtype", DT, ids=DTN.get)
+@pytest.mark.parametrize("B,T,H,hd", ATT)
+def test_attention_forward_backward(dtype, B, T, H, hd):
+    say("attention", DTN[dtype], B, T, H, hd)
+    r = rng(B * 1000 + T + H + hd)
+    C = H * hd
+    qkv = r.standard_normal((B, T, 3 * C))
+    dout = r.standard_normal((B, T, C))
+    qi, doi = as_input(qkv, dtype).astype(np.float64), as_input(dout, dtype).astype(np.float64)
+    out, lse = empty((B, T, C), dtype), empty32((B, H, T))
+    dq = dev(qkv, dtype)
+    lib.attention_forward(dtype, B, T, H, hd, dq, out, lse)
+    dqkv = empty((B, T, 3 * C), dtype)
+    lib.attention_backward(dtype, B, T, H, hd, dq, out, dev(dout, dtype), lse, dqkv)
+    q, k, v = qkv_heads(qi, B, T, H, hd)
+    ro = np.empty((B, H, T, hd))
+    rg = np.empty((B, T, 3 * C))
+    rlse = np.empty((B, H, T))
+    for b in range(B):
+        o, p = O.causal_attention_forward(q[b], k[b], v[b])
+        ro[b] = o
+        s = np.matmul(q[b], np.swapaxes(k[b], -1, -2)) / math.sqrt(hd)
+        s = np.where(np.triu(np.ones((T, T), bool), 1), -np.inf, s)
+        mx = s.max(-1)
+        rlse[b] = mx + np.log(np.exp(s - mx[..., None]).sum(-1))
+        do = doi[b].reshape(T, H, hd).transpose(1, 0, 2)
+        gq, gk, gv = O.causal_attention_backward(do, q[b], k[b], v[b], p)
+        rg[b, :, :C] = gq.transpose(1, 0, 2).reshape(T, C)
+        rg[b, :, C:2 * C] = gk.transpose(1, 0, 2).reshape(T, C)
+        rg[b, :, 2 * C:] = gv.transpose(1, 0, 2).reshape(T, C)
+    tol = {FP32: 1e-5, BF16: 6e-3}[dtype]
+    assert rel(host(out), ro.transpose(0, 2, 1, 3).reshape(B, T, C)) < tol
+    assert rel(host(lse), rlse) < 1e-5 if dtype == FP32 else rel(host(lse), rlse) < 1e-3
+    assert rel(host(dqkv), rg) < (1e-5 if dtype == FP32 else 1e-2)
+
+
+def test_attention_full_size_sampled_heads():
+    """GPT-2 124M attention (B=24, T=1024, H=12, hd=64) in bf16: three sampled
+    (batch, head) pairs recomputed by the oracle."""
+    B, T, H, hd = 24, 1024, 12, 64
+    say("attention full size", B, T, H, hd)
+    torch = __import__("torch")
+    C = H * hd
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    qkv = torch.randn((B, T, 3 * C), generator=gen, device="cuda").to(torch.bfloat16)
+    dout = torch.randn((B, T, C), generator=gen, device="cuda").to(torch.bfloat16)
+    out = torch.empty((B, T, C), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    lib.attention_forward(BF16, B, T, H, hd, qkv, out, lse)
+    dqkv = torch.empty((B, T, 3 * C), dtype=torch.bfloat16, device="cuda")
+    lib.attention_backward(BF16, B, T, H, hd, qkv, out, dout, lse, dqkv)
+    torch.cuda.synchronize()
+    qn = qkv.float().cpu().numpy().astype(np.float64)
+    dn = dout.float().cpu().numpy().astype(np.float64)
+    on, gn = out.float().cpu().numpy(), dqkv.float().cpu().numpy()
+    for b, h in [(0, 0), (11, 7), (23, 11)]:
+        sl = slice(h * hd, (h + 1) * hd)
+        q, k, v = qn[b, :, sl], qn[b, :, C + h * hd:C + (h + 1) * hd], qn[b, :, 2 * C + h * hd:2 * C + (h + 1) * hd]
+        o, p = O.causal_attention_forward(q[None], k[None], v[None])
+        gq, gk, gv = O.causal_attention_backward(dn[b, :, sl][None], q[None], k[None], v[None], p)
+        assert rel(on[b, :, sl], o[0]) < 6e-3
+        assert rel(gn[b, :, sl], gq[0]) < 1e-2
+        assert rel(gn[b, :, C + h * hd:C + (h + 1) * hd], gk[0]) < 1e-2
+        assert rel(gn[b, :, 2 * C + h * hd:2 * C + (h + 1) * hd], gv[0]) < 1e-2
+
+
+# ---------------------------------------------------------------- softmax CE
+
+@pytest.mark.parametrize("dtype", DT, ids=DTN.get)
+@pytest.mark.parametrize("N,V,Vp", [(300, 1000, 1024), (64, 512, 512), (33, 50257, 50304), (5, 8, 64)])
+def test_softmax_xent(dtype, N, V, Vp):
+    say("softmax_xent", DTN[dtype], N, V, Vp)
+    r = rng(N + V)
+    z = r.standard_normal((N, Vp)) * 2
+    z[:, V:] = 30.0          # padded columns must not matter
+    y = r.integers(0, V, N)
+    zi = as_input(z, dtype).astype(np.float64)
+    logits = dev(z, dtype)
+    losses = empty32((N,))
+    lib.softmax_xent(dtype, logits, dev_i32(y), losses, V, 1.0 / N)
+    rl, rdz = O.softmax_cross_entropy(zi[:, :V], y)
+    assert rel(host(losses), rl) < 1e-5
+    g = host(logits)
+    assert np.all(g[:, V:] == 0.0)
+    assert rel(g[:, :V], rdz) < TOL_OUT[dtype]
+    # each row of dlogits sums to zero (up to the output rounding)
+    assert np.abs(g.sum(-1)).max() < 1e-2 / N
+
+
+def test_classifier_full_size():
+    """The stand-alone classifier at GPT-2 124M shape (hidden 24x1024x768 ~
+    N(0,1), tied table 50304x768 ~ N(0,0.02) including its padded rows,
+    labels uniform in [0, 50257)): sampled rows of the losses, dlogits and
+    d_hidden against the oracle; d_wte by its invariants (padded rows exactly
+    zero, columns sum to zero because every dlogits row does)."""
+    N, C, V, Vp = 24 * 1024, 768, 50257, 50304
+    say("classifier full size", N, C, V, Vp)
+    torch = __import__("torch")
+    hidden, wte, labels = S.classifier_inputs(N, C, V, Vp, seed=17)
+    h_d, w_d = dev(hidden, BF16), dev(wte, BF16)
+    losses = empty32((N,))
+    logits = torch.empty((N, Vp), dtype=torch.bfloat16, device="cuda")
+    d_hidden = torch.empty((N, C), dtype=torch.bfloat16, device="cuda")
+    d_wte = torch.empty((Vp, C), dtype=torch.float32, device="cuda")
+    lib.classifier_fwd_bwd(BF16, h_d, w_d, dev_i32(labels), V, losses, logits, d_hidden, d_wte)
+    torch.cuda.synchronize()
+    hi = S.bf16_round(hidden).astype(np.float64)
+    wi = S.bf16_round(wte).astype(np.float64)
+    rows = rng(1).integers(0, N, 48)
+    z = hi[rows] @ wi[:V].T
+    rl, rdz = O.softmax_cross_entropy(z, labels[rows])
+    rdz = rdz * len(rows) / N          # oracle normalised by the sample size
+    gl = losses.cpu().numpy()[rows]
+    assert rel(gl, rl) < 1e-3
+    gdz = logits[torch.from_numpy(rows).cuda()].float().cpu().numpy()
+    assert np.all(gdz[:, V:] == 0)
+    assert rel(gdz[:, :V], rdz) < 1e-2
+    assert rel(d_hidden[torch.from_numpy(rows).cuda()].float().cpu().numpy(), rdz @ wi[:V]) < 1e-2
+    dw = d_wte.cpu().numpy().astype(np.float64)
+    assert np.all(dw[V:] == 0)
+    assert np.abs(dw.sum(0)).max() < 1e-3 * np.abs(dw).sum(0).max()
+    assert np.isfinite(dw).all()
+
+
+# ---------------------------------------------------------------- encoder
+
+@pytest.mark.parametrize("dtype", DT, ids=DTN.get)
+@pytest.mark.parametrize("B,T,C,V", [(4, 64, 64, 512), (24, 1024, 768, 50257), (3, 40, 128, 300)])
+def test_encoder(dtype, B, T, C, V):
+    say("encoder", DTN[dtype], B, T, C, V)
+    r = rng(B + T + C)
+    maxT = T + 8
+    if V >= 50000:
+        tok, _ = S.zipf_batch(B, T, seed=5)
+    else:
+        tok = r.integers(0, V, (B, T)).astype(np.int32)
+        tok[0, : T // 2] = 3          # a hot row
+    wte, wpe = r.standard_normal((V, C)), r.standard_normal((maxT, C))
+    out = empty((B, T, C), dtype)
+    lib.encoder_forward(dtype, dev_i32(tok), dev(wte, dtype), dev(wpe, dtype), out, V)
+    ref = O.encoder_forward(as_input(wte, dtype).astype(np.float64), as_input(wpe, dtype).astype(np.float64), tok)
+    expect = as_input(ref, dtype)
+    assert np.array_equal(host(out).astype(np.float32), expect)
+    dx0 = r.standard_normal((B, T, C)).astype(np.float32)
+    base = r.standard_normal((V, C)).astype(np.float32)
+    dwte, dwpe = dev(base, FP32), empty32((T, C))
+    lib.encoder_backward(dev_i32(tok), dev(dx0, FP32), dwte, dwpe, V)
+    rw, rp = O.encoder_backward(dx0.astype(np.float64), tok, V, T)
+    got = host(dwte)
+    assert rel(got, base + rw) < 1e-6
+    assert rel(host(dwpe), rp) < 1e-6
+    # deterministic: a second run gives identical bits
+    dwte2 = dev(base, FP32)
+    lib.encoder_backward(dev_i32(tok), dev(dx0, FP32), dwte2, dwpe, V)
+    assert np.array_equal(host(dwte2), got)
+
+
+# ---------------------------------------------------------------- AdamW
+
+@pytest.mark.parametrize("n", [1000003, 64, 5])
+def test_adamw(n):
+    say("adamw", n)
+    torch = __import__("torch")
+    r = rng(n)
+    th, g = r.standard_normal(n).astype(np.float32), r.standard_normal(n).astype(np.float32)
+    m0 = (r.standard_normal(n) * 0.1).astype(np.float32)
+    v0 = np.abs(r.standard_normal(n) * 0.1).astype(np.float32)
+    M, G, Mm, Vv = (dev(a, FP32) for a in (th, g, m0, v0))
+    pb = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    lib.adamw(M, G, Mm, Vv, pb, 6e-4, 0.9, 0.95, 1e-8, 0.1, 3)
+    rt, rm, rv = O.adamw_update(th.astype(np.float64), g.astype(np.float64), m0.astype(np.float64),
+                                v0.astype(np.float64), 6e-4, 0.9, 0.95, 1e-8, 0.1, 3)
+    assert rel(host(M), rt) < 1e-6
+    # the update itself (~lr): fp32 rounding of theta (~6e-8) bounds its relative error by ~1e-4
+    assert rel(host(M) - th, rt - th) < 1e-3
+    assert rel(host(Mm), rm) < 1e-6 and rel(host(Vv), rv) < 1e-6
+    assert np.array_equal(host(pb).astype(np.float32), S.bf16_round(host(M).astype(np.float32)))

@@ -33,6 +33,24 @@ def rel(a, b):
     return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
 
 
+# ---------------------------------------------------------------- linear
+
+def test_linear_matches_torch():
+    x = RNG.standard_normal((9, 12))
+    w = RNG.standard_normal((7, 12))
+    b = RNG.standard_normal(7)
+    dy = RNG.standard_normal((9, 7))
+    y = O.linear_forward(x, w, b)
+    dx, dw, db = O.linear_backward(dy, x, w)
+    tx, tw, tb = t(x, True), t(w, True), t(b, True)
+    ty = F.linear(tx, tw, tb)
+    ty.backward(t(dy))
+    assert rel(y, ty.detach().numpy()) < 1e-14
+    assert rel(dx, tx.grad.numpy()) < 1e-14
+    assert rel(dw, tw.grad.numpy()) < 1e-14
+    assert rel(db, tb.grad.numpy()) < 1e-14
+
+
 # ---------------------------------------------------------------- LayerNorm
 
 def test_layernorm_matches_torch_forward_and_backward():
