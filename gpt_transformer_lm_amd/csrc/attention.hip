@@ -19,6 +19,8 @@
 // storage, fp32 arithmetic on the vector ALUs): one thread (or TPR threads
 // splitting the head dim) per row, the other operand staged through LDS in
 // 64-row tiles.  dQ and dK/dV are separate kernels so no atomics are needed.
+// bf16 with head dim 64 (every GPT-2 size) runs on the matrix cores instead
+// (attention_mfma.hip); the rowsum(dO * O) pass is shared.
 
 #include "kernels.h"
 
@@ -91,19 +93,27 @@ __global__ __launch_bounds__(kRows * TPR) void attn_fwd_simt(int T_, int H, cons
   }
 }
 
-// D[bh, i] = dO_i . O_i
+// D[bh, i] = dO_i . O_i.  hd/8 lanes per row, each taking one 16-byte chunk
+// of O and dO, combined with lane swizzles.
 template <typename T>
-__global__ void attn_bwd_dot_kernel(int B, int T_, int H, int hd, const T* __restrict__ out,
-                                    const T* __restrict__ dout, float* __restrict__ D) {
-  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)B * H * T_) return;
-  int i = idx % T_, bh = idx / T_, b = bh / H, h = bh % H;
-  const int C = H * hd;
-  const T* o = out + ((size_t)b * T_ + i) * C + h * hd;
-  const T* d = dout + ((size_t)b * T_ + i) * C + h * hd;
+__global__ __launch_bounds__(256) void attn_bwd_dot_kernel(int B, int T_, int H, int hd, const T* __restrict__ out,
+                                                           const T* __restrict__ dout, float* __restrict__ D) {
+  const int lpr = hd / 8;                       // lanes per row: 2, 4, 8 or 16
+  const int64_t gl = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gl / lpr;                 // (b, h, i) in lse order
+  const int part = (int)(gl % lpr);
   float s = 0.f;
-  for (int e = 0; e < hd; ++e) s += to_f32(o[e]) * to_f32(d[e]);
-  D[idx] = s;
+  if (row < (int64_t)B * H * T_) {
+    const int i = (int)(row % T_), bh = (int)(row / T_), b = bh / H, h = bh % H;
+    const size_t off = ((size_t)b * T_ + i) * (size_t)(H * hd) + h * hd + part * 8;
+    float o[8], d[8];
+    Chunk8<T>::load(out + off, o);
+    Chunk8<T>::load(dout + off, d);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += o[e] * d[e];
+  }
+  for (int m = 1; m < lpr; m <<= 1) s += __shfl_xor(s, m, 64);
+  if (row < (int64_t)B * H * T_ && part == 0) D[row] = s;
 }
 
 template <typename T, int HD, int TPR>
@@ -294,6 +304,7 @@ int attention_forward(int dtype, int B, int T_, int H, int hd, const void* qkv, 
   if (B < 0 || T_ < 0 || H <= 0 || !qkv || !out || !lse)
     return gpt2_internal_fail(1, "attention_forward: bad arguments");
   if (B == 0 || T_ == 0) return 0;
+  if (attention_mfma_supported(dtype, hd)) return attention_forward_mfma(B, T_, H, qkv, out, lse, stream);
   return dtype == BF16 ? fwd_dispatch<bf16>(B, T_, H, hd, qkv, out, lse, stream)
                        : fwd_dispatch<float>(B, T_, H, hd, qkv, out, lse, stream);
 }
@@ -312,15 +323,17 @@ int attention_backward(int dtype, int B, int T_, int H, int hd, const void* qkv,
   if (!workspace || workspace_bytes < attention_backward_workspace_bytes(B, T_, H, hd))
     return gpt2_internal_fail(3, "attention_backward: workspace too small");
   float* D = (float*)workspace;
-  int64_t rows = (int64_t)B * H * T_;
+  const int64_t lanes = (int64_t)B * H * T_ * (hd / 8);
   if (dtype == BF16) {
-    hipLaunchKernelGGL(attn_bwd_dot_kernel<bf16>, dim3((unsigned)ceil_div64(rows, 256)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(attn_bwd_dot_kernel<bf16>, dim3((unsigned)ceil_div64(lanes, 256)), dim3(256), 0, stream,
                        B, T_, H, hd, (const bf16*)out, (const bf16*)dout, D);
   } else {
-    hipLaunchKernelGGL(attn_bwd_dot_kernel<float>, dim3((unsigned)ceil_div64(rows, 256)), dim3(256), 0,
+    hipLaunchKernelGGL(attn_bwd_dot_kernel<float>, dim3((unsigned)ceil_div64(lanes, 256)), dim3(256), 0,
                        stream, B, T_, H, hd, (const float*)out, (const float*)dout, D);
   }
   GPT2_LAUNCH_CHECK();
+  if (attention_mfma_supported(dtype, hd))
+    return attention_backward_mfma(B, T_, H, qkv, dout, lse, D, dqkv, stream);
   return dtype == BF16 ? bwd_dispatch<bf16>(B, T_, H, hd, qkv, dout, lse, D, dqkv, stream)
                        : bwd_dispatch<float>(B, T_, H, hd, qkv, dout, lse, D, dqkv, stream);
 }

@@ -66,6 +66,12 @@ int layernorm_backward(int dtype, int N, int C, const void* dy, const void* x, c
 int attention_forward(int dtype, int B, int T, int H, int hd, const void* qkv, void* out,
                       float* lse, hipStream_t stream);
 size_t attention_backward_workspace_bytes(int B, int T, int H, int hd);
+// Matrix-core kernels (attention_mfma.hip) for bf16 with head dim 64; the
+// launchers above dispatch to them when attention_mfma_supported().
+bool attention_mfma_supported(int dtype, int hd);
+int attention_forward_mfma(int B, int T, int H, const void* qkv, void* out, float* lse, hipStream_t stream);
+int attention_backward_mfma(int B, int T, int H, const void* qkv, const void* dout, const float* lse,
+                            const float* D, void* dqkv, hipStream_t stream);
 int attention_backward(int dtype, int B, int T, int H, int hd, const void* qkv, const void* out,
                        const void* dout, const float* lse, void* dqkv, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);

@@ -11,8 +11,9 @@
 // accumulated into the fp32 residual-stream gradient (the residual add of the
 // block is the identity, so its gradient is this running sum), with a
 // storage-type copy for the next GEMM.  dw = sum_rows dy * xhat and
-// db = sum_rows dy are accumulated per wave in registers, written as per-wave
-// partial rows and summed by a second kernel in a fixed order.
+// db = sum_rows dy are accumulated per wave in registers, combined per block
+// in LDS into one partial row, and the partial rows are summed by a second
+// kernel in a fixed order (deterministic).
 
 #include "kernels.h"
 
@@ -144,24 +145,43 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(int N, int C, const T* __re
       }
     }
   }
+  // reduce the block's 4 waves in LDS, one partial row per block (dw, then db)
+  extern __shared__ float red[];   // [4][C]
+  const int wi = threadIdx.x >> 6;
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    int ch = lane + 64 * c;
-    if (ch < nch) {
-      Chunk8<float>::store(part_dw + (size_t)wave_id * C + ch * 8, dwa[c]);
-      Chunk8<float>::store(part_db + (size_t)wave_id * C + ch * 8, dba[c]);
+  for (int pass = 0; pass < 2; ++pass) {
+    float(*acc)[8] = pass == 0 ? dwa : dba;
+    float* dst = pass == 0 ? part_dw : part_db;
+    if (pass == 1) __syncthreads();
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      int ch = lane + 64 * c;
+      if (ch < nch) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[wi * C + ch * 8 + e] = acc[c][e];
+      }
     }
+    __syncthreads();
+    for (int i = threadIdx.x; i < C; i += blockDim.x)
+      dst[(size_t)blockIdx.x * C + i] = (red[i] + red[C + i]) + (red[2 * C + i] + red[3 * C + i]);
   }
 }
 
-// out[c] (+)= sum_p part[p * C + c], p in order.
-__global__ void column_reduce_kernel(const float* __restrict__ part, int P, int C,
-                                     float* __restrict__ out, bool accumulate) {
-  int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= C) return;
+// out[c] (+)= sum over the P partial rows, in a fixed order: a block owns 64
+// columns; its 4 waves sum interleaved quarters of the rows, then combine.
+__global__ __launch_bounds__(256) void column_reduce_kernel(const float* __restrict__ part, int P, int C,
+                                                            float* __restrict__ out, bool accumulate) {
+  __shared__ float sh[4][64];
+  const int c = blockIdx.x * 64 + (threadIdx.x & 63), g = threadIdx.x >> 6;
   float s = 0.f;
-  for (int p = 0; p < P; ++p) s += part[(size_t)p * C + c];
-  out[c] = accumulate ? out[c] + s : s;
+  if (c < C)
+    for (int p = g; p < P; p += 4) s += part[(size_t)p * C + c];
+  sh[g][threadIdx.x & 63] = s;
+  __syncthreads();
+  if (g == 0 && c < C) {
+    const float t = (sh[0][threadIdx.x] + sh[1][threadIdx.x]) + (sh[2][threadIdx.x] + sh[3][threadIdx.x]);
+    out[c] = accumulate ? out[c] + t : t;
+  }
 }
 
 int nch_for(int C) {
@@ -173,7 +193,9 @@ int nch_for(int C) {
   return -1;
 }
 
+// waves of the backward grid (4 per block; each block writes one partial row)
 int bwd_waves(int N) { return (int)std::min<int64_t>(1024, ((int64_t)N + 3) / 4 * 4); }
+int bwd_blocks(int N) { return bwd_waves(N) / 4; }
 
 template <typename T>
 int fwd_t(int N, int C, const void* x, const void* w, const void* b, void* y, float* mean, float* rstd,
@@ -198,17 +220,17 @@ template <typename T>
 int bwd_t(int N, int C, const void* dy, const void* x, const void* w, const float* mean,
           const float* rstd, float* dres, bool ovw, void* dres_copy, float* pdw, float* pdb,
           hipStream_t s) {
-  int waves = bwd_waves(N);
-  dim3 grid((unsigned)(waves / 4)), block(256);
+  dim3 grid((unsigned)bwd_blocks(N)), block(256);
+  const size_t lds = 4 * (size_t)C * sizeof(float);
   const T* DY = (const T*)dy;
   const T* X = (const T*)x;
   const T* W = (const T*)w;
   T* DC = (T*)dres_copy;
   switch (nch_for(C)) {
-    case 1: hipLaunchKernelGGL((ln_bwd_kernel<T, 1>), grid, block, 0, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
-    case 2: hipLaunchKernelGGL((ln_bwd_kernel<T, 2>), grid, block, 0, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
-    case 4: hipLaunchKernelGGL((ln_bwd_kernel<T, 4>), grid, block, 0, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
-    case 8: hipLaunchKernelGGL((ln_bwd_kernel<T, 8>), grid, block, 0, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
+    case 1: hipLaunchKernelGGL((ln_bwd_kernel<T, 1>), grid, block, lds, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
+    case 2: hipLaunchKernelGGL((ln_bwd_kernel<T, 2>), grid, block, lds, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
+    case 4: hipLaunchKernelGGL((ln_bwd_kernel<T, 4>), grid, block, lds, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
+    case 8: hipLaunchKernelGGL((ln_bwd_kernel<T, 8>), grid, block, lds, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
     default: return gpt2_internal_fail(1, "layernorm: C=%d unsupported", C);
   }
   GPT2_LAUNCH_CHECK();
@@ -227,7 +249,7 @@ int layernorm_forward(int dtype, int N, int C, const void* x, const void* w, con
 }
 
 size_t layernorm_backward_workspace_bytes(int N, int C) {
-  return 2 * (size_t)bwd_waves(N) * C * sizeof(float) + 256;
+  return 2 * (size_t)bwd_blocks(N) * C * sizeof(float) + 256;
 }
 
 int layernorm_backward(int dtype, int N, int C, const void* dy, const void* x, const void* w,
@@ -240,16 +262,16 @@ int layernorm_backward(int dtype, int N, int C, const void* dy, const void* x, c
   size_t need = layernorm_backward_workspace_bytes(N, C);
   if (!workspace || workspace_bytes < need)
     return gpt2_internal_fail(3, "layernorm_backward: workspace too small");
-  const int P = bwd_waves(N);
+  const int P = bwd_blocks(N);
   float* pdw = (float*)workspace;
   float* pdb = pdw + (size_t)P * C;
   int rc = dtype == BF16 ? bwd_t<bf16>(N, C, dy, x, w, mean, rstd, dres, dres_overwrite, dres_copy, pdw, pdb, stream)
                          : bwd_t<float>(N, C, dy, x, w, mean, rstd, dres, dres_overwrite, dres_copy, pdw, pdb, stream);
   if (rc) return rc;
-  hipLaunchKernelGGL(column_reduce_kernel, dim3((unsigned)ceil_div64(C, 256)), dim3(256), 0, stream, pdw, P,
+  hipLaunchKernelGGL(column_reduce_kernel, dim3((unsigned)ceil_div64(C, 64)), dim3(256), 0, stream, pdw, P,
                      C, dw, accumulate);
   GPT2_LAUNCH_CHECK();
-  hipLaunchKernelGGL(column_reduce_kernel, dim3((unsigned)ceil_div64(C, 256)), dim3(256), 0, stream, pdb, P,
+  hipLaunchKernelGGL(column_reduce_kernel, dim3((unsigned)ceil_div64(C, 64)), dim3(256), 0, stream, pdb, P,
                      C, db, accumulate);
   GPT2_LAUNCH_CHECK();
   return 0;

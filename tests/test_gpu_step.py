@@ -216,11 +216,14 @@ def test_call_order_errors():
 
 def test_gpt2_124m_full_size():
     """GPT-2 124M at B=24, T=1024, bf16, initialised from a seed by the library,
-    Zipf/EoT tokens: the initial loss matches its closed form, the per-position
-    losses of one batch row match the oracle (its own init from the same seed,
-    forward of that row), gradients are finite, padded rows get exactly zero
-    gradient and stay zero after AdamW, and a second identical step reproduces
-    every bit."""
+    Zipf/EoT tokens: the per-position losses of one batch row match the oracle
+    (its own init from the same seed, forward of that row), gradients are
+    finite, padded rows get exactly zero gradient and stay zero after AdamW, and
+    a second identical step reproduces every bit.  The initial loss is only
+    bounded loosely: at C = 768 the logit of each position's own input token,
+    about |wte_tok|^2 / std(x), is far from the near-uniform regime in which
+    loss ~= ln V + sigma^2 / 2 holds (that closed form is pinned on the tiny
+    configuration)."""
     c = G124
     say("124M full size")
     tok, tgt = S.zipf_batch(c["B"], c["T"], seed=7)
@@ -238,8 +241,7 @@ def test_gpt2_124m_full_size():
         say("rep", rep, "loss", loss)
     loss, losses, g, p = res[0]
     assert res[1][0] == loss and np.array_equal(res[1][2], g) and np.array_equal(res[1][3], p)
-    expect = math.log(50257) + 0.02 ** 2 * 768 / 2
-    assert abs(loss - expect) < 0.05, loss
+    assert math.log(50257) < loss < math.log(50257) + 1.0, loss
     assert np.isfinite(g).all()
     gd = lib.unflatten(cfg, g)
     pd = lib.unflatten(cfg, p)
@@ -251,5 +253,6 @@ def test_gpt2_124m_full_size():
     b = 5
     _, ol, _, _ = O.gpt2_forward(op, tok[b:b + 1], tgt[b:b + 1], ocfg(c))
     r = rel(losses[b], ol[0])
-    say("row-5 per-token loss rel", r)
+    say("row-5 per-token loss rel", r, "mean", losses[b].mean(), "oracle", ol[0].mean())
     assert r < 1e-2
+    assert abs(losses[b].mean() - ol[0].mean()) < 1e-2 * ol[0].mean()
