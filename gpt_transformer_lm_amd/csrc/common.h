@@ -82,20 +82,25 @@ __device__ __forceinline__ float fast_exp(float x) {
 }
 
 // GELU, tanh form: 0.5 u (1 + tanh(k0 (u + k1 u^3))), with
-// tanh(z) = 1 - 2 / (1 + e^{2z}) (saturates correctly for |z| large).
+// tanh(z) = 1 - 2 / (1 + e^{2z}); e^{2z} from the hardware base-2 exponential
+// and the reciprocal from v_rcp_f32 (both ~1 ulp).  Saturates correctly:
+// e^{2z} -> inf gives tanh -> 1, e^{2z} -> 0 gives tanh -> -1.
+__device__ __forceinline__ float tanh_via_exp(float z) {
+  const float e2z = __builtin_amdgcn_exp2f(z * 2.8853900817779268f);   // 2 log2(e)
+  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e2z);
+}
+
 __device__ __forceinline__ float gelu_tanh_f(float u) {
   const float k0 = 0.7978845608028654f, k1 = 0.044715f;
-  float z = k0 * (u + k1 * u * u * u);
-  float th = 1.0f - 2.0f / (1.0f + __expf(2.0f * z));
+  const float th = tanh_via_exp(k0 * (u + k1 * u * u * u));
   return 0.5f * u * (1.0f + th);
 }
 
 // d/du of gelu_tanh_f.
 __device__ __forceinline__ float gelu_tanh_grad_f(float u) {
   const float k0 = 0.7978845608028654f, k1 = 0.044715f;
-  float z = k0 * (u + k1 * u * u * u);
-  float th = 1.0f - 2.0f / (1.0f + __expf(2.0f * z));
-  float dz = k0 * (1.0f + 3.0f * k1 * u * u);
+  const float th = tanh_via_exp(k0 * (u + k1 * u * u * u));
+  const float dz = k0 * (1.0f + 3.0f * k1 * u * u);
   return 0.5f * (1.0f + th) + 0.5f * u * (1.0f - th * th) * dz;
 }
 

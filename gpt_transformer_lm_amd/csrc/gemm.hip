@@ -72,10 +72,25 @@ __device__ __forceinline__ int swz(int row, int c) { return c ^ ((row ^ (row >> 
 struct MfmaArgs {
   const bf16* A; int64_t lda;
   const bf16* B; int64_t ldb;
+  uint32_t a_bytes, b_bytes;   // readable extent of A and B from their base pointers
   int M, N, K;
   int k_per_split;
+  bool vec_epilogue;     // every 8-column run is 16-byte aligned and inside N
   EpiArgs e;
 };
+
+// Offset past every operand extent (the host requires extents below it).
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
+
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
+  return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
 
 // Register staging of one operand tile: R rows (the M or N axis) x 64 k.
 template <int R, bool KMAJ>
@@ -85,31 +100,30 @@ struct Stager {
 
   // rows [row0, row0 + R) of the operand, k in [k0, k0 + 64); rows >= nrows and
   // k >= K read as 0 (K is a multiple of 8, so a 16-byte run never straddles K).
-  __device__ __forceinline__ void load(const bf16* __restrict__ G, int64_t ld, int row0, int nrows,
-                                       int k0, int K, int tid) {
+  // Buffer loads: an offset past the buffer's extent returns zeros, so
+  // out-of-range elements are steered there instead of branching.
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int row0, int nrows, int k0, int K,
+                                       int tid) {
     if constexpr (KMAJ) {
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
-        int row = tid / 8 + 32 * i, c = tid % 8;
-        if (row0 + row < nrows && k0 + c * 8 < K)
-          r[i] = *reinterpret_cast<const uint4*>(G + (size_t)(row0 + row) * ld + k0 + c * 8);
-        else
-          r[i] = make_uint4(0, 0, 0, 0);
+        const int row = row0 + tid / 8 + 32 * i, k = k0 + (tid % 8) * 8;
+        const bool ok = row < nrows && k < K;
+        const uint32_t off = ok ? (uint32_t)(((int64_t)row * ld + k) * 2) : kOutOfRange;
+        r[i] = load16(rs, off);
       }
     } else {
       // unit u: 8 consecutive rows (contiguous in memory) x 4 consecutive k.
 #pragma unroll
       for (int j = 0; j < R / 128; ++j) {
-        int u = tid + kThreads * j;
-        int mc = u % (R / 8), kg = u / (R / 8);
-        bool ok = row0 + mc * 8 < nrows;
+        const int u = tid + kThreads * j;
+        const int mc = u % (R / 8), kg = u / (R / 8);
+        const bool okr = row0 + mc * 8 < nrows;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int k = k0 + kg * 4 + i;
-          if (ok && k < K)
-            r[j * 4 + i] = *reinterpret_cast<const uint4*>(G + (size_t)k * ld + row0 + mc * 8);
-          else
-            r[j * 4 + i] = make_uint4(0, 0, 0, 0);
+          const uint32_t off = (okr && k < K) ? (uint32_t)(((int64_t)k * ld + row0 + mc * 8) * 2) : kOutOfRange;
+          r[j * 4 + i] = load16(rs, off);
         }
       }
     }
@@ -164,21 +178,91 @@ struct Stager {
   }
 };
 
+// Eight consecutive columns n..n+7 of row m (v = fp32 sums); 16-byte accesses.
+template <int EPI>
+__device__ __forceinline__ void epilogue_vec8(const EpiArgs& e, int m, int n, float v[8], int z) {
+  if constexpr (EPI == EPI_WGRAD) {
+    float* dst = e.partial + ((size_t)z * e.M + m) * (size_t)e.N + n;
+    Chunk8<float>::store(dst, v);
+  } else {
+    if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_RES || EPI == EPI_BIAS_GELU) {
+      float b[8];
+      Chunk8<bf16>::load(reinterpret_cast<const bf16*>(e.bias) + n, b);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] += b[i];
+    }
+    if constexpr (EPI == EPI_BIAS_RES) {
+      float r[8];
+      Chunk8<bf16>::load(reinterpret_cast<const bf16*>(e.aux_in) + (size_t)m * e.ld_aux + n, r);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] += r[i];
+    }
+    if constexpr (EPI == EPI_BIAS_GELU) {
+      Chunk8<bf16>::store(reinterpret_cast<bf16*>(e.aux_out) + (size_t)m * e.ldc + n, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = gelu_tanh_f(v[i]);
+    }
+    if constexpr (EPI == EPI_GELU_BWD) {
+      float u[8];
+      Chunk8<bf16>::load(reinterpret_cast<const bf16*>(e.aux_in) + (size_t)m * e.ld_aux + n, u);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] *= gelu_tanh_grad_f(u[i]);
+    }
+    Chunk8<bf16>::store(reinterpret_cast<bf16*>(e.C) + (size_t)m * e.ldc + n, v);
+  }
+}
+
+// Tile coordinates of workgroup `bid`.  The dispatcher hands consecutive
+// workgroup ids to the 8 XCDs in turn; each XCD is given a contiguous range of
+// tiles (so the tiles resident on one XCD share its L2), and inside a range
+// tiles run in groups of 8 M-tiles that sweep the N-tiles together.
+__device__ __forceinline__ void tile_coords(int bid, int nbm, int nbn, int& tm, int& tn) {
+  const int ntiles = nbm * nbn;
+  const int xcd = bid & 7, idx = bid >> 3;
+  const int base = ntiles >> 3, rem = ntiles & 7;
+  const int t = xcd * base + min(xcd, rem) + idx;
+  constexpr int GM = 8;
+  const int group = t / (GM * nbn);
+  const int first_m = group * GM;
+  const int gsize = min(nbm - first_m, GM);
+  const int r = t - group * GM * nbn;
+  tm = first_m + r % gsize;
+  tn = r / gsize;
+}
+
+template <int BM, int BN>
+struct MfmaShape {
+  static constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  static constexpr int TILE = (BM + BN) * kBK;                 // bf16 elements per stage
+  static constexpr int EP_PITCH = WN + 4;                      // fp32 pitch of the epilogue rows
+  static constexpr int MAIN_BYTES = 2 * TILE * 2;
+  static constexpr int EPI_BYTES = 4 * 32 * EP_PITCH * 4;
+  static constexpr int RED_BYTES = 16 * BM * 4;
+  static constexpr int SMEM = MAIN_BYTES > EPI_BYTES ? (MAIN_BYTES > RED_BYTES ? MAIN_BYTES : RED_BYTES)
+                                                     : (EPI_BYTES > RED_BYTES ? EPI_BYTES : RED_BYTES);
+};
+
 template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, bool BIAS_GRAD>
-__global__ __launch_bounds__(kThreads) void gemm_bf16_mfma_kernel(MfmaArgs p) {
-  constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
-  constexpr int TILE = (BM + BN) * kBK;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * TILE];
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, (BM == 128 && BN == 128) ? 2 : 1)))
+void gemm_bf16_mfma_kernel(MfmaArgs p) {
+  using S = MfmaShape<BM, BN>;
+  constexpr int WM = S::WM, WN = S::WN, FM = S::FM, FN = S::FN, TILE = S::TILE;
+  __shared__ __attribute__((aligned(16))) char smem_raw[S::SMEM];
+  bf16* smem = reinterpret_cast<bf16*>(smem_raw);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  const int kbeg = blockIdx.z * p.k_per_split;
-  const int KT = p.k_per_split / kBK;
-  const bool do_bias = BIAS_GRAD && blockIdx.x == 0;
+  int tm, tn;
+  tile_coords(blockIdx.x, (p.M + BM - 1) / BM, (p.N + BN - 1) / BN, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int z = blockIdx.y;
+  const int kbeg = z * p.k_per_split;
+  const int KT = (min(p.K, kbeg + p.k_per_split) - kbeg + kBK - 1) / kBK;
+  const bool do_bias = BIAS_GRAD && tn == 0;
 
   Stager<BM, A_KMAJ> sa;
   Stager<BN, B_KMAJ> sb;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, p.a_bytes), rb = make_rsrc(p.B, p.b_bytes);
   float bsum[BIAS_GRAD ? 8 * (BM / 128) : 1];
   if constexpr (BIAS_GRAD) {
 #pragma unroll
@@ -193,8 +277,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_mfma_kernel(MfmaArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  sa.load(p.A, p.lda, m0, p.M, kbeg, p.K, tid);
-  sb.load(p.B, p.ldb, n0, p.N, kbeg, p.K, tid);
+  sa.load(ra, p.lda, m0, p.M, kbeg, p.K, tid);
+  sb.load(rb, p.ldb, n0, p.N, kbeg, p.K, tid);
   sa.store(smem, tid);
   sb.store(smem + BM * kBK, tid);
   if constexpr (BIAS_GRAD) if (do_bias) sa.accumulate_rows(bsum);
@@ -205,28 +289,38 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_mfma_kernel(MfmaArgs p) {
     const bf16* Bs = As + BM * kBK;
     const bool more = kt + 1 < KT;
     if (more) {
-      sa.load(p.A, p.lda, m0, p.M, kbeg + (kt + 1) * kBK, p.K, tid);
-      sb.load(p.B, p.ldb, n0, p.N, kbeg + (kt + 1) * kBK, p.K, tid);
+      sa.load(ra, p.lda, m0, p.M, kbeg + (kt + 1) * kBK, p.K, tid);
+      sb.load(rb, p.ldb, n0, p.N, kbeg + (kt + 1) * kBK, p.K, tid);
     }
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      bf16x8 a[FM], b[FN];
+    // operand fragments of k16 step kk+1 are read from LDS while the matrix
+    // cores work on step kk
+    bf16x8 a[2][FM], b[2][FN];
+    auto frags = [&](int kk, bf16x8* fa, bf16x8* fb) {
       const int c = kk * 2 + (lane >> 5);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        int row = wm * WM + i * 32 + (lane & 31);
-        a[i] = *reinterpret_cast<const bf16x8*>(As + row * kBK + swz(row, c) * 8);
+        const int row = wm * WM + i * 32 + (lane & 31);
+        fa[i] = *reinterpret_cast<const bf16x8*>(As + row * kBK + swz(row, c) * 8);
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        int row = wn * WN + j * 32 + (lane & 31);
-        b[j] = *reinterpret_cast<const bf16x8*>(Bs + row * kBK + swz(row, c) * 8);
+        const int row = wn * WN + j * 32 + (lane & 31);
+        fb[j] = *reinterpret_cast<const bf16x8*>(Bs + row * kBK + swz(row, c) * 8);
       }
+    };
+    frags(0, a[0], b[0]);
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      if (kk + 1 < kBK / 16) frags(kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
+      // keep the reads above the MFMAs of this step (the scheduler would
+      // otherwise sink each read to just before its first use)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][i], b[kk & 1][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (more) {
       bf16* An = smem + ((kt + 1) & 1) * TILE;
@@ -237,24 +331,48 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_mfma_kernel(MfmaArgs p) {
     __syncthreads();
   }
 
-  // Epilogue.  Accumulator element r of lane l in a 32 x 32 tile is at
-  // row 8 * (r / 4) + 4 * (l / 32) + r % 4, column l % 32.
+  // Epilogue, one 32-row slab of the wave tile at a time: the accumulators
+  // (element r of lane l of a 32 x 32 tile sits at row 8(r/4) + 4(l/32) + r%4,
+  // column l%32) go to a wave-private LDS block, are read back as runs of 8
+  // columns and leave with 16-byte loads/stores.
+  float* ep = reinterpret_cast<float*>(smem_raw) + wave * 32 * S::EP_PITCH;
+  const int hi = lane >> 5;
+  const bool vec = p.vec_epilogue;
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < FM; ++i) {
+    if (i > 0) __syncthreads();
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int col = n0 + wn * WN + j * 32 + (lane & 31);
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * WM + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-        if (row < p.M && col < p.N) epilogue_store<EPI, bf16>(p.e, row, col, acc[i][j][r], blockIdx.z);
+      for (int r = 0; r < 16; ++r)
+        ep[(8 * (r >> 2) + 4 * hi + (r & 3)) * S::EP_PITCH + j * 32 + (lane & 31)] = acc[i][j][r];
+    __syncthreads();
+    const int grow0 = m0 + wm * WM + i * 32, gcol0 = n0 + wn * WN;
+    constexpr int CPR = WN / 8;
+#pragma unroll
+    for (int q = 0; q < (32 * CPR) / 64; ++q) {
+      const int idx = lane + 64 * q;
+      const int rl = idx / CPR, cc = idx % CPR;
+      const int grow = grow0 + rl, gcol = gcol0 + cc * 8;
+      if (grow < p.M && gcol < p.N) {
+        float v[8];
+        Chunk8<float>::load(ep + rl * S::EP_PITCH + cc * 8, v);
+        if (vec) {
+          epilogue_vec8<EPI>(p.e, grow, gcol, v, z);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (gcol + e < p.N) epilogue_store<EPI, bf16>(p.e, grow, gcol + e, v[e], z);
+        }
       }
     }
+  }
 
   if constexpr (BIAS_GRAD) {
-    if (do_bias) {
+    if (do_bias) {   // uniform over the block (depends on the tile only)
+      __syncthreads();
       // reduce bsum over the 16 k-groups that share each row chunk
-      float* red = reinterpret_cast<float*>(smem);   // [16][BM]
+      float* red = reinterpret_cast<float*>(smem_raw);   // [16][BM]
 #pragma unroll
       for (int j = 0; j < BM / 128; ++j) {
         int u = tid + kThreads * j;
@@ -267,7 +385,292 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_mfma_kernel(MfmaArgs p) {
         float s = 0.f;
 #pragma unroll
         for (int kg = 0; kg < 16; ++kg) s += red[kg * BM + m];
-        if (m0 + m < p.M) p.e.partial_bias[(size_t)blockIdx.z * p.M + m0 + m] = s;
+        if (m0 + m < p.M) p.e.partial_bias[(size_t)z * p.M + m0 + m] = s;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- bf16 MFMA, direct-to-LDS
+
+#define GPT2_LDS __attribute__((address_space(3)))
+
+// s_waitcnt immediate that waits for at most n outstanding vector-memory ops
+// (expcnt and lgkmcnt left at their no-wait maxima; gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Operand tile in LDS, R rows of the operand's M (or N) axis x 64 k, filled by
+// buffer_load ... lds (each wave instruction writes 1 KiB, 16 bytes per lane,
+// contiguous in lane order; the layout is realised by choosing which global
+// 16-byte run each lane fetches).
+//  * k-major operand (k contiguous in memory): [row][64 k], 128-byte rows whose
+//    16-byte chunks are XOR-swizzled by row; fragments are ds_read_b128.
+//  * m-major operand (m contiguous in memory): [k][R m], 2R-byte rows whose
+//    16-byte chunks are XOR-swizzled by (k & 3); fragments are two
+//    ds_read_b64_tr_b16 (the transpose read hands lane j of each 16-lane group
+//    element j%4 of the 8-byte runs of lanes j/4 + 4e, so with the per-lane
+//    addresses below every lane ends up with 8 consecutive k of one m).
+template <int R, bool KMAJ>
+struct DmaTile {
+  static constexpr int BYTES = R * kBK * 2;
+  static constexpr int NINST = BYTES / 1024 / 4;          // 1 KiB instructions per wave
+
+  // Per-lane part of the DMA source addresses (two registers per operand); the
+  // rest of each instruction's address is wave-uniform.
+  //  k-major: instruction q of wave w covers tile rows 8 (w NINST + q) + lane/8,
+  //    physical chunk lane%8; the swizzle (row ^ row>>3) & 7 splits into
+  //    lane/8 (per lane) xor (w NINST + q) & 7 (uniform).
+  //  m-major: instruction q covers k rows qk + lane / (R/8) with
+  //    qk = (w NINST + q) * 1024 / (2R), physical chunk lane % (R/8); the
+  //    swizzle ((k & 3) << 1) splits the same way.
+  struct Lane {
+    uint32_t base;    // bytes: row part (k-major) / row-in-group + column part (m-major)
+    uint32_t c16;     // 16 * (per-lane part of the logical chunk index)
+    int sub;          // k-major: chunk index; m-major: k row within the instruction's group
+  };
+  __device__ __forceinline__ static Lane lane_part(int wave, int lane, int row0, int64_t ld) {
+    Lane L;
+    if constexpr (KMAJ) {
+      const int c = (lane & 7) ^ (lane >> 3);
+      L.base = (uint32_t)((int64_t)(row0 + wave * NINST * 8 + (lane >> 3)) * ld * 2);
+      L.c16 = (uint32_t)(c * 16);
+      L.sub = c;
+    } else {
+      constexpr int LPR = R / 8;                       // lanes per k row
+      const int kr = lane / LPR, phys = lane % LPR;
+      const int c = phys ^ ((kr & 3) << 1);
+      L.base = (uint32_t)((int64_t)kr * ld * 2 + (int64_t)row0 * 2);
+      L.c16 = (uint32_t)(c * 16);
+      L.sub = kr;
+    }
+    return L;
+  }
+
+  // Issues this wave's NINST DMA instructions for the K step starting at k0.
+  // Rows beyond the operand's extent only feed discarded outputs (and the
+  // buffer range turns reads past the allocation into zeros); k >= K must be
+  // zero, which only the last, partial K step checks (k_tail).
+  __device__ __forceinline__ static void issue(__amdgpu_buffer_rsrc_t rs, GPT2_LDS char* tile, int wave, const Lane& L,
+                                               int k0, int K, int64_t ld, bool k_tail) {
+#pragma unroll
+    for (int q = 0; q < NINST; ++q) {
+      const int iq = wave * NINST + q;
+      uint32_t off;
+      bool ok = true;
+      if constexpr (KMAJ) {
+        const uint32_t u16 = (uint32_t)((iq & 7) * 16);
+        const uint32_t c16 = L.c16 ^ u16;
+        off = L.base + (uint32_t)q * (uint32_t)(8 * ld * 2) + (uint32_t)(k0 * 2) + c16;
+        if (k_tail) ok = k0 + (int)(c16 >> 4) * 8 < K;
+      } else {
+        constexpr int RPI = 1024 / (2 * R);              // k rows per instruction
+        const int qk = iq * RPI;
+        const uint32_t u16 = (uint32_t)((((qk & 3) << 1) & 6) * 16);
+        off = L.base + (uint32_t)((int64_t)(k0 + qk) * ld * 2) + (L.c16 ^ u16);
+        if (k_tail) ok = k0 + qk + L.sub < K;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (GPT2_LDS void*)(tile + iq * 1024), 16,
+                                               (int)(ok ? off : kOutOfRange), 0, 0, 0);
+    }
+  }
+
+  // MFMA operand fragment: rows [rbase, rbase + 32) of the tile, k16 step kk;
+  // lane l receives row rbase + l%32, k = 16 kk + 8 (l/32) + 0..7.
+  __device__ __forceinline__ static bf16x8 frag(const GPT2_LDS char* tile, int rbase, int kk, int lane) {
+    if constexpr (KMAJ) {
+      const int row = rbase + (lane & 31), c = kk * 2 + (lane >> 5);
+      return *reinterpret_cast<const GPT2_LDS bf16x8*>(tile + row * 128 + swz(row, c) * 16);
+    } else {
+      typedef bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+      const int g = lane >> 4, i = lane & 15;
+      const int m = rbase + 16 * (g & 1) + 4 * (i & 3);
+      bf16x8 out;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int kr = kk * 16 + 8 * (g >> 1) + 4 * r + (i >> 2);
+        const int c = (m >> 3) ^ ((kr & 3) << 1);
+        const GPT2_LDS bf16x4_t* q =
+            reinterpret_cast<const GPT2_LDS bf16x4_t*>(tile + kr * (2 * R) + c * 16 + (m & 7) * 2);
+        const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(const_cast<GPT2_LDS bf16x4_t*>(q));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[4 * r + e] = v[e];
+      }
+      return out;
+    }
+  }
+};
+
+template <int BM, int BN>
+struct DmaShape {
+  static constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  static constexpr int STAGE_BYTES = (BM + BN) * kBK * 2;
+  static constexpr int NS = STAGE_BYTES * 4 <= 160 * 1024 - 20 * 1024 ? 4 : STAGE_BYTES * 3 <= 160 * 1024 - 20 * 1024 ? 3 : 2;
+  static constexpr int EP_PITCH = 36;                     // fp32 pitch of a 32 x 32 epilogue block
+  static constexpr int EP_BYTES = 4 * 32 * EP_PITCH * 4;  // one block per wave
+  static constexpr int RED_BYTES = 8 * BM * 4;
+  static constexpr int AUX_BYTES = EP_BYTES > RED_BYTES ? EP_BYTES : RED_BYTES;
+};
+
+template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, bool BIAS_GRAD>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_bf16_dma_kernel(MfmaArgs p) {
+  using S = DmaShape<BM, BN>;
+  using TA = DmaTile<BM, A_KMAJ>;
+  using TB = DmaTile<BN, B_KMAJ>;
+  constexpr int WM = S::WM, WN = S::WN, FM = S::FM, FN = S::FN, NS = S::NS;
+  constexpr int A_BYTES = TA::BYTES;
+  constexpr int NDMA = TA::NINST + TB::NINST;              // DMA instructions per wave per stage
+  __shared__ __attribute__((aligned(1024))) char st0[S::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char st1[S::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char st2[NS > 2 ? S::STAGE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char st3[NS > 3 ? S::STAGE_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) char aux[S::AUX_BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  tile_coords(blockIdx.x, (p.M + BM - 1) / BM, (p.N + BN - 1) / BN, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int z = blockIdx.y;
+  const int kbeg = z * p.k_per_split;
+  const int KT = (min(p.K, kbeg + p.k_per_split) - kbeg + kBK - 1) / kBK;
+  const bool do_bias = BIAS_GRAD && tn == 0;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, p.a_bytes), rb = make_rsrc(p.B, p.b_bytes);
+
+  auto stage_ptr = [&](int s) -> GPT2_LDS char* {
+    return (GPT2_LDS char*)(s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : st3);
+  };
+  const typename TA::Lane la = TA::lane_part(wave, lane, m0, p.lda);
+  const typename TB::Lane lb = TB::lane_part(wave, lane, n0, p.ldb);
+  auto issue = [&](int kt, int s) {
+    GPT2_LDS char* base = stage_ptr(s);
+    const int k0 = kbeg + kt * kBK;
+    const bool tail = k0 + kBK > p.K;
+    TA::issue(ra, base, wave, la, k0, p.K, p.lda, tail);
+    TB::issue(rb, base + A_BYTES, wave, lb, k0, p.K, p.ldb, tail);
+  };
+
+  float bsum[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) bsum[e] = 0.f;
+  floatx16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < KT) issue(s, s);
+
+  for (int kt0 = 0; kt0 < KT; kt0 += NS) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int kt = kt0 + s;
+      if (kt < KT) {
+        // stage s of this K step has landed (for this wave), then everyone's has
+        if (kt + NS - 2 < KT) wait_vmcnt<(NS - 2) * NDMA>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        if (kt + NS - 1 < KT) issue(kt + NS - 1, (s + NS - 1) % NS);
+        const GPT2_LDS char* As = stage_ptr(s);
+        const GPT2_LDS char* Bs = As + A_BYTES;
+        if constexpr (BIAS_GRAD) {
+          // column sums of the m-major dY tile: thread t sums k rows 8*(t/32) .. +7 of chunk t%32
+          if (do_bias) {
+            constexpr int CH = BM / 8;
+            for (int u = tid; u < CH * 8; u += kThreads) {
+              const int cc = u % CH, kg = u / CH;
+#pragma unroll
+              for (int r = 0; r < 8; ++r) {
+                const int kr = kg * 8 + r;
+                const int c = cc ^ ((kr & 3) << 1);
+                const bf16x8 v = *reinterpret_cast<const GPT2_LDS bf16x8*>(As + kr * (2 * BM) + c * 16);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) bsum[e] += (float)v[e];
+              }
+            }
+          }
+        }
+        bf16x8 a[2][FM], b[2][FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) a[0][i] = TA::frag(As, wm * WM + i * 32, 0, lane);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) b[0][j] = TB::frag(Bs, wn * WN + j * 32, 0, lane);
+#pragma unroll
+        for (int kk = 0; kk < kBK / 16; ++kk) {
+          if (kk + 1 < kBK / 16) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) a[(kk + 1) & 1][i] = TA::frag(As, wm * WM + i * 32, kk + 1, lane);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) b[(kk + 1) & 1][j] = TB::frag(Bs, wn * WN + j * 32, kk + 1, lane);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][i], b[kk & 1][j], acc[i][j], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  }
+
+  // Epilogue, one 32 x 32 accumulator block at a time through this wave's own
+  // LDS block (LDS operations of one wave complete in order, so no barrier):
+  // element r of lane l sits at row 8(r/4) + 4(l/32) + r%4, column l%32.
+  float* ep = reinterpret_cast<float*>(aux) + wave * 32 * S::EP_PITCH;
+  const int hi = lane >> 5;
+  const bool vec = p.vec_epilogue;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ep[(8 * (r >> 2) + 4 * hi + (r & 3)) * S::EP_PITCH + (lane & 31)] = acc[i][j][r];
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int idx = lane + 64 * q, rl = idx >> 2, cc = idx & 3;
+        const int grow = m0 + wm * WM + i * 32 + rl, gcol = n0 + wn * WN + j * 32 + cc * 8;
+        if (grow < p.M && gcol < p.N) {
+          float v[8];
+          Chunk8<float>::load(ep + rl * S::EP_PITCH + cc * 8, v);
+          if (vec) {
+            epilogue_vec8<EPI>(p.e, grow, gcol, v, z);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (gcol + e < p.N) epilogue_store<EPI, bf16>(p.e, grow, gcol + e, v[e], z);
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+
+  if constexpr (BIAS_GRAD) {
+    if (do_bias) {   // uniform over the block
+      __syncthreads();
+      float* red = reinterpret_cast<float*>(aux);   // [8 k-groups][BM]
+      constexpr int CH = BM / 8;
+      for (int u = tid; u < CH * 8; u += kThreads) {
+        const int cc = u % CH, kg = u / CH;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[kg * BM + cc * 8 + e] = bsum[e];
+      }
+      __syncthreads();
+      for (int m = tid; m < BM; m += kThreads) {
+        float t = 0.f;
+#pragma unroll
+        for (int kg = 0; kg < 8; ++kg) t += red[kg * BM + m];
+        if (m0 + m < p.M) p.e.partial_bias[(size_t)z * p.M + m0 + m] = t;
       }
     }
   }
@@ -370,25 +773,62 @@ __global__ void wgrad_reduce_kernel(const float* __restrict__ partial, int split
 
 // ---------------------------------------------------------------- dispatch
 
-// Number of K splits of a WGRAD GEMM: enough blocks to fill the chip twice.
-int wgrad_splits(int dtype, int M, int N, int K) {
-  if (dtype == F32) return 1;
-  int tiles = (int)(ceil_div64(M, 128) * ceil_div64(N, 128));
-  int kt = (int)ceil_div64(K, kBK);
-  int want = (512 + tiles - 1) / tiles;
-  int s = 1;
-  for (int c = 1; c <= kt && c <= 64; ++c)
-    if (kt % c == 0 && c <= want) s = c;
-  return s;
+// Launch plan of a bf16 GEMM: block tile, and for WGRAD the split of K.
+struct Plan {
+  int bm, bn, splits, k_per_split;
+};
+
+Plan plan_bf16(int epi, int M, int N, int K) {
+  Plan pl;
+  pl.bm = M >= 2048 ? 256 : 128;
+  pl.bn = N >= 2048 ? 256 : 128;
+  const int kt = (int)ceil_div64(K, kBK);
+  pl.splits = 1;
+  if (epi == EPI_WGRAD) {
+    if (M < 2048 && N >= 2048) { pl.bm = 128; pl.bn = 256; }
+    else if (M >= 2048 && N < 2048) { pl.bm = 256; pl.bn = 128; }
+    else if (M < 2048 && N < 2048) { pl.bm = 128; pl.bn = 128; }
+    // choose the split count s minimising  rounds(s) * ceil(kt / s) + alpha * s :
+    // the first term is the critical path in K-steps over the 256 CUs, the
+    // second the fp32 partial-tile traffic of one split expressed in K-steps
+    // (M N 8 bytes at ~5 TB/s against one BM x BN x 64 step at ~6 TFLOP/s per CU).
+    const long tiles = ceil_div64(M, pl.bm) * ceil_div64(N, pl.bn);
+    const double alpha = ((double)M * N * 8.0 / 5e12) / ((double)pl.bm * pl.bn * kBK * 2.0 / 6e12);
+    double best = 1e300;
+    for (int sc = 1; sc <= 64 && sc <= kt; ++sc) {
+      const int kps = (kt + sc - 1) / sc;
+      const int real = (kt + kps - 1) / kps;
+      const double rounds = (double)ceil_div64(tiles * real, 256);
+      const double cost = rounds * kps + alpha * real;
+      if (cost < best - 1e-9) { best = cost; pl.splits = real; }
+    }
+  }
+  const int kps = (kt + pl.splits - 1) / pl.splits;
+  pl.k_per_split = kps * kBK;
+  pl.splits = (kt + kps - 1) / kps;
+  return pl;
 }
 
-template <int EPI, bool A_KMAJ, bool B_KMAJ, bool BIAS_GRAD>
-int launch_mfma(const MfmaArgs& a, int splits, hipStream_t stream) {
-  dim3 grid((unsigned)ceil_div64(a.N, 128), (unsigned)ceil_div64(a.M, 128), (unsigned)splits);
-  hipLaunchKernelGGL((gemm_bf16_mfma_kernel<128, 128, A_KMAJ, B_KMAJ, EPI, BIAS_GRAD>), grid,
+int wgrad_splits(int dtype, int M, int N, int K) {
+  if (dtype == F32) return 1;
+  return plan_bf16(EPI_WGRAD, M, N, K).splits;
+}
+
+template <int BM, int BN, int EPI, bool A_KMAJ, bool B_KMAJ, bool BIAS_GRAD>
+int launch_tile(const MfmaArgs& a, int splits, hipStream_t stream) {
+  const unsigned tiles = (unsigned)(ceil_div64(a.M, BM) * ceil_div64(a.N, BN));
+  hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, A_KMAJ, B_KMAJ, EPI, BIAS_GRAD>), dim3(tiles, splits),
                      dim3(kThreads), 0, stream, a);
   GPT2_LAUNCH_CHECK();
   return 0;
+}
+
+template <int EPI, bool A_KMAJ, bool B_KMAJ, bool BIAS_GRAD>
+int launch_mfma(const MfmaArgs& a, const Plan& pl, hipStream_t stream) {
+  if (pl.bm == 256 && pl.bn == 256) return launch_tile<256, 256, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
+  if (pl.bm == 256 && pl.bn == 128) return launch_tile<256, 128, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
+  if (pl.bm == 128 && pl.bn == 256) return launch_tile<128, 256, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
+  return launch_tile<128, 128, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
 }
 
 template <int EPI, bool A_KMAJ, bool B_KMAJ>
@@ -399,16 +839,25 @@ int launch_simt(const SimtArgs& a, int splits, hipStream_t stream) {
   return 0;
 }
 
+// Instantiated (layout, epilogue) pairs: forward X W^T (k-major both) with the
+// store / bias / residual / GELU epilogues; dX = dY W (B n-major) with store and
+// GELU'; dW = dY^T X (both m/n-major) with the split-K partial epilogue.
 template <int EPI>
-int dispatch_layout_bf16(const GemmDesc& d, const MfmaArgs& a, int splits, bool bias_grad,
-                         hipStream_t s) {
-  if (d.a_kmajor && d.b_kmajor) return launch_mfma<EPI, true, true, false>(a, splits, s);
-  if (d.a_kmajor && !d.b_kmajor) return launch_mfma<EPI, true, false, false>(a, splits, s);
-  if (!d.a_kmajor && !d.b_kmajor) {
-    if (bias_grad) return launch_mfma<EPI, false, false, true>(a, splits, s);
-    return launch_mfma<EPI, false, false, false>(a, splits, s);
+int dispatch_layout_bf16(const GemmDesc& d, const MfmaArgs& a, const Plan& pl, bool bias_grad, hipStream_t s) {
+  if constexpr (EPI == EPI_WGRAD) {
+    if (!d.a_kmajor && !d.b_kmajor) {
+      if (bias_grad) return launch_mfma<EPI, false, false, true>(a, pl, s);
+      return launch_mfma<EPI, false, false, false>(a, pl, s);
+    }
+  } else if constexpr (EPI == EPI_STORE || EPI == EPI_GELU_BWD) {
+    if (d.a_kmajor && !d.b_kmajor) return launch_mfma<EPI, true, false, false>(a, pl, s);
+    if constexpr (EPI == EPI_STORE)
+      if (d.a_kmajor && d.b_kmajor) return launch_mfma<EPI, true, true, false>(a, pl, s);
+  } else {
+    if (d.a_kmajor && d.b_kmajor) return launch_mfma<EPI, true, true, false>(a, pl, s);
   }
-  return gpt2_internal_fail(1, "gemm: layout (A m-major, B k-major) is not instantiated");
+  return gpt2_internal_fail(1, "gemm(bf16): layout (a_kmajor=%d, b_kmajor=%d) not instantiated for epilogue %d",
+                            (int)d.a_kmajor, (int)d.b_kmajor, EPI);
 }
 
 template <int EPI>
@@ -464,19 +913,31 @@ int gemm(const GemmDesc& d, hipStream_t stream) {
       return gpt2_internal_fail(1, "gemm(bf16): m/n-major operand extent not a multiple of 8");
     if (((uintptr_t)d.A | (uintptr_t)d.B) % 16)
       return gpt2_internal_fail(1, "gemm(bf16): A/B not 16-byte aligned");
-    const int kt_total = (int)ceil_div64(d.K, kBK);
+    const Plan pl = plan_bf16(d.epi, d.M, d.N, d.K);
+    auto al16 = [](const void* q) { return ((uintptr_t)q % 16) == 0; };
+    bool vec = d.N % 8 == 0;
+    if (!wgrad) vec = vec && d.ldc % 8 == 0 && al16(d.C);
+    if (d.bias && !wgrad) vec = vec && al16(d.bias);
+    if (d.aux_in) vec = vec && al16(d.aux_in) && d.ld_aux % 8 == 0;
+    if (d.aux_out) vec = vec && al16(d.aux_out);
+    // readable byte extents of the operands (rows x stride); buffer offsets are 32-bit
+    const int64_t a_ext = (d.a_kmajor ? (int64_t)d.M : (int64_t)d.K) * d.lda * 2;
+    const int64_t b_ext = (d.b_kmajor ? (int64_t)d.N : (int64_t)d.K) * d.ldb * 2;
+    if (a_ext >= (int64_t)kOutOfRange || b_ext >= (int64_t)kOutOfRange)
+      return gpt2_internal_fail(1, "gemm(bf16): operand larger than 4 GiB (%lld, %lld bytes)", (long long)a_ext,
+                                (long long)b_ext);
     MfmaArgs a{reinterpret_cast<const bf16*>(d.A), d.lda, reinterpret_cast<const bf16*>(d.B), d.ldb,
-               d.M, d.N, d.K, (kt_total / splits) * kBK, e};
+               (uint32_t)a_ext, (uint32_t)b_ext, d.M, d.N, d.K, pl.k_per_split, vec, e};
     const bool bias_grad = wgrad && d.bias_grad32 != nullptr;
     if (bias_grad && d.a_kmajor)
       return gpt2_internal_fail(1, "gemm: fused bias gradient needs an m-major A");
     switch (d.epi) {
-      case EPI_STORE: rc = dispatch_layout_bf16<EPI_STORE>(d, a, 1, false, stream); break;
-      case EPI_BIAS: rc = dispatch_layout_bf16<EPI_BIAS>(d, a, 1, false, stream); break;
-      case EPI_BIAS_RES: rc = dispatch_layout_bf16<EPI_BIAS_RES>(d, a, 1, false, stream); break;
-      case EPI_BIAS_GELU: rc = dispatch_layout_bf16<EPI_BIAS_GELU>(d, a, 1, false, stream); break;
-      case EPI_GELU_BWD: rc = dispatch_layout_bf16<EPI_GELU_BWD>(d, a, 1, false, stream); break;
-      case EPI_WGRAD: rc = dispatch_layout_bf16<EPI_WGRAD>(d, a, splits, bias_grad, stream); break;
+      case EPI_STORE: rc = dispatch_layout_bf16<EPI_STORE>(d, a, pl, false, stream); break;
+      case EPI_BIAS: rc = dispatch_layout_bf16<EPI_BIAS>(d, a, pl, false, stream); break;
+      case EPI_BIAS_RES: rc = dispatch_layout_bf16<EPI_BIAS_RES>(d, a, pl, false, stream); break;
+      case EPI_BIAS_GELU: rc = dispatch_layout_bf16<EPI_BIAS_GELU>(d, a, pl, false, stream); break;
+      case EPI_GELU_BWD: rc = dispatch_layout_bf16<EPI_GELU_BWD>(d, a, pl, false, stream); break;
+      case EPI_WGRAD: rc = dispatch_layout_bf16<EPI_WGRAD>(d, a, pl, bias_grad, stream); break;
       default: return gpt2_internal_fail(1, "gemm: unknown epilogue %d", d.epi);
     }
     if (rc) return rc;

@@ -8,6 +8,8 @@ never calls it and shares no code with it.
 from .gpt2_oracle import (  # noqa: F401
     OracleConfig,
     param_shapes,
+    linear_forward,
+    linear_backward,
     layernorm_forward,
     layernorm_backward,
     gelu_tanh,

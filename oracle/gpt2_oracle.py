@@ -136,6 +136,19 @@ def gelu_tanh_backward(u, dg):
     return dg * (0.5 * (1.0 + th) + 0.5 * u * (1.0 - th * th) * dkappa)
 
 
+def linear_forward(x, w, b=None):
+    """y = x W^T (+ b) for W stored [out, in]."""
+    y = x @ w.T
+    return y if b is None else y + b
+
+
+def linear_backward(dy, x, w):
+    """Gradients of y = x W^T + b:  dx = dy W,  dW = dy^T x,  db = sum over rows of dy."""
+    dy2 = dy.reshape(-1, dy.shape[-1])
+    x2 = x.reshape(-1, x.shape[-1])
+    return (dy @ w), dy2.T @ x2, dy2.sum(axis=0)
+
+
 def _softmax_rows(s):
     m = s.max(axis=-1, keepdims=True)
     e = np.exp(s - m)

@@ -36,7 +36,9 @@ def rng(seed):
 
 # ---------------------------------------------------------------- GEMM / linear
 
-SHAPES = [(256, 192, 64), (200, 136, 128), (64, 64, 64), (320, 200, 192)]
+# (M, N, K): several tiles with ragged tails in every dimension; M >= 2048 and
+# N >= 2048 select the 256-row / 256-column block tiles.
+SHAPES = [(256, 192, 64), (200, 136, 128), (64, 64, 64), (320, 200, 192), (2104, 2056, 136), (2104, 1000, 264)]
 
 
 @pytest.mark.parametrize("dtype", DT, ids=DTN.get)
@@ -58,6 +60,20 @@ def test_linear_forward(dtype, M, N, K, epi):
     assert rel(host(y), ref) < TOL_OUT[dtype]
     if g is not None:
         assert rel(host(g), O.gelu_tanh(ref)) < TOL_OUT[dtype]
+
+
+@pytest.mark.parametrize("dtype", DT, ids=DTN.get)
+@pytest.mark.parametrize("M,N,K", [(96, 100, 64), (2056, 2052, 72)])
+def test_linear_forward_unaligned_columns(dtype, M, N, K):
+    """N not a multiple of 8: the epilogue falls back to element stores."""
+    say("linear_forward unaligned", DTN[dtype], M, N, K)
+    r = rng(M + N + K)
+    x, W, b, res = r.standard_normal((M, K)), r.standard_normal((N, K)) * 0.1, r.standard_normal(N), \
+        r.standard_normal((M, N))
+    y = empty((M, N), dtype)
+    lib.linear_forward(dtype, dev(x, dtype), dev(W, dtype), b=dev(b, dtype), residual=dev(res, dtype), y=y)
+    xi, Wi, bi, ri = (as_input(a, dtype).astype(np.float64) for a in (x, W, b, res))
+    assert rel(host(y), O.linear_forward(xi, Wi, bi) + ri) < TOL_OUT[dtype]
 
 
 @pytest.mark.parametrize("dtype", DT, ids=DTN.get)
