@@ -35,11 +35,12 @@ CONFIGS = {
     "1.6b": dict(V=50257, Vp=50304, maxT=1024, L=48, H=25, C=1600, B=8, T=1024, lr=2e-4, wd=0.1),
 }
 
-# sites whose launch durations can be timed by the library (include/gpt2.h)
+# kernel sites the library can time (include/gpt2.h); each is one kernel.  The
+# GEMMs and the attention products are bounded by the matrix cores, the rest
+# by HBM bandwidth.
 GEMM_SITES = ["qkv", "attproj", "fc", "fcproj", "logits", "fcproj_dx", "fcproj_dw", "fc_dx", "fc_dw",
               "attproj_dx", "attproj_dw", "qkv_dx", "qkv_dw", "cls_dx", "cls_dw"]
-MFMA_SITES = set(GEMM_SITES)
-ALL_SITES = GEMM_SITES + ["attn_fwd", "attn_bwd", "softmax_xent", "adamw"]
+MFMA_SITES = set(GEMM_SITES) | {"attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq"}
 
 
 def flops_per_token(c) -> float:
@@ -49,9 +50,63 @@ def flops_per_token(c) -> float:
     return 6.0 * N + 12.0 * L * C * c["T"]
 
 
+# kernel that runs at each site for the 124M shapes in bf16 (the name rocprofv3
+# reports, up to its template arguments)
+KERNEL_OF = {
+    "attn_fwd": "attn_fwd_mfma_kernel", "attn_bwd_dkdv": "attn_bwd_dkdv_mfma_kernel",
+    "attn_bwd_dq": "attn_bwd_dq_mfma_kernel", "attn_bwd_dot": "attn_bwd_dot_kernel",
+    "softmax_xent": "softmax_xent_kernel", "ln_fwd": "ln_fwd_kernel", "ln_bwd": "ln_bwd_kernel",
+    "encoder_fwd": "encoder_fwd_kernel", "adamw": "adamw_kernel",
+}
+for _s in GEMM_SITES:
+    KERNEL_OF[_s] = "gemm_bf16_dma_kernel"
+
+
+def roofline_of(site, r):
+    """Roofline position of one timed site: algorithmic work per launch over
+    the average launch duration, against the MI355X dense bf16 or HBM peak."""
+    avg_ms = r["total_ms"] / max(r["launches"], 1)
+    if site in MFMA_SITES:
+        achieved = r["flops_per_launch"] / (avg_ms / 1e3) / 1e12
+        return {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                "frac": achieved / (PEAK_BF16 / 1e12), "algorithmic_per_launch": r["flops_per_launch"],
+                "avg_ms": avg_ms}
+    achieved = r["bytes_per_launch"] / (avg_ms / 1e3) / 1e9
+    return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+            "frac": achieved / (PEAK_HBM / 1e9), "algorithmic_per_launch": r["bytes_per_launch"], "avg_ms": avg_ms}
+
+
+def measured_traffic(site, config):
+    """HBM bytes per launch of the site's kernel from the committed rocprofv3
+    counter summary (FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel), or
+    None when there is none for this site and workload, or when the kernel's
+    source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{site}_{config}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    src = os.path.join(ROOT, kv.get("source", ""))
+    if not os.path.isfile(src):
+        return None
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != kv.get("source_sha256"):
+            return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(c, seed):
     """The CPU oracle (float32 numpy), as it stands, on one sequence of the
-    same workload: one forward + backward + AdamW step at B=1, T=1024."""
+    same workload: one forward + backward + AdamW step on CPU_ROWS rows of
+    T=1024 tokens (a bounded sample of the B=24 batch)."""
     import oracle as O
     from gpt_transformer_lm_amd import synthetic as S
     cores = len(os.sched_getaffinity(0))
@@ -110,16 +165,19 @@ def main():
     t = 0
     for i in range(args.warmup):
         if i == args.warmup - 1:
-            for s in ALL_SITES:
+            for s in lib.SITES:
                 model.timing_enable(s, True)
         t += 1
         step(i, t)
-    site_ms = {}
+    site_ms, sites = {}, {}
     if args.warmup > 0:
-        for s in ALL_SITES:
+        for s in lib.SITES:
             r = model.timing_read(s)
-            site_ms[s] = r["total_ms"]
             model.timing_enable(s, False)
+            if r["launches"] == 0:
+                continue
+            site_ms[s] = r["total_ms"]
+            sites[s] = dict(roofline_of(s, r), ms=r["total_ms"], launches=r["launches"])
     dom = args.site or (max(site_ms, key=site_ms.get) if site_ms else "fc")
     model.timing_enable(dom, True)
 
@@ -142,18 +200,10 @@ def main():
     tok_s = B * T * args.steps / elapsed
     ftok = flops_per_token(c)
     mfu = tok_s * ftok / PEAK_BF16
-    avg_ms = dom_t["total_ms"] / max(dom_t["launches"], 1)
-    if dom in MFMA_SITES or dom.startswith("attn"):
-        achieved = dom_t["flops_per_launch"] / (avg_ms / 1e3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-                "frac": achieved / (PEAK_BF16 / 1e12), "traffic": None}
-    else:
-        achieved = dom_t["bytes_per_launch"] / (avg_ms / 1e3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                "frac": achieved / (PEAK_HBM / 1e9), "traffic": None}
-    roof.update({"kernel_site": dom, "avg_launch_ms": avg_ms, "launches": dom_t["launches"],
-                 "algorithmic_per_launch": dom_t["flops_per_launch"] if roof["bound"] == "mfma"
-                 else dom_t["bytes_per_launch"]})
+    roof = roofline_of(dom, dom_t)
+    roof["traffic"] = measured_traffic(dom, args.config)
+    roof.update({"kernel_site": dom, "kernel": KERNEL_OF.get(dom, dom), "avg_launch_ms": roof.pop("avg_ms"),
+                 "launches": dom_t["launches"]})
 
     out = {
         "metric": METRIC,
@@ -175,6 +225,8 @@ def main():
         "model_flops_per_token": ftok,
         "loss_first_last": [losses[0], losses[-1]] if losses else None,
         "site_ms_one_step": site_ms,
+        "site_roofline_one_step": {k: {"ms": round(v["ms"], 4), "n": v["launches"], "frac": round(v["frac"], 4),
+                                       "bound": v["bound"]} for k, v in sites.items()},
         "gpu_event_ms_per_step": gpu_ms / args.steps,
         "roofline": roof,
     }

@@ -116,9 +116,11 @@ int adamw(int64_t n, float* master, const float* grad, float* m, float* v, bf16*
   const double c1 = 1.0 / (1.0 - pow((double)beta1, (double)t));
   const double c2 = 1.0 / (1.0 - pow((double)beta2, (double)t));
   unsigned grid = (unsigned)std::min<int64_t>(ceil_div64(n, 4 * 256), 8192);
+  mark_begin(0, stream);
   hipLaunchKernelGGL(adamw_kernel, dim3(grid), dim3(256), 0, stream, n, master, grad, m, v, param_bf16, lr, beta1,
                      beta2, eps, wd, (float)c1, (float)c2);
   GPT2_LAUNCH_CHECK();
+  mark_end(0, stream);
   return 0;
 }
 

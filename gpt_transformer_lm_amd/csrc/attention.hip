@@ -255,9 +255,11 @@ __global__ __launch_bounds__(kRows * TPR) void attn_bwd_dkdv_simt(int T_, int H,
 template <typename T, int HD, int TPR>
 int fwd_launch(int B, int T_, int H, const void* qkv, void* out, float* lse, hipStream_t s) {
   dim3 grid((unsigned)ceil_div64(T_, kRows), (unsigned)(B * H));
+  mark_begin(0, s);
   hipLaunchKernelGGL((attn_fwd_simt<T, HD, TPR>), grid, dim3(kRows * TPR), 0, s, T_, H, (const T*)qkv,
                      (T*)out, lse);
   GPT2_LAUNCH_CHECK();
+  mark_end(0, s);
   return 0;
 }
 
@@ -265,12 +267,16 @@ template <typename T, int HD, int TPR>
 int bwd_launch(int B, int T_, int H, const void* qkv, const void* dout, const float* lse, float* D,
                void* dqkv, hipStream_t s) {
   dim3 grid((unsigned)ceil_div64(T_, kRows), (unsigned)(B * H));
+  mark_begin(2, s);
   hipLaunchKernelGGL((attn_bwd_dq_simt<T, HD, TPR>), grid, dim3(kRows * TPR), 0, s, T_, H, (const T*)qkv,
                      (const T*)dout, lse, D, (T*)dqkv);
   GPT2_LAUNCH_CHECK();
+  mark_end(2, s);
+  mark_begin(1, s);
   hipLaunchKernelGGL((attn_bwd_dkdv_simt<T, HD, TPR>), grid, dim3(kRows * TPR), 0, s, T_, H,
                      (const T*)qkv, (const T*)dout, lse, D, (T*)dqkv);
   GPT2_LAUNCH_CHECK();
+  mark_end(1, s);
   return 0;
 }
 
@@ -324,6 +330,7 @@ int attention_backward(int dtype, int B, int T_, int H, int hd, const void* qkv,
     return gpt2_internal_fail(3, "attention_backward: workspace too small");
   float* D = (float*)workspace;
   const int64_t lanes = (int64_t)B * H * T_ * (hd / 8);
+  mark_begin(0, stream);
   if (dtype == BF16) {
     hipLaunchKernelGGL(attn_bwd_dot_kernel<bf16>, dim3((unsigned)ceil_div64(lanes, 256)), dim3(256), 0, stream,
                        B, T_, H, hd, (const bf16*)out, (const bf16*)dout, D);
@@ -332,6 +339,7 @@ int attention_backward(int dtype, int B, int T_, int H, int hd, const void* qkv,
                        stream, B, T_, H, hd, (const float*)out, (const float*)dout, D);
   }
   GPT2_LAUNCH_CHECK();
+  mark_end(0, stream);
   if (attention_mfma_supported(dtype, hd))
     return attention_backward_mfma(B, T_, H, qkv, dout, lse, D, dqkv, stream);
   return dtype == BF16 ? bwd_dispatch<bf16>(B, T_, H, hd, qkv, dout, lse, D, dqkv, stream)

@@ -458,9 +458,11 @@ bool attention_mfma_supported(int dtype, int hd) { return dtype == BF16 && hd ==
 
 int attention_forward_mfma(int B, int T, int H, const void* qkv, void* out, float* lse, hipStream_t stream) {
   dim3 grid((unsigned)ceil_div64(T, ROWS), (unsigned)(B * H));
+  mark_begin(0, stream);
   hipLaunchKernelGGL(attn_fwd_mfma_kernel, grid, dim3(256), 0, stream, T, H, (const bf16*)qkv, (bf16*)out, lse,
                      1.0f / sqrtf((float)HD));
   GPT2_LAUNCH_CHECK();
+  mark_end(0, stream);
   return 0;
 }
 
@@ -468,12 +470,16 @@ int attention_backward_mfma(int B, int T, int H, const void* qkv, const void* do
                             const float* D, void* dqkv, hipStream_t stream) {
   dim3 grid((unsigned)ceil_div64(T, ROWS), (unsigned)(B * H));
   const float scale = 1.0f / sqrtf((float)HD);
+  mark_begin(1, stream);
   hipLaunchKernelGGL(attn_bwd_dkdv_mfma_kernel, grid, dim3(256), 0, stream, T, H, (const bf16*)qkv,
                      (const bf16*)dout, lse, D, (bf16*)dqkv, scale);
   GPT2_LAUNCH_CHECK();
+  mark_end(1, stream);
+  mark_begin(2, stream);
   hipLaunchKernelGGL(attn_bwd_dq_mfma_kernel, grid, dim3(256), 0, stream, T, H, (const bf16*)qkv,
                      (const bf16*)dout, lse, D, (bf16*)dqkv, scale);
   GPT2_LAUNCH_CHECK();
+  mark_end(2, stream);
   return 0;
 }
 

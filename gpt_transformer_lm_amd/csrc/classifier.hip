@@ -123,6 +123,7 @@ int launch_t(int N, int V, int Vp, void* logits, const int32_t* labels, float* l
   const int nch = Vp / 8;
   const int need = (nch + kCeThreads - 1) / kCeThreads;
   T* L = (T*)logits;
+  mark_begin(0, s);
   if (need <= 1)
     hipLaunchKernelGGL((softmax_xent_kernel<T, 1>), dim3(N), dim3(kCeThreads), 0, s, V, Vp, L, labels, losses, dscale);
   else if (need <= 2)
@@ -136,6 +137,7 @@ int launch_t(int N, int V, int Vp, void* logits, const int32_t* labels, float* l
   else
     return gpt2_internal_fail(1, "softmax_xent: Vp=%d too large", Vp);
   GPT2_LAUNCH_CHECK();
+  mark_end(0, s);
   return 0;
 }
 

@@ -174,6 +174,7 @@ int encoder_forward(int dtype, int B, int T_, int C, int vocab_rows, const int32
   if (BT == 0) return 0;
   int64_t total = (int64_t)BT * (C / 8);
   dim3 grid((unsigned)ceil_div64(total, 256));
+  mark_begin(0, stream);
   if (dtype == BF16)
     hipLaunchKernelGGL(encoder_fwd_kernel<bf16>, grid, dim3(256), 0, stream, BT, T_, C, tokens,
                        (const bf16*)wte, (const bf16*)wpe, (bf16*)out, vocab_rows);
@@ -181,6 +182,7 @@ int encoder_forward(int dtype, int B, int T_, int C, int vocab_rows, const int32
     hipLaunchKernelGGL(encoder_fwd_kernel<float>, grid, dim3(256), 0, stream, BT, T_, C, tokens,
                        (const float*)wte, (const float*)wpe, (float*)out, vocab_rows);
   GPT2_LAUNCH_CHECK();
+  mark_end(0, stream);
   return 0;
 }
 

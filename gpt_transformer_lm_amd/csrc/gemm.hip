@@ -9,17 +9,24 @@
 // bias gradient fused into the weight-gradient pass.
 //
 // bf16 kernel (gfx950):
-//   * block tile 128 x 128, K step 64, 256 threads = 4 waves in a 2 x 2
-//     grid, each wave 64 x 64 = 2 x 2 tiles of v_mfma_f32_32x32x16_bf16;
-//   * LDS holds both operands as [row][k] bf16 rows of 64 (128 bytes) with
-//     16-byte chunks XOR-swizzled by row, so the MFMA operand reads
-//     (ds_read_b128, 32 rows per half-wave) are bank-conflict free;
-//   * operands whose K axis is strided in memory (dY^T and X in dW = dY^T X,
-//     W in dX = dY W) are loaded as 16-byte runs along their contiguous axis
-//     and transposed in registers before the LDS store;
-//   * double-buffered LDS: the global loads of step k+1 are in flight while
-//     step k runs on the matrix cores, one barrier per step;
-//   * dW splits K (the B*T positions) over grid.z into fp32 partial tiles that
+//   * block tiles 256x256, 256x128, 128x256 or 128x128 (picked per shape),
+//     K step 64, 256 threads = 4 waves in a 2 x 2 grid; each wave owns a
+//     (BM/2) x (BN/2) patch of v_mfma_f32_32x32x16_bf16 accumulators;
+//   * operand tiles go from global memory straight into LDS with
+//     buffer_load ... lds (no register staging), in a ring of 2-4 stages that
+//     fills the LDS, so several K steps are in flight while the matrix cores
+//     work on the current one; one barrier per K step;
+//   * k-major operands are stored as 128-byte rows with XOR-swizzled 16-byte
+//     chunks and read with ds_read_b128; m-major operands (dY^T and X in
+//     dW = dY^T X, W in dX = dY W) are stored as they lie in memory and read
+//     with the transposing ds_read_b64_tr_b16, so no operand is transposed in
+//     registers;
+//   * the epilogue (bias, residual, GELU and its derivative, bf16 rounding)
+//     goes through a wave-private LDS patch so stores are 16-byte vectors;
+//   * blocks are mapped to tiles XCD by XCD (consecutive blocks land on
+//     different XCDs) and in groups of 8 tile rows so each XCD's L2 sees
+//     reuse;
+//   * dW splits K (the B*T positions) over grid.y into fp32 partial tiles that
 //     a second kernel sums in a fixed order, so results are deterministic.
 // fp32 kernel (parity mode): plain LDS-tiled FMA GEMM with the same epilogues.
 
@@ -82,103 +89,10 @@ struct MfmaArgs {
 // Offset past every operand extent (the host requires extents below it).
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
 
-__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
-  typedef int v4i __attribute__((ext_vector_type(4)));
-  const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
-  return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
-}
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Register staging of one operand tile: R rows (the M or N axis) x 64 k.
-template <int R, bool KMAJ>
-struct Stager {
-  static constexpr int NLD = R / 32;  // 16-byte global loads per thread
-  uint4 r[NLD];
-
-  // rows [row0, row0 + R) of the operand, k in [k0, k0 + 64); rows >= nrows and
-  // k >= K read as 0 (K is a multiple of 8, so a 16-byte run never straddles K).
-  // Buffer loads: an offset past the buffer's extent returns zeros, so
-  // out-of-range elements are steered there instead of branching.
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int row0, int nrows, int k0, int K,
-                                       int tid) {
-    if constexpr (KMAJ) {
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        const int row = row0 + tid / 8 + 32 * i, k = k0 + (tid % 8) * 8;
-        const bool ok = row < nrows && k < K;
-        const uint32_t off = ok ? (uint32_t)(((int64_t)row * ld + k) * 2) : kOutOfRange;
-        r[i] = load16(rs, off);
-      }
-    } else {
-      // unit u: 8 consecutive rows (contiguous in memory) x 4 consecutive k.
-#pragma unroll
-      for (int j = 0; j < R / 128; ++j) {
-        const int u = tid + kThreads * j;
-        const int mc = u % (R / 8), kg = u / (R / 8);
-        const bool okr = row0 + mc * 8 < nrows;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int k = k0 + kg * 4 + i;
-          const uint32_t off = (okr && k < K) ? (uint32_t)(((int64_t)k * ld + row0 + mc * 8) * 2) : kOutOfRange;
-          r[j * 4 + i] = load16(rs, off);
-        }
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(bf16* S, int tid) const {
-    if constexpr (KMAJ) {
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        int row = tid / 8 + 32 * i, c = tid % 8;
-        *reinterpret_cast<uint4*>(S + row * kBK + swz(row, c) * 8) = r[i];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < R / 128; ++j) {
-        int u = tid + kThreads * j;
-        int mc = u % (R / 8), kg = u / (R / 8);
-        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[j * 4 + 0]);
-        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[j * 4 + 1]);
-        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[j * 4 + 2]);
-        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[j * 4 + 3]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          uint32_t lo, hi;
-          if (e % 2 == 0) {  // low halves of dword e/2
-            lo = (w0[e / 2] & 0xffffu) | (w1[e / 2] << 16);
-            hi = (w2[e / 2] & 0xffffu) | (w3[e / 2] << 16);
-          } else {           // high halves
-            lo = (w0[e / 2] >> 16) | (w1[e / 2] & 0xffff0000u);
-            hi = (w2[e / 2] >> 16) | (w3[e / 2] & 0xffff0000u);
-          }
-          int row = mc * 8 + e;
-          *reinterpret_cast<uint2*>(S + row * kBK + swz(row, kg / 2) * 8 + (kg % 2) * 4) =
-              make_uint2(lo, hi);
-        }
-      }
-    }
-  }
-
-  // Adds the staged values of each of this thread's rows into acc (M-major only).
-  __device__ __forceinline__ void accumulate_rows(float* acc) const {
-#pragma unroll
-    for (int j = 0; j < R / 128; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(&r[j * 4 + i]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          acc[j * 8 + e] += (e % 2 == 0) ? __uint_as_float(w[e / 2] << 16)
-                                         : __uint_as_float(w[e / 2] & 0xffff0000u);
-      }
-  }
-};
-
-// Eight consecutive columns n..n+7 of row m (v = fp32 sums); 16-byte accesses.
 template <int EPI>
 __device__ __forceinline__ void epilogue_vec8(const EpiArgs& e, int m, int n, float v[8], int z) {
   if constexpr (EPI == EPI_WGRAD) {
@@ -230,173 +144,12 @@ __device__ __forceinline__ void tile_coords(int bid, int nbm, int nbn, int& tm, 
   tn = r / gsize;
 }
 
-template <int BM, int BN>
-struct MfmaShape {
-  static constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
-  static constexpr int TILE = (BM + BN) * kBK;                 // bf16 elements per stage
-  static constexpr int EP_PITCH = WN + 4;                      // fp32 pitch of the epilogue rows
-  static constexpr int MAIN_BYTES = 2 * TILE * 2;
-  static constexpr int EPI_BYTES = 4 * 32 * EP_PITCH * 4;
-  static constexpr int RED_BYTES = 16 * BM * 4;
-  static constexpr int SMEM = MAIN_BYTES > EPI_BYTES ? (MAIN_BYTES > RED_BYTES ? MAIN_BYTES : RED_BYTES)
-                                                     : (EPI_BYTES > RED_BYTES ? EPI_BYTES : RED_BYTES);
-};
-
-template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, bool BIAS_GRAD>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, (BM == 128 && BN == 128) ? 2 : 1)))
-void gemm_bf16_mfma_kernel(MfmaArgs p) {
-  using S = MfmaShape<BM, BN>;
-  constexpr int WM = S::WM, WN = S::WN, FM = S::FM, FN = S::FN, TILE = S::TILE;
-  __shared__ __attribute__((aligned(16))) char smem_raw[S::SMEM];
-  bf16* smem = reinterpret_cast<bf16*>(smem_raw);
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  int tm, tn;
-  tile_coords(blockIdx.x, (p.M + BM - 1) / BM, (p.N + BN - 1) / BN, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int z = blockIdx.y;
-  const int kbeg = z * p.k_per_split;
-  const int KT = (min(p.K, kbeg + p.k_per_split) - kbeg + kBK - 1) / kBK;
-  const bool do_bias = BIAS_GRAD && tn == 0;
-
-  Stager<BM, A_KMAJ> sa;
-  Stager<BN, B_KMAJ> sb;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, p.a_bytes), rb = make_rsrc(p.B, p.b_bytes);
-  float bsum[BIAS_GRAD ? 8 * (BM / 128) : 1];
-  if constexpr (BIAS_GRAD) {
-#pragma unroll
-    for (int i = 0; i < 8 * (BM / 128); ++i) bsum[i] = 0.f;
-  }
-
-  floatx16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  sa.load(ra, p.lda, m0, p.M, kbeg, p.K, tid);
-  sb.load(rb, p.ldb, n0, p.N, kbeg, p.K, tid);
-  sa.store(smem, tid);
-  sb.store(smem + BM * kBK, tid);
-  if constexpr (BIAS_GRAD) if (do_bias) sa.accumulate_rows(bsum);
-  __syncthreads();
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const bf16* As = smem + (kt & 1) * TILE;
-    const bf16* Bs = As + BM * kBK;
-    const bool more = kt + 1 < KT;
-    if (more) {
-      sa.load(ra, p.lda, m0, p.M, kbeg + (kt + 1) * kBK, p.K, tid);
-      sb.load(rb, p.ldb, n0, p.N, kbeg + (kt + 1) * kBK, p.K, tid);
-    }
-    // operand fragments of k16 step kk+1 are read from LDS while the matrix
-    // cores work on step kk
-    bf16x8 a[2][FM], b[2][FN];
-    auto frags = [&](int kk, bf16x8* fa, bf16x8* fb) {
-      const int c = kk * 2 + (lane >> 5);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int row = wm * WM + i * 32 + (lane & 31);
-        fa[i] = *reinterpret_cast<const bf16x8*>(As + row * kBK + swz(row, c) * 8);
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int row = wn * WN + j * 32 + (lane & 31);
-        fb[j] = *reinterpret_cast<const bf16x8*>(Bs + row * kBK + swz(row, c) * 8);
-      }
-    };
-    frags(0, a[0], b[0]);
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      if (kk + 1 < kBK / 16) frags(kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
-      // keep the reads above the MFMAs of this step (the scheduler would
-      // otherwise sink each read to just before its first use)
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][i], b[kk & 1][j], acc[i][j], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (more) {
-      bf16* An = smem + ((kt + 1) & 1) * TILE;
-      sa.store(An, tid);
-      sb.store(An + BM * kBK, tid);
-      if constexpr (BIAS_GRAD) if (do_bias) sa.accumulate_rows(bsum);
-    }
-    __syncthreads();
-  }
-
-  // Epilogue, one 32-row slab of the wave tile at a time: the accumulators
-  // (element r of lane l of a 32 x 32 tile sits at row 8(r/4) + 4(l/32) + r%4,
-  // column l%32) go to a wave-private LDS block, are read back as runs of 8
-  // columns and leave with 16-byte loads/stores.
-  float* ep = reinterpret_cast<float*>(smem_raw) + wave * 32 * S::EP_PITCH;
-  const int hi = lane >> 5;
-  const bool vec = p.vec_epilogue;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    if (i > 0) __syncthreads();
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        ep[(8 * (r >> 2) + 4 * hi + (r & 3)) * S::EP_PITCH + j * 32 + (lane & 31)] = acc[i][j][r];
-    __syncthreads();
-    const int grow0 = m0 + wm * WM + i * 32, gcol0 = n0 + wn * WN;
-    constexpr int CPR = WN / 8;
-#pragma unroll
-    for (int q = 0; q < (32 * CPR) / 64; ++q) {
-      const int idx = lane + 64 * q;
-      const int rl = idx / CPR, cc = idx % CPR;
-      const int grow = grow0 + rl, gcol = gcol0 + cc * 8;
-      if (grow < p.M && gcol < p.N) {
-        float v[8];
-        Chunk8<float>::load(ep + rl * S::EP_PITCH + cc * 8, v);
-        if (vec) {
-          epilogue_vec8<EPI>(p.e, grow, gcol, v, z);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (gcol + e < p.N) epilogue_store<EPI, bf16>(p.e, grow, gcol + e, v[e], z);
-        }
-      }
-    }
-  }
-
-  if constexpr (BIAS_GRAD) {
-    if (do_bias) {   // uniform over the block (depends on the tile only)
-      __syncthreads();
-      // reduce bsum over the 16 k-groups that share each row chunk
-      float* red = reinterpret_cast<float*>(smem_raw);   // [16][BM]
-#pragma unroll
-      for (int j = 0; j < BM / 128; ++j) {
-        int u = tid + kThreads * j;
-        int mc = u % (BM / 8), kg = u / (BM / 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) red[kg * BM + mc * 8 + e] = bsum[j * 8 + e];
-      }
-      __syncthreads();
-      for (int m = tid; m < BM; m += kThreads) {
-        float s = 0.f;
-#pragma unroll
-        for (int kg = 0; kg < 16; ++kg) s += red[kg * BM + m];
-        if (m0 + m < p.M) p.e.partial_bias[(size_t)z * p.M + m0 + m] = s;
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------- bf16 MFMA, direct-to-LDS
 
 #define GPT2_LDS __attribute__((address_space(3)))
 
-// s_waitcnt immediate that waits for at most n outstanding vector-memory ops
-// (expcnt and lgkmcnt left at their no-wait maxima; gfx9 encoding).
+// s_waitcnt immediate that waits until at most N vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left at their no-wait maxima).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -817,9 +570,11 @@ int wgrad_splits(int dtype, int M, int N, int K) {
 template <int BM, int BN, int EPI, bool A_KMAJ, bool B_KMAJ, bool BIAS_GRAD>
 int launch_tile(const MfmaArgs& a, int splits, hipStream_t stream) {
   const unsigned tiles = (unsigned)(ceil_div64(a.M, BM) * ceil_div64(a.N, BN));
+  mark_begin(0, stream);
   hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, A_KMAJ, B_KMAJ, EPI, BIAS_GRAD>), dim3(tiles, splits),
                      dim3(kThreads), 0, stream, a);
   GPT2_LAUNCH_CHECK();
+  mark_end(0, stream);
   return 0;
 }
 
@@ -834,8 +589,10 @@ int launch_mfma(const MfmaArgs& a, const Plan& pl, hipStream_t stream) {
 template <int EPI, bool A_KMAJ, bool B_KMAJ>
 int launch_simt(const SimtArgs& a, int splits, hipStream_t stream) {
   dim3 grid((unsigned)ceil_div64(a.N, 64), (unsigned)ceil_div64(a.M, 64), (unsigned)splits);
+  mark_begin(0, stream);
   hipLaunchKernelGGL((gemm_f32_simt_kernel<A_KMAJ, B_KMAJ, EPI>), grid, dim3(256), 0, stream, a);
   GPT2_LAUNCH_CHECK();
+  mark_end(0, stream);
   return 0;
 }
 

@@ -8,6 +8,23 @@ namespace gpt2k {
 
 enum DType { F32 = 0, BF16 = 1 };
 
+// ------------------------------------------------------------------ timing marks
+// When armed by the caller (per host thread), a launcher records
+// kernel_marks()[i].begin / .end on its stream immediately before and after
+// its i-th main kernel, so that one event pair brackets exactly one kernel.
+// Null events are skipped.  Used only for timing.
+struct KernelMark {
+  hipEvent_t begin, end;
+};
+constexpr int kMaxMarks = 3;
+KernelMark* kernel_marks();
+inline void mark_begin(int i, hipStream_t s) {
+  if (hipEvent_t e = kernel_marks()[i].begin) (void)hipEventRecord(e, s);
+}
+inline void mark_end(int i, hipStream_t s) {
+  if (hipEvent_t e = kernel_marks()[i].end) (void)hipEventRecord(e, s);
+}
+
 // ------------------------------------------------------------------ GEMM
 //
 // C[M, N] = sum_k A(m, k) * B(n, k)

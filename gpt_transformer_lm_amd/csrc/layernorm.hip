@@ -205,6 +205,7 @@ int fwd_t(int N, int C, const void* x, const void* w, const void* b, void* y, fl
   const T* W = (const T*)w;
   const T* Bb = (const T*)b;
   T* Y = (T*)y;
+  mark_begin(0, s);
   switch (nch_for(C)) {
     case 1: hipLaunchKernelGGL((ln_fwd_kernel<T, 1>), grid, block, 0, s, N, C, X, W, Bb, Y, mean, rstd); break;
     case 2: hipLaunchKernelGGL((ln_fwd_kernel<T, 2>), grid, block, 0, s, N, C, X, W, Bb, Y, mean, rstd); break;
@@ -213,6 +214,7 @@ int fwd_t(int N, int C, const void* x, const void* w, const void* b, void* y, fl
     default: return gpt2_internal_fail(1, "layernorm: C=%d unsupported", C);
   }
   GPT2_LAUNCH_CHECK();
+  mark_end(0, s);
   return 0;
 }
 
@@ -226,6 +228,7 @@ int bwd_t(int N, int C, const void* dy, const void* x, const void* w, const floa
   const T* X = (const T*)x;
   const T* W = (const T*)w;
   T* DC = (T*)dres_copy;
+  mark_begin(0, s);
   switch (nch_for(C)) {
     case 1: hipLaunchKernelGGL((ln_bwd_kernel<T, 1>), grid, block, lds, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
     case 2: hipLaunchKernelGGL((ln_bwd_kernel<T, 2>), grid, block, lds, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
@@ -234,6 +237,7 @@ int bwd_t(int N, int C, const void* dy, const void* x, const void* w, const floa
     default: return gpt2_internal_fail(1, "layernorm: C=%d unsupported", C);
   }
   GPT2_LAUNCH_CHECK();
+  mark_end(0, s);
   return 0;
 }
 

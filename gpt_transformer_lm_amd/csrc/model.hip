@@ -34,6 +34,13 @@ using namespace gpt2k;
 
 static thread_local char g_last_error[1024] = "";
 
+namespace gpt2k {
+KernelMark* kernel_marks() {
+  static thread_local KernelMark marks[kMaxMarks] = {};
+  return marks;
+}
+}  // namespace gpt2k
+
 int gpt2_internal_fail(int status, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -205,10 +212,11 @@ void make_layout(const gpt2_config& c, Layout* lo) {
 
 // ---------------------------------------------------------------- timing sites
 
+// Each site times one kernel: the main kernel of the launcher called there.
 enum Site {
   S_QKV = 0, S_ATTPROJ, S_FC, S_FCPROJ, S_LOGITS, S_FCPROJ_DX, S_FCPROJ_DW, S_FC_DX, S_FC_DW,
-  S_ATTPROJ_DX, S_ATTPROJ_DW, S_QKV_DX, S_QKV_DW, S_CLS_DX, S_CLS_DW, S_ATTN_FWD, S_ATTN_BWD, S_XENT,
-  S_ADAMW, S_COUNT
+  S_ATTPROJ_DX, S_ATTPROJ_DW, S_QKV_DX, S_QKV_DW, S_CLS_DX, S_CLS_DW, S_ATTN_FWD, S_ATTN_DKDV, S_ATTN_DQ,
+  S_ATTN_DOT, S_XENT, S_LN_FWD, S_LN_BWD, S_ENC_FWD, S_ADAMW, S_COUNT
 };
 
 struct SiteTimer {
@@ -257,32 +265,44 @@ struct gpt2_model {
 
 namespace {
 
-int timer_begin(gpt2_model* m, int site) {
+// Points kernel mark `stage` at the next event pair of `site` (if it is being
+// timed and has events left).
+bool timer_arm(gpt2_model* m, int site, int stage) {
   SiteTimer& t = m->timers[site];
-  if (!t.on || t.used + 2 > t.ev.size()) return 0;
-  GPT2_HIP_CHECK(hipEventRecord(t.ev[t.used], m->stream));
-  return 0;
+  if (!t.on || t.used + 2 > t.ev.size()) return false;
+  kernel_marks()[stage] = KernelMark{t.ev[t.used], t.ev[t.used + 1]};
+  return true;
 }
 
-int timer_end(gpt2_model* m, int site, double flops, double bytes) {
+void timer_commit(gpt2_model* m, int site, double flops, double bytes) {
   SiteTimer& t = m->timers[site];
-  if (!t.on || t.used + 2 > t.ev.size()) return 0;
-  GPT2_HIP_CHECK(hipEventRecord(t.ev[t.used + 1], m->stream));
   t.used += 2;
   t.launches++;
   t.flops = flops;
   t.bytes = bytes;
-  return 0;
+}
+
+void marks_clear() {
+  for (int i = 0; i < kMaxMarks; ++i) kernel_marks()[i] = KernelMark{nullptr, nullptr};
+}
+
+// Calls `launch` with the launcher's main kernel timed under `site`;
+// flops / bytes are the algorithmic work of one such kernel.
+template <typename F>
+int timed(gpt2_model* m, int site, double flops, double bytes, F&& launch) {
+  const bool armed = timer_arm(m, site, 0);
+  const int rc = launch();
+  marks_clear();
+  if (armed && rc == 0) timer_commit(m, site, flops, bytes);
+  return rc;
 }
 
 // GEMM wrapper that records the timing site.
 int run_gemm(gpt2_model* m, int site, const GemmDesc& d) {
-  RC(timer_begin(m, site));
-  RC(gemm(d, m->stream));
   const double es = (double)m->es();
-  double bytes = ((double)d.M * d.K + (double)d.N * d.K) * es +
-                 (d.epi == EPI_WGRAD ? (double)d.M * d.N * 4.0 : (double)d.M * d.N * es);
-  return timer_end(m, site, 2.0 * d.M * d.N * d.K, bytes);
+  const double bytes = ((double)d.M * d.K + (double)d.N * d.K) * es +
+                       (d.epi == EPI_WGRAD ? (double)d.M * d.N * 4.0 : (double)d.M * d.N * es);
+  return timed(m, site, 2.0 * d.M * d.N * d.K, bytes, [&] { return gemm(d, m->stream); });
 }
 
 GemmDesc gdesc(int dtype) {
@@ -338,36 +358,47 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets) {
   // keep a copy of the ids for the encoder backward (the caller may reuse its buffer)
   int32_t* tok = m->at<int32_t>(lo.tokens);
   GPT2_HIP_CHECK(hipMemcpyAsync(tok, tokens, (size_t)BT * sizeof(int32_t), hipMemcpyDeviceToDevice, s));
-  RC(encoder_forward(dt, B, T, C, V, tok, m->param(0), m->param(1), m->at<char>(lo.resid[0]), s));
+  const double es = (double)m->es();
+  const double act = (double)BT * C * es;  // bytes of one [BT, C] activation
+  const double ln_fwd_bytes = 2.0 * act + BT * 8.0 + 2.0 * C * es;
+  const double causal_mm = 2.0 * hd * ((double)T * (T + 1) / 2.0) * B * H;  // one causal T x T x hd product
+  RC(timed(m, S_ENC_FWD, 0.0, 3.0 * act, [&] {
+    return encoder_forward(dt, B, T, C, V, tok, m->param(0), m->param(1), m->at<char>(lo.resid[0]), s);
+  }));
   for (int l = 0; l < c.num_layers; ++l) {
     LayerOffsets& o = lo.layer[l];
     void* x = m->at<char>(lo.resid[l]);
-    RC(layernorm_forward(dt, BT, C, x, m->lparam(2, l), m->lparam(3, l), m->at<char>(o.ln1),
-                         m->at<float>(o.ln1_mean), m->at<float>(o.ln1_rstd), s));
+    RC(timed(m, S_LN_FWD, 0.0, ln_fwd_bytes, [&] {
+      return layernorm_forward(dt, BT, C, x, m->lparam(2, l), m->lparam(3, l), m->at<char>(o.ln1),
+                               m->at<float>(o.ln1_mean), m->at<float>(o.ln1_rstd), s);
+    }));
     RC(run_gemm(m, S_QKV, fwd_desc(m, BT, 3 * C, C, m->at<char>(o.ln1), m->lparam(4, l), EPI_BIAS,
                                    m->at<char>(o.qkv), m->lparam(5, l), nullptr, nullptr)));
-    RC(timer_begin(m, S_ATTN_FWD));
-    RC(attention_forward(dt, B, T, H, hd, m->at<char>(o.qkv), m->at<char>(o.atty), m->at<float>(o.lse), s));
-    RC(timer_end(m, S_ATTN_FWD, 4.0 * B * H * hd * (double)T * (T + 1) / 2.0,
-                 (double)BT * 4 * C * m->es() + (double)B * H * T * 4));
+    RC(timed(m, S_ATTN_FWD, 2.0 * causal_mm, 4.0 * act + (double)B * H * T * 4, [&] {
+      return attention_forward(dt, B, T, H, hd, m->at<char>(o.qkv), m->at<char>(o.atty), m->at<float>(o.lse), s);
+    }));
     RC(run_gemm(m, S_ATTPROJ, fwd_desc(m, BT, C, C, m->at<char>(o.atty), m->lparam(6, l), EPI_BIAS_RES,
                                        m->at<char>(o.h), m->lparam(7, l), x, nullptr)));
-    RC(layernorm_forward(dt, BT, C, m->at<char>(o.h), m->lparam(8, l), m->lparam(9, l), m->at<char>(o.ln2),
-                         m->at<float>(o.ln2_mean), m->at<float>(o.ln2_rstd), s));
+    RC(timed(m, S_LN_FWD, 0.0, ln_fwd_bytes, [&] {
+      return layernorm_forward(dt, BT, C, m->at<char>(o.h), m->lparam(8, l), m->lparam(9, l), m->at<char>(o.ln2),
+                               m->at<float>(o.ln2_mean), m->at<float>(o.ln2_rstd), s);
+    }));
     RC(run_gemm(m, S_FC, fwd_desc(m, BT, 4 * C, C, m->at<char>(o.ln2), m->lparam(10, l), EPI_BIAS_GELU,
                                   m->at<char>(o.g), m->lparam(11, l), nullptr, m->at<char>(o.u))));
     RC(run_gemm(m, S_FCPROJ, fwd_desc(m, BT, C, 4 * C, m->at<char>(o.g), m->lparam(12, l), EPI_BIAS_RES,
                                       m->at<char>(lo.resid[l + 1]), m->lparam(13, l), m->at<char>(o.h),
                                       nullptr)));
   }
-  RC(layernorm_forward(dt, BT, C, m->at<char>(lo.resid[c.num_layers]), m->param(14), m->param(15),
-                       m->at<char>(lo.lnf), m->at<float>(lo.lnf_mean), m->at<float>(lo.lnf_rstd), s));
+  RC(timed(m, S_LN_FWD, 0.0, ln_fwd_bytes, [&] {
+    return layernorm_forward(dt, BT, C, m->at<char>(lo.resid[c.num_layers]), m->param(14), m->param(15),
+                             m->at<char>(lo.lnf), m->at<float>(lo.lnf_mean), m->at<float>(lo.lnf_rstd), s);
+  }));
   RC(run_gemm(m, S_LOGITS, fwd_desc(m, BT, Vp, C, m->at<char>(lo.lnf), m->param(0), EPI_STORE,
                                     m->at<char>(lo.logits), nullptr, nullptr, nullptr)));
   if (targets) {
-    RC(timer_begin(m, S_XENT));
-    RC(softmax_xent(dt, BT, V, Vp, m->at<char>(lo.logits), targets, m->at<float>(lo.losses), 1.0f / BT, s));
-    RC(timer_end(m, S_XENT, 0.0, 2.0 * BT * (double)Vp * m->es() + BT * 8.0));
+    RC(timed(m, S_XENT, 0.0, 2.0 * BT * (double)Vp * es + BT * 8.0, [&] {
+      return softmax_xent(dt, BT, V, Vp, m->at<char>(lo.logits), targets, m->at<float>(lo.losses), 1.0f / BT, s);
+    }));
     RC(sum_scaled(BT, m->at<float>(lo.losses), 1.0f / BT, m->at<float>(lo.mean_loss), s));
     m->have_dlogits = true;
   }
@@ -389,13 +420,22 @@ int backward_impl(gpt2_model* m) {
   void* dres_copy = dt == GPT2_BF16 ? dres_t : nullptr;
   void* logits = m->at<char>(lo.logits);
   const size_t sb = lo.scratch_bytes;
+  const double es = (double)m->es();
+  const double act = (double)BT * C * es;
+  const double causal_mm = 2.0 * hd * ((double)T * (T + 1) / 2.0) * B * H;
+  // dy, x read; fp32 residual gradient written (overwrite) or read + written; its copy; stats
+  auto ln_bwd_bytes = [&](bool ovw) {
+    return 2.0 * act + (double)BT * C * (ovw ? 4.0 : 8.0) + (dres_copy ? act : 0.0) + BT * 8.0 + C * es;
+  };
 
   // classifier: d_lnf = dz wte;  d_wte = dz^T lnf (overwrite; padded rows get exactly 0)
   RC(run_gemm(m, S_CLS_DX, dx_desc(m, BT, Vp, C, logits, m->param(0), d_ln, EPI_STORE, nullptr)));
   RC(run_gemm(m, S_CLS_DW, dw_desc(m, BT, Vp, C, logits, m->at<char>(lo.lnf), m->lgrad(0, 0), nullptr, false)));
-  RC(layernorm_backward(dt, BT, C, d_ln, m->at<char>(lo.resid[L]), m->param(14), m->at<float>(lo.lnf_mean),
-                        m->at<float>(lo.lnf_rstd), dres, true, dres_copy, m->lgrad(14, 0), m->lgrad(15, 0), false,
-                        m->scratch(), sb, s));
+  RC(timed(m, S_LN_BWD, 0.0, ln_bwd_bytes(true), [&] {
+    return layernorm_backward(dt, BT, C, d_ln, m->at<char>(lo.resid[L]), m->param(14), m->at<float>(lo.lnf_mean),
+                              m->at<float>(lo.lnf_rstd), dres, true, dres_copy, m->lgrad(14, 0), m->lgrad(15, 0),
+                              false, m->scratch(), sb, s);
+  }));
   for (int l = L - 1; l >= 0; --l) {
     LayerOffsets& o = lo.layer[l];
     // x_{l+1} = h + g Wp^T + bp
@@ -407,25 +447,37 @@ int backward_impl(gpt2_model* m) {
     RC(run_gemm(m, S_FC_DW, dw_desc(m, BT, 4 * C, C, d_big, m->at<char>(o.ln2), m->lgrad(10, l),
                                     m->lgrad(11, l), false)));
     RC(run_gemm(m, S_FC_DX, dx_desc(m, BT, 4 * C, C, d_big, m->lparam(10, l), d_ln, EPI_STORE, nullptr)));
-    RC(layernorm_backward(dt, BT, C, d_ln, m->at<char>(o.h), m->lparam(8, l), m->at<float>(o.ln2_mean),
-                          m->at<float>(o.ln2_rstd), dres, false, dres_copy, m->lgrad(8, l), m->lgrad(9, l), false,
-                          m->scratch(), sb, s));
+    RC(timed(m, S_LN_BWD, 0.0, ln_bwd_bytes(false), [&] {
+      return layernorm_backward(dt, BT, C, d_ln, m->at<char>(o.h), m->lparam(8, l), m->at<float>(o.ln2_mean),
+                                m->at<float>(o.ln2_rstd), dres, false, dres_copy, m->lgrad(8, l), m->lgrad(9, l),
+                                false, m->scratch(), sb, s);
+    }));
     // h = x + atty Wo^T + bo
     RC(run_gemm(m, S_ATTPROJ_DW, dw_desc(m, BT, C, C, dres_t, m->at<char>(o.atty), m->lgrad(6, l),
                                          m->lgrad(7, l), false)));
     RC(run_gemm(m, S_ATTPROJ_DX, dx_desc(m, BT, C, C, dres_t, m->lparam(6, l), d_ln, EPI_STORE, nullptr)));
-    RC(timer_begin(m, S_ATTN_BWD));
-    RC(attention_backward(dt, B, T, H, hd, m->at<char>(o.qkv), m->at<char>(o.atty), d_ln, m->at<float>(o.lse),
-                          d_qkv, m->scratch(), sb, s));
-    RC(timer_end(m, S_ATTN_BWD, 2.5 * 4.0 * B * H * hd * (double)T * (T + 1) / 2.0,
-                 (double)BT * 8 * C * m->es()));
+    {
+      // three kernels: D = rowsum(dO * O); dK, dV (recomputing S and dP); dQ
+      const bool a0 = timer_arm(m, S_ATTN_DOT, 0), a1 = timer_arm(m, S_ATTN_DKDV, 1),
+                 a2 = timer_arm(m, S_ATTN_DQ, 2);
+      const int rc = attention_backward(dt, B, T, H, hd, m->at<char>(o.qkv), m->at<char>(o.atty), d_ln,
+                                        m->at<float>(o.lse), d_qkv, m->scratch(), sb, s);
+      marks_clear();
+      RC(rc);
+      const double lse_b = (double)B * H * T * 4;
+      if (a0) timer_commit(m, S_ATTN_DOT, 0.0, 2.0 * act + lse_b);
+      if (a1) timer_commit(m, S_ATTN_DKDV, 4.0 * causal_mm, 4.0 * act + 2.0 * lse_b + 2.0 * act);
+      if (a2) timer_commit(m, S_ATTN_DQ, 1.0 * causal_mm, 4.0 * act + 2.0 * lse_b + act);
+    }
     // qkv = ln1 Wqkv^T + bqkv
     RC(run_gemm(m, S_QKV_DW, dw_desc(m, BT, 3 * C, C, d_qkv, m->at<char>(o.ln1), m->lgrad(4, l),
                                      m->lgrad(5, l), false)));
     RC(run_gemm(m, S_QKV_DX, dx_desc(m, BT, 3 * C, C, d_qkv, m->lparam(4, l), d_ln, EPI_STORE, nullptr)));
-    RC(layernorm_backward(dt, BT, C, d_ln, m->at<char>(lo.resid[l]), m->lparam(2, l), m->at<float>(o.ln1_mean),
-                          m->at<float>(o.ln1_rstd), dres, false, dres_copy, m->lgrad(2, l), m->lgrad(3, l), false,
-                          m->scratch(), sb, s));
+    RC(timed(m, S_LN_BWD, 0.0, ln_bwd_bytes(false), [&] {
+      return layernorm_backward(dt, BT, C, d_ln, m->at<char>(lo.resid[l]), m->lparam(2, l),
+                                m->at<float>(o.ln1_mean), m->at<float>(o.ln1_rstd), dres, false, dres_copy,
+                                m->lgrad(2, l), m->lgrad(3, l), false, m->scratch(), sb, s);
+    }));
   }
   // encoder: wpe rows >= T get no gradient
   float* dwpe = m->lgrad(1, 0);
@@ -603,11 +655,12 @@ int gpt2_adamw_step(gpt2_model* m, float lr, float beta1, float beta2, float eps
   if (!m) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "adamw: NULL model");
   if (t < 1) return gpt2_internal_fail(GPT2_E_STATE, "adamw: t must be >= 1");
   if (!m->have_grads) return gpt2_internal_fail(GPT2_E_STATE, "adamw needs a completed backward first");
-  RC(timer_begin(m, S_ADAMW));
-  RC(adamw(m->lo.P, m->master(), m->grad(), m->at<float>(m->lo.adam_m), m->at<float>(m->lo.adam_v),
-           m->cfg.dtype == GPT2_BF16 ? m->at<bf16>(m->lo.params_bf16) : nullptr, lr, beta1, beta2, eps, weight_decay,
-           t, m->stream));
-  RC(timer_end(m, S_ADAMW, 0.0, (double)m->lo.P * (m->cfg.dtype == GPT2_BF16 ? 30.0 : 28.0)));
+  // fp32 master, m, v read and written, fp32 gradient read, bf16 copy written
+  RC(timed(m, S_ADAMW, 0.0, (double)m->lo.P * (m->cfg.dtype == GPT2_BF16 ? 30.0 : 28.0), [&] {
+    return adamw(m->lo.P, m->master(), m->grad(), m->at<float>(m->lo.adam_m), m->at<float>(m->lo.adam_v),
+                 m->cfg.dtype == GPT2_BF16 ? m->at<bf16>(m->lo.params_bf16) : nullptr, lr, beta1, beta2, eps,
+                 weight_decay, t, m->stream);
+  }));
   m->have_grads = false;
   return GPT2_OK;
 }

@@ -164,13 +164,17 @@ int gpt2_get_logits(gpt2_model* m, float* host_out);
 
 /* ---- timing hooks ------------------------------------------------------- */
 
-/* Enables (1) or disables (0) HIP-event timing of the launches of one GEMM
- * site inside the step.  site: 0 QKV fwd, 1 attn-proj fwd, 2 fc fwd,
- * 3 fc-proj fwd, 4 logits fwd, 5 fc-proj dX, 6 fc-proj dW, 7 fc dX, 8 fc dW,
- * 9 attn-proj dX, 10 attn-proj dW, 11 QKV dX, 12 QKV dW, 13 classifier dX,
- * 14 classifier dW, 15 attention fwd, 16 attention bwd, 17 softmax-CE,
- * 18 AdamW.  Events are recorded on the model's stream around every launch
- * of that site. */
+/* Enables (1) or disables (0) HIP-event timing of one site of the step.
+ * Every site times exactly one kernel per launch (the main kernel of the
+ * operation there; split-K reductions and column sums are not included):
+ * 0 QKV fwd, 1 attn-proj fwd, 2 fc fwd, 3 fc-proj fwd, 4 logits fwd,
+ * 5 fc-proj dX, 6 fc-proj dW, 7 fc dX, 8 fc dW, 9 attn-proj dX,
+ * 10 attn-proj dW, 11 QKV dX, 12 QKV dW, 13 classifier dX, 14 classifier dW,
+ * 15 attention fwd, 16 attention bwd dK/dV, 17 attention bwd dQ,
+ * 18 attention bwd rowsum(dO*O), 19 softmax-CE, 20 LayerNorm fwd,
+ * 21 LayerNorm bwd, 22 encoder fwd, 23 AdamW.  Events are recorded on the
+ * model's stream immediately around that kernel.  Sites are valid in
+ * [0, 24); others give GPT2_E_INVALID_ARG. */
 int gpt2_timing_enable(gpt2_model* m, int site, int enable);
 /* Total elapsed milliseconds and launch count recorded for a site since it
  * was enabled (synchronises the stream). */
