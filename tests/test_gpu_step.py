@@ -256,3 +256,50 @@ def test_gpt2_124m_full_size():
     say("row-5 per-token loss rel", r, "mean", losses[b].mean(), "oracle", ol[0].mean())
     assert r < 1e-2
     assert abs(losses[b].mean() - ol[0].mean()) < 1e-2 * ol[0].mean()
+
+
+G350 = dict(V=50257, Vp=50304, maxT=1024, L=24, H=16, C_=1024, B=16, T=1024)
+G1600 = dict(V=50257, Vp=50304, maxT=1024, L=48, H=25, C_=1600, B=8, T=1024)
+ADAM_1600 = dict(ADAM_124, lr=2e-4)
+
+
+@pytest.mark.parametrize("name,c,adam,prefix", [("350m", G350, ADAM_124, 64), ("1.6b", G1600, ADAM_1600, 64)],
+                         ids=["350m", "1.6b"])
+def test_large_configs_full_size_and_short_sequence(name, c, adam, prefix):
+    """GPT-2 350M (B=16) and 1.6B (B=8, 25 heads of 64) at T=1024, bf16, on
+    the same seeded parameters:
+      * full batch: per-position losses of a sampled batch row, over its first
+        `prefix` positions, equal the oracle's forward of that prefix (causal:
+        nothing later influences them); finite gradients; padded rows get zero
+        gradient and stay at zero through AdamW;
+      * the same parameters at B=1, T=`prefix` (every layer, full widths):
+        loss, every gradient tensor and the post-AdamW parameters within the
+        bf16 tolerances of the oracle."""
+    say(name, "full size")
+    params = S.random_params(c["V"], c["Vp"], c["maxT"], c["L"], c["C_"], seed=701, perturbed=True)
+    tok, tgt = S.zipf_batch(c["B"], c["T"], seed=702)
+    model, cfg = make(c, BF16)
+    model.set_params(lib.flatten_params(cfg, params))
+    loss = model.forward(dev_i32(tok), dev_i32(tgt))
+    losses = model.get_token_losses().reshape(c["B"], c["T"])
+    model.backward()
+    g = model.get_grads()
+    model.adamw_step(**adam, t=1)
+    after = lib.unflatten(cfg, model.get_params())
+    model.close()
+    say("loss", loss)
+    assert np.isfinite(loss) and np.isfinite(g).all()
+    gd = lib.unflatten(cfg, g)
+    assert np.all(gd["wte"][c["V"]:] == 0) and np.all(after["wte"][c["V"]:] == 0)
+    del g, gd, after
+    b = c["B"] // 2
+    op = to_oracle(params, c, np.float32)
+    _, ol, _, _ = O.gpt2_forward(op, tok[b:b + 1, :prefix], tgt[b:b + 1, :prefix], ocfg(c))
+    r = rel(losses[b, :prefix], ol[0])
+    say("row", b, "prefix per-token loss rel", r)
+    assert r < 1e-2
+    del op
+    say(name, f"B=1 T={prefix} step parity")
+    small = dict(c, B=1, T=prefix)
+    compare_step(small, BF16, params, tok[b:b + 1, :prefix], tgt[b:b + 1, :prefix], adam, np.float32,
+                 gtol=3e-2, ltol=1e-2, ptol=1e-2)
