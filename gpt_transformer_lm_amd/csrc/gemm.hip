@@ -80,6 +80,7 @@ struct MfmaArgs {
   const bf16* A; int64_t lda;
   const bf16* B; int64_t ldb;
   uint32_t a_bytes, b_bytes;   // readable extent of A and B from their base pointers
+  uint32_t aux_bytes;          // readable extent of the epilogue input (R or U), or 0
   int M, N, K;
   int k_per_split;
   bool vec_epilogue;     // every 8-column run is 16-byte aligned and inside N
@@ -93,34 +94,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Stores of the vectorised epilogue, after bias, residual and GELU' have been
+// applied from LDS: WGRAD partials, or U (BIAS_GELU) and C.
 template <int EPI>
-__device__ __forceinline__ void epilogue_vec8(const EpiArgs& e, int m, int n, float v[8], int z) {
+__device__ __forceinline__ void epilogue_vec8_final(const EpiArgs& e, int m, int n, float v[8], int z) {
   if constexpr (EPI == EPI_WGRAD) {
     float* dst = e.partial + ((size_t)z * e.M + m) * (size_t)e.N + n;
     Chunk8<float>::store(dst, v);
   } else {
-    if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_RES || EPI == EPI_BIAS_GELU) {
-      float b[8];
-      Chunk8<bf16>::load(reinterpret_cast<const bf16*>(e.bias) + n, b);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] += b[i];
-    }
-    if constexpr (EPI == EPI_BIAS_RES) {
-      float r[8];
-      Chunk8<bf16>::load(reinterpret_cast<const bf16*>(e.aux_in) + (size_t)m * e.ld_aux + n, r);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] += r[i];
-    }
     if constexpr (EPI == EPI_BIAS_GELU) {
       Chunk8<bf16>::store(reinterpret_cast<bf16*>(e.aux_out) + (size_t)m * e.ldc + n, v);
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = gelu_tanh_f(v[i]);
-    }
-    if constexpr (EPI == EPI_GELU_BWD) {
-      float u[8];
-      Chunk8<bf16>::load(reinterpret_cast<const bf16*>(e.aux_in) + (size_t)m * e.ld_aux + n, u);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] *= gelu_tanh_grad_f(u[i]);
     }
     Chunk8<bf16>::store(reinterpret_cast<bf16*>(e.C) + (size_t)m * e.ldc + n, v);
   }
@@ -281,7 +266,10 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   __shared__ __attribute__((aligned(1024))) char st1[S::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char st2[NS > 2 ? S::STAGE_BYTES : 16];
   __shared__ __attribute__((aligned(1024))) char st3[NS > 3 ? S::STAGE_BYTES : 16];
-  __shared__ __attribute__((aligned(16))) char aux[S::AUX_BYTES];
+  __shared__ __attribute__((aligned(16))) char epi_lds[S::AUX_BYTES];
+  constexpr bool HAS_BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RES || EPI == EPI_BIAS_GELU;
+  constexpr bool HAS_AUX = EPI == EPI_BIAS_RES || EPI == EPI_GELU_BWD;
+  __shared__ __attribute__((aligned(16))) float bias_s[HAS_BIAS ? BN : 4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -306,6 +294,12 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
     TA::issue(ra, base, wave, la, k0, p.K, p.lda, tail);
     TB::issue(rb, base + A_BYTES, wave, lb, k0, p.K, p.ldb, tail);
   };
+
+  // the block's bias columns, read by the epilogue from LDS
+  if constexpr (HAS_BIAS) {
+    for (int c = tid; c < BN; c += kThreads)
+      bias_s[c] = n0 + c < p.N ? (float)reinterpret_cast<const bf16*>(p.e.bias)[n0 + c] : 0.f;
+  }
 
   float bsum[8];
 #pragma unroll
@@ -376,12 +370,36 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
     }
   }
 
+  const bool vec = p.vec_epilogue;
+  // The residual / pre-activation tile the epilogue reads (R or U, [BM][BN]
+  // bf16) is brought into the now idle stage buffers with the same DMA as the
+  // operands: [BM][64]-column sub-tiles with 128-byte swizzled rows, so the
+  // whole tile costs one memory round trip instead of one per output block.
+  constexpr int SUB_BYTES = BM * 128;
+  constexpr int PER_STAGE = S::STAGE_BYTES / SUB_BYTES;
+  static_assert(PER_STAGE >= 1 && (BN / 64 + PER_STAGE - 1) / PER_STAGE <= NS, "aux tile must fit the stages");
+  if constexpr (HAS_BIAS || HAS_AUX) __syncthreads();   // bias visible; every wave done with the stages
+  if constexpr (HAS_AUX) {
+    if (vec) {
+      using TX = DmaTile<BM, true>;
+      const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.e.aux_in, p.aux_bytes);
+      const typename TX::Lane lx = TX::lane_part(wave, lane, m0, p.e.ld_aux);
+#pragma unroll
+      for (int c = 0; c < BN / 64; ++c) {
+        const int c0 = n0 + 64 * c;
+        TX::issue(rx, stage_ptr(c / PER_STAGE) + (c % PER_STAGE) * SUB_BYTES, wave, lx, c0, p.N, p.e.ld_aux,
+                  c0 + 64 > p.N);
+      }
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
+  }
+
   // Epilogue, one 32 x 32 accumulator block at a time through this wave's own
   // LDS block (LDS operations of one wave complete in order, so no barrier):
   // element r of lane l sits at row 8(r/4) + 4(l/32) + r%4, column l%32.
-  float* ep = reinterpret_cast<float*>(aux) + wave * 32 * S::EP_PITCH;
+  float* ep = reinterpret_cast<float*>(epi_lds) + wave * 32 * S::EP_PITCH;
   const int hi = lane >> 5;
-  const bool vec = p.vec_epilogue;
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -397,7 +415,32 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
           float v[8];
           Chunk8<float>::load(ep + rl * S::EP_PITCH + cc * 8, v);
           if (vec) {
-            epilogue_vec8<EPI>(p.e, grow, gcol, v, z);
+            const int tr = wm * WM + i * 32 + rl, tc = wn * WN + j * 32 + cc * 8;
+            if constexpr (HAS_BIAS) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) v[e] += bias_s[tc + e];
+            }
+            if constexpr (HAS_AUX) {
+              const int sb = tc >> 6, ch = (tc & 63) >> 3;
+              const GPT2_LDS char* t = stage_ptr(sb / PER_STAGE) + (sb % PER_STAGE) * SUB_BYTES;
+              typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+              const u32x4 raw = *reinterpret_cast<const GPT2_LDS u32x4*>(t + tr * 128 + swz(tr, ch) * 16);
+              const uint32_t w[4] = {raw[0], raw[1], raw[2], raw[3]};
+              float x[8];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                x[2 * e] = __uint_as_float(w[e] << 16);
+                x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+              }
+              if constexpr (EPI == EPI_BIAS_RES) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] += x[e];
+              } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] *= gelu_tanh_grad_f(x[e]);
+              }
+            }
+            epilogue_vec8_final<EPI>(p.e, grow, gcol, v, z);
           } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
@@ -411,7 +454,7 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   if constexpr (BIAS_GRAD) {
     if (do_bias) {   // uniform over the block
       __syncthreads();
-      float* red = reinterpret_cast<float*>(aux);   // [8 k-groups][BM]
+      float* red = reinterpret_cast<float*>(epi_lds);   // [8 k-groups][BM]
       constexpr int CH = BM / 8;
       for (int u = tid; u < CH * 8; u += kThreads) {
         const int cc = u % CH, kg = u / CH;
@@ -524,47 +567,78 @@ __global__ void wgrad_reduce_kernel(const float* __restrict__ partial, int split
   }
 }
 
+// Split-K of a plain-store GEMM: C[m, n] (bf16, row stride ldc) = sum over
+// the splits of the fp32 partial tiles, in split order.
+__global__ void splitk_store_bf16_kernel(const float* __restrict__ partial, int splits, int M, int N,
+                                         bf16* __restrict__ C, int64_t ldc) {
+  const int64_t MN = (int64_t)M * N;
+  const int64_t i4 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i4 >= MN) return;
+  if ((N % 4) == 0) {
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int z = 0; z < splits; ++z) {
+      const float4 v = *reinterpret_cast<const float4*>(partial + (size_t)z * MN + i4);
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    const int64_t m = i4 / N, n = i4 % N;
+    bf16* dst = C + m * ldc + n;
+    dst[0] = (bf16)s.x; dst[1] = (bf16)s.y; dst[2] = (bf16)s.z; dst[3] = (bf16)s.w;
+  } else {
+    for (int64_t i = i4; i < MN && i < i4 + 4; ++i) {
+      float s = 0.f;
+      for (int z = 0; z < splits; ++z) s += partial[(size_t)z * MN + i];
+      C[(i / N) * ldc + i % N] = (bf16)s;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- dispatch
 
-// Launch plan of a bf16 GEMM: block tile, and for WGRAD the split of K.
+// Launch plan of a bf16 GEMM: block tile and the split of K.
+//
+// The time of a candidate (tile BM x BN, s splits of K) is estimated as
+//   rounds * K-steps per split * t_step(tile)  +  fp32 partial traffic / HBM rate
+// with rounds = ceil(tiles * s / 256 CUs) and t_step the measured time of one
+// 64-deep K step of a tile on one CU (256x256: 2.75 us; 256x128 and 128x256:
+// 1.83 us; 128x128: 1.25 us; the larger tile reads less LDS per MFMA).  WGRAD
+// always goes through fp32 partials (s M N floats written and read, M N
+// written); a plain store is split only when K is long enough for the
+// partials to pay off.  Other epilogues are never split.
 struct Plan {
   int bm, bn, splits, k_per_split;
 };
 
 Plan plan_bf16(int epi, int M, int N, int K) {
-  Plan pl;
-  pl.bm = M >= 2048 ? 256 : 128;
-  pl.bn = N >= 2048 ? 256 : 128;
   const int kt = (int)ceil_div64(K, kBK);
-  pl.splits = 1;
-  if (epi == EPI_WGRAD) {
-    if (M < 2048 && N >= 2048) { pl.bm = 128; pl.bn = 256; }
-    else if (M >= 2048 && N < 2048) { pl.bm = 256; pl.bn = 128; }
-    else if (M < 2048 && N < 2048) { pl.bm = 128; pl.bn = 128; }
-    // choose the split count s minimising  rounds(s) * ceil(kt / s) + alpha * s :
-    // the first term is the critical path in K-steps over the 256 CUs, the
-    // second the fp32 partial-tile traffic of one split expressed in K-steps
-    // (M N 8 bytes at ~5 TB/s against one BM x BN x 64 step at ~6 TFLOP/s per CU).
-    const long tiles = ceil_div64(M, pl.bm) * ceil_div64(N, pl.bn);
-    const double alpha = ((double)M * N * 8.0 / 5e12) / ((double)pl.bm * pl.bn * kBK * 2.0 / 6e12);
-    double best = 1e300;
-    for (int sc = 1; sc <= 64 && sc <= kt; ++sc) {
+  const bool wgrad = epi == EPI_WGRAD;
+  const bool may_split = wgrad || (epi == EPI_STORE && K >= 8192);
+  struct Cand { int bm, bn; double t_step; };
+  const Cand cands[4] = {{256, 256, 2.75e-6}, {256, 128, 1.83e-6}, {128, 256, 1.83e-6}, {128, 128, 1.25e-6}};
+  Plan best{M >= 2048 ? 256 : 128, N >= 2048 ? 256 : 128, 1, 0};
+  double best_t = 1e300;
+  for (const Cand& c : cands) {
+    if (!may_split && (c.bm != best.bm || c.bn != best.bn)) continue;   // fixed tile without splitting
+    const long tiles = ceil_div64(M, c.bm) * ceil_div64(N, c.bn);
+    const double mn4 = (double)M * N * 4.0;
+    for (int sc = 1; sc <= (may_split ? 64 : 1) && sc <= kt; ++sc) {
       const int kps = (kt + sc - 1) / sc;
       const int real = (kt + kps - 1) / kps;
       const double rounds = (double)ceil_div64(tiles * real, 256);
-      const double cost = rounds * kps + alpha * real;
-      if (cost < best - 1e-9) { best = cost; pl.splits = real; }
+      double t = rounds * kps * c.t_step;
+      if (wgrad) t += mn4 * (2.0 * real + 1.0) / 5e12;
+      else if (real > 1) t += (mn4 * 2.0 * real + (double)M * N * 2.0) / 5e12;
+      if (t < best_t * (1.0 - 1e-9)) { best_t = t; best = Plan{c.bm, c.bn, real, 0}; }
     }
   }
-  const int kps = (kt + pl.splits - 1) / pl.splits;
-  pl.k_per_split = kps * kBK;
-  pl.splits = (kt + kps - 1) / kps;
-  return pl;
+  const int kps = (kt + best.splits - 1) / best.splits;
+  best.k_per_split = kps * kBK;
+  best.splits = (kt + kps - 1) / kps;
+  return best;
 }
 
-int wgrad_splits(int dtype, int M, int N, int K) {
+int gemm_splits(int dtype, int epi, int M, int N, int K) {
   if (dtype == F32) return 1;
-  return plan_bf16(EPI_WGRAD, M, N, K).splits;
+  return plan_bf16(epi, M, N, K).splits;
 }
 
 template <int BM, int BN, int EPI, bool A_KMAJ, bool B_KMAJ, bool BIAS_GRAD>
@@ -606,6 +680,8 @@ int dispatch_layout_bf16(const GemmDesc& d, const MfmaArgs& a, const Plan& pl, b
       if (bias_grad) return launch_mfma<EPI, false, false, true>(a, pl, s);
       return launch_mfma<EPI, false, false, false>(a, pl, s);
     }
+    // split-K partials of a plain-store dX = dY W
+    if (d.a_kmajor && !d.b_kmajor && !bias_grad) return launch_mfma<EPI, true, false, false>(a, pl, s);
   } else if constexpr (EPI == EPI_STORE || EPI == EPI_GELU_BWD) {
     if (d.a_kmajor && !d.b_kmajor) return launch_mfma<EPI, true, false, false>(a, pl, s);
     if constexpr (EPI == EPI_STORE)
@@ -628,9 +704,10 @@ int dispatch_layout_f32(const GemmDesc& d, const SimtArgs& a, int splits, hipStr
 }  // namespace
 
 size_t gemm_workspace_bytes(int dtype, int epi, int M, int N, int K) {
-  if (epi != EPI_WGRAD) return 0;
-  int s = wgrad_splits(dtype, M, N, K);
-  return (size_t)s * ((size_t)M * N + (size_t)M) * sizeof(float) + 256;
+  const int s = gemm_splits(dtype, epi, M, N, K);
+  if (epi == EPI_WGRAD) return (size_t)s * ((size_t)M * N + (size_t)M) * sizeof(float) + 256;
+  if (s > 1) return (size_t)s * M * N * sizeof(float) + 256;   // split plain store
+  return 0;
 }
 
 int gemm(const GemmDesc& d, hipStream_t stream) {
@@ -646,13 +723,15 @@ int gemm(const GemmDesc& d, hipStream_t stream) {
     return gpt2_internal_fail(1, "gemm: missing aux input");
   if (d.epi == EPI_BIAS_GELU && !d.aux_out) return gpt2_internal_fail(1, "gemm: missing U output");
 
-  const int splits = wgrad ? wgrad_splits(d.dtype, d.M, d.N, d.K) : 1;
+  const int splits = gemm_splits(d.dtype, d.epi, d.M, d.N, d.K);
+  // a plain store split over K runs the partial-tile kernel, then a reduction into C
+  const bool split_store = !wgrad && splits > 1;
   float* partial = nullptr;
   float* partial_bias = nullptr;
-  if (wgrad) {
+  if (wgrad || split_store) {
     size_t need = gemm_workspace_bytes(d.dtype, d.epi, d.M, d.N, d.K);
     if (!d.workspace || d.workspace_bytes < need)
-      return gpt2_internal_fail(3, "gemm: WGRAD workspace too small (%zu < %zu)", d.workspace_bytes, need);
+      return gpt2_internal_fail(3, "gemm: workspace too small (%zu < %zu)", d.workspace_bytes, need);
     partial = reinterpret_cast<float*>(d.workspace);
     partial_bias = partial + (size_t)splits * d.M * d.N;
   }
@@ -673,7 +752,7 @@ int gemm(const GemmDesc& d, hipStream_t stream) {
     const Plan pl = plan_bf16(d.epi, d.M, d.N, d.K);
     auto al16 = [](const void* q) { return ((uintptr_t)q % 16) == 0; };
     bool vec = d.N % 8 == 0;
-    if (!wgrad) vec = vec && d.ldc % 8 == 0 && al16(d.C);
+    if (!wgrad && !split_store) vec = vec && d.ldc % 8 == 0 && al16(d.C);
     if (d.bias && !wgrad) vec = vec && al16(d.bias);
     if (d.aux_in) vec = vec && al16(d.aux_in) && d.ld_aux % 8 == 0;
     if (d.aux_out) vec = vec && al16(d.aux_out);
@@ -683,12 +762,15 @@ int gemm(const GemmDesc& d, hipStream_t stream) {
     if (a_ext >= (int64_t)kOutOfRange || b_ext >= (int64_t)kOutOfRange)
       return gpt2_internal_fail(1, "gemm(bf16): operand larger than 4 GiB (%lld, %lld bytes)", (long long)a_ext,
                                 (long long)b_ext);
+    const int64_t x_ext = d.aux_in ? (int64_t)d.M * d.ld_aux * 2 : 0;
+    if (x_ext >= (int64_t)kOutOfRange)
+      return gpt2_internal_fail(1, "gemm(bf16): epilogue input larger than 4 GiB (%lld bytes)", (long long)x_ext);
     MfmaArgs a{reinterpret_cast<const bf16*>(d.A), d.lda, reinterpret_cast<const bf16*>(d.B), d.ldb,
-               (uint32_t)a_ext, (uint32_t)b_ext, d.M, d.N, d.K, pl.k_per_split, vec, e};
+               (uint32_t)a_ext, (uint32_t)b_ext, (uint32_t)x_ext, d.M, d.N, d.K, pl.k_per_split, vec, e};
     const bool bias_grad = wgrad && d.bias_grad32 != nullptr;
     if (bias_grad && d.a_kmajor)
       return gpt2_internal_fail(1, "gemm: fused bias gradient needs an m-major A");
-    switch (d.epi) {
+    switch (split_store ? EPI_WGRAD : d.epi) {
       case EPI_STORE: rc = dispatch_layout_bf16<EPI_STORE>(d, a, pl, false, stream); break;
       case EPI_BIAS: rc = dispatch_layout_bf16<EPI_BIAS>(d, a, pl, false, stream); break;
       case EPI_BIAS_RES: rc = dispatch_layout_bf16<EPI_BIAS_RES>(d, a, pl, false, stream); break;
@@ -708,6 +790,11 @@ int gemm(const GemmDesc& d, hipStream_t stream) {
                            stream, partial_bias, splits, (int64_t)d.M, d.bias_grad32, d.accumulate);
         GPT2_LAUNCH_CHECK();
       }
+    }
+    if (split_store) {
+      hipLaunchKernelGGL(splitk_store_bf16_kernel, dim3((unsigned)ceil_div64((int64_t)d.M * d.N, 4 * 256)),
+                         dim3(256), 0, stream, partial, splits, d.M, d.N, reinterpret_cast<bf16*>(d.C), d.ldc);
+      GPT2_LAUNCH_CHECK();
     }
     return 0;
   }

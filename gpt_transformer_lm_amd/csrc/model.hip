@@ -157,6 +157,11 @@ size_t scratch_need(const gpt2_config& c) {
   upd(gemm_workspace_bytes(dt, EPI_WGRAD, 4 * C, C, BT));
   upd(gemm_workspace_bytes(dt, EPI_WGRAD, C, C, BT));
   upd(gemm_workspace_bytes(dt, EPI_WGRAD, 3 * C, C, BT));
+  // dX GEMMs (plain store; long-K ones are split)
+  upd(gemm_workspace_bytes(dt, EPI_STORE, BT, C, Vp));
+  upd(gemm_workspace_bytes(dt, EPI_STORE, BT, C, 4 * C));
+  upd(gemm_workspace_bytes(dt, EPI_STORE, BT, C, 3 * C));
+  upd(gemm_workspace_bytes(dt, EPI_STORE, BT, C, C));
   upd(layernorm_backward_workspace_bytes(BT, C));
   upd(attention_backward_workspace_bytes(c.batch_size, c.seq_len, c.num_heads, C / c.num_heads));
   upd(encoder_backward_workspace_bytes(c.batch_size, c.seq_len, C));
@@ -331,6 +336,7 @@ GemmDesc dx_desc(gpt2_model* m, int M, int N, int K, const void* dy, const void*
   d.M = M; d.N = K; d.K = N;
   d.A = dy; d.lda = N; d.B = W; d.ldb = K;
   d.epi = epi; d.C = dx; d.ldc = K; d.aux_in = gelu_u; d.ld_aux = K;
+  d.workspace = m->scratch(); d.workspace_bytes = m->lo.scratch_bytes;
   return d;
 }
 
@@ -779,7 +785,7 @@ int gpt2_op_linear_forward(int dtype, int M, int N, int K, const void* x, const 
 }
 
 size_t gpt2_op_linear_backward_workspace_bytes(int dtype, int M, int N, int K) {
-  return gemm_workspace_bytes(dtype, EPI_WGRAD, N, K, M);
+  return std::max(gemm_workspace_bytes(dtype, EPI_WGRAD, N, K, M), gemm_workspace_bytes(dtype, EPI_STORE, M, K, N));
 }
 
 int gpt2_op_linear_backward(int dtype, int M, int N, int K, const void* dy, const void* x, const void* W,
@@ -805,6 +811,7 @@ int gpt2_op_linear_backward(int dtype, int M, int N, int K, const void* dy, cons
     d.M = M; d.N = K; d.K = N;
     d.A = dy; d.lda = N; d.B = W; d.ldb = K;
     d.epi = gelu_u ? EPI_GELU_BWD : EPI_STORE; d.C = dx; d.ldc = K; d.aux_in = gelu_u; d.ld_aux = K;
+    d.workspace = workspace; d.workspace_bytes = workspace_bytes;
     RC(gemm(d, s));
   }
   return GPT2_OK;
@@ -847,7 +854,7 @@ int gpt2_op_softmax_xent(int dtype, int N, int V, int Vp, void* logits, const in
 }
 
 size_t gpt2_op_classifier_workspace_bytes(int dtype, int N, int C, int Vp) {
-  return gemm_workspace_bytes(dtype, EPI_WGRAD, Vp, C, N);
+  return gpt2_op_linear_backward_workspace_bytes(dtype, N, Vp, C);
 }
 
 int gpt2_op_classifier_fwd_bwd(int dtype, int N, int C, int V, int Vp, const void* hidden, const void* wte,

@@ -42,7 +42,11 @@ int gpt2_op_linear_forward(int dtype, int M, int N, int K, const void* x, const 
  *       if gelu_u [M, K] T != NULL:  dx = (dy W) * GELU_tanh'(gelu_u)
  *   dW [N, K] f32    = dy^T x   (overwrite, or add if accumulate)
  *   db [N] f32       = sum over rows of dy (or NULL; fused into the dW pass)
- * dW == NULL skips the weight gradient.  bf16: M, N and K multiples of 8. */
+ * dW == NULL skips the weight gradient.  bf16: M, N and K multiples of 8.
+ * workspace: at least gpt2_op_linear_backward_workspace_bytes() bytes of
+ * device scratch (fp32 partial sums of dW over row blocks and, when N is
+ * long, of dx over N blocks; summed in a fixed order, so results are
+ * deterministic); GPT2_E_OOM if it is smaller. */
 size_t gpt2_op_linear_backward_workspace_bytes(int dtype, int M, int N, int K);
 int gpt2_op_linear_backward(int dtype, int M, int N, int K, const void* dy, const void* x,
                             const void* W, const void* gelu_u, void* dx, float* dW, float* db,

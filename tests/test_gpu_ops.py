@@ -38,7 +38,8 @@ def rng(seed):
 
 # (M, N, K): several tiles with ragged tails in every dimension; M >= 2048 and
 # N >= 2048 select the 256-row / 256-column block tiles.
-SHAPES = [(256, 192, 64), (200, 136, 128), (64, 64, 64), (320, 200, 192), (2104, 2056, 136), (2104, 1000, 264)]
+SHAPES = [(256, 192, 64), (200, 136, 128), (64, 64, 64), (320, 200, 192), (2104, 2056, 136), (2104, 1000, 264),
+          (136, 8200, 72)]  # the last one has a long dX reduction (split over N)
 
 
 @pytest.mark.parametrize("dtype", DT, ids=DTN.get)
