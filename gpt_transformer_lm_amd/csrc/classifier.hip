@@ -6,7 +6,8 @@
 // vocabulary to 50304 with the padded logits masked to -inf.  Here each row
 // (one position) is handled by one 1024-thread block that keeps the whole row
 // in registers: one read of the logits gives the row maximum m and the sum
-// s = sum_{j<V} exp(z_j - m) (padded columns j >= V are excluded, i.e. -inf);
+// s = sum_{j<V} exp(z_j - m) (online: per-thread (max, sum) pairs combined in
+// one block reduction; padded columns j >= V are excluded, i.e. -inf);
 // the loss is m + ln s - z_y; then the gradient of the mean loss,
 // (exp(z_j - m) / s - [j == y]) * dscale for j < V and 0 for j >= V, is
 // written over the logits.  HBM traffic: one read and one write of the row.
@@ -19,36 +20,35 @@ namespace {
 constexpr int kCeThreads = 1024;
 constexpr int kCeWaves = kCeThreads / 64;
 
-__device__ __forceinline__ float block_reduce_max(float v, float* sh) {
-  v = wave_max(v);
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) sh[w] = v;
-  __syncthreads();
-  float r = sh[0];
-#pragma unroll
-  for (int i = 1; i < kCeWaves; ++i) r = fmaxf(r, sh[i]);
-  return r;
+// (max, sum of exp(x - max)) pairs of a wave / block, combined so that the
+// sum is rescaled to the larger maximum.
+__device__ __forceinline__ void combine(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  s = (mn == -INFINITY) ? 0.f : s * __expf(m - mn) + s2 * __expf(m2 - mn);
+  m = mn;
 }
 
-__device__ __forceinline__ float block_reduce_sum(float v, float* sh) {
-  v = wave_sum(v);
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) sh[w] = v;
-  __syncthreads();
-  float r = 0.f;
+__device__ __forceinline__ void block_reduce_max_sum(float& m, float& s, float* shm, float* shs) {
 #pragma unroll
-  for (int i = 0; i < kCeWaves; ++i) r += sh[i];
-  return r;
+  for (int o = 32; o > 0; o >>= 1) combine(m, s, __shfl_xor(m, o, 64), __shfl_xor(s, o, 64));
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) { shm[w] = m; shs[w] = s; }
+  __syncthreads();
+  m = shm[0];
+  s = shs[0];
+#pragma unroll
+  for (int i = 1; i < kCeWaves; ++i) combine(m, s, shm[i], shs[i]);
 }
 
-// NC: chunks of 8 columns cached per thread (covers Vp <= NC * 8 * 1024).
+// NC: chunks of 8 columns per thread (covers Vp <= NC * 8 * 1024).  The row is
+// kept in registers in its storage type (bf16: 4 registers per chunk) so that
+// two blocks fit on a compute unit; the exponentials are recomputed for the
+// write.
 template <typename T, int NC>
 __global__ __launch_bounds__(kCeThreads) void softmax_xent_kernel(int V, int Vp, T* __restrict__ logits,
                                                                   const int32_t* __restrict__ labels,
                                                                   float* __restrict__ losses, float dscale) {
-  __shared__ float sh[kCeWaves];
+  __shared__ float shm[kCeWaves], shs[kCeWaves];
   __shared__ float s_zy;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
@@ -57,46 +57,44 @@ __global__ __launch_bounds__(kCeThreads) void softmax_xent_kernel(int V, int Vp,
   y = y < 0 ? 0 : (y >= V ? V - 1 : y);   // memory safety only; valid labels are in [0, V)
   if (tid == 0) s_zy = to_f32(z[y]);
   const int nch = Vp / 8;
-  float v[NC][8];
-  float mx = -INFINITY;
+  typedef T T8 __attribute__((ext_vector_type(8)));
+  T8 raw[NC];
+  // per-thread maximum and sum of exp(z - max) over its columns j < V
+  float mx = -INFINITY, sm = 0.f;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int ch = tid + kCeThreads * c;
     if (ch < nch) {
-      Chunk8<T>::load(z + ch * 8, v[c]);
+      raw[c] = *reinterpret_cast<const T8*>(z + ch * 8);
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (ch * 8 + e < V) mx = fmaxf(mx, v[c][e]);
+        if (ch * 8 + e < V) mx = fmaxf(mx, (float)raw[c][e]);
     }
   }
-  mx = block_reduce_max(mx, sh);
-  float s = 0.f;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int ch = tid + kCeThreads * c;
     if (ch < nch) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float ex = (ch * 8 + e < V) ? __expf(v[c][e] - mx) : 0.f;
-        v[c][e] = ex;
-        s += ex;
-      }
+      for (int e = 0; e < 8; ++e)
+        if (ch * 8 + e < V) sm += __expf((float)raw[c][e] - mx);
     }
   }
-  s = block_reduce_sum(s, sh);   // contains a barrier: s_zy is visible after it
-  if (tid == 0) losses[row] = mx + logf(s) - s_zy;
-  const float inv = dscale / s;
+  block_reduce_max_sum(mx, sm, shm, shs);   // contains a barrier: s_zy is visible after it
+  if (tid == 0) losses[row] = mx + logf(sm) - s_zy;
+  const float inv = dscale / sm;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int ch = tid + kCeThreads * c;
     if (ch < nch) {
-      float o[8];
+      T8 o;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int j = ch * 8 + e;
-        o[e] = (j < V) ? v[c][e] * inv - (j == y ? dscale : 0.f) : 0.f;
+        const float g = (j < V) ? __expf((float)raw[c][e] - mx) * inv - (j == y ? dscale : 0.f) : 0.f;
+        o[e] = (T)g;
       }
-      Chunk8<T>::store(z + ch * 8, o);
+      *reinterpret_cast<T8*>(z + ch * 8) = o;
     }
   }
 }

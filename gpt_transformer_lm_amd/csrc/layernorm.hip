@@ -167,19 +167,30 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(int N, int C, const T* __re
   }
 }
 
-// out[c] (+)= sum over the P partial rows, in a fixed order: a block owns 64
-// columns; its 4 waves sum interleaved quarters of the rows, then combine.
-__global__ __launch_bounds__(256) void column_reduce_kernel(const float* __restrict__ part, int P, int C,
-                                                            float* __restrict__ out, bool accumulate) {
-  __shared__ float sh[4][64];
-  const int c = blockIdx.x * 64 + (threadIdx.x & 63), g = threadIdx.x >> 6;
+// dw[c] (+)= sum over the P partial rows of part_dw, db[c] likewise, in a
+// fixed order.  The 2C output columns (dw then db) are split into blocks of 16;
+// thread (g, c) of a block sums partial rows g, g + 16, ... of its column and
+// the 16 row groups are combined in order.
+__global__ __launch_bounds__(256) void column_reduce_kernel(const float* __restrict__ part_dw,
+                                                            const float* __restrict__ part_db, int P, int C,
+                                                            float* __restrict__ dw, float* __restrict__ db,
+                                                            bool accumulate) {
+  __shared__ float sh[16][17];
+  const int cl = threadIdx.x & 15, g = threadIdx.x >> 4;
+  const int col = blockIdx.x * 16 + cl;
+  const bool is_b = col >= C;
+  const int c = is_b ? col - C : col;
+  const float* part = is_b ? part_db : part_dw;
   float s = 0.f;
-  if (c < C)
-    for (int p = g; p < P; p += 4) s += part[(size_t)p * C + c];
-  sh[g][threadIdx.x & 63] = s;
+  if (col < 2 * C)
+    for (int p = g; p < P; p += 16) s += part[(size_t)p * C + c];
+  sh[g][cl] = s;
   __syncthreads();
-  if (g == 0 && c < C) {
-    const float t = (sh[0][threadIdx.x] + sh[1][threadIdx.x]) + (sh[2][threadIdx.x] + sh[3][threadIdx.x]);
+  if (g == 0 && col < 2 * C) {
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t += sh[i][cl];
+    float* out = is_b ? db : dw;
     out[c] = accumulate ? out[c] + t : t;
   }
 }
@@ -193,8 +204,9 @@ int nch_for(int C) {
   return -1;
 }
 
-// waves of the backward grid (4 per block; each block writes one partial row)
-int bwd_waves(int N) { return (int)std::min<int64_t>(1024, ((int64_t)N + 3) / 4 * 4); }
+// waves of the backward grid (4 per block; each block writes one partial row):
+// enough to keep 4 waves on every SIMD of the 256 compute units
+int bwd_waves(int N) { return (int)std::min<int64_t>(4096, ((int64_t)N + 3) / 4 * 4); }
 int bwd_blocks(int N) { return bwd_waves(N) / 4; }
 
 template <typename T>
@@ -272,11 +284,8 @@ int layernorm_backward(int dtype, int N, int C, const void* dy, const void* x, c
   int rc = dtype == BF16 ? bwd_t<bf16>(N, C, dy, x, w, mean, rstd, dres, dres_overwrite, dres_copy, pdw, pdb, stream)
                          : bwd_t<float>(N, C, dy, x, w, mean, rstd, dres, dres_overwrite, dres_copy, pdw, pdb, stream);
   if (rc) return rc;
-  hipLaunchKernelGGL(column_reduce_kernel, dim3((unsigned)ceil_div64(C, 64)), dim3(256), 0, stream, pdw, P,
-                     C, dw, accumulate);
-  GPT2_LAUNCH_CHECK();
-  hipLaunchKernelGGL(column_reduce_kernel, dim3((unsigned)ceil_div64(C, 64)), dim3(256), 0, stream, pdb, P,
-                     C, db, accumulate);
+  hipLaunchKernelGGL(column_reduce_kernel, dim3((unsigned)ceil_div64(2 * (int64_t)C, 16)), dim3(256), 0, stream,
+                     pdw, pdb, P, C, dw, db, accumulate);
   GPT2_LAUNCH_CHECK();
   return 0;
 }
