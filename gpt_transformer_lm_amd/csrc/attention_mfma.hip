@@ -5,25 +5,32 @@
 // D_i = dO_i . O_i), organised around v_mfma_f32_32x32x16_bf16:
 //
 // Forward: a block owns 128 queries of one (batch, head), 32 per wave; K and
-// V stream through LDS in 64-key stages (double buffered).  Each wave
-// computes S^T = K Q^T per 32-key slice (K from LDS, Q fragments held in
-// registers), so its accumulator holds one query per lane and 16 keys per
-// lane: the running max / sum of the online softmax are per-lane scalars
-// (the two half-waves holding the same query combine with one swizzle), the
-// probabilities P (bf16) are already in the register layout of the B operand
-// of O^T = V^T P^T, and the rescaling of O^T is a per-lane scalar multiply.
-// V is stored transposed in LDS (rows of 64 keys, padded pitch) so that the
-// V^T operand reads are two 8-byte loads per lane.
+// V stream through LDS in 64-key stages.  Each wave computes S^T = K Q^T per
+// 32-key slice (K from LDS, Q fragments held in registers), so its
+// accumulator holds one query per lane and 16 keys per lane: the running max
+// / sum of the online softmax are per-lane scalars (the two half-waves
+// holding the same query combine with one swizzle), the probabilities P
+// (bf16) are already in the register layout of the B operand of
+// O^T = V^T P^T, and the rescaling of O^T is a per-lane scalar multiply.
 //
 // Backward (deterministic, no atomics), two kernels:
 //   dK/dV: a block owns 128 keys (32 per wave) and streams 64-query stages of
-//     Q, dO (natural and transposed), lse and D through LDS; per 32-query
-//     slice: S = Q K^T, dP = dO V^T (K, V fragments in registers, one key per
-//     lane), P = exp(S/sqrt(d) - lse), dS = P (dP - D),
-//     dV^T += dO^T P, dK^T += Q^T dS.
-//   dQ: a block owns 128 queries and streams 64-key stages of K, V and K^T:
+//     Q, dO, lse and D through LDS; per 32-query slice: S = Q K^T,
+//     dP = dO V^T (K, V fragments in registers, one key per lane),
+//     P = exp(S/sqrt(d) - lse), dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS.
+//   dQ: a block owns 128 queries and streams 64-key stages of K and V:
 //     S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
 // Work per causal tile is unbalanced, so blocks take the heaviest tiles first.
+//
+// Streaming: every stage is a set of 64 x 64 bf16 tiles copied global -> LDS
+// with buffer_load ... lds (no register staging) into a ring of NS stages, so
+// NS - 1 stages are in flight while one is computed.  Tiles keep the natural
+// [row][64] layout with XOR-swizzled 16-byte chunks; the transposed operands
+// (V^T, Q^T, dO^T, K^T) are read from the same tiles with ds_read_b64_tr_b16,
+// with per-lane addresses that deliver the keys / queries in exactly the order
+// in which the 32 x 32 accumulator holds them, so P and dS feed the next
+// product without any shuffle.  Rows past the sequence end read as zeros
+// (buffer range check).
 
 #include "kernels.h"
 
@@ -35,9 +42,14 @@ typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int HD = 64;
-constexpr int ROWS = 128;     // queries (fwd, dQ) or keys (dK/dV) per block
-constexpr int STAGE = 64;     // rows streamed per LDS stage
-constexpr int TP = 68;        // pitch (bf16) of transposed LDS tiles: 136 bytes
+constexpr int ROWS = 128;            // queries (fwd, dQ) or keys (dK/dV) per block
+constexpr int STAGE = 64;            // rows streamed per LDS stage
+// Stages in each kernel's LDS ring: as deep as the LDS allows at the
+// occupancy the kernel's registers permit (forward: 4 blocks of 2 x 16 KiB per
+// compute unit; dQ: 3 blocks of 3 x 16 KiB; dK/dV: 2 blocks of 4 x 18 KiB).
+constexpr int NS_FWD = 2, NS_DQ = 3, NS_DKDV = 4;
+constexpr int TILE = STAGE * HD * 2; // bytes of one 64 x 64 bf16 tile
+constexpr uint32_t kOut = 0xFFFFFFF0u;   // offset past every buffer range
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -49,72 +61,59 @@ __device__ __forceinline__ floatx16 mfma(const bf16x8& a, const bf16x8& b, const
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// 64 rows x 64 bf16 of a row-major global matrix (row stride ld) into a
-// swizzled [row][64] LDS tile; rows >= nrows are zero.  256 threads, 2 chunks each.
-struct NaturalTile {
-  uint4 r[2];
-  __device__ __forceinline__ void load(const bf16* G, size_t ld, int row0, int nrows, int tid) {
+// Rows row0 .. row0+63, columns col0 .. col0+63 of a row-major bf16 matrix
+// (row stride ld elements, addressed from the resource's base) into a tile:
+// tile row r occupies bytes 128 r .. 128 r + 127 and its logical 16-byte chunk
+// c sits at physical chunk swz(r, c).  Each of the 4 waves issues 2 of the 8
+// one-KiB instructions (instruction iq fills rows 8 iq .. 8 iq + 7; lane L
+// writes physical chunk L % 8 of row 8 iq + L / 8).
+__device__ __forceinline__ void tile_dma(__amdgpu_buffer_rsrc_t rs, GPT2_LDS char* tile, int wave, int lane,
+                                         int row0, int ld, int col0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = tid / 8 + 32 * i, c = tid % 8;
-      r[i] = (row0 + row < nrows) ? *reinterpret_cast<const uint4*>(G + (size_t)(row0 + row) * ld + c * 8)
-                                  : make_uint4(0, 0, 0, 0);
-    }
+  for (int q = 0; q < 2; ++q) {
+    const int iq = wave * 2 + q;
+    const int r = 8 * iq + (lane >> 3);
+    const int c = (lane & 7) ^ ((r ^ (r >> 3)) & 7);
+    const uint32_t off = (uint32_t)(((int64_t)(row0 + r) * ld + col0 + c * 8) * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (GPT2_LDS void*)(tile + iq * 1024), 16, (int)off, 0, 0, 0);
   }
-  __device__ __forceinline__ void store(bf16* S, int tid) const {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = tid / 8 + 32 * i, c = tid % 8;
-      *reinterpret_cast<uint4*>(S + row * HD + swz(row, c) * 8) = r[i];
-    }
-  }
-};
-
-// The same 64 x 64 block stored transposed: S[d * TP + row].  Each of the 256
-// threads moves 2 rows x 8 columns (two 16-byte loads, eight 4-byte stores;
-// consecutive lanes write consecutive words of a row).
-struct TransposedTile {
-  uint4 r[2];
-  __device__ __forceinline__ void load(const bf16* G, size_t ld, int row0, int nrows, int tid) {
-    const int dc = tid / 32, rp = tid % 32;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = row0 + rp * 2 + i;
-      r[i] = (row < nrows) ? *reinterpret_cast<const uint4*>(G + (size_t)row * ld + dc * 8)
-                           : make_uint4(0, 0, 0, 0);
-    }
-  }
-  __device__ __forceinline__ void store(bf16* S, int tid) const {
-    const int dc = tid / 32, rp = tid % 32;
-    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[0]);
-    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[1]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t v = (e % 2 == 0) ? ((w0[e / 2] & 0xffffu) | (w1[e / 2] << 16))
-                                      : ((w0[e / 2] >> 16) | (w1[e / 2] & 0xffff0000u));
-      *reinterpret_cast<uint32_t*>(S + (dc * 8 + e) * TP + rp * 2) = v;
-    }
-  }
-};
-
-// A-operand fragment of a natural [row][64] tile: row (lane % 32) of the
-// 32-row slice at `row0`, k16 step s.
-__device__ __forceinline__ bf16x8 frag_natural(const bf16* S, int row0, int s, int lane) {
-  const int row = row0 + (lane & 31);
-  return *reinterpret_cast<const bf16x8*>(S + row * HD + swz(row, 2 * s + (lane >> 5)) * 8);
 }
 
-// A-operand fragment of a transposed tile: row d = d0 + lane % 32, columns
-// {c0 + 4*hi + 0..3, c0 + 8 + 4*hi + 0..3} (the key/query order that the
-// 32x32 accumulator uses for its registers 8u..8u+7).
-__device__ __forceinline__ bf16x8 frag_transposed(const bf16* S, int d0, int c0, int lane) {
-  const bf16* p = S + (d0 + (lane & 31)) * TP + c0 + 4 * (lane >> 5);
-  const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
-  const bf16x4 b = *reinterpret_cast<const bf16x4*>(p + 8);
-  bf16x8 r;
-  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
-  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
-  return r;
+// 64 consecutive fp32 values starting at element row0 into the first 256 bytes
+// of a 1-KiB LDS region (lanes 0..15 move 16 bytes each, the others zeros).
+__device__ __forceinline__ void vec_dma(__amdgpu_buffer_rsrc_t rs, GPT2_LDS char* dst, int lane, int row0) {
+  const uint32_t off = lane < 16 ? (uint32_t)((row0 + 4 * lane) * 4) : kOut;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (GPT2_LDS void*)dst, 16, (int)off, 0, 0, 0);
+}
+
+// A-operand fragment, natural orientation: tile row row0 + lane % 32, k16 step s
+// (columns 16 s + 8 (lane / 32) .. +7).
+__device__ __forceinline__ bf16x8 frag_nat(const GPT2_LDS char* t, int row0, int s, int lane) {
+  const int row = row0 + (lane & 31), c = 2 * s + (lane >> 5);
+  return *reinterpret_cast<const GPT2_LDS bf16x8*>(t + row * 128 + swz(row, c) * 16);
+}
+
+// A-operand fragment of the transposed tile: column d0 + lane % 32 as the
+// fragment row, and tile rows {r0 + 4 hi + 0..3, r0 + 8 + 4 hi + 0..3}
+// (hi = lane / 32) as its 8 k values -- the row order of registers 8u..8u+7
+// of a 32 x 32 accumulator.  Two ds_read_b64_tr_b16: within each 16-lane group
+// lane j receives component j % 4 of the 8-byte runs read by lanes j / 4 + 4 e,
+// so lane i of group g reads row r0 + 4 (g / 2) + 8 r + i / 4 at columns
+// d0 + 16 (g % 2) + 4 (i % 4) .. +3.
+__device__ __forceinline__ bf16x8 frag_tr(const GPT2_LDS char* t, int d0, int r0, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int d = d0 + 16 * (g & 1) + 4 * (i & 3);
+  bf16x8 out;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int row = r0 + 4 * (g >> 1) + 8 * r + (i >> 2);
+    const GPT2_LDS bf16x4* p =
+        reinterpret_cast<const GPT2_LDS bf16x4*>(t + row * 128 + swz(row, d >> 3) * 16 + (d & 7) * 2);
+    const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(const_cast<GPT2_LDS bf16x4*>(p));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[4 * r + e] = v[e];
+  }
+  return out;
 }
 
 // Row (lane % 32) of a global [row][64] matrix as four B-operand fragments.
@@ -148,20 +147,20 @@ __device__ __forceinline__ void store_row64(bf16* dst, const floatx16 acc[2], fl
 
 // ------------------------------------------------------------------ forward
 
-__global__ __launch_bounds__(256, 2) void attn_fwd_mfma_kernel(int T, int H, const bf16* __restrict__ qkv,
+__global__ __launch_bounds__(256, 4) void attn_fwd_mfma_kernel(int T, int H, const bf16* __restrict__ qkv,
                                                             bf16* __restrict__ out, float* __restrict__ lse,
                                                             float scale) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][STAGE * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[2][HD * TP];
+  constexpr int NS = NS_FWD;
+  __shared__ __attribute__((aligned(1024))) char ring[NS][2 * TILE];   // K tile, V tile
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hi = lane >> 5;
   const int nqt = (T + ROWS - 1) / ROWS;
   const int qt = nqt - 1 - (int)blockIdx.x;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int C = H * HD;
-  const size_t ld = 3 * (size_t)C;
-  const bf16* Qg = qkv + (size_t)b * T * ld + h * HD;
-  const bf16* Kg = Qg + C;
-  const bf16* Vg = Qg + 2 * C;
+  const int ld = 3 * C;
+  const bf16* Bg = qkv + (size_t)b * T * ld;                 // row 0 of this sequence
+  const bf16* Qg = Bg + h * HD;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(Bg, (uint32_t)((size_t)T * ld * 2));
   const int q0 = qt * ROWS, qw0 = q0 + wave * 32, myq = qw0 + (lane & 31);
   const float sl2 = scale * kLog2e;
 
@@ -176,22 +175,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma_kernel(int T, int H, con
 
   const int kend = min(T, q0 + ROWS);
   const int nst = (kend + STAGE - 1) / STAGE;
-  NaturalTile kt;
-  TransposedTile vt;
-  kt.load(Kg, ld, 0, T, tid);
-  vt.load(Vg, ld, 0, T, tid);
-  kt.store(Ks[0], tid);
-  vt.store(Vt[0], tid);
-  __syncthreads();
+  auto issue = [&](int st) {
+    GPT2_LDS char* base = (GPT2_LDS char*)ring[st % NS];
+    tile_dma(rs, base, wave, lane, st * STAGE, ld, C + h * HD);
+    tile_dma(rs, base + TILE, wave, lane, st * STAGE, ld, 2 * C + h * HD);
+  };
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nst) issue(s);
   for (int st = 0; st < nst; ++st) {
+    // this wave's part of stage st has landed, then everyone's has; the ring
+    // slot refilled next was last read in the previous iteration
+    if (st + NS - 2 < nst) wait_vmcnt<(NS - 2) * 4>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    if (st + NS - 1 < nst) issue(st + NS - 1);
+    const GPT2_LDS char* Kc = (const GPT2_LDS char*)ring[st % NS];
+    const GPT2_LDS char* Vc = Kc + TILE;
     const int k0 = st * STAGE;
-    const bool more = st + 1 < nst;
-    if (more) {
-      kt.load(Kg, ld, k0 + STAGE, T, tid);
-      vt.load(Vg, ld, k0 + STAGE, T, tid);
-    }
-    const bf16* Kc = Ks[st & 1];
-    const bf16* Vc = Vt[st & 1];
 #pragma unroll
     for (int ks = 0; ks < STAGE; ks += 32) {
       const int kb = k0 + ks;
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma_kernel(int T, int H, con
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) s = mfma(frag_natural(Kc, ks, k, lane), qf[k], s);
+        for (int k = 0; k < 4; ++k) s = mfma(frag_nat(Kc, ks, k, lane), qf[k], s);
         const bool edge = (kb + 31 > qw0) || (kb + 32 > T);
         float t[16];
         float mx = -INFINITY;
@@ -216,16 +217,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma_kernel(int T, int H, con
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float m_new = fmaxf(m_i, mx);
         const float alpha = ex2(m_i - m_new);
-        float rs = 0.f;
+        float rs_ = 0.f;
         bf16x8 pb[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = ex2(t[r] - m_new);
-          rs += p;
+          rs_ += p;
           pb[r >> 3][r & 7] = (bf16)p;
         }
-        rs += __shfl_xor(rs, 32, 64);
-        l_i = l_i * alpha + rs;
+        rs_ += __shfl_xor(rs_, 32, 64);
+        l_i = l_i * alpha + rs_;
         m_i = m_new;
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt)
@@ -234,14 +235,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma_kernel(int T, int H, con
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int dt = 0; dt < 2; ++dt) oacc[dt] = mfma(frag_transposed(Vc, dt * 32, ks + 16 * u, lane), pb[u], oacc[dt]);
+          for (int dt = 0; dt < 2; ++dt) oacc[dt] = mfma(frag_tr(Vc, dt * 32, ks + 16 * u, lane), pb[u], oacc[dt]);
       }
     }
-    if (more) {
-      kt.store(Ks[(st + 1) & 1], tid);
-      vt.store(Vt[(st + 1) & 1], tid);
-    }
-    __syncthreads();
   }
   if (myq < T) {
     store_row64(out + ((size_t)b * T + myq) * C + h * HD, oacc, 1.0f / l_i, lane);
@@ -251,31 +247,30 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma_kernel(int T, int H, con
 
 // ------------------------------------------------------------------ backward dK, dV
 
+constexpr int KV_STAGE_BYTES = 2 * TILE + 2048;   // Q tile, dO tile, lse (1 KiB), D (1 KiB)
+
 __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H, const bf16* __restrict__ qkv,
                                                                  const bf16* __restrict__ dout,
                                                                  const float* __restrict__ lse,
                                                                  const float* __restrict__ Dv,
                                                                  bf16* __restrict__ dqkv, float scale) {
-  __shared__ __attribute__((aligned(16))) bf16 Qn[2][STAGE * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Qt[2][HD * TP];
-  __shared__ __attribute__((aligned(16))) bf16 On[2][STAGE * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Ot[2][HD * TP];
-  __shared__ float Ls[2][STAGE], Ds[2][STAGE];
+  constexpr int NS = NS_DKDV;
+  __shared__ __attribute__((aligned(1024))) char ring[NS][KV_STAGE_BYTES];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nkt = (T + ROWS - 1) / ROWS;
   const int ktile = (int)blockIdx.x;           // lower key tiles see more queries: launch them first
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int C = H * HD;
-  const size_t ld = 3 * (size_t)C;
-  const bf16* Qg = qkv + (size_t)b * T * ld + h * HD;
-  const bf16* Kg = Qg + C;
-  const bf16* Vg = Qg + 2 * C;
-  const bf16* Og = dout + (size_t)b * T * C + h * HD;
-  const float* lseg = lse + (size_t)bh * T;
-  const float* Dg = Dv + (size_t)bh * T;
+  const int ld = 3 * C;
+  const bf16* Bg = qkv + (size_t)b * T * ld;
+  const bf16* Kg = Bg + C + h * HD;
+  const bf16* Vg = Bg + 2 * C + h * HD;
+  const bf16* Og = dout + (size_t)b * T * C;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Bg, (uint32_t)((size_t)T * ld * 2));
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(Og, (uint32_t)((size_t)T * C * 2));
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse + (size_t)bh * T, (uint32_t)(T * 4));
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(Dv + (size_t)bh * T, (uint32_t)(T * 4));
   const int k0 = ktile * ROWS, kw0 = k0 + wave * 32, mykey = kw0 + (lane & 31);
   const float sl2 = scale * kLog2e;
-  (void)nkt;
 
   bf16x8 kf[4], vf[4];
   frags_global(Kg, ld, mykey, T, lane, kf);
@@ -287,36 +282,30 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
     for (int r = 0; r < 16; ++r) { dk[dt][r] = 0.f; dv[dt][r] = 0.f; }
 
   const int qbeg = k0;                          // queries before the tile see none of its keys
-  const int nst = (T - qbeg + STAGE - 1) / STAGE;
-  NaturalTile qn, on;
-  TransposedTile qtt, ott;
-  auto load_stage = [&](int q0) {
-    qn.load(Qg, ld, q0, T, tid);
-    on.load(Og, (size_t)C, q0, T, tid);
-    qtt.load(Qg, ld, q0, T, tid);
-    ott.load(Og, (size_t)C, q0, T, tid);
-  };
-  auto store_stage = [&](int buf, int q0) {
-    qn.store(Qn[buf], tid);
-    on.store(On[buf], tid);
-    qtt.store(Qt[buf], tid);
-    ott.store(Ot[buf], tid);
-    if (tid < STAGE) {
-      const int q = q0 + tid;
-      Ls[buf][tid] = q < T ? lseg[q] * kLog2e : 0.f;
-      Ds[buf][tid] = q < T ? Dg[q] : 0.f;
-    }
-  };
-  if (nst > 0) {
-    load_stage(qbeg);
-    store_stage(0, qbeg);
-  }
-  __syncthreads();
-  for (int st = 0; st < nst; ++st) {
+  const int nst = T > qbeg ? (T - qbeg + STAGE - 1) / STAGE : 0;
+  auto issue = [&](int st) {
+    GPT2_LDS char* base = (GPT2_LDS char*)ring[st % NS];
     const int q0 = qbeg + st * STAGE;
-    const bool more = st + 1 < nst;
-    if (more) load_stage(q0 + STAGE);
-    const int buf = st & 1;
+    tile_dma(rq, base, wave, lane, q0, ld, h * HD);
+    tile_dma(ro, base + TILE, wave, lane, q0, C, h * HD);
+    if (wave == 0) vec_dma(rl, base + 2 * TILE, lane, q0);
+    if (wave == 1) vec_dma(rd, base + 2 * TILE + 1024, lane, q0);
+  };
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nst) issue(s);
+  for (int st = 0; st < nst; ++st) {
+    // at most 5 DMA instructions per wave and stage: waiting until (NS - 2) * 4
+    // remain is sufficient for every wave
+    if (st + NS - 2 < nst) wait_vmcnt<(NS - 2) * 4>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    if (st + NS - 1 < nst) issue(st + NS - 1);
+    const GPT2_LDS char* Qs = (const GPT2_LDS char*)ring[st % NS];
+    const GPT2_LDS char* Os = Qs + TILE;
+    const GPT2_LDS float* Ls = reinterpret_cast<const GPT2_LDS float*>(Qs + 2 * TILE);
+    const GPT2_LDS float* Ds = reinterpret_cast<const GPT2_LDS float*>(Qs + 2 * TILE + 1024);
+    const int q0 = qbeg + st * STAGE;
 #pragma unroll
     for (int qs = 0; qs < STAGE; qs += 32) {
       const int qb = q0 + qs;
@@ -326,8 +315,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
         for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          s = mfma(frag_natural(Qn[buf], qs, k, lane), kf[k], s);
-          dp = mfma(frag_natural(On[buf], qs, k, lane), vf[k], dp);
+          s = mfma(frag_nat(Qs, qs, k, lane), kf[k], s);
+          dp = mfma(frag_nat(Os, qs, k, lane), vf[k], dp);
         }
         // s[r]: query qb + acc_row(r), key mykey
         const bool edge = (qb < kw0 + 31) || (qb + 32 > T);
@@ -335,9 +324,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int ql = qs + acc_row(r, lane);
-          float p = ex2(s[r] * sl2 - Ls[buf][ql]);
+          float p = ex2(s[r] * sl2 - Ls[ql] * kLog2e);
           if (edge && (mykey > qb + acc_row(r, lane) || qb + acc_row(r, lane) >= T)) p = 0.f;
-          const float ds = p * (dp[r] - Ds[buf][ql]);
+          const float ds = p * (dp[r] - Ds[ql]);
           pb[r >> 3][r & 7] = (bf16)p;
           db[r >> 3][r & 7] = (bf16)ds;
         }
@@ -345,13 +334,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int dt = 0; dt < 2; ++dt) {
-            dv[dt] = mfma(frag_transposed(Ot[buf], dt * 32, qs + 16 * u, lane), pb[u], dv[dt]);
-            dk[dt] = mfma(frag_transposed(Qt[buf], dt * 32, qs + 16 * u, lane), db[u], dk[dt]);
+            dv[dt] = mfma(frag_tr(Os, dt * 32, qs + 16 * u, lane), pb[u], dv[dt]);
+            dk[dt] = mfma(frag_tr(Qs, dt * 32, qs + 16 * u, lane), db[u], dk[dt]);
           }
       }
     }
-    if (more) store_stage(buf ^ 1, q0 + STAGE);
-    __syncthreads();
   }
   if (mykey < T) {
     bf16* dst = dqkv + ((size_t)b * T + mykey) * ld + h * HD;
@@ -362,24 +349,23 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
 
 // ------------------------------------------------------------------ backward dQ
 
-__global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma_kernel(int T, int H, const bf16* __restrict__ qkv,
+__global__ __launch_bounds__(256, 3) void attn_bwd_dq_mfma_kernel(int T, int H, const bf16* __restrict__ qkv,
                                                                const bf16* __restrict__ dout,
                                                                const float* __restrict__ lse,
                                                                const float* __restrict__ Dv,
                                                                bf16* __restrict__ dqkv, float scale) {
-  __shared__ __attribute__((aligned(16))) bf16 Kn[2][STAGE * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Vn[2][STAGE * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Kt[2][HD * TP];
+  constexpr int NS = NS_DQ;
+  __shared__ __attribute__((aligned(1024))) char ring[NS][2 * TILE];   // K tile, V tile
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nqt = (T + ROWS - 1) / ROWS;
   const int qt = nqt - 1 - (int)blockIdx.x;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int C = H * HD;
-  const size_t ld = 3 * (size_t)C;
-  const bf16* Qg = qkv + (size_t)b * T * ld + h * HD;
-  const bf16* Kg = Qg + C;
-  const bf16* Vg = Qg + 2 * C;
+  const int ld = 3 * C;
+  const bf16* Bg = qkv + (size_t)b * T * ld;
+  const bf16* Qg = Bg + h * HD;
   const bf16* Og = dout + (size_t)b * T * C + h * HD;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(Bg, (uint32_t)((size_t)T * ld * 2));
   const int q0 = qt * ROWS, qw0 = q0 + wave * 32, myq = qw0 + (lane & 31);
   const float sl2 = scale * kLog2e;
 
@@ -396,24 +382,22 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma_kernel(int T, int H, 
 
   const int kend = min(T, q0 + ROWS);
   const int nst = (kend + STAGE - 1) / STAGE;
-  NaturalTile kn, vn;
-  TransposedTile ktt;
-  kn.load(Kg, ld, 0, T, tid);
-  vn.load(Vg, ld, 0, T, tid);
-  ktt.load(Kg, ld, 0, T, tid);
-  kn.store(Kn[0], tid);
-  vn.store(Vn[0], tid);
-  ktt.store(Kt[0], tid);
-  __syncthreads();
+  auto issue = [&](int st) {
+    GPT2_LDS char* base = (GPT2_LDS char*)ring[st % NS];
+    tile_dma(rs, base, wave, lane, st * STAGE, ld, C + h * HD);
+    tile_dma(rs, base + TILE, wave, lane, st * STAGE, ld, 2 * C + h * HD);
+  };
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nst) issue(s);
   for (int st = 0; st < nst; ++st) {
+    if (st + NS - 2 < nst) wait_vmcnt<(NS - 2) * 4>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    if (st + NS - 1 < nst) issue(st + NS - 1);
+    const GPT2_LDS char* Ks = (const GPT2_LDS char*)ring[st % NS];
+    const GPT2_LDS char* Vs = Ks + TILE;
     const int k0 = st * STAGE;
-    const bool more = st + 1 < nst;
-    if (more) {
-      kn.load(Kg, ld, k0 + STAGE, T, tid);
-      vn.load(Vg, ld, k0 + STAGE, T, tid);
-      ktt.load(Kg, ld, k0 + STAGE, T, tid);
-    }
-    const int buf = st & 1;
 #pragma unroll
     for (int ks = 0; ks < STAGE; ks += 32) {
       const int kb = k0 + ks;
@@ -423,8 +407,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma_kernel(int T, int H, 
         for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          s = mfma(frag_natural(Kn[buf], ks, k, lane), qf[k], s);
-          dp = mfma(frag_natural(Vn[buf], ks, k, lane), of[k], dp);
+          s = mfma(frag_nat(Ks, ks, k, lane), qf[k], s);
+          dp = mfma(frag_nat(Vs, ks, k, lane), of[k], dp);
         }
         // s[r]: key kb + acc_row(r), query myq
         const bool edge = (kb + 31 > qw0) || (kb + 32 > T);
@@ -439,15 +423,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma_kernel(int T, int H, 
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int dt = 0; dt < 2; ++dt) dq[dt] = mfma(frag_transposed(Kt[buf], dt * 32, ks + 16 * u, lane), db[u], dq[dt]);
+          for (int dt = 0; dt < 2; ++dt) dq[dt] = mfma(frag_tr(Ks, dt * 32, ks + 16 * u, lane), db[u], dq[dt]);
       }
     }
-    if (more) {
-      kn.store(Kn[buf ^ 1], tid);
-      vn.store(Vn[buf ^ 1], tid);
-      ktt.store(Kt[buf ^ 1], tid);
-    }
-    __syncthreads();
   }
   if (myq < T) store_row64(dqkv + ((size_t)b * T + myq) * ld + h * HD, dq, scale, lane);
 }

@@ -106,6 +106,25 @@ __device__ __forceinline__ float gelu_tanh_grad_f(float u) {
 
 // ---------------------------------------------------------------- host side
 
+// ---------------------------------------------------------------- gfx950 memory helpers
+
+// LDS address space (direct-to-LDS loads and LDS-only reads take such pointers).
+#define GPT2_LDS __attribute__((address_space(3)))
+
+// Buffer resource over `bytes` bytes from `base`: loads at offsets at or beyond
+// `bytes` return zeros (and direct-to-LDS loads write zeros).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// s_waitcnt immediate that waits until at most N vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 #define GPT2_HIP_CHECK(expr)                                  \
   do {                                                        \
     hipError_t _e = (expr);                                   \

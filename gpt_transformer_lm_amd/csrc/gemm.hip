@@ -90,10 +90,6 @@ struct MfmaArgs {
 // Offset past every operand extent (the host requires extents below it).
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
 // Stores of the vectorised epilogue, after bias, residual and GELU' have been
 // applied from LDS: WGRAD partials, or U (BIAS_GELU) and C.
 template <int EPI>
@@ -131,15 +127,6 @@ __device__ __forceinline__ void tile_coords(int bid, int nbm, int nbn, int& tm, 
 
 // ---------------------------------------------------------------- bf16 MFMA, direct-to-LDS
 
-#define GPT2_LDS __attribute__((address_space(3)))
-
-// s_waitcnt immediate that waits until at most N vector-memory operations of
-// this wave are outstanding (expcnt and lgkmcnt left at their no-wait maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
 
 // Operand tile in LDS, R rows of the operand's M (or N) axis x 64 k, filled by
 // buffer_load ... lds (each wave instruction writes 1 KiB, 16 bytes per lane,
