@@ -100,6 +100,36 @@ __global__ void init_normal_kernel(int64_t n, float* __restrict__ dst, uint64_t 
   dst[e] = (float)(stddev * z);
 }
 
+// dst[b][c][r] = src[b][r][c] for a batch of bf16 matrices [R, Cc] (R and Cc
+// multiples of 8): 64 x 64 tiles through LDS, 16-byte global loads and stores.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16* __restrict__ src, bf16* __restrict__ dst,
+                                                             int R, int Cc) {
+  typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  __shared__ __attribute__((aligned(16))) bf16 tile[64][72];   // 144-byte rows
+  const size_t mat = (size_t)R * Cc * blockIdx.z;
+  const bf16* S = src + mat;
+  bf16* D = dst + mat;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  for (int i = threadIdx.x; i < 512; i += 256) {
+    const int r = i >> 3, cc = (i & 7) * 8;
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (bf16)0.f;
+    if (r0 + r < R && c0 + cc < Cc) v = *reinterpret_cast<const bf16x8*>(S + (size_t)(r0 + r) * Cc + c0 + cc);
+    *reinterpret_cast<bf16x8*>(&tile[r][cc]) = v;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 512; i += 256) {
+    const int c = i >> 3, rr = (i & 7) * 8;
+    if (c0 + c < Cc && r0 + rr < R) {
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = tile[rr + e][c];
+      *reinterpret_cast<bf16x8*>(D + (size_t)(c0 + c) * R + r0 + rr) = o;
+    }
+  }
+}
+
 unsigned blocks_for(int64_t n, int per_thread = 1) {
   return (unsigned)ceil_div64(ceil_div64(n, per_thread), 256);
 }
@@ -128,6 +158,18 @@ int cast_f32_to_bf16(int64_t n, const float* src, bf16* dst, hipStream_t stream)
   if (n <= 0) return 0;
   hipLaunchKernelGGL(cast_kernel, dim3(blocks_for(n)), dim3(256), 0, stream, n, src, dst);
   GPT2_LAUNCH_CHECK();
+  return 0;
+}
+
+int transpose_bf16(int batches, int R, int Cc, const bf16* src, bf16* dst, hipStream_t stream) {
+  if (batches < 0 || R < 0 || Cc < 0 || (R % 8) || (Cc % 8) || !src || !dst)
+    return gpt2_internal_fail(1, "transpose_bf16: bad arguments (R=%d, C=%d must be multiples of 8)", R, Cc);
+  if (batches == 0 || R == 0 || Cc == 0) return 0;
+  dim3 grid((unsigned)ceil_div64(Cc, 64), (unsigned)ceil_div64(R, 64), (unsigned)batches);
+  mark_begin(0, stream);
+  hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, stream, src, dst, R, Cc);
+  GPT2_LAUNCH_CHECK();
+  mark_end(0, stream);
   return 0;
 }
 

@@ -229,21 +229,35 @@ struct DmaTile {
   }
 };
 
-template <int BM, int BN>
+// Block-tile geometry and LDS budget.  The stage ring is as deep as 160 KiB
+// allows; the epilogue's staging (and the bias-gradient reduction) goes into
+// the last stage buffer when the epilogue input tile (HAS_AUX) leaves it free,
+// else into an array of its own.
+template <int BM, int BN, bool HAS_AUX>
 struct DmaShape {
   static constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
   static constexpr int STAGE_BYTES = (BM + BN) * kBK * 2;
-  static constexpr int NS = STAGE_BYTES * 4 <= 160 * 1024 - 20 * 1024 ? 4 : STAGE_BYTES * 3 <= 160 * 1024 - 20 * 1024 ? 3 : 2;
   static constexpr int EP_PITCH = 36;                     // fp32 pitch of a 32 x 32 epilogue block
   static constexpr int EP_BYTES = 4 * 32 * EP_PITCH * 4;  // one block per wave
   static constexpr int RED_BYTES = 8 * BM * 4;
   static constexpr int AUX_BYTES = EP_BYTES > RED_BYTES ? EP_BYTES : RED_BYTES;
+  static constexpr int SUB_BYTES = BM * 128;              // [BM][64] bf16 sub-tile of the epilogue input
+  static constexpr int PER_STAGE = STAGE_BYTES / SUB_BYTES;
+  static constexpr int AUX_STAGES = HAS_AUX ? (BN / 64 + PER_STAGE - 1) / PER_STAGE : 0;
+  static constexpr int LDS_LIMIT = 160 * 1024 - BN * 4 - 1024;
+  static constexpr bool fits(int n) {
+    return AUX_STAGES <= n && n * STAGE_BYTES + (AUX_STAGES < n ? 0 : AUX_BYTES) <= LDS_LIMIT;
+  }
+  static constexpr int NS = fits(4) ? 4 : fits(3) ? 3 : 2;
+  static constexpr bool EPI_IN_STAGE = AUX_STAGES < NS && AUX_BYTES <= STAGE_BYTES;
 };
 
 template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, bool BIAS_GRAD>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_dma_kernel(MfmaArgs p) {
-  using S = DmaShape<BM, BN>;
+  constexpr bool HAS_BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RES || EPI == EPI_BIAS_GELU;
+  constexpr bool HAS_AUX = EPI == EPI_BIAS_RES || EPI == EPI_GELU_BWD;
+  using S = DmaShape<BM, BN, HAS_AUX>;
   using TA = DmaTile<BM, A_KMAJ>;
   using TB = DmaTile<BN, B_KMAJ>;
   constexpr int WM = S::WM, WN = S::WN, FM = S::FM, FN = S::FN, NS = S::NS;
@@ -253,9 +267,7 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   __shared__ __attribute__((aligned(1024))) char st1[S::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char st2[NS > 2 ? S::STAGE_BYTES : 16];
   __shared__ __attribute__((aligned(1024))) char st3[NS > 3 ? S::STAGE_BYTES : 16];
-  __shared__ __attribute__((aligned(16))) char epi_lds[S::AUX_BYTES];
-  constexpr bool HAS_BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RES || EPI == EPI_BIAS_GELU;
-  constexpr bool HAS_AUX = EPI == EPI_BIAS_RES || EPI == EPI_GELU_BWD;
+  __shared__ __attribute__((aligned(16))) char epi_own[S::EPI_IN_STAGE ? 16 : S::AUX_BYTES];
   __shared__ __attribute__((aligned(16))) float bias_s[HAS_BIAS ? BN : 4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -362,10 +374,12 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   // bf16) is brought into the now idle stage buffers with the same DMA as the
   // operands: [BM][64]-column sub-tiles with 128-byte swizzled rows, so the
   // whole tile costs one memory round trip instead of one per output block.
-  constexpr int SUB_BYTES = BM * 128;
-  constexpr int PER_STAGE = S::STAGE_BYTES / SUB_BYTES;
-  static_assert(PER_STAGE >= 1 && (BN / 64 + PER_STAGE - 1) / PER_STAGE <= NS, "aux tile must fit the stages");
-  if constexpr (HAS_BIAS || HAS_AUX) __syncthreads();   // bias visible; every wave done with the stages
+  constexpr int SUB_BYTES = S::SUB_BYTES;
+  constexpr int PER_STAGE = S::PER_STAGE;
+  static_assert(PER_STAGE >= 1 && S::AUX_STAGES <= NS, "aux tile must fit the stages");
+  // bias visible; every wave done with the stage buffers that are reused below
+  if constexpr (HAS_BIAS || HAS_AUX || S::EPI_IN_STAGE) __syncthreads();
+  GPT2_LDS char* epi_lds = S::EPI_IN_STAGE ? stage_ptr(NS - 1) : (GPT2_LDS char*)epi_own;
   if constexpr (HAS_AUX) {
     if (vec) {
       using TX = DmaTile<BM, true>;
@@ -385,7 +399,7 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   // Epilogue, one 32 x 32 accumulator block at a time through this wave's own
   // LDS block (LDS operations of one wave complete in order, so no barrier):
   // element r of lane l sits at row 8(r/4) + 4(l/32) + r%4, column l%32.
-  float* ep = reinterpret_cast<float*>(epi_lds) + wave * 32 * S::EP_PITCH;
+  GPT2_LDS float* ep = reinterpret_cast<GPT2_LDS float*>(epi_lds) + wave * 32 * S::EP_PITCH;
   const int hi = lane >> 5;
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -400,7 +414,13 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
         const int grow = m0 + wm * WM + i * 32 + rl, gcol = n0 + wn * WN + j * 32 + cc * 8;
         if (grow < p.M && gcol < p.N) {
           float v[8];
-          Chunk8<float>::load(ep + rl * S::EP_PITCH + cc * 8, v);
+          {
+            typedef float f32x4 __attribute__((ext_vector_type(4)));
+            const GPT2_LDS f32x4* q = reinterpret_cast<const GPT2_LDS f32x4*>(ep + rl * S::EP_PITCH + cc * 8);
+            const f32x4 lo = q[0], hi4 = q[1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { v[e] = lo[e]; v[4 + e] = hi4[e]; }
+          }
           if (vec) {
             const int tr = wm * WM + i * 32 + rl, tc = wn * WN + j * 32 + cc * 8;
             if constexpr (HAS_BIAS) {
@@ -441,7 +461,7 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   if constexpr (BIAS_GRAD) {
     if (do_bias) {   // uniform over the block
       __syncthreads();
-      float* red = reinterpret_cast<float*>(epi_lds);   // [8 k-groups][BM]
+      GPT2_LDS float* red = reinterpret_cast<GPT2_LDS float*>(epi_lds);   // [8 k-groups][BM]
       constexpr int CH = BM / 8;
       for (int u = tid; u < CH * 8; u += kThreads) {
         const int cc = u % CH, kg = u / CH;
@@ -587,24 +607,31 @@ __global__ void splitk_store_bf16_kernel(const float* __restrict__ partial, int 
 //   rounds * K-steps per split * t_step(tile)  +  fp32 partial traffic / HBM rate
 // with rounds = ceil(tiles * s / 256 CUs) and t_step the measured time of one
 // 64-deep K step of a tile on one CU (256x256: 2.75 us; 256x128 and 128x256:
-// 1.83 us; 128x128: 1.25 us; the larger tile reads less LDS per MFMA).  WGRAD
-// always goes through fp32 partials (s M N floats written and read, M N
-// written); a plain store is split only when K is long enough for the
-// partials to pay off.  Other epilogues are never split.
+// 1.83 us; 192x192: 1.95 us; 128x128: 1.25 us; the larger tile reads less LDS
+// per MFMA).  WGRAD always goes through fp32 partials (s M N floats written
+// and read, M N written); a plain store is split only when K is long enough
+// for the partials to pay off.  Other epilogues are never split and choose
+// between the default tile and 192x192 (both operands k-major only), which
+// tiles M = 24576, N = 768 into exactly two rounds.
 struct Plan {
   int bm, bn, splits, k_per_split;
 };
 
-Plan plan_bf16(int epi, int M, int N, int K) {
+Plan plan_bf16(int epi, int M, int N, int K, bool a_kmajor, bool b_kmajor) {
   const int kt = (int)ceil_div64(K, kBK);
   const bool wgrad = epi == EPI_WGRAD;
   const bool may_split = wgrad || (epi == EPI_STORE && K >= 8192);
   struct Cand { int bm, bn; double t_step; };
-  const Cand cands[4] = {{256, 256, 2.75e-6}, {256, 128, 1.83e-6}, {128, 256, 1.83e-6}, {128, 128, 1.25e-6}};
-  Plan best{M >= 2048 ? 256 : 128, N >= 2048 ? 256 : 128, 1, 0};
+  const Cand cands[5] = {{256, 256, 2.75e-6}, {256, 128, 1.83e-6}, {128, 256, 1.83e-6}, {128, 128, 1.25e-6},
+                         {192, 192, 1.95e-6}};
+  const int def_bm = M >= 2048 ? 256 : 128, def_bn = N >= 2048 ? 256 : 128;
+  Plan best{def_bm, def_bn, 1, 0};
   double best_t = 1e300;
   for (const Cand& c : cands) {
-    if (!may_split && (c.bm != best.bm || c.bn != best.bn)) continue;   // fixed tile without splitting
+    const bool c192 = c.bm == 192;
+    if (c192 && !(a_kmajor && b_kmajor)) continue;                  // m-major DMA needs 64 | 1024 / (2 R)
+    if (!may_split && !c192 && (c.bm != def_bm || c.bn != def_bn)) continue;
+    if (c192 && (M < 2048 || N < 192)) continue;
     const long tiles = ceil_div64(M, c.bm) * ceil_div64(N, c.bn);
     const double mn4 = (double)M * N * 4.0;
     for (int sc = 1; sc <= (may_split ? 64 : 1) && sc <= kt; ++sc) {
@@ -623,9 +650,9 @@ Plan plan_bf16(int epi, int M, int N, int K) {
   return best;
 }
 
-int gemm_splits(int dtype, int epi, int M, int N, int K) {
+int gemm_splits(int dtype, int epi, int M, int N, int K, bool a_kmajor, bool b_kmajor) {
   if (dtype == F32) return 1;
-  return plan_bf16(epi, M, N, K).splits;
+  return plan_bf16(epi, M, N, K, a_kmajor, b_kmajor).splits;
 }
 
 template <int BM, int BN, int EPI, bool A_KMAJ, bool B_KMAJ, bool BIAS_GRAD>
@@ -644,6 +671,8 @@ int launch_mfma(const MfmaArgs& a, const Plan& pl, hipStream_t stream) {
   if (pl.bm == 256 && pl.bn == 256) return launch_tile<256, 256, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
   if (pl.bm == 256 && pl.bn == 128) return launch_tile<256, 128, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
   if (pl.bm == 128 && pl.bn == 256) return launch_tile<128, 256, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
+  if constexpr (A_KMAJ && B_KMAJ)
+    if (pl.bm == 192 && pl.bn == 192) return launch_tile<192, 192, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
   return launch_tile<128, 128, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
 }
 
@@ -667,12 +696,12 @@ int dispatch_layout_bf16(const GemmDesc& d, const MfmaArgs& a, const Plan& pl, b
       if (bias_grad) return launch_mfma<EPI, false, false, true>(a, pl, s);
       return launch_mfma<EPI, false, false, false>(a, pl, s);
     }
-    // split-K partials of a plain-store dX = dY W
+    // split-K partials of a plain-store dX = dY W (W n-major, or its k-major transpose)
     if (d.a_kmajor && !d.b_kmajor && !bias_grad) return launch_mfma<EPI, true, false, false>(a, pl, s);
+    if (d.a_kmajor && d.b_kmajor && !bias_grad) return launch_mfma<EPI, true, true, false>(a, pl, s);
   } else if constexpr (EPI == EPI_STORE || EPI == EPI_GELU_BWD) {
     if (d.a_kmajor && !d.b_kmajor) return launch_mfma<EPI, true, false, false>(a, pl, s);
-    if constexpr (EPI == EPI_STORE)
-      if (d.a_kmajor && d.b_kmajor) return launch_mfma<EPI, true, true, false>(a, pl, s);
+    if (d.a_kmajor && d.b_kmajor) return launch_mfma<EPI, true, true, false>(a, pl, s);
   } else {
     if (d.a_kmajor && d.b_kmajor) return launch_mfma<EPI, true, true, false>(a, pl, s);
   }
@@ -690,8 +719,8 @@ int dispatch_layout_f32(const GemmDesc& d, const SimtArgs& a, int splits, hipStr
 
 }  // namespace
 
-size_t gemm_workspace_bytes(int dtype, int epi, int M, int N, int K) {
-  const int s = gemm_splits(dtype, epi, M, N, K);
+size_t gemm_workspace_bytes(int dtype, int epi, int M, int N, int K, bool a_kmajor, bool b_kmajor) {
+  const int s = gemm_splits(dtype, epi, M, N, K, a_kmajor, b_kmajor);
   if (epi == EPI_WGRAD) return (size_t)s * ((size_t)M * N + (size_t)M) * sizeof(float) + 256;
   if (s > 1) return (size_t)s * M * N * sizeof(float) + 256;   // split plain store
   return 0;
@@ -710,13 +739,13 @@ int gemm(const GemmDesc& d, hipStream_t stream) {
     return gpt2_internal_fail(1, "gemm: missing aux input");
   if (d.epi == EPI_BIAS_GELU && !d.aux_out) return gpt2_internal_fail(1, "gemm: missing U output");
 
-  const int splits = gemm_splits(d.dtype, d.epi, d.M, d.N, d.K);
+  const int splits = gemm_splits(d.dtype, d.epi, d.M, d.N, d.K, d.a_kmajor, d.b_kmajor);
   // a plain store split over K runs the partial-tile kernel, then a reduction into C
   const bool split_store = !wgrad && splits > 1;
   float* partial = nullptr;
   float* partial_bias = nullptr;
   if (wgrad || split_store) {
-    size_t need = gemm_workspace_bytes(d.dtype, d.epi, d.M, d.N, d.K);
+    size_t need = gemm_workspace_bytes(d.dtype, d.epi, d.M, d.N, d.K, d.a_kmajor, d.b_kmajor);
     if (!d.workspace || d.workspace_bytes < need)
       return gpt2_internal_fail(3, "gemm: workspace too small (%zu < %zu)", d.workspace_bytes, need);
     partial = reinterpret_cast<float*>(d.workspace);
@@ -736,7 +765,7 @@ int gemm(const GemmDesc& d, hipStream_t stream) {
       return gpt2_internal_fail(1, "gemm(bf16): m/n-major operand extent not a multiple of 8");
     if (((uintptr_t)d.A | (uintptr_t)d.B) % 16)
       return gpt2_internal_fail(1, "gemm(bf16): A/B not 16-byte aligned");
-    const Plan pl = plan_bf16(d.epi, d.M, d.N, d.K);
+    const Plan pl = plan_bf16(d.epi, d.M, d.N, d.K, d.a_kmajor, d.b_kmajor);
     auto al16 = [](const void* q) { return ((uintptr_t)q % 16) == 0; };
     bool vec = d.N % 8 == 0;
     if (!wgrad && !split_store) vec = vec && d.ldc % 8 == 0 && al16(d.C);

@@ -62,7 +62,7 @@ struct GemmDesc {
 };
 
 // Device bytes of scratch a GEMM with this descriptor needs (WGRAD only).
-size_t gemm_workspace_bytes(int dtype, int epi, int M, int N, int K);
+size_t gemm_workspace_bytes(int dtype, int epi, int M, int N, int K, bool a_kmajor, bool b_kmajor);
 int gemm(const GemmDesc& d, hipStream_t stream);
 
 // ------------------------------------------------------------------ LayerNorm
@@ -120,6 +120,8 @@ int adamw(int64_t n, float* master, const float* grad, float* m, float* v, bf16*
           float lr, float beta1, float beta2, float eps, float wd, int t, hipStream_t stream);
 // dst = RNE bf16 of src.
 int cast_f32_to_bf16(int64_t n, const float* src, bf16* dst, hipStream_t stream);
+// dst[b][c][r] = src[b][r][c] for `batches` bf16 matrices [R, Cc]; R, Cc multiples of 8.
+int transpose_bf16(int batches, int R, int Cc, const bf16* src, bf16* dst, hipStream_t stream);
 // Seeded GPT-2-style normal init of one tensor (see gpt2.h).
 int init_normal(int64_t n, float* dst, uint64_t seed, int tensor_index, double stddev,
                 hipStream_t stream);

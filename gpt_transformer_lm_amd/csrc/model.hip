@@ -64,6 +64,11 @@ int gpt2_internal_hip_fail(hipError_t e, const char* expr, const char* file, int
 
 namespace {
 
+// Weight matrices the dX GEMMs read transposed (token table, then per layer
+// W_qkv, W_o, W_fc, W_p); bf16 mode keeps a transposed copy of each so that
+// both operands of dX = dY W are k-major.
+const int kTransposed[5] = {0, 4, 6, 10, 12};
+
 const char* kParamNames[16] = {"wte",  "wpe",      "ln1w",     "ln1b", "qkvw", "qkvb",    "attprojw", "attprojb",
                                "ln2w", "ln2b",     "fcw",      "fcb",  "fcprojw", "fcprojb", "lnfw", "lnfb"};
 
@@ -139,6 +144,7 @@ struct Layout {
   ParamTable pt;
   int64_t P;
   size_t master, grad, adam_m, adam_v, params_bf16;
+  size_t params_t[16];                   // bf16 transposed copies of the weight matrices (0 if none)
   std::vector<size_t> resid;             // L + 1 buffers [BT, C]
   std::vector<LayerOffsets> layer;
   size_t tokens, lnf, lnf_mean, lnf_rstd, logits, losses, mean_loss;
@@ -152,16 +158,17 @@ size_t scratch_need(const gpt2_config& c) {
   const int BT = c.batch_size * c.seq_len, C = c.channels, Vp = c.padded_vocab_size;
   size_t s = 0;
   auto upd = [&](size_t x) { s = std::max(s, x); };
-  upd(gemm_workspace_bytes(dt, EPI_WGRAD, Vp, C, BT));
-  upd(gemm_workspace_bytes(dt, EPI_WGRAD, C, 4 * C, BT));
-  upd(gemm_workspace_bytes(dt, EPI_WGRAD, 4 * C, C, BT));
-  upd(gemm_workspace_bytes(dt, EPI_WGRAD, C, C, BT));
-  upd(gemm_workspace_bytes(dt, EPI_WGRAD, 3 * C, C, BT));
+  upd(gemm_workspace_bytes(dt, EPI_WGRAD, Vp, C, BT, false, false));
+  upd(gemm_workspace_bytes(dt, EPI_WGRAD, C, 4 * C, BT, false, false));
+  upd(gemm_workspace_bytes(dt, EPI_WGRAD, 4 * C, C, BT, false, false));
+  upd(gemm_workspace_bytes(dt, EPI_WGRAD, C, C, BT, false, false));
+  upd(gemm_workspace_bytes(dt, EPI_WGRAD, 3 * C, C, BT, false, false));
   // dX GEMMs (plain store; long-K ones are split)
-  upd(gemm_workspace_bytes(dt, EPI_STORE, BT, C, Vp));
-  upd(gemm_workspace_bytes(dt, EPI_STORE, BT, C, 4 * C));
-  upd(gemm_workspace_bytes(dt, EPI_STORE, BT, C, 3 * C));
-  upd(gemm_workspace_bytes(dt, EPI_STORE, BT, C, C));
+  const bool wt = dt == GPT2_BF16;   // bf16 dX reads transposed (k-major) weights
+  upd(gemm_workspace_bytes(dt, EPI_STORE, BT, C, Vp, true, wt));
+  upd(gemm_workspace_bytes(dt, EPI_STORE, BT, C, 4 * C, true, wt));
+  upd(gemm_workspace_bytes(dt, EPI_STORE, BT, C, 3 * C, true, wt));
+  upd(gemm_workspace_bytes(dt, EPI_STORE, BT, C, C, true, wt));
   upd(layernorm_backward_workspace_bytes(BT, C));
   upd(attention_backward_workspace_bytes(c.batch_size, c.seq_len, c.num_heads, C / c.num_heads));
   upd(encoder_backward_workspace_bytes(c.batch_size, c.seq_len, C));
@@ -180,6 +187,12 @@ void make_layout(const gpt2_config& c, Layout* lo) {
   lo->adam_m = p.alloc(lo->P * 4);
   lo->adam_v = p.alloc(lo->P * 4);
   lo->params_bf16 = c.dtype == GPT2_BF16 ? p.alloc(lo->P * 2) : 0;
+  for (int i = 0; i < 16; ++i) lo->params_t[i] = 0;
+  if (c.dtype == GPT2_BF16)
+    for (int i : kTransposed) {
+      const int64_t* sh = lo->pt.shape[i];
+      lo->params_t[i] = p.alloc((size_t)sh[0] * sh[1] * sh[2] * 2);
+    }
   lo->tokens = p.alloc(BT * 4);
   lo->resid.resize(L + 1);
   for (size_t l = 0; l <= L; ++l) lo->resid[l] = p.alloc(BT * C * es);
@@ -221,7 +234,7 @@ void make_layout(const gpt2_config& c, Layout* lo) {
 enum Site {
   S_QKV = 0, S_ATTPROJ, S_FC, S_FCPROJ, S_LOGITS, S_FCPROJ_DX, S_FCPROJ_DW, S_FC_DX, S_FC_DW,
   S_ATTPROJ_DX, S_ATTPROJ_DW, S_QKV_DX, S_QKV_DW, S_CLS_DX, S_CLS_DW, S_ATTN_FWD, S_ATTN_DKDV, S_ATTN_DQ,
-  S_ATTN_DOT, S_XENT, S_LN_FWD, S_LN_BWD, S_ENC_FWD, S_ADAMW, S_COUNT
+  S_ATTN_DOT, S_XENT, S_LN_FWD, S_LN_BWD, S_ENC_FWD, S_ADAMW, S_WT, S_COUNT
 };
 
 struct SiteTimer {
@@ -258,6 +271,12 @@ struct gpt2_model {
     int64_t per = lo.pt.shape[i][1] * lo.pt.shape[i][2];
     if (cfg.dtype == GPT2_BF16) return at<bf16>(lo.params_bf16) + lo.pt.off[i] + (int64_t)l * per;
     return master() + lo.pt.off[i] + (int64_t)l * per;
+  }
+  // transposed bf16 copy of weight matrix i (layer l): [in, out] row-major
+  void* wt(int i, int l) {
+    const int64_t* sh = lo.pt.shape[i];
+    const int64_t per = (lo.pt.ndim[i] == 3 ? sh[1] * sh[2] : sh[0] * sh[1]);
+    return lo.params_t[i] ? at<bf16>(lo.params_t[i]) + (int64_t)l * per : nullptr;
   }
   float* lgrad(int i, int l) {
     int64_t per = lo.pt.shape[i][1] * lo.pt.shape[i][2];
@@ -329,12 +348,15 @@ GemmDesc fwd_desc(gpt2_model* m, int M, int N, int K, const void* x, const void*
 }
 
 // dx[M,K] = dy[M,N] W[N,K]
-GemmDesc dx_desc(gpt2_model* m, int M, int N, int K, const void* dy, const void* W, void* dx, int epi,
-                 const void* gelu_u) {
+// dx[M,K] = dy[M,N] W[N,K] (+ GELU' epilogue).  W is read through its
+// transposed copy WT [K, N] (k-major) when there is one, else n-major.
+GemmDesc dx_desc(gpt2_model* m, int M, int N, int K, const void* dy, const void* W, const void* WT, void* dx,
+                 int epi, const void* gelu_u) {
   GemmDesc d = gdesc(m->dt());
-  d.a_kmajor = true; d.b_kmajor = false;
+  d.a_kmajor = true; d.b_kmajor = WT != nullptr;
   d.M = M; d.N = K; d.K = N;
-  d.A = dy; d.lda = N; d.B = W; d.ldb = K;
+  d.A = dy; d.lda = N;
+  if (WT) { d.B = WT; d.ldb = N; } else { d.B = W; d.ldb = K; }
   d.epi = epi; d.C = dx; d.ldc = K; d.aux_in = gelu_u; d.ld_aux = K;
   d.workspace = m->scratch(); d.workspace_bytes = m->lo.scratch_bytes;
   return d;
@@ -435,7 +457,7 @@ int backward_impl(gpt2_model* m) {
   };
 
   // classifier: d_lnf = dz wte;  d_wte = dz^T lnf (overwrite; padded rows get exactly 0)
-  RC(run_gemm(m, S_CLS_DX, dx_desc(m, BT, Vp, C, logits, m->param(0), d_ln, EPI_STORE, nullptr)));
+  RC(run_gemm(m, S_CLS_DX, dx_desc(m, BT, Vp, C, logits, m->param(0), m->wt(0, 0), d_ln, EPI_STORE, nullptr)));
   RC(run_gemm(m, S_CLS_DW, dw_desc(m, BT, Vp, C, logits, m->at<char>(lo.lnf), m->lgrad(0, 0), nullptr, false)));
   RC(timed(m, S_LN_BWD, 0.0, ln_bwd_bytes(true), [&] {
     return layernorm_backward(dt, BT, C, d_ln, m->at<char>(lo.resid[L]), m->param(14), m->at<float>(lo.lnf_mean),
@@ -447,12 +469,12 @@ int backward_impl(gpt2_model* m) {
     // x_{l+1} = h + g Wp^T + bp
     RC(run_gemm(m, S_FCPROJ_DW, dw_desc(m, BT, C, 4 * C, dres_t, m->at<char>(o.g), m->lgrad(12, l),
                                         m->lgrad(13, l), false)));
-    RC(run_gemm(m, S_FCPROJ_DX, dx_desc(m, BT, C, 4 * C, dres_t, m->lparam(12, l), d_big, EPI_GELU_BWD,
+    RC(run_gemm(m, S_FCPROJ_DX, dx_desc(m, BT, C, 4 * C, dres_t, m->lparam(12, l), m->wt(12, l), d_big, EPI_GELU_BWD,
                                         m->at<char>(o.u))));
     // u = ln2 Wfc^T + bfc   (d_big now holds du)
     RC(run_gemm(m, S_FC_DW, dw_desc(m, BT, 4 * C, C, d_big, m->at<char>(o.ln2), m->lgrad(10, l),
                                     m->lgrad(11, l), false)));
-    RC(run_gemm(m, S_FC_DX, dx_desc(m, BT, 4 * C, C, d_big, m->lparam(10, l), d_ln, EPI_STORE, nullptr)));
+    RC(run_gemm(m, S_FC_DX, dx_desc(m, BT, 4 * C, C, d_big, m->lparam(10, l), m->wt(10, l), d_ln, EPI_STORE, nullptr)));
     RC(timed(m, S_LN_BWD, 0.0, ln_bwd_bytes(false), [&] {
       return layernorm_backward(dt, BT, C, d_ln, m->at<char>(o.h), m->lparam(8, l), m->at<float>(o.ln2_mean),
                                 m->at<float>(o.ln2_rstd), dres, false, dres_copy, m->lgrad(8, l), m->lgrad(9, l),
@@ -461,7 +483,7 @@ int backward_impl(gpt2_model* m) {
     // h = x + atty Wo^T + bo
     RC(run_gemm(m, S_ATTPROJ_DW, dw_desc(m, BT, C, C, dres_t, m->at<char>(o.atty), m->lgrad(6, l),
                                          m->lgrad(7, l), false)));
-    RC(run_gemm(m, S_ATTPROJ_DX, dx_desc(m, BT, C, C, dres_t, m->lparam(6, l), d_ln, EPI_STORE, nullptr)));
+    RC(run_gemm(m, S_ATTPROJ_DX, dx_desc(m, BT, C, C, dres_t, m->lparam(6, l), m->wt(6, l), d_ln, EPI_STORE, nullptr)));
     {
       // three kernels: D = rowsum(dO * O); dK, dV (recomputing S and dP); dQ
       const bool a0 = timer_arm(m, S_ATTN_DOT, 0), a1 = timer_arm(m, S_ATTN_DKDV, 1),
@@ -478,7 +500,7 @@ int backward_impl(gpt2_model* m) {
     // qkv = ln1 Wqkv^T + bqkv
     RC(run_gemm(m, S_QKV_DW, dw_desc(m, BT, 3 * C, C, d_qkv, m->at<char>(o.ln1), m->lgrad(4, l),
                                      m->lgrad(5, l), false)));
-    RC(run_gemm(m, S_QKV_DX, dx_desc(m, BT, 3 * C, C, d_qkv, m->lparam(4, l), d_ln, EPI_STORE, nullptr)));
+    RC(run_gemm(m, S_QKV_DX, dx_desc(m, BT, 3 * C, C, d_qkv, m->lparam(4, l), m->wt(4, l), d_ln, EPI_STORE, nullptr)));
     RC(timed(m, S_LN_BWD, 0.0, ln_bwd_bytes(false), [&] {
       return layernorm_backward(dt, BT, C, d_ln, m->at<char>(lo.resid[l]), m->lparam(2, l),
                                 m->at<float>(o.ln1_mean), m->at<float>(o.ln1_rstd), dres, false, dres_copy,
@@ -518,9 +540,26 @@ int init_params(gpt2_model* m, uint64_t seed) {
   return 0;
 }
 
+// Transposed copies of the weight matrices from the bf16 working copy.
+int refresh_transposed(gpt2_model* m) {
+  if (m->cfg.dtype != GPT2_BF16) return 0;
+  for (int i : kTransposed) {
+    const int64_t* sh = m->lo.pt.shape[i];
+    const bool layered = m->lo.pt.ndim[i] == 3;
+    const int batches = layered ? (int)sh[0] : 1;
+    const int R = (int)(layered ? sh[1] : sh[0]), Cc = (int)(layered ? sh[2] : sh[1]);
+    RC(timed(m, S_WT, 0.0, 4.0 * batches * (double)R * Cc, [&] {
+      return transpose_bf16(batches, R, Cc, static_cast<const bf16*>(m->param(i)), static_cast<bf16*>(m->wt(i, 0)),
+                            m->stream);
+    }));
+  }
+  return 0;
+}
+
 int refresh_bf16(gpt2_model* m) {
   if (m->cfg.dtype != GPT2_BF16) return 0;
-  return cast_f32_to_bf16(m->lo.P, m->master(), m->at<bf16>(m->lo.params_bf16), m->stream);
+  RC(cast_f32_to_bf16(m->lo.P, m->master(), m->at<bf16>(m->lo.params_bf16), m->stream));
+  return refresh_transposed(m);
 }
 
 }  // namespace
@@ -667,6 +706,7 @@ int gpt2_adamw_step(gpt2_model* m, float lr, float beta1, float beta2, float eps
                  m->cfg.dtype == GPT2_BF16 ? m->at<bf16>(m->lo.params_bf16) : nullptr, lr, beta1, beta2, eps,
                  weight_decay, t, m->stream);
   }));
+  RC(refresh_transposed(m));
   m->have_grads = false;
   return GPT2_OK;
 }
@@ -785,7 +825,8 @@ int gpt2_op_linear_forward(int dtype, int M, int N, int K, const void* x, const 
 }
 
 size_t gpt2_op_linear_backward_workspace_bytes(int dtype, int M, int N, int K) {
-  return std::max(gemm_workspace_bytes(dtype, EPI_WGRAD, N, K, M), gemm_workspace_bytes(dtype, EPI_STORE, M, K, N));
+  return std::max(gemm_workspace_bytes(dtype, EPI_WGRAD, N, K, M, false, false),
+                  gemm_workspace_bytes(dtype, EPI_STORE, M, K, N, true, false));
 }
 
 int gpt2_op_linear_backward(int dtype, int M, int N, int K, const void* dy, const void* x, const void* W,
