@@ -131,6 +131,9 @@ def main():
     ap.add_argument("--seed", type=int, default=1234)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--site", default=None, help="kernel site to report in roofline (default: the slowest)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run one device-to-device copy of this many MiB (a kernel of known traffic, "
+                         "to calibrate hardware byte counters against)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -146,6 +149,14 @@ def main():
     cfg = lib.make_config(c["V"], c["Vp"], c["maxT"], c["L"], c["H"], c["C"], B, T, lib.GPT2_BF16)
     torch.cuda.init()
     stream = torch.cuda.current_stream()
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     model = lib.Model(cfg, seed=args.seed, stream=stream)
     nsteps = args.warmup + args.steps
     batches = []

@@ -96,8 +96,11 @@ __global__ __launch_bounds__(kRows * TPR) void attn_fwd_simt(int T_, int H, cons
 // D[bh, i] = dO_i . O_i.  hd/8 lanes per row, each taking one 16-byte chunk
 // of O and dO, combined with lane swizzles.
 template <typename T>
+// D_i = dO_i . O_i per (b, h, i), and the log-sum-exp in base 2
+// (L2_i = lse_i * log2(e)) that the matrix-core backward kernels use.
 __global__ __launch_bounds__(256) void attn_bwd_dot_kernel(int B, int T_, int H, int hd, const T* __restrict__ out,
-                                                           const T* __restrict__ dout, float* __restrict__ D) {
+                                                           const T* __restrict__ dout, const float* __restrict__ lse,
+                                                           float* __restrict__ D, float* __restrict__ L2) {
   const int lpr = hd / 8;                       // lanes per row: 2, 4, 8 or 16
   const int64_t gl = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t row = gl / lpr;                 // (b, h, i) in lse order
@@ -113,7 +116,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dot_kernel(int B, int T_, int H,
     for (int e = 0; e < 8; ++e) s += o[e] * d[e];
   }
   for (int m = 1; m < lpr; m <<= 1) s += __shfl_xor(s, m, 64);
-  if (row < (int64_t)B * H * T_ && part == 0) D[row] = s;
+  if (row < (int64_t)B * H * T_ && part == 0) {
+    D[row] = s;
+    L2[row] = lse[row] * 1.4426950408889634f;
+  }
 }
 
 template <typename T, int HD, int TPR>
@@ -317,7 +323,7 @@ int attention_forward(int dtype, int B, int T_, int H, int hd, const void* qkv, 
 
 size_t attention_backward_workspace_bytes(int B, int T_, int H, int hd) {
   (void)hd;
-  return (size_t)B * H * T_ * sizeof(float) + 256;
+  return 2 * (((size_t)B * H * T_ + 63) / 64 * 64) * sizeof(float) + 256;
 }
 
 int attention_backward(int dtype, int B, int T_, int H, int hd, const void* qkv, const void* out,
@@ -328,20 +334,22 @@ int attention_backward(int dtype, int B, int T_, int H, int hd, const void* qkv,
   if (B == 0 || T_ == 0) return 0;
   if (!workspace || workspace_bytes < attention_backward_workspace_bytes(B, T_, H, hd))
     return gpt2_internal_fail(3, "attention_backward: workspace too small");
+  // workspace: D [B*H*T], then L2 [B*H*T] at a 256-byte boundary
   float* D = (float*)workspace;
+  float* L2 = D + ((size_t)B * H * T_ + 63) / 64 * 64;
   const int64_t lanes = (int64_t)B * H * T_ * (hd / 8);
   mark_begin(0, stream);
   if (dtype == BF16) {
     hipLaunchKernelGGL(attn_bwd_dot_kernel<bf16>, dim3((unsigned)ceil_div64(lanes, 256)), dim3(256), 0, stream,
-                       B, T_, H, hd, (const bf16*)out, (const bf16*)dout, D);
+                       B, T_, H, hd, (const bf16*)out, (const bf16*)dout, lse, D, L2);
   } else {
     hipLaunchKernelGGL(attn_bwd_dot_kernel<float>, dim3((unsigned)ceil_div64(lanes, 256)), dim3(256), 0,
-                       stream, B, T_, H, hd, (const float*)out, (const float*)dout, D);
+                       stream, B, T_, H, hd, (const float*)out, (const float*)dout, lse, D, L2);
   }
   GPT2_LAUNCH_CHECK();
   mark_end(0, stream);
   if (attention_mfma_supported(dtype, hd))
-    return attention_backward_mfma(B, T_, H, qkv, dout, lse, D, dqkv, stream);
+    return attention_backward_mfma(B, T_, H, qkv, dout, L2, D, dqkv, stream);
   return dtype == BF16 ? bwd_dispatch<bf16>(B, T_, H, hd, qkv, dout, lse, D, dqkv, stream)
                        : bwd_dispatch<float>(B, T_, H, hd, qkv, dout, lse, D, dqkv, stream);
 }

@@ -202,17 +202,24 @@ __global__ __launch_bounds__(256, 4) void attn_fwd_mfma_kernel(int T, int H, con
         for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) s = mfma(frag_nat(Kc, ks, k, lane), qf[k], s);
+        // the causal / end-of-sequence mask only touches slices on the diagonal
+        // (a wave-uniform test, so the common case runs unmasked)
         const bool edge = (kb + 31 > qw0) || (kb + 32 > T);
         float t[16];
         float mx = -INFINITY;
+        if (edge) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          t[r] = s[r] * sl2;
-          if (edge) {
+          for (int r = 0; r < 16; ++r) {
             const int key = kb + acc_row(r, lane);
-            if (key > myq || key >= T) t[r] = -INFINITY;
+            t[r] = (key > myq || key >= T) ? -INFINITY : s[r] * sl2;
+            mx = fmaxf(mx, t[r]);
           }
-          mx = fmaxf(mx, t[r]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            t[r] = s[r] * sl2;
+            mx = fmaxf(mx, t[r]);
+          }
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float m_new = fmaxf(m_i, mx);
@@ -251,7 +258,7 @@ constexpr int KV_STAGE_BYTES = 2 * TILE + 2048;   // Q tile, dO tile, lse (1 KiB
 
 __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H, const bf16* __restrict__ qkv,
                                                                  const bf16* __restrict__ dout,
-                                                                 const float* __restrict__ lse,
+                                                                 const float* __restrict__ lse2,
                                                                  const float* __restrict__ Dv,
                                                                  bf16* __restrict__ dqkv, float scale) {
   constexpr int NS = NS_DKDV;
@@ -267,7 +274,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
   const bf16* Og = dout + (size_t)b * T * C;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(Bg, (uint32_t)((size_t)T * ld * 2));
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(Og, (uint32_t)((size_t)T * C * 2));
-  const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse + (size_t)bh * T, (uint32_t)(T * 4));
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse2 + (size_t)bh * T, (uint32_t)(T * 4));
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(Dv + (size_t)bh * T, (uint32_t)(T * 4));
   const int k0 = ktile * ROWS, kw0 = k0 + wave * 32, mykey = kw0 + (lane & 31);
   const float sl2 = scale * kLog2e;
@@ -318,17 +325,34 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
           s = mfma(frag_nat(Qs, qs, k, lane), kf[k], s);
           dp = mfma(frag_nat(Os, qs, k, lane), vf[k], dp);
         }
-        // s[r]: query qb + acc_row(r), key mykey
-        const bool edge = (qb < kw0 + 31) || (qb + 32 > T);
+        // s[r]: query qb + acc_row(r), key mykey.  The lane's 16 query rows are
+        // qs + 4 hi + 8 g + 0..3 (g = 0..3): four 16-byte reads each of L2 and D.
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        float lv[16], dv_[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 l4 = *reinterpret_cast<const GPT2_LDS f32x4*>(Ls + qs + 4 * (lane >> 5) + 8 * g);
+          const f32x4 d4 = *reinterpret_cast<const GPT2_LDS f32x4*>(Ds + qs + 4 * (lane >> 5) + 8 * g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { lv[4 * g + e] = l4[e]; dv_[4 * g + e] = d4[e]; }
+        }
+        float p[16];
+        // the causal / end-of-sequence mask only touches slices on the diagonal
+        if ((qb < kw0 + 31) || (qb + 32 > T)) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int q = qb + acc_row(r, lane);
+            p[r] = (mykey > q || q >= T) ? 0.f : ex2(fmaf(s[r], sl2, -lv[r]));
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) p[r] = ex2(fmaf(s[r], sl2, -lv[r]));
+        }
         bf16x8 pb[2], db[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int ql = qs + acc_row(r, lane);
-          float p = ex2(s[r] * sl2 - Ls[ql] * kLog2e);
-          if (edge && (mykey > qb + acc_row(r, lane) || qb + acc_row(r, lane) >= T)) p = 0.f;
-          const float ds = p * (dp[r] - Ds[ql]);
-          pb[r >> 3][r & 7] = (bf16)p;
-          db[r >> 3][r & 7] = (bf16)ds;
+          pb[r >> 3][r & 7] = (bf16)p[r];
+          db[r >> 3][r & 7] = (bf16)(p[r] * (dp[r] - dv_[r]));
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u)
@@ -351,7 +375,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
 
 __global__ __launch_bounds__(256, 3) void attn_bwd_dq_mfma_kernel(int T, int H, const bf16* __restrict__ qkv,
                                                                const bf16* __restrict__ dout,
-                                                               const float* __restrict__ lse,
+                                                               const float* __restrict__ lse2,
                                                                const float* __restrict__ Dv,
                                                                bf16* __restrict__ dqkv, float scale) {
   constexpr int NS = NS_DQ;
@@ -372,7 +396,7 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dq_mfma_kernel(int T, int H, 
   bf16x8 qf[4], of[4];
   frags_global(Qg, ld, myq, T, lane, qf);
   frags_global(Og, (size_t)C, myq, T, lane, of);
-  const float lse2 = myq < T ? lse[(size_t)bh * T + myq] * kLog2e : 0.f;
+  const float lq = myq < T ? lse2[(size_t)bh * T + myq] : 0.f;
   const float Dq = myq < T ? Dv[(size_t)bh * T + myq] : 0.f;
   floatx16 dq[2];
 #pragma unroll
@@ -410,16 +434,21 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dq_mfma_kernel(int T, int H, 
           s = mfma(frag_nat(Ks, ks, k, lane), qf[k], s);
           dp = mfma(frag_nat(Vs, ks, k, lane), of[k], dp);
         }
-        // s[r]: key kb + acc_row(r), query myq
-        const bool edge = (kb + 31 > qw0) || (kb + 32 > T);
+        // s[r]: key kb + acc_row(r), query myq; the mask only touches diagonal slices
+        float p[16];
+        if ((kb + 31 > qw0) || (kb + 32 > T)) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kb + acc_row(r, lane);
+            p[r] = (key > myq || key >= T) ? 0.f : ex2(fmaf(s[r], sl2, -lq));
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) p[r] = ex2(fmaf(s[r], sl2, -lq));
+        }
         bf16x8 db[2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = ex2(s[r] * sl2 - lse2);
-          const int key = kb + acc_row(r, lane);
-          if (edge && (key > myq || key >= T)) p = 0.f;
-          db[r >> 3][r & 7] = (bf16)(p * (dp[r] - Dq));
-        }
+        for (int r = 0; r < 16; ++r) db[r >> 3][r & 7] = (bf16)(p[r] * (dp[r] - Dq));
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -444,18 +473,18 @@ int attention_forward_mfma(int B, int T, int H, const void* qkv, void* out, floa
   return 0;
 }
 
-int attention_backward_mfma(int B, int T, int H, const void* qkv, const void* dout, const float* lse,
+int attention_backward_mfma(int B, int T, int H, const void* qkv, const void* dout, const float* lse2,
                             const float* D, void* dqkv, hipStream_t stream) {
   dim3 grid((unsigned)ceil_div64(T, ROWS), (unsigned)(B * H));
   const float scale = 1.0f / sqrtf((float)HD);
   mark_begin(1, stream);
   hipLaunchKernelGGL(attn_bwd_dkdv_mfma_kernel, grid, dim3(256), 0, stream, T, H, (const bf16*)qkv,
-                     (const bf16*)dout, lse, D, (bf16*)dqkv, scale);
+                     (const bf16*)dout, lse2, D, (bf16*)dqkv, scale);
   GPT2_LAUNCH_CHECK();
   mark_end(1, stream);
   mark_begin(2, stream);
   hipLaunchKernelGGL(attn_bwd_dq_mfma_kernel, grid, dim3(256), 0, stream, T, H, (const bf16*)qkv,
-                     (const bf16*)dout, lse, D, (bf16*)dqkv, scale);
+                     (const bf16*)dout, lse2, D, (bf16*)dqkv, scale);
   GPT2_LAUNCH_CHECK();
   mark_end(2, stream);
   return 0;
