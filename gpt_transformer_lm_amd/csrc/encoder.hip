@@ -186,32 +186,23 @@ int encoder_forward(int dtype, int B, int T_, int C, int vocab_rows, const int32
   return 0;
 }
 
-size_t encoder_backward_workspace_bytes(int B, int T_, int C) {
-  const int n = B * T_;
-  const int np = (int)ceil_div64(n, kPiece);
-  return (size_t)n * sizeof(uint32_t) + 2 * (size_t)np * C * sizeof(float) + 512;
+size_t encoder_backward_sorted_workspace_bytes(int B, int T_, int C) {
+  const int np = (int)ceil_div64((int64_t)B * T_, kPiece);
+  return 2 * (size_t)np * C * sizeof(float) + 256;
 }
 
-int encoder_backward(int B, int T_, int C, int vocab_rows, const int32_t* tokens, const float* dx0,
-                     float* dwte, float* dwpe, bool accumulate_wpe, void* workspace, size_t workspace_bytes,
-                     hipStream_t stream) {
-  if (B < 0 || T_ < 0 || C <= 0 || vocab_rows <= 0 || vocab_rows > 65536 || !tokens || !dx0 || !dwte || !dwpe)
-    return gpt2_internal_fail(1, "encoder_backward: bad arguments");
+size_t encoder_backward_workspace_bytes(int B, int T_, int C) {
   const int n = B * T_;
+  return (((size_t)n * 4 + 255) / 256) * 256 + encoder_backward_sorted_workspace_bytes(B, T_, C);
+}
+
+int encoder_sort_keys(int n, int vocab_rows, const int32_t* tokens, uint32_t* sorted, hipStream_t stream) {
+  if (n < 0 || vocab_rows <= 0 || vocab_rows > 65536 || !tokens || !sorted)
+    return gpt2_internal_fail(1, "encoder_sort_keys: bad arguments");
   if (n == 0) return 0;
   if (n > kSortMax) return gpt2_internal_fail(1, "encoder_backward: B*T=%d exceeds %d", n, kSortMax);
-  if (!workspace || workspace_bytes < encoder_backward_workspace_bytes(B, T_, C))
-    return gpt2_internal_fail(3, "encoder_backward: workspace too small");
   const int shift = pos_bits(n);
   if (shift + 16 > 32) return gpt2_internal_fail(1, "encoder_backward: key overflow");
-  const int npieces = (int)ceil_div64(n, kPiece);
-  uint32_t* sorted = (uint32_t*)workspace;
-  float* pcont = (float*)((char*)workspace + (((size_t)n * 4 + 255) / 256) * 256);
-  float* pown = pcont + (size_t)npieces * C;
-
-  hipLaunchKernelGGL(encoder_bwd_wpe_kernel, dim3((unsigned)ceil_div64((int64_t)T_ * C, 256)), dim3(256), 0,
-                     stream, B, T_, C, dx0, dwpe, accumulate_wpe);
-  GPT2_LAUNCH_CHECK();
   int np2 = 1;
   while (np2 < n) np2 <<= 1;
   static bool lds_attr_set = false;
@@ -224,6 +215,26 @@ int encoder_backward(int B, int T_, int C, int vocab_rows, const int32_t* tokens
   hipLaunchKernelGGL(sort_keys_kernel, dim3(1), dim3(1024), (size_t)np2 * sizeof(uint32_t), stream, n, shift,
                      tokens, vocab_rows, sorted);
   GPT2_LAUNCH_CHECK();
+  return 0;
+}
+
+int encoder_backward_sorted(int B, int T_, int C, const uint32_t* sorted, const float* dx0, float* dwte,
+                            float* dwpe, bool accumulate_wpe, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  if (B < 0 || T_ < 0 || C <= 0 || !sorted || !dx0 || !dwte || !dwpe)
+    return gpt2_internal_fail(1, "encoder_backward: bad arguments");
+  const int n = B * T_;
+  if (n == 0) return 0;
+  if (n > kSortMax) return gpt2_internal_fail(1, "encoder_backward: B*T=%d exceeds %d", n, kSortMax);
+  if (!workspace || workspace_bytes < encoder_backward_sorted_workspace_bytes(B, T_, C))
+    return gpt2_internal_fail(3, "encoder_backward: workspace too small");
+  const int shift = pos_bits(n);
+  const int npieces = (int)ceil_div64(n, kPiece);
+  float* pcont = (float*)workspace;
+  float* pown = pcont + (size_t)npieces * C;
+  hipLaunchKernelGGL(encoder_bwd_wpe_kernel, dim3((unsigned)ceil_div64((int64_t)T_ * C, 256)), dim3(256), 0,
+                     stream, B, T_, C, dx0, dwpe, accumulate_wpe);
+  GPT2_LAUNCH_CHECK();
   hipLaunchKernelGGL(encoder_bwd_pieces_kernel, dim3(npieces), dim3(256), 0, stream, n, C, shift, sorted, dx0,
                      dwte, pcont, pown);
   GPT2_LAUNCH_CHECK();
@@ -231,6 +242,23 @@ int encoder_backward(int B, int T_, int C, int vocab_rows, const int32_t* tokens
                      pcont, pown, dwte);
   GPT2_LAUNCH_CHECK();
   return 0;
+}
+
+int encoder_backward(int B, int T_, int C, int vocab_rows, const int32_t* tokens, const float* dx0,
+                     float* dwte, float* dwpe, bool accumulate_wpe, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  if (B < 0 || T_ < 0 || C <= 0 || vocab_rows <= 0 || vocab_rows > 65536 || !tokens || !dx0 || !dwte || !dwpe)
+    return gpt2_internal_fail(1, "encoder_backward: bad arguments");
+  const int n = B * T_;
+  if (n == 0) return 0;
+  if (!workspace || workspace_bytes < encoder_backward_workspace_bytes(B, T_, C))
+    return gpt2_internal_fail(3, "encoder_backward: workspace too small");
+  uint32_t* sorted = (uint32_t*)workspace;
+  const size_t head = (((size_t)n * 4 + 255) / 256) * 256;
+  int rc = encoder_sort_keys(n, vocab_rows, tokens, sorted, stream);
+  if (rc) return rc;
+  return encoder_backward_sorted(B, T_, C, sorted, dx0, dwte, dwpe, accumulate_wpe, (char*)workspace + head,
+                                 workspace_bytes - head, stream);
 }
 
 }  // namespace gpt2k

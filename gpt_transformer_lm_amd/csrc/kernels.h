@@ -114,6 +114,13 @@ size_t encoder_backward_workspace_bytes(int B, int T, int C);
 int encoder_backward(int B, int T, int C, int vocab_rows, const int32_t* tokens, const float* dx0,
                      float* dwte, float* dwpe, bool accumulate_wpe, void* workspace,
                      size_t workspace_bytes, hipStream_t stream);
+// The two parts of encoder_backward: the key sort depends only on the ids
+// (sorted: B*T uint32), the rest on dx0.
+int encoder_sort_keys(int n, int vocab_rows, const int32_t* tokens, uint32_t* sorted, hipStream_t stream);
+size_t encoder_backward_sorted_workspace_bytes(int B, int T, int C);
+int encoder_backward_sorted(int B, int T, int C, const uint32_t* sorted, const float* dx0, float* dwte,
+                            float* dwpe, bool accumulate_wpe, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
 
 // ------------------------------------------------------------------ optimizer
 // AdamW over n fp32 parameters; writes the bf16 copy if param_bf16 != null.

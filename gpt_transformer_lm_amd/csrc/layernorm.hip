@@ -77,8 +77,11 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int N, int C, const T* __re
   }
 }
 
-template <typename T, int NCH>
-__global__ __launch_bounds__(256) void ln_bwd_kernel(int N, int C, const T* __restrict__ dy,
+// WPB waves per block (1024 threads for C <= 1024, fewer for wider rows so
+// that the row cache fits the registers); each block writes one partial row
+// of dw and db.
+template <typename T, int NCH, int WPB>
+__global__ __launch_bounds__(WPB * 64) void ln_bwd_kernel(int N, int C, const T* __restrict__ dy,
                                                      const T* __restrict__ x, const T* __restrict__ w,
                                                      const float* __restrict__ mean,
                                                      const float* __restrict__ rstd,
@@ -86,8 +89,8 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(int N, int C, const T* __re
                                                      T* __restrict__ dres_copy,
                                                      float* __restrict__ part_dw,
                                                      float* __restrict__ part_db) {
-  const int wave_id = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int nwaves = gridDim.x * 4;
+  const int wave_id = blockIdx.x * WPB + (threadIdx.x >> 6);
+  const int nwaves = gridDim.x * WPB;
   const int lane = threadIdx.x & 63;
   const int nch = C / 8;
   const float invC = 1.0f / (float)C;
@@ -145,8 +148,8 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(int N, int C, const T* __re
       }
     }
   }
-  // reduce the block's 4 waves in LDS, one partial row per block (dw, then db)
-  extern __shared__ float red[];   // [4][C]
+  // reduce the block's waves in LDS, in wave order: one partial row per block (dw, then db)
+  extern __shared__ float red[];   // [WPB][C]
   const int wi = threadIdx.x >> 6;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
@@ -162,8 +165,12 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(int N, int C, const T* __re
       }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < C; i += blockDim.x)
-      dst[(size_t)blockIdx.x * C + i] = (red[i] + red[C + i]) + (red[2 * C + i] + red[3 * C + i]);
+    for (int i = threadIdx.x; i < C; i += blockDim.x) {
+      float t = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < WPB; ++w2) t += red[w2 * C + i];
+      dst[(size_t)blockIdx.x * C + i] = t;
+    }
   }
 }
 
@@ -204,10 +211,16 @@ int nch_for(int C) {
   return -1;
 }
 
-// waves of the backward grid (4 per block; each block writes one partial row):
-// enough to keep 4 waves on every SIMD of the 256 compute units
-int bwd_waves(int N) { return (int)std::min<int64_t>(4096, ((int64_t)N + 3) / 4 * 4); }
-int bwd_blocks(int N) { return bwd_waves(N) / 4; }
+// waves per backward block, and blocks: 4096 waves keep 4 on every SIMD of the
+// 256 compute units; each block writes one partial row
+int bwd_wpb(int C) {
+  const int n = nch_for(C);
+  return n <= 2 ? 16 : (n == 4 ? 8 : 4);
+}
+int bwd_blocks(int N, int C) {
+  const int wpb = bwd_wpb(C);
+  return (int)std::min<int64_t>(4096 / wpb, ((int64_t)N + wpb - 1) / wpb);
+}
 
 template <typename T>
 int fwd_t(int N, int C, const void* x, const void* w, const void* b, void* y, float* mean, float* rstd,
@@ -234,18 +247,19 @@ template <typename T>
 int bwd_t(int N, int C, const void* dy, const void* x, const void* w, const float* mean,
           const float* rstd, float* dres, bool ovw, void* dres_copy, float* pdw, float* pdb,
           hipStream_t s) {
-  dim3 grid((unsigned)bwd_blocks(N)), block(256);
-  const size_t lds = 4 * (size_t)C * sizeof(float);
+  const int wpb = bwd_wpb(C);
+  dim3 grid((unsigned)bwd_blocks(N, C)), block(wpb * 64);
+  const size_t lds = (size_t)wpb * C * sizeof(float);
   const T* DY = (const T*)dy;
   const T* X = (const T*)x;
   const T* W = (const T*)w;
   T* DC = (T*)dres_copy;
   mark_begin(0, s);
   switch (nch_for(C)) {
-    case 1: hipLaunchKernelGGL((ln_bwd_kernel<T, 1>), grid, block, lds, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
-    case 2: hipLaunchKernelGGL((ln_bwd_kernel<T, 2>), grid, block, lds, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
-    case 4: hipLaunchKernelGGL((ln_bwd_kernel<T, 4>), grid, block, lds, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
-    case 8: hipLaunchKernelGGL((ln_bwd_kernel<T, 8>), grid, block, lds, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
+    case 1: hipLaunchKernelGGL((ln_bwd_kernel<T, 1, 16>), grid, block, lds, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
+    case 2: hipLaunchKernelGGL((ln_bwd_kernel<T, 2, 16>), grid, block, lds, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
+    case 4: hipLaunchKernelGGL((ln_bwd_kernel<T, 4, 8>), grid, block, lds, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
+    case 8: hipLaunchKernelGGL((ln_bwd_kernel<T, 8, 4>), grid, block, lds, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
     default: return gpt2_internal_fail(1, "layernorm: C=%d unsupported", C);
   }
   GPT2_LAUNCH_CHECK();
@@ -265,7 +279,7 @@ int layernorm_forward(int dtype, int N, int C, const void* x, const void* w, con
 }
 
 size_t layernorm_backward_workspace_bytes(int N, int C) {
-  return 2 * (size_t)bwd_blocks(N) * C * sizeof(float) + 256;
+  return 2 * (size_t)bwd_blocks(N, C) * C * sizeof(float) + 256;
 }
 
 int layernorm_backward(int dtype, int N, int C, const void* dy, const void* x, const void* w,
@@ -278,7 +292,7 @@ int layernorm_backward(int dtype, int N, int C, const void* dy, const void* x, c
   size_t need = layernorm_backward_workspace_bytes(N, C);
   if (!workspace || workspace_bytes < need)
     return gpt2_internal_fail(3, "layernorm_backward: workspace too small");
-  const int P = bwd_blocks(N);
+  const int P = bwd_blocks(N, C);
   float* pdw = (float*)workspace;
   float* pdb = pdw + (size_t)P * C;
   int rc = dtype == BF16 ? bwd_t<bf16>(N, C, dy, x, w, mean, rstd, dres, dres_overwrite, dres_copy, pdw, pdb, stream)

@@ -149,6 +149,7 @@ struct Layout {
   std::vector<LayerOffsets> layer;
   size_t tokens, lnf, lnf_mean, lnf_rstd, logits, losses, mean_loss;
   size_t dres, dres_t, d_ln, d_big, d_qkv, scratch;
+  size_t sorted_keys;                    // encoder-backward key sort (computed during the forward)
   size_t scratch_bytes;
   size_t total;
 };
@@ -223,6 +224,7 @@ void make_layout(const gpt2_config& c, Layout* lo) {
   lo->d_ln = p.alloc(BT * C * es);
   lo->d_big = p.alloc(BT * 4 * C * es);
   lo->d_qkv = p.alloc(BT * 3 * C * es);
+  lo->sorted_keys = p.alloc(BT * 4);
   lo->scratch_bytes = scratch_need(c);
   lo->scratch = p.alloc(lo->scratch_bytes);
   lo->total = p.total;
@@ -251,6 +253,12 @@ struct gpt2_model {
   gpt2_config cfg;
   Layout lo;
   hipStream_t stream;
+  // Side stream for work that depends only on the token ids (the encoder
+  // backward's key sort): forked after the ids are copied, joined before the
+  // encoder backward and before the ids are overwritten by the next forward.
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  bool side_pending = false;
   char* base;
   bool owns;
   bool have_dlogits = false;
@@ -385,7 +393,19 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets) {
   m->have_grads = false;
   // keep a copy of the ids for the encoder backward (the caller may reuse its buffer)
   int32_t* tok = m->at<int32_t>(lo.tokens);
+  if (m->side_pending) {   // the previous sort still reads the ids
+    GPT2_HIP_CHECK(hipStreamWaitEvent(s, m->ev_join, 0));
+    m->side_pending = false;
+  }
   GPT2_HIP_CHECK(hipMemcpyAsync(tok, tokens, (size_t)BT * sizeof(int32_t), hipMemcpyDeviceToDevice, s));
+  if (targets) {
+    // the key sort of the encoder backward runs beside the forward
+    GPT2_HIP_CHECK(hipEventRecord(m->ev_fork, s));
+    GPT2_HIP_CHECK(hipStreamWaitEvent(m->side, m->ev_fork, 0));
+    RC(encoder_sort_keys(BT, V, tok, m->at<uint32_t>(lo.sorted_keys), m->side));
+    GPT2_HIP_CHECK(hipEventRecord(m->ev_join, m->side));
+    m->side_pending = true;
+  }
   const double es = (double)m->es();
   const double act = (double)BT * C * es;  // bytes of one [BT, C] activation
   const double ln_fwd_bytes = 2.0 * act + BT * 8.0 + 2.0 * C * es;
@@ -510,7 +530,11 @@ int backward_impl(gpt2_model* m) {
   // encoder: wpe rows >= T get no gradient
   float* dwpe = m->lgrad(1, 0);
   RC(fill_f32((int64_t)(c.max_seq_len - T) * C, dwpe + (size_t)T * C, 0.f, s));
-  RC(encoder_backward(B, T, C, V, m->at<int32_t>(lo.tokens), dres, m->lgrad(0, 0), dwpe, false, m->scratch(), sb,
+  if (m->side_pending) {
+    GPT2_HIP_CHECK(hipStreamWaitEvent(s, m->ev_join, 0));
+    m->side_pending = false;
+  }
+  RC(encoder_backward_sorted(B, T, C, m->at<uint32_t>(lo.sorted_keys), dres, m->lgrad(0, 0), dwpe, false, m->scratch(), sb,
                       s));
   (void)Vp;
   return 0;
@@ -651,13 +675,21 @@ int gpt2_create(const gpt2_config* cfg, uint64_t seed, void* stream, void* works
     m->base = (char*)p;
     m->owns = true;
   }
-  int rc = init_params(m, seed);
+  int rc = 0;
+  if (hipStreamCreateWithFlags(&m->side, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&m->ev_join, hipEventDisableTiming) != hipSuccess)
+    rc = gpt2_internal_fail(GPT2_E_HIP, "side stream / event creation failed");
+  if (!rc) rc = init_params(m, seed);
   if (!rc) rc = fill_f32(m->lo.P, m->at<float>(m->lo.adam_m), 0.f, m->stream);
   if (!rc) rc = fill_f32(m->lo.P, m->at<float>(m->lo.adam_v), 0.f, m->stream);
   if (!rc) rc = fill_f32(m->lo.P, m->grad(), 0.f, m->stream);
   if (!rc) rc = refresh_bf16(m);
   if (!rc && hipStreamSynchronize(m->stream) != hipSuccess) rc = gpt2_internal_fail(GPT2_E_HIP, "sync failed");
   if (rc) {
+    if (m->side) (void)hipStreamDestroy(m->side);
+    if (m->ev_fork) (void)hipEventDestroy(m->ev_fork);
+    if (m->ev_join) (void)hipEventDestroy(m->ev_join);
     if (m->owns) (void)hipFree(m->base);
     delete m;
     return rc;
@@ -669,6 +701,12 @@ int gpt2_create(const gpt2_config* cfg, uint64_t seed, void* stream, void* works
 void gpt2_destroy(gpt2_model* m) {
   if (!m) return;
   (void)hipStreamSynchronize(m->stream);
+  if (m->side) {
+    (void)hipStreamSynchronize(m->side);
+    (void)hipStreamDestroy(m->side);
+  }
+  if (m->ev_fork) (void)hipEventDestroy(m->ev_fork);
+  if (m->ev_join) (void)hipEventDestroy(m->ev_join);
   for (auto& t : m->timers)
     for (auto e : t.ev) (void)hipEventDestroy(e);
   if (m->owns) (void)hipFree(m->base);
