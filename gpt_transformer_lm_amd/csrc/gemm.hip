@@ -607,8 +607,8 @@ __global__ void splitk_store_bf16_kernel(const float* __restrict__ partial, int 
 //   rounds * K-steps per split * t_step(tile)  +  fp32 partial traffic / HBM rate
 // with rounds = ceil(tiles * s / 256 CUs) and t_step the measured time of one
 // 64-deep K step of a tile on one CU (256x256: 2.75 us; 256x128 and 128x256:
-// 1.83 us; 192x192: 1.95 us; 128x128: 1.25 us; the larger tile reads less LDS
-// per MFMA).  WGRAD always goes through fp32 partials (s M N floats written
+// 1.83 us; 192x192: 1.70 us, its smaller per-tile epilogue bursts included;
+// 128x128: 1.25 us; the larger tile reads less LDS per MFMA).  WGRAD always goes through fp32 partials (s M N floats written
 // and read, M N written); a plain store is split only when K is long enough
 // for the partials to pay off.  Other epilogues are never split and choose
 // between the default tile and 192x192 (both operands k-major only), which
@@ -623,7 +623,7 @@ Plan plan_bf16(int epi, int M, int N, int K, bool a_kmajor, bool b_kmajor) {
   const bool may_split = wgrad || (epi == EPI_STORE && K >= 8192);
   struct Cand { int bm, bn; double t_step; };
   const Cand cands[5] = {{256, 256, 2.75e-6}, {256, 128, 1.83e-6}, {128, 256, 1.83e-6}, {128, 128, 1.25e-6},
-                         {192, 192, 1.95e-6}};
+                         {192, 192, 1.70e-6}};
   const int def_bm = M >= 2048 ? 256 : 128, def_bn = N >= 2048 ? 256 : 128;
   Plan best{def_bm, def_bn, 1, 0};
   double best_t = 1e300;
