@@ -104,6 +104,15 @@ __device__ __forceinline__ float gelu_tanh_grad_f(float u) {
   return 0.5f * (1.0f + th) + 0.5f * u * (1.0f - th * th) * dz;
 }
 
+// gelu_tanh_f(u) and gelu_tanh_grad_f(u) from one tanh evaluation.
+__device__ __forceinline__ void gelu_tanh_and_grad_f(float u, float& g, float& d) {
+  const float k0 = 0.7978845608028654f, k1 = 0.044715f;
+  const float th = tanh_via_exp(k0 * (u + k1 * u * u * u));
+  const float dz = k0 * (1.0f + 3.0f * k1 * u * u);
+  g = 0.5f * u * (1.0f + th);
+  d = 0.5f * (1.0f + th) + 0.5f * u * (1.0f - th * th) * dz;
+}
+
 // ---------------------------------------------------------------- host side
 
 // ---------------------------------------------------------------- gfx950 memory helpers

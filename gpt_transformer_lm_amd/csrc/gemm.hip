@@ -57,7 +57,7 @@ __device__ __forceinline__ void epilogue_store(const EpiArgs& e, int m, int n, f
   if constexpr (EPI == EPI_WGRAD) {
     e.partial[((size_t)z * e.M + m) * (size_t)e.N + n] = v;
   } else {
-    if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_RES || EPI == EPI_BIAS_GELU)
+    if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_RES || EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_GELU_D)
       v += to_f32(reinterpret_cast<const T*>(e.bias)[n]);
     if constexpr (EPI == EPI_BIAS_RES)
       v += to_f32(reinterpret_cast<const T*>(e.aux_in)[(size_t)m * e.ld_aux + n]);
@@ -67,6 +67,13 @@ __device__ __forceinline__ void epilogue_store(const EpiArgs& e, int m, int n, f
     }
     if constexpr (EPI == EPI_GELU_BWD)
       v *= gelu_tanh_grad_f(to_f32(reinterpret_cast<const T*>(e.aux_in)[(size_t)m * e.ld_aux + n]));
+    if constexpr (EPI == EPI_BIAS_GELU_D) {
+      float g, d;
+      gelu_tanh_and_grad_f(v, g, d);
+      reinterpret_cast<T*>(e.aux_out)[(size_t)m * e.ldc + n] = from_f32<T>(d);
+      v = g;
+    }
+    if constexpr (EPI == EPI_MUL) v *= to_f32(reinterpret_cast<const T*>(e.aux_in)[(size_t)m * e.ld_aux + n]);
     reinterpret_cast<T*>(e.C)[(size_t)m * e.ldc + n] = from_f32<T>(v);
   }
 }
@@ -102,6 +109,12 @@ __device__ __forceinline__ void epilogue_vec8_final(const EpiArgs& e, int m, int
       Chunk8<bf16>::store(reinterpret_cast<bf16*>(e.aux_out) + (size_t)m * e.ldc + n, v);
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = gelu_tanh_f(v[i]);
+    }
+    if constexpr (EPI == EPI_BIAS_GELU_D) {
+      float d[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) gelu_tanh_and_grad_f(v[i], v[i], d[i]);
+      Chunk8<bf16>::store(reinterpret_cast<bf16*>(e.aux_out) + (size_t)m * e.ldc + n, d);
     }
     Chunk8<bf16>::store(reinterpret_cast<bf16*>(e.C) + (size_t)m * e.ldc + n, v);
   }
@@ -250,13 +263,16 @@ struct DmaShape {
   }
   static constexpr int NS = fits(4) ? 4 : fits(3) ? 3 : 2;
   static constexpr bool EPI_IN_STAGE = AUX_STAGES < NS && AUX_BYTES <= STAGE_BYTES;
+  // The epilogue input tile can be loaded during the last K step (into the
+  // stages that step does not read) when it leaves one stage free.
+  static constexpr bool EARLY_AUX = HAS_AUX && AUX_STAGES < NS;
 };
 
 template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, bool BIAS_GRAD>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_dma_kernel(MfmaArgs p) {
-  constexpr bool HAS_BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RES || EPI == EPI_BIAS_GELU;
-  constexpr bool HAS_AUX = EPI == EPI_BIAS_RES || EPI == EPI_GELU_BWD;
+  constexpr bool HAS_BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RES || EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_GELU_D;
+  constexpr bool HAS_AUX = EPI == EPI_BIAS_RES || EPI == EPI_GELU_BWD || EPI == EPI_MUL;
   using S = DmaShape<BM, BN, HAS_AUX>;
   using TA = DmaTile<BM, A_KMAJ>;
   using TB = DmaTile<BN, B_KMAJ>;
@@ -300,6 +316,23 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
       bias_s[c] = n0 + c < p.N ? (float)reinterpret_cast<const bf16*>(p.e.bias)[n0 + c] : 0.f;
   }
 
+  // The residual / pre-activation tile the epilogue reads (R or U, [BM][BN]
+  // bf16) comes into stage buffers with the same DMA as the operands:
+  // [BM][64]-column sub-tiles with 128-byte swizzled rows (one memory round
+  // trip for the whole tile).  aux_stage(j) gives the stage of its j-th part.
+  auto issue_aux = [&](auto aux_stage) {
+    using TX = DmaTile<BM, true>;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.e.aux_in, p.aux_bytes);
+    const typename TX::Lane lx = TX::lane_part(wave, lane, m0, p.e.ld_aux);
+#pragma unroll
+    for (int c = 0; c < BN / 64; ++c) {
+      const int c0 = n0 + 64 * c;
+      TX::issue(rx, aux_stage(c / S::PER_STAGE) + (c % S::PER_STAGE) * S::SUB_BYTES, wave, lx, c0, p.N,
+                p.e.ld_aux, c0 + 64 > p.N);
+    }
+  };
+  const bool vec = p.vec_epilogue;
+
   float bsum[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) bsum[e] = 0.f;
@@ -325,6 +358,10 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
         else wait_vmcnt<0>();
         __syncthreads();
         if (kt + NS - 1 < KT) issue(kt + NS - 1, (s + NS - 1) % NS);
+        if constexpr (S::EARLY_AUX) {
+          // last K step: every stage but s is idle
+          if (kt == KT - 1 && vec) issue_aux([&](int j) { return stage_ptr((s + 1 + j) % NS); });
+        }
         const GPT2_LDS char* As = stage_ptr(s);
         const GPT2_LDS char* Bs = As + A_BYTES;
         if constexpr (BIAS_GRAD) {
@@ -369,28 +406,21 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
     }
   }
 
-  const bool vec = p.vec_epilogue;
-  // The residual / pre-activation tile the epilogue reads (R or U, [BM][BN]
-  // bf16) is brought into the now idle stage buffers with the same DMA as the
-  // operands: [BM][64]-column sub-tiles with 128-byte swizzled rows, so the
-  // whole tile costs one memory round trip instead of one per output block.
   constexpr int SUB_BYTES = S::SUB_BYTES;
   constexpr int PER_STAGE = S::PER_STAGE;
   static_assert(PER_STAGE >= 1 && S::AUX_STAGES <= NS, "aux tile must fit the stages");
-  // bias visible; every wave done with the stage buffers that are reused below
+  const int s_last = (KT - 1) % NS;          // stage of the last K step
+  if constexpr (S::EARLY_AUX) {
+    if (vec) wait_vmcnt<0>();                // the epilogue input issued in the last K step
+  }
+  // bias and epilogue input visible; every wave done with the stage buffers reused below
   if constexpr (HAS_BIAS || HAS_AUX || S::EPI_IN_STAGE) __syncthreads();
-  GPT2_LDS char* epi_lds = S::EPI_IN_STAGE ? stage_ptr(NS - 1) : (GPT2_LDS char*)epi_own;
-  if constexpr (HAS_AUX) {
+  GPT2_LDS char* epi_lds =
+      S::EPI_IN_STAGE ? stage_ptr(S::EARLY_AUX ? s_last : NS - 1) : (GPT2_LDS char*)epi_own;
+  auto aux_stage = [&](int j) { return S::EARLY_AUX ? stage_ptr((s_last + 1 + j) % NS) : stage_ptr(j); };
+  if constexpr (HAS_AUX && !S::EARLY_AUX) {
     if (vec) {
-      using TX = DmaTile<BM, true>;
-      const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.e.aux_in, p.aux_bytes);
-      const typename TX::Lane lx = TX::lane_part(wave, lane, m0, p.e.ld_aux);
-#pragma unroll
-      for (int c = 0; c < BN / 64; ++c) {
-        const int c0 = n0 + 64 * c;
-        TX::issue(rx, stage_ptr(c / PER_STAGE) + (c % PER_STAGE) * SUB_BYTES, wave, lx, c0, p.N, p.e.ld_aux,
-                  c0 + 64 > p.N);
-      }
+      issue_aux([&](int j) { return stage_ptr(j); });
       wait_vmcnt<0>();
       __syncthreads();
     }
@@ -429,7 +459,7 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
             }
             if constexpr (HAS_AUX) {
               const int sb = tc >> 6, ch = (tc & 63) >> 3;
-              const GPT2_LDS char* t = stage_ptr(sb / PER_STAGE) + (sb % PER_STAGE) * SUB_BYTES;
+              const GPT2_LDS char* t = aux_stage(sb / PER_STAGE) + (sb % PER_STAGE) * SUB_BYTES;
               typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
               const u32x4 raw = *reinterpret_cast<const GPT2_LDS u32x4*>(t + tr * 128 + swz(tr, ch) * 16);
               const uint32_t w[4] = {raw[0], raw[1], raw[2], raw[3]};
@@ -442,6 +472,9 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
               if constexpr (EPI == EPI_BIAS_RES) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] += x[e];
+              } else if constexpr (EPI == EPI_MUL) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] *= x[e];
               } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] *= gelu_tanh_grad_f(x[e]);
@@ -699,7 +732,7 @@ int dispatch_layout_bf16(const GemmDesc& d, const MfmaArgs& a, const Plan& pl, b
     // split-K partials of a plain-store dX = dY W (W n-major, or its k-major transpose)
     if (d.a_kmajor && !d.b_kmajor && !bias_grad) return launch_mfma<EPI, true, false, false>(a, pl, s);
     if (d.a_kmajor && d.b_kmajor && !bias_grad) return launch_mfma<EPI, true, true, false>(a, pl, s);
-  } else if constexpr (EPI == EPI_STORE || EPI == EPI_GELU_BWD) {
+  } else if constexpr (EPI == EPI_STORE || EPI == EPI_GELU_BWD || EPI == EPI_MUL) {
     if (d.a_kmajor && !d.b_kmajor) return launch_mfma<EPI, true, false, false>(a, pl, s);
     if (d.a_kmajor && d.b_kmajor) return launch_mfma<EPI, true, true, false>(a, pl, s);
   } else {
@@ -733,11 +766,12 @@ int gemm(const GemmDesc& d, hipStream_t stream) {
   const bool wgrad = d.epi == EPI_WGRAD;
   if (wgrad && !d.out32) return gpt2_internal_fail(1, "gemm: WGRAD needs out32");
   if (!wgrad && !d.C) return gpt2_internal_fail(1, "gemm: missing C");
-  if ((d.epi == EPI_BIAS || d.epi == EPI_BIAS_RES || d.epi == EPI_BIAS_GELU) && !d.bias)
+  if ((d.epi == EPI_BIAS || d.epi == EPI_BIAS_RES || d.epi == EPI_BIAS_GELU || d.epi == EPI_BIAS_GELU_D) && !d.bias)
     return gpt2_internal_fail(1, "gemm: missing bias");
-  if ((d.epi == EPI_BIAS_RES || d.epi == EPI_GELU_BWD) && !d.aux_in)
+  if ((d.epi == EPI_BIAS_RES || d.epi == EPI_GELU_BWD || d.epi == EPI_MUL) && !d.aux_in)
     return gpt2_internal_fail(1, "gemm: missing aux input");
-  if (d.epi == EPI_BIAS_GELU && !d.aux_out) return gpt2_internal_fail(1, "gemm: missing U output");
+  if ((d.epi == EPI_BIAS_GELU || d.epi == EPI_BIAS_GELU_D) && !d.aux_out)
+    return gpt2_internal_fail(1, "gemm: missing U output");
 
   const int splits = gemm_splits(d.dtype, d.epi, d.M, d.N, d.K, d.a_kmajor, d.b_kmajor);
   // a plain store split over K runs the partial-tile kernel, then a reduction into C
@@ -792,6 +826,8 @@ int gemm(const GemmDesc& d, hipStream_t stream) {
       case EPI_BIAS_RES: rc = dispatch_layout_bf16<EPI_BIAS_RES>(d, a, pl, false, stream); break;
       case EPI_BIAS_GELU: rc = dispatch_layout_bf16<EPI_BIAS_GELU>(d, a, pl, false, stream); break;
       case EPI_GELU_BWD: rc = dispatch_layout_bf16<EPI_GELU_BWD>(d, a, pl, false, stream); break;
+      case EPI_BIAS_GELU_D: rc = dispatch_layout_bf16<EPI_BIAS_GELU_D>(d, a, pl, false, stream); break;
+      case EPI_MUL: rc = dispatch_layout_bf16<EPI_MUL>(d, a, pl, false, stream); break;
       case EPI_WGRAD: rc = dispatch_layout_bf16<EPI_WGRAD>(d, a, pl, bias_grad, stream); break;
       default: return gpt2_internal_fail(1, "gemm: unknown epilogue %d", d.epi);
     }
@@ -823,6 +859,8 @@ int gemm(const GemmDesc& d, hipStream_t stream) {
     case EPI_BIAS_RES: rc = dispatch_layout_f32<EPI_BIAS_RES>(d, a, 1, stream); break;
     case EPI_BIAS_GELU: rc = dispatch_layout_f32<EPI_BIAS_GELU>(d, a, 1, stream); break;
     case EPI_GELU_BWD: rc = dispatch_layout_f32<EPI_GELU_BWD>(d, a, 1, stream); break;
+    case EPI_BIAS_GELU_D: rc = dispatch_layout_f32<EPI_BIAS_GELU_D>(d, a, 1, stream); break;
+    case EPI_MUL: rc = dispatch_layout_f32<EPI_MUL>(d, a, 1, stream); break;
     case EPI_WGRAD: rc = dispatch_layout_f32<EPI_WGRAD>(d, a, splits, stream); break;
     default: return gpt2_internal_fail(1, "gemm: unknown epilogue %d", d.epi);
   }

@@ -41,8 +41,12 @@ inline void mark_end(int i, hipStream_t s) {
 //              bias_grad32[m] = sum_k A(m, k) (A must be !a_kmajor).
 //              Split over K into partial sums that a second kernel reduces
 //              in a fixed order (deterministic).
+//   BIAS_GELU_D  C = gelu_tanh(v + bias[n]);  U[m * ldc + n] = gelu_tanh'(v + bias[n])
+//   MUL          C = v * U[m * ld_aux + n]
+//   (the step stores the GELU derivative in the forward, so the backward
+//   epilogue of the fc-proj dX is one multiply)
 enum Epi { EPI_STORE = 0, EPI_BIAS = 1, EPI_BIAS_RES = 2, EPI_BIAS_GELU = 3, EPI_GELU_BWD = 4,
-           EPI_WGRAD = 5 };
+           EPI_WGRAD = 5, EPI_BIAS_GELU_D = 6, EPI_MUL = 7 };
 
 struct GemmDesc {
   int dtype;            // F32 or BF16 (type of A, B, C, bias, R, U)

@@ -137,7 +137,9 @@ struct Plan {
 };
 
 struct LayerOffsets {
-  size_t ln1, ln1_mean, ln1_rstd, qkv, atty, lse, h, ln2, ln2_mean, ln2_rstd, u, g;
+  size_t ln1, ln1_mean, ln1_rstd, qkv, atty, lse, h, ln2, ln2_mean, ln2_rstd;
+  size_t u;   // GELU'(fc pre-activation), written by the forward for the backward
+  size_t g;   // GELU(fc pre-activation)
 };
 
 struct Layout {
@@ -431,7 +433,8 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets) {
       return layernorm_forward(dt, BT, C, m->at<char>(o.h), m->lparam(8, l), m->lparam(9, l), m->at<char>(o.ln2),
                                m->at<float>(o.ln2_mean), m->at<float>(o.ln2_rstd), s);
     }));
-    RC(run_gemm(m, S_FC, fwd_desc(m, BT, 4 * C, C, m->at<char>(o.ln2), m->lparam(10, l), EPI_BIAS_GELU,
+    // g = GELU(u) for the fc-proj product, and GELU'(u) kept for the backward
+    RC(run_gemm(m, S_FC, fwd_desc(m, BT, 4 * C, C, m->at<char>(o.ln2), m->lparam(10, l), EPI_BIAS_GELU_D,
                                   m->at<char>(o.g), m->lparam(11, l), nullptr, m->at<char>(o.u))));
     RC(run_gemm(m, S_FCPROJ, fwd_desc(m, BT, C, 4 * C, m->at<char>(o.g), m->lparam(12, l), EPI_BIAS_RES,
                                       m->at<char>(lo.resid[l + 1]), m->lparam(13, l), m->at<char>(o.h),
@@ -489,7 +492,8 @@ int backward_impl(gpt2_model* m) {
     // x_{l+1} = h + g Wp^T + bp
     RC(run_gemm(m, S_FCPROJ_DW, dw_desc(m, BT, C, 4 * C, dres_t, m->at<char>(o.g), m->lgrad(12, l),
                                         m->lgrad(13, l), false)));
-    RC(run_gemm(m, S_FCPROJ_DX, dx_desc(m, BT, C, 4 * C, dres_t, m->lparam(12, l), m->wt(12, l), d_big, EPI_GELU_BWD,
+    // du = (dy W_p) * GELU'(u), the derivative saved by the forward
+    RC(run_gemm(m, S_FCPROJ_DX, dx_desc(m, BT, C, 4 * C, dres_t, m->lparam(12, l), m->wt(12, l), d_big, EPI_MUL,
                                         m->at<char>(o.u))));
     // u = ln2 Wfc^T + bfc   (d_big now holds du)
     RC(run_gemm(m, S_FC_DW, dw_desc(m, BT, 4 * C, C, d_big, m->at<char>(o.ln2), m->lgrad(10, l),
