@@ -205,40 +205,43 @@ __global__ __launch_bounds__(256, 4) void attn_fwd_mfma_kernel(int T, int H, con
         // the causal / end-of-sequence mask only touches slices on the diagonal
         // (a wave-uniform test, so the common case runs unmasked)
         const bool edge = (kb + 31 > qw0) || (kb + 32 > T);
-        float t[16];
         float mx = -INFINITY;
         if (edge) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kb + acc_row(r, lane);
-            t[r] = (key > myq || key >= T) ? -INFINITY : s[r] * sl2;
-            mx = fmaxf(mx, t[r]);
+            if (key > myq || key >= T) s[r] = -INFINITY;
+            mx = fmaxf(mx, s[r]);
           }
         } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            t[r] = s[r] * sl2;
-            mx = fmaxf(mx, t[r]);
-          }
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_i, mx);
-        const float alpha = ex2(m_i - m_new);
+        // the scale sl2 is positive, so the maximum of the scaled scores is the
+        // scaled maximum; the scaling then folds into the exponent's fma
+        const float m_new = fmaxf(m_i, mx * sl2);
         float rs_ = 0.f;
         bf16x8 pb[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = ex2(t[r] - m_new);
+          const float p = ex2(fmaf(s[r], sl2, -m_new));
           rs_ += p;
           pb[r >> 3][r & 7] = (bf16)p;
         }
         rs_ += __shfl_xor(rs_, 32, 64);
-        l_i = l_i * alpha + rs_;
+        // rescale the running sum and O only when some lane's maximum grew
+        // (otherwise the factor is exactly 1); the vote is wave-uniform
+        if (__any(m_new > m_i)) {
+          const float alpha = ex2(m_i - m_new);
+          l_i *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+        }
+        l_i += rs_;
         m_i = m_new;
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
