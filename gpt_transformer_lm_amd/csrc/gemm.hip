@@ -148,7 +148,8 @@ __device__ __forceinline__ void tile_coords(int bid, int nbm, int nbn, int& tm, 
 //  * k-major operand (k contiguous in memory): [row][64 k], 128-byte rows whose
 //    16-byte chunks are XOR-swizzled by row; fragments are ds_read_b128.
 //  * m-major operand (m contiguous in memory): [k][R m], 2R-byte rows whose
-//    16-byte chunks are XOR-swizzled by (k & 3); fragments are two
+//    16-byte chunk index is XORed with 4 (k & 3), so the 4 x 64 bytes that one
+//    transposing read takes from k rows 4j .. 4j + 3 cover all 64 banks; fragments are two
 //    ds_read_b64_tr_b16 (the transpose read hands lane j of each 16-lane group
 //    element j%4 of the 8-byte runs of lanes j/4 + 4e, so with the per-lane
 //    addresses below every lane ends up with 8 consecutive k of one m).
@@ -164,7 +165,7 @@ struct DmaTile {
   //    lane/8 (per lane) xor (w NINST + q) & 7 (uniform).
   //  m-major: instruction q covers k rows qk + lane / (R/8) with
   //    qk = (w NINST + q) * 1024 / (2R), physical chunk lane % (R/8); the
-  //    swizzle ((k & 3) << 1) splits the same way.
+  //    swizzle ((k & 3) << 2) splits the same way.
   struct Lane {
     uint32_t base;    // bytes: row part (k-major) / row-in-group + column part (m-major)
     uint32_t c16;     // 16 * (per-lane part of the logical chunk index)
@@ -180,7 +181,7 @@ struct DmaTile {
     } else {
       constexpr int LPR = R / 8;                       // lanes per k row
       const int kr = lane / LPR, phys = lane % LPR;
-      const int c = phys ^ ((kr & 3) << 1);
+      const int c = phys ^ ((kr & 3) << 2);
       L.base = (uint32_t)((int64_t)kr * ld * 2 + (int64_t)row0 * 2);
       L.c16 = (uint32_t)(c * 16);
       L.sub = kr;
@@ -207,7 +208,7 @@ struct DmaTile {
       } else {
         constexpr int RPI = 1024 / (2 * R);              // k rows per instruction
         const int qk = iq * RPI;
-        const uint32_t u16 = (uint32_t)((((qk & 3) << 1) & 6) * 16);
+        const uint32_t u16 = (uint32_t)((((qk & 3) << 2) & 12) * 16);
         off = L.base + (uint32_t)((int64_t)(k0 + qk) * ld * 2) + (L.c16 ^ u16);
         if (k_tail) ok = k0 + qk + L.sub < K;
       }
@@ -230,7 +231,7 @@ struct DmaTile {
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const int kr = kk * 16 + 8 * (g >> 1) + 4 * r + (i >> 2);
-        const int c = (m >> 3) ^ ((kr & 3) << 1);
+        const int c = (m >> 3) ^ ((kr & 3) << 2);
         const GPT2_LDS bf16x4_t* q =
             reinterpret_cast<const GPT2_LDS bf16x4_t*>(tile + kr * (2 * R) + c * 16 + (m & 7) * 2);
         const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(const_cast<GPT2_LDS bf16x4_t*>(q));
@@ -377,7 +378,7 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
 #pragma unroll
               for (int r = 0; r < 8; ++r) {
                 const int kr = kg * 8 + r;
-                const int c = cc ^ ((kr & 3) << 1);
+                const int c = cc ^ ((kr & 3) << 2);
                 const bf16x8 v = *reinterpret_cast<const GPT2_LDS bf16x8*>(As + kr * (2 * BM) + c * 16);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) bsum[e] += (float)v[e];
@@ -591,9 +592,20 @@ __global__ void colsum_f32_kernel(const float* A, int64_t lda, int M, int K, flo
 
 // ---------------------------------------------------------------- split-K reduce
 
+// out[i] (+)= sum over the splits of partial[z][i] (i < MN), in split order.
+// Blocks from `first_bias_block` on do the same for the bias-gradient
+// partials (pb [splits][M] -> bias_out), so one launch covers both.
 __global__ void wgrad_reduce_kernel(const float* __restrict__ partial, int splits, int64_t MN,
-                                    float* __restrict__ out, bool accumulate) {
-  int64_t i4 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+                                    float* __restrict__ out, bool accumulate, unsigned first_bias_block,
+                                    const float* __restrict__ pb, int64_t M, float* __restrict__ bias_out) {
+  unsigned blk = blockIdx.x;
+  if (blk >= first_bias_block) {   // bias segment (uniform per block)
+    blk -= first_bias_block;
+    partial = pb;
+    MN = M;
+    out = bias_out;
+  }
+  int64_t i4 = ((int64_t)blk * blockDim.x + threadIdx.x) * 4;
   if (i4 >= MN) return;
   if (i4 + 4 <= MN && (MN % 4) == 0) {
     float4 s = accumulate ? *reinterpret_cast<const float4*>(out + i4) : make_float4(0, 0, 0, 0);
@@ -846,15 +858,12 @@ int gemm(const GemmDesc& d, hipStream_t stream) {
     }
     if (rc) return rc;
     if (wgrad) {
-      int64_t MN = (int64_t)d.M * d.N;
-      hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)ceil_div64(MN, 4 * 256)), dim3(256), 0,
-                         stream, partial, splits, MN, d.out32, d.accumulate);
+      const int64_t MN = (int64_t)d.M * d.N;
+      const unsigned main_blocks = (unsigned)ceil_div64(MN, 4 * 256);
+      const unsigned bias_blocks = bias_grad ? (unsigned)ceil_div64(d.M, 4 * 256) : 0u;
+      hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(main_blocks + bias_blocks), dim3(256), 0, stream, partial, splits,
+                         MN, d.out32, d.accumulate, main_blocks, partial_bias, (int64_t)d.M, d.bias_grad32);
       GPT2_LAUNCH_CHECK();
-      if (bias_grad) {
-        hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)ceil_div64(d.M, 4 * 256)), dim3(256), 0,
-                           stream, partial_bias, splits, (int64_t)d.M, d.bias_grad32, d.accumulate);
-        GPT2_LAUNCH_CHECK();
-      }
     }
     if (split_store) {
       hipLaunchKernelGGL(splitk_store_bf16_kernel, dim3((unsigned)ceil_div64((int64_t)d.M * d.N, 4 * 256)),
@@ -880,8 +889,9 @@ int gemm(const GemmDesc& d, hipStream_t stream) {
   if (rc) return rc;
   if (wgrad) {
     int64_t MN = (int64_t)d.M * d.N;
-    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)ceil_div64(MN, 4 * 256)), dim3(256), 0,
-                       stream, partial, splits, MN, d.out32, d.accumulate);
+    const unsigned main_blocks = (unsigned)ceil_div64(MN, 4 * 256);
+    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(main_blocks), dim3(256), 0, stream, partial, splits, MN, d.out32,
+                       d.accumulate, main_blocks, (const float*)nullptr, (int64_t)0, (float*)nullptr);
     GPT2_LAUNCH_CHECK();
     if (d.bias_grad32) {
       if (d.a_kmajor) return gpt2_internal_fail(1, "gemm: bias gradient needs an m-major A");
