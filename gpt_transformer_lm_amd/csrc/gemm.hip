@@ -120,15 +120,20 @@ __device__ __forceinline__ void epilogue_vec8_final(const EpiArgs& e, int m, int
   }
 }
 
-// Tile coordinates of workgroup `bid`.  The dispatcher hands consecutive
-// workgroup ids to the 8 XCDs in turn; each XCD is given a contiguous range of
-// tiles (so the tiles resident on one XCD share its L2), and inside a range
-// tiles run in groups of 8 M-tiles that sweep the N-tiles together.
-__device__ __forceinline__ void tile_coords(int bid, int nbm, int nbn, int& tm, int& tn) {
-  const int ntiles = nbm * nbn;
-  const int xcd = bid & 7, idx = bid >> 3;
-  const int base = ntiles >> 3, rem = ntiles & 7;
-  const int t = xcd * base + min(xcd, rem) + idx;
+// Tile and K-split coordinates of this workgroup.  The dispatcher hands the
+// workgroups, in linear order (x fastest, then y = split), to the 8 XCDs in
+// turn; each XCD is given a contiguous range of the (split, tile) units, split
+// major, so the units resident on one XCD share A and B slabs of one K range
+// in its L2; inside a split, tiles run in groups of 8 M-tiles that sweep the
+// N-tiles together.
+__device__ __forceinline__ void tile_coords(int nbm, int nbn, int& tm, int& tn, int& z) {
+  const int ntiles = nbm * nbn, total = ntiles * (int)gridDim.y;
+  const int lin = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+  const int xcd = lin & 7, idx = lin >> 3;
+  const int base = total >> 3, rem = total & 7;
+  const int v = xcd * base + min(xcd, rem) + idx;
+  z = v / ntiles;
+  const int t = v - z * ntiles;
   constexpr int GM = 8;
   const int group = t / (GM * nbn);
   const int first_m = group * GM;
@@ -294,9 +299,9 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   int tm, tn;
-  tile_coords(blockIdx.x, (p.M + BM - 1) / BM, (p.N + BN - 1) / BN, tm, tn);
+  int z;
+  tile_coords((p.M + BM - 1) / BM, (p.N + BN - 1) / BN, tm, tn, z);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int z = blockIdx.y;
   const int kbeg = z * p.k_per_split;
   const int KT = (min(p.K, kbeg + p.k_per_split) - kbeg + kBK - 1) / kBK;
   const bool do_bias = BIAS_GRAD && tn == 0;
