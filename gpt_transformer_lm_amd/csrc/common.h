@@ -126,12 +126,55 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// The same resource as four dwords (base address bits 0-31 and 32-47, the
+// byte range, the format word) for the inline-assembly DMA below.
+typedef int i32x4_rsrc __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_rsrc make_rsrc4(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(size_t)base;
+  i32x4_rsrc r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)((uint32_t)(a >> 32) & 0xffffu);
+  r[2] = (int)bytes;
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Direct-to-LDS load of 16 bytes per lane: lane i's bytes at `voffset` (range
+// checked against the resource) land at lds + 16 i.  Issued as inline
+// assembly so that the compiler neither waits for it nor holds later LDS
+// reads behind it (for the builtin form it puts a full vmcnt(0) wait in front
+// of the next LDS read, which drains every later pipeline stage too).  The
+// caller owns the synchronisation: wait_vmcnt for its own lanes' data, then a
+// barrier before other waves read it.  `lds` must be wave-uniform.
+// M0 is listed as clobbered so that the scheduler orders the statement after
+// any earlier set-up of M0 and before any later one (the compiler sets M0
+// right before each of its own uses; it has no value to preserve across this).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_lds16(i32x4_rsrc rsrc, GPT2_LDS void* lds, uint32_t voffset) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+               :: "v"(voffset), "s"(m0), "s"(rsrc) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // s_waitcnt immediate that waits until at most N vector-memory operations of
 // this wave are outstanding (expcnt and lgkmcnt left at their no-wait maxima).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS operations
+// (lgkmcnt) but, unlike __syncthreads(), not for its outstanding global loads,
+// so that loads of later pipeline stages stay in flight across it.  A wave
+// must have waited (vmcnt) for any LDS data its DMA wrote and others read.
+// (The s_barrier intrinsic and __syncthreads() get a full vmcnt(0) wait in
+// front of them from the compiler; the inline form keeps only the LDS wait.
+// Its memory clobber stops the compiler from moving memory accesses across it.)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 #define GPT2_HIP_CHECK(expr)                                  \

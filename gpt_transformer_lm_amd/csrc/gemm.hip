@@ -198,7 +198,7 @@ struct DmaTile {
   // Rows beyond the operand's extent only feed discarded outputs (and the
   // buffer range turns reads past the allocation into zeros); k >= K must be
   // zero, which only the last, partial K step checks (k_tail).
-  __device__ __forceinline__ static void issue(__amdgpu_buffer_rsrc_t rs, GPT2_LDS char* tile, int wave, const Lane& L,
+  __device__ __forceinline__ static void issue(i32x4_rsrc rs, GPT2_LDS char* tile, int wave, const Lane& L,
                                                int k0, int K, int64_t ld, bool k_tail) {
 #pragma unroll
     for (int q = 0; q < NINST; ++q) {
@@ -217,8 +217,7 @@ struct DmaTile {
         off = L.base + (uint32_t)((int64_t)(k0 + qk) * ld * 2) + (L.c16 ^ u16);
         if (k_tail) ok = k0 + qk + L.sub < K;
       }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (GPT2_LDS void*)(tile + iq * 1024), 16,
-                                               (int)(ok ? off : kOutOfRange), 0, 0, 0);
+      dma_lds16(rs, (GPT2_LDS void*)(tile + iq * 1024), ok ? off : kOutOfRange);
     }
   }
 
@@ -296,7 +295,7 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   __shared__ __attribute__((aligned(16))) char epi_own[S::EPI_IN_STAGE ? 16 : S::AUX_BYTES];
   __shared__ __attribute__((aligned(16))) float bias_s[HAS_BIAS ? BN : 4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   int tm, tn;
   int z;
@@ -305,7 +304,7 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   const int kbeg = z * p.k_per_split;
   const int KT = (min(p.K, kbeg + p.k_per_split) - kbeg + kBK - 1) / kBK;
   const bool do_bias = BIAS_GRAD && tn == 0;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, p.a_bytes), rb = make_rsrc(p.B, p.b_bytes);
+  const i32x4_rsrc ra = make_rsrc4(p.A, p.a_bytes), rb = make_rsrc4(p.B, p.b_bytes);
 
   auto stage_ptr = [&](int s) -> GPT2_LDS char* {
     return (GPT2_LDS char*)(s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : st3);
@@ -332,7 +331,7 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   // trip for the whole tile).  aux_stage(j) gives the stage of its j-th part.
   auto issue_aux = [&](auto aux_stage) {
     using TX = DmaTile<BM, true>;
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.e.aux_in, p.aux_bytes);
+    const i32x4_rsrc rx = make_rsrc4(p.e.aux_in, p.aux_bytes);
     const typename TX::Lane lx = TX::lane_part(wave, lane, m0, p.e.ld_aux);
 #pragma unroll
     for (int c = 0; c < BN / 64; ++c) {
@@ -366,7 +365,7 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
         // stage s of this K step has landed (for this wave), then everyone's has
         if (kt + NS - 2 < KT) wait_vmcnt<(NS - 2) * NDMA>();
         else wait_vmcnt<0>();
-        __syncthreads();
+        lds_barrier();
         if (kt + NS - 1 < KT) issue(kt + NS - 1, (s + NS - 1) % NS);
         if constexpr (S::EARLY_AUX) {
           // last K step: every stage but s is idle
@@ -409,7 +408,7 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
           for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][i], b[kk & 1][j], acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[kk & 1][j], a[kk & 1][i], acc[i][j], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -437,8 +436,10 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   }
 
   // Epilogue, one 32 x 32 accumulator block at a time through this wave's own
-  // LDS block (LDS operations of one wave complete in order, so no barrier):
-  // element r of lane l sits at row 8(r/4) + 4(l/32) + r%4, column l%32.
+  // LDS block (LDS operations of one wave complete in order, so no barrier).
+  // The products were taken as B x A, so element r of lane l sits at row l%32,
+  // column 8(r/4) + 4(l/32) + r%4: four consecutive columns per 16-byte write.
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
   GPT2_LDS float* ep = reinterpret_cast<GPT2_LDS float*>(epi_lds) + wave * 32 * S::EP_PITCH;
   const int hi = lane >> 5;
 #pragma unroll
@@ -446,7 +447,12 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ep[(8 * (r >> 2) + 4 * hi + (r & 3)) * S::EP_PITCH + (lane & 31)] = acc[i][j][r];
+      for (int g = 0; g < 4; ++g) {
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = acc[i][j][4 * g + e];
+        *reinterpret_cast<GPT2_LDS f32x4*>(ep + (lane & 31) * S::EP_PITCH + 8 * g + 4 * hi) = w;
+      }
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
@@ -455,7 +461,6 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
         if (grow < p.M && gcol < p.N) {
           float v[8];
           {
-            typedef float f32x4 __attribute__((ext_vector_type(4)));
             const GPT2_LDS f32x4* q = reinterpret_cast<const GPT2_LDS f32x4*>(ep + rl * S::EP_PITCH + cc * 8);
             const f32x4 lo = q[0], hi4 = q[1];
 #pragma unroll
