@@ -67,7 +67,7 @@ __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x)
 // c sits at physical chunk swz(r, c).  Each of the 4 waves issues 2 of the 8
 // one-KiB instructions (instruction iq fills rows 8 iq .. 8 iq + 7; lane L
 // writes physical chunk L % 8 of row 8 iq + L / 8).
-__device__ __forceinline__ void tile_dma(__amdgpu_buffer_rsrc_t rs, GPT2_LDS char* tile, int wave, int lane,
+__device__ __forceinline__ void tile_dma(i32x4_rsrc rs, GPT2_LDS char* tile, int wave, int lane,
                                          int row0, int ld, int col0) {
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
@@ -75,15 +75,15 @@ __device__ __forceinline__ void tile_dma(__amdgpu_buffer_rsrc_t rs, GPT2_LDS cha
     const int r = 8 * iq + (lane >> 3);
     const int c = (lane & 7) ^ ((r ^ (r >> 3)) & 7);
     const uint32_t off = (uint32_t)(((int64_t)(row0 + r) * ld + col0 + c * 8) * 2);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (GPT2_LDS void*)(tile + iq * 1024), 16, (int)off, 0, 0, 0);
+    dma_lds16(rs, (GPT2_LDS void*)(tile + iq * 1024), off);
   }
 }
 
 // 64 consecutive fp32 values starting at element row0 into the first 256 bytes
 // of a 1-KiB LDS region (lanes 0..15 move 16 bytes each, the others zeros).
-__device__ __forceinline__ void vec_dma(__amdgpu_buffer_rsrc_t rs, GPT2_LDS char* dst, int lane, int row0) {
+__device__ __forceinline__ void vec_dma(i32x4_rsrc rs, GPT2_LDS char* dst, int lane, int row0) {
   const uint32_t off = lane < 16 ? (uint32_t)((row0 + 4 * lane) * 4) : kOut;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (GPT2_LDS void*)dst, 16, (int)off, 0, 0, 0);
+  dma_lds16(rs, (GPT2_LDS void*)dst, off);
 }
 
 // A-operand fragment, natural orientation: tile row row0 + lane % 32, k16 step s
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256, 4) void attn_fwd_mfma_kernel(int T, int H, con
   const int ld = 3 * C;
   const bf16* Bg = qkv + (size_t)b * T * ld;                 // row 0 of this sequence
   const bf16* Qg = Bg + h * HD;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(Bg, (uint32_t)((size_t)T * ld * 2));
+  const i32x4_rsrc rs = make_rsrc4(Bg, (uint32_t)((size_t)T * ld * 2));
   const int q0 = qt * ROWS, qw0 = q0 + wave * 32, myq = qw0 + (lane & 31);
   const float sl2 = scale * kLog2e;
 
@@ -180,6 +180,9 @@ __global__ __launch_bounds__(256, 4) void attn_fwd_mfma_kernel(int T, int H, con
     tile_dma(rs, base, wave, lane, st * STAGE, ld, C + h * HD);
     tile_dma(rs, base + TILE, wave, lane, st * STAGE, ld, 2 * C + h * HD);
   };
+  // the fragments loaded to registers above have landed: the compiler's own
+  // waits for them would otherwise sit in the loop and drain the DMA ring
+  wait_vmcnt<0>();
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < nst) issue(s);
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(256, 4) void attn_fwd_mfma_kernel(int T, int H, con
     // slot refilled next was last read in the previous iteration
     if (st + NS - 2 < nst) wait_vmcnt<(NS - 2) * 4>();
     else wait_vmcnt<0>();
-    __syncthreads();
+    lds_barrier();
     if (st + NS - 1 < nst) issue(st + NS - 1);
     const GPT2_LDS char* Kc = (const GPT2_LDS char*)ring[st % NS];
     const GPT2_LDS char* Vc = Kc + TILE;
@@ -275,10 +278,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
   const bf16* Kg = Bg + C + h * HD;
   const bf16* Vg = Bg + 2 * C + h * HD;
   const bf16* Og = dout + (size_t)b * T * C;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Bg, (uint32_t)((size_t)T * ld * 2));
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(Og, (uint32_t)((size_t)T * C * 2));
-  const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse2 + (size_t)bh * T, (uint32_t)(T * 4));
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc(Dv + (size_t)bh * T, (uint32_t)(T * 4));
+  const i32x4_rsrc rq = make_rsrc4(Bg, (uint32_t)((size_t)T * ld * 2));
+  const i32x4_rsrc ro = make_rsrc4(Og, (uint32_t)((size_t)T * C * 2));
+  const i32x4_rsrc rl = make_rsrc4(lse2 + (size_t)bh * T, (uint32_t)(T * 4));
+  const i32x4_rsrc rd = make_rsrc4(Dv + (size_t)bh * T, (uint32_t)(T * 4));
   const int k0 = ktile * ROWS, kw0 = k0 + wave * 32, mykey = kw0 + (lane & 31);
   const float sl2 = scale * kLog2e;
 
@@ -301,6 +304,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
     if (wave == 0) vec_dma(rl, base + 2 * TILE, lane, q0);
     if (wave == 1) vec_dma(rd, base + 2 * TILE + 1024, lane, q0);
   };
+  // the fragments loaded to registers above have landed: the compiler's own
+  // waits for them would otherwise sit in the loop and drain the DMA ring
+  wait_vmcnt<0>();
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < nst) issue(s);
@@ -309,7 +315,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
     // remain is sufficient for every wave
     if (st + NS - 2 < nst) wait_vmcnt<(NS - 2) * 4>();
     else wait_vmcnt<0>();
-    __syncthreads();
+    lds_barrier();
     if (st + NS - 1 < nst) issue(st + NS - 1);
     const GPT2_LDS char* Qs = (const GPT2_LDS char*)ring[st % NS];
     const GPT2_LDS char* Os = Qs + TILE;
@@ -392,7 +398,7 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dq_mfma_kernel(int T, int H, 
   const bf16* Bg = qkv + (size_t)b * T * ld;
   const bf16* Qg = Bg + h * HD;
   const bf16* Og = dout + (size_t)b * T * C + h * HD;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(Bg, (uint32_t)((size_t)T * ld * 2));
+  const i32x4_rsrc rs = make_rsrc4(Bg, (uint32_t)((size_t)T * ld * 2));
   const int q0 = qt * ROWS, qw0 = q0 + wave * 32, myq = qw0 + (lane & 31);
   const float sl2 = scale * kLog2e;
 
@@ -414,13 +420,16 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dq_mfma_kernel(int T, int H, 
     tile_dma(rs, base, wave, lane, st * STAGE, ld, C + h * HD);
     tile_dma(rs, base + TILE, wave, lane, st * STAGE, ld, 2 * C + h * HD);
   };
+  // the fragments loaded to registers above have landed: the compiler's own
+  // waits for them would otherwise sit in the loop and drain the DMA ring
+  wait_vmcnt<0>();
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < nst) issue(s);
   for (int st = 0; st < nst; ++st) {
     if (st + NS - 2 < nst) wait_vmcnt<(NS - 2) * 4>();
     else wait_vmcnt<0>();
-    __syncthreads();
+    lds_barrier();
     if (st + NS - 1 < nst) issue(st + NS - 1);
     const GPT2_LDS char* Ks = (const GPT2_LDS char*)ring[st % NS];
     const GPT2_LDS char* Vs = Ks + TILE;
