@@ -19,6 +19,7 @@ namespace {
 
 constexpr int kCeThreads = 1024;
 constexpr int kCeWaves = kCeThreads / 64;
+constexpr float kLog2eCe = 1.4426950408889634f;
 
 // (max, sum of exp(x - max)) pairs of a wave / block, combined so that the
 // sum is rescaled to the larger maximum.
@@ -99,6 +100,148 @@ __global__ __launch_bounds__(kCeThreads) void softmax_xent_kernel(int V, int Vp,
   }
 }
 
+// bf16 logits: the same result with far fewer vector instructions per
+// element (the generic form is bound by them rather than by HBM).  Per
+// element: the bf16 -> fp32 widening is a shift or mask, the exponential is
+// exp2 of one fused multiply-add, and it is kept in fp16 (relative to the
+// thread's own maximum, so in (0, 1]) in the registers that held the row, for
+// the write: g_j = e_j * exp(m_t - m) * dscale / s with the bracket one
+// per-thread constant.  The block reduction takes the maximum first, then
+// each thread rescales its sum once (one exponential per thread instead of
+// one per combining step).  Requires Vp <= NC * 8192 and (NC - 1) * 8192 <= V:
+// chunks c < NC - 1 are then whole columns j < V for every thread, and only
+// chunk NC - 1 checks the row end and the padding.  The label's -dscale is
+// applied afterwards by the thread that holds the label, with a 2-byte store
+// over its chunk.
+template <int NC>
+__global__ __launch_bounds__(kCeThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void softmax_xent_bf16_kernel(int V, int Vp, bf16* __restrict__ logits,
+                                                                       const int32_t* __restrict__ labels,
+                                                                       float* __restrict__ losses, float dscale) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  __shared__ float shm[kCeWaves], shs[kCeWaves];
+  __shared__ float s_zy;
+  const int row = blockIdx.x, tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  bf16* z = logits + (size_t)row * Vp;
+  int y = labels[row];
+  y = y < 0 ? 0 : (y >= V ? V - 1 : y);   // memory safety only; valid labels are in [0, V)
+  const int nch = Vp / 8, ych = y >> 3;
+  constexpr int L = NC - 1;                // the one chunk that may be partial or absent
+  const int chL = tid + kCeThreads * L;
+  const bool hasL = chL < nch;
+  // the row, two bf16 per word (element 2k in the low half of word k); buffer
+  // loads and stores with the chunk offset in a scalar register keep one
+  // address register per thread
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(z, (uint32_t)Vp * 2u);
+  const int voff = tid * 16;
+  uint32_t w[NC][4];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (c < L || hasL) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, kCeThreads * 16 * c, 0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[c][k] = v[k];
+    }
+  }
+  auto lo = [](uint32_t u) { return __uint_as_float(u << 16); };
+  auto hi = [](uint32_t u) { return __uint_as_float(u & 0xffff0000u); };
+  // label logit, from the registers of the thread that holds it
+  bool owner = false;
+  float zy = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (tid + kCeThreads * c == ych) {
+      owner = true;
+      uint32_t u = w[c][0];
+#pragma unroll
+      for (int k = 1; k < 4; ++k) u = ((y & 7) >> 1) == k ? w[c][k] : u;
+      zy = (y & 1) ? hi(u) : lo(u);
+      s_zy = zy;
+    }
+  }
+  float mt = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < L; ++c)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) mt = fmaxf(mt, fmaxf(lo(w[c][k]), hi(w[c][k])));
+  if (hasL) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (chL * 8 + 2 * k < V) mt = fmaxf(mt, lo(w[L][k]));
+      if (chL * 8 + 2 * k + 1 < V) mt = fmaxf(mt, hi(w[L][k]));
+    }
+  }
+  // the widened values of the maximum pass are not kept for the exponentials
+  // (56 more live registers); re-deriving them is one shift or mask each
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) asm volatile("" : "+v"(w[c][k]));
+  const float ml2 = mt * kLog2eCe;
+  float st = 0.f;
+  // exponentials of one word's pair, summed and returned as two fp16 (RNE)
+  auto exps = [&](uint32_t u, bool ok0, bool ok1) -> uint32_t {
+    float e0 = __builtin_amdgcn_exp2f(fmaf(lo(u), kLog2eCe, -ml2));
+    float e1 = __builtin_amdgcn_exp2f(fmaf(hi(u), kLog2eCe, -ml2));
+    e0 = ok0 ? e0 : 0.f;
+    e1 = ok1 ? e1 : 0.f;
+    st += e0 + e1;
+    const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)e0);
+    const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)e1);
+    return h0 | (h1 << 16);
+  };
+  // (scheduling barriers between chunks keep the live range of the
+  // temporaries to one chunk, so the kernel fits 64 registers: 2 blocks per CU)
+#pragma unroll
+  for (int c = 0; c < L; ++c) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[c][k] = exps(w[c][k], true, true);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (hasL) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[L][k] = exps(w[L][k], chL * 8 + 2 * k < V, chL * 8 + 2 * k + 1 < V);
+  }
+  // the packed exponentials are formed here, not sunk into the write pass
+  // (which would keep 56 fp32 values live across the reduction)
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) asm volatile("" : "+v"(w[c][k]));
+  float mb = mt;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mb = fmaxf(mb, __shfl_xor(mb, o, 64));
+  if (lane == 0) shm[wv] = mb;
+  __syncthreads();                          // also makes s_zy visible
+#pragma unroll
+  for (int i = 0; i < kCeWaves; ++i) mb = fmaxf(mb, shm[i]);
+  const float r = __builtin_amdgcn_exp2f((mt - mb) * kLog2eCe);   // 0 for a thread with no columns
+  const float sw = wave_sum(st * r);
+  if (lane == 0) shs[wv] = sw;
+  __syncthreads();
+  float sb = 0.f;
+#pragma unroll
+  for (int i = 0; i < kCeWaves; ++i) sb += shs[i];
+  if (tid == 0) losses[row] = mb + logf(sb) - s_zy;
+  const float scale = r * (dscale / sb);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (c < L || hasL) {
+      u32x4 o;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float g0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[c][k] & 0xffffu)) * scale;
+        const float g1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[c][k] >> 16)) * scale;
+        const uint32_t b0 = __builtin_bit_cast(uint16_t, (bf16)g0);
+        const uint32_t b1 = __builtin_bit_cast(uint16_t, (bf16)g1);
+        o[k] = b0 | (b1 << 16);
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(o, rs, voff, kCeThreads * 16 * c, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if (owner) z[y] = (bf16)(__builtin_amdgcn_exp2f(fmaf(zy, kLog2eCe, -ml2)) * scale - dscale);
+}
+
 __global__ __launch_bounds__(1024) void sum_scaled_kernel(int n, const float* __restrict__ x, float scale,
                                                           float* __restrict__ out) {
   __shared__ float sh[16];
@@ -122,6 +265,15 @@ int launch_t(int N, int V, int Vp, void* logits, const int32_t* labels, float* l
   const int need = (nch + kCeThreads - 1) / kCeThreads;
   T* L = (T*)logits;
   mark_begin(0, s);
+  if constexpr (sizeof(T) == 2) {
+    if (need <= 7 && 6 * 8 * kCeThreads <= V) {   // the bf16 kernel's precondition for NC = 7
+      hipLaunchKernelGGL((softmax_xent_bf16_kernel<7>), dim3(N), dim3(kCeThreads), 0, s, V, Vp, L, labels, losses,
+                         dscale);
+      GPT2_LAUNCH_CHECK();
+      mark_end(0, s);
+      return 0;
+    }
+  }
   if (need <= 1)
     hipLaunchKernelGGL((softmax_xent_kernel<T, 1>), dim3(N), dim3(kCeThreads), 0, s, V, Vp, L, labels, losses, dscale);
   else if (need <= 2)
