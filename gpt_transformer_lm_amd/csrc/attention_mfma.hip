@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256, 4) void attn_fwd_mfma_kernel(int T, int H, con
                                                             float scale) {
   constexpr int NS = NS_FWD;
   __shared__ __attribute__((aligned(1024))) char ring[NS][2 * TILE];   // K tile, V tile
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hi = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), hi = lane >> 5;
   const int nqt = (T + ROWS - 1) / ROWS;
   const int qt = nqt - 1 - (int)blockIdx.x;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
                                                                  bf16* __restrict__ dqkv, float scale) {
   constexpr int NS = NS_DKDV;
   __shared__ __attribute__((aligned(1024))) char ring[NS][KV_STAGE_BYTES];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ktile = (int)blockIdx.x;           // lower key tiles see more queries: launch them first
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int C = H * HD;
@@ -322,18 +322,31 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
     const GPT2_LDS float* Ls = reinterpret_cast<const GPT2_LDS float*>(Qs + 2 * TILE);
     const GPT2_LDS float* Ds = reinterpret_cast<const GPT2_LDS float*>(Qs + 2 * TILE + 1024);
     const int q0 = qbeg + st * STAGE;
+    // Both 32-query slices' score products first, then each slice's
+    // softmax-gradient work and its dV / dK products: the second slice's
+    // S and dP run on the matrix cores while the first slice's exponentials
+    // run on the vector units, and the first slice's dV / dK products while
+    // the second slice's do.
+    floatx16 s[2], dp[2];
+    bool ok[2];
 #pragma unroll
-    for (int qs = 0; qs < STAGE; qs += 32) {
-      const int qb = q0 + qs;
-      if (qb + 31 >= kw0 && qb < T && kw0 < T) {
-        floatx16 s, dp;
+    for (int u2 = 0; u2 < 2; ++u2) {
+      const int qs = 32 * u2, qb = q0 + qs;
+      ok[u2] = qb + 31 >= kw0 && qb < T && kw0 < T;
+      if (ok[u2]) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+        for (int r = 0; r < 16; ++r) { s[u2][r] = 0.f; dp[u2][r] = 0.f; }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          s = mfma(frag_nat(Qs, qs, k, lane), kf[k], s);
-          dp = mfma(frag_nat(Os, qs, k, lane), vf[k], dp);
+          s[u2] = mfma(frag_nat(Qs, qs, k, lane), kf[k], s[u2]);
+          dp[u2] = mfma(frag_nat(Os, qs, k, lane), vf[k], dp[u2]);
         }
+      }
+    }
+#pragma unroll
+    for (int u2 = 0; u2 < 2; ++u2) {
+      const int qs = 32 * u2, qb = q0 + qs;
+      if (ok[u2]) {
         // s[r]: query qb + acc_row(r), key mykey.  The lane's 16 query rows are
         // qs + 4 hi + 8 g + 0..3 (g = 0..3): four 16-byte reads each of L2 and D.
         typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -351,17 +364,17 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int q = qb + acc_row(r, lane);
-            p[r] = (mykey > q || q >= T) ? 0.f : ex2(fmaf(s[r], sl2, -lv[r]));
+            p[r] = (mykey > q || q >= T) ? 0.f : ex2(fmaf(s[u2][r], sl2, -lv[r]));
           }
         } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) p[r] = ex2(fmaf(s[r], sl2, -lv[r]));
+          for (int r = 0; r < 16; ++r) p[r] = ex2(fmaf(s[u2][r], sl2, -lv[r]));
         }
         bf16x8 pb[2], db[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           pb[r >> 3][r & 7] = (bf16)p[r];
-          db[r >> 3][r & 7] = (bf16)(p[r] * (dp[r] - dv_[r]));
+          db[r >> 3][r & 7] = (bf16)(p[r] * (dp[u2][r] - dv_[r]));
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u)
@@ -389,7 +402,7 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dq_mfma_kernel(int T, int H, 
                                                                bf16* __restrict__ dqkv, float scale) {
   constexpr int NS = NS_DQ;
   __shared__ __attribute__((aligned(1024))) char ring[NS][2 * TILE];   // K tile, V tile
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nqt = (T + ROWS - 1) / ROWS;
   const int qt = nqt - 1 - (int)blockIdx.x;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
