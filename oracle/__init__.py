@@ -23,5 +23,9 @@ from .gpt2_oracle import (  # noqa: F401
     gpt2_forward,
     gpt2_backward,
     gpt2_step,
+    accumulate_grads,
+    global_grad_norm,
+    clip_factor,
+    gpt2_step_accumulated,
 )
 from .init_rng import splitmix64_stream, gpt2_init_params  # noqa: F401

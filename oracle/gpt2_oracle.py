@@ -41,7 +41,9 @@ Pins (see tests/test_oracle_*.py): finite differences in float64, torch CPU
 float64 library routines for single layers and a whole-model autograd check,
 the closed form of the initial loss, the exact ln V loss with a zero token
 table, causality, softmax row sums, AdamW's closed form at t = 1 and brute
-force loops for the encoder scatter.
+force loops for the encoder scatter; for accumulation and clipping, the
+identity with the concatenated batch, the clipping closed forms and torch's
+clip_grad_norm_ + AdamW on the whole tiny model.
 """
 
 from __future__ import annotations
@@ -350,3 +352,64 @@ def gpt2_step(params, tokens, targets, cfg: OracleConfig, adam_state, lr, beta1,
                                               beta2, eps, wd, t)
         new_state[name] = (m, v)
     return loss, grads, new_params, new_state
+
+
+# --------------------------------------------------------------------------
+# Gradient accumulation and global-norm clipping
+# --------------------------------------------------------------------------
+# The page "State of the Union [May 3, 2024]" lists both as pending work for
+# the GPT-2 miniseries (section "Functional") and gives no formula, so the
+# readings are the standard ones:
+# * accumulation over k equal micro-batches is the gradient of the mean of
+#   their mean losses, (1/k) sum_i grad_i -- the gradient of the mean loss
+#   over the concatenated batch;
+# * clipping takes the L2 norm n of all parameter gradients as one vector
+#   and, when n exceeds max_norm > 0, multiplies every gradient by
+#   max_norm / n (no epsilon); max_norm <= 0 leaves them as they are.
+
+def accumulate_grads(grad_list):
+    """(1/k) sum of k gradient dicts."""
+    k = len(grad_list)
+    out = {name: np.zeros_like(g) for name, g in grad_list[0].items()}
+    for g in grad_list:
+        for name in out:
+            out[name] = out[name] + g[name] / k
+    return out
+
+
+def global_grad_norm(grads):
+    """L2 norm of all gradients taken as one vector (accumulated in float64)."""
+    total = 0.0
+    for g in grads.values():
+        total += float(np.sum(np.asarray(g, dtype=np.float64) ** 2))
+    return math.sqrt(total)
+
+
+def clip_factor(norm, max_norm):
+    """max_norm / norm when norm > max_norm > 0, else 1."""
+    return max_norm / norm if (max_norm > 0 and norm > max_norm) else 1.0
+
+
+def gpt2_step_accumulated(params, micro_batches, cfg: OracleConfig, adam_state, lr, beta1, beta2, eps, wd, t,
+                          max_grad_norm=0.0):
+    """Forward + backward over each (tokens, targets) micro-batch, accumulated
+    gradients, global-norm clipping, AdamW.  Returns (losses, grads, norm,
+    new_params, new_state) with grads and norm before clipping."""
+    losses, glist = [], []
+    for tokens, targets in micro_batches:
+        loss, _, _, cache = gpt2_forward(params, tokens, targets, cfg)
+        losses.append(loss)
+        glist.append(gpt2_backward(params, cache, cfg))
+    grads = accumulate_grads(glist)
+    norm = global_grad_norm(grads)
+    s = clip_factor(norm, max_grad_norm)
+    new_params, new_state = {}, {}
+    for name, theta in params.items():
+        if adam_state is None:
+            m = np.zeros_like(theta)
+            v = np.zeros_like(theta)
+        else:
+            m, v = adam_state[name]
+        new_params[name], m, v = adamw_update(theta, grads[name] * s, m, v, lr, beta1, beta2, eps, wd, t)
+        new_state[name] = (m, v)
+    return losses, grads, norm, new_params, new_state

@@ -254,3 +254,66 @@ def test_planted_mistakes_are_caught(mistake, monkeypatch, fd_problem):
     grads = G.gpt2_backward(params, cache, cfg)
     worst = _fd_check(params, tok, tgt, cfg, grads, per_tensor=6)
     assert max(worst.values()) > 1e-3, worst
+
+
+# ------------------------------------------------ accumulation and clipping
+
+def test_accumulation_equals_gradient_of_concatenated_batch():
+    # k equal micro-batches accumulated with 1/k each = the gradient of the
+    # mean loss over the whole batch (a dropped 1/k, or an overwrite instead of
+    # a sum, fails this)
+    cfg = TINY
+    params = oracle_params(cfg, 21)
+    tok, tgt = S.uniform_batch(4, 32, cfg.vocab_size, seed=9)
+    _, _, _, cache = O.gpt2_forward(params, tok, tgt, cfg)
+    full = O.gpt2_backward(params, cache, cfg)
+    glist = []
+    for i in range(2):
+        _, _, _, c = O.gpt2_forward(params, tok[2 * i:2 * i + 2], tgt[2 * i:2 * i + 2], cfg)
+        glist.append(O.gpt2_backward(params, c, cfg))
+    acc = O.accumulate_grads(glist)
+    for k in params:
+        assert rel(acc[k], full[k]) < 1e-12, k
+
+
+def test_clip_factor_closed_forms():
+    g = {"a": np.array([3.0, 0.0]), "b": np.array([[4.0]])}
+    n = O.global_grad_norm(g)
+    assert n == 5.0
+    assert O.clip_factor(n, 1.0) == 0.2          # clipped to norm 1
+    assert O.clip_factor(n, 10.0) == 1.0         # below the threshold: unchanged
+    assert O.clip_factor(n, 5.0) == 1.0          # at the threshold: unchanged
+    assert O.clip_factor(n, 0.0) == 1.0          # disabled
+    clipped = {k: v * O.clip_factor(n, 2.5) for k, v in g.items()}
+    assert abs(O.global_grad_norm(clipped) - 2.5) < 1e-15
+
+
+def test_accumulated_clipped_step_matches_torch():
+    # oracle: two micro-batches, clipping active, AdamW; torch: autograd of the
+    # mean loss over the whole batch, torch.nn.utils.clip_grad_norm_, AdamW
+    cfg = TINY
+    params = oracle_params(cfg, 23)
+    tok, tgt = S.uniform_batch(4, 32, cfg.vocab_size, seed=13)
+    micro = [(tok[:2], tgt[:2]), (tok[2:], tgt[2:])]
+    lr, b1, b2, eps, wd = 1e-3, 0.9, 0.95, 1e-8, 0.1
+    _, grads, norm, new_params, _ = O.gpt2_step_accumulated(params, micro, cfg, None, lr, b1, b2, eps, wd, 1,
+                                                            max_grad_norm=0.0)
+    max_norm = 0.3 * norm                        # so that clipping is active
+    _, _, norm2, new_params, _ = O.gpt2_step_accumulated(params, micro, cfg, None, lr, b1, b2, eps, wd, 1,
+                                                         max_grad_norm=max_norm)
+    assert norm2 == norm
+    tp = {k: torch.nn.Parameter(torch.tensor(v, dtype=torch.float64)) for k, v in params.items()}
+    loss = torch_gpt2_loss(tp, torch.tensor(tok, dtype=torch.long), torch.tensor(tgt, dtype=torch.long), cfg)
+    loss.backward()
+    tn = torch.nn.utils.clip_grad_norm_(list(tp.values()), max_norm)
+    assert abs(tn.item() - norm) / norm < 1e-10
+    s = O.clip_factor(norm, max_norm)
+    assert abs(s - 0.3) < 1e-12
+    for k in params:
+        # the clipped gradients themselves (AdamW's first step hides the scale)
+        assert rel(grads[k] * s, tp[k].grad.numpy()) < 1e-5, k
+    opt = torch.optim.AdamW(list(tp.values()), lr=lr, betas=(b1, b2), eps=eps, weight_decay=wd)
+    opt.step()
+    for k in params:
+        # torch scales by max_norm / (norm + 1e-6); the oracle by max_norm / norm
+        assert rel(new_params[k], tp[k].detach().numpy()) < 1e-6, k
