@@ -23,7 +23,10 @@ namespace {
 
 __global__ void adamw_kernel(int64_t n, float* __restrict__ master, const float* __restrict__ grad,
                              float* __restrict__ mom1, float* __restrict__ mom2, bf16* __restrict__ pbf,
-                             float lr, float b1, float b2, float eps, float wd, float c1, float c2) {
+                             float lr, float b1, float b2, float eps, float wd, float c1, float c2,
+                             const float* __restrict__ gscale) {
+  // the gradient enters scaled by *gscale (global-norm clipping) when given
+  const float gs = gscale ? *gscale : 1.0f;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
   for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
     if (i + 4 <= n) {
@@ -31,7 +34,7 @@ __global__ void adamw_kernel(int64_t n, float* __restrict__ master, const float*
       float4 g = *reinterpret_cast<const float4*>(grad + i);
       float4 m = *reinterpret_cast<const float4*>(mom1 + i);
       float4 v = *reinterpret_cast<const float4*>(mom2 + i);
-      float tv[4] = {th.x, th.y, th.z, th.w}, gv[4] = {g.x, g.y, g.z, g.w};
+      float tv[4] = {th.x, th.y, th.z, th.w}, gv[4] = {g.x * gs, g.y * gs, g.z * gs, g.w * gs};
       float mv[4] = {m.x, m.y, m.z, m.w}, vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -52,8 +55,9 @@ __global__ void adamw_kernel(int64_t n, float* __restrict__ master, const float*
       }
     } else {
       for (int64_t j = i; j < n; ++j) {
-        float mv = b1 * mom1[j] + (1.0f - b1) * grad[j];
-        float vv = b2 * mom2[j] + (1.0f - b2) * grad[j] * grad[j];
+        const float gj = grad[j] * gs;
+        float mv = b1 * mom1[j] + (1.0f - b1) * gj;
+        float vv = b2 * mom2[j] + (1.0f - b2) * gj * gj;
         float th = master[j];
         th -= lr * ((mv * c1) / (sqrtf(vv * c2) + eps) + wd * th);
         master[j] = th;
@@ -62,6 +66,47 @@ __global__ void adamw_kernel(int64_t n, float* __restrict__ master, const float*
         if (pbf) pbf[j] = (bf16)th;
       }
     }
+  }
+}
+
+// Global gradient norm for clipping: per-block partial sums of squares (a
+// fixed grid, grid-stride float4 reads), then one block adds the partials in
+// index order (deterministic), takes the square root and the clipping factor
+// max_norm / norm when norm > max_norm > 0, else 1.
+constexpr int kNormBlocks = 1024;
+
+__global__ __launch_bounds__(256) void grad_sumsq_kernel(int64_t n, const float* __restrict__ g,
+                                                         float* __restrict__ partial) {
+  float s = 0.f;
+  const int64_t n4 = n / 4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    const float4 v = reinterpret_cast<const float4*>(g)[i];
+    s += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  if (blockIdx.x == 0)
+    for (int64_t j = n4 * 4 + threadIdx.x; j < n; j += 256) s += g[j] * g[j];
+  __shared__ float sh[4];
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) partial[blockIdx.x] = (sh[0] + sh[1]) + (sh[2] + sh[3]);
+}
+
+__global__ __launch_bounds__(256) void grad_norm_finalize_kernel(const float* __restrict__ partial, int np,
+                                                                 float max_norm, float* __restrict__ out) {
+  __shared__ double sh[256];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < np; i += 256) s += (double)partial[i];
+  sh[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) sh[threadIdx.x] += sh[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const float norm = (float)sqrt(sh[0]);
+    out[0] = norm;
+    out[1] = (max_norm > 0.f && norm > max_norm) ? max_norm / norm : 1.0f;
   }
 }
 
@@ -136,8 +181,21 @@ unsigned blocks_for(int64_t n, int per_thread = 1) {
 
 }  // namespace
 
+size_t grad_norm_workspace_bytes() { return (kNormBlocks + 2) * sizeof(float); }
+
+int grad_norm(int64_t n, const float* grad, float max_norm, float* workspace, hipStream_t stream) {
+  if (n < 0 || !grad || !workspace) return gpt2_internal_fail(1, "grad_norm: bad arguments");
+  if ((uintptr_t)grad % 16) return gpt2_internal_fail(1, "grad_norm: gradient must be 16-byte aligned");
+  hipLaunchKernelGGL(grad_sumsq_kernel, dim3(kNormBlocks), dim3(256), 0, stream, n, grad, workspace + 2);
+  GPT2_LAUNCH_CHECK();
+  hipLaunchKernelGGL(grad_norm_finalize_kernel, dim3(1), dim3(256), 0, stream, workspace + 2, kNormBlocks,
+                     max_norm, workspace);
+  GPT2_LAUNCH_CHECK();
+  return 0;
+}
+
 int adamw(int64_t n, float* master, const float* grad, float* m, float* v, bf16* param_bf16, float lr,
-          float beta1, float beta2, float eps, float wd, int t, hipStream_t stream) {
+          float beta1, float beta2, float eps, float wd, int t, hipStream_t stream, const float* gscale) {
   if (n < 0 || !master || !grad || !m || !v || t < 1) return gpt2_internal_fail(1, "adamw: bad arguments");
   if (n == 0) return 0;
   if (((uintptr_t)master | (uintptr_t)grad | (uintptr_t)m | (uintptr_t)v) % 16 ||
@@ -148,7 +206,7 @@ int adamw(int64_t n, float* master, const float* grad, float* m, float* v, bf16*
   unsigned grid = (unsigned)std::min<int64_t>(ceil_div64(n, 4 * 256), 8192);
   mark_begin(0, stream);
   hipLaunchKernelGGL(adamw_kernel, dim3(grid), dim3(256), 0, stream, n, master, grad, m, v, param_bf16, lr, beta1,
-                     beta2, eps, wd, (float)c1, (float)c2);
+                     beta2, eps, wd, (float)c1, (float)c2, gscale);
   GPT2_LAUNCH_CHECK();
   mark_end(0, stream);
   return 0;

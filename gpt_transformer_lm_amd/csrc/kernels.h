@@ -128,8 +128,15 @@ int encoder_backward_sorted(int B, int T, int C, const uint32_t* sorted, const f
 
 // ------------------------------------------------------------------ optimizer
 // AdamW over n fp32 parameters; writes the bf16 copy if param_bf16 != null.
+// With gscale (device, one float) every gradient enters multiplied by *gscale.
 int adamw(int64_t n, float* master, const float* grad, float* m, float* v, bf16* param_bf16,
-          float lr, float beta1, float beta2, float eps, float wd, int t, hipStream_t stream);
+          float lr, float beta1, float beta2, float eps, float wd, int t, hipStream_t stream,
+          const float* gscale = nullptr);
+// Global L2 norm of n fp32 gradients (16-byte aligned) into workspace[0] and
+// the clipping factor (max_norm / norm if norm > max_norm > 0, else 1) into
+// workspace[1]; workspace holds grad_norm_workspace_bytes() (device).
+size_t grad_norm_workspace_bytes();
+int grad_norm(int64_t n, const float* grad, float max_norm, float* workspace, hipStream_t stream);
 // dst = RNE bf16 of src.
 int cast_f32_to_bf16(int64_t n, const float* src, bf16* dst, hipStream_t stream);
 // dst[b][c][r] = src[b][r][c] for `batches` bf16 matrices [R, Cc]; R, Cc multiples of 8.

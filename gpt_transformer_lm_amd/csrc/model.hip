@@ -150,6 +150,7 @@ struct Layout {
   std::vector<size_t> resid;             // L + 1 buffers [BT, C]
   std::vector<LayerOffsets> layer;
   size_t tokens, lnf, lnf_mean, lnf_rstd, logits, losses, mean_loss;
+  size_t gnorm;                          // gradient norm, clipping factor, per-block partial sums
   size_t dres, dres_t, d_ln, d_big, d_qkv, scratch;
   size_t sorted_keys;                    // encoder-backward key sort (computed during the forward)
   size_t scratch_bytes;
@@ -221,6 +222,7 @@ void make_layout(const gpt2_config& c, Layout* lo) {
   lo->logits = p.alloc(BT * (size_t)c.padded_vocab_size * es);
   lo->losses = p.alloc(BT * 4);
   lo->mean_loss = p.alloc(4);
+  lo->gnorm = p.alloc(grad_norm_workspace_bytes());
   lo->dres = p.alloc(BT * C * 4);
   lo->dres_t = c.dtype == GPT2_BF16 ? p.alloc(BT * C * es) : lo->dres;
   lo->d_ln = p.alloc(BT * C * es);
@@ -384,7 +386,9 @@ GemmDesc dw_desc(gpt2_model* m, int M, int N, int K, const void* dy, const void*
   return d;
 }
 
-int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets) {
+// loss_scale: the dlogits (and so every gradient of the next backward) are
+// those of loss_scale x the mean loss.
+int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets, float loss_scale) {
   const gpt2_config& c = m->cfg;
   const int B = c.batch_size, T = c.seq_len, C = c.channels, H = c.num_heads, hd = C / H;
   const int BT = B * T, Vp = c.padded_vocab_size, V = c.vocab_size;
@@ -392,7 +396,6 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets) {
   hipStream_t s = m->stream;
   Layout& lo = m->lo;
   m->have_dlogits = false;
-  m->have_grads = false;
   // keep a copy of the ids for the encoder backward (the caller may reuse its buffer)
   int32_t* tok = m->at<int32_t>(lo.tokens);
   if (m->side_pending) {   // the previous sort still reads the ids
@@ -448,7 +451,8 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets) {
                                     m->at<char>(lo.logits), nullptr, nullptr, nullptr)));
   if (targets) {
     RC(timed(m, S_XENT, 0.0, 2.0 * BT * (double)Vp * es + BT * 8.0, [&] {
-      return softmax_xent(dt, BT, V, Vp, m->at<char>(lo.logits), targets, m->at<float>(lo.losses), 1.0f / BT, s);
+      return softmax_xent(dt, BT, V, Vp, m->at<char>(lo.logits), targets, m->at<float>(lo.losses), loss_scale / BT,
+                          s);
     }));
     RC(sum_scaled(BT, m->at<float>(lo.losses), 1.0f / BT, m->at<float>(lo.mean_loss), s));
     m->have_dlogits = true;
@@ -456,7 +460,9 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets) {
   return 0;
 }
 
-int backward_impl(gpt2_model* m) {
+// acc: parameter gradients are added to the ones held (gradient accumulation)
+// instead of overwriting them.
+int backward_impl(gpt2_model* m, bool acc) {
   const gpt2_config& c = m->cfg;
   const int B = c.batch_size, T = c.seq_len, C = c.channels, H = c.num_heads, hd = C / H;
   const int BT = B * T, Vp = c.padded_vocab_size, V = c.vocab_size, L = c.num_layers;
@@ -481,32 +487,32 @@ int backward_impl(gpt2_model* m) {
 
   // classifier: d_lnf = dz wte;  d_wte = dz^T lnf (overwrite; padded rows get exactly 0)
   RC(run_gemm(m, S_CLS_DX, dx_desc(m, BT, Vp, C, logits, m->param(0), m->wt(0, 0), d_ln, EPI_STORE, nullptr)));
-  RC(run_gemm(m, S_CLS_DW, dw_desc(m, BT, Vp, C, logits, m->at<char>(lo.lnf), m->lgrad(0, 0), nullptr, false)));
+  RC(run_gemm(m, S_CLS_DW, dw_desc(m, BT, Vp, C, logits, m->at<char>(lo.lnf), m->lgrad(0, 0), nullptr, acc)));
   RC(timed(m, S_LN_BWD, 0.0, ln_bwd_bytes(true), [&] {
     return layernorm_backward(dt, BT, C, d_ln, m->at<char>(lo.resid[L]), m->param(14), m->at<float>(lo.lnf_mean),
                               m->at<float>(lo.lnf_rstd), dres, true, dres_copy, m->lgrad(14, 0), m->lgrad(15, 0),
-                              false, m->scratch(), sb, s);
+                              acc, m->scratch(), sb, s);
   }));
   for (int l = L - 1; l >= 0; --l) {
     LayerOffsets& o = lo.layer[l];
     // x_{l+1} = h + g Wp^T + bp
     RC(run_gemm(m, S_FCPROJ_DW, dw_desc(m, BT, C, 4 * C, dres_t, m->at<char>(o.g), m->lgrad(12, l),
-                                        m->lgrad(13, l), false)));
+                                        m->lgrad(13, l), acc)));
     // du = (dy W_p) * GELU'(u), the derivative saved by the forward
     RC(run_gemm(m, S_FCPROJ_DX, dx_desc(m, BT, C, 4 * C, dres_t, m->lparam(12, l), m->wt(12, l), d_big, EPI_MUL,
                                         m->at<char>(o.u))));
     // u = ln2 Wfc^T + bfc   (d_big now holds du)
     RC(run_gemm(m, S_FC_DW, dw_desc(m, BT, 4 * C, C, d_big, m->at<char>(o.ln2), m->lgrad(10, l),
-                                    m->lgrad(11, l), false)));
+                                    m->lgrad(11, l), acc)));
     RC(run_gemm(m, S_FC_DX, dx_desc(m, BT, 4 * C, C, d_big, m->lparam(10, l), m->wt(10, l), d_ln, EPI_STORE, nullptr)));
     RC(timed(m, S_LN_BWD, 0.0, ln_bwd_bytes(false), [&] {
       return layernorm_backward(dt, BT, C, d_ln, m->at<char>(o.h), m->lparam(8, l), m->at<float>(o.ln2_mean),
                                 m->at<float>(o.ln2_rstd), dres, false, dres_copy, m->lgrad(8, l), m->lgrad(9, l),
-                                false, m->scratch(), sb, s);
+                                acc, m->scratch(), sb, s);
     }));
     // h = x + atty Wo^T + bo
     RC(run_gemm(m, S_ATTPROJ_DW, dw_desc(m, BT, C, C, dres_t, m->at<char>(o.atty), m->lgrad(6, l),
-                                         m->lgrad(7, l), false)));
+                                         m->lgrad(7, l), acc)));
     RC(run_gemm(m, S_ATTPROJ_DX, dx_desc(m, BT, C, C, dres_t, m->lparam(6, l), m->wt(6, l), d_ln, EPI_STORE, nullptr)));
     {
       // three kernels: D = rowsum(dO * O); dK, dV (recomputing S and dP); dQ
@@ -523,23 +529,23 @@ int backward_impl(gpt2_model* m) {
     }
     // qkv = ln1 Wqkv^T + bqkv
     RC(run_gemm(m, S_QKV_DW, dw_desc(m, BT, 3 * C, C, d_qkv, m->at<char>(o.ln1), m->lgrad(4, l),
-                                     m->lgrad(5, l), false)));
+                                     m->lgrad(5, l), acc)));
     RC(run_gemm(m, S_QKV_DX, dx_desc(m, BT, 3 * C, C, d_qkv, m->lparam(4, l), m->wt(4, l), d_ln, EPI_STORE, nullptr)));
     RC(timed(m, S_LN_BWD, 0.0, ln_bwd_bytes(false), [&] {
       return layernorm_backward(dt, BT, C, d_ln, m->at<char>(lo.resid[l]), m->lparam(2, l),
                                 m->at<float>(o.ln1_mean), m->at<float>(o.ln1_rstd), dres, false, dres_copy,
-                                m->lgrad(2, l), m->lgrad(3, l), false, m->scratch(), sb, s);
+                                m->lgrad(2, l), m->lgrad(3, l), acc, m->scratch(), sb, s);
     }));
   }
-  // encoder: wpe rows >= T get no gradient
+  // encoder: wpe rows >= T get no gradient (zero already when accumulating)
   float* dwpe = m->lgrad(1, 0);
-  RC(fill_f32((int64_t)(c.max_seq_len - T) * C, dwpe + (size_t)T * C, 0.f, s));
+  if (!acc) RC(fill_f32((int64_t)(c.max_seq_len - T) * C, dwpe + (size_t)T * C, 0.f, s));
   if (m->side_pending) {
     GPT2_HIP_CHECK(hipStreamWaitEvent(s, m->ev_join, 0));
     m->side_pending = false;
   }
-  RC(encoder_backward_sorted(B, T, C, m->at<uint32_t>(lo.sorted_keys), dres, m->lgrad(0, 0), dwpe, false, m->scratch(), sb,
-                      s));
+  RC(encoder_backward_sorted(B, T, C, m->at<uint32_t>(lo.sorted_keys), dres, m->lgrad(0, 0), dwpe, acc, m->scratch(),
+                             sb, s));
   (void)Vp;
   return 0;
 }
@@ -718,9 +724,16 @@ void gpt2_destroy(gpt2_model* m) {
 }
 
 int gpt2_forward(gpt2_model* m, const int32_t* d_tokens, const int32_t* d_targets, float* mean_loss) {
+  return gpt2_forward_scaled(m, d_tokens, d_targets, 1.0f, mean_loss);
+}
+
+int gpt2_forward_scaled(gpt2_model* m, const int32_t* d_tokens, const int32_t* d_targets, float loss_scale,
+                        float* mean_loss) {
   if (!m || !d_tokens) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "forward: NULL model or tokens");
   if (d_targets && !mean_loss) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "forward: mean_loss is NULL");
-  RC(forward_impl(m, d_tokens, d_targets));
+  if (!isfinite(loss_scale))
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "forward: loss_scale must be finite");
+  RC(forward_impl(m, d_tokens, d_targets, loss_scale));
   if (d_targets) {
     GPT2_HIP_CHECK(hipMemcpyAsync(mean_loss, m->at<float>(m->lo.mean_loss), sizeof(float), hipMemcpyDeviceToHost,
                                   m->stream));
@@ -732,24 +745,47 @@ int gpt2_forward(gpt2_model* m, const int32_t* d_tokens, const int32_t* d_target
 int gpt2_backward(gpt2_model* m) {
   if (!m) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "backward: NULL model");
   if (!m->have_dlogits) return gpt2_internal_fail(GPT2_E_STATE, "backward needs a forward with targets first");
-  RC(backward_impl(m));
+  RC(backward_impl(m, false));
   m->have_dlogits = false;
   m->have_grads = true;
   return GPT2_OK;
 }
 
+int gpt2_backward_accumulate(gpt2_model* m) {
+  if (!m) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "backward: NULL model");
+  if (!m->have_dlogits) return gpt2_internal_fail(GPT2_E_STATE, "backward needs a forward with targets first");
+  if (!m->have_grads)
+    return gpt2_internal_fail(GPT2_E_STATE, "backward_accumulate needs gradients from a backward since the last update");
+  RC(backward_impl(m, true));
+  m->have_dlogits = false;
+  return GPT2_OK;
+}
+
 int gpt2_adamw_step(gpt2_model* m, float lr, float beta1, float beta2, float eps, float weight_decay, int32_t t) {
+  return gpt2_adamw_step_clipped(m, lr, beta1, beta2, eps, weight_decay, t, 0.0f, nullptr);
+}
+
+int gpt2_adamw_step_clipped(gpt2_model* m, float lr, float beta1, float beta2, float eps, float weight_decay,
+                            int32_t t, float max_grad_norm, float* grad_norm_out) {
   if (!m) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "adamw: NULL model");
   if (t < 1) return gpt2_internal_fail(GPT2_E_STATE, "adamw: t must be >= 1");
   if (!m->have_grads) return gpt2_internal_fail(GPT2_E_STATE, "adamw needs a completed backward first");
+  // the norm (and the clipping factor, read by the update on the device) only when asked for
+  float* gn = m->at<float>(m->lo.gnorm);
+  const bool need_norm = max_grad_norm > 0.f || grad_norm_out != nullptr;
+  if (need_norm) RC(grad_norm(m->lo.P, m->grad(), max_grad_norm, gn, m->stream));
   // fp32 master, m, v read and written, fp32 gradient read, bf16 copy written
   RC(timed(m, S_ADAMW, 0.0, (double)m->lo.P * (m->cfg.dtype == GPT2_BF16 ? 30.0 : 28.0), [&] {
     return adamw(m->lo.P, m->master(), m->grad(), m->at<float>(m->lo.adam_m), m->at<float>(m->lo.adam_v),
                  m->cfg.dtype == GPT2_BF16 ? m->at<bf16>(m->lo.params_bf16) : nullptr, lr, beta1, beta2, eps,
-                 weight_decay, t, m->stream);
+                 weight_decay, t, m->stream, max_grad_norm > 0.f ? gn + 1 : nullptr);
   }));
   RC(refresh_transposed(m));
   m->have_grads = false;
+  if (grad_norm_out) {
+    GPT2_HIP_CHECK(hipMemcpyAsync(grad_norm_out, gn, sizeof(float), hipMemcpyDeviceToHost, m->stream));
+    GPT2_HIP_CHECK(hipStreamSynchronize(m->stream));
+  }
   return GPT2_OK;
 }
 

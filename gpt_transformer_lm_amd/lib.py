@@ -60,8 +60,11 @@ def load():
         "gpt2_last_error": (C.c_char_p, []),
         "gpt2_create": (C.c_int, [cfgp, C.c_uint64, vp, vp, sz, C.POINTER(vp)]),
         "gpt2_forward": (C.c_int, [vp, vp, vp, fp]),
+        "gpt2_forward_scaled": (C.c_int, [vp, vp, vp, f32, fp]),
         "gpt2_backward": (C.c_int, [vp]),
+        "gpt2_backward_accumulate": (C.c_int, [vp]),
         "gpt2_adamw_step": (C.c_int, [vp, f32, f32, f32, f32, f32, i32]),
+        "gpt2_adamw_step_clipped": (C.c_int, [vp, f32, f32, f32, f32, f32, i32, f32, fp]),
         "gpt2_destroy": (None, [vp]),
         "gpt2_get_params": (C.c_int, [vp, vp]),
         "gpt2_set_params": (C.c_int, [vp, vp]),
@@ -104,7 +107,8 @@ def exported_symbols():
     return [
         "gpt2_validate_config", "gpt2_num_parameters", "gpt2_num_param_tensors", "gpt2_param_info",
         "gpt2_workspace_bytes", "gpt2_status_string", "gpt2_last_error", "gpt2_create", "gpt2_forward",
-        "gpt2_backward", "gpt2_adamw_step", "gpt2_destroy", "gpt2_get_params", "gpt2_set_params",
+        "gpt2_forward_scaled", "gpt2_backward", "gpt2_backward_accumulate", "gpt2_adamw_step",
+        "gpt2_adamw_step_clipped", "gpt2_destroy", "gpt2_get_params", "gpt2_set_params",
         "gpt2_get_grads", "gpt2_get_adam_state", "gpt2_get_token_losses", "gpt2_get_logits",
         "gpt2_timing_enable", "gpt2_timing_read",
         "gpt2_op_linear_forward", "gpt2_op_linear_backward_workspace_bytes", "gpt2_op_linear_backward",
@@ -205,11 +209,26 @@ class Model:
         check(self.lib.gpt2_forward(self.h, ptr(tokens), ptr(targets), C.byref(loss)), "forward")
         return loss.value if targets is not None else None
 
+    def forward_scaled(self, tokens, targets, loss_scale):
+        loss = C.c_float(0.0)
+        check(self.lib.gpt2_forward_scaled(self.h, ptr(tokens), ptr(targets), loss_scale, C.byref(loss)),
+              "forward_scaled")
+        return loss.value if targets is not None else None
+
     def backward(self):
         check(self.lib.gpt2_backward(self.h), "backward")
 
+    def backward_accumulate(self):
+        check(self.lib.gpt2_backward_accumulate(self.h), "backward_accumulate")
+
     def adamw_step(self, lr, beta1, beta2, eps, weight_decay, t):
         check(self.lib.gpt2_adamw_step(self.h, lr, beta1, beta2, eps, weight_decay, t), "adamw_step")
+
+    def adamw_step_clipped(self, lr, beta1, beta2, eps, weight_decay, t, max_grad_norm, want_norm=True):
+        norm = C.c_float(0.0)
+        check(self.lib.gpt2_adamw_step_clipped(self.h, lr, beta1, beta2, eps, weight_decay, t, max_grad_norm,
+                                               C.byref(norm) if want_norm else None), "adamw_step_clipped")
+        return norm.value if want_norm else None
 
     def _host(self, fn, n):
         out = np.empty(n, dtype=np.float32)

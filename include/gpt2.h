@@ -128,10 +128,26 @@ int gpt2_create(const gpt2_config* cfg, uint64_t seed, void* stream, void* works
 int gpt2_forward(gpt2_model* m, const int32_t* d_tokens, const int32_t* d_targets,
                  float* mean_loss);
 
+/* gpt2_forward, except that the gradients the next backward computes are
+ * those of loss_scale x (the mean loss); *mean_loss still reports the
+ * unscaled mean.  For gradient accumulation over k micro-batches pass
+ * loss_scale = 1/k to each: the accumulated gradient is then that of the
+ * mean loss over all k micro-batches (the mean of their gradients).
+ * loss_scale must be finite (GPT2_E_INVALID_ARG otherwise). */
+int gpt2_forward_scaled(gpt2_model* m, const int32_t* d_tokens, const int32_t* d_targets,
+                        float loss_scale, float* mean_loss);
+
 /* Backward pass of the mean loss of the last forward-with-targets.  Parameter
  * gradients (fp32) are overwritten.  GPT2_E_STATE if the last forward had no
  * targets. */
 int gpt2_backward(gpt2_model* m);
+
+/* Gradient accumulation: the same backward, with every parameter gradient
+ * added to the one held (from gpt2_backward and any accumulating backwards
+ * since the last update) instead of overwriting it.  Summation order is
+ * fixed, so the result is deterministic.  GPT2_E_STATE if the last forward
+ * had no targets or no gradient is held. */
+int gpt2_backward_accumulate(gpt2_model* m);
 
 /* One AdamW update of every parameter (fp32 master), then refreshes the bf16
  * copy used by the forward:  m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
@@ -139,6 +155,18 @@ int gpt2_backward(gpt2_model* m);
  * Requires t >= 1 and a completed backward (GPT2_E_STATE otherwise). */
 int gpt2_adamw_step(gpt2_model* m, float lr, float beta1, float beta2, float eps,
                     float weight_decay, int32_t t);
+
+/* gpt2_adamw_step with global-norm gradient clipping.  n = the L2 norm of all
+ * parameter gradients taken as one vector (fp32 partial sums per block, added
+ * in a fixed order in fp64).  If max_grad_norm > 0 and n > max_grad_norm,
+ * every gradient enters the update multiplied by max_grad_norm / n (the
+ * stored gradients are left as they are); max_grad_norm <= 0 disables
+ * clipping.  If grad_norm != NULL, n (before clipping) is written there
+ * (host) and the stream is synchronised; otherwise nothing waits on the
+ * host.  The norm and the factor are computed on the device, so clipping
+ * needs no host round trip. */
+int gpt2_adamw_step_clipped(gpt2_model* m, float lr, float beta1, float beta2, float eps,
+                            float weight_decay, int32_t t, float max_grad_norm, float* grad_norm);
 
 /* Releases the model (and the workspace if the library allocated it).
  * Synchronises the model's stream first.  NULL is a no-op. */

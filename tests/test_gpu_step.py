@@ -130,6 +130,95 @@ def test_tiny_fp32_three_steps():
         assert rel(mm[k][:512] if k == "wte" else mm[k], state[k][0]) < 1e-3, k
 
 
+def accumulated_clipped_steps(c, dtype, seed, odtype, gtol, ntol, ptol, k=2, steps=2, clip=0.3, resync=False):
+    """k micro-batches per update (each of the model's B x T), forward with
+    loss_scale 1/k, gpt2_backward then gpt2_backward_accumulate, then
+    gpt2_adamw_step_clipped with max_grad_norm = clip x the oracle's norm (so
+    clipping is active); two updates, since AdamW's first step hides the
+    scale of the gradient.  Compared with oracle.gpt2_step_accumulated.
+    resync: before each later update the oracle takes the library's
+    parameters and moments, so every update is held to the one-step bar (in
+    bf16 the second step's gradients otherwise also carry the first step's
+    parameter rounding)."""
+    model, cfg = make(c, dtype)
+    params = S.random_params(c["V"], c["Vp"], c["maxT"], c["L"], c["C_"], seed=seed, perturbed=True)
+    model.set_params(lib.flatten_params(cfg, params))
+    oc = ocfg(c)
+    op = to_oracle(params, c, odtype)
+    state = None
+    lr, b1, b2, eps, wd = 2e-3, 0.9, 0.95, 1e-8, 0.1
+    for t in range(1, steps + 1):
+        if resync and t > 1:
+            got = lib.unflatten(cfg, model.get_params())
+            mm, vv = (lib.unflatten(cfg, x) for x in model.get_adam_state())
+            op = to_oracle(got, c, odtype)
+            state = {n: ((mm[n][: c["V"]] if n == "wte" else mm[n]).astype(odtype),
+                         (vv[n][: c["V"]] if n == "wte" else vv[n]).astype(odtype)) for n in op}
+        micro = [S.uniform_batch(c["B"], c["T"], c["V"], seed=seed * 10 + 3 * t + i) for i in range(k)]
+        for i, (tok, tgt) in enumerate(micro):
+            model.forward_scaled(dev_i32(tok), dev_i32(tgt), 1.0 / k)
+            if i == 0:
+                model.backward()
+            else:
+                model.backward_accumulate()
+        grads = lib.unflatten(cfg, model.get_grads())
+        _, ograds, onorm, _, _ = O.gpt2_step_accumulated(op, micro, oc, state, lr, b1, b2, eps, wd, t)
+        max_norm = clip * onorm
+        norm = model.adamw_step_clipped(lr, b1, b2, eps, wd, t, max_norm)
+        _, _, _, op, state = O.gpt2_step_accumulated(op, micro, oc, state, lr, b1, b2, eps, wd, t,
+                                                     max_grad_norm=max_norm)
+        worst = {name: rel(grads[name][: c["V"]] if name == "wte" else grads[name], g) for name, g in ograds.items()}
+        say("step", t, "norm", norm, "oracle", onorm, "worst grad rel L2", max(worst.values()))
+        assert all(v <= gtol for v in worst.values()), worst
+        assert np.all(grads["wte"][c["V"]:] == 0.0)
+        assert abs(norm - onorm) / onorm <= ntol
+    after = lib.unflatten(cfg, model.get_params())
+    model.close()
+    flat_a = np.concatenate([(after[k][: c["V"]] if k == "wte" else after[k]).reshape(-1) for k in op])
+    flat_o = np.concatenate([op[k].reshape(-1) for k in op])
+    prel = rel(flat_a, flat_o)
+    say("params after", steps, "clipped accumulated updates: rel L2", prel)
+    assert prel <= ptol
+    assert np.array_equal(after["wte"][c["V"]:], params["wte"][c["V"]:].astype(np.float32))
+
+
+def test_tiny_fp32_accumulation_and_clipping():
+    say("tiny fp32 accumulation + clipping")
+    accumulated_clipped_steps(TINY, FP32, 601, np.float64, gtol=1e-4, ntol=1e-5, ptol=1e-4)
+
+
+def test_tiny_bf16_accumulation_and_clipping():
+    say("tiny bf16 accumulation + clipping")
+    accumulated_clipped_steps(TINY, BF16, 701, np.float64, gtol=3e-2, ntol=3e-2, ptol=1e-2, k=3, resync=True)
+
+
+def test_accumulation_and_clipping_state_errors():
+    say("accumulation / clipping state errors")
+    c = TINY
+    model, cfg = make(c, FP32)
+    tok, tgt = S.uniform_batch(c["B"], c["T"], c["V"], seed=801)
+    model.forward(dev_i32(tok), dev_i32(tgt))
+    with pytest.raises(lib.Gpt2Error, match="call order"):
+        model.backward_accumulate()             # no gradient held yet
+    with pytest.raises(lib.Gpt2Error):
+        model.forward_scaled(dev_i32(tok), dev_i32(tgt), float("nan"))
+    model.forward(dev_i32(tok), dev_i32(tgt))
+    model.backward()
+    g1 = model.get_grads()
+    # a clipping threshold above the norm, or none, leaves the update unclipped:
+    # the same parameters as the plain update
+    p0 = model.get_params()
+    norm = model.adamw_step_clipped(1e-3, 0.9, 0.95, 1e-8, 0.0, 1, 0.0)
+    assert abs(norm - float(np.sqrt(np.sum(g1.astype(np.float64) ** 2)))) / norm < 1e-5
+    p1 = model.get_params()
+    model.set_params(p0)
+    model.forward(dev_i32(tok), dev_i32(tgt))
+    model.backward()
+    model.adamw_step(1e-3, 0.9, 0.95, 1e-8, 0.0, 1)
+    assert np.array_equal(model.get_params(), p1)
+    model.close()
+
+
 def test_init_matches_oracle_derivation():
     say("init")
     c = dict(TINY, V=500, Vp=512)
