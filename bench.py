@@ -2,6 +2,10 @@
 AdamW) through the HIP C-ABI library on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--config 124m|350m|1.6b]
+                    [--accum M] [--max-grad-norm X]
+
+(--accum / --max-grad-norm time updates over M accumulated micro-batches with
+global-norm clipping; the defaults time the plain step of the headline metric.)
 
 Prints one JSON line.  value = tokens/s of whole training steps (inputs
 already resident in HBM), MFU against the bf16 dense MFMA peak, the roofline
@@ -57,6 +61,7 @@ KERNEL_OF = {
     "attn_bwd_dq": "attn_bwd_dq_mfma_kernel", "attn_bwd_dot": "attn_bwd_dot_kernel",
     "softmax_xent": "softmax_xent_bf16_kernel", "ln_fwd": "ln_fwd_kernel", "ln_bwd": "ln_bwd_kernel",
     "encoder_fwd": "encoder_fwd_kernel", "adamw": "adamw_kernel", "weight_transpose": "transpose_bf16_kernel",
+    "grad_norm": "grad_sumsq_kernel",
 }
 for _s in GEMM_SITES:
     KERNEL_OF[_s] = "gemm_bf16_dma_kernel"
@@ -131,6 +136,10 @@ def main():
     ap.add_argument("--seed", type=int, default=1234)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--site", default=None, help="kernel site to report in roofline (default: the slowest)")
+    ap.add_argument("--accum", type=int, default=1,
+                    help="micro-batches of B x T accumulated per update (gradient of their mean loss)")
+    ap.add_argument("--max-grad-norm", type=float, default=0.0,
+                    help="global-norm gradient clipping threshold (0: off)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a kernel of known traffic, "
                          "to calibrate hardware byte counters against)")
@@ -158,18 +167,33 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     model = lib.Model(cfg, seed=args.seed, stream=stream)
+    K = max(args.accum, 1)
+    plain = K == 1 and args.max_grad_norm <= 0
     nsteps = args.warmup + args.steps
     batches = []
-    for s in range(nsteps + 1):
+    for s in range(nsteps * K + 1):
         x, y = S.zipf_batch(B, T, seed=args.seed * 1000 + s)
         batches.append((torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda()))
     torch.cuda.synchronize()
 
     def step(i, t):
-        x, y = batches[i]
-        loss = model.forward(x, y)
-        model.backward()
-        model.adamw_step(c["lr"], 0.9, 0.999, 1e-8, c["wd"], t)
+        if plain:
+            x, y = batches[i]
+            loss = model.forward(x, y)
+            model.backward()
+            model.adamw_step(c["lr"], 0.9, 0.999, 1e-8, c["wd"], t)
+            return loss
+        # K micro-batches, each forward with loss scale 1/K, gradients accumulated,
+        # then the clipped update (norm and factor stay on the device)
+        loss = 0.0
+        for j in range(K):
+            x, y = batches[i * K + j]
+            loss += model.forward_scaled(x, y, 1.0 / K) / K
+            if j == 0:
+                model.backward()
+            else:
+                model.backward_accumulate()
+        model.adamw_step_clipped(c["lr"], 0.9, 0.999, 1e-8, c["wd"], t, args.max_grad_norm, want_norm=False)
         return loss
 
     # warmup; the last warmup step also times every kernel site once to find the dominant kernel
@@ -208,7 +232,7 @@ def main():
     dom_t = model.timing_read(dom)
     model.close()
 
-    tok_s = B * T * args.steps / elapsed
+    tok_s = K * B * T * args.steps / elapsed
     ftok = flops_per_token(c)
     mfu = tok_s * ftok / PEAK_BF16
     roof = roofline_of(dom, dom_t)
@@ -230,8 +254,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic Zipf(1.1)/EoT token ids, seeded random GPT-2 init",
         "config": {"workload": f"GPT-2 {args.config} training step (fwd+bwd+AdamW, fp32 master), "
-                               f"B={B}, T={T}, vocab 50257 padded to 50304",
-                   "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+                               f"B={B}, T={T}, vocab 50257 padded to 50304"
+                               + ("" if plain else f", {K} accumulated micro-batches per update, global-norm "
+                                                   f"clipping at {args.max_grad_norm}"),
+                   "global_batch": K * B, "seq_len": T, "parallelism": "single GPU"},
         "mfu": mfu,
         "model_flops_per_token": ftok,
         "loss_first_last": [losses[0], losses[-1]] if losses else None,

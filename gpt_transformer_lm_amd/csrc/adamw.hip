@@ -186,8 +186,10 @@ size_t grad_norm_workspace_bytes() { return (kNormBlocks + 2) * sizeof(float); }
 int grad_norm(int64_t n, const float* grad, float max_norm, float* workspace, hipStream_t stream) {
   if (n < 0 || !grad || !workspace) return gpt2_internal_fail(1, "grad_norm: bad arguments");
   if ((uintptr_t)grad % 16) return gpt2_internal_fail(1, "grad_norm: gradient must be 16-byte aligned");
+  mark_begin(0, stream);
   hipLaunchKernelGGL(grad_sumsq_kernel, dim3(kNormBlocks), dim3(256), 0, stream, n, grad, workspace + 2);
   GPT2_LAUNCH_CHECK();
+  mark_end(0, stream);
   hipLaunchKernelGGL(grad_norm_finalize_kernel, dim3(1), dim3(256), 0, stream, workspace + 2, kNormBlocks,
                      max_norm, workspace);
   GPT2_LAUNCH_CHECK();

@@ -240,7 +240,7 @@ void make_layout(const gpt2_config& c, Layout* lo) {
 enum Site {
   S_QKV = 0, S_ATTPROJ, S_FC, S_FCPROJ, S_LOGITS, S_FCPROJ_DX, S_FCPROJ_DW, S_FC_DX, S_FC_DW,
   S_ATTPROJ_DX, S_ATTPROJ_DW, S_QKV_DX, S_QKV_DW, S_CLS_DX, S_CLS_DW, S_ATTN_FWD, S_ATTN_DKDV, S_ATTN_DQ,
-  S_ATTN_DOT, S_XENT, S_LN_FWD, S_LN_BWD, S_ENC_FWD, S_ADAMW, S_WT, S_COUNT
+  S_ATTN_DOT, S_XENT, S_LN_FWD, S_LN_BWD, S_ENC_FWD, S_ADAMW, S_WT, S_GRAD_NORM, S_COUNT
 };
 
 struct SiteTimer {
@@ -773,7 +773,11 @@ int gpt2_adamw_step_clipped(gpt2_model* m, float lr, float beta1, float beta2, f
   // the norm (and the clipping factor, read by the update on the device) only when asked for
   float* gn = m->at<float>(m->lo.gnorm);
   const bool need_norm = max_grad_norm > 0.f || grad_norm_out != nullptr;
-  if (need_norm) RC(grad_norm(m->lo.P, m->grad(), max_grad_norm, gn, m->stream));
+  if (need_norm) {
+    // fp32 gradients read once
+    RC(timed(m, S_GRAD_NORM, 0.0, 4.0 * (double)m->lo.P,
+             [&] { return grad_norm(m->lo.P, m->grad(), max_grad_norm, gn, m->stream); }));
+  }
   // fp32 master, m, v read and written, fp32 gradient read, bf16 copy written
   RC(timed(m, S_ADAMW, 0.0, (double)m->lo.P * (m->cfg.dtype == GPT2_BF16 ? 30.0 : 28.0), [&] {
     return adamw(m->lo.P, m->master(), m->grad(), m->at<float>(m->lo.adam_m), m->at<float>(m->lo.adam_v),

@@ -22,7 +22,7 @@ GPT2_BF16 = 1
 SITES = ["qkv", "attproj", "fc", "fcproj", "logits", "fcproj_dx", "fcproj_dw", "fc_dx", "fc_dw",
          "attproj_dx", "attproj_dw", "qkv_dx", "qkv_dw", "cls_dx", "cls_dw", "attn_fwd", "attn_bwd_dkdv",
          "attn_bwd_dq", "attn_bwd_dot", "softmax_xent", "ln_fwd", "ln_bwd", "encoder_fwd", "adamw",
-         "weight_transpose"]
+         "weight_transpose", "grad_norm"]
 
 
 class Gpt2Config(C.Structure):

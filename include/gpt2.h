@@ -201,9 +201,10 @@ int gpt2_get_logits(gpt2_model* m, float* host_out);
  * 15 attention fwd, 16 attention bwd dK/dV, 17 attention bwd dQ,
  * 18 attention bwd rowsum(dO*O), 19 softmax-CE, 20 LayerNorm fwd,
  * 21 LayerNorm bwd, 22 encoder fwd, 23 AdamW, 24 transposed bf16 weight
- * copies (written after each AdamW step for the dX products).  Events are
+ * copies (written after each AdamW step for the dX products), 25 gradient
+ * norm (partial sums of squares; gpt2_adamw_step_clipped).  Events are
  * recorded on the model's stream immediately around that kernel.  Sites are
- * valid in [0, 25); others give GPT2_E_INVALID_ARG. */
+ * valid in [0, 26); others give GPT2_E_INVALID_ARG. */
 int gpt2_timing_enable(gpt2_model* m, int site, int enable);
 /* Total elapsed milliseconds and launch count recorded for a site since it
  * was enabled (synchronises the stream). */
