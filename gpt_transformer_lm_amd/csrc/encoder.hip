@@ -110,24 +110,35 @@ __global__ __launch_bounds__(256) void encoder_bwd_pieces_kernel(int n, int C, i
   __syncthreads();
   const int prev_tok = start > 0 ? key_tok(sorted[start - 1], shift) : -1;
   const int next_tok = end < n ? key_tok(sorted[end], shift) : -1;
+  const int len = end - start;
   for (int c = threadIdx.x; c < C; c += blockDim.x) {
     int rs = 0;   // run start (index within piece)
     float acc = 0.f;
-    for (int e = 0; e < end - start; ++e) {
-      acc += dx0[(size_t)spos[e] * C + c];
-      const bool last = (e == end - start - 1) || (stok[e + 1] != stok[e]);
-      if (last) {
-        const int tok = stok[e];
-        const bool from_prev = (rs == 0) && (prev_tok == tok);
-        const bool to_next = (e == end - start - 1) && (next_tok == tok);
-        if (from_prev)
-          pcont[(size_t)piece * C + c] = acc;
-        else if (to_next)
-          pown[(size_t)piece * C + c] = acc;
-        else
-          dwte[(size_t)tok * C + c] += acc;
-        acc = 0.f;
-        rs = e + 1;
+    // rows are read 8 at a time ahead of the (sequential, fixed-order) sums,
+    // so eight loads per thread are in flight instead of one
+    for (int e0 = 0; e0 < len; e0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = e0 + j < len ? dx0[(size_t)spos[e0 + j] * C + c] : 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e = e0 + j;
+        if (e >= len) break;
+        acc += v[j];
+        const bool last = (e == len - 1) || (stok[e + 1] != stok[e]);
+        if (last) {
+          const int tok = stok[e];
+          const bool from_prev = (rs == 0) && (prev_tok == tok);
+          const bool to_next = (e == len - 1) && (next_tok == tok);
+          if (from_prev)
+            pcont[(size_t)piece * C + c] = acc;
+          else if (to_next)
+            pown[(size_t)piece * C + c] = acc;
+          else
+            dwte[(size_t)tok * C + c] += acc;
+          acc = 0.f;
+          rs = e + 1;
+        }
       }
     }
   }
