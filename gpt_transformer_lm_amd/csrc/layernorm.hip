@@ -189,8 +189,19 @@ __global__ __launch_bounds__(256) void column_reduce_kernel(const float* __restr
   const int c = is_b ? col - C : col;
   const float* part = is_b ? part_db : part_dw;
   float s = 0.f;
-  if (col < 2 * C)
-    for (int p = g; p < P; p += 16) s += part[(size_t)p * C + c];
+  if (col < 2 * C) {
+    // the first 16 partial rows of this thread are loaded together, then
+    // summed in the same order as the loop below would
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int p = g + 16 * j;
+      v[j] = p < P ? part[(size_t)p * C + c] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += v[j];
+    for (int p = g + 256; p < P; p += 16) s += part[(size_t)p * C + c];
+  }
   sh[g][cl] = s;
   __syncthreads();
   if (g == 0 && col < 2 * C) {
