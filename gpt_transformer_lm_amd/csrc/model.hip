@@ -730,11 +730,10 @@ int gpt2_forward(gpt2_model* m, const int32_t* d_tokens, const int32_t* d_target
 int gpt2_forward_scaled(gpt2_model* m, const int32_t* d_tokens, const int32_t* d_targets, float loss_scale,
                         float* mean_loss) {
   if (!m || !d_tokens) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "forward: NULL model or tokens");
-  if (d_targets && !mean_loss) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "forward: mean_loss is NULL");
   if (!isfinite(loss_scale))
     return gpt2_internal_fail(GPT2_E_INVALID_ARG, "forward: loss_scale must be finite");
   RC(forward_impl(m, d_tokens, d_targets, loss_scale));
-  if (d_targets) {
+  if (d_targets && mean_loss) {
     GPT2_HIP_CHECK(hipMemcpyAsync(mean_loss, m->at<float>(m->lo.mean_loss), sizeof(float), hipMemcpyDeviceToHost,
                                   m->stream));
     GPT2_HIP_CHECK(hipStreamSynchronize(m->stream));
@@ -797,6 +796,11 @@ static int copy_out(gpt2_model* m, const void* src, void* dst, size_t bytes) {
   GPT2_HIP_CHECK(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, m->stream));
   GPT2_HIP_CHECK(hipStreamSynchronize(m->stream));
   return GPT2_OK;
+}
+
+int gpt2_get_mean_loss(gpt2_model* m, float* host_out) {
+  if (!m || !host_out) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "get_mean_loss: NULL");
+  return copy_out(m, m->at<float>(m->lo.mean_loss), host_out, sizeof(float));
 }
 
 int gpt2_get_params(gpt2_model* m, float* host_out) {

@@ -66,6 +66,7 @@ def load():
         "gpt2_adamw_step": (C.c_int, [vp, f32, f32, f32, f32, f32, i32]),
         "gpt2_adamw_step_clipped": (C.c_int, [vp, f32, f32, f32, f32, f32, i32, f32, fp]),
         "gpt2_destroy": (None, [vp]),
+        "gpt2_get_mean_loss": (C.c_int, [vp, fp]),
         "gpt2_get_params": (C.c_int, [vp, vp]),
         "gpt2_set_params": (C.c_int, [vp, vp]),
         "gpt2_get_grads": (C.c_int, [vp, vp]),
@@ -108,7 +109,7 @@ def exported_symbols():
         "gpt2_validate_config", "gpt2_num_parameters", "gpt2_num_param_tensors", "gpt2_param_info",
         "gpt2_workspace_bytes", "gpt2_status_string", "gpt2_last_error", "gpt2_create", "gpt2_forward",
         "gpt2_forward_scaled", "gpt2_backward", "gpt2_backward_accumulate", "gpt2_adamw_step",
-        "gpt2_adamw_step_clipped", "gpt2_destroy", "gpt2_get_params", "gpt2_set_params",
+        "gpt2_adamw_step_clipped", "gpt2_destroy", "gpt2_get_mean_loss", "gpt2_get_params", "gpt2_set_params",
         "gpt2_get_grads", "gpt2_get_adam_state", "gpt2_get_token_losses", "gpt2_get_logits",
         "gpt2_timing_enable", "gpt2_timing_read",
         "gpt2_op_linear_forward", "gpt2_op_linear_backward_workspace_bytes", "gpt2_op_linear_backward",
@@ -204,10 +205,18 @@ class Model:
         except Exception:
             pass
 
-    def forward(self, tokens, targets=None):
+    def forward(self, tokens, targets=None, read_loss=True):
+        """Mean loss with targets (read back, synchronising) unless read_loss is
+        False; then nothing waits and get_mean_loss() reads it later."""
         loss = C.c_float(0.0)
-        check(self.lib.gpt2_forward(self.h, ptr(tokens), ptr(targets), C.byref(loss)), "forward")
-        return loss.value if targets is not None else None
+        want = targets is not None and read_loss
+        check(self.lib.gpt2_forward(self.h, ptr(tokens), ptr(targets), C.byref(loss) if want else None), "forward")
+        return loss.value if want else None
+
+    def get_mean_loss(self):
+        loss = C.c_float(0.0)
+        check(self.lib.gpt2_get_mean_loss(self.h, C.byref(loss)), "get_mean_loss")
+        return loss.value
 
     def forward_scaled(self, tokens, targets, loss_scale):
         loss = C.c_float(0.0)

@@ -121,10 +121,11 @@ int gpt2_create(const gpt2_config* cfg, uint64_t seed, void* stream, void* works
 /* Forward pass over d_tokens [B, T] int32 (ids in [0, V)).  With d_targets
  * (int32 [B, T], ids in [0, V)) it also evaluates softmax cross-entropy,
  * writes the per-position losses, stores dlogits in place of the logits
- * (ready for gpt2_backward) and writes the mean loss to *mean_loss (host),
- * synchronising the stream.  With d_targets == NULL it stops at the logits
- * and does not touch *mean_loss or synchronise.  Token ids outside [0, V)
- * are undefined behaviour. */
+ * (ready for gpt2_backward) and, if mean_loss != NULL, writes the mean loss
+ * to *mean_loss (host), synchronising the stream; with mean_loss == NULL
+ * nothing waits on the host and gpt2_get_mean_loss reads it later.  With
+ * d_targets == NULL it stops at the logits and does not touch *mean_loss or
+ * synchronise.  Token ids outside [0, V) are undefined behaviour. */
 int gpt2_forward(gpt2_model* m, const int32_t* d_tokens, const int32_t* d_targets,
                  float* mean_loss);
 
@@ -173,6 +174,9 @@ int gpt2_adamw_step_clipped(gpt2_model* m, float lr, float beta1, float beta2, f
 void gpt2_destroy(gpt2_model* m);
 
 /* ---- state access (synchronous copies through host memory) -------------- */
+
+/* Mean loss of the last forward with targets (one float). */
+int gpt2_get_mean_loss(gpt2_model* m, float* host_out);
 
 /* fp32 master parameters in the flat layout, num_parameters(cfg, 1) floats. */
 int gpt2_get_params(gpt2_model* m, float* host_out);
