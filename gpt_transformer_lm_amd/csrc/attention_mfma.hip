@@ -8,10 +8,13 @@
 // V stream through LDS in 64-key stages.  Each wave computes S^T = K Q^T per
 // 32-key slice (K from LDS, Q fragments held in registers), so its
 // accumulator holds one query per lane and 16 keys per lane: the running max
-// / sum of the online softmax are per-lane scalars (the two half-waves
-// holding the same query combine with one swizzle), the probabilities P
+// / sum of the online softmax are per-lane scalars, the probabilities P
 // (bf16) are already in the register layout of the B operand of
 // O^T = V^T P^T, and the rescaling of O^T is a per-lane scalar multiply.
+// Both 32-key slices of a 64-key stage are scored before one softmax update:
+// the two half-waves holding the same query exchange their maxima once per
+// stage with v_permlane32_swap, and each keeps its own share of the row sum
+// until the end.
 //
 // Backward (deterministic, no atomics), two kernels:
 //   dK/dV: a block owns 128 keys (32 per wave) and streams 64-query stages of
@@ -60,6 +63,22 @@ __device__ __forceinline__ floatx16 mfma(const bf16x8& a, const bf16x8& b, const
 }
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Combine of a value held per half-wave: every lane gets op(own, value of
+// lane l ^ 32).  gfx950's v_permlane32_swap exchanges the two halves in the
+// VALU (no LDS round trip); its two outputs hold, in each lane, the lane's own
+// value and its partner's (in one order or the other), so the symmetric
+// combine needs no lane select.
+__device__ __forceinline__ float half_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Rows row0 .. row0+63, columns col0 .. col0+63 of a row-major bf16 matrix
 // (row stride ld elements, addressed from the resource's base) into a tile:
@@ -147,7 +166,7 @@ __device__ __forceinline__ void store_row64(bf16* dst, const floatx16 acc[2], fl
 
 // ------------------------------------------------------------------ forward
 
-__global__ __launch_bounds__(256, 4) void attn_fwd_mfma_kernel(int T, int H, const bf16* __restrict__ qkv,
+__global__ __launch_bounds__(256, 3) void attn_fwd_mfma_kernel(int T, int H, const bf16* __restrict__ qkv,
                                                             bf16* __restrict__ out, float* __restrict__ lse,
                                                             float scale) {
   constexpr int NS = NS_FWD;
@@ -196,62 +215,80 @@ __global__ __launch_bounds__(256, 4) void attn_fwd_mfma_kernel(int T, int H, con
     const GPT2_LDS char* Kc = (const GPT2_LDS char*)ring[st % NS];
     const GPT2_LDS char* Vc = Kc + TILE;
     const int k0 = st * STAGE;
+    // Both 32-key slices' score products first, then one softmax update for
+    // the 64 keys (one max exchange, one rescale), then both P V products.
+    // The second slice is skipped when it lies wholly above this wave's
+    // diagonal; keys k0 .. k0 + 31 always include key k0 <= every query of
+    // the wave, so the running maximum is finite from the first stage on.
+    if (k0 <= qw0 + 31 && k0 < T) {
+      const bool two = k0 + 32 <= qw0 + 31 && k0 + 32 < T;
+      floatx16 s[2];
 #pragma unroll
-    for (int ks = 0; ks < STAGE; ks += 32) {
-      const int kb = k0 + ks;
-      if (kb <= qw0 + 31 && kb < T) {
-        floatx16 s;
+      for (int u2 = 0; u2 < 2; ++u2) {
+        if (u2 == 0 || two) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = 0.f;
+          for (int r = 0; r < 16; ++r) s[u2][r] = 0.f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) s = mfma(frag_nat(Kc, ks, k, lane), qf[k], s);
-        // the causal / end-of-sequence mask only touches slices on the diagonal
-        // (a wave-uniform test, so the common case runs unmasked)
-        const bool edge = (kb + 31 > qw0) || (kb + 32 > T);
-        float mx = -INFINITY;
-        if (edge) {
+          for (int k = 0; k < 4; ++k) s[u2] = mfma(frag_nat(Kc, 32 * u2, k, lane), qf[k], s[u2]);
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int u2 = 0; u2 < 2; ++u2) {
+        if (u2 == 0 || two) {
+          const int kb = k0 + 32 * u2;
+          // the causal / end-of-sequence mask only touches slices on the
+          // diagonal (a wave-uniform test, so the common case runs unmasked)
+          if ((kb + 31 > qw0) || (kb + 32 > T)) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = kb + acc_row(r, lane);
+              if (key > myq || key >= T) s[u2][r] = -INFINITY;
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[u2][r]);
+        }
+      }
+      mx = half_max(mx);
+      // the scale sl2 is positive, so the maximum of the scaled scores is the
+      // scaled maximum; the scaling then folds into the exponent's fma
+      const float m_new = fmaxf(m_i, mx * sl2);
+      // rescale the running sum and O only when some lane's maximum grew
+      // (otherwise the factor is exactly 1); the vote is wave-uniform
+      if (__any(m_new > m_i)) {
+        const float alpha = ex2(m_i - m_new);
+        l_i *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+      }
+      m_i = m_new;
+#pragma unroll
+      for (int u2 = 0; u2 < 2; ++u2) {
+        if (u2 == 0 || two) {
+          float rs_ = 0.f;
+          bf16x8 pb[2];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = kb + acc_row(r, lane);
-            if (key > myq || key >= T) s[r] = -INFINITY;
-            mx = fmaxf(mx, s[r]);
+            const float p = ex2(fmaf(s[u2][r], sl2, -m_new));
+            rs_ += p;
+            pb[r >> 3][r & 7] = (bf16)p;
           }
-        } else {
+          // l_i is this half-wave's share of the row sum (both halves see the
+          // same maximum, so their shares add up at the end)
+          l_i += rs_;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt)
+              oacc[dt] = mfma(frag_tr(Vc, dt * 32, 32 * u2 + 16 * u, lane), pb[u], oacc[dt]);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        // the scale sl2 is positive, so the maximum of the scaled scores is the
-        // scaled maximum; the scaling then folds into the exponent's fma
-        const float m_new = fmaxf(m_i, mx * sl2);
-        float rs_ = 0.f;
-        bf16x8 pb[2];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = ex2(fmaf(s[r], sl2, -m_new));
-          rs_ += p;
-          pb[r >> 3][r & 7] = (bf16)p;
-        }
-        rs_ += __shfl_xor(rs_, 32, 64);
-        // rescale the running sum and O only when some lane's maximum grew
-        // (otherwise the factor is exactly 1); the vote is wave-uniform
-        if (__any(m_new > m_i)) {
-          const float alpha = ex2(m_i - m_new);
-          l_i *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-        }
-        l_i += rs_;
-        m_i = m_new;
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int dt = 0; dt < 2; ++dt) oacc[dt] = mfma(frag_tr(Vc, dt * 32, ks + 16 * u, lane), pb[u], oacc[dt]);
       }
     }
   }
+  l_i = half_sum(l_i);
   if (myq < T) {
     store_row64(out + ((size_t)b * T + myq) * C + h * HD, oacc, 1.0f / l_i, lane);
     if (hi == 0) lse[(size_t)bh * T + myq] = (m_i + __log2f(l_i)) * kLn2;

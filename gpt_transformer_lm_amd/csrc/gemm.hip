@@ -221,6 +221,21 @@ struct DmaTile {
     }
   }
 
+  // Instruction q alone of a K step that lies wholly inside K (no tail check).
+  __device__ __forceinline__ static void issue_q_full(i32x4_rsrc rs, GPT2_LDS char* tile, int wave, const Lane& L,
+                                                      int k0, int64_t ld, int q) {
+    const int iq = wave * NINST + q;
+    uint32_t off;
+    if constexpr (KMAJ) {
+      off = L.base + (uint32_t)q * (uint32_t)(8 * ld * 2) + (uint32_t)(k0 * 2) + (L.c16 ^ (uint32_t)((iq & 7) * 16));
+    } else {
+      constexpr int RPI = 1024 / (2 * R);
+      const int qk = iq * RPI;
+      off = L.base + (uint32_t)((int64_t)(k0 + qk) * ld * 2) + (L.c16 ^ (uint32_t)((((qk & 3) << 2) & 12) * 16));
+    }
+    dma_lds16(rs, (GPT2_LDS void*)(tile + iq * 1024), off);
+  }
+
   // MFMA operand fragment: rows [rbase, rbase + 32) of the tile, k16 step kk;
   // lane l receives row rbase + l%32, k = 16 kk + 8 (l/32) + 0..7.
   __device__ __forceinline__ static bf16x8 frag(const GPT2_LDS char* tile, int rbase, int kk, int lane) {
@@ -288,6 +303,8 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   constexpr int WM = S::WM, WN = S::WN, FM = S::FM, FN = S::FN, NS = S::NS;
   constexpr int A_BYTES = TA::BYTES;
   constexpr int NDMA = TA::NINST + TB::NINST;              // DMA instructions per wave per stage
+  constexpr bool IL = BM == 256 && BN == 256 && !BIAS_GRAD;  // refill spread over the MFMAs
+  static_assert(!IL || NDMA <= 4 * FM * FN, "one DMA instruction per MFMA at most");
   __shared__ __attribute__((aligned(1024))) char st0[S::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char st1[S::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char st2[NS > 2 ? S::STAGE_BYTES : 16];
@@ -366,7 +383,24 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
         if (kt + NS - 2 < KT) wait_vmcnt<(NS - 2) * NDMA>();
         else wait_vmcnt<0>();
         lds_barrier();
-        if (kt + NS - 1 < KT) issue(kt + NS - 1, (s + NS - 1) % NS);
+        // Refill of the ring slot read in the previous K step.  For the
+        // 256x256 tile (one block per compute unit, so nothing else covers the
+        // gap) the refill is spread over this step's first matrix
+        // instructions, one DMA instruction after each, so its address work
+        // issues while the matrix core runs; elsewhere (and in a partial last
+        // K step) it is issued here, ahead of the fragment reads, which gives
+        // the DMA more time to land and measured faster for the two-block
+        // 128x128 tiles and for the bias-gradient tiles.
+        const bool refill = kt + NS - 1 < KT;
+        GPT2_LDS char* const nbase = stage_ptr((s + NS - 1) % NS);
+        const int k0n = kbeg + (kt + NS - 1) * kBK;
+        const bool tail_n = k0n + kBK > p.K;
+        const bool spread = IL && refill && !tail_n;
+        if (refill && !spread) issue(kt + NS - 1, (s + NS - 1) % NS);
+        auto dma_one = [&](int d) {
+          if (d < TA::NINST) TA::issue_q_full(ra, nbase, wave, la, k0n, p.lda, d);
+          else TB::issue_q_full(rb, nbase + A_BYTES, wave, lb, k0n, p.ldb, d - TA::NINST);
+        };
         if constexpr (S::EARLY_AUX) {
           // last K step: every stage but s is idle
           if (kt == KT - 1 && vec) issue_aux([&](int j) { return stage_ptr((s + 1 + j) % NS); });
@@ -407,8 +441,16 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
 #pragma unroll
           for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
+            for (int j = 0; j < FN; ++j) {
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[kk & 1][j], a[kk & 1][i], acc[i][j], 0, 0, 0);
+              if constexpr (IL) {
+                const int t = (kk * FM + i) * FN + j;
+                if (t < NDMA) {
+                  if (spread) dma_one(t);
+                  __builtin_amdgcn_sched_barrier(0);
+                }
+              }
+            }
           __builtin_amdgcn_sched_barrier(0);
         }
       }

@@ -32,13 +32,23 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int N, int C, const T* __re
   if (row >= N) return;
   const int nch = C / 8;
   const T* xr = x + (size_t)row * C;
-  float v[NCH][8];
-  float s = 0.f;
+  float v[NCH][8], wv[NCH][8], bv[NCH][8];
+  // the gain and bias are loaded with the row, so the row needs one memory
+  // round trip before its reductions instead of two
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     int ch = lane + 64 * c;
     if (ch < nch) {
       Chunk8<T>::load(xr + ch * 8, v[c]);
+      Chunk8<T>::load(w + ch * 8, wv[c]);
+      Chunk8<T>::load(b + ch * 8, bv[c]);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    int ch = lane + 64 * c;
+    if (ch < nch) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) s += v[c][e];
     }
@@ -63,11 +73,9 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int N, int C, const T* __re
   for (int c = 0; c < NCH; ++c) {
     int ch = lane + 64 * c;
     if (ch < nch) {
-      float wv[8], bv[8], o[8];
-      Chunk8<T>::load(w + ch * 8, wv);
-      Chunk8<T>::load(b + ch * 8, bv);
+      float o[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = (v[c][e] - mu) * rs * wv[e] + bv[e];
+      for (int e = 0; e < 8; ++e) o[e] = (v[c][e] - mu) * rs * wv[c][e] + bv[c][e];
       Chunk8<T>::store(yr + ch * 8, o);
     }
   }
