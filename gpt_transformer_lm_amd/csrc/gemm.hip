@@ -303,7 +303,7 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   constexpr int WM = S::WM, WN = S::WN, FM = S::FM, FN = S::FN, NS = S::NS;
   constexpr int A_BYTES = TA::BYTES;
   constexpr int NDMA = TA::NINST + TB::NINST;              // DMA instructions per wave per stage
-  constexpr bool IL = BM == 256 && BN == 256 && !BIAS_GRAD;  // refill spread over the MFMAs
+  constexpr bool IL = S::OCC == 1;  // refill spread over the MFMAs (one block per CU)
   static_assert(!IL || NDMA <= 4 * FM * FN, "one DMA instruction per MFMA at most");
   __shared__ __attribute__((aligned(1024))) char st0[S::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char st1[S::STAGE_BYTES];
@@ -383,14 +383,14 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
         if (kt + NS - 2 < KT) wait_vmcnt<(NS - 2) * NDMA>();
         else wait_vmcnt<0>();
         lds_barrier();
-        // Refill of the ring slot read in the previous K step.  For the
-        // 256x256 tile (one block per compute unit, so nothing else covers the
-        // gap) the refill is spread over this step's first matrix
-        // instructions, one DMA instruction after each, so its address work
-        // issues while the matrix core runs; elsewhere (and in a partial last
-        // K step) it is issued here, ahead of the fragment reads, which gives
-        // the DMA more time to land and measured faster for the two-block
-        // 128x128 tiles and for the bias-gradient tiles.
+        // Refill of the ring slot read in the previous K step.  For the tiles
+        // that run one block per compute unit (nothing else covers the gap)
+        // the refill is spread over this step's first matrix instructions,
+        // one DMA instruction after each, so its address work issues while
+        // the matrix core runs; for the two-block 128x128 tile (and in a
+        // partial last K step) it is issued here, ahead of the fragment
+        // reads, which measured faster there: the other block covers the gap
+        // and the DMA gets more time to land.
         const bool refill = kt + NS - 1 < KT;
         GPT2_LDS char* const nbase = stage_ptr((s + NS - 1) % NS);
         const int k0n = kbeg + (kt + NS - 1) * kBK;
