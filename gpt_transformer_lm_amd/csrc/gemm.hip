@@ -9,9 +9,11 @@
 // bias gradient fused into the weight-gradient pass.
 //
 // bf16 kernel (gfx950):
-//   * block tiles 256x256, 256x128, 128x256 or 128x128 (picked per shape),
-//     K step 64, 256 threads = 4 waves in a 2 x 2 grid; each wave owns a
-//     (BM/2) x (BN/2) patch of v_mfma_f32_32x32x16_bf16 accumulators;
+//   * block tiles 256x256, 256x128, 192x192, 128x256 or 128x128 (picked per
+//     shape), K step 64; each wave owns a patch of v_mfma_f32_32x32x16_bf16
+//     accumulators: 4 waves in a 2 x 2 grid, except the 256-row tiles without
+//     an epilogue input, which run 8 waves (2 x 4 for 256x256, 4 x 2 for
+//     256x128) so every SIMD holds two waves of the block;
 //   * operand tiles go from global memory straight into LDS with
 //     buffer_load ... lds (no register staging), in a ring of 2-4 stages that
 //     fills the LDS, so several K steps are in flight while the matrix cores
@@ -39,7 +41,16 @@ typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBK = 64;          // K step of the MFMA kernel
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;   // fp32 kernel, split-K reductions
+
+// Waves per block of the MFMA kernel and their arrangement over the block
+// tile: the 256-row tiles run 8 waves (two per SIMD) so that one wave's LDS
+// reads and waits overlap the other's matrix instructions; the others run 4.
+// (Tiles whose epilogue reads an input tile keep 4 waves: 8 waves' epilogue
+// staging would not fit the LDS beside their stage ring.)
+constexpr bool epi_has_aux(int epi) { return epi == EPI_BIAS_RES || epi == EPI_GELU_BWD || epi == EPI_MUL; }
+constexpr int gemm_waves(int BM, int BN, int epi) { return BM == 256 && BN >= 128 && !epi_has_aux(epi) ? 8 : 4; }
+constexpr int gemm_wave_rows(int BM, int BN, int epi) { return gemm_waves(BM, BN, epi) == 8 && BN == 128 ? 4 : 2; }
 
 struct EpiArgs {
   int epi;
@@ -158,10 +169,10 @@ __device__ __forceinline__ void tile_coords(int nbm, int nbn, int& tm, int& tn, 
 //    ds_read_b64_tr_b16 (the transpose read hands lane j of each 16-lane group
 //    element j%4 of the 8-byte runs of lanes j/4 + 4e, so with the per-lane
 //    addresses below every lane ends up with 8 consecutive k of one m).
-template <int R, bool KMAJ>
+template <int R, bool KMAJ, int WAVES>
 struct DmaTile {
   static constexpr int BYTES = R * kBK * 2;
-  static constexpr int NINST = BYTES / 1024 / 4;          // 1 KiB instructions per wave
+  static constexpr int NINST = BYTES / 1024 / WAVES;      // 1 KiB instructions per wave
 
   // Per-lane part of the DMA source addresses (two registers per operand); the
   // rest of each instruction's address is wave-uniform.
@@ -266,12 +277,15 @@ struct DmaTile {
 // allows; the epilogue's staging (and the bias-gradient reduction) goes into
 // the last stage buffer when the epilogue input tile (HAS_AUX) leaves it free,
 // else into an array of its own.
-template <int BM, int BN, bool HAS_AUX>
+template <int BM, int BN, int EPI>
 struct DmaShape {
-  static constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  static constexpr bool HAS_AUX = epi_has_aux(EPI);
+  static constexpr int WAVES = gemm_waves(BM, BN, EPI), NT = 64 * WAVES;
+  static constexpr int WGM = gemm_wave_rows(BM, BN, EPI), WGN = WAVES / WGM;   // wave grid
+  static constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
   static constexpr int STAGE_BYTES = (BM + BN) * kBK * 2;
   static constexpr int EP_PITCH = 36;                     // fp32 pitch of a 32 x 32 epilogue block
-  static constexpr int EP_BYTES = 4 * 32 * EP_PITCH * 4;  // one block per wave
+  static constexpr int EP_BYTES = WAVES * 32 * EP_PITCH * 4;  // one block per wave
   static constexpr int RED_BYTES = 8 * BM * 4;
   static constexpr int AUX_BYTES = EP_BYTES > RED_BYTES ? EP_BYTES : RED_BYTES;
   static constexpr int SUB_BYTES = BM * 128;              // [BM][64] bf16 sub-tile of the epilogue input
@@ -293,13 +307,15 @@ struct DmaShape {
 };
 
 template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, bool BIAS_GRAD>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, (BM == 128 && BN == 128) ? 2 : 1)))
+__global__ __launch_bounds__(64 * gemm_waves(BM, BN, EPI))
+__attribute__((amdgpu_waves_per_eu(gemm_waves(BM, BN, EPI) / 4, (BM == 128 && BN == 128) ? 2 : gemm_waves(BM, BN, EPI) / 4)))
 void gemm_bf16_dma_kernel(MfmaArgs p) {
   constexpr bool HAS_BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RES || EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_GELU_D;
   constexpr bool HAS_AUX = EPI == EPI_BIAS_RES || EPI == EPI_GELU_BWD || EPI == EPI_MUL;
-  using S = DmaShape<BM, BN, HAS_AUX>;
-  using TA = DmaTile<BM, A_KMAJ>;
-  using TB = DmaTile<BN, B_KMAJ>;
+  using S = DmaShape<BM, BN, EPI>;
+  using TA = DmaTile<BM, A_KMAJ, S::WAVES>;
+  using TB = DmaTile<BN, B_KMAJ, S::WAVES>;
+  constexpr int NT = S::NT;
   constexpr int WM = S::WM, WN = S::WN, FM = S::FM, FN = S::FN, NS = S::NS;
   constexpr int A_BYTES = TA::BYTES;
   constexpr int NDMA = TA::NINST + TB::NINST;              // DMA instructions per wave per stage
@@ -313,7 +329,7 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   __shared__ __attribute__((aligned(16))) float bias_s[HAS_BIAS ? BN : 4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / S::WGN, wn = wave % S::WGN;
   int tm, tn;
   int z;
   tile_coords((p.M + BM - 1) / BM, (p.N + BN - 1) / BN, tm, tn, z);
@@ -338,7 +354,7 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
 
   // the block's bias columns, read by the epilogue from LDS
   if constexpr (HAS_BIAS) {
-    for (int c = tid; c < BN; c += kThreads)
+    for (int c = tid; c < BN; c += NT)
       bias_s[c] = n0 + c < p.N ? (float)reinterpret_cast<const bf16*>(p.e.bias)[n0 + c] : 0.f;
   }
 
@@ -347,7 +363,7 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   // [BM][64]-column sub-tiles with 128-byte swizzled rows (one memory round
   // trip for the whole tile).  aux_stage(j) gives the stage of its j-th part.
   auto issue_aux = [&](auto aux_stage) {
-    using TX = DmaTile<BM, true>;
+    using TX = DmaTile<BM, true, S::WAVES>;
     const i32x4_rsrc rx = make_rsrc4(p.e.aux_in, p.aux_bytes);
     const typename TX::Lane lx = TX::lane_part(wave, lane, m0, p.e.ld_aux);
 #pragma unroll
@@ -411,7 +427,7 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
           // column sums of the m-major dY tile: thread t sums k rows 8*(t/32) .. +7 of chunk t%32
           if (do_bias) {
             constexpr int CH = BM / 8;
-            for (int u = tid; u < CH * 8; u += kThreads) {
+            for (int u = tid; u < CH * 8; u += NT) {
               const int cc = u % CH, kg = u / CH;
 #pragma unroll
               for (int r = 0; r < 8; ++r) {
@@ -553,13 +569,13 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
       __syncthreads();
       GPT2_LDS float* red = reinterpret_cast<GPT2_LDS float*>(epi_lds);   // [8 k-groups][BM]
       constexpr int CH = BM / 8;
-      for (int u = tid; u < CH * 8; u += kThreads) {
+      for (int u = tid; u < CH * 8; u += NT) {
         const int cc = u % CH, kg = u / CH;
 #pragma unroll
         for (int e = 0; e < 8; ++e) red[kg * BM + cc * 8 + e] = bsum[e];
       }
       __syncthreads();
-      for (int m = tid; m < BM; m += kThreads) {
+      for (int m = tid; m < BM; m += NT) {
         float t = 0.f;
 #pragma unroll
         for (int kg = 0; kg < 8; ++kg) t += red[kg * BM + m];
@@ -770,7 +786,7 @@ int launch_tile(const MfmaArgs& a, int splits, hipStream_t stream) {
   const unsigned tiles = (unsigned)(ceil_div64(a.M, BM) * ceil_div64(a.N, BN));
   mark_begin(0, stream);
   hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, A_KMAJ, B_KMAJ, EPI, BIAS_GRAD>), dim3(tiles, splits),
-                     dim3(kThreads), 0, stream, a);
+                     dim3(64 * gemm_waves(BM, BN, EPI)), 0, stream, a);
   GPT2_LAUNCH_CHECK();
   mark_end(0, stream);
   return 0;
