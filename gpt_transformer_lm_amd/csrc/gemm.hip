@@ -744,10 +744,19 @@ Plan plan_bf16(int epi, int M, int N, int K, bool a_kmajor, bool b_kmajor) {
   const int def_bm = M >= 2048 ? 256 : 128, def_bn = N >= 2048 ? 256 : 128;
   Plan best{def_bm, def_bn, 1, 0};
   double best_t = 1e300;
-  // Short-K products with a bias / residual / GELU / multiply epilogue: the
-  // epilogue is a large share of each tile, and 128x128 tiles at two blocks
-  // per compute unit overlap it with the other block's main loop (measured
-  // 15-25% faster than one-block tiles at M = 24576, K = 768).
+  // Short-K products with a bias or GELU epilogue and a wide N (QKV, fc
+  // forward): the 8-wave 256x256 tile (measured 3-5% faster than 128x128 at
+  // M = 24576, K = 768).
+  if (!may_split && (epi == EPI_BIAS_GELU_D || epi == EPI_BIAS) && a_kmajor && b_kmajor && M >= 2048 &&
+      N >= 2048 && K <= 1024) {
+    best = Plan{256, 256, 1, kt * kBK};
+    return best;
+  }
+  // Other short-K products with an epilogue (residual add, GELU' multiply,
+  // which read an input tile): the epilogue is a large share of each tile, and
+  // 128x128 tiles at two blocks per compute unit overlap it with the other
+  // block's main loop (measured 15-25% faster than one-block tiles at
+  // M = 24576, K = 768).
   if (!may_split && epi != EPI_STORE && a_kmajor && b_kmajor && M >= 2048 && K <= 1024) {
     best = Plan{128, 128, 1, 0};
     best.k_per_split = kt * kBK;
