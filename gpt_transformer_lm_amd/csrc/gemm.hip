@@ -49,8 +49,18 @@ constexpr int kThreads = 256;   // fp32 kernel, split-K reductions
 // (Tiles whose epilogue reads an input tile keep 4 waves: 8 waves' epilogue
 // staging would not fit the LDS beside their stage ring.)
 constexpr bool epi_has_aux(int epi) { return epi == EPI_BIAS_RES || epi == EPI_GELU_BWD || epi == EPI_MUL; }
-constexpr int gemm_waves(int BM, int BN, int epi) { return BM == 256 && BN >= 128 && !epi_has_aux(epi) ? 8 : 4; }
-constexpr int gemm_wave_rows(int BM, int BN, int epi) { return gemm_waves(BM, BN, epi) == 8 && BN == 128 ? 4 : 2; }
+// With KGS = 2 (the planner's choice for a 192x192 tile whose K per tile is
+// long) the block runs 8 waves as two K-groups of 2 x 2: each group takes two
+// of the four k16 slices of every K step for the same 96 x 96 patches, and the
+// second group's sums are added to the first's through the LDS before the
+// epilogue.  (For K = 768 .. 3072 per tile that exchange costs more than the
+// second wave per SIMD gains: measured 5-25 % slower there.)
+constexpr int gemm_waves(int BM, int BN, int epi, int kgs) {
+  return (BM == 256 && BN >= 128 && !epi_has_aux(epi)) || kgs == 2 ? 8 : 4;
+}
+constexpr int gemm_wave_rows(int BM, int BN, int epi, int kgs) {
+  return gemm_waves(BM, BN, epi, kgs) == 8 && BN == 128 ? 4 : 2;
+}
 
 struct EpiArgs {
   int epi;
@@ -277,11 +287,12 @@ struct DmaTile {
 // allows; the epilogue's staging (and the bias-gradient reduction) goes into
 // the last stage buffer when the epilogue input tile (HAS_AUX) leaves it free,
 // else into an array of its own.
-template <int BM, int BN, int EPI>
+template <int BM, int BN, int EPI, int KGS>
 struct DmaShape {
   static constexpr bool HAS_AUX = epi_has_aux(EPI);
-  static constexpr int WAVES = gemm_waves(BM, BN, EPI), NT = 64 * WAVES;
-  static constexpr int WGM = gemm_wave_rows(BM, BN, EPI), WGN = WAVES / WGM;   // wave grid
+  static constexpr int WAVES = gemm_waves(BM, BN, EPI, KGS), NT = 64 * WAVES;
+  static constexpr int KG = KGS;                                             // K-groups
+  static constexpr int WGM = gemm_wave_rows(BM, BN, EPI, KGS), WGN = WAVES / (WGM * KG);   // wave grid
   static constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
   static constexpr int STAGE_BYTES = (BM + BN) * kBK * 2;
   static constexpr int EP_PITCH = 36;                     // fp32 pitch of a 32 x 32 epilogue block
@@ -306,13 +317,14 @@ struct DmaShape {
   static constexpr bool EARLY_AUX = HAS_AUX && AUX_STAGES < NS;
 };
 
-template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, bool BIAS_GRAD>
-__global__ __launch_bounds__(64 * gemm_waves(BM, BN, EPI))
-__attribute__((amdgpu_waves_per_eu(gemm_waves(BM, BN, EPI) / 4, (BM == 128 && BN == 128) ? 2 : gemm_waves(BM, BN, EPI) / 4)))
+template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, bool BIAS_GRAD, int KGS>
+__global__ __launch_bounds__(64 * gemm_waves(BM, BN, EPI, KGS))
+__attribute__((amdgpu_waves_per_eu(gemm_waves(BM, BN, EPI, KGS) / 4,
+                                   (BM == 128 && BN == 128) ? 2 : gemm_waves(BM, BN, EPI, KGS) / 4)))
 void gemm_bf16_dma_kernel(MfmaArgs p) {
   constexpr bool HAS_BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RES || EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_GELU_D;
   constexpr bool HAS_AUX = EPI == EPI_BIAS_RES || EPI == EPI_GELU_BWD || EPI == EPI_MUL;
-  using S = DmaShape<BM, BN, EPI>;
+  using S = DmaShape<BM, BN, EPI, KGS>;
   using TA = DmaTile<BM, A_KMAJ, S::WAVES>;
   using TB = DmaTile<BN, B_KMAJ, S::WAVES>;
   constexpr int NT = S::NT;
@@ -329,7 +341,10 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   __shared__ __attribute__((aligned(16))) float bias_s[HAS_BIAS ? BN : 4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / S::WGN, wn = wave % S::WGN;
+  const int wid = wave % (S::WGM * S::WGN), kg = wave / (S::WGM * S::WGN);
+  const int wm = wid / S::WGN, wn = wid % S::WGN;
+  constexpr int KK = kBK / 16 / S::KG;                    // k16 slices per K step of this wave
+  static_assert(S::KG == 1 || !BIAS_GRAD, "K-groups take no fused bias gradient");
   int tm, tn;
   int z;
   tile_coords((p.M + BM - 1) / BM, (p.N + BN - 1) / BN, tm, tn, z);
@@ -442,16 +457,16 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
         }
         bf16x8 a[2][FM], b[2][FN];
 #pragma unroll
-        for (int i = 0; i < FM; ++i) a[0][i] = TA::frag(As, wm * WM + i * 32, 0, lane);
+        for (int i = 0; i < FM; ++i) a[0][i] = TA::frag(As, wm * WM + i * 32, kg * KK, lane);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) b[0][j] = TB::frag(Bs, wn * WN + j * 32, 0, lane);
+        for (int j = 0; j < FN; ++j) b[0][j] = TB::frag(Bs, wn * WN + j * 32, kg * KK, lane);
 #pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
-          if (kk + 1 < kBK / 16) {
+        for (int kk = 0; kk < KK; ++kk) {
+          if (kk + 1 < KK) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) a[(kk + 1) & 1][i] = TA::frag(As, wm * WM + i * 32, kk + 1, lane);
+            for (int i = 0; i < FM; ++i) a[(kk + 1) & 1][i] = TA::frag(As, wm * WM + i * 32, kg * KK + kk + 1, lane);
 #pragma unroll
-            for (int j = 0; j < FN; ++j) b[(kk + 1) & 1][j] = TB::frag(Bs, wn * WN + j * 32, kk + 1, lane);
+            for (int j = 0; j < FN; ++j) b[(kk + 1) & 1][j] = TB::frag(Bs, wn * WN + j * 32, kg * KK + kk + 1, lane);
           }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -482,6 +497,48 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   }
   // bias and epilogue input visible; every wave done with the stage buffers reused below
   if constexpr (HAS_BIAS || HAS_AUX || S::EPI_IN_STAGE) __syncthreads();
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  if constexpr (S::KG == 2) {
+    // The second K-group's sums go through the idle stage buffers, one 4 KiB
+    // block per accumulator tile (16-byte runs in lane order, conflict-free),
+    // and the first group adds them to its own.
+    constexpr int PER = S::STAGE_BYTES / 4096;
+    static_assert(S::WGM * S::WGN * FM * FN <= NS * PER, "K-group partial sums must fit the stages");
+    auto blk = [&](int i, int j) -> GPT2_LDS f32x4* {
+      const int bi = (wid * FM + i) * FN + j;
+      return reinterpret_cast<GPT2_LDS f32x4*>(stage_ptr(bi / PER) + (bi % PER) * 4096) + lane;
+    };
+    if (kg == 1) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            f32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = acc[i][j][4 * g + e];
+            blk(i, j)[64 * g] = w;
+          }
+    }
+    __syncthreads();
+    if (kg == 0) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 w = blk(i, j)[64 * g];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][4 * g + e] += w[e];
+          }
+          // one tile at a time: hoisting every read would need 144 more registers
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    __syncthreads();   // the epilogue staging below reuses the stage buffers
+  }
   GPT2_LDS char* epi_lds =
       S::EPI_IN_STAGE ? stage_ptr(S::EARLY_AUX ? s_last : NS - 1) : (GPT2_LDS char*)epi_own;
   auto aux_stage = [&](int j) { return S::EARLY_AUX ? stage_ptr((s_last + 1 + j) % NS) : stage_ptr(j); };
@@ -497,72 +554,73 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   // LDS block (LDS operations of one wave complete in order, so no barrier).
   // The products were taken as B x A, so element r of lane l sits at row l%32,
   // column 8(r/4) + 4(l/32) + r%4: four consecutive columns per 16-byte write.
-  typedef float f32x4 __attribute__((ext_vector_type(4)));
-  GPT2_LDS float* ep = reinterpret_cast<GPT2_LDS float*>(epi_lds) + wave * 32 * S::EP_PITCH;
+  GPT2_LDS float* ep = reinterpret_cast<GPT2_LDS float*>(epi_lds) + wid * 32 * S::EP_PITCH;
   const int hi = lane >> 5;
+  if (S::KG == 1 || kg == 0) {   // the second K-group is done
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
+      for (int j = 0; j < FN; ++j) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 w;
+        for (int g = 0; g < 4; ++g) {
+          f32x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = acc[i][j][4 * g + e];
-        *reinterpret_cast<GPT2_LDS f32x4*>(ep + (lane & 31) * S::EP_PITCH + 8 * g + 4 * hi) = w;
-      }
-      __builtin_amdgcn_wave_barrier();
+          for (int e = 0; e < 4; ++e) w[e] = acc[i][j][4 * g + e];
+          *reinterpret_cast<GPT2_LDS f32x4*>(ep + (lane & 31) * S::EP_PITCH + 8 * g + 4 * hi) = w;
+        }
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int idx = lane + 64 * q, rl = idx >> 2, cc = idx & 3;
-        const int grow = m0 + wm * WM + i * 32 + rl, gcol = n0 + wn * WN + j * 32 + cc * 8;
-        if (grow < p.M && gcol < p.N) {
-          float v[8];
-          {
-            const GPT2_LDS f32x4* q = reinterpret_cast<const GPT2_LDS f32x4*>(ep + rl * S::EP_PITCH + cc * 8);
-            const f32x4 lo = q[0], hi4 = q[1];
+        for (int q = 0; q < 2; ++q) {
+          const int idx = lane + 64 * q, rl = idx >> 2, cc = idx & 3;
+          const int grow = m0 + wm * WM + i * 32 + rl, gcol = n0 + wn * WN + j * 32 + cc * 8;
+          if (grow < p.M && gcol < p.N) {
+            float v[8];
+            {
+              const GPT2_LDS f32x4* q = reinterpret_cast<const GPT2_LDS f32x4*>(ep + rl * S::EP_PITCH + cc * 8);
+              const f32x4 lo = q[0], hi4 = q[1];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { v[e] = lo[e]; v[4 + e] = hi4[e]; }
-          }
-          if (vec) {
-            const int tr = wm * WM + i * 32 + rl, tc = wn * WN + j * 32 + cc * 8;
-            if constexpr (HAS_BIAS) {
-#pragma unroll
-              for (int e = 0; e < 8; ++e) v[e] += bias_s[tc + e];
+              for (int e = 0; e < 4; ++e) { v[e] = lo[e]; v[4 + e] = hi4[e]; }
             }
-            if constexpr (HAS_AUX) {
-              const int sb = tc >> 6, ch = (tc & 63) >> 3;
-              const GPT2_LDS char* t = aux_stage(sb / PER_STAGE) + (sb % PER_STAGE) * SUB_BYTES;
-              typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-              const u32x4 raw = *reinterpret_cast<const GPT2_LDS u32x4*>(t + tr * 128 + swz(tr, ch) * 16);
-              const uint32_t w[4] = {raw[0], raw[1], raw[2], raw[3]};
-              float x[8];
+            if (vec) {
+              const int tr = wm * WM + i * 32 + rl, tc = wn * WN + j * 32 + cc * 8;
+              if constexpr (HAS_BIAS) {
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                x[2 * e] = __uint_as_float(w[e] << 16);
-                x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+                for (int e = 0; e < 8; ++e) v[e] += bias_s[tc + e];
               }
-              if constexpr (EPI == EPI_BIAS_RES) {
+              if constexpr (HAS_AUX) {
+                const int sb = tc >> 6, ch = (tc & 63) >> 3;
+                const GPT2_LDS char* t = aux_stage(sb / PER_STAGE) + (sb % PER_STAGE) * SUB_BYTES;
+                typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+                const u32x4 raw = *reinterpret_cast<const GPT2_LDS u32x4*>(t + tr * 128 + swz(tr, ch) * 16);
+                const uint32_t w[4] = {raw[0], raw[1], raw[2], raw[3]};
+                float x[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] += x[e];
-              } else if constexpr (EPI == EPI_MUL) {
+                for (int e = 0; e < 4; ++e) {
+                  x[2 * e] = __uint_as_float(w[e] << 16);
+                  x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+                }
+                if constexpr (EPI == EPI_BIAS_RES) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] *= x[e];
-              } else {
+                  for (int e = 0; e < 8; ++e) v[e] += x[e];
+                } else if constexpr (EPI == EPI_MUL) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] *= gelu_tanh_grad_f(x[e]);
+                  for (int e = 0; e < 8; ++e) v[e] *= x[e];
+                } else {
+#pragma unroll
+                  for (int e = 0; e < 8; ++e) v[e] *= gelu_tanh_grad_f(x[e]);
+                }
               }
+              epilogue_vec8_final<EPI>(p.e, grow, gcol, v, z);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (gcol + e < p.N) epilogue_store<EPI, bf16>(p.e, grow, gcol + e, v[e], z);
             }
-            epilogue_vec8_final<EPI>(p.e, grow, gcol, v, z);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (gcol + e < p.N) epilogue_store<EPI, bf16>(p.e, grow, gcol + e, v[e], z);
           }
         }
+        __builtin_amdgcn_wave_barrier();
       }
-      __builtin_amdgcn_wave_barrier();
-    }
+  }
 
   if constexpr (BIAS_GRAD) {
     if (do_bias) {   // uniform over the block
@@ -732,6 +790,7 @@ __global__ void splitk_store_bf16_kernel(const float* __restrict__ partial, int 
 // tiles M = 24576, N = 768 into exactly two rounds.
 struct Plan {
   int bm, bn, splits, k_per_split;
+  int kgroups = 1;   // 2: the 192x192 tile's two K-groups of waves (long K per tile)
 };
 
 Plan plan_bf16(int epi, int M, int N, int K, bool a_kmajor, bool b_kmajor) {
@@ -782,6 +841,9 @@ Plan plan_bf16(int epi, int M, int N, int K, bool a_kmajor, bool b_kmajor) {
   const int kps = (kt + best.splits - 1) / best.splits;
   best.k_per_split = kps * kBK;
   best.splits = (kt + kps - 1) / kps;
+  // a long K per tile amortises the K-groups' exchange of partial sums
+  // (measured: classifier dX, K = 50304, 1.77 -> 1.59 ms)
+  if (best.bm == 192 && best.k_per_split >= 8192 && !epi_has_aux(epi)) best.kgroups = 2;
   return best;
 }
 
@@ -790,12 +852,12 @@ int gemm_splits(int dtype, int epi, int M, int N, int K, bool a_kmajor, bool b_k
   return plan_bf16(epi, M, N, K, a_kmajor, b_kmajor).splits;
 }
 
-template <int BM, int BN, int EPI, bool A_KMAJ, bool B_KMAJ, bool BIAS_GRAD>
+template <int BM, int BN, int EPI, bool A_KMAJ, bool B_KMAJ, bool BIAS_GRAD, int KGS = 1>
 int launch_tile(const MfmaArgs& a, int splits, hipStream_t stream) {
   const unsigned tiles = (unsigned)(ceil_div64(a.M, BM) * ceil_div64(a.N, BN));
   mark_begin(0, stream);
-  hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, A_KMAJ, B_KMAJ, EPI, BIAS_GRAD>), dim3(tiles, splits),
-                     dim3(64 * gemm_waves(BM, BN, EPI)), 0, stream, a);
+  hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, A_KMAJ, B_KMAJ, EPI, BIAS_GRAD, KGS>), dim3(tiles, splits),
+                     dim3(64 * gemm_waves(BM, BN, EPI, KGS)), 0, stream, a);
   GPT2_LAUNCH_CHECK();
   mark_end(0, stream);
   return 0;
@@ -807,7 +869,11 @@ int launch_mfma(const MfmaArgs& a, const Plan& pl, hipStream_t stream) {
   if (pl.bm == 256 && pl.bn == 128) return launch_tile<256, 128, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
   if (pl.bm == 128 && pl.bn == 256) return launch_tile<128, 256, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
   if constexpr (A_KMAJ && B_KMAJ)
-    if (pl.bm == 192 && pl.bn == 192) return launch_tile<192, 192, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
+    if (pl.bm == 192 && pl.bn == 192) {
+      if constexpr (!BIAS_GRAD && !epi_has_aux(EPI))
+        if (pl.kgroups == 2) return launch_tile<192, 192, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD, 2>(a, pl.splits, stream);
+      return launch_tile<192, 192, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
+    }
   return launch_tile<128, 128, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
 }
 
