@@ -286,13 +286,18 @@ def test_softmax_xent(dtype, N, V, Vp):
     assert np.abs(g.sum(-1)).max() < 1e-2 / N
 
 
-def test_classifier_full_size():
+@pytest.mark.parametrize("N", [24 * 1024, 24 * 1024 - 104])
+def test_classifier_full_size(N):
     """The stand-alone classifier at GPT-2 124M shape (hidden 24x1024x768 ~
     N(0,1), tied table 50304x768 ~ N(0,0.02) including its padded rows,
     labels uniform in [0, 50257)): sampled rows of the losses, dlogits and
     d_hidden against the oracle; d_wte by its invariants (padded rows exactly
-    zero, columns sum to zero because every dlogits row does)."""
-    N, C, V, Vp = 24 * 1024, 768, 50257, 50304
+    zero, columns sum to zero because every dlogits row does).  The second
+    row count (a multiple of 8, as the bf16 GEMMs require of every reduction
+    length) leaves a ragged last row tile in every product and a partial last
+    K step in d_wte; the d_hidden product reduces over the whole vocabulary
+    in one tile per block."""
+    C, V, Vp = 768, 50257, 50304
     say("classifier full size", N, C, V, Vp)
     torch = __import__("torch")
     hidden, wte, labels = S.classifier_inputs(N, C, V, Vp, seed=17)
@@ -305,7 +310,7 @@ def test_classifier_full_size():
     torch.cuda.synchronize()
     hi = S.bf16_round(hidden).astype(np.float64)
     wi = S.bf16_round(wte).astype(np.float64)
-    rows = rng(1).integers(0, N, 48)
+    rows = np.concatenate([rng(1).integers(0, N, 48), [N - 1, N - 37]])
     z = hi[rows] @ wi[:V].T
     rl, rdz = O.softmax_cross_entropy(z, labels[rows])
     rdz = rdz * len(rows) / N          # oracle normalised by the sample size
