@@ -104,13 +104,22 @@ __device__ __forceinline__ float gelu_tanh_grad_f(float u) {
   return 0.5f * (1.0f + th) + 0.5f * u * (1.0f - th * th) * dz;
 }
 
-// gelu_tanh_f(u) and gelu_tanh_grad_f(u) from one tanh evaluation.
+// gelu_tanh_f(u) and gelu_tanh_grad_f(u) from one exponential, in the
+// logistic form: with z = k0 (u + k1 u^3) and s = 1 / (1 + e^{-2z}),
+// 1 + tanh z = 2 s and 1 - tanh^2 z = 4 s (1 - s), so
+//   GELU(u) = u s,   GELU'(u) = s (1 + 2 u (1 - s) dz/du),
+// dz/du = k0 (1 + 3 k1 u^2).  Eleven VALU operations besides v_exp_f32 and
+// v_rcp_f32 (the fc forward's epilogue evaluates this per output element).
+// Saturates: e^{-2z} -> inf gives s = 0 (GELU and GELU' 0), -> 0 gives s = 1.
 __device__ __forceinline__ void gelu_tanh_and_grad_f(float u, float& g, float& d) {
   const float k0 = 0.7978845608028654f, k1 = 0.044715f;
-  const float th = tanh_via_exp(k0 * (u + k1 * u * u * u));
-  const float dz = k0 * (1.0f + 3.0f * k1 * u * u);
-  g = 0.5f * u * (1.0f + th);
-  d = 0.5f * (1.0f + th) + 0.5f * u * (1.0f - th * th) * dz;
+  const float u2 = u * u;
+  const float zu = u * fmaf(k1, u2, 1.0f);                                   // z / k0
+  const float e = __builtin_amdgcn_exp2f(zu * (-2.0f * k0 * 1.4426950408889634f));  // e^{-2z}
+  const float sg = __builtin_amdgcn_rcpf(1.0f + e);
+  const float w = u * fmaf(6.0f * k0 * k1, u2, 2.0f * k0);                  // 2 u dz/du
+  g = u * sg;
+  d = sg * fmaf(w, 1.0f - sg, 1.0f);
 }
 
 // ---------------------------------------------------------------- host side
