@@ -90,18 +90,25 @@ __device__ __forceinline__ float tanh_via_exp(float z) {
   return 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e2z);
 }
 
+// GELU_tanh(u) = u (1 + tanh z) / 2 with z = k0 (u + k1 u^3), evaluated in
+// the logistic form u s, s = 1 / (1 + e^{-2z}) (1 + tanh z = 2 s).
 __device__ __forceinline__ float gelu_tanh_f(float u) {
   const float k0 = 0.7978845608028654f, k1 = 0.044715f;
-  const float th = tanh_via_exp(k0 * (u + k1 * u * u * u));
-  return 0.5f * u * (1.0f + th);
+  const float zu = u * fmaf(k1, u * u, 1.0f);                                // z / k0
+  const float e = __builtin_amdgcn_exp2f(zu * (-2.0f * k0 * 1.4426950408889634f));  // e^{-2z}
+  return u * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// d/du of gelu_tanh_f.
+// d/du of gelu_tanh_f: s (1 + 2 u (1 - s) dz/du), dz/du = k0 (1 + 3 k1 u^2)
+// (1 - tanh^2 z = 4 s (1 - s)).
 __device__ __forceinline__ float gelu_tanh_grad_f(float u) {
   const float k0 = 0.7978845608028654f, k1 = 0.044715f;
-  const float th = tanh_via_exp(k0 * (u + k1 * u * u * u));
-  const float dz = k0 * (1.0f + 3.0f * k1 * u * u);
-  return 0.5f * (1.0f + th) + 0.5f * u * (1.0f - th * th) * dz;
+  const float u2 = u * u;
+  const float zu = u * fmaf(k1, u2, 1.0f);
+  const float e = __builtin_amdgcn_exp2f(zu * (-2.0f * k0 * 1.4426950408889634f));
+  const float sg = __builtin_amdgcn_rcpf(1.0f + e);
+  const float w = u * fmaf(6.0f * k0 * k1, u2, 2.0f * k0);                  // 2 u dz/du
+  return sg * fmaf(w, 1.0f - sg, 1.0f);
 }
 
 // gelu_tanh_f(u) and gelu_tanh_grad_f(u) from one exponential, in the
