@@ -85,6 +85,61 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int N, int C, const T* __re
   }
 }
 
+// Rows of 32 * 8 * NCH elements exactly (C = 768: NCH = 3): one half-wave
+// per row, so no lane idles (a whole wave would leave a third of its lanes
+// idle in the second chunk), 8 rows per 256-thread block.  The reductions
+// use xor distances below 32, so each half-wave reduces its own row.
+template <typename T, int NCH>
+__global__ __launch_bounds__(256) void ln_fwd_half_kernel(int N, int C, const T* __restrict__ x,
+                                                          const T* __restrict__ w, const T* __restrict__ b,
+                                                          T* __restrict__ y, float* __restrict__ mean,
+                                                          float* __restrict__ rstd) {
+  const int row = blockIdx.x * 8 + (threadIdx.x >> 5);
+  const int l = threadIdx.x & 31;
+  if (row >= N) return;                     // whole half-waves leave together
+  const T* xr = x + (size_t)row * C;
+  float v[NCH][8], wv[NCH][8], bv[NCH][8];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int ch = l + 32 * c;
+    Chunk8<T>::load(xr + ch * 8, v[c]);
+    Chunk8<T>::load(w + ch * 8, wv[c]);
+    Chunk8<T>::load(b + ch * 8, bv[c]);
+  }
+  auto half_sum = [](float t) {
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+    return t;
+  };
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += v[c][e];
+  const float mu = half_sum(s) / (float)C;
+  float s2 = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float d = v[c][e] - mu;
+      s2 += d * d;
+    }
+  const float rs = 1.0f / sqrtf(half_sum(s2) / (float)C + kLnEps);
+  T* yr = y + (size_t)row * C;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (v[c][e] - mu) * rs * wv[c][e] + bv[c][e];
+    Chunk8<T>::store(yr + (l + 32 * c) * 8, o);
+  }
+  if (l == 0) {
+    mean[row] = mu;
+    rstd[row] = rs;
+  }
+}
+
 // WPB waves per block (1024 threads for C <= 1024, fewer for wider rows so
 // that the row cache fits the registers); each block writes one partial row
 // of dw and db.
@@ -250,6 +305,13 @@ int fwd_t(int N, int C, const void* x, const void* w, const void* b, void* y, fl
   const T* Bb = (const T*)b;
   T* Y = (T*)y;
   mark_begin(0, s);
+  if (C == 32 * 8 * 3) {
+    hipLaunchKernelGGL((ln_fwd_half_kernel<T, 3>), dim3((unsigned)ceil_div64(N, 8)), block, 0, s, N, C, X, W, Bb, Y,
+                       mean, rstd);
+    GPT2_LAUNCH_CHECK();
+    mark_end(0, s);
+    return 0;
+  }
   switch (nch_for(C)) {
     case 1: hipLaunchKernelGGL((ln_fwd_kernel<T, 1>), grid, block, 0, s, N, C, X, W, Bb, Y, mean, rstd); break;
     case 2: hipLaunchKernelGGL((ln_fwd_kernel<T, 2>), grid, block, 0, s, N, C, X, W, Bb, Y, mean, rstd); break;
