@@ -337,6 +337,8 @@ int attention_backward(int dtype, int B, int T_, int H, int hd, const void* qkv,
   // workspace: D [B*H*T], then L2 [B*H*T] at a 256-byte boundary
   float* D = (float*)workspace;
   float* L2 = D + ((size_t)B * H * T_ + 63) / 64 * 64;
+  if (attention_mfma_supported(dtype, hd))
+    return attention_backward_mfma(B, T_, H, qkv, out, dout, lse, L2, D, dqkv, stream);
   const int64_t lanes = (int64_t)B * H * T_ * (hd / 8);
   mark_begin(0, stream);
   if (dtype == BF16) {
@@ -348,8 +350,6 @@ int attention_backward(int dtype, int B, int T_, int H, int hd, const void* qkv,
   }
   GPT2_LAUNCH_CHECK();
   mark_end(0, stream);
-  if (attention_mfma_supported(dtype, hd))
-    return attention_backward_mfma(B, T_, H, qkv, dout, L2, D, dqkv, stream);
   return dtype == BF16 ? bwd_dispatch<bf16>(B, T_, H, hd, qkv, dout, lse, D, dqkv, stream)
                        : bwd_dispatch<float>(B, T_, H, hd, qkv, dout, lse, D, dqkv, stream);
 }

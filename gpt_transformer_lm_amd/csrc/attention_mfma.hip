@@ -432,10 +432,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
 
 // ------------------------------------------------------------------ backward dQ
 
+// Also the per-query quantities both backward kernels use, D_i = dO_i . O_i
+// and lse_i log2(e), from the rows the kernel holds anyway (so it runs before
+// the dK / dV kernel, which reads them).
 __global__ __launch_bounds__(256, 3) void attn_bwd_dq_mfma_kernel(int T, int H, const bf16* __restrict__ qkv,
+                                                               const bf16* __restrict__ out,
                                                                const bf16* __restrict__ dout,
-                                                               const float* __restrict__ lse2,
-                                                               const float* __restrict__ Dv,
+                                                               const float* __restrict__ lse,
+                                                               float* __restrict__ lse2,
+                                                               float* __restrict__ Dv,
                                                                bf16* __restrict__ dqkv, float scale) {
   constexpr int NS = NS_DQ;
   __shared__ __attribute__((aligned(1024))) char ring[NS][2 * TILE];   // K tile, V tile
@@ -455,8 +460,23 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dq_mfma_kernel(int T, int H, 
   bf16x8 qf[4], of[4];
   frags_global(Qg, ld, myq, T, lane, qf);
   frags_global(Og, (size_t)C, myq, T, lane, of);
-  const float lq = myq < T ? lse2[(size_t)bh * T + myq] : 0.f;
-  const float Dq = myq < T ? Dv[(size_t)bh * T + myq] : 0.f;
+  float Dq, lq;
+  {
+    // each half-wave holds 32 of the row's 64 dO and O values
+    bf16x8 o_[4];
+    frags_global(out + (size_t)b * T * C + h * HD, (size_t)C, myq, T, lane, o_);
+    float d = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d = fmaf((float)of[s][e], (float)o_[s][e], d);
+    Dq = half_sum(d);
+    lq = myq < T ? lse[(size_t)bh * T + myq] * kLog2e : 0.f;
+    if (myq < T && lane < 32) {
+      Dv[(size_t)bh * T + myq] = Dq;
+      lse2[(size_t)bh * T + myq] = lq;
+    }
+  }
   floatx16 dq[2];
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt)
@@ -535,20 +555,21 @@ int attention_forward_mfma(int B, int T, int H, const void* qkv, void* out, floa
   return 0;
 }
 
-int attention_backward_mfma(int B, int T, int H, const void* qkv, const void* dout, const float* lse2,
-                            const float* D, void* dqkv, hipStream_t stream) {
+int attention_backward_mfma(int B, int T, int H, const void* qkv, const void* out, const void* dout,
+                            const float* lse, float* lse2, float* D, void* dqkv, hipStream_t stream) {
   dim3 grid((unsigned)ceil_div64(T, ROWS), (unsigned)(B * H));
   const float scale = 1.0f / sqrtf((float)HD);
+  // dQ first: it also writes D and lse2 for the dK / dV kernel
+  mark_begin(2, stream);
+  hipLaunchKernelGGL(attn_bwd_dq_mfma_kernel, grid, dim3(256), 0, stream, T, H, (const bf16*)qkv, (const bf16*)out,
+                     (const bf16*)dout, lse, lse2, D, (bf16*)dqkv, scale);
+  GPT2_LAUNCH_CHECK();
+  mark_end(2, stream);
   mark_begin(1, stream);
   hipLaunchKernelGGL(attn_bwd_dkdv_mfma_kernel, grid, dim3(256), 0, stream, T, H, (const bf16*)qkv,
                      (const bf16*)dout, lse2, D, (bf16*)dqkv, scale);
   GPT2_LAUNCH_CHECK();
   mark_end(1, stream);
-  mark_begin(2, stream);
-  hipLaunchKernelGGL(attn_bwd_dq_mfma_kernel, grid, dim3(256), 0, stream, T, H, (const bf16*)qkv,
-                     (const bf16*)dout, lse2, D, (bf16*)dqkv, scale);
-  GPT2_LAUNCH_CHECK();
-  mark_end(2, stream);
   return 0;
 }
 

@@ -91,9 +91,10 @@ size_t attention_backward_workspace_bytes(int B, int T, int H, int hd);
 // launchers above dispatch to them when attention_mfma_supported().
 bool attention_mfma_supported(int dtype, int hd);
 int attention_forward_mfma(int B, int T, int H, const void* qkv, void* out, float* lse, hipStream_t stream);
-// lse2 = lse * log2(e) (base-2 log-sum-exp), D = rowsum(dO * O), both [B, H, T].
-int attention_backward_mfma(int B, int T, int H, const void* qkv, const void* dout, const float* lse2,
-                            const float* D, void* dqkv, hipStream_t stream);
+// lse2 = lse * log2(e) (base-2 log-sum-exp) and D = rowsum(dO * O), both
+// [B, H, T] scratch, are computed by the dQ kernel and read by the dK / dV one.
+int attention_backward_mfma(int B, int T, int H, const void* qkv, const void* out, const void* dout,
+                            const float* lse, float* lse2, float* D, void* dqkv, hipStream_t stream);
 int attention_backward(int dtype, int B, int T, int H, int hd, const void* qkv, const void* out,
                        const void* dout, const float* lse, void* dqkv, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);

@@ -515,8 +515,10 @@ int backward_impl(gpt2_model* m, bool acc) {
                                          m->lgrad(7, l), acc)));
     RC(run_gemm(m, S_ATTPROJ_DX, dx_desc(m, BT, C, C, dres_t, m->lparam(6, l), m->wt(6, l), d_ln, EPI_STORE, nullptr)));
     {
-      // three kernels: D = rowsum(dO * O); dK, dV (recomputing S and dP); dQ
-      const bool a0 = timer_arm(m, S_ATTN_DOT, 0), a1 = timer_arm(m, S_ATTN_DKDV, 1),
+      // dK, dV (recomputing S and dP) and dQ; D = rowsum(dO * O) is a kernel of
+      // its own except on the matrix-core path, where the dQ kernel forms it
+      const bool mfma = attention_mfma_supported(dt, hd);
+      const bool a0 = !mfma && timer_arm(m, S_ATTN_DOT, 0), a1 = timer_arm(m, S_ATTN_DKDV, 1),
                  a2 = timer_arm(m, S_ATTN_DQ, 2);
       const int rc = attention_backward(dt, B, T, H, hd, m->at<char>(o.qkv), m->at<char>(o.atty), d_ln,
                                         m->at<float>(o.lse), d_qkv, m->scratch(), sb, s);
@@ -525,7 +527,7 @@ int backward_impl(gpt2_model* m, bool acc) {
       const double lse_b = (double)B * H * T * 4;
       if (a0) timer_commit(m, S_ATTN_DOT, 0.0, 2.0 * act + lse_b);
       if (a1) timer_commit(m, S_ATTN_DKDV, 4.0 * causal_mm, 4.0 * act + 2.0 * lse_b + 2.0 * act);
-      if (a2) timer_commit(m, S_ATTN_DQ, 1.0 * causal_mm, 4.0 * act + 2.0 * lse_b + act);
+      if (a2) timer_commit(m, S_ATTN_DQ, 1.0 * causal_mm, 4.0 * act + 2.0 * lse_b + act + (mfma ? act + lse_b : 0.0));
     }
     // qkv = ln1 Wqkv^T + bqkv
     RC(run_gemm(m, S_QKV_DW, dw_desc(m, BT, 3 * C, C, d_qkv, m->at<char>(o.ln1), m->lgrad(4, l),
