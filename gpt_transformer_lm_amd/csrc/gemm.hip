@@ -13,11 +13,14 @@
 //     shape), K step 64; each wave owns a patch of v_mfma_f32_32x32x16_bf16
 //     accumulators: 4 waves in a 2 x 2 grid, except the 256-row tiles without
 //     an epilogue input, which run 8 waves (2 x 4 for 256x256, 4 x 2 for
-//     256x128) so every SIMD holds two waves of the block;
+//     256x128) so every SIMD holds two waves of the block, and the 192x192
+//     tile of a long reduction, which runs two K-groups of 2 x 2 waves;
 //   * operand tiles go from global memory straight into LDS with
 //     buffer_load ... lds (no register staging), in a ring of 2-4 stages that
 //     fills the LDS, so several K steps are in flight while the matrix cores
-//     work on the current one; one barrier per K step;
+//     work on the current one; one barrier per K step; in tiles that run one
+//     block per compute unit the refill of the ring is interleaved with the
+//     step's first matrix instructions;
 //   * k-major operands are stored as 128-byte rows with XOR-swizzled 16-byte
 //     chunks and read with ds_read_b128; m-major operands (dY^T and X in
 //     dW = dY^T X, W in dX = dY W) are stored as they lie in memory and read
