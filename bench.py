@@ -140,6 +140,8 @@ def main():
                     help="micro-batches of B x T accumulated per update (gradient of their mean loss)")
     ap.add_argument("--max-grad-norm", type=float, default=0.0,
                     help="global-norm gradient clipping threshold (0: off)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each timed step from one captured HIP graph (plain step only)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a kernel of known traffic, "
                          "to calibrate hardware byte counters against)")
@@ -157,7 +159,14 @@ def main():
     B, T = c["B"], c["T"]
     cfg = lib.make_config(c["V"], c["Vp"], c["maxT"], c["L"], c["H"], c["C"], B, T, lib.GPT2_BF16)
     torch.cuda.init()
-    stream = torch.cuda.current_stream()
+    K = max(args.accum, 1)
+    plain = K == 1 and args.max_grad_norm <= 0
+    if args.graph and not plain:
+        print("--graph replays the plain step (no --accum / --max-grad-norm)", file=sys.stderr)
+        sys.exit(2)
+    # a captured graph needs a stream other than the null stream
+    stream = torch.cuda.Stream() if args.graph else torch.cuda.current_stream()
+    torch.cuda.set_stream(stream)
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -167,8 +176,6 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     model = lib.Model(cfg, seed=args.seed, stream=stream)
-    K = max(args.accum, 1)
-    plain = K == 1 and args.max_grad_norm <= 0
     nsteps = args.warmup + args.steps
     batches = []
     for s in range(nsteps * K + 1):
@@ -215,7 +222,20 @@ def main():
             site_ms[s] = r["total_ms"]
             sites[s] = dict(roofline_of(s, r), ms=r["total_ms"], launches=r["launches"])
     dom = args.site or (max(site_ms, key=site_ms.get) if site_ms else "fc")
-    model.timing_enable(dom, True)
+    if args.graph:
+        # the timing events sit outside the graph: the dominant kernel's launch
+        # time comes from the last warmup step, then the step is captured
+        tok_buf = torch.zeros((B, T), dtype=torch.int32, device="cuda")
+        tgt_buf = torch.zeros((B, T), dtype=torch.int32, device="cuda")
+        model.graph_capture(tok_buf, tgt_buf)
+
+        def step(i, t):
+            x, y = batches[i]
+            tok_buf.copy_(x)
+            tgt_buf.copy_(y)
+            model.graph_step(c["lr"], 0.9, 0.999, 1e-8, c["wd"], t, read_loss=False)
+    else:
+        model.timing_enable(dom, True)
 
     torch.cuda.synchronize()
     loss_before = model.get_mean_loss() if args.warmup > 0 else None   # last warmup step
@@ -230,17 +250,19 @@ def main():
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1)
     elapsed = wall
-    dom_t = model.timing_read(dom)
+    dom_t = sites[dom] if args.graph else model.timing_read(dom)
     loss_last = model.get_mean_loss() if args.steps > 0 else None
     model.close()
 
     tok_s = K * B * T * args.steps / elapsed
     ftok = flops_per_token(c)
     mfu = tok_s * ftok / PEAK_BF16
-    roof = roofline_of(dom, dom_t)
+    roof = roofline_of(dom, dom_t) if not args.graph else {k: dom_t[k] for k in (
+        "bound", "achieved", "peak", "unit", "frac", "algorithmic_per_launch", "avg_ms")}
     roof["traffic"] = measured_traffic(dom, args.config)
     roof.update({"kernel_site": dom, "kernel": KERNEL_OF.get(dom, dom), "avg_launch_ms": roof.pop("avg_ms"),
-                 "launches": dom_t["launches"]})
+                 "launches": dom_t["launches"],
+                 "timed_in": "the last warmup step (eager)" if args.graph else "the timed steps"})
 
     out = {
         "metric": METRIC,
@@ -258,7 +280,8 @@ def main():
         "config": {"workload": f"GPT-2 {args.config} training step (fwd+bwd+AdamW, fp32 master), "
                                f"B={B}, T={T}, vocab 50257 padded to 50304"
                                + ("" if plain else f", {K} accumulated micro-batches per update, global-norm "
-                                                   f"clipping at {args.max_grad_norm}"),
+                                                   f"clipping at {args.max_grad_norm}")
+                               + (", each step one HIP graph replay" if args.graph else ""),
                    "global_batch": K * B, "seq_len": T, "parallelism": "single GPU"},
         "mfu": mfu,
         "model_flops_per_token": ftok,

@@ -21,10 +21,13 @@
 namespace gpt2k {
 namespace {
 
+// Hyperparameters come by value, or from device memory when hp_dev is set
+// (a captured graph replays with the values its caller last wrote there).
 __global__ void adamw_kernel(int64_t n, float* __restrict__ master, const float* __restrict__ grad,
                              float* __restrict__ mom1, float* __restrict__ mom2, bf16* __restrict__ pbf,
-                             float lr, float b1, float b2, float eps, float wd, float c1, float c2,
-                             const float* __restrict__ gscale) {
+                             AdamHP hp_val, const AdamHP* __restrict__ hp_dev, const float* __restrict__ gscale) {
+  const AdamHP hp = hp_dev ? *hp_dev : hp_val;
+  const float lr = hp.lr, b1 = hp.b1, b2 = hp.b2, eps = hp.eps, wd = hp.wd, c1 = hp.c1, c2 = hp.c2;
   // the gradient enters scaled by *gscale (global-norm clipping) when given
   const float gs = gscale ? *gscale : 1.0f;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
@@ -108,6 +111,13 @@ __global__ __launch_bounds__(256) void grad_norm_finalize_kernel(const float* __
     out[0] = norm;
     out[1] = (max_norm > 0.f && norm > max_norm) ? max_norm / norm : 1.0f;
   }
+}
+
+__global__ void set_adam_hp_kernel(AdamHP* dst, AdamHP v) { *dst = v; }
+
+__global__ void copy_i32_kernel(int64_t n, const int32_t* __restrict__ src, int32_t* __restrict__ dst) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src[i];
 }
 
 __global__ void cast_kernel(int64_t n, const float* __restrict__ src, bf16* __restrict__ dst) {
@@ -196,21 +206,44 @@ int grad_norm(int64_t n, const float* grad, float max_norm, float* workspace, hi
   return 0;
 }
 
+AdamHP adam_hparams(float lr, float beta1, float beta2, float eps, float wd, int t) {
+  AdamHP h;
+  h.lr = lr; h.b1 = beta1; h.b2 = beta2; h.eps = eps; h.wd = wd;
+  h.c1 = (float)(1.0 / (1.0 - pow((double)beta1, (double)t)));
+  h.c2 = (float)(1.0 / (1.0 - pow((double)beta2, (double)t)));
+  return h;
+}
+
+int set_adam_hparams(AdamHP* dst, const AdamHP& v, hipStream_t stream) {
+  if (!dst) return gpt2_internal_fail(1, "set_adam_hparams: NULL destination");
+  hipLaunchKernelGGL(set_adam_hp_kernel, dim3(1), dim3(1), 0, stream, dst, v);
+  GPT2_LAUNCH_CHECK();
+  return 0;
+}
+
 int adamw(int64_t n, float* master, const float* grad, float* m, float* v, bf16* param_bf16, float lr,
-          float beta1, float beta2, float eps, float wd, int t, hipStream_t stream, const float* gscale) {
+          float beta1, float beta2, float eps, float wd, int t, hipStream_t stream, const float* gscale,
+          const AdamHP* hp_dev) {
   if (n < 0 || !master || !grad || !m || !v || t < 1) return gpt2_internal_fail(1, "adamw: bad arguments");
   if (n == 0) return 0;
   if (((uintptr_t)master | (uintptr_t)grad | (uintptr_t)m | (uintptr_t)v) % 16 ||
       (param_bf16 && (uintptr_t)param_bf16 % 8))
     return gpt2_internal_fail(1, "adamw: buffers must be 16-byte aligned");
-  const double c1 = 1.0 / (1.0 - pow((double)beta1, (double)t));
-  const double c2 = 1.0 / (1.0 - pow((double)beta2, (double)t));
+  const AdamHP hp = adam_hparams(lr, beta1, beta2, eps, wd, t);
   unsigned grid = (unsigned)std::min<int64_t>(ceil_div64(n, 4 * 256), 8192);
   mark_begin(0, stream);
-  hipLaunchKernelGGL(adamw_kernel, dim3(grid), dim3(256), 0, stream, n, master, grad, m, v, param_bf16, lr, beta1,
-                     beta2, eps, wd, (float)c1, (float)c2, gscale);
+  hipLaunchKernelGGL(adamw_kernel, dim3(grid), dim3(256), 0, stream, n, master, grad, m, v, param_bf16, hp, hp_dev,
+                     gscale);
   GPT2_LAUNCH_CHECK();
   mark_end(0, stream);
+  return 0;
+}
+
+int copy_i32(int64_t n, const int32_t* src, int32_t* dst, hipStream_t stream) {
+  if (n <= 0) return 0;
+  if (!src || !dst) return gpt2_internal_fail(1, "copy_i32: NULL buffer");
+  hipLaunchKernelGGL(copy_i32_kernel, dim3(blocks_for(n)), dim3(256), 0, stream, n, src, dst);
+  GPT2_LAUNCH_CHECK();
   return 0;
 }
 

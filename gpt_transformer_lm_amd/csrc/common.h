@@ -81,38 +81,8 @@ __device__ __forceinline__ float fast_exp(float x) {
   return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
 }
 
-// GELU, tanh form: 0.5 u (1 + tanh(k0 (u + k1 u^3))), with
-// tanh(z) = 1 - 2 / (1 + e^{2z}); e^{2z} from the hardware base-2 exponential
-// and the reciprocal from v_rcp_f32 (both ~1 ulp).  Saturates correctly:
-// e^{2z} -> inf gives tanh -> 1, e^{2z} -> 0 gives tanh -> -1.
-__device__ __forceinline__ float tanh_via_exp(float z) {
-  const float e2z = __builtin_amdgcn_exp2f(z * 2.8853900817779268f);   // 2 log2(e)
-  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e2z);
-}
-
-// GELU_tanh(u) = u (1 + tanh z) / 2 with z = k0 (u + k1 u^3), evaluated in
-// the logistic form u s, s = 1 / (1 + e^{-2z}) (1 + tanh z = 2 s).
-__device__ __forceinline__ float gelu_tanh_f(float u) {
-  const float k0 = 0.7978845608028654f, k1 = 0.044715f;
-  const float zu = u * fmaf(k1, u * u, 1.0f);                                // z / k0
-  const float e = __builtin_amdgcn_exp2f(zu * (-2.0f * k0 * 1.4426950408889634f));  // e^{-2z}
-  return u * __builtin_amdgcn_rcpf(1.0f + e);
-}
-
-// d/du of gelu_tanh_f: s (1 + 2 u (1 - s) dz/du), dz/du = k0 (1 + 3 k1 u^2)
-// (1 - tanh^2 z = 4 s (1 - s)).
-__device__ __forceinline__ float gelu_tanh_grad_f(float u) {
-  const float k0 = 0.7978845608028654f, k1 = 0.044715f;
-  const float u2 = u * u;
-  const float zu = u * fmaf(k1, u2, 1.0f);
-  const float e = __builtin_amdgcn_exp2f(zu * (-2.0f * k0 * 1.4426950408889634f));
-  const float sg = __builtin_amdgcn_rcpf(1.0f + e);
-  const float w = u * fmaf(6.0f * k0 * k1, u2, 2.0f * k0);                  // 2 u dz/du
-  return sg * fmaf(w, 1.0f - sg, 1.0f);
-}
-
-// gelu_tanh_f(u) and gelu_tanh_grad_f(u) from one exponential, in the
-// logistic form: with z = k0 (u + k1 u^3) and s = 1 / (1 + e^{-2z}),
+// GELU, tanh form (0.5 u (1 + tanh z), z = k0 (u + k1 u^3)), and its
+// derivative, from one exponential, in the logistic form: with z = k0 (u + k1 u^3) and s = 1 / (1 + e^{-2z}),
 // 1 + tanh z = 2 s and 1 - tanh^2 z = 4 s (1 - s), so
 //   GELU(u) = u s,   GELU'(u) = s (1 + 2 u (1 - s) dz/du),
 // dz/du = k0 (1 + 3 k1 u^2).  Eleven VALU operations besides v_exp_f32 and

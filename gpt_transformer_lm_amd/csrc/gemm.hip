@@ -51,7 +51,7 @@ constexpr int kThreads = 256;   // fp32 kernel, split-K reductions
 // reads and waits overlap the other's matrix instructions; the others run 4.
 // (Tiles whose epilogue reads an input tile keep 4 waves: 8 waves' epilogue
 // staging would not fit the LDS beside their stage ring.)
-constexpr bool epi_has_aux(int epi) { return epi == EPI_BIAS_RES || epi == EPI_GELU_BWD || epi == EPI_MUL; }
+constexpr bool epi_has_aux(int epi) { return epi == EPI_BIAS_RES || epi == EPI_MUL; }
 // With KGS = 2 (the planner's choice for a 192x192 tile whose K per tile is
 // long) the block runs 8 waves as two K-groups of 2 x 2: each group takes two
 // of the four k16 slices of every K step for the same 96 x 96 patches, and the
@@ -81,16 +81,10 @@ __device__ __forceinline__ void epilogue_store(const EpiArgs& e, int m, int n, f
   if constexpr (EPI == EPI_WGRAD) {
     e.partial[((size_t)z * e.M + m) * (size_t)e.N + n] = v;
   } else {
-    if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_RES || EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_GELU_D)
+    if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_RES || EPI == EPI_BIAS_GELU_D)
       v += to_f32(reinterpret_cast<const T*>(e.bias)[n]);
     if constexpr (EPI == EPI_BIAS_RES)
       v += to_f32(reinterpret_cast<const T*>(e.aux_in)[(size_t)m * e.ld_aux + n]);
-    if constexpr (EPI == EPI_BIAS_GELU) {
-      reinterpret_cast<T*>(e.aux_out)[(size_t)m * e.ldc + n] = from_f32<T>(v);
-      v = gelu_tanh_f(v);
-    }
-    if constexpr (EPI == EPI_GELU_BWD)
-      v *= gelu_tanh_grad_f(to_f32(reinterpret_cast<const T*>(e.aux_in)[(size_t)m * e.ld_aux + n]));
     if constexpr (EPI == EPI_BIAS_GELU_D) {
       float g, d;
       gelu_tanh_and_grad_f(v, g, d);
@@ -121,19 +115,14 @@ struct MfmaArgs {
 // Offset past every operand extent (the host requires extents below it).
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
 
-// Stores of the vectorised epilogue, after bias, residual and GELU' have been
-// applied from LDS: WGRAD partials, or U (BIAS_GELU) and C.
+// Stores of the vectorised epilogue, after bias, residual and the GELU'
+// multiply have been applied from LDS: WGRAD partials, or C (and GELU'(u)).
 template <int EPI>
 __device__ __forceinline__ void epilogue_vec8_final(const EpiArgs& e, int m, int n, float v[8], int z) {
   if constexpr (EPI == EPI_WGRAD) {
     float* dst = e.partial + ((size_t)z * e.M + m) * (size_t)e.N + n;
     Chunk8<float>::store(dst, v);
   } else {
-    if constexpr (EPI == EPI_BIAS_GELU) {
-      Chunk8<bf16>::store(reinterpret_cast<bf16*>(e.aux_out) + (size_t)m * e.ldc + n, v);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = gelu_tanh_f(v[i]);
-    }
     if constexpr (EPI == EPI_BIAS_GELU_D) {
       float d[8];
 #pragma unroll
@@ -325,8 +314,8 @@ __global__ __launch_bounds__(64 * gemm_waves(BM, BN, EPI, KGS))
 __attribute__((amdgpu_waves_per_eu(gemm_waves(BM, BN, EPI, KGS) / 4,
                                    (BM == 128 && BN == 128) ? 2 : gemm_waves(BM, BN, EPI, KGS) / 4)))
 void gemm_bf16_dma_kernel(MfmaArgs p) {
-  constexpr bool HAS_BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RES || EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_GELU_D;
-  constexpr bool HAS_AUX = EPI == EPI_BIAS_RES || EPI == EPI_GELU_BWD || EPI == EPI_MUL;
+  constexpr bool HAS_BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RES || EPI == EPI_BIAS_GELU_D;
+  constexpr bool HAS_AUX = epi_has_aux(EPI);
   using S = DmaShape<BM, BN, EPI, KGS>;
   using TA = DmaTile<BM, A_KMAJ, S::WAVES>;
   using TB = DmaTile<BN, B_KMAJ, S::WAVES>;
@@ -335,7 +324,6 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   constexpr int A_BYTES = TA::BYTES;
   constexpr int NDMA = TA::NINST + TB::NINST;              // DMA instructions per wave per stage
   constexpr bool IL = S::OCC == 1;  // refill spread over the MFMAs (one block per CU)
-  static_assert(!IL || NDMA <= 4 * FM * FN, "one DMA instruction per MFMA at most");
   __shared__ __attribute__((aligned(1024))) char st0[S::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char st1[S::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char st2[NS > 2 ? S::STAGE_BYTES : 16];
@@ -347,6 +335,9 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   const int wid = wave % (S::WGM * S::WGN), kg = wave / (S::WGM * S::WGN);
   const int wm = wid / S::WGN, wn = wid % S::WGN;
   constexpr int KK = kBK / 16 / S::KG;                    // k16 slices per K step of this wave
+  // the spread refill issues one DMA instruction after each of the step's
+  // KK * FM * FN matrix instructions, so it needs that many slots
+  static_assert(!IL || NDMA <= KK * FM * FN, "one DMA instruction per MFMA at most");
   static_assert(S::KG == 1 || !BIAS_GRAD, "K-groups take no fused bias gradient");
   int tm, tn;
   int z;
@@ -605,12 +596,9 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
                 if constexpr (EPI == EPI_BIAS_RES) {
 #pragma unroll
                   for (int e = 0; e < 8; ++e) v[e] += x[e];
-                } else if constexpr (EPI == EPI_MUL) {
-#pragma unroll
-                  for (int e = 0; e < 8; ++e) v[e] *= x[e];
                 } else {
 #pragma unroll
-                  for (int e = 0; e < 8; ++e) v[e] *= gelu_tanh_grad_f(x[e]);
+                  for (int e = 0; e < 8; ++e) v[e] *= x[e];
                 }
               }
               epilogue_vec8_final<EPI>(p.e, grow, gcol, v, z);
@@ -903,7 +891,7 @@ int dispatch_layout_bf16(const GemmDesc& d, const MfmaArgs& a, const Plan& pl, b
     // split-K partials of a plain-store dX = dY W (W n-major, or its k-major transpose)
     if (d.a_kmajor && !d.b_kmajor && !bias_grad) return launch_mfma<EPI, true, false, false>(a, pl, s);
     if (d.a_kmajor && d.b_kmajor && !bias_grad) return launch_mfma<EPI, true, true, false>(a, pl, s);
-  } else if constexpr (EPI == EPI_STORE || EPI == EPI_GELU_BWD || EPI == EPI_MUL) {
+  } else if constexpr (EPI == EPI_STORE || EPI == EPI_MUL) {
     if (d.a_kmajor && !d.b_kmajor) return launch_mfma<EPI, true, false, false>(a, pl, s);
     if (d.a_kmajor && d.b_kmajor) return launch_mfma<EPI, true, true, false>(a, pl, s);
   } else {
@@ -923,6 +911,27 @@ int dispatch_layout_f32(const GemmDesc& d, const SimtArgs& a, int splits, hipStr
 
 }  // namespace
 
+GemmLaunchInfo gemm_launch_info(const GemmDesc& d) {
+  GemmLaunchInfo r{};
+  const bool wgrad = d.epi == EPI_WGRAD;
+  r.bias_grad = wgrad && d.bias_grad32 != nullptr;
+  if (d.dtype != BF16) {   // fp32 SIMT kernel: 64 x 64 tiles, 4 waves, no split
+    r.tile_m = r.tile_n = 64;
+    r.waves = 4;
+    r.kgroups = r.splits = 1;
+    return r;
+  }
+  const Plan pl = plan_bf16(d.epi, d.M, d.N, d.K, d.a_kmajor, d.b_kmajor);
+  r.tile_m = pl.bm;
+  r.tile_n = pl.bn;
+  r.kgroups = pl.kgroups;
+  r.splits = pl.splits;
+  // a split plain store runs the partial-sum (WGRAD) instantiation
+  const int epi = (!wgrad && pl.splits > 1) ? (int)EPI_WGRAD : d.epi;
+  r.waves = gemm_waves(pl.bm, pl.bn, epi, pl.kgroups);
+  return r;
+}
+
 size_t gemm_workspace_bytes(int dtype, int epi, int M, int N, int K, bool a_kmajor, bool b_kmajor) {
   const int s = gemm_splits(dtype, epi, M, N, K, a_kmajor, b_kmajor);
   if (epi == EPI_WGRAD) return (size_t)s * ((size_t)M * N + (size_t)M) * sizeof(float) + 256;
@@ -937,11 +946,11 @@ int gemm(const GemmDesc& d, hipStream_t stream) {
   const bool wgrad = d.epi == EPI_WGRAD;
   if (wgrad && !d.out32) return gpt2_internal_fail(1, "gemm: WGRAD needs out32");
   if (!wgrad && !d.C) return gpt2_internal_fail(1, "gemm: missing C");
-  if ((d.epi == EPI_BIAS || d.epi == EPI_BIAS_RES || d.epi == EPI_BIAS_GELU || d.epi == EPI_BIAS_GELU_D) && !d.bias)
+  if ((d.epi == EPI_BIAS || d.epi == EPI_BIAS_RES || d.epi == EPI_BIAS_GELU_D) && !d.bias)
     return gpt2_internal_fail(1, "gemm: missing bias");
-  if ((d.epi == EPI_BIAS_RES || d.epi == EPI_GELU_BWD || d.epi == EPI_MUL) && !d.aux_in)
+  if ((d.epi == EPI_BIAS_RES || d.epi == EPI_MUL) && !d.aux_in)
     return gpt2_internal_fail(1, "gemm: missing aux input");
-  if ((d.epi == EPI_BIAS_GELU || d.epi == EPI_BIAS_GELU_D) && !d.aux_out)
+  if (d.epi == EPI_BIAS_GELU_D && !d.aux_out)
     return gpt2_internal_fail(1, "gemm: missing U output");
 
   const int splits = gemm_splits(d.dtype, d.epi, d.M, d.N, d.K, d.a_kmajor, d.b_kmajor);
@@ -995,8 +1004,6 @@ int gemm(const GemmDesc& d, hipStream_t stream) {
       case EPI_STORE: rc = dispatch_layout_bf16<EPI_STORE>(d, a, pl, false, stream); break;
       case EPI_BIAS: rc = dispatch_layout_bf16<EPI_BIAS>(d, a, pl, false, stream); break;
       case EPI_BIAS_RES: rc = dispatch_layout_bf16<EPI_BIAS_RES>(d, a, pl, false, stream); break;
-      case EPI_BIAS_GELU: rc = dispatch_layout_bf16<EPI_BIAS_GELU>(d, a, pl, false, stream); break;
-      case EPI_GELU_BWD: rc = dispatch_layout_bf16<EPI_GELU_BWD>(d, a, pl, false, stream); break;
       case EPI_BIAS_GELU_D: rc = dispatch_layout_bf16<EPI_BIAS_GELU_D>(d, a, pl, false, stream); break;
       case EPI_MUL: rc = dispatch_layout_bf16<EPI_MUL>(d, a, pl, false, stream); break;
       case EPI_WGRAD: rc = dispatch_layout_bf16<EPI_WGRAD>(d, a, pl, bias_grad, stream); break;
@@ -1025,8 +1032,6 @@ int gemm(const GemmDesc& d, hipStream_t stream) {
     case EPI_STORE: rc = dispatch_layout_f32<EPI_STORE>(d, a, 1, stream); break;
     case EPI_BIAS: rc = dispatch_layout_f32<EPI_BIAS>(d, a, 1, stream); break;
     case EPI_BIAS_RES: rc = dispatch_layout_f32<EPI_BIAS_RES>(d, a, 1, stream); break;
-    case EPI_BIAS_GELU: rc = dispatch_layout_f32<EPI_BIAS_GELU>(d, a, 1, stream); break;
-    case EPI_GELU_BWD: rc = dispatch_layout_f32<EPI_GELU_BWD>(d, a, 1, stream); break;
     case EPI_BIAS_GELU_D: rc = dispatch_layout_f32<EPI_BIAS_GELU_D>(d, a, 1, stream); break;
     case EPI_MUL: rc = dispatch_layout_f32<EPI_MUL>(d, a, 1, stream); break;
     case EPI_WGRAD: rc = dispatch_layout_f32<EPI_WGRAD>(d, a, splits, stream); break;

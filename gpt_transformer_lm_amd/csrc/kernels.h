@@ -31,22 +31,19 @@ inline void mark_end(int i, hipStream_t s) {
 //   A(m, k) = A[m * lda + k]  (a_kmajor)   or  A[k * lda + m]  (!a_kmajor)
 //   B(n, k) = B[n * ldb + k]  (b_kmajor)   or  B[k * ldb + n]  (!b_kmajor)
 // Epilogues (element (m, n), v = the fp32 sum):
-//   STORE      C = v
-//   BIAS       C = v + bias[n]
-//   BIAS_RES   C = v + bias[n] + R[m * ld_aux + n]
-//   BIAS_GELU  U[m * ldc + n] = v + bias[n];  C = gelu_tanh(v + bias[n])
-//   GELU_BWD   C = v * gelu_tanh'(U[m * ld_aux + n])
-//   WGRAD      fp32 result into out32[m * N + n] (overwrite, or add if
-//              accumulate), and if bias_grad32 != null also
-//              bias_grad32[m] = sum_k A(m, k) (A must be !a_kmajor).
-//              Split over K into partial sums that a second kernel reduces
-//              in a fixed order (deterministic).
+//   STORE        C = v
+//   BIAS         C = v + bias[n]
+//   BIAS_RES     C = v + bias[n] + R[m * ld_aux + n]
+//   WGRAD        fp32 result into out32[m * N + n] (overwrite, or add if
+//                accumulate), and if bias_grad32 != null also
+//                bias_grad32[m] = sum_k A(m, k) (A must be !a_kmajor).
+//                Split over K into partial sums that a second kernel reduces
+//                in a fixed order (deterministic).
 //   BIAS_GELU_D  C = gelu_tanh(v + bias[n]);  U[m * ldc + n] = gelu_tanh'(v + bias[n])
 //   MUL          C = v * U[m * ld_aux + n]
 //   (the step stores the GELU derivative in the forward, so the backward
 //   epilogue of the fc-proj dX is one multiply)
-enum Epi { EPI_STORE = 0, EPI_BIAS = 1, EPI_BIAS_RES = 2, EPI_BIAS_GELU = 3, EPI_GELU_BWD = 4,
-           EPI_WGRAD = 5, EPI_BIAS_GELU_D = 6, EPI_MUL = 7 };
+enum Epi { EPI_STORE = 0, EPI_BIAS = 1, EPI_BIAS_RES = 2, EPI_WGRAD = 5, EPI_BIAS_GELU_D = 6, EPI_MUL = 7 };
 
 struct GemmDesc {
   int dtype;            // F32 or BF16 (type of A, B, C, bias, R, U)
@@ -57,13 +54,22 @@ struct GemmDesc {
   int epi;
   void* C; int64_t ldc;
   const void* bias;
-  const void* aux_in; int64_t ld_aux;   // R (BIAS_RES) or U (GELU_BWD)
-  void* aux_out;                        // U (BIAS_GELU)
+  const void* aux_in; int64_t ld_aux;   // R (BIAS_RES) or U (MUL)
+  void* aux_out;                        // U (BIAS_GELU_D)
   float* out32;                         // WGRAD result [M, N]
   float* bias_grad32;                   // WGRAD bias gradient [M] (optional)
   bool accumulate;                      // WGRAD: add into out32 / bias_grad32
   void* workspace; size_t workspace_bytes;
 };
+
+// Kernel configuration gemm() launches for a descriptor (host-only): block
+// tile, waves per block, K-groups, K-splits and whether the bias gradient is
+// fused (the fp32 parity kernel reports 64 x 64, 4 waves, no split).
+struct GemmLaunchInfo {
+  int tile_m, tile_n, waves, kgroups, splits;
+  bool bias_grad;
+};
+GemmLaunchInfo gemm_launch_info(const GemmDesc& d);
 
 // Device bytes of scratch a GEMM with this descriptor needs (WGRAD only).
 size_t gemm_workspace_bytes(int dtype, int epi, int M, int N, int K, bool a_kmajor, bool b_kmajor);
@@ -128,11 +134,24 @@ int encoder_backward_sorted(int B, int T, int C, const uint32_t* sorted, const f
                             hipStream_t stream);
 
 // ------------------------------------------------------------------ optimizer
+// AdamW hyperparameters with the bias corrections c1 = 1 / (1 - b1^t) and
+// c2 = 1 / (1 - b2^t) (evaluated in double on the host).
+struct AdamHP {
+  float lr, b1, b2, eps, wd, c1, c2;
+};
+AdamHP adam_hparams(float lr, float beta1, float beta2, float eps, float wd, int t);
+// *dst = v on the device, in stream order (a one-thread kernel: the values
+// travel as kernel arguments, so no host buffer must outlive the call).
+int set_adam_hparams(AdamHP* dst, const AdamHP& v, hipStream_t stream);
 // AdamW over n fp32 parameters; writes the bf16 copy if param_bf16 != null.
 // With gscale (device, one float) every gradient enters multiplied by *gscale.
+// With hp_dev (device) the kernel reads its hyperparameters there instead of
+// taking (lr, beta1, beta2, eps, wd, t).
 int adamw(int64_t n, float* master, const float* grad, float* m, float* v, bf16* param_bf16,
           float lr, float beta1, float beta2, float eps, float wd, int t, hipStream_t stream,
-          const float* gscale = nullptr);
+          const float* gscale = nullptr, const AdamHP* hp_dev = nullptr);
+// dst[i] = src[i], i < n (device int32 arrays).
+int copy_i32(int64_t n, const int32_t* src, int32_t* dst, hipStream_t stream);
 // Global L2 norm of n fp32 gradients (16-byte aligned) into workspace[0] and
 // the clipping factor (max_norm / norm if norm > max_norm > 0, else 1) into
 // workspace[1]; workspace holds grad_norm_workspace_bytes() (device).

@@ -20,8 +20,10 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <exception>
 #include <new>
-#include <string>
+#include <stdexcept>
 #include <vector>
 
 #include "../../include/gpt2.h"
@@ -59,6 +61,63 @@ int gpt2_internal_hip_fail(hipError_t e, const char* expr, const char* file, int
     int _rc = (x);           \
     if (_rc) return _rc;     \
   } while (0)
+
+// No C++ exception crosses the C ABI: every extern "C" body runs inside
+// GPT2_ABI_BEGIN / GPT2_ABI_END_STATUS (status-returning calls: the
+// exception becomes GPT2_E_OOM for a failed host allocation, GPT2_E_INTERNAL
+// otherwise, with its text in gpt2_last_error()) or GPT2_ABI_END(value)
+// (other return types: the same text, and `value` is returned).
+#define GPT2_ABI_BEGIN try {
+#define GPT2_ABI_END_STATUS                                                                 \
+  }                                                                                        \
+  catch (const std::bad_alloc&) {                                                          \
+    return gpt2_internal_fail(GPT2_E_OOM, "host allocation failed");                       \
+  }                                                                                        \
+  catch (const std::length_error&) {                                                       \
+    return gpt2_internal_fail(GPT2_E_OOM, "host allocation failed (size out of range)");   \
+  }                                                                                        \
+  catch (const std::exception& ex) {                                                       \
+    return gpt2_internal_fail(GPT2_E_INTERNAL, "unexpected C++ exception: %s", ex.what()); \
+  }                                                                                        \
+  catch (...) {                                                                            \
+    return gpt2_internal_fail(GPT2_E_INTERNAL, "unexpected C++ exception");                \
+  }
+#define GPT2_ABI_END(fail_value)                                                           \
+  }                                                                                        \
+  catch (const std::bad_alloc&) {                                                          \
+    gpt2_internal_fail(GPT2_E_OOM, "host allocation failed");                              \
+    return fail_value;                                                                     \
+  }                                                                                        \
+  catch (const std::length_error&) {                                                       \
+    gpt2_internal_fail(GPT2_E_OOM, "host allocation failed (size out of range)");          \
+    return fail_value;                                                                     \
+  }                                                                                        \
+  catch (const std::exception& ex) {                                                       \
+    gpt2_internal_fail(GPT2_E_INTERNAL, "unexpected C++ exception: %s", ex.what());        \
+    return fail_value;                                                                     \
+  }                                                                                        \
+  catch (...) {                                                                            \
+    gpt2_internal_fail(GPT2_E_INTERNAL, "unexpected C++ exception");                       \
+    return fail_value;                                                                     \
+  }
+
+namespace {
+
+// Host allocations of the library's own bookkeeping (arena plan, timing
+// events) go through grow(), which fails the next g_fail_allocs of them on
+// request (gpt2_test_fail_host_allocations) so the error paths can be tested.
+std::atomic<int> g_fail_allocs{0};
+
+template <typename V>
+void grow(V& v, size_t n) {
+  int k = g_fail_allocs.load();
+  while (k > 0 && !g_fail_allocs.compare_exchange_weak(k, k - 1)) {
+  }
+  if (k > 0) throw std::bad_alloc();
+  v.resize(n);
+}
+
+}  // namespace
 
 // ---------------------------------------------------------------- config
 
@@ -122,6 +181,11 @@ int validate(const gpt2_config* c) {
   if (BT % 64 || BT > 32768)
     return gpt2_internal_fail(GPT2_E_INVALID_ARG, "batch_size*seq_len = %lld must be a multiple of 64 and <= 32768",
                               (long long)BT);
+  if (c->arch_flags & ~(GPT2_ARCH_RELU2 | GPT2_ARCH_QK_NORM | GPT2_ARCH_ROPE))
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "arch_flags 0x%x has unknown bits", (unsigned)c->arch_flags);
+  if (c->arch_flags)
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "arch_flags 0x%x: architecture variants not available",
+                              (unsigned)c->arch_flags);
   return GPT2_OK;
 }
 
@@ -151,6 +215,7 @@ struct Layout {
   std::vector<LayerOffsets> layer;
   size_t tokens, lnf, lnf_mean, lnf_rstd, logits, losses, mean_loss;
   size_t gnorm;                          // gradient norm, clipping factor, per-block partial sums
+  size_t adam_hp;                        // AdamW hyperparameters read by the update kernel
   size_t dres, dres_t, d_ln, d_big, d_qkv, scratch;
   size_t sorted_keys;                    // encoder-backward key sort (computed during the forward)
   size_t scratch_bytes;
@@ -198,9 +263,9 @@ void make_layout(const gpt2_config& c, Layout* lo) {
       lo->params_t[i] = p.alloc((size_t)sh[0] * sh[1] * sh[2] * 2);
     }
   lo->tokens = p.alloc(BT * 4);
-  lo->resid.resize(L + 1);
+  grow(lo->resid, L + 1);
   for (size_t l = 0; l <= L; ++l) lo->resid[l] = p.alloc(BT * C * es);
-  lo->layer.resize(L);
+  grow(lo->layer, L);
   for (size_t l = 0; l < L; ++l) {
     LayerOffsets& o = lo->layer[l];
     o.ln1 = p.alloc(BT * C * es);
@@ -223,6 +288,7 @@ void make_layout(const gpt2_config& c, Layout* lo) {
   lo->losses = p.alloc(BT * 4);
   lo->mean_loss = p.alloc(4);
   lo->gnorm = p.alloc(grad_norm_workspace_bytes());
+  lo->adam_hp = p.alloc(sizeof(AdamHP));
   lo->dres = p.alloc(BT * C * 4);
   lo->dres_t = c.dtype == GPT2_BF16 ? p.alloc(BT * C * es) : lo->dres;
   lo->d_ln = p.alloc(BT * C * es);
@@ -269,6 +335,14 @@ struct gpt2_model {
   bool have_grads = false;
   int device = 0;
   SiteTimer timers[S_COUNT];
+  // Planning mode (gpt2_step_gemm_plans): no device memory and nothing is
+  // enqueued; the forward and backward sequences only record each GEMM they
+  // would launch, with its timing site.
+  std::vector<std::pair<int, GemmDesc>>* plan_log = nullptr;
+  bool dry() const { return plan_log != nullptr; }
+  // A captured training step (gpt2_graph_capture) and its executable form.
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t graph_exec = nullptr;
 
   template <typename P> P* at(size_t off) { return reinterpret_cast<P*>(base + off); }
   float* master() { return at<float>(lo.master); }
@@ -326,6 +400,7 @@ void marks_clear() {
 // flops / bytes are the algorithmic work of one such kernel.
 template <typename F>
 int timed(gpt2_model* m, int site, double flops, double bytes, F&& launch) {
+  if (m->dry()) return 0;
   const bool armed = timer_arm(m, site, 0);
   const int rc = launch();
   marks_clear();
@@ -335,6 +410,10 @@ int timed(gpt2_model* m, int site, double flops, double bytes, F&& launch) {
 
 // GEMM wrapper that records the timing site.
 int run_gemm(gpt2_model* m, int site, const GemmDesc& d) {
+  if (m->dry()) {
+    m->plan_log->push_back({site, d});
+    return 0;
+  }
   const double es = (double)m->es();
   const double bytes = ((double)d.M * d.K + (double)d.N * d.K) * es +
                        (d.epi == EPI_WGRAD ? (double)d.M * d.N * 4.0 : (double)d.M * d.N * es);
@@ -348,42 +427,60 @@ GemmDesc gdesc(int dtype) {
   return d;
 }
 
-// y[M,N] = x[M,K] W[N,K]^T (+ epilogue)
-GemmDesc fwd_desc(gpt2_model* m, int M, int N, int K, const void* x, const void* W, int epi, void* C,
-                  const void* bias, const void* aux_in, void* aux_out) {
-  GemmDesc d = gdesc(m->dt());
+// The three GEMM forms of a linear layer y = x W^T + b (W stored [N, K]),
+// shared by the training step and the op-level ABI so that both launch the
+// same kernels.
+// Forward y[M,N] = x[M,K] W[N,K]^T (+ epilogue): both operands k-major.
+GemmDesc linear_fwd_desc(int dtype, int M, int N, int K, const void* x, const void* W, int epi, void* y,
+                         const void* bias, const void* aux_in, void* aux_out) {
+  GemmDesc d = gdesc(dtype);
   d.a_kmajor = true; d.b_kmajor = true;
   d.M = M; d.N = N; d.K = K;
   d.A = x; d.lda = K; d.B = W; d.ldb = K;
-  d.epi = epi; d.C = C; d.ldc = N; d.bias = bias; d.aux_in = aux_in; d.ld_aux = N; d.aux_out = aux_out;
+  d.epi = epi; d.C = y; d.ldc = N; d.bias = bias; d.aux_in = aux_in; d.ld_aux = N; d.aux_out = aux_out;
   return d;
 }
 
-// dx[M,K] = dy[M,N] W[N,K]
-// dx[M,K] = dy[M,N] W[N,K] (+ GELU' epilogue).  W is read through its
-// transposed copy WT [K, N] (k-major) when there is one, else n-major.
-GemmDesc dx_desc(gpt2_model* m, int M, int N, int K, const void* dy, const void* W, const void* WT, void* dx,
-                 int epi, const void* gelu_u) {
-  GemmDesc d = gdesc(m->dt());
+// dx[M,K] = dy[M,N] W[N,K] (+ a multiply by U[M,K], the saved GELU'(u)).  W
+// is read through its transposed copy WT [K, N] (k-major) when there is one
+// (bf16), else n-major.
+GemmDesc linear_dx_desc(int dtype, int M, int N, int K, const void* dy, const void* W, const void* WT, void* dx,
+                        int epi, const void* gelu_grad, void* ws, size_t ws_bytes) {
+  GemmDesc d = gdesc(dtype);
   d.a_kmajor = true; d.b_kmajor = WT != nullptr;
   d.M = M; d.N = K; d.K = N;
   d.A = dy; d.lda = N;
   if (WT) { d.B = WT; d.ldb = N; } else { d.B = W; d.ldb = K; }
-  d.epi = epi; d.C = dx; d.ldc = K; d.aux_in = gelu_u; d.ld_aux = K;
-  d.workspace = m->scratch(); d.workspace_bytes = m->lo.scratch_bytes;
+  d.epi = epi; d.C = dx; d.ldc = K; d.aux_in = gelu_grad; d.ld_aux = K;
+  d.workspace = ws; d.workspace_bytes = ws_bytes;
   return d;
 }
 
-// dW[N,K] (+)= dy[M,N]^T x[M,K];  db[N] = sum_rows dy
-GemmDesc dw_desc(gpt2_model* m, int M, int N, int K, const void* dy, const void* x, float* dW, float* db,
-                 bool acc) {
-  GemmDesc d = gdesc(m->dt());
+// dW[N,K] (+)= dy[M,N]^T x[M,K];  db[N] (+)= sum_rows dy (fused; NULL: none).
+GemmDesc linear_dw_desc(int dtype, int M, int N, int K, const void* dy, const void* x, float* dW, float* db, bool acc,
+                        void* ws, size_t ws_bytes) {
+  GemmDesc d = gdesc(dtype);
   d.a_kmajor = false; d.b_kmajor = false;
   d.M = N; d.N = K; d.K = M;
   d.A = dy; d.lda = N; d.B = x; d.ldb = K;
   d.epi = EPI_WGRAD; d.out32 = dW; d.bias_grad32 = db; d.accumulate = acc;
-  d.workspace = m->scratch(); d.workspace_bytes = m->lo.scratch_bytes;
+  d.workspace = ws; d.workspace_bytes = ws_bytes;
   return d;
+}
+
+GemmDesc fwd_desc(gpt2_model* m, int M, int N, int K, const void* x, const void* W, int epi, void* C,
+                  const void* bias, const void* aux_in, void* aux_out) {
+  return linear_fwd_desc(m->dt(), M, N, K, x, W, epi, C, bias, aux_in, aux_out);
+}
+
+GemmDesc dx_desc(gpt2_model* m, int M, int N, int K, const void* dy, const void* W, const void* WT, void* dx,
+                 int epi, const void* gelu_grad) {
+  return linear_dx_desc(m->dt(), M, N, K, dy, W, WT, dx, epi, gelu_grad, m->scratch(), m->lo.scratch_bytes);
+}
+
+GemmDesc dw_desc(gpt2_model* m, int M, int N, int K, const void* dy, const void* x, float* dW, float* db,
+                 bool acc) {
+  return linear_dw_desc(m->dt(), M, N, K, dy, x, dW, db, acc, m->scratch(), m->lo.scratch_bytes);
 }
 
 // loss_scale: the dlogits (and so every gradient of the next backward) are
@@ -402,8 +499,8 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets, f
     GPT2_HIP_CHECK(hipStreamWaitEvent(s, m->ev_join, 0));
     m->side_pending = false;
   }
-  GPT2_HIP_CHECK(hipMemcpyAsync(tok, tokens, (size_t)BT * sizeof(int32_t), hipMemcpyDeviceToDevice, s));
-  if (targets) {
+  if (!m->dry()) RC(copy_i32(BT, tokens, tok, s));
+  if (targets && !m->dry()) {
     // the key sort of the encoder backward runs beside the forward
     GPT2_HIP_CHECK(hipEventRecord(m->ev_fork, s));
     GPT2_HIP_CHECK(hipStreamWaitEvent(m->side, m->ev_fork, 0));
@@ -454,7 +551,7 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets, f
       return softmax_xent(dt, BT, V, Vp, m->at<char>(lo.logits), targets, m->at<float>(lo.losses), loss_scale / BT,
                           s);
     }));
-    RC(sum_scaled(BT, m->at<float>(lo.losses), 1.0f / BT, m->at<float>(lo.mean_loss), s));
+    if (!m->dry()) RC(sum_scaled(BT, m->at<float>(lo.losses), 1.0f / BT, m->at<float>(lo.mean_loss), s));
     m->have_dlogits = true;
   }
   return 0;
@@ -465,7 +562,7 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets, f
 int backward_impl(gpt2_model* m, bool acc) {
   const gpt2_config& c = m->cfg;
   const int B = c.batch_size, T = c.seq_len, C = c.channels, H = c.num_heads, hd = C / H;
-  const int BT = B * T, Vp = c.padded_vocab_size, V = c.vocab_size, L = c.num_layers;
+  const int BT = B * T, Vp = c.padded_vocab_size, L = c.num_layers;
   const int dt = m->dt();
   hipStream_t s = m->stream;
   Layout& lo = m->lo;
@@ -514,7 +611,7 @@ int backward_impl(gpt2_model* m, bool acc) {
     RC(run_gemm(m, S_ATTPROJ_DW, dw_desc(m, BT, C, C, dres_t, m->at<char>(o.atty), m->lgrad(6, l),
                                          m->lgrad(7, l), acc)));
     RC(run_gemm(m, S_ATTPROJ_DX, dx_desc(m, BT, C, C, dres_t, m->lparam(6, l), m->wt(6, l), d_ln, EPI_STORE, nullptr)));
-    {
+    if (!m->dry()) {
       // dK, dV (recomputing S and dP) and dQ; D = rowsum(dO * O) is a kernel of
       // its own except on the matrix-core path, where the dQ kernel forms it
       const bool mfma = attention_mfma_supported(dt, hd);
@@ -525,8 +622,12 @@ int backward_impl(gpt2_model* m, bool acc) {
       marks_clear();
       RC(rc);
       const double lse_b = (double)B * H * T * 4;
+      // algorithmic work: the method's backward is four causal products (dV,
+      // dP, dQ, dK); the dK/dV kernel is credited with dV, dP and dK, the dQ
+      // kernel with dQ (the recomputed S, and dP again in the dQ kernel, are
+      // not counted)
       if (a0) timer_commit(m, S_ATTN_DOT, 0.0, 2.0 * act + lse_b);
-      if (a1) timer_commit(m, S_ATTN_DKDV, 4.0 * causal_mm, 4.0 * act + 2.0 * lse_b + 2.0 * act);
+      if (a1) timer_commit(m, S_ATTN_DKDV, 3.0 * causal_mm, 4.0 * act + 2.0 * lse_b + 2.0 * act);
       if (a2) timer_commit(m, S_ATTN_DQ, 1.0 * causal_mm, 4.0 * act + 2.0 * lse_b + act + (mfma ? act + lse_b : 0.0));
     }
     // qkv = ln1 Wqkv^T + bqkv
@@ -541,6 +642,7 @@ int backward_impl(gpt2_model* m, bool acc) {
   }
   // encoder: wpe rows >= T get no gradient (zero already when accumulating)
   float* dwpe = m->lgrad(1, 0);
+  if (m->dry()) return 0;
   if (!acc) RC(fill_f32((int64_t)(c.max_seq_len - T) * C, dwpe + (size_t)T * C, 0.f, s));
   if (m->side_pending) {
     GPT2_HIP_CHECK(hipStreamWaitEvent(s, m->ev_join, 0));
@@ -548,7 +650,6 @@ int backward_impl(gpt2_model* m, bool acc) {
   }
   RC(encoder_backward_sorted(B, T, C, m->at<uint32_t>(lo.sorted_keys), dres, m->lgrad(0, 0), dwpe, acc, m->scratch(),
                              sb, s));
-  (void)Vp;
   return 0;
 }
 
@@ -559,12 +660,11 @@ int init_params(gpt2_model* m, uint64_t seed) {
   for (int i = 0; i < 16; ++i) {
     const int64_t n = m->lo.pt.shape[i][0] * m->lo.pt.shape[i][1] * m->lo.pt.shape[i][2];
     float* dst = m->master() + m->lo.pt.off[i];
-    const std::string name = kParamNames[i];
-    if (name == "ln1w" || name == "ln2w" || name == "lnfw") {
+    auto is = [&](const char* x) { return strcmp(kParamNames[i], x) == 0; };
+    if (is("ln1w") || is("ln2w") || is("lnfw")) {
       RC(fill_f32(n, dst, 1.0f, s));
-    } else if (name == "wte" || name == "wpe" || name == "qkvw" || name == "fcw" || name == "attprojw" ||
-               name == "fcprojw") {
-      const double sd = (name == "attprojw" || name == "fcprojw") ? resid_std : 0.02;
+    } else if (is("wte") || is("wpe") || is("qkvw") || is("fcw") || is("attprojw") || is("fcprojw")) {
+      const double sd = (is("attprojw") || is("fcprojw")) ? resid_std : 0.02;
       RC(init_normal(n, dst, seed, i, sd, s));
       if (i == 0)
         RC(fill_f32((int64_t)(c.padded_vocab_size - c.vocab_size) * c.channels,
@@ -598,9 +698,76 @@ int refresh_bf16(gpt2_model* m) {
   return refresh_transposed(m);
 }
 
+// The parameter update: optional gradient norm and clipping factor, AdamW
+// with its hyperparameters read from the arena's block (written beforehand in
+// stream order), the transposed bf16 weight copies.
+int update_impl(gpt2_model* m, float max_grad_norm, bool need_norm) {
+  float* gn = m->at<float>(m->lo.gnorm);
+  if (need_norm) {
+    // fp32 gradients read once
+    RC(timed(m, S_GRAD_NORM, 0.0, 4.0 * (double)m->lo.P,
+             [&] { return grad_norm(m->lo.P, m->grad(), max_grad_norm, gn, m->stream); }));
+  }
+  // fp32 master, m, v read and written, fp32 gradient read, bf16 copy written
+  RC(timed(m, S_ADAMW, 0.0, (double)m->lo.P * (m->cfg.dtype == GPT2_BF16 ? 30.0 : 28.0), [&] {
+    return adamw(m->lo.P, m->master(), m->grad(), m->at<float>(m->lo.adam_m), m->at<float>(m->lo.adam_v),
+                 m->cfg.dtype == GPT2_BF16 ? m->at<bf16>(m->lo.params_bf16) : nullptr, 0.f, 0.f, 0.f, 0.f, 0.f, 1,
+                 m->stream, max_grad_norm > 0.f ? gn + 1 : nullptr, m->at<AdamHP>(m->lo.adam_hp));
+  }));
+  return refresh_transposed(m);
+}
+
+void graph_release(gpt2_model* m) {
+  if (m->graph_exec) (void)hipGraphExecDestroy(m->graph_exec);
+  if (m->graph) (void)hipGraphDestroy(m->graph);
+  m->graph_exec = nullptr;
+  m->graph = nullptr;
+}
+
 }  // namespace
 
 // ================================================================ C ABI
+
+static_assert(GPT2_EPI_STORE == EPI_STORE && GPT2_EPI_BIAS == EPI_BIAS && GPT2_EPI_BIAS_RESIDUAL == EPI_BIAS_RES &&
+                  GPT2_EPI_WGRAD == EPI_WGRAD && GPT2_EPI_BIAS_GELU == EPI_BIAS_GELU_D && GPT2_EPI_MUL == EPI_MUL,
+              "epilogue codes of gpt2_ops.h");
+
+namespace {
+
+const char* site_name(int site) {
+  static const char* const names[S_COUNT] = {
+      "qkv", "attproj", "fc", "fcproj", "logits", "fcproj_dx", "fcproj_dw", "fc_dx", "fc_dw", "attproj_dx",
+      "attproj_dw", "qkv_dx", "qkv_dw", "cls_dx", "cls_dw", "attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq",
+      "attn_bwd_dot", "softmax_xent", "ln_fwd", "ln_bwd", "encoder_fwd", "adamw", "weight_transpose", "grad_norm"};
+  return site >= 0 && site < S_COUNT ? names[site] : "";
+}
+
+void fill_plan(const GemmDesc& d, const char* site, gpt2_gemm_plan* out) {
+  memset(out, 0, sizeof(*out));
+  snprintf(out->site, sizeof(out->site), "%s", site);
+  const GemmLaunchInfo li = gemm_launch_info(d);
+  out->M = d.M; out->N = d.N; out->K = d.K;
+  out->epilogue = d.epi;
+  out->a_kmajor = d.a_kmajor; out->b_kmajor = d.b_kmajor;
+  out->tile_m = li.tile_m; out->tile_n = li.tile_n;
+  out->waves = li.waves; out->k_groups = li.kgroups; out->k_splits = li.splits;
+  out->bias_grad = li.bias_grad;
+}
+
+bool any_timer_on(const gpt2_model* m) {
+  for (const auto& t : m->timers)
+    if (t.on) return true;
+  return false;
+}
+
+// The op-level linear layer's GEMMs (forward; dW; dX) for these arguments.
+// bf16 dX reads W through a transposed copy WT [K, N] that the op writes at
+// the start of its workspace (the step keeps the same copy of each weight).
+size_t op_wt_bytes(int dtype, int N, int K) {
+  return dtype == GPT2_BF16 ? ((size_t)N * K * 2 + 255) / 256 * 256 : 0;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -609,13 +776,19 @@ const char* gpt2_status_string(int st) {
     case GPT2_OK: return "ok";
     case GPT2_E_INVALID_ARG: return "invalid argument";
     case GPT2_E_STATE: return "invalid call order";
-    case GPT2_E_OOM: return "out of device memory / workspace too small";
+    case GPT2_E_OOM: return "out of memory / workspace too small";
     case GPT2_E_HIP: return "HIP runtime error";
+    case GPT2_E_INTERNAL: return "internal error";
   }
   return "unknown status";
 }
 
 const char* gpt2_last_error(void) { return g_last_error; }
+
+int gpt2_test_fail_host_allocations(int n) {
+  g_fail_allocs.store(n > 0 ? n : 0);
+  return GPT2_OK;
+}
 
 int gpt2_validate_config(const gpt2_config* cfg) {
   g_last_error[0] = 0;
@@ -646,22 +819,53 @@ int gpt2_param_info(const gpt2_config* cfg, int i, const char** name, int64_t* o
 }
 
 size_t gpt2_workspace_bytes(const gpt2_config* cfg) {
+  GPT2_ABI_BEGIN
   if (validate(cfg)) return 0;
   Layout lo;
   make_layout(*cfg, &lo);
   return lo.total;
+  GPT2_ABI_END(0)
+}
+
+int gpt2_step_gemm_plans(const gpt2_config* cfg, gpt2_gemm_plan* out, int max_plans, int* count) {
+  GPT2_ABI_BEGIN
+  RC(validate(cfg));
+  if (!count || max_plans < 0 || (max_plans > 0 && !out))
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "step_gemm_plans: bad output arguments");
+  gpt2_model m;
+  m.cfg = *cfg;
+  make_layout(*cfg, &m.lo);
+  m.base = nullptr;
+  m.stream = nullptr;
+  std::vector<std::pair<int, GemmDesc>> log;
+  m.plan_log = &log;
+  // a forward with targets and a full backward, planning only
+  static const int32_t kNoIds = 0;
+  RC(forward_impl(&m, &kNoIds, &kNoIds, 1.0f));
+  RC(backward_impl(&m, false));
+  const int n = (int)log.size();
+  for (int i = 0; i < n && i < max_plans; ++i) fill_plan(log[i].second, site_name(log[i].first), &out[i]);
+  *count = n;
+  return GPT2_OK;
+  GPT2_ABI_END_STATUS
 }
 
 int gpt2_create(const gpt2_config* cfg, uint64_t seed, void* stream, void* workspace, size_t workspace_bytes,
                 gpt2_model** out) {
+  GPT2_ABI_BEGIN
   g_last_error[0] = 0;
   if (!out) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "out is NULL");
   *out = nullptr;
   RC(validate(cfg));
   gpt2_model* m = new (std::nothrow) gpt2_model();
   if (!m) return gpt2_internal_fail(GPT2_E_OOM, "host allocation failed");
-  m->cfg = *cfg;
-  make_layout(*cfg, &m->lo);
+  try {
+    m->cfg = *cfg;
+    make_layout(*cfg, &m->lo);
+  } catch (...) {
+    delete m;
+    throw;
+  }
   m->stream = (hipStream_t)stream;
   if (hipGetDevice(&m->device) != hipSuccess) {
     delete m;
@@ -708,21 +912,28 @@ int gpt2_create(const gpt2_config* cfg, uint64_t seed, void* stream, void* works
   }
   *out = m;
   return GPT2_OK;
+  GPT2_ABI_END_STATUS
 }
 
 void gpt2_destroy(gpt2_model* m) {
   if (!m) return;
-  (void)hipStreamSynchronize(m->stream);
-  if (m->side) {
-    (void)hipStreamSynchronize(m->side);
-    (void)hipStreamDestroy(m->side);
+  try {
+    (void)hipStreamSynchronize(m->stream);
+    graph_release(m);
+    if (m->side) {
+      (void)hipStreamSynchronize(m->side);
+      (void)hipStreamDestroy(m->side);
+    }
+    if (m->ev_fork) (void)hipEventDestroy(m->ev_fork);
+    if (m->ev_join) (void)hipEventDestroy(m->ev_join);
+    for (auto& t : m->timers)
+      for (auto e : t.ev)
+        if (e) (void)hipEventDestroy(e);
+    if (m->owns) (void)hipFree(m->base);
+    delete m;
+  } catch (...) {
+    // nothing may escape; the model is leaked rather than half destroyed
   }
-  if (m->ev_fork) (void)hipEventDestroy(m->ev_fork);
-  if (m->ev_join) (void)hipEventDestroy(m->ev_join);
-  for (auto& t : m->timers)
-    for (auto e : t.ev) (void)hipEventDestroy(e);
-  if (m->owns) (void)hipFree(m->base);
-  delete m;
 }
 
 int gpt2_forward(gpt2_model* m, const int32_t* d_tokens, const int32_t* d_targets, float* mean_loss) {
@@ -731,6 +942,7 @@ int gpt2_forward(gpt2_model* m, const int32_t* d_tokens, const int32_t* d_target
 
 int gpt2_forward_scaled(gpt2_model* m, const int32_t* d_tokens, const int32_t* d_targets, float loss_scale,
                         float* mean_loss) {
+  GPT2_ABI_BEGIN
   if (!m || !d_tokens) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "forward: NULL model or tokens");
   if (!isfinite(loss_scale))
     return gpt2_internal_fail(GPT2_E_INVALID_ARG, "forward: loss_scale must be finite");
@@ -741,18 +953,22 @@ int gpt2_forward_scaled(gpt2_model* m, const int32_t* d_tokens, const int32_t* d
     GPT2_HIP_CHECK(hipStreamSynchronize(m->stream));
   }
   return GPT2_OK;
+  GPT2_ABI_END_STATUS
 }
 
 int gpt2_backward(gpt2_model* m) {
+  GPT2_ABI_BEGIN
   if (!m) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "backward: NULL model");
   if (!m->have_dlogits) return gpt2_internal_fail(GPT2_E_STATE, "backward needs a forward with targets first");
   RC(backward_impl(m, false));
   m->have_dlogits = false;
   m->have_grads = true;
   return GPT2_OK;
+  GPT2_ABI_END_STATUS
 }
 
 int gpt2_backward_accumulate(gpt2_model* m) {
+  GPT2_ABI_BEGIN
   if (!m) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "backward: NULL model");
   if (!m->have_dlogits) return gpt2_internal_fail(GPT2_E_STATE, "backward needs a forward with targets first");
   if (!m->have_grads)
@@ -760,6 +976,7 @@ int gpt2_backward_accumulate(gpt2_model* m) {
   RC(backward_impl(m, true));
   m->have_dlogits = false;
   return GPT2_OK;
+  GPT2_ABI_END_STATUS
 }
 
 int gpt2_adamw_step(gpt2_model* m, float lr, float beta1, float beta2, float eps, float weight_decay, int32_t t) {
@@ -768,30 +985,78 @@ int gpt2_adamw_step(gpt2_model* m, float lr, float beta1, float beta2, float eps
 
 int gpt2_adamw_step_clipped(gpt2_model* m, float lr, float beta1, float beta2, float eps, float weight_decay,
                             int32_t t, float max_grad_norm, float* grad_norm_out) {
+  GPT2_ABI_BEGIN
   if (!m) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "adamw: NULL model");
   if (t < 1) return gpt2_internal_fail(GPT2_E_STATE, "adamw: t must be >= 1");
   if (!m->have_grads) return gpt2_internal_fail(GPT2_E_STATE, "adamw needs a completed backward first");
+  RC(set_adam_hparams(m->at<AdamHP>(m->lo.adam_hp), adam_hparams(lr, beta1, beta2, eps, weight_decay, t), m->stream));
   // the norm (and the clipping factor, read by the update on the device) only when asked for
-  float* gn = m->at<float>(m->lo.gnorm);
-  const bool need_norm = max_grad_norm > 0.f || grad_norm_out != nullptr;
-  if (need_norm) {
-    // fp32 gradients read once
-    RC(timed(m, S_GRAD_NORM, 0.0, 4.0 * (double)m->lo.P,
-             [&] { return grad_norm(m->lo.P, m->grad(), max_grad_norm, gn, m->stream); }));
-  }
-  // fp32 master, m, v read and written, fp32 gradient read, bf16 copy written
-  RC(timed(m, S_ADAMW, 0.0, (double)m->lo.P * (m->cfg.dtype == GPT2_BF16 ? 30.0 : 28.0), [&] {
-    return adamw(m->lo.P, m->master(), m->grad(), m->at<float>(m->lo.adam_m), m->at<float>(m->lo.adam_v),
-                 m->cfg.dtype == GPT2_BF16 ? m->at<bf16>(m->lo.params_bf16) : nullptr, lr, beta1, beta2, eps,
-                 weight_decay, t, m->stream, max_grad_norm > 0.f ? gn + 1 : nullptr);
-  }));
-  RC(refresh_transposed(m));
+  RC(update_impl(m, max_grad_norm, max_grad_norm > 0.f || grad_norm_out != nullptr));
   m->have_grads = false;
   if (grad_norm_out) {
-    GPT2_HIP_CHECK(hipMemcpyAsync(grad_norm_out, gn, sizeof(float), hipMemcpyDeviceToHost, m->stream));
+    GPT2_HIP_CHECK(hipMemcpyAsync(grad_norm_out, m->at<float>(m->lo.gnorm), sizeof(float), hipMemcpyDeviceToHost,
+                                  m->stream));
     GPT2_HIP_CHECK(hipStreamSynchronize(m->stream));
   }
   return GPT2_OK;
+  GPT2_ABI_END_STATUS
+}
+
+int gpt2_graph_capture(gpt2_model* m, const int32_t* d_tokens, const int32_t* d_targets) {
+  GPT2_ABI_BEGIN
+  if (!m || !d_tokens || !d_targets)
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "graph_capture: NULL model, tokens or targets");
+  if (!m->stream)
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "graph_capture: the model's stream is the null stream");
+  if (any_timer_on(m)) return gpt2_internal_fail(GPT2_E_STATE, "graph_capture: disable timing sites first");
+  graph_release(m);
+  if (m->side_pending) {   // the last eager forward's key sort joins before the capture starts
+    GPT2_HIP_CHECK(hipStreamWaitEvent(m->stream, m->ev_join, 0));
+    m->side_pending = false;
+  }
+  GPT2_HIP_CHECK(hipStreamBeginCapture(m->stream, hipStreamCaptureModeThreadLocal));
+  int rc = forward_impl(m, d_tokens, d_targets, 1.0f);
+  if (!rc) rc = backward_impl(m, false);
+  if (!rc) rc = update_impl(m, 0.0f, false);
+  hipGraph_t g = nullptr;
+  const hipError_t e = hipStreamEndCapture(m->stream, &g);
+  m->side_pending = false;
+  m->have_dlogits = m->have_grads = false;
+  if (rc || e != hipSuccess) {
+    if (g) (void)hipGraphDestroy(g);
+    if (rc) return rc;
+    return gpt2_internal_hip_fail(e, "hipStreamEndCapture", __FILE__, __LINE__);
+  }
+  m->graph = g;
+  const hipError_t ei = hipGraphInstantiate(&m->graph_exec, g, nullptr, nullptr, 0);
+  if (ei != hipSuccess) {
+    graph_release(m);
+    return gpt2_internal_hip_fail(ei, "hipGraphInstantiate", __FILE__, __LINE__);
+  }
+  return GPT2_OK;
+  GPT2_ABI_END_STATUS
+}
+
+int gpt2_graph_step(gpt2_model* m, float lr, float beta1, float beta2, float eps, float weight_decay, int32_t t,
+                    float* mean_loss) {
+  GPT2_ABI_BEGIN
+  if (!m) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "graph_step: NULL model");
+  if (!m->graph_exec) return gpt2_internal_fail(GPT2_E_STATE, "graph_step: no captured step (gpt2_graph_capture)");
+  if (t < 1) return gpt2_internal_fail(GPT2_E_STATE, "graph_step: t must be >= 1");
+  if (m->side_pending) {
+    GPT2_HIP_CHECK(hipStreamWaitEvent(m->stream, m->ev_join, 0));
+    m->side_pending = false;
+  }
+  RC(set_adam_hparams(m->at<AdamHP>(m->lo.adam_hp), adam_hparams(lr, beta1, beta2, eps, weight_decay, t), m->stream));
+  GPT2_HIP_CHECK(hipGraphLaunch(m->graph_exec, m->stream));
+  m->have_dlogits = m->have_grads = false;
+  if (mean_loss) {
+    GPT2_HIP_CHECK(hipMemcpyAsync(mean_loss, m->at<float>(m->lo.mean_loss), sizeof(float), hipMemcpyDeviceToHost,
+                                  m->stream));
+    GPT2_HIP_CHECK(hipStreamSynchronize(m->stream));
+  }
+  return GPT2_OK;
+  GPT2_ABI_END_STATUS
 }
 
 static int copy_out(gpt2_model* m, const void* src, void* dst, size_t bytes) {
@@ -801,16 +1066,21 @@ static int copy_out(gpt2_model* m, const void* src, void* dst, size_t bytes) {
 }
 
 int gpt2_get_mean_loss(gpt2_model* m, float* host_out) {
+  GPT2_ABI_BEGIN
   if (!m || !host_out) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "get_mean_loss: NULL");
   return copy_out(m, m->at<float>(m->lo.mean_loss), host_out, sizeof(float));
+  GPT2_ABI_END_STATUS
 }
 
 int gpt2_get_params(gpt2_model* m, float* host_out) {
+  GPT2_ABI_BEGIN
   if (!m || !host_out) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "get_params: NULL");
   return copy_out(m, m->master(), host_out, m->lo.P * sizeof(float));
+  GPT2_ABI_END_STATUS
 }
 
 int gpt2_set_params(gpt2_model* m, const float* host_in) {
+  GPT2_ABI_BEGIN
   if (!m || !host_in) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "set_params: NULL");
   GPT2_HIP_CHECK(hipMemcpyAsync(m->master(), host_in, m->lo.P * sizeof(float), hipMemcpyHostToDevice, m->stream));
   RC(fill_f32(m->lo.P, m->at<float>(m->lo.adam_m), 0.f, m->stream));
@@ -819,31 +1089,39 @@ int gpt2_set_params(gpt2_model* m, const float* host_in) {
   GPT2_HIP_CHECK(hipStreamSynchronize(m->stream));
   m->have_dlogits = m->have_grads = false;
   return GPT2_OK;
+  GPT2_ABI_END_STATUS
 }
 
 int gpt2_get_grads(gpt2_model* m, float* host_out) {
+  GPT2_ABI_BEGIN
   if (!m || !host_out) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "get_grads: NULL");
   return copy_out(m, m->grad(), host_out, m->lo.P * sizeof(float));
+  GPT2_ABI_END_STATUS
 }
 
 int gpt2_get_adam_state(gpt2_model* m, float* host_m, float* host_v) {
+  GPT2_ABI_BEGIN
   if (!m) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "get_adam_state: NULL");
   if (host_m) RC(copy_out(m, m->at<float>(m->lo.adam_m), host_m, m->lo.P * sizeof(float)));
   if (host_v) RC(copy_out(m, m->at<float>(m->lo.adam_v), host_v, m->lo.P * sizeof(float)));
   return GPT2_OK;
+  GPT2_ABI_END_STATUS
 }
 
 int gpt2_get_token_losses(gpt2_model* m, float* host_out) {
+  GPT2_ABI_BEGIN
   if (!m || !host_out) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "get_token_losses: NULL");
   return copy_out(m, m->at<float>(m->lo.losses), host_out,
                   (size_t)m->cfg.batch_size * m->cfg.seq_len * sizeof(float));
+  GPT2_ABI_END_STATUS
 }
 
 int gpt2_get_logits(gpt2_model* m, float* host_out) {
+  GPT2_ABI_BEGIN
   if (!m || !host_out) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "get_logits: NULL");
   const int64_t n = (int64_t)m->cfg.batch_size * m->cfg.seq_len * m->cfg.padded_vocab_size;
   if (m->cfg.dtype == GPT2_FP32) return copy_out(m, m->at<float>(m->lo.logits), host_out, n * sizeof(float));
-  // convert through the d_big scratch region chunk by chunk
+  // convert through the scratch region chunk by chunk
   float* tmp = m->at<float>(m->lo.scratch);
   const int64_t chunk = (int64_t)(m->lo.scratch_bytes / sizeof(float)) / 4096 * 4096;
   if (chunk <= 0) return gpt2_internal_fail(GPT2_E_OOM, "get_logits: scratch too small");
@@ -853,23 +1131,27 @@ int gpt2_get_logits(gpt2_model* m, float* host_out) {
     RC(copy_out(m, tmp, host_out + i, k * sizeof(float)));
   }
   return GPT2_OK;
+  GPT2_ABI_END_STATUS
 }
 
 int gpt2_timing_enable(gpt2_model* m, int site, int enable) {
+  GPT2_ABI_BEGIN
   if (!m || site < 0 || site >= S_COUNT) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "timing_enable: bad site");
   SiteTimer& t = m->timers[site];
   if (enable && t.ev.empty()) {
-    t.ev.resize(2 * 4096);
+    grow(t.ev, 2 * 4096);
     for (auto& e : t.ev) GPT2_HIP_CHECK(hipEventCreate(&e));
   }
   t.on = enable != 0;
   t.used = 0;
   t.launches = 0;
   return GPT2_OK;
+  GPT2_ABI_END_STATUS
 }
 
 int gpt2_timing_read(gpt2_model* m, int site, double* total_ms, int64_t* launches, double* flops_per_launch,
                      double* bytes_per_launch) {
+  GPT2_ABI_BEGIN
   if (!m || site < 0 || site >= S_COUNT) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "timing_read: bad site");
   SiteTimer& t = m->timers[site];
   GPT2_HIP_CHECK(hipStreamSynchronize(m->stream));
@@ -886,69 +1168,83 @@ int gpt2_timing_read(gpt2_model* m, int site, double* total_ms, int64_t* launche
   t.used = 0;
   t.launches = 0;
   return GPT2_OK;
+  GPT2_ABI_END_STATUS
 }
 
 // ================================================================ op-level ABI
 
 int gpt2_op_linear_forward(int dtype, int M, int N, int K, const void* x, const void* W, const void* b,
-                           const void* residual, void* y, void* gelu_out, void* stream) {
-  if (residual && gelu_out) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "residual and gelu_out are exclusive");
-  GemmDesc d;
-  memset(&d, 0, sizeof(d));
-  d.dtype = dtype;
-  d.a_kmajor = d.b_kmajor = true;
-  d.M = M; d.N = N; d.K = K;
-  d.A = x; d.lda = K; d.B = W; d.ldb = K;
-  d.ldc = N; d.ld_aux = N; d.bias = b;
-  if (gelu_out) {
-    if (!b) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "gelu epilogue needs a bias");
-    d.epi = EPI_BIAS_GELU; d.C = gelu_out; d.aux_out = y;
-  } else if (residual) {
-    if (!b) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "residual epilogue needs a bias");
-    d.epi = EPI_BIAS_RES; d.C = y; d.aux_in = residual;
-  } else {
-    d.epi = b ? EPI_BIAS : EPI_STORE; d.C = y;
-  }
-  return gemm(d, (hipStream_t)stream);
+                           const void* residual, void* y, void* gelu_grad, void* stream) {
+  GPT2_ABI_BEGIN
+  if (residual && gelu_grad) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "residual and gelu_grad are exclusive");
+  if ((residual || gelu_grad) && !b)
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "the residual and GELU epilogues need a bias");
+  const int epi = gelu_grad ? EPI_BIAS_GELU_D : residual ? EPI_BIAS_RES : b ? EPI_BIAS : EPI_STORE;
+  return gemm(linear_fwd_desc(dtype, M, N, K, x, W, epi, y, b, residual, gelu_grad), (hipStream_t)stream);
+  GPT2_ABI_END_STATUS
 }
 
 size_t gpt2_op_linear_backward_workspace_bytes(int dtype, int M, int N, int K) {
-  return std::max(gemm_workspace_bytes(dtype, EPI_WGRAD, N, K, M, false, false),
-                  gemm_workspace_bytes(dtype, EPI_STORE, M, K, N, true, false));
+  GPT2_ABI_BEGIN
+  const bool wt = dtype == GPT2_BF16;
+  return op_wt_bytes(dtype, N, K) + std::max(gemm_workspace_bytes(dtype, EPI_WGRAD, N, K, M, false, false),
+                                             gemm_workspace_bytes(dtype, EPI_STORE, M, K, N, true, wt));
+  GPT2_ABI_END(0)
 }
 
 int gpt2_op_linear_backward(int dtype, int M, int N, int K, const void* dy, const void* x, const void* W,
-                            const void* gelu_u, void* dx, float* dW, float* db, int accumulate, void* workspace,
+                            const void* gelu_grad, void* dx, float* dW, float* db, int accumulate, void* workspace,
                             size_t workspace_bytes, void* stream) {
+  GPT2_ABI_BEGIN
   hipStream_t s = (hipStream_t)stream;
-  if (dW) {
-    GemmDesc d;
-    memset(&d, 0, sizeof(d));
-    d.dtype = dtype; d.a_kmajor = false; d.b_kmajor = false;
-    d.M = N; d.N = K; d.K = M;
-    d.A = dy; d.lda = N; d.B = x; d.ldb = K;
-    d.epi = EPI_WGRAD; d.out32 = dW; d.bias_grad32 = db; d.accumulate = accumulate != 0;
-    d.workspace = workspace; d.workspace_bytes = workspace_bytes;
-    RC(gemm(d, s));
-  } else if (db) {
-    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "db is computed in the dW pass; pass dW too");
-  }
+  if (db && !dW) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "db is computed in the dW pass; pass dW too");
+  const size_t wtb = dx ? op_wt_bytes(dtype, N, K) : 0;
+  const size_t need = gpt2_op_linear_backward_workspace_bytes(dtype, M, N, K);
+  if ((dx || dW) && (!workspace || workspace_bytes < need))
+    return gpt2_internal_fail(GPT2_E_OOM, "linear_backward: workspace of %zu bytes (need %zu)", workspace_bytes, need);
+  char* ws = static_cast<char*>(workspace);
+  if (dW)
+    RC(gemm(linear_dw_desc(dtype, M, N, K, dy, x, dW, db, accumulate != 0, ws + wtb, workspace_bytes - wtb), s));
   if (dx) {
-    GemmDesc d;
-    memset(&d, 0, sizeof(d));
-    d.dtype = dtype; d.a_kmajor = true; d.b_kmajor = false;
-    d.M = M; d.N = K; d.K = N;
-    d.A = dy; d.lda = N; d.B = W; d.ldb = K;
-    d.epi = gelu_u ? EPI_GELU_BWD : EPI_STORE; d.C = dx; d.ldc = K; d.aux_in = gelu_u; d.ld_aux = K;
-    d.workspace = workspace; d.workspace_bytes = workspace_bytes;
-    RC(gemm(d, s));
+    void* WT = nullptr;
+    if (wtb) {   // W [N, K] -> WT [K, N], the layout the step's dX products read
+      if (!W) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "linear_backward: W is NULL");
+      RC(transpose_bf16(1, N, K, static_cast<const bf16*>(W), reinterpret_cast<bf16*>(ws), s));
+      WT = ws;
+    }
+    RC(gemm(linear_dx_desc(dtype, M, N, K, dy, W, WT, dx, gelu_grad ? EPI_MUL : EPI_STORE, gelu_grad, ws + wtb,
+                           workspace_bytes - wtb),
+            s));
   }
   return GPT2_OK;
+  GPT2_ABI_END_STATUS
+}
+
+int gpt2_op_linear_plans(int dtype, int M, int N, int K, int has_bias, int has_residual, int has_gelu, int has_db,
+                         gpt2_gemm_plan out[3]) {
+  GPT2_ABI_BEGIN
+  if (!out) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "linear_plans: out is NULL");
+  // placeholders: planning reads shapes, epilogues and layouts, never memory
+  void* const p = reinterpret_cast<void*>((uintptr_t)4096);
+  const int epi = has_gelu ? EPI_BIAS_GELU_D : has_residual ? EPI_BIAS_RES : has_bias ? EPI_BIAS : EPI_STORE;
+  fill_plan(linear_fwd_desc(dtype, M, N, K, p, p, epi, p, has_bias ? p : nullptr, has_residual ? p : nullptr,
+                            has_gelu ? p : nullptr),
+            "forward", &out[0]);
+  fill_plan(linear_dw_desc(dtype, M, N, K, p, p, static_cast<float*>(p), has_db ? static_cast<float*>(p) : nullptr,
+                           false, p, 0),
+            "dW", &out[1]);
+  fill_plan(linear_dx_desc(dtype, M, N, K, p, p, dtype == GPT2_BF16 ? p : nullptr, p, has_gelu ? EPI_MUL : EPI_STORE,
+                           has_gelu ? p : nullptr, p, 0),
+            "dX", &out[2]);
+  return GPT2_OK;
+  GPT2_ABI_END_STATUS
 }
 
 int gpt2_op_layernorm_forward(int dtype, int N, int C, const void* x, const void* w, const void* b, void* y,
                               float* mean, float* rstd, void* stream) {
+  GPT2_ABI_BEGIN
   return layernorm_forward(dtype, N, C, x, w, b, y, mean, rstd, (hipStream_t)stream);
+  GPT2_ABI_END_STATUS
 }
 
 size_t gpt2_op_layernorm_backward_workspace_bytes(int N, int C) { return layernorm_backward_workspace_bytes(N, C); }
@@ -957,13 +1253,17 @@ int gpt2_op_layernorm_backward(int dtype, int N, int C, const void* dy, const vo
                                const float* mean, const float* rstd, float* dres, int dres_overwrite,
                                void* dres_copy, float* dw, float* db, int accumulate, void* workspace,
                                size_t workspace_bytes, void* stream) {
+  GPT2_ABI_BEGIN
   return layernorm_backward(dtype, N, C, dy, x, w, mean, rstd, dres, dres_overwrite != 0, dres_copy, dw, db,
                             accumulate != 0, workspace, workspace_bytes, (hipStream_t)stream);
+  GPT2_ABI_END_STATUS
 }
 
 int gpt2_op_attention_forward(int dtype, int B, int T, int H, int hd, const void* qkv, void* out, float* lse,
                               void* stream) {
+  GPT2_ABI_BEGIN
   return attention_forward(dtype, B, T, H, hd, qkv, out, lse, (hipStream_t)stream);
+  GPT2_ABI_END_STATUS
 }
 
 size_t gpt2_op_attention_backward_workspace_bytes(int B, int T, int H, int hd) {
@@ -973,13 +1273,17 @@ size_t gpt2_op_attention_backward_workspace_bytes(int B, int T, int H, int hd) {
 int gpt2_op_attention_backward(int dtype, int B, int T, int H, int hd, const void* qkv, const void* out,
                                const void* dout, const float* lse, void* dqkv, void* workspace,
                                size_t workspace_bytes, void* stream) {
+  GPT2_ABI_BEGIN
   return attention_backward(dtype, B, T, H, hd, qkv, out, dout, lse, dqkv, workspace, workspace_bytes,
                             (hipStream_t)stream);
+  GPT2_ABI_END_STATUS
 }
 
 int gpt2_op_softmax_xent(int dtype, int N, int V, int Vp, void* logits, const int32_t* labels, float* losses,
                          float dscale, void* stream) {
+  GPT2_ABI_BEGIN
   return softmax_xent(dtype, N, V, Vp, logits, labels, losses, dscale, (hipStream_t)stream);
+  GPT2_ABI_END_STATUS
 }
 
 size_t gpt2_op_classifier_workspace_bytes(int dtype, int N, int C, int Vp) {
@@ -989,19 +1293,23 @@ size_t gpt2_op_classifier_workspace_bytes(int dtype, int N, int C, int Vp) {
 int gpt2_op_classifier_fwd_bwd(int dtype, int N, int C, int V, int Vp, const void* hidden, const void* wte,
                                const int32_t* labels, float* losses, void* logits, void* d_hidden, float* d_wte,
                                void* workspace, size_t workspace_bytes, void* stream) {
+  GPT2_ABI_BEGIN
   if (N <= 0 || C <= 0 || V <= 0 || Vp < V || !hidden || !wte || !labels || !losses || !logits || !d_hidden || !d_wte)
     return gpt2_internal_fail(GPT2_E_INVALID_ARG, "classifier: bad arguments");
   hipStream_t s = (hipStream_t)stream;
   RC(gpt2_op_linear_forward(dtype, N, Vp, C, hidden, wte, nullptr, nullptr, logits, nullptr, stream));
   RC(softmax_xent(dtype, N, V, Vp, logits, labels, losses, 1.0f / N, s));
-  // d_hidden = dlogits wte  (a linear backward with W = wte [Vp, C])
+  // d_hidden = dlogits wte, d_wte = dlogits^T hidden: a linear backward with W = wte [Vp, C]
   return gpt2_op_linear_backward(dtype, N, Vp, C, logits, hidden, wte, nullptr, d_hidden, d_wte, nullptr, 0,
                                  workspace, workspace_bytes, stream);
+  GPT2_ABI_END_STATUS
 }
 
 int gpt2_op_encoder_forward(int dtype, int B, int T, int C, int V, const int32_t* tokens, const void* wte,
                             const void* wpe, void* out, void* stream) {
+  GPT2_ABI_BEGIN
   return encoder_forward(dtype, B, T, C, V, tokens, wte, wpe, out, (hipStream_t)stream);
+  GPT2_ABI_END_STATUS
 }
 
 size_t gpt2_op_encoder_backward_workspace_bytes(int B, int T, int C) {
@@ -1010,14 +1318,18 @@ size_t gpt2_op_encoder_backward_workspace_bytes(int B, int T, int C) {
 
 int gpt2_op_encoder_backward(int B, int T, int C, int V, const int32_t* tokens, const float* dx0, float* dwte,
                              float* dwpe, int accumulate_wpe, void* workspace, size_t workspace_bytes, void* stream) {
+  GPT2_ABI_BEGIN
   return encoder_backward(B, T, C, V, tokens, dx0, dwte, dwpe, accumulate_wpe != 0, workspace, workspace_bytes,
                           (hipStream_t)stream);
+  GPT2_ABI_END_STATUS
 }
 
 int gpt2_op_adamw(int64_t n, float* master, const float* grad, float* m, float* v, void* param_bf16, float lr,
                   float beta1, float beta2, float eps, float weight_decay, int32_t t, void* stream) {
+  GPT2_ABI_BEGIN
   return adamw(n, master, grad, m, v, (bf16*)param_bf16, lr, beta1, beta2, eps, weight_decay, t,
                (hipStream_t)stream);
+  GPT2_ABI_END_STATUS
 }
 
 }  // extern "C"

@@ -25,10 +25,28 @@ SITES = ["qkv", "attproj", "fc", "fcproj", "logits", "fcproj_dx", "fcproj_dw", "
          "weight_transpose", "grad_norm"]
 
 
+GPT2_ARCH_RELU2 = 1
+GPT2_ARCH_QK_NORM = 2
+GPT2_ARCH_ROPE = 4
+
+EPILOGUES = {0: "store", 1: "bias", 2: "bias+residual", 5: "wgrad", 6: "bias+gelu", 7: "mul"}
+
+
 class Gpt2Config(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "vocab_size", "padded_vocab_size", "max_seq_len", "num_layers", "num_heads", "channels",
-        "batch_size", "seq_len", "dtype")]
+        "batch_size", "seq_len", "dtype", "arch_flags")]
+
+
+class GemmPlan(C.Structure):
+    _fields_ = [("site", C.c_char * 16)] + [(n, C.c_int32) for n in (
+        "M", "N", "K", "epilogue", "a_kmajor", "b_kmajor", "tile_m", "tile_n", "waves", "k_groups", "k_splits",
+        "bias_grad")]
+
+    def as_dict(self):
+        d = {n: getattr(self, n) for n, _ in self._fields_[1:]}
+        d["site"] = self.site.decode()
+        return d
 
 
 class Gpt2Error(RuntimeError):
@@ -58,6 +76,11 @@ def load():
         "gpt2_workspace_bytes": (sz, [cfgp]),
         "gpt2_status_string": (C.c_char_p, [C.c_int]),
         "gpt2_last_error": (C.c_char_p, []),
+        "gpt2_test_fail_host_allocations": (C.c_int, [C.c_int]),
+        "gpt2_step_gemm_plans": (C.c_int, [cfgp, C.POINTER(GemmPlan), C.c_int, C.POINTER(C.c_int)]),
+        "gpt2_op_linear_plans": (C.c_int, [C.c_int] * 8 + [C.POINTER(GemmPlan)]),
+        "gpt2_graph_capture": (C.c_int, [vp, vp, vp]),
+        "gpt2_graph_step": (C.c_int, [vp, f32, f32, f32, f32, f32, i32, fp]),
         "gpt2_create": (C.c_int, [cfgp, C.c_uint64, vp, vp, sz, C.POINTER(vp)]),
         "gpt2_forward": (C.c_int, [vp, vp, vp, fp]),
         "gpt2_forward_scaled": (C.c_int, [vp, vp, vp, f32, fp]),
@@ -107,7 +130,9 @@ def exported_symbols():
     """Names every header declares (checked against the library's exports)."""
     return [
         "gpt2_validate_config", "gpt2_num_parameters", "gpt2_num_param_tensors", "gpt2_param_info",
-        "gpt2_workspace_bytes", "gpt2_status_string", "gpt2_last_error", "gpt2_create", "gpt2_forward",
+        "gpt2_workspace_bytes", "gpt2_status_string", "gpt2_last_error", "gpt2_test_fail_host_allocations",
+        "gpt2_graph_capture", "gpt2_graph_step", "gpt2_step_gemm_plans", "gpt2_op_linear_plans",
+        "gpt2_create", "gpt2_forward",
         "gpt2_forward_scaled", "gpt2_backward", "gpt2_backward_accumulate", "gpt2_adamw_step",
         "gpt2_adamw_step_clipped", "gpt2_destroy", "gpt2_get_mean_loss", "gpt2_get_params", "gpt2_set_params",
         "gpt2_get_grads", "gpt2_get_adam_state", "gpt2_get_token_losses", "gpt2_get_logits",
@@ -129,8 +154,26 @@ def check(rc: int, what: str = ""):
         raise Gpt2Error(f"{what}: {lib.gpt2_status_string(rc).decode()} ({rc}): {msg}")
 
 
-def make_config(V, Vp, maxT, L, H, C_, B, T, dtype) -> Gpt2Config:
-    return Gpt2Config(V, Vp, maxT, L, H, C_, B, T, dtype)
+def make_config(V, Vp, maxT, L, H, C_, B, T, dtype, arch_flags=0) -> Gpt2Config:
+    return Gpt2Config(V, Vp, maxT, L, H, C_, B, T, dtype, arch_flags)
+
+
+def step_gemm_plans(cfg: Gpt2Config):
+    """Every GEMM launch of one training step of cfg (host-only query)."""
+    lib = load()
+    n = C.c_int()
+    check(lib.gpt2_step_gemm_plans(C.byref(cfg), None, 0, C.byref(n)), "step_gemm_plans")
+    out = (GemmPlan * max(n.value, 1))()
+    check(lib.gpt2_step_gemm_plans(C.byref(cfg), out, n.value, C.byref(n)), "step_gemm_plans")
+    return [out[i].as_dict() for i in range(n.value)]
+
+
+def op_linear_plans(dtype, M, N, K, bias=False, residual=False, gelu=False, db=False):
+    """The GEMM launches of gpt2_op_linear_forward / _backward: forward, dW, dX."""
+    out = (GemmPlan * 3)()
+    check(load().gpt2_op_linear_plans(dtype, M, N, K, int(bias), int(residual), int(gelu), int(db), out),
+          "op_linear_plans")
+    return [out[i].as_dict() for i in range(3)]
 
 
 def param_layout(cfg: Gpt2Config):
@@ -213,6 +256,16 @@ class Model:
         check(self.lib.gpt2_forward(self.h, ptr(tokens), ptr(targets), C.byref(loss) if want else None), "forward")
         return loss.value if want else None
 
+    def graph_capture(self, tokens, targets):
+        """Captures one training step reading ids from these device buffers."""
+        check(self.lib.gpt2_graph_capture(self.h, ptr(tokens), ptr(targets)), "graph_capture")
+
+    def graph_step(self, lr, beta1, beta2, eps, weight_decay, t, read_loss=True):
+        loss = C.c_float(0.0)
+        check(self.lib.gpt2_graph_step(self.h, lr, beta1, beta2, eps, weight_decay, t,
+                                       C.byref(loss) if read_loss else None), "graph_step")
+        return loss.value if read_loss else None
+
     def get_mean_loss(self):
         loss = C.c_float(0.0)
         check(self.lib.gpt2_get_mean_loss(self.h, C.byref(loss)), "get_mean_loss")
@@ -288,19 +341,19 @@ def _ws(nbytes):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device="cuda")
 
 
-def linear_forward(dtype, x, W, b=None, residual=None, gelu_out=None, y=None, stream=None):
+def linear_forward(dtype, x, W, b=None, residual=None, gelu_grad=None, y=None, stream=None):
     M, K = x.shape
     N = W.shape[0]
     check(load().gpt2_op_linear_forward(dtype, M, N, K, ptr(x), ptr(W), ptr(b), ptr(residual), ptr(y),
-                                        ptr(gelu_out), _stream_ptr(stream)), "linear_forward")
+                                        ptr(gelu_grad), _stream_ptr(stream)), "linear_forward")
 
 
-def linear_backward(dtype, dy, x, W, dx=None, dW=None, db=None, gelu_u=None, accumulate=False, stream=None):
+def linear_backward(dtype, dy, x, W, dx=None, dW=None, db=None, gelu_grad=None, accumulate=False, stream=None):
     lib = load()
     M, N = dy.shape
     K = x.shape[1]
     ws = _ws(lib.gpt2_op_linear_backward_workspace_bytes(dtype, M, N, K))
-    check(lib.gpt2_op_linear_backward(dtype, M, N, K, ptr(dy), ptr(x), ptr(W), ptr(gelu_u), ptr(dx), ptr(dW),
+    check(lib.gpt2_op_linear_backward(dtype, M, N, K, ptr(dy), ptr(x), ptr(W), ptr(gelu_grad), ptr(dx), ptr(dW),
                                       ptr(db), int(accumulate), ptr(ws), ws.numel(), _stream_ptr(stream)),
           "linear_backward")
     return ws

@@ -2,8 +2,12 @@
  * gpt2_ops.h -- op-level C ABI of the GPT-2 step library (gfx950).
  *
  * Each call launches exactly the kernels the training step uses for that
- * operation, on caller-owned device buffers, so every step of the path can be
- * checked in isolation at its real shapes.  All calls are asynchronous on
+ * operation (same GEMM planner, operand layouts and epilogues: the linear
+ * backward's dX reads the weight through the same transposed bf16 copy the
+ * step keeps; gpt2_op_linear_plans / gpt2_step_gemm_plans report the kernel
+ * configuration each launch gets), on caller-owned device buffers, so every
+ * step of the path can be checked in isolation at its real shapes.  All
+ * calls are asynchronous on
  * `stream` (a hipStream_t as void*, NULL = null stream) and return a gpt2
  * status (see gpt2.h); on failure nothing has been enqueued.
  *
@@ -20,6 +24,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "gpt2.h"
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -27,30 +33,77 @@ extern "C" {
 /* Linear layer forward, y = x W^T + b (the block's QKV, attention-projection,
  * fc and fc-projection matmuls and the tied classifier; the kernel table of
  * "State of the Union [May 3, 2024]", section "Runtime, DRAM traffic,
- * instructions", attributes most of the step to these GEMMs):
+ * instructions", attributes most of the step to these GEMMs and lists the
+ * residual add and GELU as kernels of their own, fused here into the GEMM):
  *   x [M, K] T, W [N, K] T, b [N] T or NULL (no bias), y [M, N] T.
  *   residual [M, N] T or NULL:  y += residual   (the block's residual add)
- *   gelu_out [M, N] T or NULL:  y holds u = xW^T + b and gelu_out = GELU_tanh(u)
- * residual and gelu_out are exclusive.  bf16: K % 8 == 0 and 16-byte aligned
- * x and W (reduction tails are zero-filled inside the kernel). */
+ *   gelu_grad [M, N] T or NULL: with u = x W^T + b, y = GELU_tanh(u) and
+ *                               gelu_grad = GELU_tanh'(u) (the fc layer; the
+ *                               backward multiplies by the saved derivative)
+ * residual and gelu_grad are exclusive and need b.  bf16: K % 8 == 0 and
+ * 16-byte aligned x and W (reduction tails are zero-filled inside the
+ * kernel). */
 int gpt2_op_linear_forward(int dtype, int M, int N, int K, const void* x, const void* W,
-                           const void* b, const void* residual, void* y, void* gelu_out,
+                           const void* b, const void* residual, void* y, void* gelu_grad,
                            void* stream);
 
-/* Linear layer backward for y = x W^T + b with upstream gradient dy [M, N]:
+/* Linear layer backward for y = x W^T + b with upstream gradient dy [M, N]
+ * (the kernel table's matmul backward and bias-gradient kernels, and the
+ * GELU backward, which becomes the multiply below):
  *   dx [M, K] T      = dy W                  (skipped if dx == NULL)
- *       if gelu_u [M, K] T != NULL:  dx = (dy W) * GELU_tanh'(gelu_u)
+ *       if gelu_grad [M, K] T != NULL:  dx = (dy W) * gelu_grad
  *   dW [N, K] f32    = dy^T x   (overwrite, or add if accumulate)
  *   db [N] f32       = sum over rows of dy (or NULL; fused into the dW pass)
- * dW == NULL skips the weight gradient.  bf16: M, N and K multiples of 8.
+ * dW == NULL skips the weight gradient.  bf16: M, N and K multiples of 8; dx
+ * reads W through a transposed copy W^T [K, N] that this call writes at the
+ * start of the workspace (the training step keeps the same copy of each
+ * weight matrix, refreshed after every update).
  * workspace: at least gpt2_op_linear_backward_workspace_bytes() bytes of
- * device scratch (fp32 partial sums of dW over row blocks and, when N is
- * long, of dx over N blocks; summed in a fixed order, so results are
- * deterministic); GPT2_E_OOM if it is smaller. */
+ * device scratch (the transposed copy; fp32 partial sums of dW over row
+ * blocks and, when N is long, of dx over N blocks, summed in a fixed order,
+ * so results are deterministic); GPT2_E_OOM if it is smaller. */
 size_t gpt2_op_linear_backward_workspace_bytes(int dtype, int M, int N, int K);
 int gpt2_op_linear_backward(int dtype, int M, int N, int K, const void* dy, const void* x,
-                            const void* W, const void* gelu_u, void* dx, float* dW, float* db,
+                            const void* W, const void* gelu_grad, void* dx, float* dW, float* db,
                             int accumulate, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- GEMM launch plans (host-only introspection, no HIP call) ------------
+ * The configuration the library's GEMM kernel is launched with for one
+ * product C[M, N] = sum over k of A(m, k) B(n, k): block tile, waves per
+ * block, K-groups of waves, K-splits (fp32 partial sums reduced in a fixed
+ * order) and whether the bias gradient is fused.  The fp32 parity kernel
+ * reports a 64 x 64 tile, 4 waves, no split. */
+enum {
+  GPT2_EPI_STORE = 0,         /* C = sum                                      */
+  GPT2_EPI_BIAS = 1,          /* C = sum + bias                               */
+  GPT2_EPI_BIAS_RESIDUAL = 2, /* C = sum + bias + residual                    */
+  GPT2_EPI_WGRAD = 5,         /* fp32 weight gradient (+ fused bias gradient) */
+  GPT2_EPI_BIAS_GELU = 6,     /* C = GELU(sum + bias), U = GELU'(sum + bias)  */
+  GPT2_EPI_MUL = 7            /* C = sum * U                                  */
+};
+
+typedef struct gpt2_gemm_plan {
+  char site[16];                /* timing-site name ("qkv", "fcproj_dx", ...), or
+                                   "forward" / "dW" / "dX" for the op plans       */
+  int32_t M, N, K;              /* product shape                                 */
+  int32_t epilogue;             /* GPT2_EPI_*                                    */
+  int32_t a_kmajor, b_kmajor;   /* operand layouts (1: k contiguous in memory)    */
+  int32_t tile_m, tile_n;       /* block tile                                    */
+  int32_t waves;                /* waves per block                               */
+  int32_t k_groups;             /* groups of waves splitting each K step         */
+  int32_t k_splits;             /* blocks splitting K (partial sums)             */
+  int32_t bias_grad;            /* 1: bias gradient fused into the dW product     */
+} gpt2_gemm_plan;
+
+/* Every GEMM one training step of cfg launches (forward with targets, then
+ * backward; one entry per launch, in launch order): *count is set to their
+ * number and the first min(count, max_plans) are written to out. */
+int gpt2_step_gemm_plans(const gpt2_config* cfg, gpt2_gemm_plan* out, int max_plans, int* count);
+
+/* The three GEMMs of gpt2_op_linear_forward and gpt2_op_linear_backward for
+ * these shapes and options: out[0] the forward, out[1] dW, out[2] dX. */
+int gpt2_op_linear_plans(int dtype, int M, int N, int K, int has_bias, int has_residual, int has_gelu,
+                         int has_db, gpt2_gemm_plan out[3]);
 
 /* LayerNorm forward over rows of C (eps 1e-5, biased variance):
  *   x [N, C] T, w, b [C] T -> y [N, C] T, mean [N] f32, rstd [N] f32. C % 8 == 0. */

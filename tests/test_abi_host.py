@@ -124,6 +124,85 @@ def test_workspace_is_sized_for_the_124m_step():
 def test_status_strings_and_null_create():
     from gpt_transformer_lm_amd import lib
     L = lib.load()
-    for st in range(5):
-        assert L.gpt2_status_string(st)
+    for st in range(6):
+        assert L.gpt2_status_string(st) != b"unknown status"
     assert L.gpt2_create(None, 0, None, None, 0, None) == 1
+
+
+def test_failed_host_allocation_is_a_status_not_a_crash():
+    """A host allocation that fails inside the library (forced by the test
+    hook) comes back through the C ABI as GPT2_E_OOM / a zero size with the
+    reason in gpt2_last_error(), and the next call works again."""
+    from gpt_transformer_lm_amd import lib
+    L = lib.load()
+    c = cfg()
+    good = L.gpt2_workspace_bytes(C.byref(c))
+    assert good > 0
+    assert L.gpt2_test_fail_host_allocations(1) == 0
+    assert L.gpt2_workspace_bytes(C.byref(c)) == 0
+    assert b"host allocation" in L.gpt2_last_error()
+    assert L.gpt2_workspace_bytes(C.byref(c)) == good          # the hook fired once
+    n = C.c_int(-1)
+    assert L.gpt2_test_fail_host_allocations(2) == 0
+    assert L.gpt2_step_gemm_plans(C.byref(c), None, 0, C.byref(n)) == 3
+    assert b"host allocation" in L.gpt2_last_error()
+    L.gpt2_test_fail_host_allocations(0)
+    assert L.gpt2_step_gemm_plans(C.byref(c), None, 0, C.byref(n)) == 0 and n.value > 0
+
+
+def test_unknown_arch_flags_are_rejected():
+    from gpt_transformer_lm_amd import lib
+    L = lib.load()
+    c = cfg()
+    c.arch_flags = 8
+    assert L.gpt2_validate_config(C.byref(c)) == 1
+    assert b"arch_flags" in L.gpt2_last_error()
+
+
+# The three GPT-2 sizes at their benchmark batch (T = 1024).
+SIZES = {"124m": dict(L=12, H=12, C_=768, B=24), "350m": dict(L=24, H=16, C_=1024, B=16),
+         "1.6b": dict(L=48, H=25, C_=1600, B=8)}
+PLAN_KEYS = ("M", "N", "K", "epilogue", "a_kmajor", "b_kmajor", "tile_m", "tile_n", "waves", "k_groups",
+             "k_splits", "bias_grad")
+
+
+def op_plan_for_site(site, BT, Cc, Vp):
+    """The op-level linear call (and which of its three GEMMs) that performs
+    the step's GEMM at `site`, with the options the step uses there."""
+    from gpt_transformer_lm_amd import lib
+    layer = {"qkv": (3 * Cc, Cc, dict(bias=True)), "attproj": (Cc, Cc, dict(bias=True, residual=True)),
+             "fc": (4 * Cc, Cc, dict(bias=True, gelu=True)), "fcproj": (Cc, 4 * Cc, dict(bias=True, residual=True)),
+             "logits": (Vp, Cc, dict())}
+    if site in layer:
+        N, K, kw = layer[site]
+        return lib.op_linear_plans(1, BT, N, K, **kw)[0]
+    base, kind = site.rsplit("_", 1)
+    name = {"cls": "logits"}.get(base, base)
+    N, K, _ = layer[name]
+    if kind == "dw":
+        return lib.op_linear_plans(1, BT, N, K, db=name != "logits")[1]
+    # dX of the fc-proj layer multiplies by the fc layer's saved GELU'
+    return lib.op_linear_plans(1, BT, N, K, gelu=name == "fcproj")[2]
+
+
+@pytest.mark.parametrize("size", sorted(SIZES))
+def test_step_gemm_plans_reached_by_the_full_width_tests(size):
+    """Every GEMM instantiation the full-depth step launches is launched by
+    the two-layer step at the same width and batch (the GEMM shapes do not
+    depend on L) and by the op-level linear calls at the same shapes: the
+    full-width step-parity tests and the full-size op tests reach the same
+    kernels as the benchmarked step."""
+    from gpt_transformer_lm_amd import lib
+    k = SIZES[size]
+    full = lib.step_gemm_plans(cfg(**k))
+    two = lib.step_gemm_plans(cfg(**dict(k, L=2)))
+    assert len(full) == 12 * k["L"] + 3
+    key = lambda p: (p["site"],) + tuple(p[x] for x in PLAN_KEYS)
+    assert {key(p) for p in full} == {key(p) for p in two}
+    seen = {}
+    for p in full:
+        seen.setdefault(p["site"], p)
+    assert len(seen) == 15
+    for site, p in seen.items():
+        o = op_plan_for_site(site, k["B"] * 1024, k["C_"], 50304)
+        assert tuple(o[x] for x in PLAN_KEYS) == tuple(p[x] for x in PLAN_KEYS), (site, o, p)

@@ -46,6 +46,9 @@ SHAPES = [(256, 192, 64), (200, 136, 128), (64, 64, 64), (320, 200, 192), (2104,
 @pytest.mark.parametrize("M,N,K", SHAPES)
 @pytest.mark.parametrize("epi", ["store", "bias", "bias_res", "bias_gelu"])
 def test_linear_forward(dtype, M, N, K, epi):
+    """The four forward epilogues of the step: plain (logits), bias (QKV),
+    bias + residual (attention and MLP projections) and bias + GELU with
+    GELU' saved (fc)."""
     say("linear_forward", DTN[dtype], M, N, K, epi)
     r = rng(M * 7 + N + K)
     x, W = r.standard_normal((M, K)), r.standard_normal((N, K)) * 0.1
@@ -54,13 +57,15 @@ def test_linear_forward(dtype, M, N, K, epi):
     y = empty((M, N), dtype)
     g = empty((M, N), dtype) if epi == "bias_gelu" else None
     lib.linear_forward(dtype, dev(x, dtype), dev(W, dtype), b=None if epi == "store" else dev(b, dtype),
-                       residual=dev(res, dtype) if epi == "bias_res" else None, gelu_out=g, y=y)
+                       residual=dev(res, dtype) if epi == "bias_res" else None, gelu_grad=g, y=y)
     ref = O.linear_forward(xi, Wi, None if epi == "store" else bi)
     if epi == "bias_res":
         ref = ref + ri
-    assert rel(host(y), ref) < TOL_OUT[dtype]
-    if g is not None:
-        assert rel(host(g), O.gelu_tanh(ref)) < TOL_OUT[dtype]
+    if g is None:
+        assert rel(host(y), ref) < TOL_OUT[dtype]
+    else:
+        assert rel(host(y), O.gelu_tanh(ref)) < TOL_OUT[dtype]
+        assert rel(host(g), O.gelu_tanh_backward(ref, np.ones_like(ref))) < TOL_OUT[dtype]
 
 
 @pytest.mark.parametrize("dtype", DT, ids=DTN.get)
@@ -81,19 +86,22 @@ def test_linear_forward_unaligned_columns(dtype, M, N, K):
 @pytest.mark.parametrize("M,N,K", SHAPES)
 @pytest.mark.parametrize("gelu", [False, True])
 def test_linear_backward(dtype, M, N, K, gelu):
+    """dX (plain, or multiplied by a saved GELU'(u) as in the fc-projection
+    layer's backward), dW and the fused bias gradient."""
     say("linear_backward", DTN[dtype], M, N, K, "gelu" if gelu else "")
     r = rng(M + 3 * N + 5 * K + gelu)
     dy, x, W, u = r.standard_normal((M, N)), r.standard_normal((M, K)), r.standard_normal((N, K)) * 0.1, \
         r.standard_normal((M, K))
-    dyi, xi, Wi, ui = (as_input(a, dtype).astype(np.float64) for a in (dy, x, W, u))
+    dgelu = O.gelu_tanh_backward(u, np.ones_like(u))       # the derivative the forward saves
+    dyi, xi, Wi, di = (as_input(a, dtype).astype(np.float64) for a in (dy, x, W, dgelu))
     dx = empty((M, K), dtype)
     dW = empty32((N, K))
     db = empty32((N,))
     lib.linear_backward(dtype, dev(dy, dtype), dev(x, dtype), dev(W, dtype), dx=dx, dW=dW, db=db,
-                        gelu_u=dev(u, dtype) if gelu else None)
+                        gelu_grad=dev(dgelu, dtype) if gelu else None)
     rdx, rdW, rdb = O.linear_backward(dyi, xi, Wi)
     if gelu:
-        rdx = O.gelu_tanh_backward(ui, rdx)
+        rdx = rdx * di
     assert rel(host(dx), rdx) < TOL_OUT[dtype]
     assert rel(host(dW), rdW) < TOL_F32
     assert rel(host(db), rdb) < TOL_F32
@@ -114,40 +122,72 @@ def test_linear_backward_accumulates(dtype):
     assert rel(host(db), base_b.astype(np.float32) + rdb) < TOL_F32
 
 
-# The GEMMs of the GPT-2 124M step (B*T = 24576, C = 768, Vp = 50304) at full
-# size, in the launch configuration the step uses; 512 sampled outputs each are
-# recomputed as float64 dot products.
-FULL = [("qkv", 24576, 2304, 768), ("attproj", 24576, 768, 768), ("fc", 24576, 3072, 768),
-        ("fcproj", 24576, 768, 3072), ("logits", 24576, 50304, 768)]
+# The GEMMs of the GPT-2 124M, 350M and 1.6B steps at their benchmark batch
+# (B*T = 24576, 16384, 8192; Vp = 50304) at full size, with the epilogues the
+# step uses at each site, so every (tile, waves, K-groups, K-splits,
+# epilogue, layout) the steps launch runs here (the host test
+# test_step_gemm_plans_reached_by_the_full_width_tests checks that the plans
+# agree).  512 sampled outputs of each product are recomputed as float64 dot
+# products from the same bf16 operands.
+FULL_SIZES = {"124m": (24576, 768), "350m": (16384, 1024), "1.6b": (8192, 1600)}
+FULL_SITES = ["qkv", "attproj", "fc", "fcproj", "logits"]
 
 
-@pytest.mark.parametrize("name,M,N,K", FULL)
-def test_linear_full_size_sampled(name, M, N, K):
-    say("full-size linear", name, M, N, K)
+def _site_shape(site, Cc):
+    return {"qkv": (3 * Cc, Cc), "attproj": (Cc, Cc), "fc": (4 * Cc, Cc), "fcproj": (Cc, 4 * Cc),
+            "logits": (50304, Cc)}[site]
+
+
+@pytest.mark.parametrize("site", FULL_SITES)
+@pytest.mark.parametrize("size", sorted(FULL_SIZES))
+def test_linear_full_size_sampled(size, site):
+    M, Cc = FULL_SIZES[size]
+    N, K = _site_shape(site, Cc)
+    say("full-size linear", size, site, M, N, K)
     torch = __import__("torch")
-    gen = torch.Generator(device="cuda").manual_seed(11)
-    x = torch.randn((M, K), generator=gen, device="cuda").to(torch.bfloat16)
-    W = (torch.randn((N, K), generator=gen, device="cuda") * 0.05).to(torch.bfloat16)
-    dy = (torch.randn((M, N), generator=gen, device="cuda") * 0.1).to(torch.bfloat16)
-    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    lib.linear_forward(BF16, x, W, y=y)
-    dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    bias, residual, gelu = site != "logits", site in ("attproj", "fcproj"), site == "fc"
+    gelu_dx = site == "fcproj"        # the fc-projection dX multiplies by the fc layer's saved GELU'
+    gen = torch.Generator(device="cuda").manual_seed(11 + M + N)
+    bf = torch.bfloat16
+    x = torch.randn((M, K), generator=gen, device="cuda").to(bf)
+    W = (torch.randn((N, K), generator=gen, device="cuda") * 0.05).to(bf)
+    b = (torch.randn((N,), generator=gen, device="cuda") * 0.1).to(bf) if bias else None
+    res = torch.randn((M, N), generator=gen, device="cuda").to(bf) if residual else None
+    dy = (torch.randn((M, N), generator=gen, device="cuda") * 0.1).to(bf)
+    dg = (torch.rand((M, K), generator=gen, device="cuda") * 1.4 - 0.2).to(bf) if gelu_dx else None
+    y = torch.empty((M, N), dtype=bf, device="cuda")
+    g = torch.empty((M, N), dtype=bf, device="cuda") if gelu else None
+    lib.linear_forward(BF16, x, W, b=b, residual=res, gelu_grad=g, y=y)
+    dx = torch.empty((M, K), dtype=bf, device="cuda")
     dW = torch.empty((N, K), dtype=torch.float32, device="cuda")
-    db = torch.empty((N,), dtype=torch.float32, device="cuda")
-    lib.linear_backward(BF16, dy, x, W, dx=dx, dW=dW, db=db)
+    db = torch.empty((N,), dtype=torch.float32, device="cuda") if bias else None
+    lib.linear_backward(BF16, dy, x, W, dx=dx, dW=dW, db=db, gelu_grad=dg)
     torch.cuda.synchronize()
-    r = rng(M + N)
+    r = rng(M + N + K)
     im, in_, ik = r.integers(0, M, 512), r.integers(0, N, 512), r.integers(0, K, 512)
-    xs = x.float().cpu().numpy().astype(np.float64)
-    Ws = W.float().cpu().numpy().astype(np.float64)
-    dys = dy.float().cpu().numpy().astype(np.float64)
-    ref_y = np.einsum("ik,ik->i", xs[im], Ws[in_])
-    assert rel(y.float().cpu().numpy()[im, in_], ref_y) < 3e-3
-    ref_dx = np.einsum("in,in->i", dys[im], Ws[:, ik].T)
-    assert rel(dx.float().cpu().numpy()[im, ik], ref_dx) < 3e-3
-    ref_dw = np.einsum("mi,mi->i", dys[:, in_], xs[:, ik])
-    assert rel(dW.cpu().numpy()[in_, ik], ref_dw) < 1e-4
-    assert rel(db.cpu().numpy(), dys.sum(0)) < 1e-4
+    tim, tin, tik = (torch.from_numpy(a).cuda() for a in (im, in_, ik))
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
+    # forward at the sampled (m, n) pairs
+    u = np.einsum("ik,ik->i", f64(x[tim]), f64(W[tin]))
+    if bias:
+        u = u + f64(b)[in_]
+    if residual:
+        u = u + f64(res[tim, tin])
+    if gelu:
+        assert rel(f64(y[tim, tin]), O.gelu_tanh(u)) < 3e-3
+        assert rel(f64(g[tim, tin]), O.gelu_tanh_backward(u, np.ones_like(u))) < 3e-3
+    else:
+        assert rel(f64(y[tim, tin]), u) < 3e-3
+    # dX at the sampled (m, k) pairs
+    rdx = np.einsum("in,in->i", f64(dy[tim]), f64(W[:, tik].T.contiguous()))
+    if gelu_dx:
+        rdx = rdx * f64(dg[tim, tik])
+    assert rel(f64(dx[tim, tik]), rdx) < 3e-3
+    # dW at the sampled (n, k) pairs, reduced over every row
+    rdw = np.einsum("mi,mi->i", f64(dy[:, tin]), f64(x[:, tik]))
+    assert rel(dW[tin, tik].cpu().numpy(), rdw) < 1e-4
+    if bias:
+        assert rel(db.cpu().numpy(), f64(dy).sum(0)) < 1e-4
 
 
 # ---------------------------------------------------------------- LayerNorm
@@ -290,13 +330,16 @@ def test_softmax_xent(dtype, N, V, Vp):
 def test_classifier_full_size(N):
     """The stand-alone classifier at GPT-2 124M shape (hidden 24x1024x768 ~
     N(0,1), tied table 50304x768 ~ N(0,0.02) including its padded rows,
-    labels uniform in [0, 50257)): sampled rows of the losses, dlogits and
-    d_hidden against the oracle; d_wte by its invariants (padded rows exactly
-    zero, columns sum to zero because every dlogits row does).  The second
-    row count (a multiple of 8, as the bf16 GEMMs require of every reduction
-    length) leaves a ragged last row tile in every product and a partial last
-    K step in d_wte; the d_hidden product reduces over the whole vocabulary
-    in one tile per block."""
+    labels uniform in [0, 50257)), through the step's own kernels (d_hidden
+    reads the table through the transposed copy with the K-grouped 192x192
+    tile over the whole vocabulary).  The oracle runs on every row, in row
+    chunks: the losses of all rows, dlogits and d_hidden of sampled rows,
+    and 64 sampled rows of d_wte element by element (the mean-loss gradient
+    over all rows is the sum of the chunks' gradients, each scaled by its
+    share of the rows); padded rows of dlogits and d_wte are exactly zero.
+    The second row count (a multiple of 8, as the bf16 GEMMs require of every
+    reduction length) leaves a ragged last row tile in every product and a
+    partial last K step in d_wte."""
     C, V, Vp = 768, 50257, 50304
     say("classifier full size", N, C, V, Vp)
     torch = __import__("torch")
@@ -308,21 +351,34 @@ def test_classifier_full_size(N):
     d_wte = torch.empty((Vp, C), dtype=torch.float32, device="cuda")
     lib.classifier_fwd_bwd(BF16, h_d, w_d, dev_i32(labels), V, losses, logits, d_hidden, d_wte)
     torch.cuda.synchronize()
-    hi = S.bf16_round(hidden).astype(np.float64)
-    wi = S.bf16_round(wte).astype(np.float64)
-    rows = np.concatenate([rng(1).integers(0, N, 48), [N - 1, N - 37]])
-    z = hi[rows] @ wi[:V].T
-    rl, rdz = O.softmax_cross_entropy(z, labels[rows])
-    rdz = rdz * len(rows) / N          # oracle normalised by the sample size
-    gl = losses.cpu().numpy()[rows]
-    assert rel(gl, rl) < 1e-3
-    gdz = logits[torch.from_numpy(rows).cuda()].float().cpu().numpy()
+    hi = S.bf16_round(hidden).astype(np.float32)
+    wi = S.bf16_round(wte)[:V].astype(np.float32)
+    rows = np.unique(np.concatenate([rng(1).integers(0, N, 48), [0, N - 1, N - 37]]))
+    vrows = np.unique(np.concatenate([rng(2).integers(0, V, 60), [0, V - 1], labels[rows[:2]]]))
+    rl = np.empty(N)
+    rdwte = np.zeros((len(vrows), C))
+    rdz, rdh = {}, {}
+    chunk = 2048
+    for r0 in range(0, N, chunk):
+        r1 = min(N, r0 + chunk)
+        l, dz = O.softmax_cross_entropy(hi[r0:r1] @ wi.T, labels[r0:r1])
+        dz = dz.astype(np.float64) * ((r1 - r0) / N)        # chunk mean -> share of the mean over N rows
+        rl[r0:r1] = l
+        rdwte += dz[:, vrows].T @ hi[r0:r1].astype(np.float64)
+        for i in rows[(rows >= r0) & (rows < r1)]:
+            rdz[i] = dz[i - r0]
+            rdh[i] = dz[i - r0] @ wi.astype(np.float64)
+    assert rel(losses.cpu().numpy(), rl) < 1e-3
+    trows = torch.from_numpy(rows).cuda()
+    gdz = logits[trows].float().cpu().numpy()
     assert np.all(gdz[:, V:] == 0)
-    assert rel(gdz[:, :V], rdz) < 1e-2
-    assert rel(d_hidden[torch.from_numpy(rows).cuda()].float().cpu().numpy(), rdz @ wi[:V]) < 1e-2
+    assert rel(gdz[:, :V], np.stack([rdz[i] for i in rows])) < 1e-2
+    assert rel(d_hidden[trows].float().cpu().numpy(), np.stack([rdh[i] for i in rows])) < 1e-2
     dw = d_wte.cpu().numpy().astype(np.float64)
     assert np.all(dw[V:] == 0)
-    assert np.abs(dw.sum(0)).max() < 1e-3 * np.abs(dw).sum(0).max()
+    assert rel(dw[vrows], rdwte) < 1e-2
+    for j, v in enumerate(vrows[:8]):            # and row by row
+        assert rel(dw[v], rdwte[j]) < 3e-2, v
     assert np.isfinite(dw).all()
 
 

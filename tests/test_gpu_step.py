@@ -104,6 +104,113 @@ def test_mid_bf16_step_parity():
     compare_step(c, BF16, params, tok, tgt, ADAM_124, np.float32, gtol=3e-2, ltol=1e-2, ptol=1e-2)
 
 
+# Two-layer models at each GPT-2 size's full width and benchmark batch
+# (T = 1024): every GEMM, attention and memory-bound kernel instantiation the
+# full-depth step launches (the GEMM shapes do not depend on the depth; the
+# host test test_step_gemm_plans_reached_by_the_full_width_tests compares the
+# plans) runs here and is compared with the oracle.
+FULL_WIDTH = {
+    "124m": dict(V=50257, Vp=50304, maxT=1024, L=2, H=12, C_=768, B=24, T=1024),
+    "350m": dict(V=50257, Vp=50304, maxT=1024, L=2, H=16, C_=1024, B=16, T=1024),
+    "1.6b": dict(V=50257, Vp=50304, maxT=1024, L=2, H=25, C_=1600, B=8, T=1024),
+}
+ORACLE_ROWS = 4          # batch rows per oracle chunk (bounds the oracle's host memory)
+
+
+@pytest.mark.parametrize("size", ["124m", "350m", "1.6b"])
+def test_full_width_step_parity(size):
+    """One bf16 training step (forward, backward, AdamW) at full width and
+    full batch against the float32 oracle at the bf16 tolerances: loss, every
+    parameter gradient tensor, and the post-AdamW parameters.  The oracle
+    runs the batch in chunks of ORACLE_ROWS rows and combines them with
+    oracle.gpt2_step_accumulated: the gradient of the mean loss over the
+    batch is the mean of the chunks' gradients (equal chunks), the identity
+    the oracle's accumulation is pinned to."""
+    c = FULL_WIDTH[size]
+    say(size, "full-width two-layer bf16 step, B =", c["B"])
+    adam = ADAM_1600 if size == "1.6b" else ADAM_124
+    params = S.random_params(c["V"], c["Vp"], c["maxT"], c["L"], c["C_"], seed=901, perturbed=True)
+    tok, tgt = S.zipf_batch(c["B"], c["T"], seed=902)
+    model, cfg = make(c, BF16)
+    loss, grads, after = lib_step(model, cfg, params, tok, tgt, adam)
+    model.close()
+    say("library loss", loss)
+    assert np.all(grads["wte"][c["V"]:] == 0.0)
+    assert np.array_equal(after["wte"][c["V"]:], params["wte"][c["V"]:].astype(np.float32))
+    op = to_oracle(params, c, np.float32)
+    micro = [(tok[r:r + ORACLE_ROWS], tgt[r:r + ORACLE_ROWS]) for r in range(0, c["B"], ORACLE_ROWS)]
+    losses, ograds, _, oafter, _ = O.gpt2_step_accumulated(op, micro, ocfg(c), None, adam["lr"], adam["beta1"],
+                                                           adam["beta2"], adam["eps"], adam["weight_decay"], 1)
+    oloss = float(np.mean(losses))
+    say("oracle loss", oloss)
+    assert abs(loss - oloss) / abs(oloss) <= 1e-2
+    worst = {name: rel(grads[name][: c["V"]] if name == "wte" else grads[name], g) for name, g in ograds.items()}
+    say("grad rel L2", {k: f"{v:.2e}" for k, v in worst.items()})
+    assert all(v <= 3e-2 for v in worst.values()), worst
+    flat_a = np.concatenate([(after[k][: c["V"]] if k == "wte" else after[k]).reshape(-1) for k in oafter])
+    flat_o = np.concatenate([oafter[k].reshape(-1) for k in oafter])
+    prel = rel(flat_a, flat_o)
+    say("post-AdamW params rel L2", prel)
+    assert prel <= 1e-2
+
+
+def test_graph_step_bit_identical_to_eager():
+    """Three training steps replayed from one captured HIP graph equal three
+    eager steps bit for bit (losses and parameters after every step), with
+    eager work (the next batch copied into the graph's input buffers) and a
+    synchronisation between replays."""
+    torch = torch_mod()
+    c = MID
+    say("graph vs eager, 124M widths, L = 2, B = 4")
+    stream = torch.cuda.Stream()
+    batches = [S.zipf_batch(c["B"], c["T"], seed=950 + i) for i in range(3)]
+    lr, b1, b2, eps, wd = 6e-4, 0.9, 0.999, 1e-8, 0.1
+    with torch.cuda.stream(stream):
+        cfg = lib.make_config(c["V"], c["Vp"], c["maxT"], c["L"], c["H"], c["C_"], c["B"], c["T"], BF16)
+        eager = lib.Model(cfg, seed=77, stream=stream)
+        ref = []
+        for t, (tok, tgt) in enumerate(batches, 1):
+            loss = eager.forward(dev_i32(tok), dev_i32(tgt))
+            eager.backward()
+            eager.adamw_step(lr, b1, b2, eps, wd, t)
+            ref.append((loss, eager.get_params()))
+        eager.close()
+        graphed = lib.Model(cfg, seed=77, stream=stream)
+        tok_buf = torch.zeros((c["B"], c["T"]), dtype=torch.int32, device="cuda")
+        tgt_buf = torch.zeros((c["B"], c["T"]), dtype=torch.int32, device="cuda")
+        graphed.graph_capture(tok_buf, tgt_buf)
+        for t, (tok, tgt) in enumerate(batches, 1):
+            tok_buf.copy_(dev_i32(tok))
+            tgt_buf.copy_(dev_i32(tgt))
+            loss = graphed.graph_step(lr, b1, b2, eps, wd, t)
+            p = graphed.get_params()
+            say("step", t, "graph loss", loss, "eager loss", ref[t - 1][0])
+            assert loss == ref[t - 1][0]
+            assert np.array_equal(p, ref[t - 1][1])
+        graphed.close()
+    stream.synchronize()
+
+
+def test_graph_capture_errors():
+    torch = torch_mod()
+    c = TINY
+    model, cfg = make(c, FP32)          # the null stream cannot be captured
+    tok = dev_i32(np.zeros((c["B"], c["T"])))
+    with pytest.raises(lib.Gpt2Error, match="invalid argument"):
+        model.graph_capture(tok, tok)
+    with pytest.raises(lib.Gpt2Error, match="call order"):
+        model.graph_step(1e-3, 0.9, 0.999, 1e-8, 0.0, 1)
+    model.close()
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        model = lib.Model(cfg, seed=1, stream=stream)
+        model.timing_enable("adamw", True)
+        with pytest.raises(lib.Gpt2Error, match="call order"):
+            model.graph_capture(tok, tok)
+        model.close()
+    stream.synchronize()
+
+
 def test_tiny_fp32_three_steps():
     """Three consecutive steps (AdamW moments and bias correction carried)."""
     say("tiny fp32 three steps")
