@@ -63,6 +63,12 @@ def load():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise Gpt2Error(f"{LIB_PATH} is missing: build it first (python -m gpt_transformer_lm_amd.build)")
+    # torch first: its wheel carries its own HIP runtime (same soname as the
+    # system one the library is linked against).  Loaded after torch, the
+    # library binds to torch's runtime, so device pointers and streams are
+    # shared; loaded before, a second runtime would be mapped beside torch's
+    # and the library's kernels would not see torch's device state.
+    import torch  # noqa: F401
     lib = C.CDLL(LIB_PATH)
     vp, i32, i64, sz, f32 = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t, C.c_float
     cfgp = C.POINTER(Gpt2Config)
