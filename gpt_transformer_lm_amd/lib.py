@@ -116,6 +116,7 @@ def load():
         "gpt2_op_attention_forward": (C.c_int, [C.c_int] * 5 + [vp, vp, vp, vp]),
         "gpt2_op_attention_backward_workspace_bytes": (sz, [C.c_int] * 4),
         "gpt2_op_attention_backward": (C.c_int, [C.c_int] * 5 + [vp, vp, vp, vp, vp, vp, sz, vp]),
+        "gpt2_op_attention_backward_noalloc": (C.c_int, [C.c_int] * 5 + [vp, vp, vp, vp, vp, vp]),
         "gpt2_op_softmax_xent": (C.c_int, [C.c_int] * 4 + [vp, vp, vp, f32, vp]),
         "gpt2_op_classifier_workspace_bytes": (sz, [C.c_int] * 4),
         "gpt2_op_classifier_fwd_bwd": (C.c_int, [C.c_int] * 5 + [vp] * 7 + [vp, sz, vp]),
@@ -147,6 +148,7 @@ def exported_symbols():
         "gpt2_op_layernorm_forward", "gpt2_op_layernorm_backward_workspace_bytes",
         "gpt2_op_layernorm_backward", "gpt2_op_attention_forward",
         "gpt2_op_attention_backward_workspace_bytes", "gpt2_op_attention_backward",
+        "gpt2_op_attention_backward_noalloc",
         "gpt2_op_softmax_xent", "gpt2_op_classifier_workspace_bytes", "gpt2_op_classifier_fwd_bwd",
         "gpt2_op_encoder_forward", "gpt2_op_encoder_backward_workspace_bytes",
         "gpt2_op_encoder_backward", "gpt2_op_adamw",
@@ -393,6 +395,11 @@ def attention_backward(dtype, B, T, H, hd, qkv, out, dout, lse, dqkv, stream=Non
     check(lib.gpt2_op_attention_backward(dtype, B, T, H, hd, ptr(qkv), ptr(out), ptr(dout), ptr(lse), ptr(dqkv),
                                          ptr(ws), ws.numel(), _stream_ptr(stream)), "attention_backward")
     return ws
+
+
+def attention_backward_noalloc(dtype, B, T, H, hd, qkv, out, dout, lse, dqkv, stream=None):
+    check(load().gpt2_op_attention_backward_noalloc(dtype, B, T, H, hd, ptr(qkv), ptr(out), ptr(dout), ptr(lse),
+                                                    ptr(dqkv), _stream_ptr(stream)), "attention_backward_noalloc")
 
 
 def softmax_xent(dtype, logits, labels, losses, V, dscale, stream=None):

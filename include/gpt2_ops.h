@@ -131,6 +131,25 @@ int gpt2_op_attention_backward(int dtype, int B, int T, int H, int hd, const voi
                                const void* out, const void* dout, const float* lse, void* dqkv,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Allocation-free attention backward, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): gpt2_op_attention_backward with the same kernels
+ * and results, but its scratch (rowsum(dO * O) and the base-2 log-sum-exp,
+ * two floats per (b, h, t) row) lives in a library-owned device array of
+ * GPT2_NOALLOC_SCRATCH_BYTES per GPU (held from the first call on a device
+ * until the process ends) instead of a workspace argument.  Shapes whose
+ * scratch exceeds that (B*H*T above about one million rows) are rejected with
+ * GPT2_E_INVALID_ARG before anything is enqueued.  The call allocates nothing
+ * (no hipMalloc, no allocating library routine).  Every call on one GPU uses
+ * that GPU's single array: calls that overlap on one GPU (other streams or
+ * threads) race on it and must be serialised by the caller.  Every scratch
+ * element a call reads is written earlier in the same call, so nothing needs
+ * clearing between calls. */
+#define GPT2_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int gpt2_op_attention_backward_noalloc(int dtype, int B, int T, int H, int hd, const void* qkv,
+                                       const void* out, const void* dout, const float* lse, void* dqkv,
+                                       void* stream);
+
 /* Fused softmax cross-entropy in place over logits [N, Vp] T (columns >= V
  * are padding, masked to -inf):  losses [N] f32 = logsumexp - logit at the
  * label; logits <- (softmax - onehot(label)) * dscale, 0 in padded columns.
