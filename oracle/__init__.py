@@ -14,6 +14,15 @@ from .gpt2_oracle import (  # noqa: F401
     layernorm_backward,
     gelu_tanh,
     gelu_tanh_backward,
+    relu2,
+    relu2_backward,
+    rms_norm_forward,
+    rms_norm_backward,
+    rope_angles,
+    rope_forward,
+    rope_backward,
+    RMS_EPS,
+    ROPE_BASE,
     causal_attention_forward,
     causal_attention_backward,
     softmax_cross_entropy,

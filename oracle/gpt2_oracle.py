@@ -65,6 +65,10 @@ class OracleConfig:
     num_layers: int      # L
     num_heads: int       # H
     channels: int        # C
+    # architecture variants (see "Architecture variants" below); all off is GPT-2
+    relu2: bool = False
+    qk_norm: bool = False
+    rope: bool = False
 
     @property
     def head_dim(self) -> int:
@@ -230,6 +234,75 @@ def adamw_update(theta, g, m, v, lr, beta1, beta2, eps, wd, t):
 
 
 # --------------------------------------------------------------------------
+# Architecture variants
+# --------------------------------------------------------------------------
+# The page "NanoGPT (124M) in 90 seconds" (section "How it works", item
+# "Architecture Changes") names rotary embeddings, QK-Norm and ReLU^2 and
+# gives no formula.  The readings here are the plainest ones:
+# * ReLU^2: the MLP activation relu(u)^2 in place of GELU-tanh.
+# * QK-Norm: q and k of every head divided by their root mean square over the
+#   head dimension, sqrt(mean(x^2) + eps) with eps = 1e-6, no learned gain;
+#   the attention scale stays 1/sqrt(hd).
+# * Rotary embedding (Su et al., RoFormer, 2021): at position t the pair of
+#   head coordinates (i, i + hd/2), i < hd/2, is rotated by the angle
+#   t * 10000^(-2i/hd): (a, b) -> (a cos - b sin, a sin + b cos).  It acts on
+#   q and k after QK-Norm; the learned position table is then not added to
+#   the token embedding (it stays a parameter, with zero gradient).
+
+RMS_EPS = 1e-6
+ROPE_BASE = 10000.0
+
+
+def relu2(u):
+    """relu(u)^2."""
+    r = np.maximum(u, 0.0)
+    return r * r
+
+
+def relu2_backward(u, dg):
+    """dg * d/du relu(u)^2 = dg * 2 relu(u)."""
+    return dg * (2.0 * np.maximum(u, 0.0))
+
+
+def rms_norm_forward(x, eps=RMS_EPS):
+    """y = x / sqrt(mean(x^2) + eps) over the last axis; returns y and the
+    cache (y, r) with r = 1 / sqrt(mean(x^2) + eps)."""
+    r = 1.0 / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps)
+    y = x * r
+    return y, (y, r)
+
+
+def rms_norm_backward(dy, cache):
+    """Gradient of rms_norm_forward: with y = x r and dr/dx = -r^3 x / n,
+    dx = r (dy - y mean(dy * y))."""
+    y, r = cache
+    return r * (dy - y * (dy * y).mean(axis=-1, keepdims=True))
+
+
+def rope_angles(T, hd, base=ROPE_BASE):
+    """[T, hd/2] angles t * base^(-2i/hd)."""
+    i = np.arange(hd // 2, dtype=np.float64)
+    theta = base ** (-2.0 * i / hd)
+    return np.arange(T, dtype=np.float64)[:, None] * theta[None, :]
+
+
+def rope_forward(x, ang):
+    """Rotate the (i, i + hd/2) coordinate pairs of x [..., T, hd] by ang [T, hd/2]."""
+    h = x.shape[-1] // 2
+    a, b = x[..., :h], x[..., h:]
+    c, s = np.cos(ang), np.sin(ang)
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+
+
+def rope_backward(dy, ang):
+    """Gradient of rope_forward: the transposed (inverse) rotation of dy."""
+    h = dy.shape[-1] // 2
+    da, db = dy[..., :h], dy[..., h:]
+    c, s = np.cos(ang), np.sin(ang)
+    return np.concatenate([da * c + db * s, -da * s + db * c], axis=-1)
+
+
+# --------------------------------------------------------------------------
 # Whole model
 # --------------------------------------------------------------------------
 
@@ -254,32 +327,43 @@ def gpt2_forward(params, tokens, targets, cfg: OracleConfig):
     Returns (mean_loss or None, per-position losses or None, logits, cache)."""
     B, T = tokens.shape
     C, H, L = cfg.channels, cfg.num_heads, cfg.num_layers
-    x = encoder_forward(params["wte"], params["wpe"], tokens)
+    if cfg.rope:     # positions enter through the rotation only
+        x = params["wte"][tokens]
+    else:
+        x = encoder_forward(params["wte"], params["wpe"], tokens)
+    ang = rope_angles(T, C // H) if cfg.rope else None
     layers = []
     for l in range(L):
         ln1, ln1_c = layernorm_forward(x, params["ln1w"][l], params["ln1b"][l])
         qkv = ln1 @ params["qkvw"][l].T + params["qkvb"][l]
         att = np.empty_like(x)
-        probs = []
+        probs, qk = [], []
         for b in range(B):
             q = _split_heads(qkv[b, :, 0:C], H)
             k = _split_heads(qkv[b, :, C:2 * C], H)
             v = _split_heads(qkv[b, :, 2 * C:3 * C], H)
+            qc = kc = None
+            if cfg.qk_norm:
+                q, qc = rms_norm_forward(q)
+                k, kc = rms_norm_forward(k)
+            if cfg.rope:
+                q, k = rope_forward(q, ang), rope_forward(k, ang)
             o, p = causal_attention_forward(q, k, v)
             att[b] = _merge_heads(o)
             probs.append(p)
+            qk.append((q, k, qc, kc))
         h = x + att @ params["attprojw"][l].T + params["attprojb"][l]
         ln2, ln2_c = layernorm_forward(h, params["ln2w"][l], params["ln2b"][l])
         u = ln2 @ params["fcw"][l].T + params["fcb"][l]
-        g = gelu_tanh(u)
+        g = relu2(u) if cfg.relu2 else gelu_tanh(u)
         x_next = h + g @ params["fcprojw"][l].T + params["fcprojb"][l]
-        layers.append(dict(x=x, ln1=ln1, ln1_c=ln1_c, qkv=qkv, att=att,
+        layers.append(dict(x=x, ln1=ln1, ln1_c=ln1_c, qkv=qkv, att=att, qk=qk,
                            probs=probs, h=h, ln2=ln2, ln2_c=ln2_c, u=u, g=g))
         x = x_next
     lnf, lnf_c = layernorm_forward(x, params["lnfw"], params["lnfb"])
     logits = lnf.reshape(B * T, C) @ params["wte"].T
     cache = dict(tokens=tokens, layers=layers, xL=x, lnf=lnf, lnf_c=lnf_c,
-                 logits=logits, B=B, T=T)
+                 logits=logits, B=B, T=T, ang=ang)
     if targets is None:
         return None, None, logits.reshape(B, T, -1), cache
     losses, dz = softmax_cross_entropy(logits, targets.reshape(-1))
@@ -304,7 +388,7 @@ def gpt2_backward(params, cache, cfg: OracleConfig):
         dg = dx @ params["fcprojw"][l]
         grads["fcprojw"][l] = _wgrad(dx, c["g"])
         grads["fcprojb"][l] = dx.sum(axis=(0, 1))
-        du = gelu_tanh_backward(c["u"], dg)
+        du = relu2_backward(c["u"], dg) if cfg.relu2 else gelu_tanh_backward(c["u"], dg)
         grads["fcw"][l] = _wgrad(du, c["ln2"])
         grads["fcb"][l] = du.sum(axis=(0, 1))
         dln2 = du @ params["fcw"][l]
@@ -316,11 +400,14 @@ def gpt2_backward(params, cache, cfg: OracleConfig):
         grads["attprojb"][l] = dh.sum(axis=(0, 1))
         dqkv = np.empty_like(c["qkv"])
         for b in range(B):
-            q = _split_heads(c["qkv"][b, :, 0:C], H)
-            k = _split_heads(c["qkv"][b, :, C:2 * C], H)
+            q, k, qc, kc = c["qk"][b]          # as the attention saw them
             v = _split_heads(c["qkv"][b, :, 2 * C:3 * C], H)
             do = _split_heads(datt[b], H)
             dq, dk, dv = causal_attention_backward(do, q, k, v, c["probs"][b])
+            if cfg.rope:
+                dq, dk = rope_backward(dq, cache["ang"]), rope_backward(dk, cache["ang"])
+            if cfg.qk_norm:
+                dq, dk = rms_norm_backward(dq, qc), rms_norm_backward(dk, kc)
             dqkv[b, :, 0:C] = _merge_heads(dq)
             dqkv[b, :, C:2 * C] = _merge_heads(dk)
             dqkv[b, :, 2 * C:3 * C] = _merge_heads(dv)
@@ -331,7 +418,8 @@ def gpt2_backward(params, cache, cfg: OracleConfig):
         dx = dh + dx_ln
     dwte, dwpe = encoder_backward(dx, cache["tokens"], cfg.vocab_size, cfg.max_seq_len)
     grads["wte"] += dwte
-    grads["wpe"] += dwpe
+    if not cfg.rope:         # with rotary embeddings the position table is not used
+        grads["wpe"] += dwpe
     return grads
 
 
