@@ -2,10 +2,12 @@
 AdamW) through the HIP C-ABI library on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--config 124m|350m|1.6b]
-                    [--accum M] [--max-grad-norm X]
+                    [--accum M] [--max-grad-norm X] [--graph] [--arch relu2,qk_norm,rope]
 
 (--accum / --max-grad-norm time updates over M accumulated micro-batches with
-global-norm clipping; the defaults time the plain step of the headline metric.)
+global-norm clipping; --graph replays each step from one captured HIP graph;
+--arch turns on architecture variants of the block; the defaults time the
+plain step of the headline metric.)
 
 Prints one JSON line.  value = tokens/s of whole training steps (inputs
 already resident in HBM), MFU against the bf16 dense MFMA peak, the roofline
@@ -61,7 +63,7 @@ KERNEL_OF = {
     "attn_bwd_dq": "attn_bwd_dq_mfma_kernel", "attn_bwd_dot": "attn_bwd_dot_kernel",
     "softmax_xent": "softmax_xent_bf16_kernel", "ln_fwd": "ln_fwd_half_kernel", "ln_bwd": "ln_bwd_kernel",
     "encoder_fwd": "encoder_fwd_kernel", "adamw": "adamw_kernel", "weight_transpose": "transpose_bf16_kernel",
-    "grad_norm": "grad_sumsq_kernel",
+    "grad_norm": "grad_sumsq_kernel", "qk_fwd": "qk_fwd_kernel", "qk_bwd": "qk_bwd_kernel",
 }
 for _s in GEMM_SITES:
     KERNEL_OF[_s] = "gemm_bf16_dma_kernel"
@@ -140,6 +142,8 @@ def main():
                     help="micro-batches of B x T accumulated per update (gradient of their mean loss)")
     ap.add_argument("--max-grad-norm", type=float, default=0.0,
                     help="global-norm gradient clipping threshold (0: off)")
+    ap.add_argument("--arch", default="",
+                    help="comma-separated architecture variants: relu2, qk_norm, rope (default: GPT-2 as published)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each timed step from one captured HIP graph (plain step only)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -157,7 +161,13 @@ def main():
 
     c = CONFIGS[args.config]
     B, T = c["B"], c["T"]
-    cfg = lib.make_config(c["V"], c["Vp"], c["maxT"], c["L"], c["H"], c["C"], B, T, lib.GPT2_BF16)
+    flag_of = {"relu2": lib.GPT2_ARCH_RELU2, "qk_norm": lib.GPT2_ARCH_QK_NORM, "rope": lib.GPT2_ARCH_ROPE}
+    arch = [a for a in args.arch.split(",") if a]
+    if any(a not in flag_of for a in arch):
+        print(f"--arch takes {sorted(flag_of)}", file=sys.stderr)
+        sys.exit(2)
+    cfg = lib.make_config(c["V"], c["Vp"], c["maxT"], c["L"], c["H"], c["C"], B, T, lib.GPT2_BF16,
+                          sum(flag_of[a] for a in set(arch)))
     torch.cuda.init()
     K = max(args.accum, 1)
     plain = K == 1 and args.max_grad_norm <= 0
@@ -281,7 +291,8 @@ def main():
                                f"B={B}, T={T}, vocab 50257 padded to 50304"
                                + ("" if plain else f", {K} accumulated micro-batches per update, global-norm "
                                                    f"clipping at {args.max_grad_norm}")
-                               + (", each step one HIP graph replay" if args.graph else ""),
+                               + (", each step one HIP graph replay" if args.graph else "")
+                               + (f", variants {'+'.join(sorted(set(arch)))}" if arch else ""),
                    "global_batch": K * B, "seq_len": T, "parallelism": "single GPU"},
         "mfu": mfu,
         "model_flops_per_token": ftok,

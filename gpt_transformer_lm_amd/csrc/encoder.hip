@@ -37,9 +37,11 @@ __global__ void encoder_fwd_kernel(int BT, int T_, int C, const int32_t* __restr
   tok = tok < 0 ? 0 : (tok >= Vrows ? Vrows - 1 : tok);   // memory safety only
   float a[8], b[8];
   Chunk8<T>::load(wte + (size_t)tok * C + ch * 8, a);
-  Chunk8<T>::load(wpe + (size_t)t * C + ch * 8, b);
+  if (wpe) {
+    Chunk8<T>::load(wpe + (size_t)t * C + ch * 8, b);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) a[e] += b[e];
+    for (int e = 0; e < 8; ++e) a[e] += b[e];
+  }
   Chunk8<T>::store(out + (size_t)p * C + ch * 8, a);
 }
 
@@ -179,7 +181,7 @@ int pos_bits(int n) {
 
 int encoder_forward(int dtype, int B, int T_, int C, int vocab_rows, const int32_t* tokens, const void* wte,
                     const void* wpe, void* out, hipStream_t stream) {
-  if (B < 0 || T_ < 0 || C <= 0 || C % 8 || vocab_rows <= 0 || !tokens || !wte || !wpe || !out)
+  if (B < 0 || T_ < 0 || C <= 0 || C % 8 || vocab_rows <= 0 || !tokens || !wte || !out)
     return gpt2_internal_fail(1, "encoder_forward: bad arguments");
   const int BT = B * T_;
   if (BT == 0) return 0;
@@ -232,7 +234,7 @@ int encoder_sort_keys(int n, int vocab_rows, const int32_t* tokens, uint32_t* so
 int encoder_backward_sorted(int B, int T_, int C, const uint32_t* sorted, const float* dx0, float* dwte,
                             float* dwpe, bool accumulate_wpe, void* workspace, size_t workspace_bytes,
                             hipStream_t stream) {
-  if (B < 0 || T_ < 0 || C <= 0 || !sorted || !dx0 || !dwte || !dwpe)
+  if (B < 0 || T_ < 0 || C <= 0 || !sorted || !dx0 || !dwte)
     return gpt2_internal_fail(1, "encoder_backward: bad arguments");
   const int n = B * T_;
   if (n == 0) return 0;
@@ -243,9 +245,11 @@ int encoder_backward_sorted(int B, int T_, int C, const uint32_t* sorted, const 
   const int npieces = (int)ceil_div64(n, kPiece);
   float* pcont = (float*)workspace;
   float* pown = pcont + (size_t)npieces * C;
-  hipLaunchKernelGGL(encoder_bwd_wpe_kernel, dim3((unsigned)ceil_div64((int64_t)T_ * C, 256)), dim3(256), 0,
-                     stream, B, T_, C, dx0, dwpe, accumulate_wpe);
-  GPT2_LAUNCH_CHECK();
+  if (dwpe) {
+    hipLaunchKernelGGL(encoder_bwd_wpe_kernel, dim3((unsigned)ceil_div64((int64_t)T_ * C, 256)), dim3(256), 0,
+                       stream, B, T_, C, dx0, dwpe, accumulate_wpe);
+    GPT2_LAUNCH_CHECK();
+  }
   hipLaunchKernelGGL(encoder_bwd_pieces_kernel, dim3(npieces), dim3(256), 0, stream, n, C, shift, sorted, dx0,
                      dwte, pcont, pown);
   GPT2_LAUNCH_CHECK();

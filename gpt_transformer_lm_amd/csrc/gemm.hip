@@ -81,7 +81,7 @@ __device__ __forceinline__ void epilogue_store(const EpiArgs& e, int m, int n, f
   if constexpr (EPI == EPI_WGRAD) {
     e.partial[((size_t)z * e.M + m) * (size_t)e.N + n] = v;
   } else {
-    if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_RES || EPI == EPI_BIAS_GELU_D)
+    if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_RES || EPI == EPI_BIAS_GELU_D || EPI == EPI_BIAS_RELU2_D)
       v += to_f32(reinterpret_cast<const T*>(e.bias)[n]);
     if constexpr (EPI == EPI_BIAS_RES)
       v += to_f32(reinterpret_cast<const T*>(e.aux_in)[(size_t)m * e.ld_aux + n]);
@@ -90,6 +90,11 @@ __device__ __forceinline__ void epilogue_store(const EpiArgs& e, int m, int n, f
       gelu_tanh_and_grad_f(v, g, d);
       reinterpret_cast<T*>(e.aux_out)[(size_t)m * e.ldc + n] = from_f32<T>(d);
       v = g;
+    }
+    if constexpr (EPI == EPI_BIAS_RELU2_D) {
+      const float r = fmaxf(v, 0.0f);
+      reinterpret_cast<T*>(e.aux_out)[(size_t)m * e.ldc + n] = from_f32<T>(2.0f * r);
+      v = r * r;
     }
     if constexpr (EPI == EPI_MUL) v *= to_f32(reinterpret_cast<const T*>(e.aux_in)[(size_t)m * e.ld_aux + n]);
     reinterpret_cast<T*>(e.C)[(size_t)m * e.ldc + n] = from_f32<T>(v);
@@ -127,6 +132,16 @@ __device__ __forceinline__ void epilogue_vec8_final(const EpiArgs& e, int m, int
       float d[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) gelu_tanh_and_grad_f(v[i], v[i], d[i]);
+      Chunk8<bf16>::store(reinterpret_cast<bf16*>(e.aux_out) + (size_t)m * e.ldc + n, d);
+    }
+    if constexpr (EPI == EPI_BIAS_RELU2_D) {
+      float d[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float r = fmaxf(v[i], 0.0f);
+        d[i] = 2.0f * r;
+        v[i] = r * r;
+      }
       Chunk8<bf16>::store(reinterpret_cast<bf16*>(e.aux_out) + (size_t)m * e.ldc + n, d);
     }
     Chunk8<bf16>::store(reinterpret_cast<bf16*>(e.C) + (size_t)m * e.ldc + n, v);
@@ -314,7 +329,7 @@ __global__ __launch_bounds__(64 * gemm_waves(BM, BN, EPI, KGS))
 __attribute__((amdgpu_waves_per_eu(gemm_waves(BM, BN, EPI, KGS) / 4,
                                    (BM == 128 && BN == 128) ? 2 : gemm_waves(BM, BN, EPI, KGS) / 4)))
 void gemm_bf16_dma_kernel(MfmaArgs p) {
-  constexpr bool HAS_BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RES || EPI == EPI_BIAS_GELU_D;
+  constexpr bool HAS_BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RES || EPI == EPI_BIAS_GELU_D || EPI == EPI_BIAS_RELU2_D;
   constexpr bool HAS_AUX = epi_has_aux(EPI);
   using S = DmaShape<BM, BN, EPI, KGS>;
   using TA = DmaTile<BM, A_KMAJ, S::WAVES>;
@@ -797,7 +812,8 @@ Plan plan_bf16(int epi, int M, int N, int K, bool a_kmajor, bool b_kmajor) {
   // Short-K products with a bias or GELU epilogue and a wide N (QKV, fc
   // forward): the 8-wave 256x256 tile (measured 3-5% faster than 128x128 at
   // M = 24576, K = 768).
-  if (!may_split && (epi == EPI_BIAS_GELU_D || epi == EPI_BIAS) && a_kmajor && b_kmajor && M >= 2048 &&
+  if (!may_split && (epi == EPI_BIAS_GELU_D || epi == EPI_BIAS_RELU2_D || epi == EPI_BIAS) && a_kmajor && b_kmajor &&
+      M >= 2048 &&
       N >= 2048 && K <= 1024) {
     best = Plan{256, 256, 1, kt * kBK};
     return best;
@@ -946,11 +962,12 @@ int gemm(const GemmDesc& d, hipStream_t stream) {
   const bool wgrad = d.epi == EPI_WGRAD;
   if (wgrad && !d.out32) return gpt2_internal_fail(1, "gemm: WGRAD needs out32");
   if (!wgrad && !d.C) return gpt2_internal_fail(1, "gemm: missing C");
-  if ((d.epi == EPI_BIAS || d.epi == EPI_BIAS_RES || d.epi == EPI_BIAS_GELU_D) && !d.bias)
+  if ((d.epi == EPI_BIAS || d.epi == EPI_BIAS_RES || d.epi == EPI_BIAS_GELU_D || d.epi == EPI_BIAS_RELU2_D) &&
+      !d.bias)
     return gpt2_internal_fail(1, "gemm: missing bias");
   if ((d.epi == EPI_BIAS_RES || d.epi == EPI_MUL) && !d.aux_in)
     return gpt2_internal_fail(1, "gemm: missing aux input");
-  if (d.epi == EPI_BIAS_GELU_D && !d.aux_out)
+  if ((d.epi == EPI_BIAS_GELU_D || d.epi == EPI_BIAS_RELU2_D) && !d.aux_out)
     return gpt2_internal_fail(1, "gemm: missing U output");
 
   const int splits = gemm_splits(d.dtype, d.epi, d.M, d.N, d.K, d.a_kmajor, d.b_kmajor);
@@ -1005,6 +1022,7 @@ int gemm(const GemmDesc& d, hipStream_t stream) {
       case EPI_BIAS: rc = dispatch_layout_bf16<EPI_BIAS>(d, a, pl, false, stream); break;
       case EPI_BIAS_RES: rc = dispatch_layout_bf16<EPI_BIAS_RES>(d, a, pl, false, stream); break;
       case EPI_BIAS_GELU_D: rc = dispatch_layout_bf16<EPI_BIAS_GELU_D>(d, a, pl, false, stream); break;
+      case EPI_BIAS_RELU2_D: rc = dispatch_layout_bf16<EPI_BIAS_RELU2_D>(d, a, pl, false, stream); break;
       case EPI_MUL: rc = dispatch_layout_bf16<EPI_MUL>(d, a, pl, false, stream); break;
       case EPI_WGRAD: rc = dispatch_layout_bf16<EPI_WGRAD>(d, a, pl, bias_grad, stream); break;
       default: return gpt2_internal_fail(1, "gemm: unknown epilogue %d", d.epi);
@@ -1033,6 +1051,7 @@ int gemm(const GemmDesc& d, hipStream_t stream) {
     case EPI_BIAS: rc = dispatch_layout_f32<EPI_BIAS>(d, a, 1, stream); break;
     case EPI_BIAS_RES: rc = dispatch_layout_f32<EPI_BIAS_RES>(d, a, 1, stream); break;
     case EPI_BIAS_GELU_D: rc = dispatch_layout_f32<EPI_BIAS_GELU_D>(d, a, 1, stream); break;
+    case EPI_BIAS_RELU2_D: rc = dispatch_layout_f32<EPI_BIAS_RELU2_D>(d, a, 1, stream); break;
     case EPI_MUL: rc = dispatch_layout_f32<EPI_MUL>(d, a, 1, stream); break;
     case EPI_WGRAD: rc = dispatch_layout_f32<EPI_WGRAD>(d, a, splits, stream); break;
     default: return gpt2_internal_fail(1, "gemm: unknown epilogue %d", d.epi);

@@ -40,10 +40,12 @@ inline void mark_end(int i, hipStream_t s) {
 //                Split over K into partial sums that a second kernel reduces
 //                in a fixed order (deterministic).
 //   BIAS_GELU_D  C = gelu_tanh(v + bias[n]);  U[m * ldc + n] = gelu_tanh'(v + bias[n])
+//   BIAS_RELU2_D C = relu(v + bias[n])^2;     U[m * ldc + n] = 2 relu(v + bias[n])
 //   MUL          C = v * U[m * ld_aux + n]
-//   (the step stores the GELU derivative in the forward, so the backward
-//   epilogue of the fc-proj dX is one multiply)
-enum Epi { EPI_STORE = 0, EPI_BIAS = 1, EPI_BIAS_RES = 2, EPI_WGRAD = 5, EPI_BIAS_GELU_D = 6, EPI_MUL = 7 };
+//   (the step stores the activation's derivative in the forward, so the
+//   backward epilogue of the fc-proj dX is one multiply)
+enum Epi { EPI_STORE = 0, EPI_BIAS = 1, EPI_BIAS_RES = 2, EPI_BIAS_RELU2_D = 3, EPI_WGRAD = 5, EPI_BIAS_GELU_D = 6,
+           EPI_MUL = 7 };
 
 struct GemmDesc {
   int dtype;            // F32 or BF16 (type of A, B, C, bias, R, U)
@@ -105,6 +107,18 @@ int attention_backward(int dtype, int B, int T, int H, int hd, const void* qkv, 
                        const void* dout, const float* lse, void* dqkv, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
 
+// ------------------------------------------------------------------ QK-Norm / rotary
+// In place on the q and k columns of qkv [BT, 3C] (hd = C / H): QK-Norm (RMS
+// normalisation per head, eps 1e-6; rstd [BT, 2H] fp32 saved, q heads then k
+// heads per token) and the rotary embedding with cos / sin table cs
+// [maxT][hd/2] (position t = row mod T).  The backward works in place on
+// dqkv, reading the transformed values from qkv.
+int rope_table(int maxT, int hd, float2* cs, hipStream_t stream);
+int qk_transform_forward(int dtype, int BT, int T, int H, int hd, void* qkv, float* rstd, const float2* cs,
+                         bool norm, bool rope, hipStream_t stream);
+int qk_transform_backward(int dtype, int BT, int T, int H, int hd, const void* qkv, void* dqkv, const float* rstd,
+                          const float2* cs, bool norm, bool rope, hipStream_t stream);
+
 // ------------------------------------------------------------------ classifier
 // In place over logits [N, Vp] (row stride Vp): columns >= V are masked.
 // losses[i] = logsumexp_{j<V} z_ij - z_i,y_i;  z_ij <- (softmax_ij - [j==y_i]) * dscale
@@ -116,7 +130,8 @@ int sum_scaled(int n, const float* x, float scale, float* out, hipStream_t strea
 
 // ------------------------------------------------------------------ encoder
 // Token ids are clamped to [0, vocab_rows) for memory safety only (ids outside
-// [0, V) are undefined behaviour of the step).
+// [0, V) are undefined behaviour of the step).  wpe == NULL: no position
+// term (out = wte[tokens]); the backward skips dwpe when it is NULL.
 int encoder_forward(int dtype, int B, int T, int C, int vocab_rows, const int32_t* tokens,
                     const void* wte, const void* wpe, void* out, hipStream_t stream);
 size_t encoder_backward_workspace_bytes(int B, int T, int C);

@@ -183,9 +183,6 @@ int validate(const gpt2_config* c) {
                               (long long)BT);
   if (c->arch_flags & ~(GPT2_ARCH_RELU2 | GPT2_ARCH_QK_NORM | GPT2_ARCH_ROPE))
     return gpt2_internal_fail(GPT2_E_INVALID_ARG, "arch_flags 0x%x has unknown bits", (unsigned)c->arch_flags);
-  if (c->arch_flags)
-    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "arch_flags 0x%x: architecture variants not available",
-                              (unsigned)c->arch_flags);
   return GPT2_OK;
 }
 
@@ -202,8 +199,9 @@ struct Plan {
 
 struct LayerOffsets {
   size_t ln1, ln1_mean, ln1_rstd, qkv, atty, lse, h, ln2, ln2_mean, ln2_rstd;
-  size_t u;   // GELU'(fc pre-activation), written by the forward for the backward
-  size_t g;   // GELU(fc pre-activation)
+  size_t u;   // activation derivative at the fc pre-activation (GELU' or 2 relu), for the backward
+  size_t g;   // activation of the fc pre-activation (GELU or relu^2)
+  size_t qk_rstd;   // QK-Norm: 1 / rms of every q and k head vector [BT, 2H] fp32 (0 if unused)
 };
 
 struct Layout {
@@ -218,6 +216,7 @@ struct Layout {
   size_t adam_hp;                        // AdamW hyperparameters read by the update kernel
   size_t dres, dres_t, d_ln, d_big, d_qkv, scratch;
   size_t sorted_keys;                    // encoder-backward key sort (computed during the forward)
+  size_t rope_cs;                        // rotary embedding cos / sin table [maxT][hd/2] (0 if unused)
   size_t scratch_bytes;
   size_t total;
 };
@@ -280,6 +279,7 @@ void make_layout(const gpt2_config& c, Layout* lo) {
     o.ln2_rstd = p.alloc(BT * 4);
     o.u = p.alloc(BT * 4 * C * es);
     o.g = p.alloc(BT * 4 * C * es);
+    o.qk_rstd = (c.arch_flags & GPT2_ARCH_QK_NORM) ? p.alloc((size_t)BT * 2 * c.num_heads * 4) : 0;
   }
   lo->lnf = p.alloc(BT * C * es);
   lo->lnf_mean = p.alloc(BT * 4);
@@ -295,6 +295,9 @@ void make_layout(const gpt2_config& c, Layout* lo) {
   lo->d_big = p.alloc(BT * 4 * C * es);
   lo->d_qkv = p.alloc(BT * 3 * C * es);
   lo->sorted_keys = p.alloc(BT * 4);
+  lo->rope_cs = (c.arch_flags & GPT2_ARCH_ROPE)
+                    ? p.alloc((size_t)c.max_seq_len * (c.channels / c.num_heads / 2) * sizeof(float2))
+                    : 0;
   lo->scratch_bytes = scratch_need(c);
   lo->scratch = p.alloc(lo->scratch_bytes);
   lo->total = p.total;
@@ -306,7 +309,7 @@ void make_layout(const gpt2_config& c, Layout* lo) {
 enum Site {
   S_QKV = 0, S_ATTPROJ, S_FC, S_FCPROJ, S_LOGITS, S_FCPROJ_DX, S_FCPROJ_DW, S_FC_DX, S_FC_DW,
   S_ATTPROJ_DX, S_ATTPROJ_DW, S_QKV_DX, S_QKV_DW, S_CLS_DX, S_CLS_DW, S_ATTN_FWD, S_ATTN_DKDV, S_ATTN_DQ,
-  S_ATTN_DOT, S_XENT, S_LN_FWD, S_LN_BWD, S_ENC_FWD, S_ADAMW, S_WT, S_GRAD_NORM, S_COUNT
+  S_ATTN_DOT, S_XENT, S_LN_FWD, S_LN_BWD, S_ENC_FWD, S_ADAMW, S_WT, S_GRAD_NORM, S_QK_FWD, S_QK_BWD, S_COUNT
 };
 
 struct SiteTimer {
@@ -369,6 +372,10 @@ struct gpt2_model {
     return grad() + lo.pt.off[i] + (int64_t)l * per;
   }
   int dt() const { return cfg.dtype; }
+  bool qk_norm() const { return (cfg.arch_flags & GPT2_ARCH_QK_NORM) != 0; }
+  bool rope() const { return (cfg.arch_flags & GPT2_ARCH_ROPE) != 0; }
+  bool relu2() const { return (cfg.arch_flags & GPT2_ARCH_RELU2) != 0; }
+  const float2* rope_cs() { return rope() ? at<float2>(lo.rope_cs) : nullptr; }
   size_t es() const { return cfg.dtype == GPT2_BF16 ? 2 : 4; }
   void* scratch() { return base + lo.scratch; }
 };
@@ -512,9 +519,12 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets, f
   const double act = (double)BT * C * es;  // bytes of one [BT, C] activation
   const double ln_fwd_bytes = 2.0 * act + BT * 8.0 + 2.0 * C * es;
   const double causal_mm = 2.0 * hd * ((double)T * (T + 1) / 2.0) * B * H;  // one causal T x T x hd product
-  RC(timed(m, S_ENC_FWD, 0.0, 3.0 * act, [&] {
-    return encoder_forward(dt, B, T, C, V, tok, m->param(0), m->param(1), m->at<char>(lo.resid[0]), s);
+  // with rotary embeddings positions enter through q and k only: no position table
+  RC(timed(m, S_ENC_FWD, 0.0, (m->rope() ? 2.0 : 3.0) * act, [&] {
+    return encoder_forward(dt, B, T, C, V, tok, m->param(0), m->rope() ? nullptr : m->param(1),
+                           m->at<char>(lo.resid[0]), s);
   }));
+  const double qk_bytes = 2.0 * (2.0 * act) + (m->qk_norm() ? (double)BT * 2 * H * 4 : 0.0);
   for (int l = 0; l < c.num_layers; ++l) {
     LayerOffsets& o = lo.layer[l];
     void* x = m->at<char>(lo.resid[l]);
@@ -524,6 +534,11 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets, f
     }));
     RC(run_gemm(m, S_QKV, fwd_desc(m, BT, 3 * C, C, m->at<char>(o.ln1), m->lparam(4, l), EPI_BIAS,
                                    m->at<char>(o.qkv), m->lparam(5, l), nullptr, nullptr)));
+    if (m->qk_norm() || m->rope())     // q and k transformed in place before the attention reads them
+      RC(timed(m, S_QK_FWD, 0.0, qk_bytes, [&] {
+        return qk_transform_forward(dt, BT, T, H, hd, m->at<char>(o.qkv), m->at<float>(o.qk_rstd), m->rope_cs(),
+                                    m->qk_norm(), m->rope(), s);
+      }));
     RC(timed(m, S_ATTN_FWD, 2.0 * causal_mm, 4.0 * act + (double)B * H * T * 4, [&] {
       return attention_forward(dt, B, T, H, hd, m->at<char>(o.qkv), m->at<char>(o.atty), m->at<float>(o.lse), s);
     }));
@@ -534,8 +549,9 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets, f
                                m->at<float>(o.ln2_mean), m->at<float>(o.ln2_rstd), s);
     }));
     // g = GELU(u) for the fc-proj product, and GELU'(u) kept for the backward
-    RC(run_gemm(m, S_FC, fwd_desc(m, BT, 4 * C, C, m->at<char>(o.ln2), m->lparam(10, l), EPI_BIAS_GELU_D,
-                                  m->at<char>(o.g), m->lparam(11, l), nullptr, m->at<char>(o.u))));
+    RC(run_gemm(m, S_FC, fwd_desc(m, BT, 4 * C, C, m->at<char>(o.ln2), m->lparam(10, l),
+                                  m->relu2() ? EPI_BIAS_RELU2_D : EPI_BIAS_GELU_D, m->at<char>(o.g),
+                                  m->lparam(11, l), nullptr, m->at<char>(o.u))));
     RC(run_gemm(m, S_FCPROJ, fwd_desc(m, BT, C, 4 * C, m->at<char>(o.g), m->lparam(12, l), EPI_BIAS_RES,
                                       m->at<char>(lo.resid[l + 1]), m->lparam(13, l), m->at<char>(o.h),
                                       nullptr)));
@@ -630,6 +646,11 @@ int backward_impl(gpt2_model* m, bool acc) {
       if (a1) timer_commit(m, S_ATTN_DKDV, 3.0 * causal_mm, 4.0 * act + 2.0 * lse_b + 2.0 * act);
       if (a2) timer_commit(m, S_ATTN_DQ, 1.0 * causal_mm, 4.0 * act + 2.0 * lse_b + act + (mfma ? act + lse_b : 0.0));
     }
+    if (m->qk_norm() || m->rope())     // gradient back through the rotation and the normalisation
+      RC(timed(m, S_QK_BWD, 0.0, (m->qk_norm() ? 3.0 : 2.0) * (2.0 * act) + (m->qk_norm() ? (double)BT * 2 * H * 4 : 0.0), [&] {
+        return qk_transform_backward(dt, BT, T, H, hd, m->at<char>(o.qkv), d_qkv, m->at<float>(o.qk_rstd),
+                                     m->rope_cs(), m->qk_norm(), m->rope(), s);
+      }));
     // qkv = ln1 Wqkv^T + bqkv
     RC(run_gemm(m, S_QKV_DW, dw_desc(m, BT, 3 * C, C, d_qkv, m->at<char>(o.ln1), m->lgrad(4, l),
                                      m->lgrad(5, l), acc)));
@@ -640,10 +661,15 @@ int backward_impl(gpt2_model* m, bool acc) {
                                 m->lgrad(2, l), m->lgrad(3, l), acc, m->scratch(), sb, s);
     }));
   }
-  // encoder: wpe rows >= T get no gradient (zero already when accumulating)
+  // encoder: wpe rows >= T get no gradient (zero already when accumulating),
+  // and none at all with rotary embeddings (the table is not used)
   float* dwpe = m->lgrad(1, 0);
   if (m->dry()) return 0;
-  if (!acc) RC(fill_f32((int64_t)(c.max_seq_len - T) * C, dwpe + (size_t)T * C, 0.f, s));
+  if (!acc) {
+    const int first_zero = m->rope() ? 0 : T;
+    RC(fill_f32((int64_t)(c.max_seq_len - first_zero) * C, dwpe + (size_t)first_zero * C, 0.f, s));
+  }
+  if (m->rope()) dwpe = nullptr;
   if (m->side_pending) {
     GPT2_HIP_CHECK(hipStreamWaitEvent(s, m->ev_join, 0));
     m->side_pending = false;
@@ -729,7 +755,8 @@ void graph_release(gpt2_model* m) {
 // ================================================================ C ABI
 
 static_assert(GPT2_EPI_STORE == EPI_STORE && GPT2_EPI_BIAS == EPI_BIAS && GPT2_EPI_BIAS_RESIDUAL == EPI_BIAS_RES &&
-                  GPT2_EPI_WGRAD == EPI_WGRAD && GPT2_EPI_BIAS_GELU == EPI_BIAS_GELU_D && GPT2_EPI_MUL == EPI_MUL,
+                  GPT2_EPI_BIAS_RELU2 == EPI_BIAS_RELU2_D && GPT2_EPI_WGRAD == EPI_WGRAD &&
+                  GPT2_EPI_BIAS_GELU == EPI_BIAS_GELU_D && GPT2_EPI_MUL == EPI_MUL,
               "epilogue codes of gpt2_ops.h");
 
 namespace {
@@ -738,7 +765,8 @@ const char* site_name(int site) {
   static const char* const names[S_COUNT] = {
       "qkv", "attproj", "fc", "fcproj", "logits", "fcproj_dx", "fcproj_dw", "fc_dx", "fc_dw", "attproj_dx",
       "attproj_dw", "qkv_dx", "qkv_dw", "cls_dx", "cls_dw", "attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq",
-      "attn_bwd_dot", "softmax_xent", "ln_fwd", "ln_bwd", "encoder_fwd", "adamw", "weight_transpose", "grad_norm"};
+      "attn_bwd_dot", "softmax_xent", "ln_fwd", "ln_bwd", "encoder_fwd", "adamw", "weight_transpose", "grad_norm",
+      "qk_fwd", "qk_bwd"};
   return site >= 0 && site < S_COUNT ? names[site] : "";
 }
 
@@ -897,6 +925,8 @@ int gpt2_create(const gpt2_config* cfg, uint64_t seed, void* stream, void* works
       hipEventCreateWithFlags(&m->ev_join, hipEventDisableTiming) != hipSuccess)
     rc = gpt2_internal_fail(GPT2_E_HIP, "side stream / event creation failed");
   if (!rc) rc = init_params(m, seed);
+  if (!rc && m->rope()) rc = rope_table(cfg->max_seq_len, cfg->channels / cfg->num_heads, m->at<float2>(m->lo.rope_cs),
+                                        m->stream);
   if (!rc) rc = fill_f32(m->lo.P, m->at<float>(m->lo.adam_m), 0.f, m->stream);
   if (!rc) rc = fill_f32(m->lo.P, m->at<float>(m->lo.adam_v), 0.f, m->stream);
   if (!rc) rc = fill_f32(m->lo.P, m->grad(), 0.f, m->stream);

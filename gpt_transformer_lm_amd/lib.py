@@ -22,14 +22,14 @@ GPT2_BF16 = 1
 SITES = ["qkv", "attproj", "fc", "fcproj", "logits", "fcproj_dx", "fcproj_dw", "fc_dx", "fc_dw",
          "attproj_dx", "attproj_dw", "qkv_dx", "qkv_dw", "cls_dx", "cls_dw", "attn_fwd", "attn_bwd_dkdv",
          "attn_bwd_dq", "attn_bwd_dot", "softmax_xent", "ln_fwd", "ln_bwd", "encoder_fwd", "adamw",
-         "weight_transpose", "grad_norm"]
+         "weight_transpose", "grad_norm", "qk_fwd", "qk_bwd"]
 
 
 GPT2_ARCH_RELU2 = 1
 GPT2_ARCH_QK_NORM = 2
 GPT2_ARCH_ROPE = 4
 
-EPILOGUES = {0: "store", 1: "bias", 2: "bias+residual", 5: "wgrad", 6: "bias+gelu", 7: "mul"}
+EPILOGUES = {0: "store", 1: "bias", 2: "bias+residual", 3: "bias+relu2", 5: "wgrad", 6: "bias+gelu", 7: "mul"}
 
 
 class Gpt2Config(C.Structure):

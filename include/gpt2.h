@@ -68,11 +68,16 @@ enum {
 
 /* Architecture variants of the block ("NanoGPT (124M) in 90 seconds",
  * section "How it works", item "Architecture Changes": rotary embeddings,
- * QK-Norm and ReLU^2).  0 is GPT-2 as published. */
+ * QK-Norm and ReLU^2; the page gives no formulas, these are the plainest
+ * readings).  0 is GPT-2 as published; the bits combine.  The parameter
+ * layout is the same for every combination. */
 enum {
-  GPT2_ARCH_RELU2 = 1,   /* MLP activation relu(u)^2 instead of GELU-tanh             */
-  GPT2_ARCH_QK_NORM = 2, /* q and k of every head RMS-normalised before the scores    */
-  GPT2_ARCH_ROPE = 4     /* rotary position embedding of q and k (after QK-Norm)      */
+  GPT2_ARCH_RELU2 = 1,   /* MLP activation relu(u)^2 instead of GELU-tanh              */
+  GPT2_ARCH_QK_NORM = 2, /* q and k of every head divided by sqrt(mean(x^2) + 1e-6)
+                            over the head dimension (no gain; scale 1/sqrt(hd) kept)   */
+  GPT2_ARCH_ROPE = 4     /* rotary embedding of q and k (after QK-Norm): at position t
+                            the pair (i, i + hd/2) rotated by t * 10000^(-2i/hd); the
+                            position table wpe is then not used (zero gradient)        */
 };
 
 typedef struct gpt2_config {
@@ -274,9 +279,11 @@ int gpt2_get_logits(gpt2_model* m, float* host_out);
  * 18 attention bwd rowsum(dO*O), 19 softmax-CE, 20 LayerNorm fwd,
  * 21 LayerNorm bwd, 22 encoder fwd, 23 AdamW, 24 transposed bf16 weight
  * copies (written after each AdamW step for the dX products), 25 gradient
- * norm (partial sums of squares; gpt2_adamw_step_clipped).  Events are
- * recorded on the model's stream immediately around that kernel.  Sites are
- * valid in [0, 26); others give GPT2_E_INVALID_ARG. */
+ * norm (partial sums of squares; gpt2_adamw_step_clipped), 26 QK-Norm /
+ * rotary transform of q and k, 27 its backward (GPT2_ARCH_QK_NORM or
+ * GPT2_ARCH_ROPE).  Events are recorded on the model's stream immediately
+ * around that kernel.  Sites are valid in [0, 28); others give
+ * GPT2_E_INVALID_ARG. */
 int gpt2_timing_enable(gpt2_model* m, int site, int enable);
 /* Total elapsed milliseconds and launch count recorded for a site since it
  * was enabled (synchronises the stream), with the algorithmic FLOPs and HBM

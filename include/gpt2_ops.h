@@ -77,6 +77,7 @@ enum {
   GPT2_EPI_STORE = 0,         /* C = sum                                      */
   GPT2_EPI_BIAS = 1,          /* C = sum + bias                               */
   GPT2_EPI_BIAS_RESIDUAL = 2, /* C = sum + bias + residual                    */
+  GPT2_EPI_BIAS_RELU2 = 3,    /* C = relu(sum + bias)^2, U = 2 relu(sum + bias) */
   GPT2_EPI_WGRAD = 5,         /* fp32 weight gradient (+ fused bias gradient) */
   GPT2_EPI_BIAS_GELU = 6,     /* C = GELU(sum + bias), U = GELU'(sum + bias)  */
   GPT2_EPI_MUL = 7            /* C = sum * U                                  */

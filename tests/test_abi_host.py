@@ -150,13 +150,22 @@ def test_failed_host_allocation_is_a_status_not_a_crash():
     assert L.gpt2_step_gemm_plans(C.byref(c), None, 0, C.byref(n)) == 0 and n.value > 0
 
 
-def test_unknown_arch_flags_are_rejected():
+def test_arch_flags():
     from gpt_transformer_lm_amd import lib
     L = lib.load()
     c = cfg()
+    for f in range(8):          # every combination of ReLU^2, QK-Norm and rotary embeddings
+        c.arch_flags = f
+        assert L.gpt2_validate_config(C.byref(c)) == 0
     c.arch_flags = 8
     assert L.gpt2_validate_config(C.byref(c)) == 1
     assert b"arch_flags" in L.gpt2_last_error()
+    # the ReLU^2 variant changes the fc epilogue only
+    c.arch_flags = lib.GPT2_ARCH_RELU2
+    plans = {p["site"]: lib.EPILOGUES[p["epilogue"]] for p in lib.step_gemm_plans(c)}
+    assert plans["fc"] == "bias+relu2" and plans["fcproj_dx"] == "mul"
+    c.arch_flags = 0
+    assert {p["site"]: lib.EPILOGUES[p["epilogue"]] for p in lib.step_gemm_plans(c)}["fc"] == "bias+gelu"
 
 
 # The three GPT-2 sizes at their benchmark batch (T = 1024).

@@ -29,13 +29,16 @@ ADAM_124 = dict(lr=6e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1)
 
 def make(c, dtype, seed=0):
     torch_mod()
-    cfg = lib.make_config(c["V"], c["Vp"], c["maxT"], c["L"], c["H"], c["C_"], c["B"], c["T"], dtype)
+    cfg = lib.make_config(c["V"], c["Vp"], c["maxT"], c["L"], c["H"], c["C_"], c["B"], c["T"], dtype,
+                          c.get("arch", 0))
     return lib.Model(cfg, seed=seed), cfg
 
 
 def ocfg(c):
+    a = c.get("arch", 0)
     return O.OracleConfig(vocab_size=c["V"], max_seq_len=c["maxT"], num_layers=c["L"], num_heads=c["H"],
-                          channels=c["C_"])
+                          channels=c["C_"], relu2=bool(a & lib.GPT2_ARCH_RELU2),
+                          qk_norm=bool(a & lib.GPT2_ARCH_QK_NORM), rope=bool(a & lib.GPT2_ARCH_ROPE))
 
 
 def to_oracle(params, c, dtype=np.float64):
@@ -209,6 +212,59 @@ def test_graph_capture_errors():
             model.graph_capture(tok, tok)
         model.close()
     stream.synchronize()
+
+
+# Architecture variants ("NanoGPT (124M) in 90 seconds", architecture
+# changes): ReLU^2, QK-Norm, rotary embeddings, and all three together.
+ARCH = {"relu2": lib.GPT2_ARCH_RELU2, "qk_norm": lib.GPT2_ARCH_QK_NORM, "rope": lib.GPT2_ARCH_ROPE,
+        "all": lib.GPT2_ARCH_RELU2 | lib.GPT2_ARCH_QK_NORM | lib.GPT2_ARCH_ROPE}
+
+
+@pytest.mark.parametrize("variant", sorted(ARCH))
+def test_tiny_fp32_variant_step_parity(variant):
+    say("tiny fp32 step, variant", variant)
+    c = dict(TINY, arch=ARCH[variant])
+    params = S.random_params(512, 512, 64, 2, 64, seed=1101, perturbed=True)
+    tok, tgt = S.uniform_batch(4, 64, 512, seed=1102)
+    compare_step(c, FP32, params, tok, tgt, ADAM_TINY, np.float64, gtol=1e-4, ltol=1e-4, ptol=1e-4)
+
+
+@pytest.mark.parametrize("variant", ["all", "relu2"])
+def test_mid_bf16_variant_step_parity(variant):
+    """124M widths (hd = 64 matrix-core attention, padded vocabulary), two
+    layers, B = 4, T = 1024, with the variants on, at the bf16 tolerances."""
+    say("mid bf16 step, variant", variant)
+    c = dict(MID, arch=ARCH[variant])
+    params = S.random_params(c["V"], c["Vp"], c["maxT"], c["L"], c["C_"], seed=1201, perturbed=True)
+    tok, tgt = S.zipf_batch(c["B"], c["T"], seed=1202)
+    compare_step(c, BF16, params, tok, tgt, ADAM_124, np.float32, gtol=3e-2, ltol=1e-2, ptol=1e-2)
+
+
+def test_rope_variant_causality_and_unused_position_table():
+    say("rope variant: causality, position table unused")
+    c = dict(TINY, arch=ARCH["all"])
+    params = S.random_params(512, 512, 64, 2, 64, seed=1301, perturbed=True)
+    tok, tgt = S.uniform_batch(4, 64, 512, seed=1302)
+    model, cfg = make(c, FP32)
+    model.set_params(lib.flatten_params(cfg, params))
+    model.forward(dev_i32(tok), dev_i32(tgt))
+    base = model.get_token_losses().reshape(4, 64)
+    model.backward()
+    g = lib.unflatten(cfg, model.get_grads())
+    assert np.all(g["wpe"] == 0.0)
+    for p in (3, 40):
+        t2 = tok.copy()
+        t2[1, p] = (t2[1, p] + 7) % 512
+        model.forward(dev_i32(t2), dev_i32(tgt))
+        l2 = model.get_token_losses().reshape(4, 64)
+        assert np.array_equal(l2[1, :p], base[1, :p]) and not np.array_equal(l2[1, p:], base[1, p:])
+    # the position table does not enter the loss at all
+    p2 = dict(params)
+    p2["wpe"] = params["wpe"] + 1.0
+    model.set_params(lib.flatten_params(cfg, p2))
+    model.forward(dev_i32(tok), dev_i32(tgt))
+    assert np.array_equal(model.get_token_losses().reshape(4, 64), base)
+    model.close()
 
 
 def test_tiny_fp32_three_steps():
