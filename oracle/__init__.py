@@ -38,3 +38,15 @@ from .gpt2_oracle import (  # noqa: F401
     gpt2_step_accumulated,
 )
 from .init_rng import splitmix64_stream, gpt2_init_params  # noqa: F401
+from .fp8 import (  # noqa: F401
+    E4M3,
+    E5M2,
+    fp8_decode,
+    fp8_encode,
+    fp8_linear_backward,
+    fp8_linear_forward,
+    fp8_matmul_nt,
+    fp8_scales,
+    quantize,
+    round_to_fp8,
+)

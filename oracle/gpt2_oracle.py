@@ -53,6 +53,8 @@ from dataclasses import dataclass
 
 import numpy as np
 
+from .fp8 import fp8_linear_backward, fp8_linear_forward
+
 LN_EPS = 1e-5
 GELU_K0 = math.sqrt(2.0 / math.pi)
 GELU_K1 = 0.044715
@@ -69,6 +71,8 @@ class OracleConfig:
     relu2: bool = False
     qk_norm: bool = False
     rope: bool = False
+    # FP8 products (oracle/fp8.py) for the QKV projection, the MLP and the head
+    fp8: bool = False
 
     @property
     def head_dim(self) -> int:
@@ -321,6 +325,23 @@ def _merge_heads(x):
     return x.transpose(1, 0, 2).reshape(T, H * hd)
 
 
+def _lin(cfg, x, w, b=None):
+    """A linear layer of the FP8 set (QKV, fc, fc-proj, head): the fp8
+    product when cfg.fp8 (its cache kept for the backward), else x W^T + b."""
+    if cfg.fp8:
+        y, c = fp8_linear_forward(x, w, b)
+        return y.astype(x.dtype), c
+    return linear_forward(x, w, b), None
+
+
+def _lin_grads(cfg, dy, x, w, cache):
+    """(dx, dW, db) of a layer of the FP8 set."""
+    if cfg.fp8:
+        dx, dw, db = fp8_linear_backward(dy, cache)
+        return dx.astype(dy.dtype), dw.astype(dy.dtype), db
+    return dy @ w, _wgrad(dy, x), dy.reshape(-1, dy.shape[-1]).sum(axis=0)
+
+
 def gpt2_forward(params, tokens, targets, cfg: OracleConfig):
     """Forward pass.  tokens, targets: int arrays [B, T] (targets may be None).
 
@@ -335,7 +356,7 @@ def gpt2_forward(params, tokens, targets, cfg: OracleConfig):
     layers = []
     for l in range(L):
         ln1, ln1_c = layernorm_forward(x, params["ln1w"][l], params["ln1b"][l])
-        qkv = ln1 @ params["qkvw"][l].T + params["qkvb"][l]
+        qkv, qkv_q = _lin(cfg, ln1, params["qkvw"][l], params["qkvb"][l])
         att = np.empty_like(x)
         probs, qk = [], []
         for b in range(B):
@@ -354,16 +375,18 @@ def gpt2_forward(params, tokens, targets, cfg: OracleConfig):
             qk.append((q, k, qc, kc))
         h = x + att @ params["attprojw"][l].T + params["attprojb"][l]
         ln2, ln2_c = layernorm_forward(h, params["ln2w"][l], params["ln2b"][l])
-        u = ln2 @ params["fcw"][l].T + params["fcb"][l]
+        u, fc_q = _lin(cfg, ln2, params["fcw"][l], params["fcb"][l])
         g = relu2(u) if cfg.relu2 else gelu_tanh(u)
-        x_next = h + g @ params["fcprojw"][l].T + params["fcprojb"][l]
+        proj, fcproj_q = _lin(cfg, g, params["fcprojw"][l], params["fcprojb"][l])
+        x_next = h + proj
         layers.append(dict(x=x, ln1=ln1, ln1_c=ln1_c, qkv=qkv, att=att, qk=qk,
-                           probs=probs, h=h, ln2=ln2, ln2_c=ln2_c, u=u, g=g))
+                           probs=probs, h=h, ln2=ln2, ln2_c=ln2_c, u=u, g=g,
+                           qkv_q=qkv_q, fc_q=fc_q, fcproj_q=fcproj_q))
         x = x_next
     lnf, lnf_c = layernorm_forward(x, params["lnfw"], params["lnfb"])
-    logits = lnf.reshape(B * T, C) @ params["wte"].T
+    logits, head_q = _lin(cfg, lnf.reshape(B * T, C), params["wte"])
     cache = dict(tokens=tokens, layers=layers, xL=x, lnf=lnf, lnf_c=lnf_c,
-                 logits=logits, B=B, T=T, ang=ang)
+                 logits=logits, B=B, T=T, ang=ang, head_q=head_q)
     if targets is None:
         return None, None, logits.reshape(B, T, -1), cache
     losses, dz = softmax_cross_entropy(logits, targets.reshape(-1))
@@ -379,19 +402,17 @@ def gpt2_backward(params, cache, cfg: OracleConfig):
     grads = {k: np.zeros_like(v) for k, v in params.items()}
     dz = cache["dlogits"]                                    # [BT, V]
     lnf = cache["lnf"].reshape(B * T, C)
-    grads["wte"] += dz.T @ lnf
-    dlnf = (dz @ params["wte"]).reshape(B, T, C)
+    dlnf, dwte_head, _ = _lin_grads(cfg, dz, lnf, params["wte"], cache["head_q"])
+    grads["wte"] += dwte_head
+    dlnf = dlnf.reshape(B, T, C)
     dx, grads["lnfw"], grads["lnfb"] = layernorm_backward(dlnf, cache["lnf_c"])
     for l in reversed(range(L)):
         c = cache["layers"][l]
         # x_next = h + g Wp^T + bp
-        dg = dx @ params["fcprojw"][l]
-        grads["fcprojw"][l] = _wgrad(dx, c["g"])
-        grads["fcprojb"][l] = dx.sum(axis=(0, 1))
+        dg, grads["fcprojw"][l], grads["fcprojb"][l] = _lin_grads(cfg, dx, c["g"], params["fcprojw"][l],
+                                                                  c["fcproj_q"])
         du = relu2_backward(c["u"], dg) if cfg.relu2 else gelu_tanh_backward(c["u"], dg)
-        grads["fcw"][l] = _wgrad(du, c["ln2"])
-        grads["fcb"][l] = du.sum(axis=(0, 1))
-        dln2 = du @ params["fcw"][l]
+        dln2, grads["fcw"][l], grads["fcb"][l] = _lin_grads(cfg, du, c["ln2"], params["fcw"][l], c["fc_q"])
         dh_ln, grads["ln2w"][l], grads["ln2b"][l] = layernorm_backward(dln2, c["ln2_c"])
         dh = dx + dh_ln
         # h = x + att Wo^T + bo
@@ -411,9 +432,7 @@ def gpt2_backward(params, cache, cfg: OracleConfig):
             dqkv[b, :, 0:C] = _merge_heads(dq)
             dqkv[b, :, C:2 * C] = _merge_heads(dk)
             dqkv[b, :, 2 * C:3 * C] = _merge_heads(dv)
-        grads["qkvw"][l] = _wgrad(dqkv, c["ln1"])
-        grads["qkvb"][l] = dqkv.sum(axis=(0, 1))
-        dln1 = dqkv @ params["qkvw"][l]
+        dln1, grads["qkvw"][l], grads["qkvb"][l] = _lin_grads(cfg, dqkv, c["ln1"], params["qkvw"][l], c["qkv_q"])
         dx_ln, grads["ln1w"][l], grads["ln1b"][l] = layernorm_backward(dln1, c["ln1_c"])
         dx = dh + dx_ln
     dwte, dwpe = encoder_backward(dx, cache["tokens"], cfg.vocab_size, cfg.max_seq_len)
