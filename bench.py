@@ -64,6 +64,7 @@ KERNEL_OF = {
     "softmax_xent": "softmax_xent_bf16_kernel", "ln_fwd": "ln_fwd_half_kernel", "ln_bwd": "ln_bwd_kernel",
     "encoder_fwd": "encoder_fwd_kernel", "adamw": "adamw_kernel", "weight_transpose": "transpose_bf16_kernel",
     "grad_norm": "grad_sumsq_kernel", "qk_fwd": "qk_fwd_kernel", "qk_bwd": "qk_bwd_kernel",
+    "fp8_quant": "quantize_kernel",
 }
 for _s in GEMM_SITES:
     KERNEL_OF[_s] = "gemm_bf16_dma_kernel"
@@ -144,6 +145,8 @@ def main():
                     help="global-norm gradient clipping threshold (0: off)")
     ap.add_argument("--arch", default="",
                     help="comma-separated architecture variants: relu2, qk_norm, rope (default: GPT-2 as published)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="FP8 products for the QKV projection, the MLP and the head (GPT2_BF16_FP8)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each timed step from one captured HIP graph (plain step only)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -166,8 +169,8 @@ def main():
     if any(a not in flag_of for a in arch):
         print(f"--arch takes {sorted(flag_of)}", file=sys.stderr)
         sys.exit(2)
-    cfg = lib.make_config(c["V"], c["Vp"], c["maxT"], c["L"], c["H"], c["C"], B, T, lib.GPT2_BF16,
-                          sum(flag_of[a] for a in set(arch)))
+    cfg = lib.make_config(c["V"], c["Vp"], c["maxT"], c["L"], c["H"], c["C"], B, T,
+                          lib.GPT2_BF16_FP8 if args.fp8 else lib.GPT2_BF16, sum(flag_of[a] for a in set(arch)))
     torch.cuda.init()
     K = max(args.accum, 1)
     plain = K == 1 and args.max_grad_norm <= 0
@@ -285,14 +288,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16+fp8" if args.fp8 else "bf16",
         "data": "synthetic Zipf(1.1)/EoT token ids, seeded random GPT-2 init",
         "config": {"workload": f"GPT-2 {args.config} training step (fwd+bwd+AdamW, fp32 master), "
                                f"B={B}, T={T}, vocab 50257 padded to 50304"
                                + ("" if plain else f", {K} accumulated micro-batches per update, global-norm "
                                                    f"clipping at {args.max_grad_norm}")
                                + (", each step one HIP graph replay" if args.graph else "")
-                               + (f", variants {'+'.join(sorted(set(arch)))}" if arch else ""),
+                               + (f", variants {'+'.join(sorted(set(arch)))}" if arch else "")
+                               + (", FP8 (E4M3/E5M2) QKV, MLP and head products" if args.fp8 else ""),
                    "global_batch": K * B, "seq_len": T, "parallelism": "single GPU"},
         "mfu": mfu,
         "model_flops_per_token": ftok,

@@ -62,6 +62,13 @@ struct GemmDesc {
   float* bias_grad32;                   // WGRAD bias gradient [M] (optional)
   bool accumulate;                      // WGRAD: add into out32 / bias_grad32
   void* workspace; size_t workspace_bytes;
+  // FP8 product (dtype BF16 for C, bias, R and U): 0 off; 1 A and B E4M3
+  // (forward); 2 A E5M2, B E4M3 (backward, A the gradient).  A and B are then
+  // byte arrays of fp8 codes, both k-major, K and the row strides multiples of
+  // 16; scale_a / scale_b (device, one float each) multiply the sums.
+  int fp8;
+  const float* scale_a;
+  const float* scale_b;
 };
 
 // Kernel configuration gemm() launches for a descriptor (host-only): block
@@ -73,8 +80,9 @@ struct GemmLaunchInfo {
 };
 GemmLaunchInfo gemm_launch_info(const GemmDesc& d);
 
-// Device bytes of scratch a GEMM with this descriptor needs (WGRAD only).
-size_t gemm_workspace_bytes(int dtype, int epi, int M, int N, int K, bool a_kmajor, bool b_kmajor);
+// Device bytes of scratch a GEMM with this descriptor needs (WGRAD and split
+// plain stores).
+size_t gemm_workspace_bytes(int dtype, int epi, int M, int N, int K, bool a_kmajor, bool b_kmajor, int fp8 = 0);
 int gemm(const GemmDesc& d, hipStream_t stream);
 
 // ------------------------------------------------------------------ LayerNorm
@@ -106,6 +114,27 @@ int attention_backward_mfma(int B, int T, int H, const void* qkv, const void* ou
 int attention_backward(int dtype, int B, int T, int H, int hd, const void* qkv, const void* out,
                        const void* dout, const float* lse, void* dqkv, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
+
+// ------------------------------------------------------------------ FP8 quantisation
+// Per-tensor scale of an fp8 operand: inv = FMAX / amax, s = amax / FMAX
+// (fp32; 1 and 1 for amax = 0); FMAX 448 for fmt 0 (E4M3), 57344 for fmt 1
+// (E5M2).
+struct Fp8Scale {
+  float amax, inv, s, unused;
+};
+size_t fp8_scale_workspace_bytes();
+// *out = the scale of the n contiguous values x (bf16 or fp32, 16-byte aligned).
+int fp8_compute_scale(int dtype_in, int64_t n, const void* x, int fmt, Fp8Scale* out, float* workspace,
+                      hipStream_t stream);
+// Codes of fp8(x * inv) for x [R, Cc] (row stride ldx): row-major into qrow
+// [R, Cc] and / or transposed into qt [Cc, R] (either may be NULL).
+// Cc % 8 == 0; R % 16 == 0 when qt.
+int fp8_quantize(int dtype_in, int fmt, int R, int Cc, const void* x, int64_t ldx, const Fp8Scale* sc,
+                 uint8_t* qrow, uint8_t* qt, hipStream_t stream);
+// db[n] (+)= sum over the R rows of dy [R, N] (bf16), fixed summation order.
+size_t bias_grad_workspace_bytes(int N);
+int bias_grad_bf16(int R, int N, const bf16* dy, float* db, bool accumulate, float* workspace,
+                   size_t workspace_bytes, hipStream_t stream);
 
 // ------------------------------------------------------------------ QK-Norm / rotary
 // In place on the q and k columns of qkv [BT, 3C] (hd = C / H): QK-Norm (RMS

@@ -156,10 +156,14 @@ void param_table(const gpt2_config& c, bool padded, ParamTable* t) {
   t->total = o;
 }
 
+// Storage of parameters copies, activations and activation gradients: bf16
+// in the two mixed-precision modes, fp32 in the parity mode.
+bool is_bf16(const gpt2_config& c) { return c.dtype != GPT2_FP32; }
+
 int validate(const gpt2_config* c) {
   if (!c) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "config is NULL");
-  if (c->dtype != GPT2_FP32 && c->dtype != GPT2_BF16)
-    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "dtype %d is neither GPT2_FP32 nor GPT2_BF16", c->dtype);
+  if (c->dtype != GPT2_FP32 && c->dtype != GPT2_BF16 && c->dtype != GPT2_BF16_FP8)
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "dtype %d is not GPT2_FP32, GPT2_BF16 or GPT2_BF16_FP8", c->dtype);
   if (c->vocab_size <= 0 || c->vocab_size > 65536)
     return gpt2_internal_fail(GPT2_E_INVALID_ARG, "vocab_size %d outside (0, 65536]", c->vocab_size);
   if (c->padded_vocab_size < c->vocab_size || c->padded_vocab_size % 64 || c->padded_vocab_size > 65536)
@@ -202,7 +206,23 @@ struct LayerOffsets {
   size_t u;   // activation derivative at the fc pre-activation (GELU' or 2 relu), for the backward
   size_t g;   // activation of the fc pre-activation (GELU or relu^2)
   size_t qk_rstd;   // QK-Norm: 1 / rms of every q and k head vector [BT, 2H] fp32 (0 if unused)
+  // fp8 mode: codes of the fp8 products' inputs, row-major (q) and transposed (qt)
+  size_t ln1_q, ln1_qt, ln2_q, ln2_qt, g_q, g_qt;
 };
+
+// fp8 mode: the weight tensors of the fp8 products (token table, W_qkv, W_fc,
+// W_p) and the slots of their per-tensor scales.
+const int kFp8Weights[4] = {0, 4, 10, 12};
+enum Fp8Kind { Q_WEIGHT = 0, Q_ACT = 1, Q_GRAD = 2 };
+// Scale slot: weights (token table; then W_qkv, W_fc, W_p of each layer),
+// activations (ln1, ln2, g of each layer; lnf), gradients (dlogits; the
+// fc-proj, fc and QKV output gradients of each layer).
+int fp8_slot(int L, int kind, int which, int l) {
+  if (kind == Q_WEIGHT) return which == 0 ? 0 : 1 + (which - 1) * L + l;
+  if (kind == Q_ACT) return which == 3 ? 1 + 6 * L : 1 + 3 * L + 3 * l + which;
+  return which == 3 ? 2 + 6 * L : 3 + 6 * L + 3 * l + which;
+}
+int fp8_slots(int L) { return 3 + 9 * L; }
 
 struct Layout {
   ParamTable pt;
@@ -217,12 +237,16 @@ struct Layout {
   size_t dres, dres_t, d_ln, d_big, d_qkv, scratch;
   size_t sorted_keys;                    // encoder-backward key sort (computed during the forward)
   size_t rope_cs;                        // rotary embedding cos / sin table [maxT][hd/2] (0 if unused)
+  // fp8 mode (0 otherwise): weight codes per parameter tensor (row-major and
+  // transposed, all layers), lnf codes, the current output gradient's codes,
+  // per-tensor scales, absmax partials
+  size_t wq[16], wqt[16], lnf_q, lnf_qt, dq, dqt, fp8_scales, fp8_amax;
   size_t scratch_bytes;
   size_t total;
 };
 
 size_t scratch_need(const gpt2_config& c) {
-  const int dt = c.dtype;
+  const int dt = is_bf16(c) ? GPT2_BF16 : GPT2_FP32;
   const int BT = c.batch_size * c.seq_len, C = c.channels, Vp = c.padded_vocab_size;
   size_t s = 0;
   auto upd = [&](size_t x) { s = std::max(s, x); };
@@ -238,6 +262,14 @@ size_t scratch_need(const gpt2_config& c) {
   upd(gemm_workspace_bytes(dt, EPI_STORE, BT, C, 3 * C, true, wt));
   upd(gemm_workspace_bytes(dt, EPI_STORE, BT, C, C, true, wt));
   upd(layernorm_backward_workspace_bytes(BT, C));
+  if (c.dtype == GPT2_BF16_FP8) {   // fp8 weight gradients (split-K partials) and dX, bias gradients
+    const int fp8_n[4][2] = {{Vp, C}, {3 * C, C}, {4 * C, C}, {C, 4 * C}};
+    for (auto& nk : fp8_n) {
+      upd(gemm_workspace_bytes(GPT2_BF16, EPI_WGRAD, nk[0], nk[1], BT, true, true, 2));
+      upd(gemm_workspace_bytes(GPT2_BF16, EPI_STORE, BT, nk[1], nk[0], true, true, 2));
+      upd(bias_grad_workspace_bytes(nk[0]));
+    }
+  }
   upd(attention_backward_workspace_bytes(c.batch_size, c.seq_len, c.num_heads, C / c.num_heads));
   upd(encoder_backward_workspace_bytes(c.batch_size, c.seq_len, C));
   return s;
@@ -246,7 +278,7 @@ size_t scratch_need(const gpt2_config& c) {
 void make_layout(const gpt2_config& c, Layout* lo) {
   param_table(c, true, &lo->pt);
   lo->P = lo->pt.total;
-  const size_t es = c.dtype == GPT2_BF16 ? 2 : 4;
+  const size_t es = is_bf16(c) ? 2 : 4;
   const size_t BT = (size_t)c.batch_size * c.seq_len, C = c.channels, L = c.num_layers;
   const size_t BHT = (size_t)c.batch_size * c.num_heads * c.seq_len;
   Plan p;
@@ -254,10 +286,11 @@ void make_layout(const gpt2_config& c, Layout* lo) {
   lo->grad = p.alloc(lo->P * 4);
   lo->adam_m = p.alloc(lo->P * 4);
   lo->adam_v = p.alloc(lo->P * 4);
-  lo->params_bf16 = c.dtype == GPT2_BF16 ? p.alloc(lo->P * 2) : 0;
+  lo->params_bf16 = is_bf16(c) ? p.alloc(lo->P * 2) : 0;
   for (int i = 0; i < 16; ++i) lo->params_t[i] = 0;
-  if (c.dtype == GPT2_BF16)
+  if (is_bf16(c))
     for (int i : kTransposed) {
+      if (c.dtype == GPT2_BF16_FP8 && i != 6) continue;   // the fp8 weights keep fp8 transposed codes instead
       const int64_t* sh = lo->pt.shape[i];
       lo->params_t[i] = p.alloc((size_t)sh[0] * sh[1] * sh[2] * 2);
     }
@@ -280,6 +313,13 @@ void make_layout(const gpt2_config& c, Layout* lo) {
     o.u = p.alloc(BT * 4 * C * es);
     o.g = p.alloc(BT * 4 * C * es);
     o.qk_rstd = (c.arch_flags & GPT2_ARCH_QK_NORM) ? p.alloc((size_t)BT * 2 * c.num_heads * 4) : 0;
+    const bool f8 = c.dtype == GPT2_BF16_FP8;
+    o.ln1_q = f8 ? p.alloc(BT * C) : 0;
+    o.ln1_qt = f8 ? p.alloc(BT * C) : 0;
+    o.ln2_q = f8 ? p.alloc(BT * C) : 0;
+    o.ln2_qt = f8 ? p.alloc(BT * C) : 0;
+    o.g_q = f8 ? p.alloc(BT * 4 * C) : 0;
+    o.g_qt = f8 ? p.alloc(BT * 4 * C) : 0;
   }
   lo->lnf = p.alloc(BT * C * es);
   lo->lnf_mean = p.alloc(BT * 4);
@@ -290,7 +330,7 @@ void make_layout(const gpt2_config& c, Layout* lo) {
   lo->gnorm = p.alloc(grad_norm_workspace_bytes());
   lo->adam_hp = p.alloc(sizeof(AdamHP));
   lo->dres = p.alloc(BT * C * 4);
-  lo->dres_t = c.dtype == GPT2_BF16 ? p.alloc(BT * C * es) : lo->dres;
+  lo->dres_t = is_bf16(c) ? p.alloc(BT * C * es) : lo->dres;
   lo->d_ln = p.alloc(BT * C * es);
   lo->d_big = p.alloc(BT * 4 * C * es);
   lo->d_qkv = p.alloc(BT * 3 * C * es);
@@ -298,6 +338,22 @@ void make_layout(const gpt2_config& c, Layout* lo) {
   lo->rope_cs = (c.arch_flags & GPT2_ARCH_ROPE)
                     ? p.alloc((size_t)c.max_seq_len * (c.channels / c.num_heads / 2) * sizeof(float2))
                     : 0;
+  for (int i = 0; i < 16; ++i) lo->wq[i] = lo->wqt[i] = 0;
+  lo->lnf_q = lo->lnf_qt = lo->dq = lo->dqt = lo->fp8_scales = lo->fp8_amax = 0;
+  if (c.dtype == GPT2_BF16_FP8) {
+    for (int i : kFp8Weights) {
+      const int64_t* sh = lo->pt.shape[i];
+      lo->wq[i] = p.alloc((size_t)sh[0] * sh[1] * sh[2]);
+      lo->wqt[i] = p.alloc((size_t)sh[0] * sh[1] * sh[2]);
+    }
+    lo->lnf_q = p.alloc(BT * C);
+    lo->lnf_qt = p.alloc(BT * C);
+    const size_t big = BT * std::max<size_t>((size_t)c.padded_vocab_size, 4 * C);   // the largest output gradient
+    lo->dq = p.alloc(big);
+    lo->dqt = p.alloc(big);
+    lo->fp8_scales = p.alloc((size_t)fp8_slots((int)L) * sizeof(Fp8Scale));
+    lo->fp8_amax = p.alloc(fp8_scale_workspace_bytes());
+  }
   lo->scratch_bytes = scratch_need(c);
   lo->scratch = p.alloc(lo->scratch_bytes);
   lo->total = p.total;
@@ -309,7 +365,8 @@ void make_layout(const gpt2_config& c, Layout* lo) {
 enum Site {
   S_QKV = 0, S_ATTPROJ, S_FC, S_FCPROJ, S_LOGITS, S_FCPROJ_DX, S_FCPROJ_DW, S_FC_DX, S_FC_DW,
   S_ATTPROJ_DX, S_ATTPROJ_DW, S_QKV_DX, S_QKV_DW, S_CLS_DX, S_CLS_DW, S_ATTN_FWD, S_ATTN_DKDV, S_ATTN_DQ,
-  S_ATTN_DOT, S_XENT, S_LN_FWD, S_LN_BWD, S_ENC_FWD, S_ADAMW, S_WT, S_GRAD_NORM, S_QK_FWD, S_QK_BWD, S_COUNT
+  S_ATTN_DOT, S_XENT, S_LN_FWD, S_LN_BWD, S_ENC_FWD, S_ADAMW, S_WT, S_GRAD_NORM, S_QK_FWD, S_QK_BWD, S_FP8_QUANT,
+  S_COUNT
 };
 
 struct SiteTimer {
@@ -352,13 +409,13 @@ struct gpt2_model {
   float* grad() { return at<float>(lo.grad); }
   // parameter tensor i as read by the forward (bf16 copy or fp32 master)
   void* param(int i) {
-    if (cfg.dtype == GPT2_BF16) return at<bf16>(lo.params_bf16) + lo.pt.off[i];
+    if (is_bf16(cfg)) return at<bf16>(lo.params_bf16) + lo.pt.off[i];
     return master() + lo.pt.off[i];
   }
   // layer slice of a per-layer parameter tensor (storage type)
   void* lparam(int i, int l) {
     int64_t per = lo.pt.shape[i][1] * lo.pt.shape[i][2];
-    if (cfg.dtype == GPT2_BF16) return at<bf16>(lo.params_bf16) + lo.pt.off[i] + (int64_t)l * per;
+    if (is_bf16(cfg)) return at<bf16>(lo.params_bf16) + lo.pt.off[i] + (int64_t)l * per;
     return master() + lo.pt.off[i] + (int64_t)l * per;
   }
   // transposed bf16 copy of weight matrix i (layer l): [in, out] row-major
@@ -371,12 +428,21 @@ struct gpt2_model {
     int64_t per = lo.pt.shape[i][1] * lo.pt.shape[i][2];
     return grad() + lo.pt.off[i] + (int64_t)l * per;
   }
-  int dt() const { return cfg.dtype; }
+  int dt() const { return is_bf16(cfg) ? GPT2_BF16 : GPT2_FP32; }
+  bool fp8() const { return cfg.dtype == GPT2_BF16_FP8; }
   bool qk_norm() const { return (cfg.arch_flags & GPT2_ARCH_QK_NORM) != 0; }
   bool rope() const { return (cfg.arch_flags & GPT2_ARCH_ROPE) != 0; }
   bool relu2() const { return (cfg.arch_flags & GPT2_ARCH_RELU2) != 0; }
   const float2* rope_cs() { return rope() ? at<float2>(lo.rope_cs) : nullptr; }
-  size_t es() const { return cfg.dtype == GPT2_BF16 ? 2 : 4; }
+  // fp8 mode: scale slot, and the weight codes of tensor i, layer l
+  Fp8Scale* fscale(int slot) { return at<Fp8Scale>(lo.fp8_scales) + slot; }
+  int64_t wq_per_layer(int i) const {
+    const int64_t* sh = lo.pt.shape[i];
+    return lo.pt.ndim[i] == 3 ? sh[1] * sh[2] : 0;
+  }
+  uint8_t* wq(int i, int l) { return at<uint8_t>(lo.wq[i]) + (int64_t)l * wq_per_layer(i); }
+  uint8_t* wqt(int i, int l) { return at<uint8_t>(lo.wqt[i]) + (int64_t)l * wq_per_layer(i); }
+  size_t es() const { return is_bf16(cfg) ? 2 : 4; }
   void* scratch() { return base + lo.scratch; }
 };
 
@@ -490,12 +556,66 @@ GemmDesc dw_desc(gpt2_model* m, int M, int N, int K, const void* dy, const void*
   return linear_dw_desc(m->dt(), M, N, K, dy, x, dW, db, acc, m->scratch(), m->lo.scratch_bytes);
 }
 
+// ---- fp8 mode (QKV, fc, fc-proj and head products)
+
+// Per-tensor scale of x [R, Cc] (bf16 or fp32) into `slot`, then its codes
+// row-major (q) and / or transposed (qt).  fmt 0: E4M3, 1: E5M2.
+int fp8_quant(gpt2_model* m, int dtype_in, const void* x, int R, int Cc, int fmt, int slot, uint8_t* q, uint8_t* qt) {
+  if (m->dry()) return 0;
+  Fp8Scale* sc = m->fscale(slot);
+  RC(fp8_compute_scale(dtype_in, (int64_t)R * Cc, x, fmt, sc, m->at<float>(m->lo.fp8_amax), m->stream));
+  const double in_b = (double)R * Cc * (dtype_in == GPT2_BF16 ? 2 : 4);
+  return timed(m, S_FP8_QUANT, 0.0, in_b + (double)R * Cc * ((q ? 1 : 0) + (qt ? 1 : 0)),
+               [&] { return fp8_quantize(dtype_in, fmt, R, Cc, x, Cc, sc, q, qt, m->stream); });
+}
+
+// The forward product x W^T as an fp8 product of the codes xq (scale slot
+// xs) and wq (slot ws); d is the bf16 descriptor (shape, epilogue, outputs).
+GemmDesc fp8_fwd(gpt2_model* m, GemmDesc d, const uint8_t* xq, int xs, const uint8_t* wq, int ws) {
+  d.A = xq; d.B = wq; d.fp8 = 1;
+  d.scale_a = &m->fscale(xs)->s; d.scale_b = &m->fscale(ws)->s;
+  return d;
+}
+
+// dX = dY W from the gradient codes dq [M, N] (slot ds) and the transposed
+// weight codes wqt [K, N] (slot ws).
+GemmDesc fp8_dx(gpt2_model* m, int M, int N, int K, const uint8_t* dq, int ds, const uint8_t* wqt, int ws, void* dx,
+                int epi, const void* gelu_grad) {
+  GemmDesc d = linear_dx_desc(GPT2_BF16, M, N, K, dq, nullptr, wqt, dx, epi, gelu_grad, m->scratch(),
+                              m->lo.scratch_bytes);
+  d.fp8 = 2;
+  d.scale_a = &m->fscale(ds)->s; d.scale_b = &m->fscale(ws)->s;
+  return d;
+}
+
+// dW [N, K] (+)= dY^T X from the transposed codes dqt [N, M] (slot ds) and
+// xqt [K, M] (slot xs); the bias gradient is taken separately.
+GemmDesc fp8_dw(gpt2_model* m, int M, int N, int K, const uint8_t* dqt, int ds, const uint8_t* xqt, int xs, float* dW,
+                bool acc) {
+  GemmDesc d = gdesc(GPT2_BF16);
+  d.a_kmajor = d.b_kmajor = true;
+  d.M = N; d.N = K; d.K = M;
+  d.A = dqt; d.lda = M; d.B = xqt; d.ldb = M;
+  d.epi = EPI_WGRAD; d.out32 = dW; d.accumulate = acc;
+  d.workspace = m->scratch(); d.workspace_bytes = m->lo.scratch_bytes;
+  d.fp8 = 2;
+  d.scale_a = &m->fscale(ds)->s; d.scale_b = &m->fscale(xs)->s;
+  return d;
+}
+
+// Bias gradient of an fp8 weight-gradient product (from the bf16 gradient).
+int fp8_bias_grad(gpt2_model* m, int M, int N, const void* dy, float* db, bool acc) {
+  if (m->dry()) return 0;
+  return bias_grad_bf16(M, N, static_cast<const bf16*>(dy), db, acc, static_cast<float*>(m->scratch()),
+                        m->lo.scratch_bytes, m->stream);
+}
+
 // loss_scale: the dlogits (and so every gradient of the next backward) are
 // those of loss_scale x the mean loss.
 int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets, float loss_scale) {
   const gpt2_config& c = m->cfg;
   const int B = c.batch_size, T = c.seq_len, C = c.channels, H = c.num_heads, hd = C / H;
-  const int BT = B * T, Vp = c.padded_vocab_size, V = c.vocab_size;
+  const int BT = B * T, Vp = c.padded_vocab_size, V = c.vocab_size, L = c.num_layers;
   const int dt = m->dt();
   hipStream_t s = m->stream;
   Layout& lo = m->lo;
@@ -532,8 +652,16 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets, f
       return layernorm_forward(dt, BT, C, x, m->lparam(2, l), m->lparam(3, l), m->at<char>(o.ln1),
                                m->at<float>(o.ln1_mean), m->at<float>(o.ln1_rstd), s);
     }));
-    RC(run_gemm(m, S_QKV, fwd_desc(m, BT, 3 * C, C, m->at<char>(o.ln1), m->lparam(4, l), EPI_BIAS,
-                                   m->at<char>(o.qkv), m->lparam(5, l), nullptr, nullptr)));
+    {
+      GemmDesc d = fwd_desc(m, BT, 3 * C, C, m->at<char>(o.ln1), m->lparam(4, l), EPI_BIAS, m->at<char>(o.qkv),
+                            m->lparam(5, l), nullptr, nullptr);
+      if (m->fp8()) {
+        RC(fp8_quant(m, GPT2_BF16, m->at<char>(o.ln1), BT, C, 0, fp8_slot(L, Q_ACT, 0, l), m->at<uint8_t>(o.ln1_q),
+                     m->at<uint8_t>(o.ln1_qt)));
+        d = fp8_fwd(m, d, m->at<uint8_t>(o.ln1_q), fp8_slot(L, Q_ACT, 0, l), m->wq(4, l), fp8_slot(L, Q_WEIGHT, 1, l));
+      }
+      RC(run_gemm(m, S_QKV, d));
+    }
     if (m->qk_norm() || m->rope())     // q and k transformed in place before the attention reads them
       RC(timed(m, S_QK_FWD, 0.0, qk_bytes, [&] {
         return qk_transform_forward(dt, BT, T, H, hd, m->at<char>(o.qkv), m->at<float>(o.qk_rstd), m->rope_cs(),
@@ -549,19 +677,44 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets, f
                                m->at<float>(o.ln2_mean), m->at<float>(o.ln2_rstd), s);
     }));
     // g = GELU(u) for the fc-proj product, and GELU'(u) kept for the backward
-    RC(run_gemm(m, S_FC, fwd_desc(m, BT, 4 * C, C, m->at<char>(o.ln2), m->lparam(10, l),
-                                  m->relu2() ? EPI_BIAS_RELU2_D : EPI_BIAS_GELU_D, m->at<char>(o.g),
-                                  m->lparam(11, l), nullptr, m->at<char>(o.u))));
-    RC(run_gemm(m, S_FCPROJ, fwd_desc(m, BT, C, 4 * C, m->at<char>(o.g), m->lparam(12, l), EPI_BIAS_RES,
-                                      m->at<char>(lo.resid[l + 1]), m->lparam(13, l), m->at<char>(o.h),
-                                      nullptr)));
+    {
+      GemmDesc d = fwd_desc(m, BT, 4 * C, C, m->at<char>(o.ln2), m->lparam(10, l),
+                            m->relu2() ? EPI_BIAS_RELU2_D : EPI_BIAS_GELU_D, m->at<char>(o.g), m->lparam(11, l),
+                            nullptr, m->at<char>(o.u));
+      if (m->fp8()) {
+        RC(fp8_quant(m, GPT2_BF16, m->at<char>(o.ln2), BT, C, 0, fp8_slot(L, Q_ACT, 1, l), m->at<uint8_t>(o.ln2_q),
+                     m->at<uint8_t>(o.ln2_qt)));
+        d = fp8_fwd(m, d, m->at<uint8_t>(o.ln2_q), fp8_slot(L, Q_ACT, 1, l), m->wq(10, l),
+                    fp8_slot(L, Q_WEIGHT, 2, l));
+      }
+      RC(run_gemm(m, S_FC, d));
+    }
+    {
+      GemmDesc d = fwd_desc(m, BT, C, 4 * C, m->at<char>(o.g), m->lparam(12, l), EPI_BIAS_RES,
+                            m->at<char>(lo.resid[l + 1]), m->lparam(13, l), m->at<char>(o.h), nullptr);
+      if (m->fp8()) {
+        RC(fp8_quant(m, GPT2_BF16, m->at<char>(o.g), BT, 4 * C, 0, fp8_slot(L, Q_ACT, 2, l), m->at<uint8_t>(o.g_q),
+                     m->at<uint8_t>(o.g_qt)));
+        d = fp8_fwd(m, d, m->at<uint8_t>(o.g_q), fp8_slot(L, Q_ACT, 2, l), m->wq(12, l),
+                    fp8_slot(L, Q_WEIGHT, 3, l));
+      }
+      RC(run_gemm(m, S_FCPROJ, d));
+    }
   }
   RC(timed(m, S_LN_FWD, 0.0, ln_fwd_bytes, [&] {
     return layernorm_forward(dt, BT, C, m->at<char>(lo.resid[c.num_layers]), m->param(14), m->param(15),
                              m->at<char>(lo.lnf), m->at<float>(lo.lnf_mean), m->at<float>(lo.lnf_rstd), s);
   }));
-  RC(run_gemm(m, S_LOGITS, fwd_desc(m, BT, Vp, C, m->at<char>(lo.lnf), m->param(0), EPI_STORE,
-                                    m->at<char>(lo.logits), nullptr, nullptr, nullptr)));
+  {
+    GemmDesc d = fwd_desc(m, BT, Vp, C, m->at<char>(lo.lnf), m->param(0), EPI_STORE, m->at<char>(lo.logits), nullptr,
+                          nullptr, nullptr);
+    if (m->fp8()) {
+      RC(fp8_quant(m, GPT2_BF16, m->at<char>(lo.lnf), BT, C, 0, fp8_slot(L, Q_ACT, 3, 0), m->at<uint8_t>(lo.lnf_q),
+                   m->at<uint8_t>(lo.lnf_qt)));
+      d = fp8_fwd(m, d, m->at<uint8_t>(lo.lnf_q), fp8_slot(L, Q_ACT, 3, 0), m->wq(0, 0), fp8_slot(L, Q_WEIGHT, 0, 0));
+    }
+    RC(run_gemm(m, S_LOGITS, d));
+  }
   if (targets) {
     RC(timed(m, S_XENT, 0.0, 2.0 * BT * (double)Vp * es + BT * 8.0, [&] {
       return softmax_xent(dt, BT, V, Vp, m->at<char>(lo.logits), targets, m->at<float>(lo.losses), loss_scale / BT,
@@ -598,9 +751,20 @@ int backward_impl(gpt2_model* m, bool acc) {
     return 2.0 * act + (double)BT * C * (ovw ? 4.0 : 8.0) + (dres_copy ? act : 0.0) + BT * 8.0 + C * es;
   };
 
+  uint8_t* dq = m->at<uint8_t>(lo.dq);
+  uint8_t* dqt = m->at<uint8_t>(lo.dqt);
   // classifier: d_lnf = dz wte;  d_wte = dz^T lnf (overwrite; padded rows get exactly 0)
-  RC(run_gemm(m, S_CLS_DX, dx_desc(m, BT, Vp, C, logits, m->param(0), m->wt(0, 0), d_ln, EPI_STORE, nullptr)));
-  RC(run_gemm(m, S_CLS_DW, dw_desc(m, BT, Vp, C, logits, m->at<char>(lo.lnf), m->lgrad(0, 0), nullptr, acc)));
+  if (m->fp8()) {
+    const int gs = fp8_slot(L, Q_GRAD, 3, 0);
+    RC(fp8_quant(m, GPT2_BF16, logits, BT, Vp, 1, gs, dq, dqt));
+    RC(run_gemm(m, S_CLS_DX, fp8_dx(m, BT, Vp, C, dq, gs, m->wqt(0, 0), fp8_slot(L, Q_WEIGHT, 0, 0), d_ln, EPI_STORE,
+                                    nullptr)));
+    RC(run_gemm(m, S_CLS_DW, fp8_dw(m, BT, Vp, C, dqt, gs, m->at<uint8_t>(lo.lnf_qt), fp8_slot(L, Q_ACT, 3, 0),
+                                    m->lgrad(0, 0), acc)));
+  } else {
+    RC(run_gemm(m, S_CLS_DX, dx_desc(m, BT, Vp, C, logits, m->param(0), m->wt(0, 0), d_ln, EPI_STORE, nullptr)));
+    RC(run_gemm(m, S_CLS_DW, dw_desc(m, BT, Vp, C, logits, m->at<char>(lo.lnf), m->lgrad(0, 0), nullptr, acc)));
+  }
   RC(timed(m, S_LN_BWD, 0.0, ln_bwd_bytes(true), [&] {
     return layernorm_backward(dt, BT, C, d_ln, m->at<char>(lo.resid[L]), m->param(14), m->at<float>(lo.lnf_mean),
                               m->at<float>(lo.lnf_rstd), dres, true, dres_copy, m->lgrad(14, 0), m->lgrad(15, 0),
@@ -608,16 +772,36 @@ int backward_impl(gpt2_model* m, bool acc) {
   }));
   for (int l = L - 1; l >= 0; --l) {
     LayerOffsets& o = lo.layer[l];
-    // x_{l+1} = h + g Wp^T + bp
-    RC(run_gemm(m, S_FCPROJ_DW, dw_desc(m, BT, C, 4 * C, dres_t, m->at<char>(o.g), m->lgrad(12, l),
-                                        m->lgrad(13, l), acc)));
-    // du = (dy W_p) * GELU'(u), the derivative saved by the forward
-    RC(run_gemm(m, S_FCPROJ_DX, dx_desc(m, BT, C, 4 * C, dres_t, m->lparam(12, l), m->wt(12, l), d_big, EPI_MUL,
-                                        m->at<char>(o.u))));
-    // u = ln2 Wfc^T + bfc   (d_big now holds du)
-    RC(run_gemm(m, S_FC_DW, dw_desc(m, BT, 4 * C, C, d_big, m->at<char>(o.ln2), m->lgrad(10, l),
-                                    m->lgrad(11, l), acc)));
-    RC(run_gemm(m, S_FC_DX, dx_desc(m, BT, 4 * C, C, d_big, m->lparam(10, l), m->wt(10, l), d_ln, EPI_STORE, nullptr)));
+    if (m->fp8()) {
+      // x_{l+1} = h + g Wp^T + bp: dY = the residual gradient (bf16 copy)
+      const int gp = fp8_slot(L, Q_GRAD, 0, l), gf = fp8_slot(L, Q_GRAD, 1, l);
+      RC(fp8_quant(m, GPT2_BF16, dres_t, BT, C, 1, gp, dq, dqt));
+      RC(run_gemm(m, S_FCPROJ_DW, fp8_dw(m, BT, C, 4 * C, dqt, gp, m->at<uint8_t>(o.g_qt), fp8_slot(L, Q_ACT, 2, l),
+                                         m->lgrad(12, l), acc)));
+      RC(fp8_bias_grad(m, BT, C, dres_t, m->lgrad(13, l), acc));
+      // du = (dy W_p) * GELU'(u), the derivative saved by the forward
+      RC(run_gemm(m, S_FCPROJ_DX, fp8_dx(m, BT, C, 4 * C, dq, gp, m->wqt(12, l), fp8_slot(L, Q_WEIGHT, 3, l), d_big,
+                                         EPI_MUL, m->at<char>(o.u))));
+      // u = ln2 Wfc^T + bfc   (d_big now holds du)
+      RC(fp8_quant(m, GPT2_BF16, d_big, BT, 4 * C, 1, gf, dq, dqt));
+      RC(run_gemm(m, S_FC_DW, fp8_dw(m, BT, 4 * C, C, dqt, gf, m->at<uint8_t>(o.ln2_qt), fp8_slot(L, Q_ACT, 1, l),
+                                     m->lgrad(10, l), acc)));
+      RC(fp8_bias_grad(m, BT, 4 * C, d_big, m->lgrad(11, l), acc));
+      RC(run_gemm(m, S_FC_DX, fp8_dx(m, BT, 4 * C, C, dq, gf, m->wqt(10, l), fp8_slot(L, Q_WEIGHT, 2, l), d_ln,
+                                     EPI_STORE, nullptr)));
+    } else {
+      // x_{l+1} = h + g Wp^T + bp
+      RC(run_gemm(m, S_FCPROJ_DW, dw_desc(m, BT, C, 4 * C, dres_t, m->at<char>(o.g), m->lgrad(12, l),
+                                          m->lgrad(13, l), acc)));
+      // du = (dy W_p) * GELU'(u), the derivative saved by the forward
+      RC(run_gemm(m, S_FCPROJ_DX, dx_desc(m, BT, C, 4 * C, dres_t, m->lparam(12, l), m->wt(12, l), d_big, EPI_MUL,
+                                          m->at<char>(o.u))));
+      // u = ln2 Wfc^T + bfc   (d_big now holds du)
+      RC(run_gemm(m, S_FC_DW, dw_desc(m, BT, 4 * C, C, d_big, m->at<char>(o.ln2), m->lgrad(10, l),
+                                      m->lgrad(11, l), acc)));
+      RC(run_gemm(m, S_FC_DX, dx_desc(m, BT, 4 * C, C, d_big, m->lparam(10, l), m->wt(10, l), d_ln, EPI_STORE,
+                                      nullptr)));
+    }
     RC(timed(m, S_LN_BWD, 0.0, ln_bwd_bytes(false), [&] {
       return layernorm_backward(dt, BT, C, d_ln, m->at<char>(o.h), m->lparam(8, l), m->at<float>(o.ln2_mean),
                                 m->at<float>(o.ln2_rstd), dres, false, dres_copy, m->lgrad(8, l), m->lgrad(9, l),
@@ -652,9 +836,20 @@ int backward_impl(gpt2_model* m, bool acc) {
                                      m->rope_cs(), m->qk_norm(), m->rope(), s);
       }));
     // qkv = ln1 Wqkv^T + bqkv
-    RC(run_gemm(m, S_QKV_DW, dw_desc(m, BT, 3 * C, C, d_qkv, m->at<char>(o.ln1), m->lgrad(4, l),
-                                     m->lgrad(5, l), acc)));
-    RC(run_gemm(m, S_QKV_DX, dx_desc(m, BT, 3 * C, C, d_qkv, m->lparam(4, l), m->wt(4, l), d_ln, EPI_STORE, nullptr)));
+    if (m->fp8()) {
+      const int gq = fp8_slot(L, Q_GRAD, 2, l);
+      RC(fp8_quant(m, GPT2_BF16, d_qkv, BT, 3 * C, 1, gq, dq, dqt));
+      RC(run_gemm(m, S_QKV_DW, fp8_dw(m, BT, 3 * C, C, dqt, gq, m->at<uint8_t>(o.ln1_qt), fp8_slot(L, Q_ACT, 0, l),
+                                      m->lgrad(4, l), acc)));
+      RC(fp8_bias_grad(m, BT, 3 * C, d_qkv, m->lgrad(5, l), acc));
+      RC(run_gemm(m, S_QKV_DX, fp8_dx(m, BT, 3 * C, C, dq, gq, m->wqt(4, l), fp8_slot(L, Q_WEIGHT, 1, l), d_ln,
+                                      EPI_STORE, nullptr)));
+    } else {
+      RC(run_gemm(m, S_QKV_DW, dw_desc(m, BT, 3 * C, C, d_qkv, m->at<char>(o.ln1), m->lgrad(4, l),
+                                       m->lgrad(5, l), acc)));
+      RC(run_gemm(m, S_QKV_DX, dx_desc(m, BT, 3 * C, C, d_qkv, m->lparam(4, l), m->wt(4, l), d_ln, EPI_STORE,
+                                       nullptr)));
+    }
     RC(timed(m, S_LN_BWD, 0.0, ln_bwd_bytes(false), [&] {
       return layernorm_backward(dt, BT, C, d_ln, m->at<char>(lo.resid[l]), m->lparam(2, l),
                                 m->at<float>(o.ln1_mean), m->at<float>(o.ln1_rstd), dres, false, dres_copy,
@@ -704,8 +899,9 @@ int init_params(gpt2_model* m, uint64_t seed) {
 
 // Transposed copies of the weight matrices from the bf16 working copy.
 int refresh_transposed(gpt2_model* m) {
-  if (m->cfg.dtype != GPT2_BF16) return 0;
+  if (!is_bf16(m->cfg)) return 0;
   for (int i : kTransposed) {
+    if (!m->lo.params_t[i]) continue;   // (fp8 mode: only the attention projection keeps a bf16 copy)
     const int64_t* sh = m->lo.pt.shape[i];
     const bool layered = m->lo.pt.ndim[i] == 3;
     const int batches = layered ? (int)sh[0] : 1;
@@ -718,9 +914,28 @@ int refresh_transposed(gpt2_model* m) {
   return 0;
 }
 
+// fp8 mode: E4M3 codes (row-major and transposed) of the fp8 products'
+// weights, quantised per matrix from the fp32 master.
+int refresh_fp8_weights(gpt2_model* m) {
+  if (!m->fp8()) return 0;
+  const int L = m->cfg.num_layers;
+  for (int w = 0; w < 4; ++w) {
+    const int i = kFp8Weights[w];
+    const int64_t* sh = m->lo.pt.shape[i];
+    const bool layered = m->lo.pt.ndim[i] == 3;
+    const int R = (int)(layered ? sh[1] : sh[0]), Cc = (int)(layered ? sh[2] : sh[1]);
+    for (int l = 0; l < (layered ? L : 1); ++l) {
+      const float* src = m->master() + m->lo.pt.off[i] + (int64_t)l * R * Cc;
+      RC(fp8_quant(m, GPT2_FP32, src, R, Cc, 0, fp8_slot(L, Q_WEIGHT, w, l), m->wq(i, l), m->wqt(i, l)));
+    }
+  }
+  return 0;
+}
+
 int refresh_bf16(gpt2_model* m) {
-  if (m->cfg.dtype != GPT2_BF16) return 0;
+  if (!is_bf16(m->cfg)) return 0;
   RC(cast_f32_to_bf16(m->lo.P, m->master(), m->at<bf16>(m->lo.params_bf16), m->stream));
+  RC(refresh_fp8_weights(m));
   return refresh_transposed(m);
 }
 
@@ -735,11 +950,12 @@ int update_impl(gpt2_model* m, float max_grad_norm, bool need_norm) {
              [&] { return grad_norm(m->lo.P, m->grad(), max_grad_norm, gn, m->stream); }));
   }
   // fp32 master, m, v read and written, fp32 gradient read, bf16 copy written
-  RC(timed(m, S_ADAMW, 0.0, (double)m->lo.P * (m->cfg.dtype == GPT2_BF16 ? 30.0 : 28.0), [&] {
+  RC(timed(m, S_ADAMW, 0.0, (double)m->lo.P * (is_bf16(m->cfg) ? 30.0 : 28.0), [&] {
     return adamw(m->lo.P, m->master(), m->grad(), m->at<float>(m->lo.adam_m), m->at<float>(m->lo.adam_v),
-                 m->cfg.dtype == GPT2_BF16 ? m->at<bf16>(m->lo.params_bf16) : nullptr, 0.f, 0.f, 0.f, 0.f, 0.f, 1,
+                 is_bf16(m->cfg) ? m->at<bf16>(m->lo.params_bf16) : nullptr, 0.f, 0.f, 0.f, 0.f, 0.f, 1,
                  m->stream, max_grad_norm > 0.f ? gn + 1 : nullptr, m->at<AdamHP>(m->lo.adam_hp));
   }));
+  RC(refresh_fp8_weights(m));
   return refresh_transposed(m);
 }
 
@@ -766,7 +982,7 @@ const char* site_name(int site) {
       "qkv", "attproj", "fc", "fcproj", "logits", "fcproj_dx", "fcproj_dw", "fc_dx", "fc_dw", "attproj_dx",
       "attproj_dw", "qkv_dx", "qkv_dw", "cls_dx", "cls_dw", "attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq",
       "attn_bwd_dot", "softmax_xent", "ln_fwd", "ln_bwd", "encoder_fwd", "adamw", "weight_transpose", "grad_norm",
-      "qk_fwd", "qk_bwd"};
+      "qk_fwd", "qk_bwd", "fp8_quant"};
   return site >= 0 && site < S_COUNT ? names[site] : "";
 }
 
@@ -780,6 +996,7 @@ void fill_plan(const GemmDesc& d, const char* site, gpt2_gemm_plan* out) {
   out->tile_m = li.tile_m; out->tile_n = li.tile_n;
   out->waves = li.waves; out->k_groups = li.kgroups; out->k_splits = li.splits;
   out->bias_grad = li.bias_grad;
+  out->fp8 = d.fp8;
 }
 
 bool any_timer_on(const gpt2_model* m) {
@@ -1266,6 +1483,133 @@ int gpt2_op_linear_plans(int dtype, int M, int N, int K, int has_bias, int has_r
   fill_plan(linear_dx_desc(dtype, M, N, K, p, p, dtype == GPT2_BF16 ? p : nullptr, p, has_gelu ? EPI_MUL : EPI_STORE,
                            has_gelu ? p : nullptr, p, 0),
             "dX", &out[2]);
+  return GPT2_OK;
+  GPT2_ABI_END_STATUS
+}
+
+size_t gpt2_op_fp8_quantize_workspace_bytes(void) { return fp8_scale_workspace_bytes(); }
+
+int gpt2_op_fp8_quantize(int in_dtype, int fmt, int R, int C, const void* x, float* scale, uint8_t* q, uint8_t* qt,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  GPT2_ABI_BEGIN
+  if (!scale || !workspace || workspace_bytes < fp8_scale_workspace_bytes() || (uintptr_t)scale % 16)
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "fp8_quantize: scale (16-byte aligned) and workspace needed");
+  hipStream_t s = (hipStream_t)stream;
+  Fp8Scale* sc = reinterpret_cast<Fp8Scale*>(scale);
+  RC(fp8_compute_scale(in_dtype, (int64_t)R * C, x, fmt, sc, static_cast<float*>(workspace), s));
+  return fp8_quantize(in_dtype, fmt, R, C, x, C, sc, q, qt, s);
+  GPT2_ABI_END_STATUS
+}
+
+namespace {
+// Workspace of the op-level fp8 linear layer: 4 scales, absmax partials, the
+// codes of x, W (row-major and transposed) and dY (row-major and
+// transposed), then the products' split-K / bias-gradient scratch.
+struct OpFp8Ws {
+  size_t scales, amax, xq, xqt, wq, wqt, dq, dqt, scratch, scratch_bytes, total;
+};
+OpFp8Ws op_fp8_ws(int M, int N, int K) {
+  Plan p;
+  OpFp8Ws w;
+  w.scales = p.alloc(4 * sizeof(Fp8Scale));
+  w.amax = p.alloc(fp8_scale_workspace_bytes());
+  w.xq = p.alloc((size_t)M * K);
+  w.xqt = p.alloc((size_t)M * K);
+  w.wq = p.alloc((size_t)N * K);
+  w.wqt = p.alloc((size_t)N * K);
+  w.dq = p.alloc((size_t)M * N);
+  w.dqt = p.alloc((size_t)M * N);
+  w.scratch_bytes = std::max({gemm_workspace_bytes(GPT2_BF16, EPI_WGRAD, N, K, M, true, true, 2),
+                              gemm_workspace_bytes(GPT2_BF16, EPI_STORE, M, K, N, true, true, 2),
+                              gemm_workspace_bytes(GPT2_BF16, EPI_STORE, M, N, K, true, true, 1),
+                              bias_grad_workspace_bytes(N)});
+  w.scratch = p.alloc(w.scratch_bytes);
+  w.total = p.total;
+  return w;
+}
+}  // namespace
+
+size_t gpt2_op_linear_fp8_workspace_bytes(int M, int N, int K) {
+  GPT2_ABI_BEGIN
+  if (M < 0 || N < 0 || K < 0) return 0;
+  return op_fp8_ws(M, N, K).total;
+  GPT2_ABI_END(0)
+}
+
+int gpt2_op_linear_fp8_forward(int M, int N, int K, const void* x, const void* W, const void* b, const void* residual,
+                               void* y, void* gelu_grad, void* workspace, size_t workspace_bytes, void* stream) {
+  GPT2_ABI_BEGIN
+  if (residual && gelu_grad) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "residual and gelu_grad are exclusive");
+  if ((residual || gelu_grad) && !b)
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "the residual and GELU epilogues need a bias");
+  if (!x || !W || !y || M <= 0 || N <= 0 || K <= 0 || K % 16 || N % 16)
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "linear_fp8_forward: bad arguments (K, N multiples of 16)");
+  const OpFp8Ws w = op_fp8_ws(M, N, K);
+  if (!workspace || workspace_bytes < w.total)
+    return gpt2_internal_fail(GPT2_E_OOM, "linear_fp8_forward: workspace of %zu bytes (need %zu)", workspace_bytes,
+                              w.total);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = static_cast<char*>(workspace);
+  Fp8Scale* sc = reinterpret_cast<Fp8Scale*>(ws + w.scales);
+  float* amax = reinterpret_cast<float*>(ws + w.amax);
+  uint8_t* xq = reinterpret_cast<uint8_t*>(ws + w.xq);
+  uint8_t* wq = reinterpret_cast<uint8_t*>(ws + w.wq);
+  RC(fp8_compute_scale(GPT2_BF16, (int64_t)M * K, x, 0, &sc[0], amax, s));
+  RC(fp8_quantize(GPT2_BF16, 0, M, K, x, K, &sc[0], xq, nullptr, s));
+  RC(fp8_compute_scale(GPT2_BF16, (int64_t)N * K, W, 0, &sc[1], amax, s));
+  RC(fp8_quantize(GPT2_BF16, 0, N, K, W, K, &sc[1], wq, nullptr, s));
+  const int epi = gelu_grad ? EPI_BIAS_GELU_D : residual ? EPI_BIAS_RES : b ? EPI_BIAS : EPI_STORE;
+  GemmDesc d = linear_fwd_desc(GPT2_BF16, M, N, K, xq, wq, epi, y, b, residual, gelu_grad);
+  d.fp8 = 1;
+  d.scale_a = &sc[0].s; d.scale_b = &sc[1].s;
+  d.workspace = ws + w.scratch; d.workspace_bytes = w.scratch_bytes;
+  return gemm(d, s);
+  GPT2_ABI_END_STATUS
+}
+
+int gpt2_op_linear_fp8_backward(int M, int N, int K, const void* dy, const void* x, const void* W,
+                                const void* gelu_grad, void* dx, float* dW, float* db, int accumulate, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  GPT2_ABI_BEGIN
+  if (!dy || M <= 0 || N <= 0 || K <= 0 || K % 16 || N % 16 || M % 16 || (dW && !x) || (dx && !W) || (db && !dW))
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "linear_fp8_backward: bad arguments (M, N, K multiples of 16)");
+  const OpFp8Ws w = op_fp8_ws(M, N, K);
+  if (!workspace || workspace_bytes < w.total)
+    return gpt2_internal_fail(GPT2_E_OOM, "linear_fp8_backward: workspace of %zu bytes (need %zu)", workspace_bytes,
+                              w.total);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = static_cast<char*>(workspace);
+  Fp8Scale* sc = reinterpret_cast<Fp8Scale*>(ws + w.scales);
+  float* amax = reinterpret_cast<float*>(ws + w.amax);
+  uint8_t* dq = reinterpret_cast<uint8_t*>(ws + w.dq);
+  uint8_t* dqt = reinterpret_cast<uint8_t*>(ws + w.dqt);
+  RC(fp8_compute_scale(GPT2_BF16, (int64_t)M * N, dy, 1, &sc[2], amax, s));
+  RC(fp8_quantize(GPT2_BF16, 1, M, N, dy, N, &sc[2], dq, dqt, s));
+  if (dW) {
+    uint8_t* xqt = reinterpret_cast<uint8_t*>(ws + w.xqt);
+    RC(fp8_compute_scale(GPT2_BF16, (int64_t)M * K, x, 0, &sc[0], amax, s));
+    RC(fp8_quantize(GPT2_BF16, 0, M, K, x, K, &sc[0], nullptr, xqt, s));
+    GemmDesc d = gdesc(GPT2_BF16);
+    d.a_kmajor = d.b_kmajor = true;
+    d.M = N; d.N = K; d.K = M;
+    d.A = dqt; d.lda = M; d.B = xqt; d.ldb = M;
+    d.epi = EPI_WGRAD; d.out32 = dW; d.accumulate = accumulate != 0;
+    d.workspace = ws + w.scratch; d.workspace_bytes = w.scratch_bytes;
+    d.fp8 = 2; d.scale_a = &sc[2].s; d.scale_b = &sc[0].s;
+    RC(gemm(d, s));
+    if (db)
+      RC(bias_grad_bf16(M, N, static_cast<const bf16*>(dy), db, accumulate != 0,
+                        reinterpret_cast<float*>(ws + w.scratch), w.scratch_bytes, s));
+  }
+  if (dx) {
+    uint8_t* wqt = reinterpret_cast<uint8_t*>(ws + w.wqt);
+    RC(fp8_compute_scale(GPT2_BF16, (int64_t)N * K, W, 0, &sc[1], amax, s));
+    RC(fp8_quantize(GPT2_BF16, 0, N, K, W, K, &sc[1], nullptr, wqt, s));
+    GemmDesc d = linear_dx_desc(GPT2_BF16, M, N, K, dq, nullptr, wqt, dx, gelu_grad ? EPI_MUL : EPI_STORE, gelu_grad,
+                                ws + w.scratch, w.scratch_bytes);
+    d.fp8 = 2; d.scale_a = &sc[2].s; d.scale_b = &sc[1].s;
+    RC(gemm(d, s));
+  }
   return GPT2_OK;
   GPT2_ABI_END_STATUS
 }

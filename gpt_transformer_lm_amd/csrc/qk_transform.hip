@@ -136,9 +136,11 @@ __global__ __launch_bounds__(256) void qk_bwd_kernel(int BT, int T_, int H, cons
 template <typename T, int HD>
 int launch_fwd(int BT, int T_, int H, void* qkv, float* rstd, const float2* cs, bool norm, bool rope, hipStream_t s) {
   const int64_t lanes = (int64_t)BT * 2 * H * (HD / 8);
+  mark_begin(0, s);
   hipLaunchKernelGGL((qk_fwd_kernel<T, HD>), dim3((unsigned)ceil_div64(lanes, 256)), dim3(256), 0, s, BT, T_, H,
                      static_cast<T*>(qkv), rstd, cs, norm, rope);
   GPT2_LAUNCH_CHECK();
+  mark_end(0, s);
   return 0;
 }
 
@@ -146,9 +148,11 @@ template <typename T, int HD>
 int launch_bwd(int BT, int T_, int H, const void* qkv, void* dqkv, const float* rstd, const float2* cs, bool norm,
                bool rope, hipStream_t s) {
   const int64_t lanes = (int64_t)BT * 2 * H * (HD / 8);
+  mark_begin(0, s);
   hipLaunchKernelGGL((qk_bwd_kernel<T, HD>), dim3((unsigned)ceil_div64(lanes, 256)), dim3(256), 0, s, BT, T_, H,
                      static_cast<const T*>(qkv), static_cast<T*>(dqkv), rstd, cs, norm, rope);
   GPT2_LAUNCH_CHECK();
+  mark_end(0, s);
   return 0;
 }
 

@@ -18,11 +18,12 @@ LIB_PATH = os.path.join(HERE, "libgpt2_hip.so")
 
 GPT2_FP32 = 0
 GPT2_BF16 = 1
+GPT2_BF16_FP8 = 2
 
 SITES = ["qkv", "attproj", "fc", "fcproj", "logits", "fcproj_dx", "fcproj_dw", "fc_dx", "fc_dw",
          "attproj_dx", "attproj_dw", "qkv_dx", "qkv_dw", "cls_dx", "cls_dw", "attn_fwd", "attn_bwd_dkdv",
          "attn_bwd_dq", "attn_bwd_dot", "softmax_xent", "ln_fwd", "ln_bwd", "encoder_fwd", "adamw",
-         "weight_transpose", "grad_norm", "qk_fwd", "qk_bwd"]
+         "weight_transpose", "grad_norm", "qk_fwd", "qk_bwd", "fp8_quant"]
 
 
 GPT2_ARCH_RELU2 = 1
@@ -41,7 +42,7 @@ class Gpt2Config(C.Structure):
 class GemmPlan(C.Structure):
     _fields_ = [("site", C.c_char * 16)] + [(n, C.c_int32) for n in (
         "M", "N", "K", "epilogue", "a_kmajor", "b_kmajor", "tile_m", "tile_n", "waves", "k_groups", "k_splits",
-        "bias_grad")]
+        "bias_grad", "fp8")]
 
     def as_dict(self):
         d = {n: getattr(self, n) for n, _ in self._fields_[1:]}
@@ -109,6 +110,11 @@ def load():
         "gpt2_op_linear_backward_workspace_bytes": (sz, [C.c_int, C.c_int, C.c_int, C.c_int]),
         "gpt2_op_linear_backward": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, vp, vp, vp, vp, vp, vp, vp,
                                               C.c_int, vp, sz, vp]),
+        "gpt2_op_fp8_quantize_workspace_bytes": (sz, []),
+        "gpt2_op_fp8_quantize": (C.c_int, [C.c_int] * 4 + [vp] * 4 + [vp, sz, vp]),
+        "gpt2_op_linear_fp8_workspace_bytes": (sz, [C.c_int] * 3),
+        "gpt2_op_linear_fp8_forward": (C.c_int, [C.c_int] * 3 + [vp] * 7 + [sz, vp]),
+        "gpt2_op_linear_fp8_backward": (C.c_int, [C.c_int] * 3 + [vp] * 7 + [C.c_int, vp, sz, vp]),
         "gpt2_op_layernorm_forward": (C.c_int, [C.c_int, C.c_int, C.c_int, vp, vp, vp, vp, vp, vp, vp]),
         "gpt2_op_layernorm_backward_workspace_bytes": (sz, [C.c_int, C.c_int]),
         "gpt2_op_layernorm_backward": (C.c_int, [C.c_int, C.c_int, C.c_int, vp, vp, vp, vp, vp, vp, C.c_int, vp,
@@ -145,6 +151,8 @@ def exported_symbols():
         "gpt2_get_grads", "gpt2_get_adam_state", "gpt2_get_token_losses", "gpt2_get_logits",
         "gpt2_timing_enable", "gpt2_timing_read",
         "gpt2_op_linear_forward", "gpt2_op_linear_backward_workspace_bytes", "gpt2_op_linear_backward",
+        "gpt2_op_fp8_quantize_workspace_bytes", "gpt2_op_fp8_quantize", "gpt2_op_linear_fp8_workspace_bytes",
+        "gpt2_op_linear_fp8_forward", "gpt2_op_linear_fp8_backward",
         "gpt2_op_layernorm_forward", "gpt2_op_layernorm_backward_workspace_bytes",
         "gpt2_op_layernorm_backward", "gpt2_op_attention_forward",
         "gpt2_op_attention_backward_workspace_bytes", "gpt2_op_attention_backward",
@@ -364,6 +372,36 @@ def linear_backward(dtype, dy, x, W, dx=None, dW=None, db=None, gelu_grad=None, 
     check(lib.gpt2_op_linear_backward(dtype, M, N, K, ptr(dy), ptr(x), ptr(W), ptr(gelu_grad), ptr(dx), ptr(dW),
                                       ptr(db), int(accumulate), ptr(ws), ws.numel(), _stream_ptr(stream)),
           "linear_backward")
+    return ws
+
+
+def fp8_quantize(in_dtype, fmt, x, scale, q=None, qt=None, stream=None):
+    lib = load()
+    R, Cc = x.shape
+    ws = _ws(lib.gpt2_op_fp8_quantize_workspace_bytes())
+    check(lib.gpt2_op_fp8_quantize(in_dtype, fmt, R, Cc, ptr(x), ptr(scale), ptr(q), ptr(qt), ptr(ws), ws.numel(),
+                                   _stream_ptr(stream)), "fp8_quantize")
+    return ws
+
+
+def linear_fp8_forward(x, W, b=None, residual=None, gelu_grad=None, y=None, stream=None):
+    lib = load()
+    M, K = x.shape
+    N = W.shape[0]
+    ws = _ws(lib.gpt2_op_linear_fp8_workspace_bytes(M, N, K))
+    check(lib.gpt2_op_linear_fp8_forward(M, N, K, ptr(x), ptr(W), ptr(b), ptr(residual), ptr(y), ptr(gelu_grad),
+                                         ptr(ws), ws.numel(), _stream_ptr(stream)), "linear_fp8_forward")
+    return ws
+
+
+def linear_fp8_backward(dy, x, W, dx=None, dW=None, db=None, gelu_grad=None, accumulate=False, stream=None):
+    lib = load()
+    M, N = dy.shape
+    K = x.shape[1]
+    ws = _ws(lib.gpt2_op_linear_fp8_workspace_bytes(M, N, K))
+    check(lib.gpt2_op_linear_fp8_backward(M, N, K, ptr(dy), ptr(x), ptr(W), ptr(gelu_grad), ptr(dx), ptr(dW), ptr(db),
+                                          int(accumulate), ptr(ws), ws.numel(), _stream_ptr(stream)),
+          "linear_fp8_backward")
     return ws
 
 

@@ -59,11 +59,22 @@ enum {
 };
 
 enum {
-  GPT2_FP32 = 0, /* every tensor fp32 (parity mode) */
-  GPT2_BF16 = 1  /* bf16 weights copy, activations and activation gradients;
-                    fp32 master weights, parameter gradients, AdamW moments,
-                    LayerNorm statistics, softmax statistics, residual-stream
-                    gradient and every accumulator */
+  GPT2_FP32 = 0,     /* every tensor fp32 (parity mode) */
+  GPT2_BF16 = 1,     /* bf16 weights copy, activations and activation gradients;
+                        fp32 master weights, parameter gradients, AdamW moments,
+                        LayerNorm statistics, softmax statistics, residual-stream
+                        gradient and every accumulator */
+  GPT2_BF16_FP8 = 2  /* GPT2_BF16, with the products of the QKV projection,
+                        the MLP (fc, fc-proj) and the head (logits) forward and
+                        backward in FP8 ("NanoGPT (124M) in 90 seconds",
+                        section "How it works", item "Precision & Hardware"):
+                        OCP E4M3 weights (quantised from the fp32 master after
+                        every update) and activations, OCP E5M2 output
+                        gradients, per-tensor scales from each tensor's
+                        absolute maximum (inv = FMAX / amax, s = amax / FMAX in
+                        fp32), round to nearest even, fp32 accumulation, the
+                        sums multiplied by s_a s_b; bias gradients from the
+                        unquantised gradient */
 };
 
 /* Architecture variants of the block ("NanoGPT (124M) in 90 seconds",
@@ -281,8 +292,9 @@ int gpt2_get_logits(gpt2_model* m, float* host_out);
  * copies (written after each AdamW step for the dX products), 25 gradient
  * norm (partial sums of squares; gpt2_adamw_step_clipped), 26 QK-Norm /
  * rotary transform of q and k, 27 its backward (GPT2_ARCH_QK_NORM or
- * GPT2_ARCH_ROPE).  Events are recorded on the model's stream immediately
- * around that kernel.  Sites are valid in [0, 28); others give
+ * GPT2_ARCH_ROPE), 28 fp8 quantisation (the codes of one operand;
+ * GPT2_BF16_FP8).  Events are recorded on the model's stream immediately
+ * around that kernel.  Sites are valid in [0, 29); others give
  * GPT2_E_INVALID_ARG. */
 int gpt2_timing_enable(gpt2_model* m, int site, int enable);
 /* Total elapsed milliseconds and launch count recorded for a site since it

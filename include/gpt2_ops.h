@@ -94,6 +94,7 @@ typedef struct gpt2_gemm_plan {
   int32_t k_groups;             /* groups of waves splitting each K step         */
   int32_t k_splits;             /* blocks splitting K (partial sums)             */
   int32_t bias_grad;            /* 1: bias gradient fused into the dW product     */
+  int32_t fp8;                  /* 0 bf16 / fp32; 1 fp8 E4M3 x E4M3; 2 fp8 E5M2 x E4M3 */
 } gpt2_gemm_plan;
 
 /* Every GEMM one training step of cfg launches (forward with targets, then
@@ -105,6 +106,35 @@ int gpt2_step_gemm_plans(const gpt2_config* cfg, gpt2_gemm_plan* out, int max_pl
  * these shapes and options: out[0] the forward, out[1] dW, out[2] dX. */
 int gpt2_op_linear_plans(int dtype, int M, int N, int K, int has_bias, int has_residual, int has_gelu,
                          int has_db, gpt2_gemm_plan out[3]);
+
+/* ---- FP8 products ("NanoGPT (124M) in 90 seconds", section "How it works",
+ * item "Precision & Hardware"; the training step's GPT2_BF16_FP8 mode) ------
+ * Per-tensor scaling from the tensor's absolute maximum: inv = FMAX / amax
+ * and s = amax / FMAX in fp32 (1 and 1 for amax = 0), FMAX = 448 (fmt 0, OCP
+ * E4M3) or 57344 (fmt 1, OCP E5M2); code = fp8(fp32(x * inv)), round to
+ * nearest even with subnormals. */
+
+/* scale [4] f32 (device, 16-byte aligned) = {amax, inv, s, 0}; q [R, C] and
+ * / or qt [C, R] (either may be NULL) receive the codes of x [R, C] (in_dtype
+ * GPT2_FP32 or GPT2_BF16), row-major and transposed.  C % 8 == 0, R % 16 ==
+ * 0 when qt.  workspace: gpt2_op_fp8_quantize_workspace_bytes() bytes. */
+size_t gpt2_op_fp8_quantize_workspace_bytes(void);
+int gpt2_op_fp8_quantize(int in_dtype, int fmt, int R, int C, const void* x, float* scale, uint8_t* q,
+                         uint8_t* qt, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The step's fp8 linear layer on bf16 buffers (same arguments and epilogues
+ * as gpt2_op_linear_forward / _backward in GPT2_BF16): x and W are quantised
+ * to E4M3 and dy to E5M2 per tensor inside the call (into the workspace),
+ * y = s_x s_w Q(x) Q(W)^T (+ epilogue), dx = s_dy s_w Q(dy) Q(W),
+ * dW = s_dy s_x Q(dy)^T Q(x) (fp32 accumulation), db = the sum over rows of
+ * the unquantised dy.  M, N, K multiples of 16 (N, K for the forward). */
+size_t gpt2_op_linear_fp8_workspace_bytes(int M, int N, int K);
+int gpt2_op_linear_fp8_forward(int M, int N, int K, const void* x, const void* W, const void* b,
+                               const void* residual, void* y, void* gelu_grad, void* workspace,
+                               size_t workspace_bytes, void* stream);
+int gpt2_op_linear_fp8_backward(int M, int N, int K, const void* dy, const void* x, const void* W,
+                                const void* gelu_grad, void* dx, float* dW, float* db, int accumulate,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* LayerNorm forward over rows of C (eps 1e-5, biased variance):
  *   x [N, C] T, w, b [C] T -> y [N, C] T, mean [N] f32, rstd [N] f32. C % 8 == 0. */

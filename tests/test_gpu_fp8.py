@@ -1,0 +1,225 @@
+"""FP8 products ("NanoGPT (124M) in 90 seconds", precision item) on the GPU
+against the oracle's FP8 arithmetic (oracle/fp8.py), through the C ABI.
+
+* Quantisation: the same bf16 / fp32 inputs on both sides give the same
+  per-tensor scale and the same codes, bit for bit (row-major and
+  transposed; E4M3 and E5M2).
+* FP8 linear layers: on the same bf16 inputs both sides quantise to the same
+  codes, so the products differ only by the accumulation and the bf16
+  rounding of the outputs: 3e-3 for bf16 outputs; 1e-4 for the fp32 weight
+  gradient, because the fp8 matrix instruction sums the 64 products of each
+  step to about 2^-17 relative precision, not fp32's 2^-24 (measured: 1.2e-5
+  rel L2 even where every output is one instruction, K = 64; the bf16
+  instruction meets 1e-5).
+* The training step in GPT2_BF16_FP8 mode against the oracle's FP8 model.
+  Here the GPU quantises its bf16 activations and gradients and the oracle
+  its float32 ones: a bf16 rounding (relative 2^-9) moves an E4M3 code
+  (relative spacing 2^-3 .. 2^-4) to its neighbour for ~2 x 2^-9 / 2^-3 ~ 3 %
+  of the elements (E5M2: ~1.5 %), each such element off by one spacing, so
+  each fp8 product carries ~2-3 % relative noise that the plain bf16 path does
+  not.  Bars: loss rel <= 1e-2, gradient tensors rel L2 <= 1e-1, post-AdamW
+  parameters rel L2 <= 3e-2.
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+from gpt_transformer_lm_amd import lib
+from gpt_transformer_lm_amd import synthetic as S
+from gpu_util import BF16, FP32, as_input, dev, dev_i32, empty, empty32, host, rel, say, torch_mod
+
+pytestmark = pytest.mark.gpu
+FMTS = {0: O.E4M3, 1: O.E5M2}
+
+
+def rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def codes_equal(gpu, ref):
+    """Bit-exact, except that +0 and -0 count as equal."""
+    g = np.asarray(gpu, dtype=np.uint8)
+    r = np.asarray(ref, dtype=np.uint8)
+    zero = ((g & 0x7F) == 0) & ((r & 0x7F) == 0)
+    return np.array_equal(np.where(zero, 0, g), np.where(zero, 0, r))
+
+
+@pytest.mark.parametrize("fmt", [0, 1], ids=["e4m3", "e5m2"])
+@pytest.mark.parametrize("in_dtype", [BF16, FP32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("R,Cc", [(208, 136), (16, 8), (2048, 768)])
+def test_quantize_matches_oracle_codes(fmt, in_dtype, R, Cc):
+    torch = torch_mod()
+    say("fp8 quantize", FMTS[fmt].name, "bf16" if in_dtype == BF16 else "fp32", R, Cc)
+    r = rng(R * 3 + Cc + fmt)
+    x = r.standard_normal((R, Cc)) * np.exp(r.uniform(-12, 2, (R, Cc)))    # wide dynamic range, subnormal codes
+    x[0, :3] = [0.0, -0.0, 5.0]
+    xi = as_input(x, in_dtype)                                              # the values the kernel reads (float32)
+    scale = torch.zeros(4, dtype=torch.float32, device="cuda")
+    q = torch.full((R, Cc), 0xAA, dtype=torch.uint8, device="cuda")
+    qt = torch.full((Cc, R), 0xAA, dtype=torch.uint8, device="cuda")
+    lib.fp8_quantize(in_dtype, fmt, dev(x, in_dtype), scale, q, qt)
+    torch.cuda.synchronize()
+    f = FMTS[fmt]
+    qref, sref = O.quantize(xi, f)
+    inv, s = O.fp8_scales(np.max(np.abs(xi)), f)
+    sc = scale.cpu().numpy()
+    assert sc[0] == np.max(np.abs(xi)) and sc[1] == inv and sc[2] == s and sref == s
+    ref_codes = O.fp8_encode(qref, f)
+    assert codes_equal(q.cpu().numpy(), ref_codes)
+    assert codes_equal(qt.cpu().numpy(), ref_codes.T)
+
+
+def test_quantize_zero_tensor_has_unit_scale():
+    torch = torch_mod()
+    scale = torch.zeros(4, dtype=torch.float32, device="cuda")
+    q = torch.full((32, 64), 0xAA, dtype=torch.uint8, device="cuda")
+    lib.fp8_quantize(BF16, 0, torch.zeros((32, 64), dtype=torch.bfloat16, device="cuda"), scale, q)
+    torch.cuda.synchronize()
+    assert list(scale.cpu().numpy()[:3]) == [0.0, 1.0, 1.0]
+    assert np.all(q.cpu().numpy() == 0)
+
+
+SHAPES8 = [(64, 64, 64), (208, 144, 160), (2064, 2080, 784), (320, 8192, 96)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES8)
+@pytest.mark.parametrize("epi", ["store", "bias", "bias_res", "bias_gelu"])
+def test_linear_fp8_forward(M, N, K, epi):
+    torch_mod()
+    say("fp8 linear forward", M, N, K, epi)
+    r = rng(M + 5 * N + K)
+    x, W = r.standard_normal((M, K)), r.standard_normal((N, K)) * 0.05
+    b, res = r.standard_normal(N) * 0.3, r.standard_normal((M, N))
+    xi, Wi, bi, ri = (as_input(a, BF16).astype(np.float64) for a in (x, W, b, res))
+    y = empty((M, N), BF16)
+    g = empty((M, N), BF16) if epi == "bias_gelu" else None
+    lib.linear_fp8_forward(dev(x, BF16), dev(W, BF16), b=None if epi == "store" else dev(b, BF16),
+                           residual=dev(res, BF16) if epi == "bias_res" else None, gelu_grad=g, y=y)
+    ref, _ = O.fp8_linear_forward(xi, Wi, None if epi == "store" else bi)
+    if epi == "bias_res":
+        ref = ref + ri
+    if g is None:
+        assert rel(host(y), ref) < 3e-3
+    else:
+        assert rel(host(y), O.gelu_tanh(ref)) < 3e-3
+        assert rel(host(g), O.gelu_tanh_backward(ref, np.ones_like(ref))) < 3e-3
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES8)
+@pytest.mark.parametrize("gelu", [False, True])
+def test_linear_fp8_backward(M, N, K, gelu):
+    torch_mod()
+    say("fp8 linear backward", M, N, K, "gelu" if gelu else "")
+    r = rng(7 * M + N + 3 * K + gelu)
+    dy, x, W = r.standard_normal((M, N)) * 1e-3, r.standard_normal((M, K)), r.standard_normal((N, K)) * 0.05
+    d = O.gelu_tanh_backward(r.standard_normal((M, K)), np.ones((M, K)))
+    dyi, xi, Wi, di = (as_input(a, BF16).astype(np.float64) for a in (dy, x, W, d))
+    dx, dW, db = empty((M, K), BF16), empty32((N, K)), empty32((N,))
+    lib.linear_fp8_backward(dev(dy, BF16), dev(x, BF16), dev(W, BF16), dx=dx, dW=dW, db=db,
+                            gelu_grad=dev(d, BF16) if gelu else None)
+    _, cache = O.fp8_linear_forward(xi, Wi)
+    rdx, rdw, rdb = O.fp8_linear_backward(dyi, cache)
+    if gelu:
+        rdx = rdx * di
+    assert rel(host(dx), rdx) < 3e-3
+    assert rel(host(dW), rdw) < 1e-4
+    assert rel(host(db), rdb) < 1e-5
+
+
+# The fp8 products of the GPT-2 124M step at full size (B*T = 24576), each
+# with its step epilogue; 512 sampled outputs of each product against the
+# oracle's fp8 product of the same bf16 operands.
+FULL8 = [("qkv", 2304, 768, dict(bias=True)), ("fc", 3072, 768, dict(gelu=True)),
+         ("fcproj", 768, 3072, dict(residual=True)), ("logits", 50304, 768, dict())]
+
+
+@pytest.mark.parametrize("site,N,K,kw", FULL8, ids=[f[0] for f in FULL8])
+def test_linear_fp8_full_size_sampled(site, N, K, kw):
+    torch = torch_mod()
+    M = 24576
+    say("fp8 full-size", site, M, N, K)
+    gen = torch.Generator(device="cuda").manual_seed(5 + N)
+    bf = torch.bfloat16
+    x = torch.randn((M, K), generator=gen, device="cuda").to(bf)
+    W = (torch.randn((N, K), generator=gen, device="cuda") * 0.05).to(bf)
+    b = (torch.randn((N,), generator=gen, device="cuda") * 0.1).to(bf) if kw else None
+    res = torch.randn((M, N), generator=gen, device="cuda").to(bf) if kw.get("residual") else None
+    dy = (torch.randn((M, N), generator=gen, device="cuda") * 1e-3).to(bf)
+    y = torch.empty((M, N), dtype=bf, device="cuda")
+    g = torch.empty((M, N), dtype=bf, device="cuda") if kw.get("gelu") else None
+    lib.linear_fp8_forward(x, W, b=b, residual=res, gelu_grad=g, y=y)
+    dx = torch.empty((M, K), dtype=bf, device="cuda")
+    dW = torch.empty((N, K), dtype=torch.float32, device="cuda")
+    lib.linear_fp8_backward(dy, x, W, dx=dx, dW=dW)
+    torch.cuda.synchronize()
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
+    xs, Ws, dys = f64(x), f64(W), f64(dy)
+    qx, sx = O.quantize(xs, O.E4M3)
+    qw, sw = O.quantize(Ws, O.E4M3)
+    qd, sd = O.quantize(dys, O.E5M2)
+    r = rng(N + K)
+    im, in_, ik = r.integers(0, M, 512), r.integers(0, N, 512), r.integers(0, K, 512)
+    u = np.einsum("ik,ik->i", qx[im], qw[in_]) * np.float64(np.float32(sx * sw))
+    if b is not None:
+        u = u + f64(b)[in_]
+    if res is not None:
+        u = u + f64(res)[im, in_]
+    yg = f64(y)[im, in_]
+    assert rel(yg, O.gelu_tanh(u) if g is not None else u) < 3e-3
+    rdx = np.einsum("in,in->i", qd[im], qw[:, ik].T) * np.float64(np.float32(sd * sw))
+    assert rel(f64(dx)[im, ik], rdx) < 3e-3
+    rdw = np.einsum("mi,mi->i", qd[:, in_], qx[:, ik]) * np.float64(np.float32(sd * sx))
+    assert rel(dW.cpu().numpy()[in_, ik], rdw) < 1e-4
+
+
+# ---------------------------------------------------------------- the step in fp8 mode
+
+TINY8 = dict(V=512, Vp=512, maxT=64, L=2, H=4, C_=64, B=4, T=64)
+MID8 = dict(V=50257, Vp=50304, maxT=1024, L=2, H=12, C_=768, B=4, T=1024)
+
+
+def fp8_step_parity(c, params, tok, tgt, adam, odtype, ltol=1e-2, gtol=1e-1, ptol=3e-2):
+    cfg = lib.make_config(c["V"], c["Vp"], c["maxT"], c["L"], c["H"], c["C_"], c["B"], c["T"], lib.GPT2_BF16_FP8)
+    model = lib.Model(cfg, seed=0)
+    model.set_params(lib.flatten_params(cfg, params))
+    loss = model.forward(dev_i32(tok), dev_i32(tgt))
+    model.backward()
+    grads = lib.unflatten(cfg, model.get_grads())
+    model.adamw_step(adam["lr"], adam["beta1"], adam["beta2"], adam["eps"], adam["weight_decay"], 1)
+    after = lib.unflatten(cfg, model.get_params())
+    model.close()
+    oc = O.OracleConfig(vocab_size=c["V"], max_seq_len=c["maxT"], num_layers=c["L"], num_heads=c["H"],
+                        channels=c["C_"], fp8=True)
+    op = {k: v.astype(odtype) for k, v in params.items()}
+    op["wte"] = op["wte"][: c["V"]].copy()
+    oloss, ograds, oafter, _ = O.gpt2_step(op, tok, tgt, oc, None, adam["lr"], adam["beta1"], adam["beta2"],
+                                           adam["eps"], adam["weight_decay"], 1)
+    say("fp8 loss", loss, "oracle", float(oloss))
+    worst = {n: rel(grads[n][: c["V"]] if n == "wte" else grads[n], g) for n, g in ograds.items()}
+    say("fp8 grad rel L2", {k: f"{v:.2e}" for k, v in worst.items()})
+    flat_a = np.concatenate([(after[k][: c["V"]] if k == "wte" else after[k]).reshape(-1) for k in oafter])
+    flat_o = np.concatenate([oafter[k].reshape(-1) for k in oafter])
+    prel = rel(flat_a, flat_o)
+    say("fp8 post-AdamW rel L2", prel)
+    assert abs(loss - oloss) / abs(oloss) <= ltol
+    assert all(v <= gtol for v in worst.values()), worst
+    assert prel <= ptol
+    assert np.all(grads["wte"][c["V"]:] == 0.0)
+
+
+def test_tiny_fp8_step_parity():
+    say("tiny fp8 step")
+    params = S.random_params(512, 512, 64, 2, 64, seed=1401, perturbed=True)
+    tok, tgt = S.uniform_batch(4, 64, 512, seed=1402)
+    fp8_step_parity(TINY8, params, tok, tgt, dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0),
+                    np.float64)
+
+
+def test_mid_fp8_step_parity():
+    say("mid fp8 step (124M widths, L = 2, B = 4, T = 1024)")
+    c = MID8
+    params = S.random_params(c["V"], c["Vp"], c["maxT"], c["L"], c["C_"], seed=1501, perturbed=True)
+    tok, tgt = S.zipf_batch(c["B"], c["T"], seed=1502)
+    fp8_step_parity(c, params, tok, tgt, dict(lr=6e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1),
+                    np.float32)
