@@ -135,6 +135,42 @@ __device__ __forceinline__ bf16x8 frag_tr(const GPT2_LDS char* t, int d0, int r0
   return out;
 }
 
+// The same two reads with the per-lane byte offsets precomputed (frag_off /
+// frag_tr_off below), for loops whose tile base is a compile-time LDS address:
+// each read is then one instruction with an immediate offset.
+__device__ __forceinline__ uint32_t frag_off(int row0, int s, int lane) {
+  const int row = row0 + (lane & 31), c = 2 * s + (lane >> 5);
+  return (uint32_t)(row * 128 + swz(row, c) * 16);
+}
+__device__ __forceinline__ uint32_t frag_tr_off(int d0, int r0, int r, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int d = d0 + 16 * (g & 1) + 4 * (i & 3);
+  const int row = r0 + 4 * (g >> 1) + 8 * r + (i >> 2);
+  return (uint32_t)(row * 128 + swz(row, d >> 3) * 16 + (d & 7) * 2);
+}
+// Keeps a precomputed offset in one register (the compiler would otherwise
+// re-form it from its parts with an add before every read).
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+__device__ __forceinline__ bf16x8 frag_at(const GPT2_LDS char* t, uint32_t off) {
+  return *reinterpret_cast<const GPT2_LDS bf16x8*>(t + off);
+}
+__device__ __forceinline__ bf16x8 frag_tr_at(const GPT2_LDS char* t, uint32_t off0, uint32_t off1) {
+  const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      const_cast<GPT2_LDS bf16x4*>(reinterpret_cast<const GPT2_LDS bf16x4*>(t + off0)));
+  const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      const_cast<GPT2_LDS bf16x4*>(reinterpret_cast<const GPT2_LDS bf16x4*>(t + off1)));
+  bf16x8 out;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    out[e] = v0[e];
+    out[4 + e] = v1[e];
+  }
+  return out;
+}
+
 // Row (lane % 32) of a global [row][64] matrix as four B-operand fragments.
 __device__ __forceinline__ void frags_global(const bf16* G, size_t ld, int row, int nrows, int lane, bf16x8 f[4]) {
 #pragma unroll
@@ -179,7 +215,6 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_mfma_kernel(int T, int H, con
   const int ld = 3 * C;
   const bf16* Bg = qkv + (size_t)b * T * ld;                 // row 0 of this sequence
   const bf16* Qg = Bg + h * HD;
-  const i32x4_rsrc rs = make_rsrc4(Bg, (uint32_t)((size_t)T * ld * 2));
   const int q0 = qt * ROWS, qw0 = q0 + wave * 32, myq = qw0 + (lane & 31);
   const float sl2 = scale * kLog2e;
 
@@ -194,96 +229,139 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_mfma_kernel(int T, int H, con
 
   const int kend = min(T, q0 + ROWS);
   const int nst = (kend + STAGE - 1) / STAGE;
-  auto issue = [&](int st) {
-    GPT2_LDS char* base = (GPT2_LDS char*)ring[st % NS];
-    tile_dma(rs, base, wave, lane, st * STAGE, ld, C + h * HD);
-    tile_dma(rs, base + TILE, wave, lane, st * STAGE, ld, 2 * C + h * HD);
+  // Per-lane byte offsets of this wave's two DMA instructions per tile,
+  // relative to the first row of a stage; each stage gets a buffer resource
+  // based at its first key row (scalar arithmetic), so the range check still
+  // zero-fills rows past the sequence end and the lane offsets stay fixed.
+  uint32_t koff[2], voff[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int iq = wave * 2 + q;
+    const int r = 8 * iq + (lane >> 3);
+    const int c = (lane & 7) ^ ((r ^ (r >> 3)) & 7);
+    koff[q] = (uint32_t)((r * ld + C + h * HD + c * 8) * 2);
+    voff[q] = (uint32_t)((r * ld + 2 * C + h * HD + c * 8) * 2);
+  }
+  auto issue = [&](int st, int slot) {
+    const int row0 = st * STAGE;
+    const i32x4_rsrc rst = make_rsrc4(Bg + (size_t)row0 * ld, (uint32_t)((size_t)(T - row0) * ld * 2));
+    GPT2_LDS char* base = (GPT2_LDS char*)ring[slot];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int iq = wave * 2 + q;
+      dma_lds16(rst, (GPT2_LDS void*)(base + iq * 1024), koff[q]);
+      dma_lds16(rst, (GPT2_LDS void*)(base + TILE + iq * 1024), voff[q]);
+    }
   };
+  // LDS offsets of the K fragments (slice u2, k16 step k) and of the two
+  // halves of the transposed V fragments (d block dt, 16-key group j, half r)
+  uint32_t koffs[2][4], voffs[2][4][2];
+#pragma unroll
+  for (int u2 = 0; u2 < 2; ++u2)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) koffs[u2][k] = opaque(frag_off(32 * u2, k, lane));
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) voffs[dt][j][r] = opaque(frag_tr_off(32 * dt, 16 * j, r, lane));
   // the fragments loaded to registers above have landed: the compiler's own
   // waits for them would otherwise sit in the loop and drain the DMA ring
   wait_vmcnt<0>();
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    if (s < nst) issue(s);
-  for (int st = 0; st < nst; ++st) {
-    // this wave's part of stage st has landed, then everyone's has; the ring
-    // slot refilled next was last read in the previous iteration
-    if (st + NS - 2 < nst) wait_vmcnt<(NS - 2) * 4>();
-    else wait_vmcnt<0>();
-    lds_barrier();
-    if (st + NS - 1 < nst) issue(st + NS - 1);
-    const GPT2_LDS char* Kc = (const GPT2_LDS char*)ring[st % NS];
-    const GPT2_LDS char* Vc = Kc + TILE;
-    const int k0 = st * STAGE;
-    // Both 32-key slices' score products first, then one softmax update for
-    // the 64 keys (one max exchange, one rescale), then both P V products.
-    // The second slice is skipped when it lies wholly above this wave's
-    // diagonal; keys k0 .. k0 + 31 always include key k0 <= every query of
-    // the wave, so the running maximum is finite from the first stage on.
-    if (k0 <= qw0 + 31 && k0 < T) {
-      const bool two = k0 + 32 <= qw0 + 31 && k0 + 32 < T;
-      floatx16 s[2];
+    if (s < nst) issue(s, s);
+  // The stage loop is unrolled by the ring depth so that every LDS address is
+  // a per-lane offset computed once plus an immediate.
+  for (int st0 = 0; st0 < nst; st0 += NS) {
 #pragma unroll
-      for (int u2 = 0; u2 < 2; ++u2) {
-        if (u2 == 0 || two) {
+    for (int sl = 0; sl < NS; ++sl) {
+      const int st = st0 + sl;
+      if (st >= nst) break;
+      // this wave's part of stage st has landed, then everyone's has; the ring
+      // slot refilled next was last read in the previous iteration
+      if (st + NS - 2 < nst) wait_vmcnt<(NS - 2) * 4>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      if (st + NS - 1 < nst) issue(st + NS - 1, (sl + NS - 1) % NS);
+      const GPT2_LDS char* Kc = (const GPT2_LDS char*)ring[sl];
+      const GPT2_LDS char* Vc = Kc + TILE;
+      const int k0 = st * STAGE;
+      // Both 32-key slices' score products first, then one softmax update for
+      // the 64 keys (one max exchange, at most one rescale), then both P V
+      // products.  The second slice is skipped when it lies wholly above this
+      // wave's diagonal; keys k0 .. k0 + 31 always include key k0 <= every
+      // query of the wave, so the running maximum is finite from the first
+      // stage on.
+      if (k0 <= qw0 + 31 && k0 < T) {
+        const bool two = k0 + 32 <= qw0 + 31 && k0 + 32 < T;
+        floatx16 s[2];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[u2][r] = 0.f;
+        for (int u2 = 0; u2 < 2; ++u2) {
+          if (u2 == 0 || two) {
 #pragma unroll
-          for (int k = 0; k < 4; ++k) s[u2] = mfma(frag_nat(Kc, 32 * u2, k, lane), qf[k], s[u2]);
+            for (int r = 0; r < 16; ++r) s[u2][r] = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) s[u2] = mfma(frag_at(Kc, koffs[u2][k]), qf[k], s[u2]);
+          }
         }
-      }
-      float mx = -INFINITY;
+        float mx = -INFINITY;
 #pragma unroll
-      for (int u2 = 0; u2 < 2; ++u2) {
-        if (u2 == 0 || two) {
-          const int kb = k0 + 32 * u2;
-          // the causal / end-of-sequence mask only touches slices on the
-          // diagonal (a wave-uniform test, so the common case runs unmasked)
-          if ((kb + 31 > qw0) || (kb + 32 > T)) {
+        for (int u2 = 0; u2 < 2; ++u2) {
+          if (u2 == 0 || two) {
+            const int kb = k0 + 32 * u2;
+            // the causal / end-of-sequence mask only touches slices on the
+            // diagonal (a wave-uniform test, so the common case runs unmasked)
+            if ((kb + 31 > qw0) || (kb + 32 > T)) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int key = kb + acc_row(r, lane);
+                if (key > myq || key >= T) s[u2][r] = -INFINITY;
+              }
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[u2][r]);
+          }
+        }
+        mx = half_max(mx);
+        // The exponent's reference m_i only moves when some lane's maximum
+        // exceeds it by more than 2^8 (a wave-uniform vote): below that the
+        // probabilities exp2(s - m_i) stay under 256 and the row sum and O
+        // just carry the common factor, which the final division and the
+        // log-sum-exp (taken against the same m_i) remove exactly.  On the
+        // first stage m_i = -inf, so it always moves there.
+        const float m_run = fmaxf(m_i, mx * sl2);   // sl2 > 0: scaled max = max of scaled
+        if (__any(m_run > m_i + 8.0f)) {
+          const float alpha = ex2(m_i - m_run);
+          l_i *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+          m_i = m_run;
+        }
+#pragma unroll
+        for (int u2 = 0; u2 < 2; ++u2) {
+          if (u2 == 0 || two) {
+            float rs_ = 0.f;
+            bf16x8 pb[2];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int key = kb + acc_row(r, lane);
-              if (key > myq || key >= T) s[u2][r] = -INFINITY;
+              const float p = ex2(fmaf(s[u2][r], sl2, -m_i));
+              rs_ += p;
+              pb[r >> 3][r & 7] = (bf16)p;
             }
+            // l_i is this half-wave's share of the row sum (both halves use
+            // the same reference, so their shares add up at the end)
+            l_i += rs_;
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+              for (int dt = 0; dt < 2; ++dt)
+                oacc[dt] = mfma(frag_tr_at(Vc, voffs[dt][2 * u2 + u][0], voffs[dt][2 * u2 + u][1]), pb[u],
+                                oacc[dt]);
           }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[u2][r]);
-        }
-      }
-      mx = half_max(mx);
-      // the scale sl2 is positive, so the maximum of the scaled scores is the
-      // scaled maximum; the scaling then folds into the exponent's fma
-      const float m_new = fmaxf(m_i, mx * sl2);
-      // rescale the running sum and O only when some lane's maximum grew
-      // (otherwise the factor is exactly 1); the vote is wave-uniform
-      if (__any(m_new > m_i)) {
-        const float alpha = ex2(m_i - m_new);
-        l_i *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-      }
-      m_i = m_new;
-#pragma unroll
-      for (int u2 = 0; u2 < 2; ++u2) {
-        if (u2 == 0 || two) {
-          float rs_ = 0.f;
-          bf16x8 pb[2];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = ex2(fmaf(s[u2][r], sl2, -m_new));
-            rs_ += p;
-            pb[r >> 3][r & 7] = (bf16)p;
-          }
-          // l_i is this half-wave's share of the row sum (both halves see the
-          // same maximum, so their shares add up at the end)
-          l_i += rs_;
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int dt = 0; dt < 2; ++dt)
-              oacc[dt] = mfma(frag_tr(Vc, dt * 32, 32 * u2 + 16 * u, lane), pb[u], oacc[dt]);
         }
       }
     }
@@ -315,10 +393,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
   const bf16* Kg = Bg + C + h * HD;
   const bf16* Vg = Bg + 2 * C + h * HD;
   const bf16* Og = dout + (size_t)b * T * C;
-  const i32x4_rsrc rq = make_rsrc4(Bg, (uint32_t)((size_t)T * ld * 2));
-  const i32x4_rsrc ro = make_rsrc4(Og, (uint32_t)((size_t)T * C * 2));
-  const i32x4_rsrc rl = make_rsrc4(lse2 + (size_t)bh * T, (uint32_t)(T * 4));
-  const i32x4_rsrc rd = make_rsrc4(Dv + (size_t)bh * T, (uint32_t)(T * 4));
   const int k0 = ktile * ROWS, kw0 = k0 + wave * 32, mykey = kw0 + (lane & 31);
   const float sl2 = scale * kLog2e;
 
@@ -333,93 +407,138 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
 
   const int qbeg = k0;                          // queries before the tile see none of its keys
   const int nst = T > qbeg ? (T - qbeg + STAGE - 1) / STAGE : 0;
-  auto issue = [&](int st) {
-    GPT2_LDS char* base = (GPT2_LDS char*)ring[st % NS];
+  // DMA with fixed per-lane offsets and one set of buffer resources per stage
+  // based at its first query row (scalar arithmetic; the range check still
+  // zero-fills rows past the sequence end)
+  uint32_t qoff[2], ooff[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int iq = wave * 2 + q;
+    const int r = 8 * iq + (lane >> 3);
+    const int c = (lane & 7) ^ ((r ^ (r >> 3)) & 7);
+    qoff[q] = (uint32_t)((r * ld + h * HD + c * 8) * 2);
+    ooff[q] = (uint32_t)((r * C + h * HD + c * 8) * 2);
+  }
+  const uint32_t vecoff = lane < 16 ? (uint32_t)(16 * lane) : kOut;
+  auto issue = [&](int st, int slot) {
+    GPT2_LDS char* base = (GPT2_LDS char*)ring[slot];
     const int q0 = qbeg + st * STAGE;
-    tile_dma(rq, base, wave, lane, q0, ld, h * HD);
-    tile_dma(ro, base + TILE, wave, lane, q0, C, h * HD);
-    if (wave == 0) vec_dma(rl, base + 2 * TILE, lane, q0);
-    if (wave == 1) vec_dma(rd, base + 2 * TILE + 1024, lane, q0);
+    const i32x4_rsrc rq = make_rsrc4(Bg + (size_t)q0 * ld, (uint32_t)((size_t)(T - q0) * ld * 2));
+    const i32x4_rsrc ro = make_rsrc4(Og + (size_t)q0 * C, (uint32_t)((size_t)(T - q0) * C * 2));
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int iq = wave * 2 + q;
+      dma_lds16(rq, (GPT2_LDS void*)(base + iq * 1024), qoff[q]);
+      dma_lds16(ro, (GPT2_LDS void*)(base + TILE + iq * 1024), ooff[q]);
+    }
+    if (wave == 0)
+      dma_lds16(make_rsrc4(lse2 + (size_t)bh * T + q0, (uint32_t)((T - q0) * 4)), (GPT2_LDS void*)(base + 2 * TILE),
+                vecoff);
+    if (wave == 1)
+      dma_lds16(make_rsrc4(Dv + (size_t)bh * T + q0, (uint32_t)((T - q0) * 4)),
+                (GPT2_LDS void*)(base + 2 * TILE + 1024), vecoff);
   };
+  // LDS offsets of the Q / dO fragments (32-query slice u2, k16 step k), of
+  // the two halves of the transposed ones (d block dt, 16-query group j) and
+  // of this lane's lse / D values
+  uint32_t noffs[2][4], toffs[2][4][2];
+#pragma unroll
+  for (int u2 = 0; u2 < 2; ++u2)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) noffs[u2][k] = frag_off(32 * u2, k, lane);
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) toffs[dt][j][r] = frag_tr_off(32 * dt, 16 * j, r, lane);
+  const uint32_t ldoff = (uint32_t)(16 * (lane >> 5));
   // the fragments loaded to registers above have landed: the compiler's own
   // waits for them would otherwise sit in the loop and drain the DMA ring
   wait_vmcnt<0>();
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    if (s < nst) issue(s);
-  for (int st = 0; st < nst; ++st) {
-    // at most 5 DMA instructions per wave and stage: waiting until (NS - 2) * 4
-    // remain is sufficient for every wave
-    if (st + NS - 2 < nst) wait_vmcnt<(NS - 2) * 4>();
-    else wait_vmcnt<0>();
-    lds_barrier();
-    if (st + NS - 1 < nst) issue(st + NS - 1);
-    const GPT2_LDS char* Qs = (const GPT2_LDS char*)ring[st % NS];
-    const GPT2_LDS char* Os = Qs + TILE;
-    const GPT2_LDS float* Ls = reinterpret_cast<const GPT2_LDS float*>(Qs + 2 * TILE);
-    const GPT2_LDS float* Ds = reinterpret_cast<const GPT2_LDS float*>(Qs + 2 * TILE + 1024);
-    const int q0 = qbeg + st * STAGE;
-    // Both 32-query slices' score products first, then each slice's
-    // softmax-gradient work and its dV / dK products: the second slice's
-    // S and dP run on the matrix cores while the first slice's exponentials
-    // run on the vector units, and the first slice's dV / dK products while
-    // the second slice's do.
-    floatx16 s[2], dp[2];
-    bool ok[2];
+    if (s < nst) issue(s, s);
+  // unrolled by the ring depth: LDS addresses are fixed offsets + immediates
+  for (int st0 = 0; st0 < nst; st0 += NS) {
+#pragma unroll 1
+    for (int sl = 0; sl < NS; ++sl) {
+      const int st = st0 + sl;
+      if (st >= nst) break;
+      // at most 5 DMA instructions per wave and stage: waiting until (NS - 2) * 4
+      // remain is sufficient for every wave
+      if (st + NS - 2 < nst) wait_vmcnt<(NS - 2) * 4>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      if (st + NS - 1 < nst) issue(st + NS - 1, (sl + NS - 1) % NS);
+      const GPT2_LDS char* Qs = (const GPT2_LDS char*)ring[sl];
+      const GPT2_LDS char* Os = Qs + TILE;
+      const GPT2_LDS char* Ls = Qs + 2 * TILE;
+      const GPT2_LDS char* Ds = Qs + 2 * TILE + 1024;
+      const int q0 = qbeg + st * STAGE;
+      // Both 32-query slices' score products first, then each slice's
+      // softmax-gradient work and its dV / dK products: the second slice's
+      // S and dP run on the matrix cores while the first slice's exponentials
+      // run on the vector units, and the first slice's dV / dK products while
+      // the second slice's do.
+      floatx16 s[2], dp[2];
+      bool ok[2];
 #pragma unroll
-    for (int u2 = 0; u2 < 2; ++u2) {
-      const int qs = 32 * u2, qb = q0 + qs;
-      ok[u2] = qb + 31 >= kw0 && qb < T && kw0 < T;
-      if (ok[u2]) {
+      for (int u2 = 0; u2 < 2; ++u2) {
+        const int qb = q0 + 32 * u2;
+        ok[u2] = qb + 31 >= kw0 && qb < T && kw0 < T;
+        if (ok[u2]) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) { s[u2][r] = 0.f; dp[u2][r] = 0.f; }
+          for (int r = 0; r < 16; ++r) { s[u2][r] = 0.f; dp[u2][r] = 0.f; }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          s[u2] = mfma(frag_nat(Qs, qs, k, lane), kf[k], s[u2]);
-          dp[u2] = mfma(frag_nat(Os, qs, k, lane), vf[k], dp[u2]);
+          for (int k = 0; k < 4; ++k) {
+            s[u2] = mfma(frag_at(Qs, noffs[u2][k]), kf[k], s[u2]);
+            dp[u2] = mfma(frag_at(Os, noffs[u2][k]), vf[k], dp[u2]);
+          }
         }
       }
-    }
 #pragma unroll
-    for (int u2 = 0; u2 < 2; ++u2) {
-      const int qs = 32 * u2, qb = q0 + qs;
-      if (ok[u2]) {
-        // s[r]: query qb + acc_row(r), key mykey.  The lane's 16 query rows are
-        // qs + 4 hi + 8 g + 0..3 (g = 0..3): four 16-byte reads each of L2 and D.
-        typedef float f32x4 __attribute__((ext_vector_type(4)));
-        float lv[16], dv_[16];
+      for (int u2 = 0; u2 < 2; ++u2) {
+        const int qs = 32 * u2, qb = q0 + qs;
+        if (ok[u2]) {
+          // s[r]: query qb + acc_row(r), key mykey.  The lane's 16 query rows are
+          // qs + 4 hi + 8 g + 0..3 (g = 0..3): four 16-byte reads each of L2 and D.
+          typedef float f32x4 __attribute__((ext_vector_type(4)));
+          float lv[16], dv_[16];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 l4 = *reinterpret_cast<const GPT2_LDS f32x4*>(Ls + qs + 4 * (lane >> 5) + 8 * g);
-          const f32x4 d4 = *reinterpret_cast<const GPT2_LDS f32x4*>(Ds + qs + 4 * (lane >> 5) + 8 * g);
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 l4 = *reinterpret_cast<const GPT2_LDS f32x4*>(Ls + ldoff + 4 * (qs + 8 * g));
+            const f32x4 d4 = *reinterpret_cast<const GPT2_LDS f32x4*>(Ds + ldoff + 4 * (qs + 8 * g));
 #pragma unroll
-          for (int e = 0; e < 4; ++e) { lv[4 * g + e] = l4[e]; dv_[4 * g + e] = d4[e]; }
-        }
-        float p[16];
-        // the causal / end-of-sequence mask only touches slices on the diagonal
-        if ((qb < kw0 + 31) || (qb + 32 > T)) {
+            for (int e = 0; e < 4; ++e) { lv[4 * g + e] = l4[e]; dv_[4 * g + e] = d4[e]; }
+          }
+          float p[16];
+          // the causal / end-of-sequence mask only touches slices on the diagonal
+          if ((qb < kw0 + 31) || (qb + 32 > T)) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int q = qb + acc_row(r, lane);
+              p[r] = (mykey > q || q >= T) ? 0.f : ex2(fmaf(s[u2][r], sl2, -lv[r]));
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) p[r] = ex2(fmaf(s[u2][r], sl2, -lv[r]));
+          }
+          bf16x8 pb[2], db[2];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int q = qb + acc_row(r, lane);
-            p[r] = (mykey > q || q >= T) ? 0.f : ex2(fmaf(s[u2][r], sl2, -lv[r]));
+            pb[r >> 3][r & 7] = (bf16)p[r];
+            db[r >> 3][r & 7] = (bf16)(p[r] * (dp[u2][r] - dv_[r]));
           }
-        } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) p[r] = ex2(fmaf(s[u2][r], sl2, -lv[r]));
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt) {
+              const uint32_t o0 = toffs[dt][2 * u2 + u][0], o1 = toffs[dt][2 * u2 + u][1];
+              dv[dt] = mfma(frag_tr_at(Os, o0, o1), pb[u], dv[dt]);
+              dk[dt] = mfma(frag_tr_at(Qs, o0, o1), db[u], dk[dt]);
+            }
         }
-        bf16x8 pb[2], db[2];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          pb[r >> 3][r & 7] = (bf16)p[r];
-          db[r >> 3][r & 7] = (bf16)(p[r] * (dp[u2][r] - dv_[r]));
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int dt = 0; dt < 2; ++dt) {
-            dv[dt] = mfma(frag_tr(Os, dt * 32, qs + 16 * u, lane), pb[u], dv[dt]);
-            dk[dt] = mfma(frag_tr(Qs, dt * 32, qs + 16 * u, lane), db[u], dk[dt]);
-          }
       }
     }
   }
@@ -453,7 +572,6 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dq_mfma_kernel(int T, int H, 
   const bf16* Bg = qkv + (size_t)b * T * ld;
   const bf16* Qg = Bg + h * HD;
   const bf16* Og = dout + (size_t)b * T * C + h * HD;
-  const i32x4_rsrc rs = make_rsrc4(Bg, (uint32_t)((size_t)T * ld * 2));
   const int q0 = qt * ROWS, qw0 = q0 + wave * 32, myq = qw0 + (lane & 31);
   const float sl2 = scale * kLog2e;
 
@@ -485,56 +603,93 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dq_mfma_kernel(int T, int H, 
 
   const int kend = min(T, q0 + ROWS);
   const int nst = (kend + STAGE - 1) / STAGE;
-  auto issue = [&](int st) {
-    GPT2_LDS char* base = (GPT2_LDS char*)ring[st % NS];
-    tile_dma(rs, base, wave, lane, st * STAGE, ld, C + h * HD);
-    tile_dma(rs, base + TILE, wave, lane, st * STAGE, ld, 2 * C + h * HD);
+  // DMA as in the forward kernel: fixed per-lane offsets, one buffer resource
+  // per stage based at its first key row
+  uint32_t koff[2], voff[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int iq = wave * 2 + q;
+    const int r = 8 * iq + (lane >> 3);
+    const int c = (lane & 7) ^ ((r ^ (r >> 3)) & 7);
+    koff[q] = (uint32_t)((r * ld + C + h * HD + c * 8) * 2);
+    voff[q] = (uint32_t)((r * ld + 2 * C + h * HD + c * 8) * 2);
+  }
+  auto issue = [&](int st, int slot) {
+    const int row0 = st * STAGE;
+    const i32x4_rsrc rst = make_rsrc4(Bg + (size_t)row0 * ld, (uint32_t)((size_t)(T - row0) * ld * 2));
+    GPT2_LDS char* base = (GPT2_LDS char*)ring[slot];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int iq = wave * 2 + q;
+      dma_lds16(rst, (GPT2_LDS void*)(base + iq * 1024), koff[q]);
+      dma_lds16(rst, (GPT2_LDS void*)(base + TILE + iq * 1024), voff[q]);
+    }
   };
+  // LDS offsets of the K / V fragments (32-key slice u2, k16 step k) and of
+  // the two halves of the transposed K fragments (d block dt, 16-key group j)
+  uint32_t noffs[2][4], toffs[2][4][2];
+#pragma unroll
+  for (int u2 = 0; u2 < 2; ++u2)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) noffs[u2][k] = opaque(frag_off(32 * u2, k, lane));
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) toffs[dt][j][r] = opaque(frag_tr_off(32 * dt, 16 * j, r, lane));
   // the fragments loaded to registers above have landed: the compiler's own
   // waits for them would otherwise sit in the loop and drain the DMA ring
   wait_vmcnt<0>();
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    if (s < nst) issue(s);
-  for (int st = 0; st < nst; ++st) {
-    if (st + NS - 2 < nst) wait_vmcnt<(NS - 2) * 4>();
-    else wait_vmcnt<0>();
-    lds_barrier();
-    if (st + NS - 1 < nst) issue(st + NS - 1);
-    const GPT2_LDS char* Ks = (const GPT2_LDS char*)ring[st % NS];
-    const GPT2_LDS char* Vs = Ks + TILE;
-    const int k0 = st * STAGE;
+    if (s < nst) issue(s, s);
+  // unrolled by the ring depth: LDS addresses are fixed offsets + immediates
+  for (int st0 = 0; st0 < nst; st0 += NS) {
 #pragma unroll
-    for (int ks = 0; ks < STAGE; ks += 32) {
-      const int kb = k0 + ks;
-      if (kb <= qw0 + 31 && kb < T) {
-        floatx16 s, dp;
+    for (int sl = 0; sl < NS; ++sl) {
+      const int st = st0 + sl;
+      if (st >= nst) break;
+      if (st + NS - 2 < nst) wait_vmcnt<(NS - 2) * 4>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      if (st + NS - 1 < nst) issue(st + NS - 1, (sl + NS - 1) % NS);
+      const GPT2_LDS char* Ks = (const GPT2_LDS char*)ring[sl];
+      const GPT2_LDS char* Vs = Ks + TILE;
+      const int k0 = st * STAGE;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+      for (int u2 = 0; u2 < 2; ++u2) {
+        const int kb = k0 + 32 * u2;
+        if (kb <= qw0 + 31 && kb < T) {
+          floatx16 s, dp;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          s = mfma(frag_nat(Ks, ks, k, lane), qf[k], s);
-          dp = mfma(frag_nat(Vs, ks, k, lane), of[k], dp);
-        }
-        // s[r]: key kb + acc_row(r), query myq; the mask only touches diagonal slices
-        float p[16];
-        if ((kb + 31 > qw0) || (kb + 32 > T)) {
+          for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kb + acc_row(r, lane);
-            p[r] = (key > myq || key >= T) ? 0.f : ex2(fmaf(s[r], sl2, -lq));
+          for (int k = 0; k < 4; ++k) {
+            s = mfma(frag_at(Ks, noffs[u2][k]), qf[k], s);
+            dp = mfma(frag_at(Vs, noffs[u2][k]), of[k], dp);
           }
-        } else {
+          // s[r]: key kb + acc_row(r), query myq; the mask only touches diagonal slices
+          float p[16];
+          if ((kb + 31 > qw0) || (kb + 32 > T)) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) p[r] = ex2(fmaf(s[r], sl2, -lq));
+            for (int r = 0; r < 16; ++r) {
+              const int key = kb + acc_row(r, lane);
+              p[r] = (key > myq || key >= T) ? 0.f : ex2(fmaf(s[r], sl2, -lq));
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) p[r] = ex2(fmaf(s[r], sl2, -lq));
+          }
+          bf16x8 db[2];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) db[r >> 3][r & 7] = (bf16)(p[r] * (dp[r] - Dq));
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt)
+              dq[dt] = mfma(frag_tr_at(Ks, toffs[dt][2 * u2 + u][0], toffs[dt][2 * u2 + u][1]), db[u], dq[dt]);
         }
-        bf16x8 db[2];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) db[r >> 3][r & 7] = (bf16)(p[r] * (dp[r] - Dq));
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int dt = 0; dt < 2; ++dt) dq[dt] = mfma(frag_tr(Ks, dt * 32, ks + 16 * u, lane), db[u], dq[dt]);
       }
     }
   }

@@ -13,8 +13,8 @@
 // operands k-major.
 //
 // The bias gradient of an fp8 weight-gradient product is the column sum of
-// the unquantised bf16 gradient: per-row-block partial sums, then an
-// in-order sum (deterministic).
+// the unquantised bf16 gradient: per-row-block partial sums (256 row blocks,
+// eight columns per thread), then an in-order sum (deterministic).
 
 #include "kernels.h"
 
@@ -22,14 +22,25 @@ namespace gpt2k {
 namespace {
 
 constexpr int kAmaxBlocks = 1024;
-constexpr int kColsumRowBlocks = 64;
+constexpr int kColsumRowBlocks = 256;
 
 template <typename T>
 __global__ __launch_bounds__(256) void absmax_partial_kernel(int64_t n, const T* __restrict__ x,
                                                              float* __restrict__ partial) {
   float m = 0.f;
-  const int64_t n8 = n / 8;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+  const int64_t n8 = n / 8, stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  // four independent 8-element loads in flight per thread
+  for (; i + 3 * stride < n8; i += 4 * stride) {
+    float v[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) Chunk8<T>::load(x + (i + u * stride) * 8, v[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[u][e]));
+  }
+  for (; i < n8; i += stride) {
     float v[8];
     Chunk8<T>::load(x + i * 8, v);
 #pragma unroll
@@ -113,16 +124,24 @@ __global__ __launch_bounds__(256) void quantize_kernel(int R, int Cc, const T* _
   }
 }
 
-// part[b][n] = sum of dy[r][n] over rows r of row block b.
+// part[b][n] = sum of dy[r][n] over rows r of row block b; each thread sums
+// eight adjacent columns (one 16-byte load per row), N % 8 == 0.
 __global__ __launch_bounds__(256) void colsum_partial_kernel(int R, int N, const bf16* __restrict__ dy,
                                                              float* __restrict__ part) {
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
+  const int c8 = blockIdx.x * 256 + threadIdx.x;
+  if (c8 * 8 >= N) return;
   const int rows = (R + gridDim.y - 1) / gridDim.y;
   const int r_beg = blockIdx.y * rows, r_end = min(R, r_beg + rows);
-  float s = 0.f;
-  for (int r = r_beg; r < r_end; ++r) s += (float)dy[(int64_t)r * N + n];
-  part[(int64_t)blockIdx.y * N + n] = s;
+  float s[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s[e] = 0.f;
+  for (int r = r_beg; r < r_end; ++r) {
+    float v[8];
+    Chunk8<bf16>::load(dy + (int64_t)r * N + c8 * 8, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] += v[e];
+  }
+  Chunk8<float>::store(part + (int64_t)blockIdx.y * N + c8 * 8, s);
 }
 
 __global__ __launch_bounds__(256) void colsum_final_kernel(int N, int nb, const float* __restrict__ part,
@@ -187,12 +206,14 @@ size_t bias_grad_workspace_bytes(int N) { return (size_t)kColsumRowBlocks * N * 
 
 int bias_grad_bf16(int R, int N, const bf16* dy, float* db, bool accumulate, float* workspace, size_t workspace_bytes,
                    hipStream_t stream) {
-  if (R < 0 || N < 0 || !dy || !db || !workspace || workspace_bytes < bias_grad_workspace_bytes(N))
+  if (R < 0 || N < 0 || N % 8 || !dy || (uintptr_t)dy % 16 || !db || !workspace ||
+      workspace_bytes < bias_grad_workspace_bytes(N))
     return gpt2_internal_fail(1, "bias_grad_bf16: bad arguments");
   if (N == 0) return 0;
-  const unsigned nx = (unsigned)ceil_div64(N, 256);
-  hipLaunchKernelGGL(colsum_partial_kernel, dim3(nx, kColsumRowBlocks), dim3(256), 0, stream, R, N, dy, workspace);
+  hipLaunchKernelGGL(colsum_partial_kernel, dim3((unsigned)ceil_div64(N / 8, 256), kColsumRowBlocks), dim3(256), 0,
+                     stream, R, N, dy, workspace);
   GPT2_LAUNCH_CHECK();
+  const unsigned nx = (unsigned)ceil_div64(N, 256);
   hipLaunchKernelGGL(colsum_final_kernel, dim3(nx), dim3(256), 0, stream, N, kColsumRowBlocks, workspace, db,
                      accumulate);
   GPT2_LAUNCH_CHECK();

@@ -68,6 +68,8 @@ struct MfmaArgs {
   EpiArgs e;
   const float* scale_a;   // fp8: per-tensor scales of A and B (device), else unused
   const float* scale_b;
+  int splits;             // K splits (units = tiles x splits)
+  int persistent;         // the grid holds one block per compute unit slot and each block loops over units
 };
 
 struct Plan {
@@ -172,18 +174,18 @@ __device__ __forceinline__ void epilogue_vec8_final(const EpiArgs& e, int m, int
   }
 }
 
-// Tile and K-split coordinates of this workgroup.  The dispatcher hands the
-// workgroups, in linear order (x fastest, then y = split), to the 8 XCDs in
-// turn; each XCD is given a contiguous range of the (split, tile) units, split
-// major, so the units resident on one XCD share A and B slabs of one K range
-// in its L2; inside a split, tiles run in groups of 8 M-tiles that sweep the
-// N-tiles together.
-__device__ __forceinline__ void tile_coords(int nbm, int nbn, int& tm, int& tn, int& z) {
-  const int ntiles = nbm * nbn, total = ntiles * (int)gridDim.y;
-  const int lin = (int)(blockIdx.y * gridDim.x + blockIdx.x);
-  const int xcd = lin & 7, idx = lin >> 3;
+// Work units are (split, tile) pairs, v = split * tiles + tile.  The
+// dispatcher hands workgroups, in linear order, to the 8 XCDs in turn; each
+// XCD is given a contiguous range of units, split major, so the units resident
+// on one XCD share A and B slabs of one K range in its L2; inside a split,
+// tiles run in groups of 8 M-tiles that sweep the N-tiles together.
+__device__ __forceinline__ void xcd_range(int total, int xcd, int& beg, int& end) {
   const int base = total >> 3, rem = total & 7;
-  const int v = xcd * base + min(xcd, rem) + idx;
+  beg = xcd * base + min(xcd, rem);
+  end = beg + base + (xcd < rem ? 1 : 0);
+}
+__device__ __forceinline__ void unit_coords(int v, int nbm, int nbn, int& tm, int& tn, int& z) {
+  const int ntiles = nbm * nbn;
   z = v / ntiles;
   const int t = v - z * ntiles;
   constexpr int GM = 8;
@@ -193,6 +195,23 @@ __device__ __forceinline__ void tile_coords(int nbm, int nbn, int& tm, int& tn, 
   const int r = t - group * GM * nbn;
   tm = first_m + r % gsize;
   tn = r / gsize;
+}
+// Units of this workgroup: one (grid = units, linear id -> its XCD's range)
+// or, for a persistent grid of G blocks (G a multiple of 8), units
+// beg + j, beg + j + G/8, ... of its XCD's range, j = its index on the XCD.
+__device__ __forceinline__ void block_units(int total, bool persistent, int& u, int& u_end, int& u_step) {
+  const int lin = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+  int beg, end;
+  xcd_range(total, lin & 7, beg, end);
+  if (persistent) {
+    u = beg + (lin >> 3);
+    u_end = end;
+    u_step = (int)(gridDim.x * gridDim.y) >> 3;
+  } else {
+    u = beg + (lin >> 3);
+    u_end = u + 1;
+    u_step = 1;
+  }
 }
 
 // ---------------------------------------------------------------- bf16 MFMA, direct-to-LDS
@@ -352,7 +371,7 @@ struct DmaShape {
   static constexpr int SUB_BYTES = BM * 128;              // [BM][64] bf16 sub-tile of the epilogue input
   static constexpr int PER_STAGE = STAGE_BYTES / SUB_BYTES;
   static constexpr int AUX_STAGES = HAS_AUX ? (BN / 64 + PER_STAGE - 1) / PER_STAGE : 0;
-  static constexpr int LDS_LIMIT = 160 * 1024 - BN * 4 - 1024;
+  static constexpr int LDS_LIMIT = 160 * 1024 - 2 * BN * 4 - 1024;   // two bias buffers
   static constexpr bool fits(int n) {
     return AUX_STAGES <= n && n * STAGE_BYTES + (AUX_STAGES < n ? 0 : AUX_BYTES) <= LDS_LIMIT;
   }
@@ -394,7 +413,7 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   __shared__ __attribute__((aligned(1024))) char st2[NS > 2 ? S::STAGE_BYTES : 16];
   __shared__ __attribute__((aligned(1024))) char st3[NS > 3 ? S::STAGE_BYTES : 16];
   __shared__ __attribute__((aligned(16))) char epi_own[S::EPI_IN_STAGE ? 16 : S::AUX_BYTES];
-  __shared__ __attribute__((aligned(16))) float bias_s[HAS_BIAS ? BN : 4];
+  __shared__ __attribute__((aligned(16))) float bias_s[2][HAS_BIAS ? BN : 4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wid = wave % (S::WGM * S::WGN), kg = wave / (S::WGM * S::WGN);
@@ -404,32 +423,51 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   // KK * FM * FN matrix instructions, so it needs that many slots
   static_assert(!IL || NDMA <= KK * FM * FN, "one DMA instruction per MFMA at most");
   static_assert(S::KG == 1 || !BIAS_GRAD, "K-groups take no fused bias gradient");
-  int tm, tn;
-  int z;
-  tile_coords((p.M + BM - 1) / BM, (p.N + BN - 1) / BN, tm, tn, z);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int kbeg = z * p.k_per_split;
-  const int KT = (min(p.K, kbeg + p.k_per_split) - kbeg + KE - 1) / KE;
-  const bool do_bias = BIAS_GRAD && tn == 0;
+  // A tile's epilogue stages its output through the last ring slot and reads
+  // no input tile, so the next tile's first NS - 1 K steps can be loaded into
+  // the other slots while it runs: such kernels run persistent (one block per
+  // compute-unit slot, looping over their XCD's units) when the grid says so.
+  constexpr bool PERSIST = !HAS_AUX && S::KG == 1 && S::EPI_IN_STAGE;
+  const int nbm = (p.M + BM - 1) / BM, nbn = (p.N + BN - 1) / BN;
+  const bool persistent = PERSIST && p.persistent;
+  int u, u_end, u_step;
+  block_units(nbm * nbn * p.splits, persistent, u, u_end, u_step);
   const i32x4_rsrc ra = make_rsrc4(p.A, p.a_bytes), rb = make_rsrc4(p.B, p.b_bytes);
 
   auto stage_ptr = [&](int s) -> GPT2_LDS char* {
     return (GPT2_LDS char*)(s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : st3);
   };
+  // K step kt of the unit whose lane parts and first k are given, into ring slot s
+  auto issue_unit = [&](const typename TA::Lane& la_, const typename TB::Lane& lb_, int kbeg_, int kt, int s) {
+    GPT2_LDS char* base = stage_ptr(s);
+    const int k0 = kbeg_ + kt * KE;
+    const bool tail = k0 + KE > p.K;
+    TA::issue(ra, base, wave, la_, k0, p.K, p.lda, tail);
+    TB::issue(rb, base + A_BYTES, wave, lb_, k0, p.K, p.ldb, tail);
+  };
+  const bool vec = p.vec_epilogue;
+  // fp8: the sums of products of the quantised operands times s_a s_b
+  float sc = 1.0f;
+  if constexpr (F8) sc = p.scale_a[0] * p.scale_b[0];
+
+  for (int it = 0; u < u_end; u += u_step, ++it) {
+  const bool first = it == 0;
+  const int bp = it & 1;                     // bias buffer of this unit
+  int tm, tn, z;
+  unit_coords(u, nbm, nbn, tm, tn, z);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kbeg = z * p.k_per_split;
+  const int KT = (min(p.K, kbeg + p.k_per_split) - kbeg + KE - 1) / KE;
+  const bool do_bias = BIAS_GRAD && tn == 0;
   const typename TA::Lane la = TA::lane_part(wave, lane, m0, p.lda);
   const typename TB::Lane lb = TB::lane_part(wave, lane, n0, p.ldb);
-  auto issue = [&](int kt, int s) {
-    GPT2_LDS char* base = stage_ptr(s);
-    const int k0 = kbeg + kt * KE;
-    const bool tail = k0 + KE > p.K;
-    TA::issue(ra, base, wave, la, k0, p.K, p.lda, tail);
-    TB::issue(rb, base + A_BYTES, wave, lb, k0, p.K, p.ldb, tail);
-  };
+  auto issue = [&](int kt, int s) { issue_unit(la, lb, kbeg, kt, s); };
 
-  // the block's bias columns, read by the epilogue from LDS
+  // the block's bias columns, read by the epilogue from LDS (two buffers: the
+  // previous unit's epilogue may still be reading the other)
   if constexpr (HAS_BIAS) {
     for (int c = tid; c < BN; c += NT)
-      bias_s[c] = n0 + c < p.N ? (float)reinterpret_cast<const bf16*>(p.e.bias)[n0 + c] : 0.f;
+      bias_s[bp][c] = n0 + c < p.N ? (float)reinterpret_cast<const bf16*>(p.e.bias)[n0 + c] : 0.f;
   }
 
   // The residual / pre-activation tile the epilogue reads (R or U, [BM][BN]
@@ -447,7 +485,7 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
                 p.e.ld_aux, c0 + 64 > p.N);
     }
   };
-  const bool vec = p.vec_epilogue;
+
 
   float bsum[8];
 #pragma unroll
@@ -460,9 +498,13 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // the first unit loads its first NS - 1 K steps here; later units' were
+  // issued during the previous unit's epilogue
+  if (first) {
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < KT) issue(s, s);
+    for (int s = 0; s < NS - 1; ++s)
+      if (s < KT) issue(s, s);
+  }
 
   for (int kt0 = 0; kt0 < KT; kt0 += NS) {
 #pragma unroll
@@ -470,7 +512,10 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
       const int kt = kt0 + s;
       if (kt < KT) {
         // stage s of this K step has landed (for this wave), then everyone's has
-        if (kt + NS - 2 < KT) wait_vmcnt<(NS - 2) * NDMA>();
+        // (a later unit's first step waits for everything: the previous
+        // epilogue's stores are in flight too, and stores and loads need not
+        // complete in order)
+        if (kt + NS - 2 < KT && (first || kt > 0)) wait_vmcnt<(NS - 2) * NDMA>();
         else wait_vmcnt<0>();
         lds_barrier();
         // Refill of the ring slot read in the previous K step.  For the tiles
@@ -501,8 +546,8 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
           // column sums of the m-major dY tile: thread t sums k rows 8*(t/32) .. +7 of chunk t%32
           if (do_bias) {
             constexpr int CH = BM / 8;
-            for (int u = tid; u < CH * 8; u += NT) {
-              const int cc = u % CH, kg = u / CH;
+            for (int w8 = tid; w8 < CH * 8; w8 += NT) {
+              const int cc = w8 % CH, kg = w8 / CH;
 #pragma unroll
               for (int r = 0; r < 8; ++r) {
                 const int kr = kg * 8 + r;
@@ -623,6 +668,22 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
     }
     __syncthreads();   // the epilogue staging below reuses the stage buffers
   }
+  // Persistent: every wave is past the barrier above, so the ring slots
+  // 0 .. NS - 2 are free; the next unit's first K steps load into them while
+  // this unit's epilogue runs in slot NS - 1.
+  if constexpr (PERSIST) {
+    if (persistent && u + u_step < u_end) {
+      int tm2, tn2, z2;
+      unit_coords(u + u_step, nbm, nbn, tm2, tn2, z2);
+      const int kbeg2 = z2 * p.k_per_split;
+      const int KT2 = (min(p.K, kbeg2 + p.k_per_split) - kbeg2 + KE - 1) / KE;
+      const typename TA::Lane la2 = TA::lane_part(wave, lane, tm2 * BM, p.lda);
+      const typename TB::Lane lb2 = TB::lane_part(wave, lane, tn2 * BN, p.ldb);
+#pragma unroll
+      for (int s = 0; s < NS - 1; ++s)
+        if (s < KT2) issue_unit(la2, lb2, kbeg2, s, s);
+    }
+  }
   GPT2_LDS char* epi_lds =
       S::EPI_IN_STAGE ? stage_ptr(S::EARLY_AUX ? s_last : NS - 1) : (GPT2_LDS char*)epi_own;
   auto aux_stage = [&](int j) { return S::EARLY_AUX ? stage_ptr((s_last + 1 + j) % NS) : stage_ptr(j); };
@@ -640,9 +701,6 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   // column 8(r/4) + 4(l/32) + r%4: four consecutive columns per 16-byte write.
   GPT2_LDS float* ep = reinterpret_cast<GPT2_LDS float*>(epi_lds) + wid * 32 * S::EP_PITCH;
   const int hi = lane >> 5;
-  // fp8: the sums of products of the quantised operands times s_a s_b
-  float sc = 1.0f;
-  if constexpr (F8) sc = p.scale_a[0] * p.scale_b[0];
   if (S::KG == 1 || kg == 0) {   // the second K-group is done
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -672,7 +730,7 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
               const int tr = wm * WM + i * 32 + rl, tc = wn * WN + j * 32 + cc * 8;
               if constexpr (HAS_BIAS) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] += bias_s[tc + e];
+                for (int e = 0; e < 8; ++e) v[e] += bias_s[bp][tc + e];
               }
               if constexpr (HAS_AUX) {
                 const int sb = tc >> 6, ch = (tc & 63) >> 3;
@@ -711,8 +769,8 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
       __syncthreads();
       GPT2_LDS float* red = reinterpret_cast<GPT2_LDS float*>(epi_lds);   // [8 k-groups][BM]
       constexpr int CH = BM / 8;
-      for (int u = tid; u < CH * 8; u += NT) {
-        const int cc = u % CH, kg = u / CH;
+      for (int w8 = tid; w8 < CH * 8; w8 += NT) {
+        const int cc = w8 % CH, kg = w8 / CH;
 #pragma unroll
         for (int e = 0; e < 8; ++e) red[kg * BM + cc * 8 + e] = bsum[e];
       }
@@ -725,6 +783,7 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
       }
     }
   }
+  }   // units
 }
 
 // ---------------------------------------------------------------- fp32 SIMT
@@ -972,13 +1031,38 @@ int gemm_splits(int dtype, int epi, int M, int N, int K, bool a_kmajor, bool b_k
   return plan_gemm(dtype, fp8, epi, M, N, K, a_kmajor, b_kmajor).splits;
 }
 
+// Compute units of the current device (the persistent grid's size).
+inline int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess)
+    return 0;
+  return cus;
+}
+
+// One block per unit, or -- for the kernels that prefetch the next unit
+// during the epilogue, when there are more units than block slots -- one
+// block per slot (compute units x blocks per unit; a multiple of the 8 XCDs)
+// looping over units.
 template <int BM, int BN, int EPI, bool A_KMAJ, bool B_KMAJ, bool BIAS_GRAD, int KGS = 1, bool F8 = false,
           int FMT_A = 0>
 int launch_tile(const MfmaArgs& a, int splits, hipStream_t stream) {
+  using S = DmaShape<BM, BN, EPI, KGS>;
   const unsigned tiles = (unsigned)(ceil_div64(a.M, BM) * ceil_div64(a.N, BN));
+  MfmaArgs b = a;
+  b.splits = splits;
+  b.persistent = 0;
+  dim3 grid(tiles, (unsigned)splits);
+  if constexpr (!epi_has_aux(EPI) && KGS == 1 && S::EPI_IN_STAGE) {
+    const long slots = (long)device_cus() * S::OCC;
+    if (slots > 0 && slots % 8 == 0 && (long)tiles * splits > slots) {
+      b.persistent = 1;
+      grid = dim3((unsigned)slots, 1);
+    }
+  }
   mark_begin(0, stream);
-  hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, A_KMAJ, B_KMAJ, EPI, BIAS_GRAD, KGS, F8, FMT_A>), dim3(tiles, splits),
-                     dim3(64 * gemm_waves(BM, BN, EPI, KGS)), 0, stream, a);
+  hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, A_KMAJ, B_KMAJ, EPI, BIAS_GRAD, KGS, F8, FMT_A>), grid,
+                     dim3(64 * gemm_waves(BM, BN, EPI, KGS)), 0, stream, b);
   GPT2_LAUNCH_CHECK();
   mark_end(0, stream);
   return 0;
