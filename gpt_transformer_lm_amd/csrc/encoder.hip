@@ -7,7 +7,10 @@
 // Token ids are heavily skewed (Zipf-like text statistics: the most frequent
 // id can own >10% of all positions), so the scatter is done without atomics
 // and in a fixed order:
-//   1. sort the keys (token << S) | position in one workgroup (bitonic, LDS);
+//   1. sort the 64-bit keys (token << 32) | position: a bitonic network whose
+//      layers up to 4096 keys run inside one workgroup's LDS and whose longer
+//      compare distances are one launch per layer over the whole array (the
+//      keys are distinct, so the sorted order is unique);
 //   2. cut the sorted list into pieces of 64 entries; each piece sums its runs
 //      of equal tokens; a run that lies wholly inside the piece is added to
 //      its dwte row directly (only this piece touches that row); a run that
@@ -21,7 +24,8 @@
 namespace gpt2k {
 namespace {
 
-constexpr int kSortMax = 32768;   // B*T limit of the one-workgroup sort
+constexpr int kSortChunk = 4096;        // keys sorted per workgroup in LDS (32 KiB)
+constexpr int kSortMax = 1 << 22;       // B*T limit of the sort (keys buffer of 32 MiB)
 constexpr int kPiece = 64;
 
 template <typename T>
@@ -55,47 +59,83 @@ __global__ void encoder_bwd_wpe_kernel(int B, int T_, int C, const float* __rest
   dwpe[idx] = accumulate ? dwpe[idx] + s : s;
 }
 
-// One workgroup: sorts keys[i] = (tok[i] << shift) | i, i < n, ascending.
-__global__ __launch_bounds__(1024) void sort_keys_kernel(int n, int shift, const int32_t* __restrict__ tokens,
-                                                         int Vrows, uint32_t* __restrict__ sorted) {
-  extern __shared__ uint32_t keys[];
-  int np = 1;
-  while (np < n) np <<= 1;
-  for (int i = threadIdx.x; i < np; i += 1024) {
-    if (i < n) {
-      int tok = tokens[i];
-      tok = tok < 0 ? 0 : (tok >= Vrows ? Vrows - 1 : tok);
-      keys[i] = ((uint32_t)tok << shift) | (uint32_t)i;
+// Bitonic network over np (a power of two) keys, ascending: layer (k, j)
+// compares elements i and i ^ j and orders each pair ascending when
+// i & k == 0, descending otherwise.
+
+// Layers k = 2 .. chunk of the network on one chunk of the array, built from
+// the tokens (keys past n are all-ones, so they sort last).
+__global__ __launch_bounds__(1024) void sort_chunks_kernel(int n, int chunk, const int32_t* __restrict__ tokens,
+                                                           int Vrows, uint64_t* __restrict__ keys) {
+  __shared__ uint64_t sk[kSortChunk];
+  const int base = blockIdx.x * chunk;
+  for (int i = threadIdx.x; i < chunk; i += 1024) {
+    const int g = base + i;
+    if (g < n) {
+      int tok = tokens[g];
+      tok = tok < 0 ? 0 : (tok >= Vrows ? Vrows - 1 : tok);   // memory safety only
+      sk[i] = ((uint64_t)(uint32_t)tok << 32) | (uint32_t)g;
     } else {
-      keys[i] = 0xffffffffu;
+      sk[i] = ~0ull;
     }
   }
   __syncthreads();
-  for (int k = 2; k <= np; k <<= 1) {
+  for (int k = 2; k <= chunk; k <<= 1)
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < np; i += 1024) {
-        int ixj = i ^ j;
-        if (ixj > i) {
-          uint32_t a = keys[i], b = keys[ixj];
-          bool up = (i & k) == 0;
-          if ((a > b) == up) {
-            keys[i] = b;
-            keys[ixj] = a;
-          }
+      for (int i = threadIdx.x; i < chunk; i += 1024) {
+        const int l = i ^ j;
+        if (l > i) {
+          const uint64_t a = sk[i], b = sk[l];
+          if ((a > b) == (((base + i) & k) == 0)) { sk[i] = b; sk[l] = a; }
         }
       }
       __syncthreads();
     }
-  }
-  for (int i = threadIdx.x; i < n; i += 1024) sorted[i] = keys[i];
+  for (int i = threadIdx.x; i < chunk; i += 1024) keys[base + i] = sk[i];
 }
 
-__device__ __forceinline__ int key_tok(uint32_t k, int shift) { return (int)(k >> shift); }
-__device__ __forceinline__ int key_pos(uint32_t k, int shift) { return (int)(k & ((1u << shift) - 1)); }
+// One layer (k, j) with j >= chunk over the whole array.
+__global__ __launch_bounds__(256) void sort_layer_kernel(int np, int k, int j, uint64_t* __restrict__ keys) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= np) return;
+  const int l = i ^ j;
+  if (l > i) {
+    const uint64_t a = keys[i], b = keys[l];
+    if ((a > b) == ((i & k) == 0)) { keys[i] = b; keys[l] = a; }
+  }
+}
+
+// Layers (k, chunk/2) .. (k, 1) of one chunk in LDS.
+__global__ __launch_bounds__(1024) void sort_chunk_merge_kernel(int chunk, int k, uint64_t* __restrict__ keys) {
+  __shared__ uint64_t sk[kSortChunk];
+  const int base = blockIdx.x * chunk;
+  for (int i = threadIdx.x; i < chunk; i += 1024) sk[i] = keys[base + i];
+  __syncthreads();
+  for (int j = chunk >> 1; j > 0; j >>= 1) {
+    for (int i = threadIdx.x; i < chunk; i += 1024) {
+      const int l = i ^ j;
+      if (l > i) {
+        const uint64_t a = sk[i], b = sk[l];
+        if ((a > b) == (((base + i) & k) == 0)) { sk[i] = b; sk[l] = a; }
+      }
+    }
+    __syncthreads();
+  }
+  for (int i = threadIdx.x; i < chunk; i += 1024) keys[base + i] = sk[i];
+}
+
+__device__ __forceinline__ int key_tok(uint64_t k) { return (int)(k >> 32); }
+__device__ __forceinline__ int key_pos(uint64_t k) { return (int)(uint32_t)k; }
+
+int next_pow2(int n) {
+  int np = 1;
+  while (np < n) np <<= 1;
+  return np;
+}
 
 // Step 2: one block per piece; threads stride over channels.
-__global__ __launch_bounds__(256) void encoder_bwd_pieces_kernel(int n, int C, int shift,
-                                                                 const uint32_t* __restrict__ sorted,
+__global__ __launch_bounds__(256) void encoder_bwd_pieces_kernel(int n, int C,
+                                                                 const uint64_t* __restrict__ sorted,
                                                                  const float* __restrict__ dx0,
                                                                  float* __restrict__ dwte,
                                                                  float* __restrict__ pcont,
@@ -105,13 +145,13 @@ __global__ __launch_bounds__(256) void encoder_bwd_pieces_kernel(int n, int C, i
   const int end = min(n, start + kPiece);
   __shared__ int stok[kPiece], spos[kPiece];
   for (int e = threadIdx.x; e < end - start; e += blockDim.x) {
-    uint32_t k = sorted[start + e];
-    stok[e] = key_tok(k, shift);
-    spos[e] = key_pos(k, shift);
+    const uint64_t k = sorted[start + e];
+    stok[e] = key_tok(k);
+    spos[e] = key_pos(k);
   }
   __syncthreads();
-  const int prev_tok = start > 0 ? key_tok(sorted[start - 1], shift) : -1;
-  const int next_tok = end < n ? key_tok(sorted[end], shift) : -1;
+  const int prev_tok = start > 0 ? key_tok(sorted[start - 1]) : -1;
+  const int next_tok = end < n ? key_tok(sorted[end]) : -1;
   const int len = end - start;
   for (int c = threadIdx.x; c < C; c += blockDim.x) {
     int rs = 0;   // run start (index within piece)
@@ -147,8 +187,8 @@ __global__ __launch_bounds__(256) void encoder_bwd_pieces_kernel(int n, int C, i
 }
 
 // Step 3: one block per piece whose last run starts a boundary-crossing run.
-__global__ __launch_bounds__(256) void encoder_bwd_spans_kernel(int n, int C, int shift, int npieces,
-                                                                const uint32_t* __restrict__ sorted,
+__global__ __launch_bounds__(256) void encoder_bwd_spans_kernel(int n, int C, int npieces,
+                                                                const uint64_t* __restrict__ sorted,
                                                                 const float* __restrict__ pcont,
                                                                 const float* __restrict__ pown,
                                                                 float* __restrict__ dwte) {
@@ -156,25 +196,19 @@ __global__ __launch_bounds__(256) void encoder_bwd_spans_kernel(int n, int C, in
   const int start = piece * kPiece;
   const int end = min(n, start + kPiece);
   if (end >= n) return;
-  const int tok = key_tok(sorted[end - 1], shift);
-  if (key_tok(sorted[end], shift) != tok) return;    // last run does not continue
+  const int tok = key_tok(sorted[end - 1]);
+  if (key_tok(sorted[end]) != tok) return;    // last run does not continue
   // find where the last run starts; if it started in an earlier piece this
   // piece holds a continuation, not the owner partial
   int rs = end - 1;
-  while (rs > start && key_tok(sorted[rs - 1], shift) == tok) --rs;
-  if (rs == start && start > 0 && key_tok(sorted[start - 1], shift) == tok) return;
+  while (rs > start && key_tok(sorted[rs - 1]) == tok) --rs;
+  if (rs == start && start > 0 && key_tok(sorted[start - 1]) == tok) return;
   for (int c = threadIdx.x; c < C; c += blockDim.x) {
     float acc = pown[(size_t)piece * C + c];
-    for (int q = piece + 1; q < npieces && key_tok(sorted[q * kPiece], shift) == tok; ++q)
+    for (int q = piece + 1; q < npieces && key_tok(sorted[q * kPiece]) == tok; ++q)
       acc += pcont[(size_t)q * C + c];
     dwte[(size_t)tok * C + c] += acc;
   }
-}
-
-int pos_bits(int n) {
-  int s = 0;
-  while ((1 << s) < n) ++s;
-  return s;
 }
 
 }  // namespace
@@ -204,34 +238,32 @@ size_t encoder_backward_sorted_workspace_bytes(int B, int T_, int C) {
   return 2 * (size_t)np * C * sizeof(float) + 256;
 }
 
+size_t encoder_sort_keys_bytes(int n) { return n > 0 ? (((size_t)next_pow2(n) * 8 + 255) / 256) * 256 : 0; }
+
 size_t encoder_backward_workspace_bytes(int B, int T_, int C) {
-  const int n = B * T_;
-  return (((size_t)n * 4 + 255) / 256) * 256 + encoder_backward_sorted_workspace_bytes(B, T_, C);
+  return encoder_sort_keys_bytes(B * T_) + encoder_backward_sorted_workspace_bytes(B, T_, C);
 }
 
-int encoder_sort_keys(int n, int vocab_rows, const int32_t* tokens, uint32_t* sorted, hipStream_t stream) {
-  if (n < 0 || vocab_rows <= 0 || vocab_rows > 65536 || !tokens || !sorted)
-    return gpt2_internal_fail(1, "encoder_sort_keys: bad arguments");
+int encoder_sort_keys(int n, int vocab_rows, const int32_t* tokens, uint64_t* sorted, hipStream_t stream) {
+  if (n < 0 || vocab_rows <= 0 || !tokens || !sorted) return gpt2_internal_fail(1, "encoder_sort_keys: bad arguments");
   if (n == 0) return 0;
   if (n > kSortMax) return gpt2_internal_fail(1, "encoder_backward: B*T=%d exceeds %d", n, kSortMax);
-  const int shift = pos_bits(n);
-  if (shift + 16 > 32) return gpt2_internal_fail(1, "encoder_backward: key overflow");
-  int np2 = 1;
-  while (np2 < n) np2 <<= 1;
-  static bool lds_attr_set = false;
-  if (!lds_attr_set) {
-    GPT2_HIP_CHECK(hipFuncSetAttribute((const void*)sort_keys_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       kSortMax * (int)sizeof(uint32_t)));
-    lds_attr_set = true;
-  }
-  hipLaunchKernelGGL(sort_keys_kernel, dim3(1), dim3(1024), (size_t)np2 * sizeof(uint32_t), stream, n, shift,
-                     tokens, vocab_rows, sorted);
+  const int np = next_pow2(n), chunk = np < kSortChunk ? np : kSortChunk;
+  hipLaunchKernelGGL(sort_chunks_kernel, dim3((unsigned)(np / chunk)), dim3(1024), 0, stream, n, chunk, tokens,
+                     vocab_rows, sorted);
   GPT2_LAUNCH_CHECK();
+  for (int k = 2 * chunk; k <= np; k <<= 1) {
+    for (int j = k >> 1; j >= chunk; j >>= 1) {
+      hipLaunchKernelGGL(sort_layer_kernel, dim3((unsigned)ceil_div64(np, 256)), dim3(256), 0, stream, np, k, j, sorted);
+      GPT2_LAUNCH_CHECK();
+    }
+    hipLaunchKernelGGL(sort_chunk_merge_kernel, dim3((unsigned)(np / chunk)), dim3(1024), 0, stream, chunk, k, sorted);
+    GPT2_LAUNCH_CHECK();
+  }
   return 0;
 }
 
-int encoder_backward_sorted(int B, int T_, int C, const uint32_t* sorted, const float* dx0, float* dwte,
+int encoder_backward_sorted(int B, int T_, int C, const uint64_t* sorted, const float* dx0, float* dwte,
                             float* dwpe, bool accumulate_wpe, void* workspace, size_t workspace_bytes,
                             hipStream_t stream) {
   if (B < 0 || T_ < 0 || C <= 0 || !sorted || !dx0 || !dwte)
@@ -241,7 +273,6 @@ int encoder_backward_sorted(int B, int T_, int C, const uint32_t* sorted, const 
   if (n > kSortMax) return gpt2_internal_fail(1, "encoder_backward: B*T=%d exceeds %d", n, kSortMax);
   if (!workspace || workspace_bytes < encoder_backward_sorted_workspace_bytes(B, T_, C))
     return gpt2_internal_fail(3, "encoder_backward: workspace too small");
-  const int shift = pos_bits(n);
   const int npieces = (int)ceil_div64(n, kPiece);
   float* pcont = (float*)workspace;
   float* pown = pcont + (size_t)npieces * C;
@@ -250,11 +281,11 @@ int encoder_backward_sorted(int B, int T_, int C, const uint32_t* sorted, const 
                        stream, B, T_, C, dx0, dwpe, accumulate_wpe);
     GPT2_LAUNCH_CHECK();
   }
-  hipLaunchKernelGGL(encoder_bwd_pieces_kernel, dim3(npieces), dim3(256), 0, stream, n, C, shift, sorted, dx0,
-                     dwte, pcont, pown);
+  hipLaunchKernelGGL(encoder_bwd_pieces_kernel, dim3(npieces), dim3(256), 0, stream, n, C, sorted, dx0, dwte, pcont,
+                     pown);
   GPT2_LAUNCH_CHECK();
-  hipLaunchKernelGGL(encoder_bwd_spans_kernel, dim3(npieces), dim3(256), 0, stream, n, C, shift, npieces, sorted,
-                     pcont, pown, dwte);
+  hipLaunchKernelGGL(encoder_bwd_spans_kernel, dim3(npieces), dim3(256), 0, stream, n, C, npieces, sorted, pcont,
+                     pown, dwte);
   GPT2_LAUNCH_CHECK();
   return 0;
 }
@@ -262,14 +293,14 @@ int encoder_backward_sorted(int B, int T_, int C, const uint32_t* sorted, const 
 int encoder_backward(int B, int T_, int C, int vocab_rows, const int32_t* tokens, const float* dx0,
                      float* dwte, float* dwpe, bool accumulate_wpe, void* workspace, size_t workspace_bytes,
                      hipStream_t stream) {
-  if (B < 0 || T_ < 0 || C <= 0 || vocab_rows <= 0 || vocab_rows > 65536 || !tokens || !dx0 || !dwte || !dwpe)
+  if (B < 0 || T_ < 0 || C <= 0 || vocab_rows <= 0 || !tokens || !dx0 || !dwte || !dwpe)
     return gpt2_internal_fail(1, "encoder_backward: bad arguments");
   const int n = B * T_;
   if (n == 0) return 0;
   if (!workspace || workspace_bytes < encoder_backward_workspace_bytes(B, T_, C))
     return gpt2_internal_fail(3, "encoder_backward: workspace too small");
-  uint32_t* sorted = (uint32_t*)workspace;
-  const size_t head = (((size_t)n * 4 + 255) / 256) * 256;
+  uint64_t* sorted = (uint64_t*)workspace;
+  const size_t head = encoder_sort_keys_bytes(n);
   int rc = encoder_sort_keys(n, vocab_rows, tokens, sorted, stream);
   if (rc) return rc;
   return encoder_backward_sorted(B, T_, C, sorted, dx0, dwte, dwpe, accumulate_wpe, (char*)workspace + head,

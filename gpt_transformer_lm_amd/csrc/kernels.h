@@ -165,15 +165,17 @@ int encoder_forward(int dtype, int B, int T, int C, int vocab_rows, const int32_
                     const void* wte, const void* wpe, void* out, hipStream_t stream);
 size_t encoder_backward_workspace_bytes(int B, int T, int C);
 // dwte[tok] += dx0 rows (fp32, deterministic order); dwpe[0:T] = (or +=) sum over b.
-// B*T <= 32768 and vocab_rows <= 65536 (one-workgroup key sort).
+// B*T <= 4194304 (the key sort's buffer).
 int encoder_backward(int B, int T, int C, int vocab_rows, const int32_t* tokens, const float* dx0,
                      float* dwte, float* dwpe, bool accumulate_wpe, void* workspace,
                      size_t workspace_bytes, hipStream_t stream);
 // The two parts of encoder_backward: the key sort depends only on the ids
-// (sorted: B*T uint32), the rest on dx0.
-int encoder_sort_keys(int n, int vocab_rows, const int32_t* tokens, uint32_t* sorted, hipStream_t stream);
+// (sorted: encoder_sort_keys_bytes(B*T) bytes of 64-bit keys, the first B*T
+// of them valid afterwards), the rest on dx0.
+size_t encoder_sort_keys_bytes(int n);
+int encoder_sort_keys(int n, int vocab_rows, const int32_t* tokens, uint64_t* sorted, hipStream_t stream);
 size_t encoder_backward_sorted_workspace_bytes(int B, int T, int C);
-int encoder_backward_sorted(int B, int T, int C, const uint32_t* sorted, const float* dx0, float* dwte,
+int encoder_backward_sorted(int B, int T, int C, const uint64_t* sorted, const float* dx0, float* dwte,
                             float* dwpe, bool accumulate_wpe, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
 

@@ -182,9 +182,14 @@ int validate(const gpt2_config* c) {
     return gpt2_internal_fail(GPT2_E_INVALID_ARG, "seq_len %d / max_seq_len %d", c->seq_len, c->max_seq_len);
   if (c->batch_size <= 0) return gpt2_internal_fail(GPT2_E_INVALID_ARG, "batch_size %d", c->batch_size);
   const int64_t BT = (int64_t)c->batch_size * c->seq_len;
-  if (BT % 64 || BT > 32768)
-    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "batch_size*seq_len = %lld must be a multiple of 64 and <= 32768",
+  if (BT % 64 || BT > (1 << 22))
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG, "batch_size*seq_len = %lld must be a multiple of 64 and <= 4194304",
                               (long long)BT);
+  // the classifier products address the bf16 logits with 32-bit offsets
+  if (c->dtype != GPT2_FP32 && BT * c->padded_vocab_size * 2 >= (int64_t)0xFFFFFFF0)
+    return gpt2_internal_fail(GPT2_E_INVALID_ARG,
+                              "batch_size*seq_len*padded_vocab_size*2 = %lld bytes of logits reach 4 GiB",
+                              (long long)(BT * c->padded_vocab_size * 2));
   if (c->arch_flags & ~(GPT2_ARCH_RELU2 | GPT2_ARCH_QK_NORM | GPT2_ARCH_ROPE))
     return gpt2_internal_fail(GPT2_E_INVALID_ARG, "arch_flags 0x%x has unknown bits", (unsigned)c->arch_flags);
   return GPT2_OK;
@@ -334,7 +339,7 @@ void make_layout(const gpt2_config& c, Layout* lo) {
   lo->d_ln = p.alloc(BT * C * es);
   lo->d_big = p.alloc(BT * 4 * C * es);
   lo->d_qkv = p.alloc(BT * 3 * C * es);
-  lo->sorted_keys = p.alloc(BT * 4);
+  lo->sorted_keys = p.alloc(encoder_sort_keys_bytes((int)BT));
   lo->rope_cs = (c.arch_flags & GPT2_ARCH_ROPE)
                     ? p.alloc((size_t)c.max_seq_len * (c.channels / c.num_heads / 2) * sizeof(float2))
                     : 0;
@@ -631,7 +636,7 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets, f
     // the key sort of the encoder backward runs beside the forward
     GPT2_HIP_CHECK(hipEventRecord(m->ev_fork, s));
     GPT2_HIP_CHECK(hipStreamWaitEvent(m->side, m->ev_fork, 0));
-    RC(encoder_sort_keys(BT, V, tok, m->at<uint32_t>(lo.sorted_keys), m->side));
+    RC(encoder_sort_keys(BT, V, tok, m->at<uint64_t>(lo.sorted_keys), m->side));
     GPT2_HIP_CHECK(hipEventRecord(m->ev_join, m->side));
     m->side_pending = true;
   }
@@ -869,7 +874,7 @@ int backward_impl(gpt2_model* m, bool acc) {
     GPT2_HIP_CHECK(hipStreamWaitEvent(s, m->ev_join, 0));
     m->side_pending = false;
   }
-  RC(encoder_backward_sorted(B, T, C, m->at<uint32_t>(lo.sorted_keys), dres, m->lgrad(0, 0), dwpe, acc, m->scratch(),
+  RC(encoder_backward_sorted(B, T, C, m->at<uint64_t>(lo.sorted_keys), dres, m->lgrad(0, 0), dwpe, acc, m->scratch(),
                              sb, s));
   return 0;
 }

@@ -99,8 +99,11 @@ typedef struct gpt2_config {
   int32_t num_heads;         /* H, C % H == 0                                  */
   int32_t channels;          /* C, multiple of 64                              */
   int32_t batch_size;        /* B: activation buffers are sized for B x T      */
-  int32_t seq_len;           /* T <= maxT; B*T multiple of 64, B*T <= 32768    */
-  int32_t dtype;             /* GPT2_FP32 or GPT2_BF16                         */
+  int32_t seq_len;           /* T <= maxT; B*T a multiple of 64, <= 4194304;
+                                 bf16 modes: B*T*Vp*2 < 4 GiB (B*T <= 42688 at
+                                 Vp = 50304: the classifier products address the
+                                 logits with 32-bit offsets)                    */
+  int32_t dtype;             /* GPT2_FP32, GPT2_BF16 or GPT2_BF16_FP8           */
   int32_t arch_flags;        /* GPT2_ARCH_* bits, 0 for GPT-2                  */
 } gpt2_config;
 

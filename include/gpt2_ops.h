@@ -204,7 +204,7 @@ int gpt2_op_encoder_forward(int dtype, int B, int T, int C, int V, const int32_t
 
 /* Encoder backward: dwte [V.., C] f32 += scatter of dx0 [B, T, C] f32 rows by
  * token (deterministic order); dwpe [T, C] f32 = (or += if accumulate_wpe)
- * sum over the batch.  B*T <= 32768, V <= 65536. */
+ * sum over the batch.  B*T <= 4194304. */
 size_t gpt2_op_encoder_backward_workspace_bytes(int B, int T, int C);
 int gpt2_op_encoder_backward(int B, int T, int C, int V, const int32_t* tokens, const float* dx0,
                              float* dwte, float* dwpe, int accumulate_wpe, void* workspace,

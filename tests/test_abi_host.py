@@ -89,7 +89,8 @@ def test_param_layout_is_contiguous_and_ordered():
     dict(Vp=50240),               # smaller than V
     dict(T=2048),                 # beyond maxT
     dict(B=0),
-    dict(B=64),                   # B*T > 32768
+    dict(B=64),                   # bf16 logits of B*T rows reach 4 GiB
+    dict(B=4160, T=1024, maxT=1024, dtype=0),   # B*T beyond the key sort's 4194304
     dict(dtype=7),
     dict(L=-1),
     dict(B=1, T=1000),            # B*T not a multiple of 64

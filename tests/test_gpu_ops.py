@@ -385,7 +385,10 @@ def test_classifier_full_size(N):
 # ---------------------------------------------------------------- encoder
 
 @pytest.mark.parametrize("dtype", DT, ids=DTN.get)
-@pytest.mark.parametrize("B,T,C,V", [(4, 64, 64, 512), (24, 1024, 768, 50257), (3, 40, 128, 300)])
+# (40, 1024): more positions than one workgroup's key sort held (32768);
+# (1, 5000): a non-power-of-two count above the 4096-key LDS chunk
+@pytest.mark.parametrize("B,T,C,V", [(4, 64, 64, 512), (24, 1024, 768, 50257), (3, 40, 128, 300),
+                                     (40, 1024, 64, 50257), (1, 5000, 64, 300)])
 def test_encoder(dtype, B, T, C, V):
     say("encoder", DTN[dtype], B, T, C, V)
     r = rng(B + T + C)
