@@ -62,7 +62,7 @@ KERNEL_OF = {
     "attn_fwd": "attn_fwd_mfma_kernel", "attn_bwd_dkdv": "attn_bwd_dkdv_mfma_kernel",
     "attn_bwd_dq": "attn_bwd_dq_mfma_kernel", "attn_bwd_dot": "attn_bwd_dot_kernel",
     "softmax_xent": "softmax_xent_bf16_kernel", "ln_fwd": "ln_fwd_half_kernel", "ln_bwd": "ln_bwd_kernel",
-    "encoder_fwd": "encoder_fwd_kernel", "adamw": "adamw_kernel", "weight_transpose": "transpose_bf16_kernel",
+    "encoder_fwd": "encoder_fwd_kernel", "adamw": "adamw_fused_kernel", "weight_transpose": "transpose_bf16_kernel",
     "grad_norm": "grad_sumsq_kernel", "qk_fwd": "qk_fwd_kernel", "qk_bwd": "qk_bwd_kernel",
     "fp8_quant": "quantize_kernel",
 }

@@ -72,6 +72,112 @@ __global__ void adamw_kernel(int64_t n, float* __restrict__ master, const float*
   }
 }
 
+// One AdamW element update (the formula above).
+__device__ __forceinline__ void adam_elem(float& th, float g, float& m, float& v, float lr, float b1, float b2,
+                                          float eps, float wd, float c1, float c2) {
+  m = b1 * m + (1.0f - b1) * g;
+  v = b2 * v + (1.0f - b2) * g * g;
+  th -= lr * ((m * c1) / (sqrtf(v * c2) + eps) + wd * th);
+}
+
+// The same update over the whole parameter array in one launch, where the
+// matrices whose bf16 copy the backward also reads transposed get that copy
+// here too: blocks [0, flat_blocks) sweep the flat ranges (everything but
+// those matrices) four elements per thread; each later block updates one
+// 64 x 64 tile of one matrix, stages its bf16 values in LDS and writes them
+// transposed as well (so the transposed copy costs 2 bytes per element
+// instead of a separate read-and-write pass).
+__global__ __launch_bounds__(256) void adamw_fused_kernel(AdamSegs sg, float* __restrict__ master,
+                                                          const float* __restrict__ grad, float* __restrict__ mom1,
+                                                          float* __restrict__ mom2, bf16* __restrict__ pbf,
+                                                          AdamHP hp_val, const AdamHP* __restrict__ hp_dev,
+                                                          const float* __restrict__ gscale) {
+  const AdamHP hp = hp_dev ? *hp_dev : hp_val;
+  const float lr = hp.lr, b1 = hp.b1, b2 = hp.b2, eps = hp.eps, wd = hp.wd, c1 = hp.c1, c2 = hp.c2;
+  const float gs = gscale ? *gscale : 1.0f;
+  typedef bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  if ((int)blockIdx.x < sg.flat_blocks) {
+    // flat ranges: index space [0, flat_total) in range order; every range
+    // starts and ends on a multiple of 4 elements
+    const int64_t stride = (int64_t)sg.flat_blocks * 256 * 4;
+    for (int64_t x = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; x < sg.flat_total; x += stride) {
+      int r = 0;
+      int64_t base = 0;
+      while (r + 1 < sg.nflat && x >= base + sg.flat_len[r]) base += sg.flat_len[r++];
+      const int64_t i = sg.flat_off[r] + (x - base);
+      float4 th = *reinterpret_cast<const float4*>(master + i);
+      const float4 g = *reinterpret_cast<const float4*>(grad + i);
+      float4 m = *reinterpret_cast<const float4*>(mom1 + i);
+      float4 v = *reinterpret_cast<const float4*>(mom2 + i);
+      adam_elem(th.x, g.x * gs, m.x, v.x, lr, b1, b2, eps, wd, c1, c2);
+      adam_elem(th.y, g.y * gs, m.y, v.y, lr, b1, b2, eps, wd, c1, c2);
+      adam_elem(th.z, g.z * gs, m.z, v.z, lr, b1, b2, eps, wd, c1, c2);
+      adam_elem(th.w, g.w * gs, m.w, v.w, lr, b1, b2, eps, wd, c1, c2);
+      *reinterpret_cast<float4*>(master + i) = th;
+      *reinterpret_cast<float4*>(mom1 + i) = m;
+      *reinterpret_cast<float4*>(mom2 + i) = v;
+      if (pbf) {
+        bf16x4_t o;
+        o[0] = (bf16)th.x; o[1] = (bf16)th.y; o[2] = (bf16)th.z; o[3] = (bf16)th.w;
+        *reinterpret_cast<bf16x4_t*>(pbf + i) = o;
+      }
+    }
+    return;
+  }
+  // one 64 x 64 tile of matrix k (batch bt): rows r0 .., columns c0 ..
+  int t = (int)blockIdx.x - sg.flat_blocks, k = 0;
+  while (k + 1 < sg.nmat && t >= sg.mat[k].tiles) t -= sg.mat[k++].tiles;
+  const AdamMatrix mt = sg.mat[k];
+  const int tr = (mt.R + 63) / 64, tc = (mt.Cc + 63) / 64;
+  const int bt = t / (tr * tc), rem = t % (tr * tc);
+  const int r0 = (rem / tc) * 64, c0 = (rem % tc) * 64;
+  const int64_t mbase = mt.off + (int64_t)bt * mt.R * mt.Cc;
+  __shared__ __attribute__((aligned(16))) bf16 tile[64][72];   // 144-byte rows
+  const int tid = threadIdx.x, cq = (tid & 15) * 4;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = (tid >> 4) + 16 * q;
+    bf16x4_t o;
+    if (r0 + r < mt.R && c0 + cq < mt.Cc) {
+      const int64_t i = mbase + (int64_t)(r0 + r) * mt.Cc + c0 + cq;
+      float4 th = *reinterpret_cast<const float4*>(master + i);
+      const float4 g = *reinterpret_cast<const float4*>(grad + i);
+      float4 m = *reinterpret_cast<const float4*>(mom1 + i);
+      float4 v = *reinterpret_cast<const float4*>(mom2 + i);
+      adam_elem(th.x, g.x * gs, m.x, v.x, lr, b1, b2, eps, wd, c1, c2);
+      adam_elem(th.y, g.y * gs, m.y, v.y, lr, b1, b2, eps, wd, c1, c2);
+      adam_elem(th.z, g.z * gs, m.z, v.z, lr, b1, b2, eps, wd, c1, c2);
+      adam_elem(th.w, g.w * gs, m.w, v.w, lr, b1, b2, eps, wd, c1, c2);
+      *reinterpret_cast<float4*>(master + i) = th;
+      *reinterpret_cast<float4*>(mom1 + i) = m;
+      *reinterpret_cast<float4*>(mom2 + i) = v;
+      o[0] = (bf16)th.x; o[1] = (bf16)th.y; o[2] = (bf16)th.z; o[3] = (bf16)th.w;
+      *reinterpret_cast<bf16x4_t*>(pbf + i) = o;
+    } else {
+      o[0] = o[1] = o[2] = o[3] = (bf16)0.f;
+    }
+    *reinterpret_cast<bf16x4_t*>(&tile[r][cq]) = o;
+  }
+  __syncthreads();
+  // transposed: row c0 + c of [batch][Cc][R] gets tile column c, 16 rows per thread
+  {
+    typedef bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+    const int c = tid >> 2, rr = (tid & 3) * 16;
+    bf16* dst = mt.dst_t + (int64_t)bt * mt.R * mt.Cc + (int64_t)(c0 + c) * mt.R + r0 + rr;
+    if (c0 + c < mt.Cc) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (r0 + rr + 8 * h + 8 <= mt.R) {
+          bf16x8_t o;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = tile[rr + 8 * h + e][c];
+          *reinterpret_cast<bf16x8_t*>(dst + 8 * h) = o;
+        }
+      }
+    }
+  }
+}
+
 // Global gradient norm for clipping: per-block partial sums of squares (a
 // fixed grid, grid-stride float4 reads), then one block adds the partials in
 // index order (deterministic), takes the square root and the clipping factor
@@ -234,6 +340,55 @@ int adamw(int64_t n, float* master, const float* grad, float* m, float* v, bf16*
   mark_begin(0, stream);
   hipLaunchKernelGGL(adamw_kernel, dim3(grid), dim3(256), 0, stream, n, master, grad, m, v, param_bf16, hp, hp_dev,
                      gscale);
+  GPT2_LAUNCH_CHECK();
+  mark_end(0, stream);
+  return 0;
+}
+
+int adamw_transposed(int64_t n, float* master, const float* grad, float* m, float* v, bf16* param_bf16,
+                     const AdamMatrix* mats, int nmats, hipStream_t stream, const float* gscale,
+                     const AdamHP* hp_dev) {
+  if (n < 0 || !master || !grad || !m || !v || !param_bf16 || !hp_dev || nmats < 0 || nmats > kAdamMaxMats ||
+      (nmats && !mats))
+    return gpt2_internal_fail(1, "adamw_transposed: bad arguments");
+  if (((uintptr_t)master | (uintptr_t)grad | (uintptr_t)m | (uintptr_t)v) % 16 || (uintptr_t)param_bf16 % 8)
+    return gpt2_internal_fail(1, "adamw_transposed: buffers must be 16-byte aligned");
+  AdamSegs sg{};
+  sg.nmat = nmats;
+  int64_t prev_end = 0;
+  int total_tiles = 0;
+  for (int k = 0; k < nmats; ++k) {
+    AdamMatrix mt = mats[k];
+    const int64_t len = (int64_t)mt.batches * mt.R * mt.Cc;
+    if (mt.off < prev_end || mt.off + len > n || mt.R <= 0 || mt.Cc <= 0 || mt.R % 8 || mt.Cc % 4 || mt.off % 4 ||
+        !mt.dst_t || (uintptr_t)mt.dst_t % 16)
+      return gpt2_internal_fail(1, "adamw_transposed: matrix %d not in order, unaligned or out of range", k);
+    if (mt.off > prev_end) {
+      if (sg.nflat == kAdamMaxMats + 1) return gpt2_internal_fail(1, "adamw_transposed: too many ranges");
+      sg.flat_off[sg.nflat] = prev_end;
+      sg.flat_len[sg.nflat++] = mt.off - prev_end;
+    }
+    mt.tiles = mt.batches * ((mt.R + 63) / 64) * ((mt.Cc + 63) / 64);
+    total_tiles += mt.tiles;
+    sg.mat[k] = mt;
+    prev_end = mt.off + len;
+  }
+  if (n > prev_end) {
+    if (sg.nflat == kAdamMaxMats + 1) return gpt2_internal_fail(1, "adamw_transposed: too many ranges");
+    sg.flat_off[sg.nflat] = prev_end;
+    sg.flat_len[sg.nflat++] = n - prev_end;
+  }
+  for (int r = 0; r < sg.nflat; ++r) {
+    if (sg.flat_off[r] % 4 || sg.flat_len[r] % 4)
+      return gpt2_internal_fail(1, "adamw_transposed: flat range %d not a multiple of 4 elements", r);
+    sg.flat_total += sg.flat_len[r];
+  }
+  sg.flat_blocks = (int)std::min<int64_t>(ceil_div64(sg.flat_total, 4 * 256), 2048);
+  const unsigned grid = (unsigned)(sg.flat_blocks + total_tiles);
+  if (grid == 0) return 0;
+  mark_begin(0, stream);
+  hipLaunchKernelGGL(adamw_fused_kernel, dim3(grid), dim3(256), 0, stream, sg, master, grad, m, v, param_bf16,
+                     AdamHP{}, hp_dev, gscale);
   GPT2_LAUNCH_CHECK();
   mark_end(0, stream);
   return 0;

@@ -196,6 +196,27 @@ int set_adam_hparams(AdamHP* dst, const AdamHP& v, hipStream_t stream);
 int adamw(int64_t n, float* master, const float* grad, float* m, float* v, bf16* param_bf16,
           float lr, float beta1, float beta2, float eps, float wd, int t, hipStream_t stream,
           const float* gscale = nullptr, const AdamHP* hp_dev = nullptr);
+// AdamW as above (hyperparameters from hp_dev) that also writes, for each
+// listed matrix block (`batches` row-major [R][Cc] fp32 matrices starting at
+// element `off`, in increasing order, R % 8 == 0, Cc % 4 == 0), the
+// transposed bf16 copy dst_t[b][c][r]; the ranges between the matrices must
+// start and end on multiples of 4 elements.  One launch.
+constexpr int kAdamMaxMats = 6;
+struct AdamMatrix {
+  int64_t off;
+  int batches, R, Cc;
+  bf16* dst_t;
+  int tiles;   // set by the launcher
+};
+struct AdamSegs {
+  int nflat, nmat, flat_blocks;
+  int64_t flat_total;
+  int64_t flat_off[kAdamMaxMats + 1], flat_len[kAdamMaxMats + 1];
+  AdamMatrix mat[kAdamMaxMats];
+};
+int adamw_transposed(int64_t n, float* master, const float* grad, float* m, float* v, bf16* param_bf16,
+                     const AdamMatrix* mats, int nmats, hipStream_t stream, const float* gscale,
+                     const AdamHP* hp_dev);
 // dst[i] = src[i], i < n (device int32 arrays).
 int copy_i32(int64_t n, const int32_t* src, int32_t* dst, hipStream_t stream);
 // Global L2 norm of n fp32 gradients (16-byte aligned) into workspace[0] and

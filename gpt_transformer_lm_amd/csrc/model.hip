@@ -954,14 +954,35 @@ int update_impl(gpt2_model* m, float max_grad_norm, bool need_norm) {
     RC(timed(m, S_GRAD_NORM, 0.0, 4.0 * (double)m->lo.P,
              [&] { return grad_norm(m->lo.P, m->grad(), max_grad_norm, gn, m->stream); }));
   }
-  // fp32 master, m, v read and written, fp32 gradient read, bf16 copy written
-  RC(timed(m, S_ADAMW, 0.0, (double)m->lo.P * (is_bf16(m->cfg) ? 30.0 : 28.0), [&] {
-    return adamw(m->lo.P, m->master(), m->grad(), m->at<float>(m->lo.adam_m), m->at<float>(m->lo.adam_v),
-                 is_bf16(m->cfg) ? m->at<bf16>(m->lo.params_bf16) : nullptr, 0.f, 0.f, 0.f, 0.f, 0.f, 1,
-                 m->stream, max_grad_norm > 0.f ? gn + 1 : nullptr, m->at<AdamHP>(m->lo.adam_hp));
+  const float* gscale = max_grad_norm > 0.f ? gn + 1 : nullptr;
+  if (!is_bf16(m->cfg)) {
+    // fp32 master, m, v read and written, fp32 gradient read
+    return timed(m, S_ADAMW, 0.0, (double)m->lo.P * 28.0, [&] {
+      return adamw(m->lo.P, m->master(), m->grad(), m->at<float>(m->lo.adam_m), m->at<float>(m->lo.adam_v),
+                   nullptr, 0.f, 0.f, 0.f, 0.f, 0.f, 1, m->stream, gscale, m->at<AdamHP>(m->lo.adam_hp));
+    });
+  }
+  // bf16 modes: one launch that also writes the transposed bf16 weight
+  // copies; bytes: master, m, v read and written, gradient read, bf16 copy
+  // written (30 per parameter) and the transposed copies (2 per element)
+  AdamMatrix mats[kAdamMaxMats];
+  int nm = 0;
+  double tbytes = 0.0;
+  for (int i : kTransposed) {
+    if (!m->lo.params_t[i]) continue;   // (fp8 mode: only the attention projection keeps a bf16 copy)
+    const int64_t* sh = m->lo.pt.shape[i];
+    const bool layered = m->lo.pt.ndim[i] == 3;
+    const int R = (int)(layered ? sh[1] : sh[0]), Cc = (int)(layered ? sh[2] : sh[1]);
+    mats[nm++] = AdamMatrix{(int64_t)m->lo.pt.off[i], layered ? (int)sh[0] : 1, R, Cc, static_cast<bf16*>(m->wt(i, 0)),
+                            0};
+    tbytes += 2.0 * (layered ? (double)sh[0] : 1.0) * R * Cc;
+  }
+  RC(timed(m, S_ADAMW, 0.0, (double)m->lo.P * 30.0 + tbytes, [&] {
+    return adamw_transposed(m->lo.P, m->master(), m->grad(), m->at<float>(m->lo.adam_m), m->at<float>(m->lo.adam_v),
+                            m->at<bf16>(m->lo.params_bf16), mats, nm, m->stream, gscale,
+                            m->at<AdamHP>(m->lo.adam_hp));
   }));
-  RC(refresh_fp8_weights(m));
-  return refresh_transposed(m);
+  return refresh_fp8_weights(m);
 }
 
 void graph_release(gpt2_model* m) {
