@@ -99,12 +99,17 @@ def measured_traffic(site, config):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    src = os.path.join(ROOT, kv.get("source", ""))
-    if not os.path.isfile(src):
+    srcs = [s.strip() for s in kv.get("source", "").split(",") if s.strip()]
+    shas = [s.strip() for s in kv.get("source_sha256", "").split(",")]
+    if not srcs or len(srcs) != len(shas):
         return None
-    with open(src, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != kv.get("source_sha256"):
+    for src, sha in zip(srcs, shas):
+        path_src = os.path.join(ROOT, src)
+        if not os.path.isfile(path_src):
             return None
+        with open(path_src, "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != sha:
+                return None
     try:
         return float(kv["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
