@@ -13,8 +13,9 @@
 // operands k-major.
 //
 // The bias gradient of an fp8 weight-gradient product is the column sum of
-// the unquantised bf16 gradient: per-row-block partial sums (256 row blocks,
-// eight columns per thread), then an in-order sum (deterministic).
+// the unquantised bf16 gradient, taken while the gradient is quantised: each
+// 64 x 64 tile adds its 64 rows per column in order into a per-row-block
+// partial, and a second kernel adds the row blocks in order (deterministic).
 
 #include "kernels.h"
 
@@ -22,7 +23,6 @@ namespace gpt2k {
 namespace {
 
 constexpr int kAmaxBlocks = 1024;
-constexpr int kColsumRowBlocks = 256;
 
 template <typename T>
 __global__ __launch_bounds__(256) void absmax_partial_kernel(int64_t n, const T* __restrict__ x,
@@ -90,12 +90,34 @@ __device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
 
 // x [R, Cc] (row stride ldx) -> qrow [R, Cc] and / or qt [Cc, R] codes.
 // Grid (ceil(Cc / 64), ceil(R / 64)); Cc % 8 == 0, R % 16 == 0 when qt.
-template <typename T, int FMT>
+// With CS, also colsum[blockIdx.y][c] = sum of x[r][c] over the tile's rows
+// (in row order), for the bias gradient.
+// The scale comes from the np per-block maxima of the amax pass: every block
+// takes their maximum (exact, so all agree) and forms inv and s as above;
+// block (0, 0) stores (amax, inv, s) for the products.
+template <typename T, int FMT, bool CS>
 __global__ __launch_bounds__(256) void quantize_kernel(int R, int Cc, const T* __restrict__ x, int64_t ldx,
-                                                       const Fp8Scale* __restrict__ sc, uint8_t* __restrict__ qrow,
-                                                       uint8_t* __restrict__ qt) {
+                                                       const float* __restrict__ amax_part, int np, float fmax,
+                                                       Fp8Scale* __restrict__ sc, uint8_t* __restrict__ qrow,
+                                                       uint8_t* __restrict__ qt, float* __restrict__ colsum) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[64][64 + 16];
-  const float inv = sc->inv;
+  __shared__ float ftile[CS ? 64 : 1][CS ? 65 : 1];
+  __shared__ float smax[4];
+  float am = 0.f;
+  for (int i = threadIdx.x; i < np; i += 256) am = fmaxf(am, amax_part[i]);
+  am = wave_max(am);
+  if ((threadIdx.x & 63) == 0) smax[threadIdx.x >> 6] = am;
+  __syncthreads();
+  am = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
+  const float inv = am > 0.f ? fmax / am : 1.0f;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    Fp8Scale r;
+    r.amax = am;
+    r.inv = inv;
+    r.s = am > 0.f ? am / fmax : 1.0f;
+    r.unused = 0.f;
+    *sc = r;
+  }
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   for (int i = threadIdx.x; i < 64 * 8; i += 256) {
     const int r = i >> 3, cc = (i & 7) * 8;
@@ -104,11 +126,23 @@ __global__ __launch_bounds__(256) void quantize_kernel(int R, int Cc, const T* _
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = 0.f;
     if (in) Chunk8<T>::load(x + (int64_t)(r0 + r) * ldx + c0 + cc, v);
+    if constexpr (CS) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ftile[r][cc + e] = v[e];
+    }
     uint2 w;
     w.x = pack4<FMT>(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
     w.y = pack4<FMT>(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
     if (qrow && in) *reinterpret_cast<uint2*>(qrow + (int64_t)(r0 + r) * Cc + c0 + cc) = w;
     if (qt) *reinterpret_cast<uint2*>(&tile[r][cc]) = w;
+  }
+  if constexpr (CS) {
+    __syncthreads();
+    if (threadIdx.x < 64 && c0 + (int)threadIdx.x < Cc) {
+      float t = 0.f;
+      for (int r = 0; r < 64; ++r) t += ftile[r][threadIdx.x];
+      colsum[(int64_t)blockIdx.y * Cc + c0 + threadIdx.x] = t;
+    }
   }
   if (qt) {
     __syncthreads();
@@ -124,98 +158,92 @@ __global__ __launch_bounds__(256) void quantize_kernel(int R, int Cc, const T* _
   }
 }
 
-// part[b][n] = sum of dy[r][n] over rows r of row block b; each thread sums
-// eight adjacent columns (one 16-byte load per row), N % 8 == 0.
-__global__ __launch_bounds__(256) void colsum_partial_kernel(int R, int N, const bf16* __restrict__ dy,
-                                                             float* __restrict__ part) {
-  const int c8 = blockIdx.x * 256 + threadIdx.x;
-  if (c8 * 8 >= N) return;
-  const int rows = (R + gridDim.y - 1) / gridDim.y;
-  const int r_beg = blockIdx.y * rows, r_end = min(R, r_beg + rows);
-  float s[8];
+// db[n] (+)= sum over the row blocks b of part[b][n], in a fixed order:
+// sixteen groups of 64 threads take every sixteenth block, then the groups'
+// sums are added in group order.
+__global__ __launch_bounds__(1024) void colsum_reduce_kernel(int nb, int N, const float* __restrict__ part,
+                                                             float* __restrict__ db, bool acc) {
+  __shared__ float sh[16][64];
+  const int c = threadIdx.x & 63, g = threadIdx.x >> 6, n = blockIdx.x * 64 + c;
+  float t = 0.f;
+  if (n < N)
+#pragma unroll 4
+    for (int b = g; b < nb; b += 16) t += part[(int64_t)b * N + n];
+  sh[g][c] = t;
+  __syncthreads();
+  if (g == 0 && n < N) {
+    float s = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) s[e] = 0.f;
-  for (int r = r_beg; r < r_end; ++r) {
-    float v[8];
-    Chunk8<bf16>::load(dy + (int64_t)r * N + c8 * 8, v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s[e] += v[e];
+    for (int k = 0; k < 16; ++k) s += sh[k][c];
+    db[n] = acc ? db[n] + s : s;
   }
-  Chunk8<float>::store(part + (int64_t)blockIdx.y * N + c8 * 8, s);
-}
-
-__global__ __launch_bounds__(256) void colsum_final_kernel(int N, int nb, const float* __restrict__ part,
-                                                           float* __restrict__ db, bool acc) {
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
-  float s = acc ? db[n] : 0.f;
-  for (int b = 0; b < nb; ++b) s += part[(int64_t)b * N + n];
-  db[n] = s;
 }
 
 }  // namespace
 
 size_t fp8_scale_workspace_bytes() { return kAmaxBlocks * sizeof(float); }
 
-int fp8_compute_scale(int dtype_in, int64_t n, const void* x, int fmt, Fp8Scale* out, float* workspace,
-                      hipStream_t stream) {
-  if (n < 0 || !x || !out || !workspace || (fmt != 0 && fmt != 1) || (uintptr_t)x % 16)
-    return gpt2_internal_fail(1, "fp8_compute_scale: bad arguments");
-  const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>(kAmaxBlocks, ceil_div64(n, 8 * 256)));
+int amax_blocks(int64_t n) {
+  return (int)std::max<int64_t>(1, std::min<int64_t>(kAmaxBlocks, ceil_div64(n, 8 * 256)));
+}
+
+int fp8_amax(int dtype_in, int64_t n, const void* x, float* workspace, hipStream_t stream) {
+  if (n < 0 || !x || !workspace || (uintptr_t)x % 16) return gpt2_internal_fail(1, "fp8_amax: bad arguments");
+  const unsigned blocks = (unsigned)amax_blocks(n);
   if (dtype_in == BF16)
     hipLaunchKernelGGL(absmax_partial_kernel<bf16>, dim3(blocks), dim3(256), 0, stream, n, (const bf16*)x, workspace);
   else
     hipLaunchKernelGGL(absmax_partial_kernel<float>, dim3(blocks), dim3(256), 0, stream, n, (const float*)x,
                        workspace);
   GPT2_LAUNCH_CHECK();
-  hipLaunchKernelGGL(fp8_scale_finalize_kernel, dim3(1), dim3(256), 0, stream, workspace, (int)blocks,
-                     fmt == 0 ? 448.0f : 57344.0f, out);
-  GPT2_LAUNCH_CHECK();
   return 0;
 }
 
-int fp8_quantize(int dtype_in, int fmt, int R, int Cc, const void* x, int64_t ldx, const Fp8Scale* sc, uint8_t* qrow,
-                 uint8_t* qt, hipStream_t stream) {
-  if (R < 0 || Cc < 0 || !x || !sc || (!qrow && !qt) || Cc % 8 || ldx % 8 || (qt && R % 16) || (uintptr_t)x % 16 ||
-      (fmt != 0 && fmt != 1))
+template <typename T, int FMT>
+void launch_quantize(dim3 grid, int R, int Cc, const void* x, int64_t ldx, const float* amax_part, int np,
+                     Fp8Scale* sc, uint8_t* qrow, uint8_t* qt, float* colsum, hipStream_t stream) {
+  const float fmax = FMT == 0 ? 448.0f : 57344.0f;
+  if (colsum)
+    hipLaunchKernelGGL((quantize_kernel<T, FMT, true>), grid, dim3(256), 0, stream, R, Cc, (const T*)x, ldx, amax_part,
+                       np, fmax, sc, qrow, qt, colsum);
+  else
+    hipLaunchKernelGGL((quantize_kernel<T, FMT, false>), grid, dim3(256), 0, stream, R, Cc, (const T*)x, ldx,
+                       amax_part, np, fmax, sc, qrow, qt, colsum);
+}
+
+int fp8_quantize(int dtype_in, int fmt, int R, int Cc, const void* x, int64_t ldx, const float* amax_part,
+                 Fp8Scale* sc, uint8_t* qrow, uint8_t* qt, hipStream_t stream, float* colsum) {
+  if (R < 0 || Cc < 0 || !x || !amax_part || !sc || (!qrow && !qt) || Cc % 8 || ldx % 8 || (qt && R % 16) ||
+      (uintptr_t)x % 16 || (fmt != 0 && fmt != 1))
     return gpt2_internal_fail(1, "fp8_quantize: bad arguments (R=%d, C=%d)", R, Cc);
-  if (R == 0 || Cc == 0) return 0;
+  const int np = amax_blocks((int64_t)R * Cc);
+  if (R == 0 || Cc == 0) {   // no tile to store the scale: the one-block form
+    hipLaunchKernelGGL(fp8_scale_finalize_kernel, dim3(1), dim3(256), 0, stream, amax_part, np,
+                       fmt == 0 ? 448.0f : 57344.0f, sc);
+    GPT2_LAUNCH_CHECK();
+    return 0;
+  }
   dim3 grid((unsigned)ceil_div64(Cc, 64), (unsigned)ceil_div64(R, 64));
   mark_begin(0, stream);
   if (dtype_in == BF16) {
-    if (fmt == 0)
-      hipLaunchKernelGGL((quantize_kernel<bf16, 0>), grid, dim3(256), 0, stream, R, Cc, (const bf16*)x, ldx, sc, qrow,
-                         qt);
-    else
-      hipLaunchKernelGGL((quantize_kernel<bf16, 1>), grid, dim3(256), 0, stream, R, Cc, (const bf16*)x, ldx, sc, qrow,
-                         qt);
+    if (fmt == 0) launch_quantize<bf16, 0>(grid, R, Cc, x, ldx, amax_part, np, sc, qrow, qt, colsum, stream);
+    else launch_quantize<bf16, 1>(grid, R, Cc, x, ldx, amax_part, np, sc, qrow, qt, colsum, stream);
   } else {
-    if (fmt == 0)
-      hipLaunchKernelGGL((quantize_kernel<float, 0>), grid, dim3(256), 0, stream, R, Cc, (const float*)x, ldx, sc,
-                         qrow, qt);
-    else
-      hipLaunchKernelGGL((quantize_kernel<float, 1>), grid, dim3(256), 0, stream, R, Cc, (const float*)x, ldx, sc,
-                         qrow, qt);
+    if (fmt == 0) launch_quantize<float, 0>(grid, R, Cc, x, ldx, amax_part, np, sc, qrow, qt, colsum, stream);
+    else launch_quantize<float, 1>(grid, R, Cc, x, ldx, amax_part, np, sc, qrow, qt, colsum, stream);
   }
   GPT2_LAUNCH_CHECK();
   mark_end(0, stream);
   return 0;
 }
 
-size_t bias_grad_workspace_bytes(int N) { return (size_t)kColsumRowBlocks * N * sizeof(float); }
+size_t fp8_colsum_bytes(int R, int N) { return (size_t)ceil_div64(R, 64) * N * sizeof(float); }
 
-int bias_grad_bf16(int R, int N, const bf16* dy, float* db, bool accumulate, float* workspace, size_t workspace_bytes,
-                   hipStream_t stream) {
-  if (R < 0 || N < 0 || N % 8 || !dy || (uintptr_t)dy % 16 || !db || !workspace ||
-      workspace_bytes < bias_grad_workspace_bytes(N))
-    return gpt2_internal_fail(1, "bias_grad_bf16: bad arguments");
+int colsum_reduce(int R, int N, const float* part, float* db, bool accumulate, hipStream_t stream) {
+  if (R < 0 || N < 0 || !part || !db) return gpt2_internal_fail(1, "colsum_reduce: bad arguments");
   if (N == 0) return 0;
-  hipLaunchKernelGGL(colsum_partial_kernel, dim3((unsigned)ceil_div64(N / 8, 256), kColsumRowBlocks), dim3(256), 0,
-                     stream, R, N, dy, workspace);
-  GPT2_LAUNCH_CHECK();
-  const unsigned nx = (unsigned)ceil_div64(N, 256);
-  hipLaunchKernelGGL(colsum_final_kernel, dim3(nx), dim3(256), 0, stream, N, kColsumRowBlocks, workspace, db,
-                     accumulate);
+  hipLaunchKernelGGL(colsum_reduce_kernel, dim3((unsigned)ceil_div64(N, 64)), dim3(1024), 0, stream,
+                     (int)ceil_div64(R, 64), N, part, db, accumulate);
   GPT2_LAUNCH_CHECK();
   return 0;
 }

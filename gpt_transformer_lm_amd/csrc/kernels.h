@@ -123,18 +123,22 @@ struct Fp8Scale {
   float amax, inv, s, unused;
 };
 size_t fp8_scale_workspace_bytes();
-// *out = the scale of the n contiguous values x (bf16 or fp32, 16-byte aligned).
-int fp8_compute_scale(int dtype_in, int64_t n, const void* x, int fmt, Fp8Scale* out, float* workspace,
-                      hipStream_t stream);
-// Codes of fp8(x * inv) for x [R, Cc] (row stride ldx): row-major into qrow
-// [R, Cc] and / or transposed into qt [Cc, R] (either may be NULL).
-// Cc % 8 == 0; R % 16 == 0 when qt.
-int fp8_quantize(int dtype_in, int fmt, int R, int Cc, const void* x, int64_t ldx, const Fp8Scale* sc,
-                 uint8_t* qrow, uint8_t* qt, hipStream_t stream);
-// db[n] (+)= sum over the R rows of dy [R, N] (bf16), fixed summation order.
-size_t bias_grad_workspace_bytes(int N);
-int bias_grad_bf16(int R, int N, const bf16* dy, float* db, bool accumulate, float* workspace,
-                   size_t workspace_bytes, hipStream_t stream);
+// Per-block maxima of |x| over the n contiguous values x (bf16 or fp32,
+// 16-byte aligned) into workspace (fp8_scale_workspace_bytes()), for the
+// quantisation of the same n values.
+int fp8_amax(int dtype_in, int64_t n, const void* x, float* workspace, hipStream_t stream);
+// The scale of x from those maxima (stored into *sc) and the codes of
+// fp8(x * inv) for x [R, Cc] (row stride ldx, R * Cc the n of fp8_amax):
+// row-major into qrow [R, Cc] and / or transposed into qt [Cc, R] (either may
+// be NULL).  Cc % 8 == 0; R % 16 == 0 when qt.  With colsum
+// (fp8_colsum_bytes(R, Cc), device) also the per-64-row-block column sums of
+// x that colsum_reduce turns into a bias gradient.
+int fp8_quantize(int dtype_in, int fmt, int R, int Cc, const void* x, int64_t ldx, const float* amax_part,
+                 Fp8Scale* sc, uint8_t* qrow, uint8_t* qt, hipStream_t stream, float* colsum = nullptr);
+size_t fp8_colsum_bytes(int R, int N);
+// db[n] (+)= sum of the column sums left by fp8_quantize for R rows, in a
+// fixed order.
+int colsum_reduce(int R, int N, const float* colsum, float* db, bool accumulate, hipStream_t stream);
 
 // ------------------------------------------------------------------ QK-Norm / rotary
 // In place on the q and k columns of qkv [BT, 3C] (hd = C / H): QK-Norm (RMS

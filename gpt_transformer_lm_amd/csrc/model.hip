@@ -245,7 +245,7 @@ struct Layout {
   // fp8 mode (0 otherwise): weight codes per parameter tensor (row-major and
   // transposed, all layers), lnf codes, the current output gradient's codes,
   // per-tensor scales, absmax partials
-  size_t wq[16], wqt[16], lnf_q, lnf_qt, dq, dqt, fp8_scales, fp8_amax;
+  size_t wq[16], wqt[16], lnf_q, lnf_qt, dq, dqt, fp8_scales, fp8_amax, fp8_colsum;
   size_t scratch_bytes;
   size_t total;
 };
@@ -272,7 +272,6 @@ size_t scratch_need(const gpt2_config& c) {
     for (auto& nk : fp8_n) {
       upd(gemm_workspace_bytes(GPT2_BF16, EPI_WGRAD, nk[0], nk[1], BT, true, true, 2));
       upd(gemm_workspace_bytes(GPT2_BF16, EPI_STORE, BT, nk[1], nk[0], true, true, 2));
-      upd(bias_grad_workspace_bytes(nk[0]));
     }
   }
   upd(attention_backward_workspace_bytes(c.batch_size, c.seq_len, c.num_heads, C / c.num_heads));
@@ -344,7 +343,7 @@ void make_layout(const gpt2_config& c, Layout* lo) {
                     ? p.alloc((size_t)c.max_seq_len * (c.channels / c.num_heads / 2) * sizeof(float2))
                     : 0;
   for (int i = 0; i < 16; ++i) lo->wq[i] = lo->wqt[i] = 0;
-  lo->lnf_q = lo->lnf_qt = lo->dq = lo->dqt = lo->fp8_scales = lo->fp8_amax = 0;
+  lo->lnf_q = lo->lnf_qt = lo->dq = lo->dqt = lo->fp8_scales = lo->fp8_amax = lo->fp8_colsum = 0;
   if (c.dtype == GPT2_BF16_FP8) {
     for (int i : kFp8Weights) {
       const int64_t* sh = lo->pt.shape[i];
@@ -358,6 +357,7 @@ void make_layout(const gpt2_config& c, Layout* lo) {
     lo->dqt = p.alloc(big);
     lo->fp8_scales = p.alloc((size_t)fp8_slots((int)L) * sizeof(Fp8Scale));
     lo->fp8_amax = p.alloc(fp8_scale_workspace_bytes());
+    lo->fp8_colsum = p.alloc(fp8_colsum_bytes((int)BT, 4 * C));
   }
   lo->scratch_bytes = scratch_need(c);
   lo->scratch = p.alloc(lo->scratch_bytes);
@@ -565,13 +565,19 @@ GemmDesc dw_desc(gpt2_model* m, int M, int N, int K, const void* dy, const void*
 
 // Per-tensor scale of x [R, Cc] (bf16 or fp32) into `slot`, then its codes
 // row-major (q) and / or transposed (qt).  fmt 0: E4M3, 1: E5M2.
-int fp8_quant(gpt2_model* m, int dtype_in, const void* x, int R, int Cc, int fmt, int slot, uint8_t* q, uint8_t* qt) {
+// colsum: also leave the column sums of x (for a bias gradient) in the
+// arena's column-sum buffer.
+int fp8_quant(gpt2_model* m, int dtype_in, const void* x, int R, int Cc, int fmt, int slot, uint8_t* q, uint8_t* qt,
+              bool colsum = false) {
   if (m->dry()) return 0;
   Fp8Scale* sc = m->fscale(slot);
-  RC(fp8_compute_scale(dtype_in, (int64_t)R * Cc, x, fmt, sc, m->at<float>(m->lo.fp8_amax), m->stream));
+  float* amax = m->at<float>(m->lo.fp8_amax);
+  RC(fp8_amax(dtype_in, (int64_t)R * Cc, x, amax, m->stream));
   const double in_b = (double)R * Cc * (dtype_in == GPT2_BF16 ? 2 : 4);
-  return timed(m, S_FP8_QUANT, 0.0, in_b + (double)R * Cc * ((q ? 1 : 0) + (qt ? 1 : 0)),
-               [&] { return fp8_quantize(dtype_in, fmt, R, Cc, x, Cc, sc, q, qt, m->stream); });
+  return timed(m, S_FP8_QUANT, 0.0, in_b + (double)R * Cc * ((q ? 1 : 0) + (qt ? 1 : 0)), [&] {
+    return fp8_quantize(dtype_in, fmt, R, Cc, x, Cc, amax, sc, q, qt, m->stream,
+                        colsum ? m->at<float>(m->lo.fp8_colsum) : nullptr);
+  });
 }
 
 // The forward product x W^T as an fp8 product of the codes xq (scale slot
@@ -608,11 +614,11 @@ GemmDesc fp8_dw(gpt2_model* m, int M, int N, int K, const uint8_t* dqt, int ds, 
   return d;
 }
 
-// Bias gradient of an fp8 weight-gradient product (from the bf16 gradient).
-int fp8_bias_grad(gpt2_model* m, int M, int N, const void* dy, float* db, bool acc) {
+// Bias gradient of an fp8 weight-gradient product: the column sums of the
+// unquantised bf16 gradient that its quantisation left (fp8_quant(colsum)).
+int fp8_bias_grad(gpt2_model* m, int M, int N, float* db, bool acc) {
   if (m->dry()) return 0;
-  return bias_grad_bf16(M, N, static_cast<const bf16*>(dy), db, acc, static_cast<float*>(m->scratch()),
-                        m->lo.scratch_bytes, m->stream);
+  return colsum_reduce(M, N, m->at<float>(m->lo.fp8_colsum), db, acc, m->stream);
 }
 
 // loss_scale: the dlogits (and so every gradient of the next backward) are
@@ -780,18 +786,18 @@ int backward_impl(gpt2_model* m, bool acc) {
     if (m->fp8()) {
       // x_{l+1} = h + g Wp^T + bp: dY = the residual gradient (bf16 copy)
       const int gp = fp8_slot(L, Q_GRAD, 0, l), gf = fp8_slot(L, Q_GRAD, 1, l);
-      RC(fp8_quant(m, GPT2_BF16, dres_t, BT, C, 1, gp, dq, dqt));
+      RC(fp8_quant(m, GPT2_BF16, dres_t, BT, C, 1, gp, dq, dqt, true));
       RC(run_gemm(m, S_FCPROJ_DW, fp8_dw(m, BT, C, 4 * C, dqt, gp, m->at<uint8_t>(o.g_qt), fp8_slot(L, Q_ACT, 2, l),
                                          m->lgrad(12, l), acc)));
-      RC(fp8_bias_grad(m, BT, C, dres_t, m->lgrad(13, l), acc));
+      RC(fp8_bias_grad(m, BT, C, m->lgrad(13, l), acc));
       // du = (dy W_p) * GELU'(u), the derivative saved by the forward
       RC(run_gemm(m, S_FCPROJ_DX, fp8_dx(m, BT, C, 4 * C, dq, gp, m->wqt(12, l), fp8_slot(L, Q_WEIGHT, 3, l), d_big,
                                          EPI_MUL, m->at<char>(o.u))));
       // u = ln2 Wfc^T + bfc   (d_big now holds du)
-      RC(fp8_quant(m, GPT2_BF16, d_big, BT, 4 * C, 1, gf, dq, dqt));
+      RC(fp8_quant(m, GPT2_BF16, d_big, BT, 4 * C, 1, gf, dq, dqt, true));
       RC(run_gemm(m, S_FC_DW, fp8_dw(m, BT, 4 * C, C, dqt, gf, m->at<uint8_t>(o.ln2_qt), fp8_slot(L, Q_ACT, 1, l),
                                      m->lgrad(10, l), acc)));
-      RC(fp8_bias_grad(m, BT, 4 * C, d_big, m->lgrad(11, l), acc));
+      RC(fp8_bias_grad(m, BT, 4 * C, m->lgrad(11, l), acc));
       RC(run_gemm(m, S_FC_DX, fp8_dx(m, BT, 4 * C, C, dq, gf, m->wqt(10, l), fp8_slot(L, Q_WEIGHT, 2, l), d_ln,
                                      EPI_STORE, nullptr)));
     } else {
@@ -843,10 +849,10 @@ int backward_impl(gpt2_model* m, bool acc) {
     // qkv = ln1 Wqkv^T + bqkv
     if (m->fp8()) {
       const int gq = fp8_slot(L, Q_GRAD, 2, l);
-      RC(fp8_quant(m, GPT2_BF16, d_qkv, BT, 3 * C, 1, gq, dq, dqt));
+      RC(fp8_quant(m, GPT2_BF16, d_qkv, BT, 3 * C, 1, gq, dq, dqt, true));
       RC(run_gemm(m, S_QKV_DW, fp8_dw(m, BT, 3 * C, C, dqt, gq, m->at<uint8_t>(o.ln1_qt), fp8_slot(L, Q_ACT, 0, l),
                                       m->lgrad(4, l), acc)));
-      RC(fp8_bias_grad(m, BT, 3 * C, d_qkv, m->lgrad(5, l), acc));
+      RC(fp8_bias_grad(m, BT, 3 * C, m->lgrad(5, l), acc));
       RC(run_gemm(m, S_QKV_DX, fp8_dx(m, BT, 3 * C, C, dq, gq, m->wqt(4, l), fp8_slot(L, Q_WEIGHT, 1, l), d_ln,
                                       EPI_STORE, nullptr)));
     } else {
@@ -1522,8 +1528,8 @@ int gpt2_op_fp8_quantize(int in_dtype, int fmt, int R, int C, const void* x, flo
     return gpt2_internal_fail(GPT2_E_INVALID_ARG, "fp8_quantize: scale (16-byte aligned) and workspace needed");
   hipStream_t s = (hipStream_t)stream;
   Fp8Scale* sc = reinterpret_cast<Fp8Scale*>(scale);
-  RC(fp8_compute_scale(in_dtype, (int64_t)R * C, x, fmt, sc, static_cast<float*>(workspace), s));
-  return fp8_quantize(in_dtype, fmt, R, C, x, C, sc, q, qt, s);
+  RC(fp8_amax(in_dtype, (int64_t)R * C, x, static_cast<float*>(workspace), s));
+  return fp8_quantize(in_dtype, fmt, R, C, x, C, static_cast<const float*>(workspace), sc, q, qt, s);
   GPT2_ABI_END_STATUS
 }
 
@@ -1532,7 +1538,7 @@ namespace {
 // codes of x, W (row-major and transposed) and dY (row-major and
 // transposed), then the products' split-K / bias-gradient scratch.
 struct OpFp8Ws {
-  size_t scales, amax, xq, xqt, wq, wqt, dq, dqt, scratch, scratch_bytes, total;
+  size_t scales, amax, xq, xqt, wq, wqt, dq, dqt, colsum, scratch, scratch_bytes, total;
 };
 OpFp8Ws op_fp8_ws(int M, int N, int K) {
   Plan p;
@@ -1545,10 +1551,10 @@ OpFp8Ws op_fp8_ws(int M, int N, int K) {
   w.wqt = p.alloc((size_t)N * K);
   w.dq = p.alloc((size_t)M * N);
   w.dqt = p.alloc((size_t)M * N);
+  w.colsum = p.alloc(fp8_colsum_bytes(M, N));
   w.scratch_bytes = std::max({gemm_workspace_bytes(GPT2_BF16, EPI_WGRAD, N, K, M, true, true, 2),
                               gemm_workspace_bytes(GPT2_BF16, EPI_STORE, M, K, N, true, true, 2),
-                              gemm_workspace_bytes(GPT2_BF16, EPI_STORE, M, N, K, true, true, 1),
-                              bias_grad_workspace_bytes(N)});
+                              gemm_workspace_bytes(GPT2_BF16, EPI_STORE, M, N, K, true, true, 1)});
   w.scratch = p.alloc(w.scratch_bytes);
   w.total = p.total;
   return w;
@@ -1580,10 +1586,10 @@ int gpt2_op_linear_fp8_forward(int M, int N, int K, const void* x, const void* W
   float* amax = reinterpret_cast<float*>(ws + w.amax);
   uint8_t* xq = reinterpret_cast<uint8_t*>(ws + w.xq);
   uint8_t* wq = reinterpret_cast<uint8_t*>(ws + w.wq);
-  RC(fp8_compute_scale(GPT2_BF16, (int64_t)M * K, x, 0, &sc[0], amax, s));
-  RC(fp8_quantize(GPT2_BF16, 0, M, K, x, K, &sc[0], xq, nullptr, s));
-  RC(fp8_compute_scale(GPT2_BF16, (int64_t)N * K, W, 0, &sc[1], amax, s));
-  RC(fp8_quantize(GPT2_BF16, 0, N, K, W, K, &sc[1], wq, nullptr, s));
+  RC(fp8_amax(GPT2_BF16, (int64_t)M * K, x, amax, s));
+  RC(fp8_quantize(GPT2_BF16, 0, M, K, x, K, amax, &sc[0], xq, nullptr, s));
+  RC(fp8_amax(GPT2_BF16, (int64_t)N * K, W, amax, s));
+  RC(fp8_quantize(GPT2_BF16, 0, N, K, W, K, amax, &sc[1], wq, nullptr, s));
   const int epi = gelu_grad ? EPI_BIAS_GELU_D : residual ? EPI_BIAS_RES : b ? EPI_BIAS : EPI_STORE;
   GemmDesc d = linear_fwd_desc(GPT2_BF16, M, N, K, xq, wq, epi, y, b, residual, gelu_grad);
   d.fp8 = 1;
@@ -1609,12 +1615,13 @@ int gpt2_op_linear_fp8_backward(int M, int N, int K, const void* dy, const void*
   float* amax = reinterpret_cast<float*>(ws + w.amax);
   uint8_t* dq = reinterpret_cast<uint8_t*>(ws + w.dq);
   uint8_t* dqt = reinterpret_cast<uint8_t*>(ws + w.dqt);
-  RC(fp8_compute_scale(GPT2_BF16, (int64_t)M * N, dy, 1, &sc[2], amax, s));
-  RC(fp8_quantize(GPT2_BF16, 1, M, N, dy, N, &sc[2], dq, dqt, s));
+  RC(fp8_amax(GPT2_BF16, (int64_t)M * N, dy, amax, s));
+  float* colsum = db ? reinterpret_cast<float*>(ws + w.colsum) : nullptr;
+  RC(fp8_quantize(GPT2_BF16, 1, M, N, dy, N, amax, &sc[2], dq, dqt, s, colsum));
   if (dW) {
     uint8_t* xqt = reinterpret_cast<uint8_t*>(ws + w.xqt);
-    RC(fp8_compute_scale(GPT2_BF16, (int64_t)M * K, x, 0, &sc[0], amax, s));
-    RC(fp8_quantize(GPT2_BF16, 0, M, K, x, K, &sc[0], nullptr, xqt, s));
+    RC(fp8_amax(GPT2_BF16, (int64_t)M * K, x, amax, s));
+    RC(fp8_quantize(GPT2_BF16, 0, M, K, x, K, amax, &sc[0], nullptr, xqt, s));
     GemmDesc d = gdesc(GPT2_BF16);
     d.a_kmajor = d.b_kmajor = true;
     d.M = N; d.N = K; d.K = M;
@@ -1623,14 +1630,12 @@ int gpt2_op_linear_fp8_backward(int M, int N, int K, const void* dy, const void*
     d.workspace = ws + w.scratch; d.workspace_bytes = w.scratch_bytes;
     d.fp8 = 2; d.scale_a = &sc[2].s; d.scale_b = &sc[0].s;
     RC(gemm(d, s));
-    if (db)
-      RC(bias_grad_bf16(M, N, static_cast<const bf16*>(dy), db, accumulate != 0,
-                        reinterpret_cast<float*>(ws + w.scratch), w.scratch_bytes, s));
+    if (db) RC(colsum_reduce(M, N, colsum, db, accumulate != 0, s));
   }
   if (dx) {
     uint8_t* wqt = reinterpret_cast<uint8_t*>(ws + w.wqt);
-    RC(fp8_compute_scale(GPT2_BF16, (int64_t)N * K, W, 0, &sc[1], amax, s));
-    RC(fp8_quantize(GPT2_BF16, 0, N, K, W, K, &sc[1], nullptr, wqt, s));
+    RC(fp8_amax(GPT2_BF16, (int64_t)N * K, W, amax, s));
+    RC(fp8_quantize(GPT2_BF16, 0, N, K, W, K, amax, &sc[1], nullptr, wqt, s));
     GemmDesc d = linear_dx_desc(GPT2_BF16, M, N, K, dq, nullptr, wqt, dx, gelu_grad ? EPI_MUL : EPI_STORE, gelu_grad,
                                 ws + w.scratch, w.scratch_bytes);
     d.fp8 = 2; d.scale_a = &sc[2].s; d.scale_b = &sc[1].s;
