@@ -113,10 +113,13 @@ __global__ __launch_bounds__(kCeThreads) void softmax_xent_kernel(int V, int Vp,
 // chunk NC - 1 checks the row end and the padding.  The label's -dscale is
 // applied afterwards by the thread that holds the label, with a 2-byte store
 // over its chunk.
-template <int NC>
+// AM: also the maximum |dz| of the row (as stored) into the amax slots, for
+// the fp8 quantisation of the dlogits.
+template <int NC, bool AM>
 __global__ __launch_bounds__(kCeThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void softmax_xent_bf16_kernel(int V, int Vp, bf16* __restrict__ logits,
                                                                        const int32_t* __restrict__ labels,
-                                                                       float* __restrict__ losses, float dscale) {
+                                                                       float* __restrict__ losses, float dscale,
+                                                                       float* __restrict__ amax) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   __shared__ float shm[kCeWaves], shs[kCeWaves];
   __shared__ float s_zy;
@@ -223,6 +226,7 @@ __global__ __launch_bounds__(kCeThreads) __attribute__((amdgpu_waves_per_eu(8, 8
   for (int i = 0; i < kCeWaves; ++i) sb += shs[i];
   if (tid == 0) losses[row] = mb + logf(sb) - s_zy;
   const float scale = r * (dscale / sb);
+  uint32_t m16 = 0;   // AM: largest bf16 magnitude written (bits), the label's old entry excluded
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     if (c < L || hasL) {
@@ -234,12 +238,33 @@ __global__ __launch_bounds__(kCeThreads) __attribute__((amdgpu_waves_per_eu(8, 8
         const uint32_t b0 = __builtin_bit_cast(uint16_t, (bf16)g0);
         const uint32_t b1 = __builtin_bit_cast(uint16_t, (bf16)g1);
         o[k] = b0 | (b1 << 16);
+        if constexpr (AM) {
+          const bool lab = tid + kCeThreads * c == ych && k == ((y & 7) >> 1);
+          m16 = max(m16, (lab && !(y & 1)) ? 0u : (b0 & 0x7fffu));
+          m16 = max(m16, (lab && (y & 1)) ? 0u : (b1 & 0x7fffu));
+        }
       }
       __builtin_amdgcn_raw_buffer_store_b128(o, rs, voff, kCeThreads * 16 * c, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  if (owner) z[y] = (bf16)(__builtin_amdgcn_exp2f(fmaf(zy, kLog2eCe, -ml2)) * scale - dscale);
+  if (owner) {
+    const bf16 zl = (bf16)(__builtin_amdgcn_exp2f(fmaf(zy, kLog2eCe, -ml2)) * scale - dscale);
+    z[y] = zl;
+    if constexpr (AM) m16 = max(m16, (uint32_t)__builtin_bit_cast(uint16_t, zl) & 0x7fffu);
+  }
+  if constexpr (AM) {
+    __shared__ float sam[kCeWaves];
+    const float mw = wave_max(__uint_as_float(m16 << 16));
+    if (lane == 0) sam[wv] = mw;
+    __syncthreads();
+    if (tid == 0) {
+      float mb2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < kCeWaves; ++i) mb2 = fmaxf(mb2, sam[i]);
+      amax_atomic_bf16(amax, row, mb2);   // already a bf16 value: rounding leaves it
+    }
+  }
 }
 
 __global__ __launch_bounds__(1024) void sum_scaled_kernel(int n, const float* __restrict__ x, float scale,
@@ -258,22 +283,32 @@ __global__ __launch_bounds__(1024) void sum_scaled_kernel(int n, const float* __
   }
 }
 
+bool bf16_kernel_fits(int V, int Vp) {
+  const int need = (Vp / 8 + kCeThreads - 1) / kCeThreads;
+  return need <= 7 && 6 * 8 * kCeThreads <= V;   // the bf16 kernel's precondition for NC = 7
+}
+
 template <typename T>
-int launch_t(int N, int V, int Vp, void* logits, const int32_t* labels, float* losses, float dscale,
+int launch_t(int N, int V, int Vp, void* logits, const int32_t* labels, float* losses, float dscale, float* amax,
              hipStream_t s) {
   const int nch = Vp / 8;
   const int need = (nch + kCeThreads - 1) / kCeThreads;
   T* L = (T*)logits;
   mark_begin(0, s);
   if constexpr (sizeof(T) == 2) {
-    if (need <= 7 && 6 * 8 * kCeThreads <= V) {   // the bf16 kernel's precondition for NC = 7
-      hipLaunchKernelGGL((softmax_xent_bf16_kernel<7>), dim3(N), dim3(kCeThreads), 0, s, V, Vp, L, labels, losses,
-                         dscale);
+    if (bf16_kernel_fits(V, Vp)) {
+      if (amax)
+        hipLaunchKernelGGL((softmax_xent_bf16_kernel<7, true>), dim3(N), dim3(kCeThreads), 0, s, V, Vp, L, labels,
+                           losses, dscale, amax);
+      else
+        hipLaunchKernelGGL((softmax_xent_bf16_kernel<7, false>), dim3(N), dim3(kCeThreads), 0, s, V, Vp, L, labels,
+                           losses, dscale, amax);
       GPT2_LAUNCH_CHECK();
       mark_end(0, s);
       return 0;
     }
   }
+  if (amax) return gpt2_internal_fail(1, "softmax_xent: the dlogits maximum needs the bf16 full-vocabulary kernel");
   if (need <= 1)
     hipLaunchKernelGGL((softmax_xent_kernel<T, 1>), dim3(N), dim3(kCeThreads), 0, s, V, Vp, L, labels, losses, dscale);
   else if (need <= 2)
@@ -294,13 +329,15 @@ int launch_t(int N, int V, int Vp, void* logits, const int32_t* labels, float* l
 }  // namespace
 
 int softmax_xent(int dtype, int N, int V, int Vp, void* logits, const int32_t* labels, float* losses,
-                 float dscale, hipStream_t stream) {
+                 float dscale, hipStream_t stream, float* amax) {
   if (N < 0 || V <= 0 || Vp < V || Vp % 8 || !logits || !labels || !losses)
     return gpt2_internal_fail(1, "softmax_xent: bad arguments");
   if (N == 0) return 0;
-  return dtype == BF16 ? launch_t<bf16>(N, V, Vp, logits, labels, losses, dscale, stream)
-                       : launch_t<float>(N, V, Vp, logits, labels, losses, dscale, stream);
+  return dtype == BF16 ? launch_t<bf16>(N, V, Vp, logits, labels, losses, dscale, amax, stream)
+                       : launch_t<float>(N, V, Vp, logits, labels, losses, dscale, amax, stream);
 }
+
+bool softmax_xent_has_amax(int dtype, int V, int Vp) { return dtype == BF16 && bf16_kernel_fits(V, Vp); }
 
 int sum_scaled(int n, const float* x, float scale, float* out, hipStream_t stream) {
   if (n < 0 || !x || !out) return gpt2_internal_fail(1, "sum_scaled: bad arguments");

@@ -62,6 +62,24 @@ template <> struct Chunk8<bf16> {
 
 // ---------------------------------------------------------------- reductions
 
+// Producers of a tensor that is quantised to fp8 next leave their maxima in
+// kAmaxWays slots, kAmaxStride floats apart (each slot on a 128-byte line of
+// its own, so atomics on different slots do not queue on one line); the
+// quantisation takes the maximum of the slots.
+constexpr int kAmaxWays = 64;
+constexpr int kAmaxStride = 32;
+
+// slot i % kAmaxWays of `slots` = max(itself, m) for m >= 0 (not NaN): the
+// bit patterns of non-negative floats order like the values, so an integer
+// atomic maximum gives the same result in any order.  m is first rounded to
+// bf16 (rounding is monotonic, so this is the maximum of the rounded values a
+// bf16 tensor holds).
+__device__ __forceinline__ void amax_atomic_bf16(float* slots, int i, float m) {
+  const uint32_t b = __float_as_uint(m);
+  const uint32_t r = ((b + 0x7fffu + ((b >> 16) & 1u)) & 0xffff0000u);   // round to nearest even
+  atomicMax(reinterpret_cast<unsigned int*>(slots + (i % kAmaxWays) * kAmaxStride), r);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -55,10 +55,10 @@ __global__ __launch_bounds__(256) void absmax_partial_kernel(int64_t n, const T*
   if (threadIdx.x == 0) partial[blockIdx.x] = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
 }
 
-__global__ __launch_bounds__(256) void fp8_scale_finalize_kernel(const float* __restrict__ partial, int np, float fmax,
-                                                                 Fp8Scale* __restrict__ out) {
+__global__ __launch_bounds__(256) void fp8_scale_finalize_kernel(const float* __restrict__ partial, int np, int pstride,
+                                                                 float fmax, Fp8Scale* __restrict__ out) {
   float m = 0.f;
-  for (int i = threadIdx.x; i < np; i += 256) m = fmaxf(m, partial[i]);
+  for (int i = threadIdx.x; i < np; i += 256) m = fmaxf(m, partial[(size_t)i * pstride]);
   __shared__ float sh[4];
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = m;
@@ -92,19 +92,21 @@ __device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
 // Grid (ceil(Cc / 64), ceil(R / 64)); Cc % 8 == 0, R % 16 == 0 when qt.
 // With CS, also colsum[blockIdx.y][c] = sum of x[r][c] over the tile's rows
 // (in row order), for the bias gradient.
-// The scale comes from the np per-block maxima of the amax pass: every block
-// takes their maximum (exact, so all agree) and forms inv and s as above;
-// block (0, 0) stores (amax, inv, s) for the products.
+// The scale comes from the np maxima amax_part[i * pstride] (the amax pass's
+// per-block maxima, or a producer's slots): every block takes their maximum
+// (exact, so all agree) and forms inv and s as above; block (0, 0) stores
+// (amax, inv, s) for the products.
 template <typename T, int FMT, bool CS>
 __global__ __launch_bounds__(256) void quantize_kernel(int R, int Cc, const T* __restrict__ x, int64_t ldx,
-                                                       const float* __restrict__ amax_part, int np, float fmax,
+                                                       const float* __restrict__ amax_part, int np, int pstride,
+                                                       float fmax,
                                                        Fp8Scale* __restrict__ sc, uint8_t* __restrict__ qrow,
                                                        uint8_t* __restrict__ qt, float* __restrict__ colsum) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[64][64 + 16];
   __shared__ float ftile[CS ? 64 : 1][CS ? 65 : 1];
   __shared__ float smax[4];
   float am = 0.f;
-  for (int i = threadIdx.x; i < np; i += 256) am = fmaxf(am, amax_part[i]);
+  for (int i = threadIdx.x; i < np; i += 256) am = fmaxf(am, amax_part[(size_t)i * pstride]);
   am = wave_max(am);
   if ((threadIdx.x & 63) == 0) smax[threadIdx.x >> 6] = am;
   __syncthreads();
@@ -201,24 +203,26 @@ int fp8_amax(int dtype_in, int64_t n, const void* x, float* workspace, hipStream
 
 template <typename T, int FMT>
 void launch_quantize(dim3 grid, int R, int Cc, const void* x, int64_t ldx, const float* amax_part, int np,
-                     Fp8Scale* sc, uint8_t* qrow, uint8_t* qt, float* colsum, hipStream_t stream) {
+                     int pstride, Fp8Scale* sc, uint8_t* qrow, uint8_t* qt, float* colsum, hipStream_t stream) {
   const float fmax = FMT == 0 ? 448.0f : 57344.0f;
   if (colsum)
     hipLaunchKernelGGL((quantize_kernel<T, FMT, true>), grid, dim3(256), 0, stream, R, Cc, (const T*)x, ldx, amax_part,
-                       np, fmax, sc, qrow, qt, colsum);
+                       np, pstride, fmax, sc, qrow, qt, colsum);
   else
     hipLaunchKernelGGL((quantize_kernel<T, FMT, false>), grid, dim3(256), 0, stream, R, Cc, (const T*)x, ldx,
-                       amax_part, np, fmax, sc, qrow, qt, colsum);
+                       amax_part, np, pstride, fmax, sc, qrow, qt, colsum);
 }
 
 int fp8_quantize(int dtype_in, int fmt, int R, int Cc, const void* x, int64_t ldx, const float* amax_part,
-                 Fp8Scale* sc, uint8_t* qrow, uint8_t* qt, hipStream_t stream, float* colsum) {
+                 Fp8Scale* sc, uint8_t* qrow, uint8_t* qt, hipStream_t stream, float* colsum, int amax_np) {
   if (R < 0 || Cc < 0 || !x || !amax_part || !sc || (!qrow && !qt) || Cc % 8 || ldx % 8 || (qt && R % 16) ||
       (uintptr_t)x % 16 || (fmt != 0 && fmt != 1))
     return gpt2_internal_fail(1, "fp8_quantize: bad arguments (R=%d, C=%d)", R, Cc);
-  const int np = amax_blocks((int64_t)R * Cc);
+  if (amax_np < 0 || amax_np > kAmaxWays) return gpt2_internal_fail(1, "fp8_quantize: amax_np=%d", amax_np);
+  const int np = amax_np ? amax_np : amax_blocks((int64_t)R * Cc);
+  const int ps = amax_np ? kAmaxStride : 1;
   if (R == 0 || Cc == 0) {   // no tile to store the scale: the one-block form
-    hipLaunchKernelGGL(fp8_scale_finalize_kernel, dim3(1), dim3(256), 0, stream, amax_part, np,
+    hipLaunchKernelGGL(fp8_scale_finalize_kernel, dim3(1), dim3(256), 0, stream, amax_part, np, ps,
                        fmt == 0 ? 448.0f : 57344.0f, sc);
     GPT2_LAUNCH_CHECK();
     return 0;
@@ -226,11 +230,11 @@ int fp8_quantize(int dtype_in, int fmt, int R, int Cc, const void* x, int64_t ld
   dim3 grid((unsigned)ceil_div64(Cc, 64), (unsigned)ceil_div64(R, 64));
   mark_begin(0, stream);
   if (dtype_in == BF16) {
-    if (fmt == 0) launch_quantize<bf16, 0>(grid, R, Cc, x, ldx, amax_part, np, sc, qrow, qt, colsum, stream);
-    else launch_quantize<bf16, 1>(grid, R, Cc, x, ldx, amax_part, np, sc, qrow, qt, colsum, stream);
+    if (fmt == 0) launch_quantize<bf16, 0>(grid, R, Cc, x, ldx, amax_part, np, ps, sc, qrow, qt, colsum, stream);
+    else launch_quantize<bf16, 1>(grid, R, Cc, x, ldx, amax_part, np, ps, sc, qrow, qt, colsum, stream);
   } else {
-    if (fmt == 0) launch_quantize<float, 0>(grid, R, Cc, x, ldx, amax_part, np, sc, qrow, qt, colsum, stream);
-    else launch_quantize<float, 1>(grid, R, Cc, x, ldx, amax_part, np, sc, qrow, qt, colsum, stream);
+    if (fmt == 0) launch_quantize<float, 0>(grid, R, Cc, x, ldx, amax_part, np, ps, sc, qrow, qt, colsum, stream);
+    else launch_quantize<float, 1>(grid, R, Cc, x, ldx, amax_part, np, ps, sc, qrow, qt, colsum, stream);
   }
   GPT2_LAUNCH_CHECK();
   mark_end(0, stream);

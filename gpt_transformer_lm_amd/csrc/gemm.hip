@@ -96,11 +96,12 @@ int gemm(const GemmDesc& d, hipStream_t stream) {
     partial = reinterpret_cast<float*>(d.workspace);
     partial_bias = partial + (size_t)splits * d.M * d.N;
   }
-  EpiArgs e{d.epi, d.M, d.N, d.C, d.ldc, d.bias, d.aux_in, d.ld_aux, d.aux_out, partial, partial_bias};
+  EpiArgs e{d.epi, d.M, d.N, d.C, d.ldc, d.bias, d.aux_in, d.ld_aux, d.aux_out, partial, partial_bias, d.amax};
 
   if (d.K == 0) return gpt2_internal_fail(1, "gemm: K == 0 is not supported");
 
   int rc = 0;
+  if (d.amax && !d.fp8) return gpt2_internal_fail(1, "gemm: the output maximum is taken only by fp8 products");
   if (d.fp8 && (d.dtype != BF16 || !d.a_kmajor || !d.b_kmajor || !d.scale_a || !d.scale_b || d.K % 16 ||
                 d.lda % 16 || d.ldb % 16 || d.fp8 > 2 || (wgrad && d.bias_grad32)))
     return gpt2_internal_fail(1, "gemm(fp8): needs bf16 outputs, k-major A and B, K and row strides multiples of "
@@ -131,6 +132,10 @@ int gemm(const GemmDesc& d, hipStream_t stream) {
     const int64_t x_ext = d.aux_in ? (int64_t)d.M * d.ld_aux * 2 : 0;
     if (x_ext >= (int64_t)kOutOfRange)
       return gpt2_internal_fail(1, "gemm(bf16): epilogue input larger than 4 GiB (%lld bytes)", (long long)x_ext);
+    if (d.amax && (!d.fp8 || split_store || !vec ||
+                   (d.epi != EPI_BIAS_GELU_D && d.epi != EPI_BIAS_RELU2_D && d.epi != EPI_MUL)))
+      return gpt2_internal_fail(1, "gemm: the output maximum is taken only by unsplit fp8 activation epilogues with "
+                                   "16-byte aligned rows");
     MfmaArgs a{d.A, d.lda, d.B, d.ldb, (uint32_t)a_ext, (uint32_t)b_ext, (uint32_t)x_ext, d.M, d.N, d.K,
                pl.k_per_split, vec, e, d.scale_a, d.scale_b};
     const bool bias_grad = wgrad && d.bias_grad32 != nullptr;

@@ -55,6 +55,7 @@ struct EpiArgs {
   void* aux_out;
   float* partial;        // [splits][M][N]
   float* partial_bias;   // [splits][M]
+  float* amax;           // fp8 activation epilogues: max |C| into the amax slots (amax_atomic_bf16), or NULL
 };
 
 struct MfmaArgs {
@@ -449,6 +450,10 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   // fp8: the sums of products of the quantised operands times s_a s_b
   float sc = 1.0f;
   if constexpr (F8) sc = p.scale_a[0] * p.scale_b[0];
+  // fp8 activation epilogues: the largest |C| this thread stores (its fp8
+  // quantisation comes next); the host asks for it only with the vector epilogue
+  constexpr bool AMX = F8 && (EPI == EPI_BIAS_GELU_D || EPI == EPI_BIAS_RELU2_D || EPI == EPI_MUL);
+  float cmax = 0.f;
 
   for (int it = 0; u < u_end; u += u_step, ++it) {
   const bool first = it == 0;
@@ -753,6 +758,10 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
                 }
               }
               epilogue_vec8_final<EPI>(p.e, grow, gcol, v, z);
+              if constexpr (AMX) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) cmax = fmaxf(cmax, fabsf(v[e]));
+              }
             } else {
 #pragma unroll
               for (int e = 0; e < 8; ++e)
@@ -784,6 +793,12 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
     }
   }
   }   // units
+  if constexpr (AMX) {
+    if (p.e.amax) {   // uniform
+      cmax = wave_max(cmax);
+      if (lane == 0) amax_atomic_bf16(p.e.amax, blockIdx.x * S::WAVES + wave, cmax);   // rounded as C was
+    }
+  }
 }
 
 // ---------------------------------------------------------------- fp32 SIMT

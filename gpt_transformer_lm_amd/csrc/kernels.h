@@ -69,6 +69,11 @@ struct GemmDesc {
   int fp8;
   const float* scale_a;
   const float* scale_b;
+  // fp8 products with epilogue BIAS_GELU_D, BIAS_RELU2_D or MUL (unsplit, C
+  // rows 16-byte aligned): also the maximum |C| (as stored) into the slots
+  // amax (kAmaxWays x kAmaxStride floats, zero beforehand; amax_atomic_bf16),
+  // for the quantisation of C that follows.  NULL: not taken.
+  float* amax;
 };
 
 // Kernel configuration gemm() launches for a descriptor (host-only): block
@@ -86,17 +91,22 @@ size_t gemm_workspace_bytes(int dtype, int epi, int M, int N, int K, bool a_kmaj
 int gemm(const GemmDesc& d, hipStream_t stream);
 
 // ------------------------------------------------------------------ LayerNorm
-// y = (x - mean) * rstd * w + b per row of C; mean, rstd fp32 [N].
+// y = (x - mean) * rstd * w + b per row of C; mean, rstd fp32 [N].  With
+// amax (bf16 only; kAmaxWays x kAmaxStride floats, zero beforehand) also the
+// maximum |y| (as stored) into those slots (amax_atomic_bf16), for
+// fp8_quantize.
 int layernorm_forward(int dtype, int N, int C, const void* x, const void* w, const void* b,
-                      void* y, float* mean, float* rstd, hipStream_t stream);
+                      void* y, float* mean, float* rstd, hipStream_t stream, float* amax = nullptr);
 // dres[N, C] (fp32) += dx; dres_copy (dtype, optional) = new dres;
 // dw, db (fp32 [C]) = (or +=, if accumulate) column sums.  If dres_overwrite,
-// dres is written (= dx) instead of accumulated.
+// dres is written (= dx) instead of accumulated.  With amax (bf16 with
+// dres_copy only) also the maximum |dres_copy| into those slots, as in the
+// forward.
 size_t layernorm_backward_workspace_bytes(int N, int C);
 int layernorm_backward(int dtype, int N, int C, const void* dy, const void* x, const void* w,
                        const float* mean, const float* rstd, float* dres, bool dres_overwrite,
                        void* dres_copy, float* dw, float* db, bool accumulate, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream);
+                       size_t workspace_bytes, hipStream_t stream, float* amax = nullptr);
 
 // ------------------------------------------------------------------ attention
 // qkv [B, T, 3C] -> out [B, T, C], lse [B, H, T] fp32.
@@ -132,9 +142,12 @@ int fp8_amax(int dtype_in, int64_t n, const void* x, float* workspace, hipStream
 // row-major into qrow [R, Cc] and / or transposed into qt [Cc, R] (either may
 // be NULL).  Cc % 8 == 0; R % 16 == 0 when qt.  With colsum
 // (fp8_colsum_bytes(R, Cc), device) also the per-64-row-block column sums of
-// x that colsum_reduce turns into a bias gradient.
+// x that colsum_reduce turns into a bias gradient.  amax_np > 0 (at most
+// kAmaxWays): amax_part holds that many slots, kAmaxStride floats apart, left
+// by a producer kernel (amax_atomic_bf16), instead of fp8_amax's maxima.
 int fp8_quantize(int dtype_in, int fmt, int R, int Cc, const void* x, int64_t ldx, const float* amax_part,
-                 Fp8Scale* sc, uint8_t* qrow, uint8_t* qt, hipStream_t stream, float* colsum = nullptr);
+                 Fp8Scale* sc, uint8_t* qrow, uint8_t* qt, hipStream_t stream, float* colsum = nullptr,
+                 int amax_np = 0);
 size_t fp8_colsum_bytes(int R, int N);
 // db[n] (+)= sum of the column sums left by fp8_quantize for R rows, in a
 // fixed order.
@@ -155,9 +168,12 @@ int qk_transform_backward(int dtype, int BT, int T, int H, int hd, const void* q
 // ------------------------------------------------------------------ classifier
 // In place over logits [N, Vp] (row stride Vp): columns >= V are masked.
 // losses[i] = logsumexp_{j<V} z_ij - z_i,y_i;  z_ij <- (softmax_ij - [j==y_i]) * dscale
-// for j < V and 0 for j >= V.
+// for j < V and 0 for j >= V.  With amax (kAmaxWays x kAmaxStride floats,
+// zero beforehand; bf16 only, and only where softmax_xent_has_amax holds), the
+// maximum |z_ij| written is max-ed into those slots (amax_atomic_bf16).
 int softmax_xent(int dtype, int N, int V, int Vp, void* logits, const int32_t* labels,
-                 float* losses, float dscale, hipStream_t stream);
+                 float* losses, float dscale, hipStream_t stream, float* amax = nullptr);
+bool softmax_xent_has_amax(int dtype, int V, int Vp);
 // out[0] = sum_i x[i] * scale  (fixed order; single block).
 int sum_scaled(int n, const float* x, float scale, float* out, hipStream_t stream);
 

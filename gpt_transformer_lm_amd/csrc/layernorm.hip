@@ -22,14 +22,20 @@ namespace {
 
 constexpr float kLnEps = 1e-5f;
 
-template <typename T, int NCH>
+// AM: also the maximum |y| over the block's rows into the amax slots (the fp8
+// quantisation of y reads them instead of taking a pass of its own).  Waves
+// past the last row compute on a copy of it and store nothing, so every wave
+// reaches the block's barrier.
+template <typename T, int NCH, bool AM>
 __global__ __launch_bounds__(256) void ln_fwd_kernel(int N, int C, const T* __restrict__ x,
                                                      const T* __restrict__ w, const T* __restrict__ b,
                                                      T* __restrict__ y, float* __restrict__ mean,
-                                                     float* __restrict__ rstd) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+                                                     float* __restrict__ rstd, float* __restrict__ amax) {
+  const int row_ = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (row >= N) return;
+  if (!AM && row_ >= N) return;
+  const bool live = row_ < N;
+  const int row = live ? row_ : N - 1;
   const int nch = C / 8;
   const T* xr = x + (size_t)row * C;
   float v[NCH][8], wv[NCH][8], bv[NCH][8];
@@ -69,6 +75,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int N, int C, const T* __re
   const float var = wave_sum(s2) / (float)C;
   const float rs = 1.0f / sqrtf(var + kLnEps);
   T* yr = y + (size_t)row * C;
+  float am = 0.f;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     int ch = lane + 64 * c;
@@ -76,12 +83,24 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int N, int C, const T* __re
       float o[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = (v[c][e] - mu) * rs * wv[c][e] + bv[c][e];
-      Chunk8<T>::store(yr + ch * 8, o);
+      if (live) Chunk8<T>::store(yr + ch * 8, o);
+      if constexpr (AM) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(o[e]));
+      }
     }
   }
-  if (lane == 0) {
+  if (live && lane == 0) {
     mean[row] = mu;
     rstd[row] = rs;
+  }
+  if constexpr (AM) {
+    __shared__ float wm[4];
+    am = wave_max(live ? am : 0.f);
+    if (lane == 0) wm[threadIdx.x >> 6] = am;
+    __syncthreads();
+    if (threadIdx.x == 0)
+      amax_atomic_bf16(amax, blockIdx.x, fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3])));
   }
 }
 
@@ -89,14 +108,16 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int N, int C, const T* __re
 // per row, so no lane idles (a whole wave would leave a third of its lanes
 // idle in the second chunk), 8 rows per 256-thread block.  The reductions
 // use xor distances below 32, so each half-wave reduces its own row.
-template <typename T, int NCH>
+template <typename T, int NCH, bool AM>
 __global__ __launch_bounds__(256) void ln_fwd_half_kernel(int N, int C, const T* __restrict__ x,
                                                           const T* __restrict__ w, const T* __restrict__ b,
                                                           T* __restrict__ y, float* __restrict__ mean,
-                                                          float* __restrict__ rstd) {
-  const int row = blockIdx.x * 8 + (threadIdx.x >> 5);
+                                                          float* __restrict__ rstd, float* __restrict__ amax) {
+  const int row_ = blockIdx.x * 8 + (threadIdx.x >> 5);
   const int l = threadIdx.x & 31;
-  if (row >= N) return;                     // whole half-waves leave together
+  if (!AM && row_ >= N) return;             // whole half-waves leave together
+  const bool live = row_ < N;               // (AM: every wave reaches the barrier)
+  const int row = live ? row_ : N - 1;
   const T* xr = x + (size_t)row * C;
   float v[NCH][8], wv[NCH][8], bv[NCH][8];
 #pragma unroll
@@ -127,23 +148,37 @@ __global__ __launch_bounds__(256) void ln_fwd_half_kernel(int N, int C, const T*
     }
   const float rs = 1.0f / sqrtf(half_sum(s2) / (float)C + kLnEps);
   T* yr = y + (size_t)row * C;
+  float am = 0.f;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = (v[c][e] - mu) * rs * wv[c][e] + bv[c][e];
-    Chunk8<T>::store(yr + (l + 32 * c) * 8, o);
+    if (live) Chunk8<T>::store(yr + (l + 32 * c) * 8, o);
+    if constexpr (AM) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(o[e]));
+    }
   }
-  if (l == 0) {
+  if (live && l == 0) {
     mean[row] = mu;
     rstd[row] = rs;
+  }
+  if constexpr (AM) {
+    __shared__ float wm[4];
+    am = wave_max(live ? am : 0.f);   // the wave's two rows
+    if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = am;
+    __syncthreads();
+    if (threadIdx.x == 0)
+      amax_atomic_bf16(amax, blockIdx.x, fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3])));
   }
 }
 
 // WPB waves per block (1024 threads for C <= 1024, fewer for wider rows so
 // that the row cache fits the registers); each block writes one partial row
 // of dw and db.
-template <typename T, int NCH, int WPB>
+// AM: also the maximum |dres_copy| over the block's rows into the amax slots.
+template <typename T, int NCH, int WPB, bool AM>
 __global__ __launch_bounds__(WPB * 64) void ln_bwd_kernel(int N, int C, const T* __restrict__ dy,
                                                      const T* __restrict__ x, const T* __restrict__ w,
                                                      const float* __restrict__ mean,
@@ -151,7 +186,7 @@ __global__ __launch_bounds__(WPB * 64) void ln_bwd_kernel(int N, int C, const T*
                                                      float* __restrict__ dres, bool dres_overwrite,
                                                      T* __restrict__ dres_copy,
                                                      float* __restrict__ part_dw,
-                                                     float* __restrict__ part_db) {
+                                                     float* __restrict__ part_db, float* __restrict__ amax) {
   const int wave_id = blockIdx.x * WPB + (threadIdx.x >> 6);
   const int nwaves = gridDim.x * WPB;
   const int lane = threadIdx.x & 63;
@@ -165,6 +200,7 @@ __global__ __launch_bounds__(WPB * 64) void ln_bwd_kernel(int N, int C, const T*
     for (int e = 0; e < 8; ++e) { dwa[c][e] = 0.f; dba[c][e] = 0.f; wv[c][e] = 0.f; }
     if (ch < nch) Chunk8<T>::load(w + ch * 8, wv[c]);
   }
+  float am = 0.f;   // AM: over this wave's rows
   for (int row = wave_id; row < N; row += nwaves) {
     const float mu = mean[row], rs = rstd[row];
     const T* dyr = dy + (size_t)row * C;
@@ -208,12 +244,21 @@ __global__ __launch_bounds__(WPB * 64) void ln_bwd_kernel(int N, int C, const T*
           o[e] += rs * (dyv[c][e] * wv[c][e] - mg - xh[c][e] * mgx);
         Chunk8<float>::store(dr + ch * 8, o);
         if (dres_copy) Chunk8<T>::store(dres_copy + (size_t)row * C + ch * 8, o);
+        if constexpr (AM) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(o[e]));
+        }
       }
     }
   }
   // reduce the block's waves in LDS, in wave order: one partial row per block (dw, then db)
   extern __shared__ float red[];   // [WPB][C]
   const int wi = threadIdx.x >> 6;
+  __shared__ float wm[AM ? WPB : 1];
+  if constexpr (AM) {
+    am = wave_max(am);
+    if (lane == 0) wm[wi] = am;
+  }
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     float(*acc)[8] = pass == 0 ? dwa : dba;
@@ -228,6 +273,14 @@ __global__ __launch_bounds__(WPB * 64) void ln_bwd_kernel(int N, int C, const T*
       }
     }
     __syncthreads();
+    if constexpr (AM) {
+      if (pass == 0 && threadIdx.x == 0) {
+        float mb = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < WPB; ++w2) mb = fmaxf(mb, wm[w2]);
+        amax_atomic_bf16(amax, blockIdx.x, mb);
+      }
+    }
     for (int i = threadIdx.x; i < C; i += blockDim.x) {
       float t = 0.f;
 #pragma unroll
@@ -296,8 +349,8 @@ int bwd_blocks(int N, int C) {
   return (int)std::min<int64_t>(4096 / wpb, ((int64_t)N + wpb - 1) / wpb);
 }
 
-template <typename T>
-int fwd_t(int N, int C, const void* x, const void* w, const void* b, void* y, float* mean, float* rstd,
+template <typename T, bool AM>
+int fwd_t(int N, int C, const void* x, const void* w, const void* b, void* y, float* mean, float* rstd, float* amax,
           hipStream_t s) {
   dim3 grid((unsigned)ceil_div64(N, 4)), block(256);
   const T* X = (const T*)x;
@@ -306,17 +359,17 @@ int fwd_t(int N, int C, const void* x, const void* w, const void* b, void* y, fl
   T* Y = (T*)y;
   mark_begin(0, s);
   if (C == 32 * 8 * 3) {
-    hipLaunchKernelGGL((ln_fwd_half_kernel<T, 3>), dim3((unsigned)ceil_div64(N, 8)), block, 0, s, N, C, X, W, Bb, Y,
-                       mean, rstd);
+    hipLaunchKernelGGL((ln_fwd_half_kernel<T, 3, AM>), dim3((unsigned)ceil_div64(N, 8)), block, 0, s, N, C, X, W, Bb,
+                       Y, mean, rstd, amax);
     GPT2_LAUNCH_CHECK();
     mark_end(0, s);
     return 0;
   }
   switch (nch_for(C)) {
-    case 1: hipLaunchKernelGGL((ln_fwd_kernel<T, 1>), grid, block, 0, s, N, C, X, W, Bb, Y, mean, rstd); break;
-    case 2: hipLaunchKernelGGL((ln_fwd_kernel<T, 2>), grid, block, 0, s, N, C, X, W, Bb, Y, mean, rstd); break;
-    case 4: hipLaunchKernelGGL((ln_fwd_kernel<T, 4>), grid, block, 0, s, N, C, X, W, Bb, Y, mean, rstd); break;
-    case 8: hipLaunchKernelGGL((ln_fwd_kernel<T, 8>), grid, block, 0, s, N, C, X, W, Bb, Y, mean, rstd); break;
+    case 1: hipLaunchKernelGGL((ln_fwd_kernel<T, 1, AM>), grid, block, 0, s, N, C, X, W, Bb, Y, mean, rstd, amax); break;
+    case 2: hipLaunchKernelGGL((ln_fwd_kernel<T, 2, AM>), grid, block, 0, s, N, C, X, W, Bb, Y, mean, rstd, amax); break;
+    case 4: hipLaunchKernelGGL((ln_fwd_kernel<T, 4, AM>), grid, block, 0, s, N, C, X, W, Bb, Y, mean, rstd, amax); break;
+    case 8: hipLaunchKernelGGL((ln_fwd_kernel<T, 8, AM>), grid, block, 0, s, N, C, X, W, Bb, Y, mean, rstd, amax); break;
     default: return gpt2_internal_fail(1, "layernorm: C=%d unsupported", C);
   }
   GPT2_LAUNCH_CHECK();
@@ -324,9 +377,9 @@ int fwd_t(int N, int C, const void* x, const void* w, const void* b, void* y, fl
   return 0;
 }
 
-template <typename T>
+template <typename T, bool AM>
 int bwd_t(int N, int C, const void* dy, const void* x, const void* w, const float* mean,
-          const float* rstd, float* dres, bool ovw, void* dres_copy, float* pdw, float* pdb,
+          const float* rstd, float* dres, bool ovw, void* dres_copy, float* pdw, float* pdb, float* amax,
           hipStream_t s) {
   const int wpb = bwd_wpb(C);
   dim3 grid((unsigned)bwd_blocks(N, C)), block(wpb * 64);
@@ -337,10 +390,10 @@ int bwd_t(int N, int C, const void* dy, const void* x, const void* w, const floa
   T* DC = (T*)dres_copy;
   mark_begin(0, s);
   switch (nch_for(C)) {
-    case 1: hipLaunchKernelGGL((ln_bwd_kernel<T, 1, 16>), grid, block, lds, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
-    case 2: hipLaunchKernelGGL((ln_bwd_kernel<T, 2, 16>), grid, block, lds, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
-    case 4: hipLaunchKernelGGL((ln_bwd_kernel<T, 4, 8>), grid, block, lds, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
-    case 8: hipLaunchKernelGGL((ln_bwd_kernel<T, 8, 4>), grid, block, lds, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb); break;
+    case 1: hipLaunchKernelGGL((ln_bwd_kernel<T, 1, 16, AM>), grid, block, lds, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb, amax); break;
+    case 2: hipLaunchKernelGGL((ln_bwd_kernel<T, 2, 16, AM>), grid, block, lds, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb, amax); break;
+    case 4: hipLaunchKernelGGL((ln_bwd_kernel<T, 4, 8, AM>), grid, block, lds, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb, amax); break;
+    case 8: hipLaunchKernelGGL((ln_bwd_kernel<T, 8, 4, AM>), grid, block, lds, s, N, C, DY, X, W, mean, rstd, dres, ovw, DC, pdw, pdb, amax); break;
     default: return gpt2_internal_fail(1, "layernorm: C=%d unsupported", C);
   }
   GPT2_LAUNCH_CHECK();
@@ -351,12 +404,13 @@ int bwd_t(int N, int C, const void* dy, const void* x, const void* w, const floa
 }  // namespace
 
 int layernorm_forward(int dtype, int N, int C, const void* x, const void* w, const void* b, void* y,
-                      float* mean, float* rstd, hipStream_t stream) {
-  if (N < 0 || C <= 0 || C % 8 || !x || !w || !b || !y || !mean || !rstd)
+                      float* mean, float* rstd, hipStream_t stream, float* amax) {
+  if (N < 0 || C <= 0 || C % 8 || !x || !w || !b || !y || !mean || !rstd || (amax && dtype != BF16))
     return gpt2_internal_fail(1, "layernorm_forward: bad arguments");
   if (N == 0) return 0;
-  return dtype == BF16 ? fwd_t<bf16>(N, C, x, w, b, y, mean, rstd, stream)
-                       : fwd_t<float>(N, C, x, w, b, y, mean, rstd, stream);
+  if (amax) return fwd_t<bf16, true>(N, C, x, w, b, y, mean, rstd, amax, stream);
+  return dtype == BF16 ? fwd_t<bf16, false>(N, C, x, w, b, y, mean, rstd, nullptr, stream)
+                       : fwd_t<float, false>(N, C, x, w, b, y, mean, rstd, nullptr, stream);
 }
 
 size_t layernorm_backward_workspace_bytes(int N, int C) {
@@ -366,8 +420,9 @@ size_t layernorm_backward_workspace_bytes(int N, int C) {
 int layernorm_backward(int dtype, int N, int C, const void* dy, const void* x, const void* w,
                        const float* mean, const float* rstd, float* dres, bool dres_overwrite,
                        void* dres_copy, float* dw, float* db, bool accumulate, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream) {
-  if (N < 0 || C <= 0 || C % 8 || !dy || !x || !w || !mean || !rstd || !dres || !dw || !db)
+                       size_t workspace_bytes, hipStream_t stream, float* amax) {
+  if (N < 0 || C <= 0 || C % 8 || !dy || !x || !w || !mean || !rstd || !dres || !dw || !db ||
+      (amax && (dtype != BF16 || !dres_copy)))
     return gpt2_internal_fail(1, "layernorm_backward: bad arguments");
   if (N == 0) return 0;
   size_t need = layernorm_backward_workspace_bytes(N, C);
@@ -376,8 +431,11 @@ int layernorm_backward(int dtype, int N, int C, const void* dy, const void* x, c
   const int P = bwd_blocks(N, C);
   float* pdw = (float*)workspace;
   float* pdb = pdw + (size_t)P * C;
-  int rc = dtype == BF16 ? bwd_t<bf16>(N, C, dy, x, w, mean, rstd, dres, dres_overwrite, dres_copy, pdw, pdb, stream)
-                         : bwd_t<float>(N, C, dy, x, w, mean, rstd, dres, dres_overwrite, dres_copy, pdw, pdb, stream);
+  int rc = amax ? bwd_t<bf16, true>(N, C, dy, x, w, mean, rstd, dres, dres_overwrite, dres_copy, pdw, pdb, amax, stream)
+           : dtype == BF16
+               ? bwd_t<bf16, false>(N, C, dy, x, w, mean, rstd, dres, dres_overwrite, dres_copy, pdw, pdb, nullptr, stream)
+               : bwd_t<float, false>(N, C, dy, x, w, mean, rstd, dres, dres_overwrite, dres_copy, pdw, pdb, nullptr,
+                                     stream);
   if (rc) return rc;
   hipLaunchKernelGGL(column_reduce_kernel, dim3((unsigned)ceil_div64(2 * (int64_t)C, 16)), dim3(256), 0, stream,
                      pdw, pdb, P, C, dw, db, accumulate);

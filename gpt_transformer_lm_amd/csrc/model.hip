@@ -244,8 +244,9 @@ struct Layout {
   size_t rope_cs;                        // rotary embedding cos / sin table [maxT][hd/2] (0 if unused)
   // fp8 mode (0 otherwise): weight codes per parameter tensor (row-major and
   // transposed, all layers), lnf codes, the current output gradient's codes,
-  // per-tensor scales, absmax partials
-  size_t wq[16], wqt[16], lnf_q, lnf_qt, dq, dqt, fp8_scales, fp8_amax, fp8_colsum;
+  // per-tensor scales, absmax partials, the maxima producer kernels leave
+  // (kAmaxWays slots, kAmaxStride floats apart, per scale slot)
+  size_t wq[16], wqt[16], lnf_q, lnf_qt, dq, dqt, fp8_scales, fp8_amax, fp8_colsum, fp8_slot_max;
   size_t scratch_bytes;
   size_t total;
 };
@@ -343,7 +344,7 @@ void make_layout(const gpt2_config& c, Layout* lo) {
                     ? p.alloc((size_t)c.max_seq_len * (c.channels / c.num_heads / 2) * sizeof(float2))
                     : 0;
   for (int i = 0; i < 16; ++i) lo->wq[i] = lo->wqt[i] = 0;
-  lo->lnf_q = lo->lnf_qt = lo->dq = lo->dqt = lo->fp8_scales = lo->fp8_amax = lo->fp8_colsum = 0;
+  lo->lnf_q = lo->lnf_qt = lo->dq = lo->dqt = lo->fp8_scales = lo->fp8_amax = lo->fp8_colsum = lo->fp8_slot_max = 0;
   if (c.dtype == GPT2_BF16_FP8) {
     for (int i : kFp8Weights) {
       const int64_t* sh = lo->pt.shape[i];
@@ -358,6 +359,7 @@ void make_layout(const gpt2_config& c, Layout* lo) {
     lo->fp8_scales = p.alloc((size_t)fp8_slots((int)L) * sizeof(Fp8Scale));
     lo->fp8_amax = p.alloc(fp8_scale_workspace_bytes());
     lo->fp8_colsum = p.alloc(fp8_colsum_bytes((int)BT, 4 * C));
+    lo->fp8_slot_max = p.alloc((size_t)fp8_slots((int)L) * kAmaxWays * kAmaxStride * sizeof(float));
   }
   lo->scratch_bytes = scratch_need(c);
   lo->scratch = p.alloc(lo->scratch_bytes);
@@ -441,6 +443,11 @@ struct gpt2_model {
   const float2* rope_cs() { return rope() ? at<float2>(lo.rope_cs) : nullptr; }
   // fp8 mode: scale slot, and the weight codes of tensor i, layer l
   Fp8Scale* fscale(int slot) { return at<Fp8Scale>(lo.fp8_scales) + slot; }
+  // the maxima a producer kernel leaves for the quantisation into `slot`
+  // (null outside fp8 mode)
+  float* slot_max(int slot) {
+    return fp8() ? at<float>(lo.fp8_slot_max) + (size_t)slot * kAmaxWays * kAmaxStride : nullptr;
+  }
   int64_t wq_per_layer(int i) const {
     const int64_t* sh = lo.pt.shape[i];
     return lo.pt.ndim[i] == 3 ? sh[1] * sh[2] : 0;
@@ -566,17 +573,19 @@ GemmDesc dw_desc(gpt2_model* m, int M, int N, int K, const void* dy, const void*
 // Per-tensor scale of x [R, Cc] (bf16 or fp32) into `slot`, then its codes
 // row-major (q) and / or transposed (qt).  fmt 0: E4M3, 1: E5M2.
 // colsum: also leave the column sums of x (for a bias gradient) in the
-// arena's column-sum buffer.
+// arena's column-sum buffer.  produced: the kernel that wrote x also left its
+// maximum in slot_max(slot) (zeroed at the start of the forward), so no pass
+// of its own takes it.
 int fp8_quant(gpt2_model* m, int dtype_in, const void* x, int R, int Cc, int fmt, int slot, uint8_t* q, uint8_t* qt,
-              bool colsum = false) {
+              bool colsum = false, bool produced = false) {
   if (m->dry()) return 0;
   Fp8Scale* sc = m->fscale(slot);
-  float* amax = m->at<float>(m->lo.fp8_amax);
-  RC(fp8_amax(dtype_in, (int64_t)R * Cc, x, amax, m->stream));
+  float* amax = produced ? m->slot_max(slot) : m->at<float>(m->lo.fp8_amax);
+  if (!produced) RC(fp8_amax(dtype_in, (int64_t)R * Cc, x, amax, m->stream));
   const double in_b = (double)R * Cc * (dtype_in == GPT2_BF16 ? 2 : 4);
   return timed(m, S_FP8_QUANT, 0.0, in_b + (double)R * Cc * ((q ? 1 : 0) + (qt ? 1 : 0)), [&] {
     return fp8_quantize(dtype_in, fmt, R, Cc, x, Cc, amax, sc, q, qt, m->stream,
-                        colsum ? m->at<float>(m->lo.fp8_colsum) : nullptr);
+                        colsum ? m->at<float>(m->lo.fp8_colsum) : nullptr, produced ? kAmaxWays : 0);
   });
 }
 
@@ -638,6 +647,8 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets, f
     m->side_pending = false;
   }
   if (!m->dry()) RC(copy_i32(BT, tokens, tok, s));
+  if (m->fp8() && !m->dry())   // maxima of this forward and the backward after it
+    RC(fill_f32((int64_t)fp8_slots(L) * kAmaxWays * kAmaxStride, m->slot_max(0), 0.0f, s));
   if (targets && !m->dry()) {
     // the key sort of the encoder backward runs beside the forward
     GPT2_HIP_CHECK(hipEventRecord(m->ev_fork, s));
@@ -661,14 +672,15 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets, f
     void* x = m->at<char>(lo.resid[l]);
     RC(timed(m, S_LN_FWD, 0.0, ln_fwd_bytes, [&] {
       return layernorm_forward(dt, BT, C, x, m->lparam(2, l), m->lparam(3, l), m->at<char>(o.ln1),
-                               m->at<float>(o.ln1_mean), m->at<float>(o.ln1_rstd), s);
+                               m->at<float>(o.ln1_mean), m->at<float>(o.ln1_rstd), s,
+                               m->slot_max(fp8_slot(L, Q_ACT, 0, l)));
     }));
     {
       GemmDesc d = fwd_desc(m, BT, 3 * C, C, m->at<char>(o.ln1), m->lparam(4, l), EPI_BIAS, m->at<char>(o.qkv),
                             m->lparam(5, l), nullptr, nullptr);
       if (m->fp8()) {
         RC(fp8_quant(m, GPT2_BF16, m->at<char>(o.ln1), BT, C, 0, fp8_slot(L, Q_ACT, 0, l), m->at<uint8_t>(o.ln1_q),
-                     m->at<uint8_t>(o.ln1_qt)));
+                     m->at<uint8_t>(o.ln1_qt), false, true));
         d = fp8_fwd(m, d, m->at<uint8_t>(o.ln1_q), fp8_slot(L, Q_ACT, 0, l), m->wq(4, l), fp8_slot(L, Q_WEIGHT, 1, l));
       }
       RC(run_gemm(m, S_QKV, d));
@@ -685,7 +697,8 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets, f
                                        m->at<char>(o.h), m->lparam(7, l), x, nullptr)));
     RC(timed(m, S_LN_FWD, 0.0, ln_fwd_bytes, [&] {
       return layernorm_forward(dt, BT, C, m->at<char>(o.h), m->lparam(8, l), m->lparam(9, l), m->at<char>(o.ln2),
-                               m->at<float>(o.ln2_mean), m->at<float>(o.ln2_rstd), s);
+                               m->at<float>(o.ln2_mean), m->at<float>(o.ln2_rstd), s,
+                               m->slot_max(fp8_slot(L, Q_ACT, 1, l)));
     }));
     // g = GELU(u) for the fc-proj product, and GELU'(u) kept for the backward
     {
@@ -694,9 +707,10 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets, f
                             nullptr, m->at<char>(o.u));
       if (m->fp8()) {
         RC(fp8_quant(m, GPT2_BF16, m->at<char>(o.ln2), BT, C, 0, fp8_slot(L, Q_ACT, 1, l), m->at<uint8_t>(o.ln2_q),
-                     m->at<uint8_t>(o.ln2_qt)));
+                     m->at<uint8_t>(o.ln2_qt), false, true));
         d = fp8_fwd(m, d, m->at<uint8_t>(o.ln2_q), fp8_slot(L, Q_ACT, 1, l), m->wq(10, l),
                     fp8_slot(L, Q_WEIGHT, 2, l));
+        d.amax = m->slot_max(fp8_slot(L, Q_ACT, 2, l));   // g's maximum, for its quantisation below
       }
       RC(run_gemm(m, S_FC, d));
     }
@@ -705,7 +719,7 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets, f
                             m->at<char>(lo.resid[l + 1]), m->lparam(13, l), m->at<char>(o.h), nullptr);
       if (m->fp8()) {
         RC(fp8_quant(m, GPT2_BF16, m->at<char>(o.g), BT, 4 * C, 0, fp8_slot(L, Q_ACT, 2, l), m->at<uint8_t>(o.g_q),
-                     m->at<uint8_t>(o.g_qt)));
+                     m->at<uint8_t>(o.g_qt), false, true));
         d = fp8_fwd(m, d, m->at<uint8_t>(o.g_q), fp8_slot(L, Q_ACT, 2, l), m->wq(12, l),
                     fp8_slot(L, Q_WEIGHT, 3, l));
       }
@@ -714,14 +728,15 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets, f
   }
   RC(timed(m, S_LN_FWD, 0.0, ln_fwd_bytes, [&] {
     return layernorm_forward(dt, BT, C, m->at<char>(lo.resid[c.num_layers]), m->param(14), m->param(15),
-                             m->at<char>(lo.lnf), m->at<float>(lo.lnf_mean), m->at<float>(lo.lnf_rstd), s);
+                             m->at<char>(lo.lnf), m->at<float>(lo.lnf_mean), m->at<float>(lo.lnf_rstd), s,
+                             m->slot_max(fp8_slot(L, Q_ACT, 3, 0)));
   }));
   {
     GemmDesc d = fwd_desc(m, BT, Vp, C, m->at<char>(lo.lnf), m->param(0), EPI_STORE, m->at<char>(lo.logits), nullptr,
                           nullptr, nullptr);
     if (m->fp8()) {
       RC(fp8_quant(m, GPT2_BF16, m->at<char>(lo.lnf), BT, C, 0, fp8_slot(L, Q_ACT, 3, 0), m->at<uint8_t>(lo.lnf_q),
-                   m->at<uint8_t>(lo.lnf_qt)));
+                   m->at<uint8_t>(lo.lnf_qt), false, true));
       d = fp8_fwd(m, d, m->at<uint8_t>(lo.lnf_q), fp8_slot(L, Q_ACT, 3, 0), m->wq(0, 0), fp8_slot(L, Q_WEIGHT, 0, 0));
     }
     RC(run_gemm(m, S_LOGITS, d));
@@ -729,7 +744,7 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets, f
   if (targets) {
     RC(timed(m, S_XENT, 0.0, 2.0 * BT * (double)Vp * es + BT * 8.0, [&] {
       return softmax_xent(dt, BT, V, Vp, m->at<char>(lo.logits), targets, m->at<float>(lo.losses), loss_scale / BT,
-                          s);
+                          s, softmax_xent_has_amax(dt, V, Vp) ? m->slot_max(fp8_slot(L, Q_GRAD, 3, 0)) : nullptr);
     }));
     if (!m->dry()) RC(sum_scaled(BT, m->at<float>(lo.losses), 1.0f / BT, m->at<float>(lo.mean_loss), s));
     m->have_dlogits = true;
@@ -767,7 +782,7 @@ int backward_impl(gpt2_model* m, bool acc) {
   // classifier: d_lnf = dz wte;  d_wte = dz^T lnf (overwrite; padded rows get exactly 0)
   if (m->fp8()) {
     const int gs = fp8_slot(L, Q_GRAD, 3, 0);
-    RC(fp8_quant(m, GPT2_BF16, logits, BT, Vp, 1, gs, dq, dqt));
+    RC(fp8_quant(m, GPT2_BF16, logits, BT, Vp, 1, gs, dq, dqt, false, softmax_xent_has_amax(dt, c.vocab_size, Vp)));
     RC(run_gemm(m, S_CLS_DX, fp8_dx(m, BT, Vp, C, dq, gs, m->wqt(0, 0), fp8_slot(L, Q_WEIGHT, 0, 0), d_ln, EPI_STORE,
                                     nullptr)));
     RC(run_gemm(m, S_CLS_DW, fp8_dw(m, BT, Vp, C, dqt, gs, m->at<uint8_t>(lo.lnf_qt), fp8_slot(L, Q_ACT, 3, 0),
@@ -779,22 +794,24 @@ int backward_impl(gpt2_model* m, bool acc) {
   RC(timed(m, S_LN_BWD, 0.0, ln_bwd_bytes(true), [&] {
     return layernorm_backward(dt, BT, C, d_ln, m->at<char>(lo.resid[L]), m->param(14), m->at<float>(lo.lnf_mean),
                               m->at<float>(lo.lnf_rstd), dres, true, dres_copy, m->lgrad(14, 0), m->lgrad(15, 0),
-                              acc, m->scratch(), sb, s);
+                              acc, m->scratch(), sb, s, m->slot_max(fp8_slot(L, Q_GRAD, 0, L - 1)));
   }));
   for (int l = L - 1; l >= 0; --l) {
     LayerOffsets& o = lo.layer[l];
     if (m->fp8()) {
       // x_{l+1} = h + g Wp^T + bp: dY = the residual gradient (bf16 copy)
       const int gp = fp8_slot(L, Q_GRAD, 0, l), gf = fp8_slot(L, Q_GRAD, 1, l);
-      RC(fp8_quant(m, GPT2_BF16, dres_t, BT, C, 1, gp, dq, dqt, true));
+      RC(fp8_quant(m, GPT2_BF16, dres_t, BT, C, 1, gp, dq, dqt, true, true));
       RC(run_gemm(m, S_FCPROJ_DW, fp8_dw(m, BT, C, 4 * C, dqt, gp, m->at<uint8_t>(o.g_qt), fp8_slot(L, Q_ACT, 2, l),
                                          m->lgrad(12, l), acc)));
       RC(fp8_bias_grad(m, BT, C, m->lgrad(13, l), acc));
       // du = (dy W_p) * GELU'(u), the derivative saved by the forward
-      RC(run_gemm(m, S_FCPROJ_DX, fp8_dx(m, BT, C, 4 * C, dq, gp, m->wqt(12, l), fp8_slot(L, Q_WEIGHT, 3, l), d_big,
-                                         EPI_MUL, m->at<char>(o.u))));
+      GemmDesc ddx = fp8_dx(m, BT, C, 4 * C, dq, gp, m->wqt(12, l), fp8_slot(L, Q_WEIGHT, 3, l), d_big, EPI_MUL,
+                            m->at<char>(o.u));
+      ddx.amax = m->slot_max(gf);   // du's maximum, for its quantisation below
+      RC(run_gemm(m, S_FCPROJ_DX, ddx));
       // u = ln2 Wfc^T + bfc   (d_big now holds du)
-      RC(fp8_quant(m, GPT2_BF16, d_big, BT, 4 * C, 1, gf, dq, dqt, true));
+      RC(fp8_quant(m, GPT2_BF16, d_big, BT, 4 * C, 1, gf, dq, dqt, true, true));
       RC(run_gemm(m, S_FC_DW, fp8_dw(m, BT, 4 * C, C, dqt, gf, m->at<uint8_t>(o.ln2_qt), fp8_slot(L, Q_ACT, 1, l),
                                      m->lgrad(10, l), acc)));
       RC(fp8_bias_grad(m, BT, 4 * C, m->lgrad(11, l), acc));
@@ -864,7 +881,8 @@ int backward_impl(gpt2_model* m, bool acc) {
     RC(timed(m, S_LN_BWD, 0.0, ln_bwd_bytes(false), [&] {
       return layernorm_backward(dt, BT, C, d_ln, m->at<char>(lo.resid[l]), m->lparam(2, l),
                                 m->at<float>(o.ln1_mean), m->at<float>(o.ln1_rstd), dres, false, dres_copy,
-                                m->lgrad(2, l), m->lgrad(3, l), acc, m->scratch(), sb, s);
+                                m->lgrad(2, l), m->lgrad(3, l), acc, m->scratch(), sb, s,
+                                l > 0 ? m->slot_max(fp8_slot(L, Q_GRAD, 0, l - 1)) : nullptr);
     }));
   }
   // encoder: wpe rows >= T get no gradient (zero already when accumulating),
