@@ -9,13 +9,14 @@
 // conversion (round to nearest even, subnormals kept); x * inv never exceeds
 // FMAX by more than two fp32 roundings, which the conversion rounds back to
 // FMAX.  The quantisation kernel writes the codes row-major and/or
-// transposed (64 x 64 tiles through LDS), so every fp8 product reads both
+// transposed (128 x 128 tiles through LDS), so every fp8 product reads both
 // operands k-major.
 //
 // The bias gradient of an fp8 weight-gradient product is the column sum of
 // the unquantised bf16 gradient, taken while the gradient is quantised: each
-// 64 x 64 tile adds its 64 rows per column in order into a per-row-block
-// partial, and a second kernel adds the row blocks in order (deterministic).
+// 128 x 128 tile adds its 128 rows per column in a fixed order into a
+// per-row-block partial, and a second kernel adds the row blocks in order
+// (deterministic).
 
 #include "kernels.h"
 
@@ -88,31 +89,60 @@ __device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
   return (uint32_t)w;
 }
 
+// Rows and columns of x per block of the quantisation (a multiple of 16:
+// whole 128-byte lines of codes in both layouts).
+constexpr int kQT = 128;
+
 // x [R, Cc] (row stride ldx) -> qrow [R, Cc] and / or qt [Cc, R] codes.
-// Grid (ceil(Cc / 64), ceil(R / 64)); Cc % 8 == 0, R % 16 == 0 when qt.
+// Grid (ceil(Cc / kQT), ceil(R / kQT)), 256 threads; Cc % 8 == 0, R % 16 == 0
+// when qt.  Thread t takes columns 16 (t % 8) .. + 15 of rows t / 8 + 32 p
+// (p < 4) of the tile: 16-byte code stores, whole lines per 8 threads.  The
+// transposed codes go through LDS: thread t then gathers 4 columns x 16 rows
+// (16 dword reads, a 4 x 4 byte transpose per dword quad) and stores 4
+// 16-byte runs of qt.
 // With CS, also colsum[blockIdx.y][c] = sum of x[r][c] over the tile's rows
-// (in row order), for the bias gradient.
+// (each thread's 4 rows in order, then the 8 row groups of a wave by
+// butterfly, then the 4 waves in order: fixed, so run to run identical), for
+// the bias gradient.
 // The scale comes from the np maxima amax_part[i * pstride] (the amax pass's
 // per-block maxima, or a producer's slots): every block takes their maximum
 // (exact, so all agree) and forms inv and s as above; block (0, 0) stores
-// (amax, inv, s) for the products.
+// (amax, inv, s) for the products.  The tile's loads are issued first: they
+// do not depend on the scale.
 template <typename T, int FMT, bool CS>
 __global__ __launch_bounds__(256) void quantize_kernel(int R, int Cc, const T* __restrict__ x, int64_t ldx,
                                                        const float* __restrict__ amax_part, int np, int pstride,
                                                        float fmax,
                                                        Fp8Scale* __restrict__ sc, uint8_t* __restrict__ qrow,
                                                        uint8_t* __restrict__ qt, float* __restrict__ colsum) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[64][64 + 16];
-  __shared__ float ftile[CS ? 64 : 1][CS ? 65 : 1];
+  constexpr int kPitch = kQT / 4 + 2;   // dwords per LDS row: the two half-waves' rows 16 apart differ by 32 banks
+  __shared__ uint32_t tile[kQT][kPitch];
   __shared__ float smax[4];
+  __shared__ float csw[CS ? 4 : 1][CS ? kQT : 1];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r0 = blockIdx.y * kQT, c0 = blockIdx.x * kQT;
+  const int cq = (tid & 7) * 16, rq = tid >> 3;
+  const bool in0 = c0 + cq < Cc, in1 = c0 + cq + 8 < Cc;
+  float v[4][16];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int r = r0 + rq + 32 * p;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[p][e] = 0.f;
+    if (r < R) {
+      const T* src = x + (int64_t)r * ldx + c0 + cq;
+      if (in0) Chunk8<T>::load(src, &v[p][0]);
+      if (in1) Chunk8<T>::load(src + 8, &v[p][8]);
+    }
+  }
   float am = 0.f;
-  for (int i = threadIdx.x; i < np; i += 256) am = fmaxf(am, amax_part[(size_t)i * pstride]);
+  for (int i = tid; i < np; i += 256) am = fmaxf(am, amax_part[(size_t)i * pstride]);
   am = wave_max(am);
-  if ((threadIdx.x & 63) == 0) smax[threadIdx.x >> 6] = am;
+  if (lane == 0) smax[wv] = am;
   __syncthreads();
   am = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
   const float inv = am > 0.f ? fmax / am : 1.0f;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
     Fp8Scale r;
     r.amax = am;
     r.inv = inv;
@@ -120,42 +150,65 @@ __global__ __launch_bounds__(256) void quantize_kernel(int R, int Cc, const T* _
     r.unused = 0.f;
     *sc = r;
   }
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
-    const int r = i >> 3, cc = (i & 7) * 8;
-    const bool in = r0 + r < R && c0 + cc < Cc;
-    float v[8];
+  float cs[16];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = 0.f;
-    if (in) Chunk8<T>::load(x + (int64_t)(r0 + r) * ldx + c0 + cc, v);
+  for (int e = 0; e < 16; ++e) cs[e] = 0.f;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int rl = rq + 32 * p, r = r0 + rl;
     if constexpr (CS) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ftile[r][cc + e] = v[e];
+      for (int e = 0; e < 16; ++e) cs[e] += v[p][e];   // zeros outside the tensor
     }
-    uint2 w;
-    w.x = pack4<FMT>(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-    w.y = pack4<FMT>(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
-    if (qrow && in) *reinterpret_cast<uint2*>(qrow + (int64_t)(r0 + r) * Cc + c0 + cc) = w;
-    if (qt) *reinterpret_cast<uint2*>(&tile[r][cc]) = w;
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = pack4<FMT>(v[p][4 * k] * inv, v[p][4 * k + 1] * inv, v[p][4 * k + 2] * inv, v[p][4 * k + 3] * inv);
+    if (qrow && r < R) {
+      uint8_t* dst = qrow + (int64_t)r * Cc + c0 + cq;
+      if (in1) *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+      else if (in0) *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+    }
+    if (qt) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) tile[rl][cq / 4 + k] = w[k];
+    }
   }
   if constexpr (CS) {
-    __syncthreads();
-    if (threadIdx.x < 64 && c0 + (int)threadIdx.x < Cc) {
-      float t = 0.f;
-      for (int r = 0; r < 64; ++r) t += ftile[r][threadIdx.x];
-      colsum[(int64_t)blockIdx.y * Cc + c0 + threadIdx.x] = t;
+    // lanes l, l ^ 8, l ^ 16, l ^ 32 hold the same columns
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      cs[e] += __shfl_xor(cs[e], 8, 64);
+      cs[e] += __shfl_xor(cs[e], 16, 64);
+      cs[e] += __shfl_xor(cs[e], 32, 64);
+    }
+    if (lane < 8) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) csw[wv][cq + e] = cs[e];
     }
   }
+  if (CS || qt) __syncthreads();
+  if constexpr (CS) {
+    if (tid < kQT && c0 + tid < Cc)
+      colsum[(int64_t)blockIdx.y * Cc + c0 + tid] = ((csw[0][tid] + csw[1][tid]) + csw[2][tid]) + csw[3][tid];
+  }
   if (qt) {
-    __syncthreads();
-    const int c = threadIdx.x >> 2, rr = (threadIdx.x & 3) * 16;
-    if (c0 + c < Cc && r0 + rr < R) {
-      uint32_t w[4];
+    const int cg = (tid & 31) * 4, rg = (tid >> 5) * 16;
+    if (r0 + rg < R) {
+      uint32_t d[16];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        w[q] = (uint32_t)tile[rr + 4 * q][c] | ((uint32_t)tile[rr + 4 * q + 1][c] << 8) |
-               ((uint32_t)tile[rr + 4 * q + 2][c] << 16) | ((uint32_t)tile[rr + 4 * q + 3][c] << 24);
-      *reinterpret_cast<uint4*>(qt + (int64_t)(c0 + c) * R + r0 + rr) = make_uint4(w[0], w[1], w[2], w[3]);
+      for (int k = 0; k < 16; ++k) d[k] = tile[rg + k][cg / 4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (c0 + cg + j < Cc) {
+          uint32_t o[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)   // byte j of rows 4q .. 4q + 3
+            o[q] = ((d[4 * q] >> (8 * j)) & 0xffu) | (((d[4 * q + 1] >> (8 * j)) & 0xffu) << 8) |
+                   (((d[4 * q + 2] >> (8 * j)) & 0xffu) << 16) | (((d[4 * q + 3] >> (8 * j)) & 0xffu) << 24);
+          *reinterpret_cast<uint4*>(qt + (int64_t)(c0 + cg + j) * R + r0 + rg) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+      }
     }
   }
 }
@@ -227,7 +280,7 @@ int fp8_quantize(int dtype_in, int fmt, int R, int Cc, const void* x, int64_t ld
     GPT2_LAUNCH_CHECK();
     return 0;
   }
-  dim3 grid((unsigned)ceil_div64(Cc, 64), (unsigned)ceil_div64(R, 64));
+  dim3 grid((unsigned)ceil_div64(Cc, kQT), (unsigned)ceil_div64(R, kQT));
   mark_begin(0, stream);
   if (dtype_in == BF16) {
     if (fmt == 0) launch_quantize<bf16, 0>(grid, R, Cc, x, ldx, amax_part, np, ps, sc, qrow, qt, colsum, stream);
@@ -241,13 +294,13 @@ int fp8_quantize(int dtype_in, int fmt, int R, int Cc, const void* x, int64_t ld
   return 0;
 }
 
-size_t fp8_colsum_bytes(int R, int N) { return (size_t)ceil_div64(R, 64) * N * sizeof(float); }
+size_t fp8_colsum_bytes(int R, int N) { return (size_t)ceil_div64(R, kQT) * N * sizeof(float); }
 
 int colsum_reduce(int R, int N, const float* part, float* db, bool accumulate, hipStream_t stream) {
   if (R < 0 || N < 0 || !part || !db) return gpt2_internal_fail(1, "colsum_reduce: bad arguments");
   if (N == 0) return 0;
   hipLaunchKernelGGL(colsum_reduce_kernel, dim3((unsigned)ceil_div64(N, 64)), dim3(1024), 0, stream,
-                     (int)ceil_div64(R, 64), N, part, db, accumulate);
+                     (int)ceil_div64(R, kQT), N, part, db, accumulate);
   GPT2_LAUNCH_CHECK();
   return 0;
 }

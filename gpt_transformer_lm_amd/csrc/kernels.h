@@ -141,7 +141,7 @@ int fp8_amax(int dtype_in, int64_t n, const void* x, float* workspace, hipStream
 // fp8(x * inv) for x [R, Cc] (row stride ldx, R * Cc the n of fp8_amax):
 // row-major into qrow [R, Cc] and / or transposed into qt [Cc, R] (either may
 // be NULL).  Cc % 8 == 0; R % 16 == 0 when qt.  With colsum
-// (fp8_colsum_bytes(R, Cc), device) also the per-64-row-block column sums of
+// (fp8_colsum_bytes(R, Cc), device) also the per-row-block column sums of
 // x that colsum_reduce turns into a bias gradient.  amax_np > 0 (at most
 // kAmaxWays): amax_part holds that many slots, kAmaxStride floats apart, left
 // by a producer kernel (amax_atomic_bf16), instead of fp8_amax's maxima.
