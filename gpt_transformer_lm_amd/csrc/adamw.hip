@@ -134,6 +134,7 @@ __global__ __launch_bounds__(256) void adamw_fused_kernel(AdamSegs sg, float* __
   const int64_t mbase = mt.off + (int64_t)bt * mt.R * mt.Cc;
   __shared__ __attribute__((aligned(16))) bf16 tile[64][72];   // 144-byte rows
   const int tid = threadIdx.x, cq = (tid & 15) * 4;
+  float am = 0.f;   // largest |updated value| of the tile (matrices quantised to fp8)
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int r = (tid >> 4) + 16 * q;
@@ -153,11 +154,17 @@ __global__ __launch_bounds__(256) void adamw_fused_kernel(AdamSegs sg, float* __
       *reinterpret_cast<float4*>(mom2 + i) = v;
       o[0] = (bf16)th.x; o[1] = (bf16)th.y; o[2] = (bf16)th.z; o[3] = (bf16)th.w;
       *reinterpret_cast<bf16x4_t*>(pbf + i) = o;
+      am = fmaxf(am, fmaxf(fmaxf(fabsf(th.x), fabsf(th.y)), fmaxf(fabsf(th.z), fabsf(th.w))));
     } else {
       o[0] = o[1] = o[2] = o[3] = (bf16)0.f;
     }
     *reinterpret_cast<bf16x4_t*>(&tile[r][cq]) = o;
   }
+  if (mt.amax) {   // (uniform)
+    am = wave_max(am);
+    if ((tid & 63) == 0) amax_atomic_f32(mt.amax + (size_t)bt * kAmaxWays * kAmaxStride, t * 4 + (tid >> 6), am);
+  }
+  if (!mt.dst_t) return;   // (uniform)
   __syncthreads();
   // transposed: row c0 + c of [batch][Cc][R] gets tile column c, 16 rows per thread
   {
@@ -361,7 +368,7 @@ int adamw_transposed(int64_t n, float* master, const float* grad, float* m, floa
     AdamMatrix mt = mats[k];
     const int64_t len = (int64_t)mt.batches * mt.R * mt.Cc;
     if (mt.off < prev_end || mt.off + len > n || mt.R <= 0 || mt.Cc <= 0 || mt.R % 8 || mt.Cc % 4 || mt.off % 4 ||
-        !mt.dst_t || (uintptr_t)mt.dst_t % 16)
+        (!mt.dst_t && !mt.amax) || (uintptr_t)mt.dst_t % 16)
       return gpt2_internal_fail(1, "adamw_transposed: matrix %d not in order, unaligned or out of range", k);
     if (mt.off > prev_end) {
       if (sg.nflat == kAdamMaxMats + 1) return gpt2_internal_fail(1, "adamw_transposed: too many ranges");

@@ -328,8 +328,9 @@ size_t attention_backward_workspace_bytes(int B, int T_, int H, int hd) {
 
 int attention_backward(int dtype, int B, int T_, int H, int hd, const void* qkv, const void* out,
                        const void* dout, const float* lse, void* dqkv, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream) {
-  if (B < 0 || T_ < 0 || H <= 0 || !qkv || !out || !dout || !lse || !dqkv)
+                       size_t workspace_bytes, hipStream_t stream, float* amax) {
+  if (B < 0 || T_ < 0 || H <= 0 || !qkv || !out || !dout || !lse || !dqkv ||
+      (amax && !attention_mfma_supported(dtype, hd)))
     return gpt2_internal_fail(1, "attention_backward: bad arguments");
   if (B == 0 || T_ == 0) return 0;
   if (!workspace || workspace_bytes < attention_backward_workspace_bytes(B, T_, H, hd))
@@ -338,7 +339,7 @@ int attention_backward(int dtype, int B, int T_, int H, int hd, const void* qkv,
   float* D = (float*)workspace;
   float* L2 = D + ((size_t)B * H * T_ + 63) / 64 * 64;
   if (attention_mfma_supported(dtype, hd))
-    return attention_backward_mfma(B, T_, H, qkv, out, dout, lse, L2, D, dqkv, stream);
+    return attention_backward_mfma(B, T_, H, qkv, out, dout, lse, L2, D, dqkv, stream, amax);
   const int64_t lanes = (int64_t)B * H * T_ * (hd / 8);
   mark_begin(0, stream);
   if (dtype == BF16) {

@@ -188,16 +188,23 @@ __device__ __forceinline__ void frags_global(const bf16* G, size_t ld, int row, 
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
 // Writes 64 values of row `row` held as two 32 x 32 accumulators (d on registers).
-__device__ __forceinline__ void store_row64(bf16* dst, const floatx16 acc[2], float mul, int lane) {
+// Returns the largest |acc * mul| stored (for an fp8 quantisation that follows).
+__device__ __forceinline__ float store_row64(bf16* dst, const floatx16 acc[2], float mul, int lane) {
+  float m = 0.f;
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       bf16x4 v;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (bf16)(acc[dt][4 * g + e] * mul);
+      for (int e = 0; e < 4; ++e) {
+        const float x = acc[dt][4 * g + e] * mul;
+        v[e] = (bf16)x;
+        m = fmaxf(m, fabsf(x));
+      }
       *reinterpret_cast<bf16x4*>(dst + dt * 32 + 8 * g + 4 * (lane >> 5)) = v;
     }
+  return m;
 }
 
 // ------------------------------------------------------------------ forward
@@ -381,7 +388,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
                                                                  const bf16* __restrict__ dout,
                                                                  const float* __restrict__ lse2,
                                                                  const float* __restrict__ Dv,
-                                                                 bf16* __restrict__ dqkv, float scale) {
+                                                                 bf16* __restrict__ dqkv, float scale,
+                                                                 float* __restrict__ amax) {
   constexpr int NS = NS_DKDV;
   __shared__ __attribute__((aligned(1024))) char ring[NS][KV_STAGE_BYTES];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -542,10 +550,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
       }
     }
   }
+  float mx = 0.f;
   if (mykey < T) {
     bf16* dst = dqkv + ((size_t)b * T + mykey) * ld + h * HD;
-    store_row64(dst + C, dk, scale, lane);
-    store_row64(dst + 2 * C, dv, 1.0f, lane);
+    mx = store_row64(dst + C, dk, scale, lane);
+    mx = fmaxf(mx, store_row64(dst + 2 * C, dv, 1.0f, lane));
+  }
+  if (amax) {   // (uniform) the fp8 quantisation of dqkv reads the maximum from these slots
+    mx = wave_max(mx);
+    if (lane == 0) amax_atomic_bf16(amax, (int)(blockIdx.y * gridDim.x + blockIdx.x) * 4 + wave, mx);
   }
 }
 
@@ -553,14 +566,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
 
 // Also the per-query quantities both backward kernels use, D_i = dO_i . O_i
 // and lse_i log2(e), from the rows the kernel holds anyway (so it runs before
-// the dK / dV kernel, which reads them).
+// the dK / dV kernel, which reads them).  AM: also dQ's maximum into the
+// amax slots (an instance of its own: at three blocks per compute unit the
+// extra epilogue work would cost the plain kernel a register).
+template <bool AM>
 __global__ __launch_bounds__(256, 3) void attn_bwd_dq_mfma_kernel(int T, int H, const bf16* __restrict__ qkv,
                                                                const bf16* __restrict__ out,
                                                                const bf16* __restrict__ dout,
                                                                const float* __restrict__ lse,
                                                                float* __restrict__ lse2,
                                                                float* __restrict__ Dv,
-                                                               bf16* __restrict__ dqkv, float scale) {
+                                                               bf16* __restrict__ dqkv, float scale,
+                                                               float* __restrict__ amax) {
   constexpr int NS = NS_DQ;
   __shared__ __attribute__((aligned(1024))) char ring[NS][2 * TILE];   // K tile, V tile
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -693,7 +710,12 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dq_mfma_kernel(int T, int H, 
       }
     }
   }
-  if (myq < T) store_row64(dqkv + ((size_t)b * T + myq) * ld + h * HD, dq, scale, lane);
+  float mx = 0.f;
+  if (myq < T) mx = store_row64(dqkv + ((size_t)b * T + myq) * ld + h * HD, dq, scale, lane);
+  if constexpr (AM) {   // as in the dK / dV kernel
+    mx = wave_max(mx);
+    if (lane == 0) amax_atomic_bf16(amax, (int)(blockIdx.y * gridDim.x + blockIdx.x) * 4 + wave, mx);
+  }
 }
 
 }  // namespace
@@ -711,18 +733,22 @@ int attention_forward_mfma(int B, int T, int H, const void* qkv, void* out, floa
 }
 
 int attention_backward_mfma(int B, int T, int H, const void* qkv, const void* out, const void* dout,
-                            const float* lse, float* lse2, float* D, void* dqkv, hipStream_t stream) {
+                            const float* lse, float* lse2, float* D, void* dqkv, hipStream_t stream, float* amax) {
   dim3 grid((unsigned)ceil_div64(T, ROWS), (unsigned)(B * H));
   const float scale = 1.0f / sqrtf((float)HD);
   // dQ first: it also writes D and lse2 for the dK / dV kernel
   mark_begin(2, stream);
-  hipLaunchKernelGGL(attn_bwd_dq_mfma_kernel, grid, dim3(256), 0, stream, T, H, (const bf16*)qkv, (const bf16*)out,
-                     (const bf16*)dout, lse, lse2, D, (bf16*)dqkv, scale);
+  if (amax)
+    hipLaunchKernelGGL(attn_bwd_dq_mfma_kernel<true>, grid, dim3(256), 0, stream, T, H, (const bf16*)qkv,
+                       (const bf16*)out, (const bf16*)dout, lse, lse2, D, (bf16*)dqkv, scale, amax);
+  else
+    hipLaunchKernelGGL(attn_bwd_dq_mfma_kernel<false>, grid, dim3(256), 0, stream, T, H, (const bf16*)qkv,
+                       (const bf16*)out, (const bf16*)dout, lse, lse2, D, (bf16*)dqkv, scale, amax);
   GPT2_LAUNCH_CHECK();
   mark_end(2, stream);
   mark_begin(1, stream);
   hipLaunchKernelGGL(attn_bwd_dkdv_mfma_kernel, grid, dim3(256), 0, stream, T, H, (const bf16*)qkv,
-                     (const bf16*)dout, lse2, D, (bf16*)dqkv, scale);
+                     (const bf16*)dout, lse2, D, (bf16*)dqkv, scale, amax);
   GPT2_LAUNCH_CHECK();
   mark_end(1, stream);
   return 0;

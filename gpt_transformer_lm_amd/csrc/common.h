@@ -79,6 +79,10 @@ __device__ __forceinline__ void amax_atomic_bf16(float* slots, int i, float m) {
   const uint32_t r = ((b + 0x7fffu + ((b >> 16) & 1u)) & 0xffff0000u);   // round to nearest even
   atomicMax(reinterpret_cast<unsigned int*>(slots + (i % kAmaxWays) * kAmaxStride), r);
 }
+// The same for an fp32 tensor: m is max-ed in exactly.
+__device__ __forceinline__ void amax_atomic_f32(float* slots, int i, float m) {
+  atomicMax(reinterpret_cast<unsigned int*>(slots + (i % kAmaxWays) * kAmaxStride), __float_as_uint(m));
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

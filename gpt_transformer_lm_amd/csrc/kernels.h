@@ -120,10 +120,14 @@ int attention_forward_mfma(int B, int T, int H, const void* qkv, void* out, floa
 // lse2 = lse * log2(e) (base-2 log-sum-exp) and D = rowsum(dO * O), both
 // [B, H, T] scratch, are computed by the dQ kernel and read by the dK / dV one.
 int attention_backward_mfma(int B, int T, int H, const void* qkv, const void* out, const void* dout,
-                            const float* lse, float* lse2, float* D, void* dqkv, hipStream_t stream);
+                            const float* lse, float* lse2, float* D, void* dqkv, hipStream_t stream,
+                            float* amax = nullptr);
+// amax (only where attention_mfma_supported; kAmaxWays x kAmaxStride floats,
+// zero beforehand): also the maximum |dqkv| written, into those slots
+// (amax_atomic_bf16), for the fp8 quantisation of dqkv.
 int attention_backward(int dtype, int B, int T, int H, int hd, const void* qkv, const void* out,
                        const void* dout, const float* lse, void* dqkv, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream);
+                       size_t workspace_bytes, hipStream_t stream, float* amax = nullptr);
 
 // ------------------------------------------------------------------ FP8 quantisation
 // Per-tensor scale of an fp8 operand: inv = FMAX / amax, s = amax / FMAX
@@ -225,8 +229,12 @@ constexpr int kAdamMaxMats = 6;
 struct AdamMatrix {
   int64_t off;
   int batches, R, Cc;
-  bf16* dst_t;
-  int tiles;   // set by the launcher
+  bf16* dst_t;   // transposed bf16 copy [batches][Cc][R], or NULL (none)
+  int tiles;     // set by the launcher
+  // or NULL: the maximum |updated fp32 value| of batch b max-ed into the slots
+  // amax + b * kAmaxWays * kAmaxStride (amax_atomic_f32; zero beforehand),
+  // for the fp8 quantisation of the matrices
+  float* amax;
 };
 struct AdamSegs {
   int nflat, nmat, flat_blocks;

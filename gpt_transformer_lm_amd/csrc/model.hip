@@ -835,6 +835,9 @@ int backward_impl(gpt2_model* m, bool acc) {
                                 m->at<float>(o.ln2_rstd), dres, false, dres_copy, m->lgrad(8, l), m->lgrad(9, l),
                                 acc, m->scratch(), sb, s);
     }));
+    // fp8: the attention backward kernels also take dqkv's maximum for its
+    // quantisation, unless the QK transform rewrites dq and dk after them
+    const bool qkv_max = m->fp8() && attention_mfma_supported(dt, hd) && !m->qk_norm() && !m->rope();
     // h = x + atty Wo^T + bo
     RC(run_gemm(m, S_ATTPROJ_DW, dw_desc(m, BT, C, C, dres_t, m->at<char>(o.atty), m->lgrad(6, l),
                                          m->lgrad(7, l), acc)));
@@ -846,7 +849,8 @@ int backward_impl(gpt2_model* m, bool acc) {
       const bool a0 = !mfma && timer_arm(m, S_ATTN_DOT, 0), a1 = timer_arm(m, S_ATTN_DKDV, 1),
                  a2 = timer_arm(m, S_ATTN_DQ, 2);
       const int rc = attention_backward(dt, B, T, H, hd, m->at<char>(o.qkv), m->at<char>(o.atty), d_ln,
-                                        m->at<float>(o.lse), d_qkv, m->scratch(), sb, s);
+                                        m->at<float>(o.lse), d_qkv, m->scratch(), sb, s,
+                                        qkv_max ? m->slot_max(fp8_slot(L, Q_GRAD, 2, l)) : nullptr);
       marks_clear();
       RC(rc);
       const double lse_b = (double)B * H * T * 4;
@@ -866,7 +870,7 @@ int backward_impl(gpt2_model* m, bool acc) {
     // qkv = ln1 Wqkv^T + bqkv
     if (m->fp8()) {
       const int gq = fp8_slot(L, Q_GRAD, 2, l);
-      RC(fp8_quant(m, GPT2_BF16, d_qkv, BT, 3 * C, 1, gq, dq, dqt, true));
+      RC(fp8_quant(m, GPT2_BF16, d_qkv, BT, 3 * C, 1, gq, dq, dqt, true, qkv_max));
       RC(run_gemm(m, S_QKV_DW, fp8_dw(m, BT, 3 * C, C, dqt, gq, m->at<uint8_t>(o.ln1_qt), fp8_slot(L, Q_ACT, 0, l),
                                       m->lgrad(4, l), acc)));
       RC(fp8_bias_grad(m, BT, 3 * C, m->lgrad(5, l), acc));
@@ -944,8 +948,9 @@ int refresh_transposed(gpt2_model* m) {
 }
 
 // fp8 mode: E4M3 codes (row-major and transposed) of the fp8 products'
-// weights, quantised per matrix from the fp32 master.
-int refresh_fp8_weights(gpt2_model* m) {
+// weights, quantised per matrix from the fp32 master.  produced: the AdamW
+// update left each matrix's maximum in its scale slot.
+int refresh_fp8_weights(gpt2_model* m, bool produced = false) {
   if (!m->fp8()) return 0;
   const int L = m->cfg.num_layers;
   for (int w = 0; w < 4; ++w) {
@@ -955,7 +960,8 @@ int refresh_fp8_weights(gpt2_model* m) {
     const int R = (int)(layered ? sh[1] : sh[0]), Cc = (int)(layered ? sh[2] : sh[1]);
     for (int l = 0; l < (layered ? L : 1); ++l) {
       const float* src = m->master() + m->lo.pt.off[i] + (int64_t)l * R * Cc;
-      RC(fp8_quant(m, GPT2_FP32, src, R, Cc, 0, fp8_slot(L, Q_WEIGHT, w, l), m->wq(i, l), m->wqt(i, l)));
+      RC(fp8_quant(m, GPT2_FP32, src, R, Cc, 0, fp8_slot(L, Q_WEIGHT, w, l), m->wq(i, l), m->wqt(i, l), false,
+                   produced));
     }
   }
   return 0;
@@ -987,26 +993,34 @@ int update_impl(gpt2_model* m, float max_grad_norm, bool need_norm) {
     });
   }
   // bf16 modes: one launch that also writes the transposed bf16 weight
-  // copies; bytes: master, m, v read and written, gradient read, bf16 copy
-  // written (30 per parameter) and the transposed copies (2 per element)
+  // copies and, in fp8 mode, takes the fp8 weights' maxima; bytes: master, m,
+  // v read and written, gradient read, bf16 copy written (30 per parameter)
+  // and the transposed copies (2 per element)
   AdamMatrix mats[kAdamMaxMats];
   int nm = 0;
   double tbytes = 0.0;
-  for (int i : kTransposed) {
-    if (!m->lo.params_t[i]) continue;   // (fp8 mode: only the attention projection keeps a bf16 copy)
+  const int L = m->cfg.num_layers;
+  if (m->fp8() && !m->dry())   // the weight slots (0 .. 3L) start from zero
+    RC(fill_f32((int64_t)(1 + 3 * L) * kAmaxWays * kAmaxStride, m->slot_max(0), 0.0f, m->stream));
+  for (int i : kTransposed) {   // (in parameter order; a superset of the fp8 weights)
+    float* amax = nullptr;
+    for (int w = 0; w < 4; ++w)
+      if (m->fp8() && kFp8Weights[w] == i) amax = m->slot_max(fp8_slot(L, Q_WEIGHT, w, 0));
+    // (fp8 mode: only the attention projection keeps a transposed bf16 copy)
+    bf16* dst_t = m->lo.params_t[i] ? static_cast<bf16*>(m->wt(i, 0)) : nullptr;
+    if (!dst_t && !amax) continue;
     const int64_t* sh = m->lo.pt.shape[i];
     const bool layered = m->lo.pt.ndim[i] == 3;
     const int R = (int)(layered ? sh[1] : sh[0]), Cc = (int)(layered ? sh[2] : sh[1]);
-    mats[nm++] = AdamMatrix{(int64_t)m->lo.pt.off[i], layered ? (int)sh[0] : 1, R, Cc, static_cast<bf16*>(m->wt(i, 0)),
-                            0};
-    tbytes += 2.0 * (layered ? (double)sh[0] : 1.0) * R * Cc;
+    mats[nm++] = AdamMatrix{(int64_t)m->lo.pt.off[i], layered ? (int)sh[0] : 1, R, Cc, dst_t, 0, amax};
+    if (dst_t) tbytes += 2.0 * (layered ? (double)sh[0] : 1.0) * R * Cc;
   }
   RC(timed(m, S_ADAMW, 0.0, (double)m->lo.P * 30.0 + tbytes, [&] {
     return adamw_transposed(m->lo.P, m->master(), m->grad(), m->at<float>(m->lo.adam_m), m->at<float>(m->lo.adam_v),
                             m->at<bf16>(m->lo.params_bf16), mats, nm, m->stream, gscale,
                             m->at<AdamHP>(m->lo.adam_hp));
   }));
-  return refresh_fp8_weights(m);
+  return refresh_fp8_weights(m, true);
 }
 
 void graph_release(gpt2_model* m) {
