@@ -133,13 +133,30 @@ int next_pow2(int n) {
   return np;
 }
 
-// Step 2: one block per piece; threads stride over channels.
+// Step 2: one block per piece; threads stride over groups of VW channels
+// (VW = 4: 16-byte loads and stores).
+template <int VW>
+struct ChanVec;
+template <> struct ChanVec<1> {
+  typedef float T;
+  __device__ static T zero() { return 0.f; }
+  __device__ static T add(T a, T b) { return a + b; }
+};
+template <> struct ChanVec<4> {
+  typedef float4 T;
+  __device__ static T zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ static T add(T a, T b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
+};
+
+template <int VW>
 __global__ __launch_bounds__(256) void encoder_bwd_pieces_kernel(int n, int C,
                                                                  const uint64_t* __restrict__ sorted,
                                                                  const float* __restrict__ dx0,
                                                                  float* __restrict__ dwte,
                                                                  float* __restrict__ pcont,
                                                                  float* __restrict__ pown) {
+  using CV = ChanVec<VW>;
+  typedef typename CV::T V;
   const int piece = blockIdx.x;
   const int start = piece * kPiece;
   const int end = min(n, start + kPiece);
@@ -153,32 +170,35 @@ __global__ __launch_bounds__(256) void encoder_bwd_pieces_kernel(int n, int C,
   const int prev_tok = start > 0 ? key_tok(sorted[start - 1]) : -1;
   const int next_tok = end < n ? key_tok(sorted[end]) : -1;
   const int len = end - start;
-  for (int c = threadIdx.x; c < C; c += blockDim.x) {
+  for (int c = threadIdx.x * VW; c < C; c += blockDim.x * VW) {
     int rs = 0;   // run start (index within piece)
-    float acc = 0.f;
+    V acc = CV::zero();
     // rows are read 8 at a time ahead of the (sequential, fixed-order) sums,
     // so eight loads per thread are in flight instead of one
     for (int e0 = 0; e0 < len; e0 += 8) {
-      float v[8];
+      V v[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = e0 + j < len ? dx0[(size_t)spos[e0 + j] * C + c] : 0.f;
+      for (int j = 0; j < 8; ++j)
+        v[j] = e0 + j < len ? *reinterpret_cast<const V*>(dx0 + (size_t)spos[e0 + j] * C + c) : CV::zero();
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int e = e0 + j;
         if (e >= len) break;
-        acc += v[j];
+        acc = CV::add(acc, v[j]);
         const bool last = (e == len - 1) || (stok[e + 1] != stok[e]);
         if (last) {
           const int tok = stok[e];
           const bool from_prev = (rs == 0) && (prev_tok == tok);
           const bool to_next = (e == len - 1) && (next_tok == tok);
           if (from_prev)
-            pcont[(size_t)piece * C + c] = acc;
+            *reinterpret_cast<V*>(pcont + (size_t)piece * C + c) = acc;
           else if (to_next)
-            pown[(size_t)piece * C + c] = acc;
-          else
-            dwte[(size_t)tok * C + c] += acc;
-          acc = 0.f;
+            *reinterpret_cast<V*>(pown + (size_t)piece * C + c) = acc;
+          else {
+            V* d = reinterpret_cast<V*>(dwte + (size_t)tok * C + c);
+            *d = CV::add(*d, acc);
+          }
+          acc = CV::zero();
           rs = e + 1;
         }
       }
@@ -186,28 +206,42 @@ __global__ __launch_bounds__(256) void encoder_bwd_pieces_kernel(int n, int C,
   }
 }
 
-// Step 3: one block per piece whose last run starts a boundary-crossing run.
+// Step 3: one block per piece whose last run starts a boundary-crossing run:
+// the owner partial plus the continuation partials of the following pieces,
+// in piece order.
+template <int VW>
 __global__ __launch_bounds__(256) void encoder_bwd_spans_kernel(int n, int C, int npieces,
                                                                 const uint64_t* __restrict__ sorted,
                                                                 const float* __restrict__ pcont,
                                                                 const float* __restrict__ pown,
                                                                 float* __restrict__ dwte) {
+  using CV = ChanVec<VW>;
+  typedef typename CV::T V;
   const int piece = blockIdx.x;
   const int start = piece * kPiece;
   const int end = min(n, start + kPiece);
   if (end >= n) return;
   const int tok = key_tok(sorted[end - 1]);
   if (key_tok(sorted[end]) != tok) return;    // last run does not continue
-  // find where the last run starts; if it started in an earlier piece this
-  // piece holds a continuation, not the owner partial
-  int rs = end - 1;
-  while (rs > start && key_tok(sorted[rs - 1]) == tok) --rs;
-  if (rs == start && start > 0 && key_tok(sorted[start - 1]) == tok) return;
-  for (int c = threadIdx.x; c < C; c += blockDim.x) {
-    float acc = pown[(size_t)piece * C + c];
-    for (int q = piece + 1; q < npieces && key_tok(sorted[q * kPiece]) == tok; ++q)
-      acc += pcont[(size_t)q * C + c];
-    dwte[(size_t)tok * C + c] += acc;
+  // (keys are sorted: the last run covers the whole piece exactly when the
+  // first key has its token too; then, if the run began before the piece,
+  // this piece holds a continuation, not the owner partial)
+  if (start > 0 && key_tok(sorted[start]) == tok && key_tok(sorted[start - 1]) == tok) return;
+  // the run continues through pieces piece + 1 .. qend - 1 (found in parallel:
+  // the first later piece whose first key has another token)
+  __shared__ int s_end;
+  if (threadIdx.x == 0) s_end = npieces;
+  __syncthreads();
+  for (int q = piece + 1 + (int)threadIdx.x; q < npieces; q += blockDim.x)
+    if (key_tok(sorted[(size_t)q * kPiece]) != tok) atomicMin(&s_end, q);
+  __syncthreads();
+  const int qend = s_end;
+  for (int c = threadIdx.x * VW; c < C; c += blockDim.x * VW) {
+    V acc = *reinterpret_cast<const V*>(pown + (size_t)piece * C + c);
+#pragma unroll 4
+    for (int q = piece + 1; q < qend; ++q) acc = CV::add(acc, *reinterpret_cast<const V*>(pcont + (size_t)q * C + c));
+    V* d = reinterpret_cast<V*>(dwte + (size_t)tok * C + c);
+    *d = CV::add(*d, acc);
   }
 }
 
@@ -281,11 +315,22 @@ int encoder_backward_sorted(int B, int T_, int C, const uint64_t* sorted, const 
                        stream, B, T_, C, dx0, dwpe, accumulate_wpe);
     GPT2_LAUNCH_CHECK();
   }
-  hipLaunchKernelGGL(encoder_bwd_pieces_kernel, dim3(npieces), dim3(256), 0, stream, n, C, sorted, dx0, dwte, pcont,
-                     pown);
-  GPT2_LAUNCH_CHECK();
-  hipLaunchKernelGGL(encoder_bwd_spans_kernel, dim3(npieces), dim3(256), 0, stream, n, C, npieces, sorted, pcont,
-                     pown, dwte);
+  // 16-byte channel groups where every row of dx0, dwte and the partials
+  // starts 16-byte aligned
+  const bool v4 = C % 4 == 0 && (((uintptr_t)dx0 | (uintptr_t)dwte | (uintptr_t)pcont) % 16) == 0;
+  if (v4) {
+    hipLaunchKernelGGL(encoder_bwd_pieces_kernel<4>, dim3(npieces), dim3(256), 0, stream, n, C, sorted, dx0, dwte,
+                       pcont, pown);
+    GPT2_LAUNCH_CHECK();
+    hipLaunchKernelGGL(encoder_bwd_spans_kernel<4>, dim3(npieces), dim3(256), 0, stream, n, C, npieces, sorted, pcont,
+                       pown, dwte);
+  } else {
+    hipLaunchKernelGGL(encoder_bwd_pieces_kernel<1>, dim3(npieces), dim3(256), 0, stream, n, C, sorted, dx0, dwte,
+                       pcont, pown);
+    GPT2_LAUNCH_CHECK();
+    hipLaunchKernelGGL(encoder_bwd_spans_kernel<1>, dim3(npieces), dim3(256), 0, stream, n, C, npieces, sorted, pcont,
+                       pown, dwte);
+  }
   GPT2_LAUNCH_CHECK();
   return 0;
 }

@@ -418,6 +418,22 @@ def test_encoder(dtype, B, T, C, V):
     assert np.array_equal(host(dwte2), got)
 
 
+@pytest.mark.parametrize("B,T,C,V", [(2, 300, 6, 40), (3, 200, 20, 5)])
+def test_encoder_backward_narrow(B, T, C, V):
+    # widths that are not a multiple of 4 (the scalar channel path), and a
+    # vocabulary so small that runs of one token cross many 64-position pieces
+    say("encoder_backward", B, T, C, V)
+    r = rng(B * T + C)
+    tok = r.integers(0, V, (B, T)).astype(np.int32)
+    dx0 = r.standard_normal((B, T, C)).astype(np.float32)
+    base = r.standard_normal((V, C)).astype(np.float32)
+    dwte, dwpe = dev(base, FP32), empty32((T, C))
+    lib.encoder_backward(dev_i32(tok), dev(dx0, FP32), dwte, dwpe, V)
+    rw, rp = O.encoder_backward(dx0.astype(np.float64), tok, V, T)
+    assert rel(host(dwte), base + rw) < 1e-6
+    assert rel(host(dwpe), rp) < 1e-6
+
+
 # ---------------------------------------------------------------- AdamW
 
 @pytest.mark.parametrize("n", [1000003, 64, 5])
