@@ -106,10 +106,10 @@ constexpr bool epi_has_aux(int epi) { return epi == EPI_BIAS_RES || epi == EPI_M
 // epilogue.  (For K = 768 .. 3072 per tile that exchange costs more than the
 // second wave per SIMD gains: measured 5-25 % slower there.)
 constexpr int gemm_waves(int BM, int BN, int epi, int kgs) {
-  return (BM == 256 && BN >= 128 && !epi_has_aux(epi)) || kgs == 2 ? 8 : 4;
+  return (BM == 256 && BN >= 128 && !epi_has_aux(epi)) || BM == 384 || kgs == 2 ? 8 : 4;
 }
 constexpr int gemm_wave_rows(int BM, int BN, int epi, int kgs) {
-  return gemm_waves(BM, BN, epi, kgs) == 8 && BN == 128 ? 4 : 2;
+  return gemm_waves(BM, BN, epi, kgs) == 8 && (BN == 128 || BM == 384) ? 4 : 2;
 }
 
 
@@ -576,9 +576,10 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
         // The next k slice's fragments load while this one's products run (two
         // buffers), except where that would not fit the 256 registers of a
         // wave at two waves per SIMD: fp8 (fragments twice as large, and only
-        // two slices per K step), the K-grouped 192x192 tile and the 256-row
-        // weight-gradient tile with the fused bias gradient
-        constexpr int NB = (F8 || S::KG == 2 || (BIAS_GRAD && S::WAVES == 8)) ? 1 : 2;
+        // two slices per K step), the K-grouped 192x192 tile, the 256-row
+        // weight-gradient tile with the fused bias gradient and the 384x192
+        // tile (96 x 96 patches: 144 accumulator registers)
+        constexpr int NB = (F8 || S::KG == 2 || (BIAS_GRAD && S::WAVES == 8) || BM == 384) ? 1 : 2;
         Frag a[NB][FM], b[NB][FN];
 #pragma unroll
         for (int i = 0; i < FM; ++i) a[0][i] = frag_a(i, kg * KK);
@@ -976,6 +977,14 @@ Plan plan_bf16(int epi, int M, int N, int K, bool a_kmajor, bool b_kmajor) {
     best.k_per_split = kt * kBK;
     return best;
   }
+  // Plain stores with N a multiple of 192 (the N = 768 products' dX):
+  // 384x192 tiles of 8 waves (4 x 2 patches of 96 x 96), 64 x 4 = 256 tiles
+  // at M = 24576, one round, and a third less operand traffic per product
+  // than 192x192
+  if (!may_split && epi == EPI_STORE && a_kmajor && b_kmajor && N % 192 == 0 && M >= 8192) {
+    best = Plan{384, 192, 1, kt * kBK};
+    return best;
+  }
   for (const Cand& c : cands) {
     const bool c192 = c.bm == 192;
     if (c192 && !(a_kmajor && b_kmajor)) continue;                  // m-major DMA needs 64 | 1024 / (2 R)
@@ -1088,6 +1097,8 @@ int launch_mfma(const MfmaArgs& a, const Plan& pl, hipStream_t stream) {
   if (pl.bm == 256 && pl.bn == 256) return launch_tile<256, 256, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
   if (pl.bm == 256 && pl.bn == 128) return launch_tile<256, 128, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
   if (pl.bm == 128 && pl.bn == 256) return launch_tile<128, 256, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
+  if constexpr (A_KMAJ && B_KMAJ && !BIAS_GRAD && EPI == EPI_STORE)
+    if (pl.bm == 384 && pl.bn == 192) return launch_tile<384, 192, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
   if constexpr (A_KMAJ && B_KMAJ)
     if (pl.bm == 192 && pl.bn == 192) {
       if constexpr (!BIAS_GRAD && !epi_has_aux(EPI))
