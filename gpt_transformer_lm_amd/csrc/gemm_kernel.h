@@ -371,7 +371,11 @@ struct DmaShape {
   static constexpr int AUX_BYTES = EP_BYTES > RED_BYTES ? EP_BYTES : RED_BYTES;
   static constexpr int SUB_BYTES = BM * 128;              // [BM][64] bf16 sub-tile of the epilogue input
   static constexpr int PER_STAGE = STAGE_BYTES / SUB_BYTES;
-  static constexpr int AUX_STAGES = HAS_AUX ? (BN / 64 + PER_STAGE - 1) / PER_STAGE : 0;
+  // 384x192: the epilogue input tile (144 KiB) would not fit beside the ring;
+  // each wave loads its share straight into registers after the main loop
+  // (the fragment registers are free by then)
+  static constexpr bool AUX_DIRECT = HAS_AUX && BM == 384;
+  static constexpr int AUX_STAGES = HAS_AUX && !AUX_DIRECT ? (BN / 64 + PER_STAGE - 1) / PER_STAGE : 0;
   static constexpr int LDS_LIMIT = 160 * 1024 - 2 * BN * 4 - 1024;   // two bias buffers
   static constexpr bool fits(int n) {
     return AUX_STAGES <= n && n * STAGE_BYTES + (AUX_STAGES < n ? 0 : AUX_BYTES) <= LDS_LIMIT;
@@ -384,7 +388,7 @@ struct DmaShape {
   static constexpr bool EPI_IN_STAGE = AUX_STAGES < NS && AUX_BYTES <= STAGE_BYTES;
   // The epilogue input tile can be loaded during the last K step (into the
   // stages that step does not read) when it leaves one stage free.
-  static constexpr bool EARLY_AUX = HAS_AUX && AUX_STAGES < NS;
+  static constexpr bool EARLY_AUX = HAS_AUX && !AUX_DIRECT && AUX_STAGES < NS;
 };
 
 // F8: both operands fp8 (OCP formats; B E4M3, A E4M3 or, with FMT_A = 1,
@@ -632,6 +636,28 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   }
   // bias and epilogue input visible; every wave done with the stage buffers reused below
   if constexpr (HAS_BIAS || HAS_AUX || S::EPI_IN_STAGE) __syncthreads();
+  // AUX_DIRECT: this wave's part of the epilogue input (the two 16-byte runs
+  // per lane of each 32 x 32 block, as the epilogue below reads them), all in
+  // flight at once; out-of-range runs read zeros through the buffer range
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 auxr[S::AUX_DIRECT ? FM : 1][S::AUX_DIRECT ? FN : 1][2];
+  if constexpr (S::AUX_DIRECT) {
+    if (vec) {
+      const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.e.aux_in, p.aux_bytes);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int idx = lane + 64 * q, rl = idx >> 2, cc = idx & 3;
+            const int grow = m0 + wm * WM + i * 32 + rl, gcol = n0 + wn * WN + j * 32 + cc * 8;
+            const uint32_t off = grow < p.M && gcol < p.N ? (uint32_t)(((int64_t)grow * p.e.ld_aux + gcol) * 2)
+                                                          : kOutOfRange;
+            auxr[i][j][q] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+          }
+    }
+  }
   typedef float f32x4 __attribute__((ext_vector_type(4)));
   if constexpr (S::KG == 2) {
     // The second K-group's sums go through the idle stage buffers, one 4 KiB
@@ -693,7 +719,7 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   GPT2_LDS char* epi_lds =
       S::EPI_IN_STAGE ? stage_ptr(S::EARLY_AUX ? s_last : NS - 1) : (GPT2_LDS char*)epi_own;
   auto aux_stage = [&](int j) { return S::EARLY_AUX ? stage_ptr((s_last + 1 + j) % NS) : stage_ptr(j); };
-  if constexpr (HAS_AUX && !S::EARLY_AUX) {
+  if constexpr (HAS_AUX && !S::EARLY_AUX && !S::AUX_DIRECT) {
     if (vec) {
       issue_aux([&](int j) { return stage_ptr(j); });
       wait_vmcnt<0>();
@@ -739,10 +765,14 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
                 for (int e = 0; e < 8; ++e) v[e] += bias_s[bp][tc + e];
               }
               if constexpr (HAS_AUX) {
-                const int sb = tc >> 6, ch = (tc & 63) >> 3;
-                const GPT2_LDS char* t = aux_stage(sb / PER_STAGE) + (sb % PER_STAGE) * SUB_BYTES;
-                typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-                const u32x4 raw = *reinterpret_cast<const GPT2_LDS u32x4*>(t + tr * 128 + swz(tr, ch) * 16);
+                u32x4 raw;
+                if constexpr (S::AUX_DIRECT) {
+                  raw = auxr[i][j][q];
+                } else {
+                  const int sb = tc >> 6, ch = (tc & 63) >> 3;
+                  const GPT2_LDS char* t = aux_stage(sb / PER_STAGE) + (sb % PER_STAGE) * SUB_BYTES;
+                  raw = *reinterpret_cast<const GPT2_LDS u32x4*>(t + tr * 128 + swz(tr, ch) * 16);
+                }
                 const uint32_t w[4] = {raw[0], raw[1], raw[2], raw[3]};
                 float x[8];
 #pragma unroll
@@ -977,11 +1007,13 @@ Plan plan_bf16(int epi, int M, int N, int K, bool a_kmajor, bool b_kmajor) {
     best.k_per_split = kt * kBK;
     return best;
   }
-  // Plain stores with N a multiple of 192 (the N = 768 products' dX):
-  // 384x192 tiles of 8 waves (4 x 2 patches of 96 x 96), 64 x 4 = 256 tiles
-  // at M = 24576, one round, and a third less operand traffic per product
-  // than 192x192
-  if (!may_split && epi == EPI_STORE && a_kmajor && b_kmajor && N % 192 == 0 && M >= 8192) {
+  // Plain stores and (past the short-K rule above) residual adds with N a
+  // multiple of 192 (the N = 768 products' dX, the fc-proj forward): 384x192
+  // tiles of 8 waves (4 x 2 patches of 96 x 96), 64 x 4 = 256 tiles at
+  // M = 24576, one round, and a third less operand traffic per product than
+  // 192x192; the residual tile goes straight to registers after the main loop
+  if (!may_split && (epi == EPI_STORE || epi == EPI_BIAS_RES) && a_kmajor && b_kmajor && N % 192 == 0 &&
+      M >= 8192) {
     best = Plan{384, 192, 1, kt * kBK};
     return best;
   }
@@ -1097,7 +1129,7 @@ int launch_mfma(const MfmaArgs& a, const Plan& pl, hipStream_t stream) {
   if (pl.bm == 256 && pl.bn == 256) return launch_tile<256, 256, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
   if (pl.bm == 256 && pl.bn == 128) return launch_tile<256, 128, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
   if (pl.bm == 128 && pl.bn == 256) return launch_tile<128, 256, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
-  if constexpr (A_KMAJ && B_KMAJ && !BIAS_GRAD && EPI == EPI_STORE)
+  if constexpr (A_KMAJ && B_KMAJ && !BIAS_GRAD && (EPI == EPI_STORE || EPI == EPI_BIAS_RES))
     if (pl.bm == 384 && pl.bn == 192) return launch_tile<384, 192, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
   if constexpr (A_KMAJ && B_KMAJ)
     if (pl.bm == 192 && pl.bn == 192) {
