@@ -14,6 +14,8 @@ namespace {
 
 template <int EPI, int FMT_A>
 int launch_f8(const MfmaArgs& a, const Plan& pl, hipStream_t s) {
+  if constexpr (EPI == EPI_STORE || EPI == EPI_BIAS_RES)
+    if (pl.bm == 384) return launch_tile<384, 192, EPI, true, true, false, 1, true, FMT_A>(a, pl.splits, s);
   if constexpr (!epi_has_aux(EPI))
     if (pl.bm == 256) return launch_tile<256, 256, EPI, true, true, false, 1, true, FMT_A>(a, pl.splits, s);
   return launch_tile<128, 128, EPI, true, true, false, 1, true, FMT_A>(a, pl.splits, s);

@@ -1048,11 +1048,17 @@ Plan plan_bf16(int epi, int M, int N, int K, bool a_kmajor, bool b_kmajor) {
 // the weight gradient and long plain stores, by the bf16 cost model (an fp8
 // K step of 128 takes as many matrix-core cycles as a bf16 step of 64).
 // Epilogues that read an input tile (residual add, GELU' multiply) take the
-// two-block 128x128 tile, as in bf16.
+// two-block 128x128 tile, as in bf16, and the N = 768 products the 384x192
+// tile, as in bf16 (the plain-store form spills 12 registers with the larger
+// fp8 fragments and is still faster: FP8 step 27.84 -> 27.41 ms).
 Plan plan_fp8(int epi, int M, int N, int K) {
   const int kt = (int)ceil_div64(K, kBK8);
   const bool wgrad = epi == EPI_WGRAD;
   const bool may_split = wgrad || (epi == EPI_STORE && K >= 8192);
+  // as in bf16: the 8-wave 384x192 tile for N = 768 plain stores (dX) and
+  // the long-K residual add (fc-proj forward)
+  if (!may_split && (epi == EPI_STORE || (epi == EPI_BIAS_RES && K > 1024)) && N % 192 == 0 && M >= 8192)
+    return Plan{384, 192, 1, kt * kBK8};
   if (!may_split && epi_has_aux(epi)) return Plan{128, 128, 1, kt * kBK8};
   struct Cand { int bm, bn; double t_step; };
   const Cand cands[2] = {{256, 256, 2.75e-6}, {128, 128, 1.25e-6}};
