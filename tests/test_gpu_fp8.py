@@ -179,8 +179,9 @@ TINY8 = dict(V=512, Vp=512, maxT=64, L=2, H=4, C_=64, B=4, T=64)
 MID8 = dict(V=50257, Vp=50304, maxT=1024, L=2, H=12, C_=768, B=4, T=1024)
 
 
-def fp8_step_parity(c, params, tok, tgt, adam, odtype, ltol=1e-2, gtol=1e-1, ptol=3e-2):
-    cfg = lib.make_config(c["V"], c["Vp"], c["maxT"], c["L"], c["H"], c["C_"], c["B"], c["T"], lib.GPT2_BF16_FP8)
+def fp8_step_parity(c, params, tok, tgt, adam, odtype, ltol=1e-2, gtol=1e-1, ptol=3e-2, arch=0):
+    cfg = lib.make_config(c["V"], c["Vp"], c["maxT"], c["L"], c["H"], c["C_"], c["B"], c["T"], lib.GPT2_BF16_FP8,
+                          arch)
     model = lib.Model(cfg, seed=0)
     model.set_params(lib.flatten_params(cfg, params))
     loss = model.forward(dev_i32(tok), dev_i32(tgt))
@@ -190,7 +191,8 @@ def fp8_step_parity(c, params, tok, tgt, adam, odtype, ltol=1e-2, gtol=1e-1, pto
     after = lib.unflatten(cfg, model.get_params())
     model.close()
     oc = O.OracleConfig(vocab_size=c["V"], max_seq_len=c["maxT"], num_layers=c["L"], num_heads=c["H"],
-                        channels=c["C_"], fp8=True)
+                        channels=c["C_"], fp8=True, relu2=bool(arch & lib.GPT2_ARCH_RELU2),
+                        qk_norm=bool(arch & lib.GPT2_ARCH_QK_NORM), rope=bool(arch & lib.GPT2_ARCH_ROPE))
     op = {k: v.astype(odtype) for k, v in params.items()}
     op["wte"] = op["wte"][: c["V"]].copy()
     oloss, ograds, oafter, _ = O.gpt2_step(op, tok, tgt, oc, None, adam["lr"], adam["beta1"], adam["beta2"],
@@ -216,6 +218,17 @@ def test_tiny_fp8_step_parity():
                     np.float64)
 
 
+def test_tiny_fp8_variant_step_parity():
+    # ReLU^2 (its fp8 epilogue takes the maximum of relu^2), QK-Norm and
+    # rotary embeddings (the QK transform rewrites dq, dk after the attention
+    # backward, so dQKV's maximum comes from a pass of its own)
+    say("tiny fp8 step, all variants")
+    params = S.random_params(512, 512, 64, 2, 64, seed=1411, perturbed=True)
+    tok, tgt = S.uniform_batch(4, 64, 512, seed=1412)
+    fp8_step_parity(TINY8, params, tok, tgt, dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0),
+                    np.float64, arch=lib.GPT2_ARCH_RELU2 | lib.GPT2_ARCH_QK_NORM | lib.GPT2_ARCH_ROPE)
+
+
 def test_mid_fp8_step_parity():
     say("mid fp8 step (124M widths, L = 2, B = 4, T = 1024)")
     c = MID8
@@ -223,3 +236,30 @@ def test_mid_fp8_step_parity():
     tok, tgt = S.zipf_batch(c["B"], c["T"], seed=1502)
     fp8_step_parity(c, params, tok, tgt, dict(lr=6e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1),
                     np.float32)
+
+
+def test_fp8_weight_scales_after_update_match_fresh_quantisation():
+    # After an update the fp8 weight codes are quantised with the maxima the
+    # AdamW tiles took; a model given the same parameters quantises them with
+    # a pass of its own.  The maxima are exact either way, so the next
+    # forward must give the same loss bit for bit (two steps, so the second
+    # update starts from slots the first one used).
+    say("fp8 weight scales after AdamW")
+    c = TINY8
+    cfg = lib.make_config(c["V"], c["Vp"], c["maxT"], c["L"], c["H"], c["C_"], c["B"], c["T"], lib.GPT2_BF16_FP8)
+    params = S.random_params(c["V"], c["Vp"], c["maxT"], c["L"], c["C_"], seed=1601, perturbed=True)
+    tok, tgt = S.uniform_batch(c["B"], c["T"], c["V"], seed=1602)
+    a = lib.Model(cfg, seed=0)
+    a.set_params(lib.flatten_params(cfg, params))
+    for t in (1, 2):
+        a.forward(dev_i32(tok), dev_i32(tgt))
+        a.backward()
+        a.adamw_step(1e-2, 0.9, 0.999, 1e-8, 0.1, t)
+    loss_a = a.forward(dev_i32(tok), dev_i32(tgt))
+    b = lib.Model(cfg, seed=0)
+    b.set_params(a.get_params())
+    loss_b = b.forward(dev_i32(tok), dev_i32(tgt))
+    a.close()
+    b.close()
+    say("losses", loss_a, loss_b)
+    assert loss_a == loss_b
