@@ -216,3 +216,15 @@ def test_step_gemm_plans_reached_by_the_full_width_tests(size):
     for site, p in seen.items():
         o = op_plan_for_site(site, k["B"] * 1024, k["C_"], 50304)
         assert tuple(o[x] for x in PLAN_KEYS) == tuple(p[x] for x in PLAN_KEYS), (site, o, p)
+
+
+def test_ragged_384x192_test_shapes_reach_that_tile():
+    """test_linear_384x192_ragged_rows (GPU) runs the 8-wave 384x192 tile:
+    its forward with and without the residual, and its backward's dX."""
+    from gpt_transformer_lm_amd import lib
+    M, N, K = 8392, 768, 1096
+    for kw in (dict(), dict(bias=True, residual=True)):
+        p = lib.op_linear_plans(1, M, N, K, **kw)[0]
+        assert (p["tile_m"], p["tile_n"], p["waves"], p["k_splits"]) == (384, 192, 8, 1), (kw, p)
+    p = lib.op_linear_plans(1, M, K, N, db=True)[2]     # dX: M x 768, reduced over 1096
+    assert (p["N"], p["tile_m"], p["tile_n"], p["waves"]) == (N, 384, 192, 8), p

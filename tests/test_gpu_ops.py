@@ -68,6 +68,35 @@ def test_linear_forward(dtype, M, N, K, epi):
         assert rel(host(g), O.gelu_tanh_backward(ref, np.ones_like(ref))) < TOL_OUT[dtype]
 
 
+@pytest.mark.parametrize("epi", ["store", "bias_res"])
+def test_linear_384x192_ragged_rows(epi):
+    """The 8-wave 384x192 tile (plain stores and residual adds with N a
+    multiple of 192 and M >= 8192) with a partial last row tile and a partial
+    last K step; the residual comes straight to registers after the main
+    loop.  Its backward: dX of an N = 768 input layer on the same tile."""
+    M, N, K = 8392, 768, 1096   # (test_abi_host checks these reach the 384x192 plans)
+    say("linear 384x192", epi, M, N, K)
+    r = rng(M + N + K + len(epi))
+    x, W = r.standard_normal((M, K)), r.standard_normal((N, K)) * 0.1
+    b, res = r.standard_normal(N) * 0.5, r.standard_normal((M, N))
+    xi, Wi, bi, ri = (as_input(a, BF16).astype(np.float64) for a in (x, W, b, res))
+    y = empty((M, N), BF16)
+    lib.linear_forward(BF16, dev(x, BF16), dev(W, BF16), b=None if epi == "store" else dev(b, BF16),
+                       residual=dev(res, BF16) if epi == "bias_res" else None, y=y)
+    ref = O.linear_forward(xi, Wi, None if epi == "store" else bi)
+    if epi == "bias_res":
+        ref = ref + ri
+    assert rel(host(y), ref) < TOL_OUT[BF16]
+    # backward of a layer with 768 inputs and 200 outputs: dX = dY W is M x 768
+    dy, x2, W2 = r.standard_normal((M, K)), r.standard_normal((M, N)), r.standard_normal((K, N)) * 0.1
+    dx, dW, db = empty((M, N), BF16), empty32((K, N)), empty32((K,))
+    lib.linear_backward(BF16, dev(dy, BF16), dev(x2, BF16), dev(W2, BF16), dx=dx, dW=dW, db=db)
+    rdx, rdW, rdb = O.linear_backward(*(as_input(a, BF16).astype(np.float64) for a in (dy, x2, W2)))
+    assert rel(host(dx), rdx) < TOL_OUT[BF16]
+    assert rel(host(dW), rdW) < TOL_F32
+    assert rel(host(db), rdb) < TOL_F32
+
+
 @pytest.mark.parametrize("dtype", DT, ids=DTN.get)
 @pytest.mark.parametrize("M,N,K", [(96, 100, 64), (2056, 2052, 72)])
 def test_linear_forward_unaligned_columns(dtype, M, N, K):
