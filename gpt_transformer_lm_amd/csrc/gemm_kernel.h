@@ -988,9 +988,17 @@ Plan plan_bf16(int epi, int M, int N, int K, bool a_kmajor, bool b_kmajor) {
   const int def_bm = M >= 2048 ? 256 : 128, def_bn = N >= 2048 ? 256 : 128;
   Plan best{def_bm, def_bn, 1, 0};
   double best_t = 1e300;
-  // Short-K products with a bias or GELU epilogue and a wide N (QKV, fc
-  // forward): the 8-wave 256x256 tile (measured 3-5% faster than 128x128 at
-  // M = 24576, K = 768).
+  // Short-K products with a bias or GELU epilogue (QKV, fc forward): the
+  // 8-wave 384x192 tile where N is a multiple of 192 (QKV N = 2304: 768
+  // tiles, three whole rounds, against 3.4 rounds of 256x256; fc N = 3072:
+  // 1024 tiles, four rounds, against 4.5; 1.25 -> 1.16 and 2.07 -> 1.99 ms
+  // per step), else for a wide N the 8-wave 256x256 tile (measured 3-5%
+  // faster than 128x128 at M = 24576, K = 768).
+  if (!may_split && (epi == EPI_BIAS_GELU_D || epi == EPI_BIAS_RELU2_D || epi == EPI_BIAS) && a_kmajor && b_kmajor &&
+      M >= 8192 && N % 192 == 0 && K <= 1024) {
+    best = Plan{384, 192, 1, kt * kBK};
+    return best;
+  }
   if (!may_split && (epi == EPI_BIAS_GELU_D || epi == EPI_BIAS_RELU2_D || epi == EPI_BIAS) && a_kmajor && b_kmajor &&
       M >= 2048 &&
       N >= 2048 && K <= 1024) {
@@ -1135,7 +1143,9 @@ int launch_mfma(const MfmaArgs& a, const Plan& pl, hipStream_t stream) {
   if (pl.bm == 256 && pl.bn == 256) return launch_tile<256, 256, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
   if (pl.bm == 256 && pl.bn == 128) return launch_tile<256, 128, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
   if (pl.bm == 128 && pl.bn == 256) return launch_tile<128, 256, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
-  if constexpr (A_KMAJ && B_KMAJ && !BIAS_GRAD && (EPI == EPI_STORE || EPI == EPI_BIAS_RES))
+  if constexpr (A_KMAJ && B_KMAJ && !BIAS_GRAD &&
+                (EPI == EPI_STORE || EPI == EPI_BIAS_RES || EPI == EPI_BIAS || EPI == EPI_BIAS_GELU_D ||
+                 EPI == EPI_BIAS_RELU2_D))
     if (pl.bm == 384 && pl.bn == 192) return launch_tile<384, 192, EPI, A_KMAJ, B_KMAJ, BIAS_GRAD>(a, pl.splits, stream);
   if constexpr (A_KMAJ && B_KMAJ)
     if (pl.bm == 192 && pl.bn == 192) {
