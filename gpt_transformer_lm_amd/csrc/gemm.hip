@@ -102,10 +102,12 @@ int gemm(const GemmDesc& d, hipStream_t stream) {
 
   int rc = 0;
   if (d.amax && !d.fp8) return gpt2_internal_fail(1, "gemm: the output maximum is taken only by fp8 products");
-  if (d.fp8 && (d.dtype != BF16 || !d.a_kmajor || !d.b_kmajor || !d.scale_a || !d.scale_b || d.K % 16 ||
-                d.lda % 16 || d.ldb % 16 || d.fp8 > 2 || (wgrad && d.bias_grad32)))
-    return gpt2_internal_fail(1, "gemm(fp8): needs bf16 outputs, k-major A and B, K and row strides multiples of "
-                                 "16, both scales, and no fused bias gradient");
+  if (d.fp8 && (d.dtype != BF16 || !d.scale_a || !d.scale_b || d.K % 16 || d.lda % 16 || d.ldb % 16 || d.fp8 > 2 ||
+                (wgrad && d.bias_grad32) || (d.a_kmajor != d.b_kmajor) || (!d.a_kmajor && !wgrad) ||
+                (!d.a_kmajor && (d.M % 16 || d.N % 16))))
+    return gpt2_internal_fail(1, "gemm(fp8): needs bf16 outputs, K and row strides multiples of 16, both scales, no "
+                                 "fused bias gradient, and both operands k-major (or, for a weight gradient, both "
+                                 "m-major with M and N multiples of 16)");
   if (d.dtype == BF16) {
     // shape contract of the MFMA kernel: K a multiple of 8, 16-byte aligned rows,
     // contiguous axis of m-/n-major operands a multiple of 8.
@@ -141,7 +143,7 @@ int gemm(const GemmDesc& d, hipStream_t stream) {
     const bool bias_grad = wgrad && d.bias_grad32 != nullptr;
     if (bias_grad && d.a_kmajor)
       return gpt2_internal_fail(1, "gemm: fused bias gradient needs an m-major A");
-    if (d.fp8) rc = gemm_fp8_launch(split_store ? EPI_WGRAD : d.epi, d.fp8 - 1, a, pl, stream);
+    if (d.fp8) rc = gemm_fp8_launch(split_store ? EPI_WGRAD : d.epi, d.fp8 - 1, d.a_kmajor, a, pl, stream);
     else switch (split_store ? EPI_WGRAD : d.epi) {
       case EPI_STORE: rc = dispatch_layout_bf16<EPI_STORE>(d, a, pl, false, stream); break;
       case EPI_BIAS: rc = dispatch_layout_bf16<EPI_BIAS>(d, a, pl, false, stream); break;

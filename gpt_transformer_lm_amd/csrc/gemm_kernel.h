@@ -80,8 +80,9 @@ struct Plan {
 
 // Launches the fp8 kernel for a planned product (gemm_fp8.hip): epi is the
 // epilogue the kernel runs (EPI_WGRAD for split-K partials), fmt_a the format
-// of A (0: E4M3, 1: E5M2).
-int gemm_fp8_launch(int epi, int fmt_a, const MfmaArgs& a, const Plan& pl, hipStream_t stream);
+// of A (0: E4M3, 1: E5M2), kmajor whether both operands are k-major (else
+// both m-major: weight gradients from the row-major codes).
+int gemm_fp8_launch(int epi, int fmt_a, bool kmajor, const MfmaArgs& a, const Plan& pl, hipStream_t stream);
 
 namespace {
 
@@ -224,28 +225,40 @@ __device__ __forceinline__ void block_units(int total, bool persistent, int& u, 
 // 16-byte run each lane fetches).
 //  * k-major operand (k contiguous in memory): [row][64 k], 128-byte rows whose
 //    16-byte chunks are XOR-swizzled by row; fragments are ds_read_b128.
-//  * m-major operand (m contiguous in memory): [k][R m], 2R-byte rows whose
-//    16-byte chunk index is XORed with 4 (k & 3), so the 4 x 64 bytes that one
-//    transposing read takes from k rows 4j .. 4j + 3 cover all 64 banks; fragments are two
-//    ds_read_b64_tr_b16 (the transpose read hands lane j of each 16-lane group
-//    element j%4 of the 8-byte runs of lanes j/4 + 4e, so with the per-lane
-//    addresses below every lane ends up with 8 consecutive k of one m).
+//  * m-major operand (m contiguous in memory): [k][R m], R * ES-byte rows
+//    whose 16-byte chunk index is XORed with mswz(k): bf16 4 (k & 3), so the
+//    4 x 64 bytes that one transposing read takes from k rows 4j .. 4j + 3
+//    cover all 64 banks; fragments are two ds_read_b64_tr_b16 (the transpose
+//    read hands lane j of each 16-lane group element j%4 of the 8-byte runs
+//    of lanes j/4 + 4e, so with the per-lane addresses below every lane ends
+//    up with 8 consecutive k of one m).  fp8 (k & 7), so the 8 x 16 bytes one
+//    16-lane group of a ds_read_b64_tr_b8 takes from k rows 8j .. 8j + 7 sit
+//    in 8 distinct bank groups; fragments are four such reads (that read
+//    hands lane j of each 16-lane group byte j%8 of the 8-byte runs of lanes
+//    2e + j/8, e = 0..7: 8 consecutive k of one m when lanes 2e and 2e + 1
+//    address the two halves of the same 16 columns of k row e).
 template <int R, bool KMAJ, int WAVES, int ES = 2>
 struct DmaTile {
-  // ES: bytes per element (2: bf16, 1: fp8, k-major only); a K step is
-  // always 128 bytes of every row
-  static_assert(ES == 2 || (ES == 1 && KMAJ), "fp8 operand tiles are k-major");
+  // ES: bytes per element (2: bf16, 1: fp8); a K step is always 128 bytes of
+  // every k-major row (64 bf16 / 128 fp8 k), i.e. 64 (bf16) or 128 (fp8)
+  // m-major k rows
+  static_assert(ES == 2 || ES == 1, "bf16 or fp8 operand tiles");
   static constexpr int BYTES = R * 128;
   static constexpr int NINST = BYTES / 1024 / WAVES;      // 1 KiB instructions per wave
+  // m-major: chunk swizzle of k row k, lanes per k row, k rows per DMA instruction
+  __device__ __forceinline__ static int mswz(int k) { return ES == 2 ? ((k & 3) << 2) : (k & 7); }
+  static constexpr int MLPR = R * ES / 16;
+  static constexpr int MRPI = 1024 / (R * ES);
 
   // Per-lane part of the DMA source addresses (two registers per operand); the
   // rest of each instruction's address is wave-uniform.
   //  k-major: instruction q of wave w covers tile rows 8 (w NINST + q) + lane/8,
   //    physical chunk lane%8; the swizzle (row ^ row>>3) & 7 splits into
   //    lane/8 (per lane) xor (w NINST + q) & 7 (uniform).
-  //  m-major: instruction q covers k rows qk + lane / (R/8) with
-  //    qk = (w NINST + q) * 1024 / (2R), physical chunk lane % (R/8); the
-  //    swizzle ((k & 3) << 2) splits the same way.
+  //  m-major: instruction q covers k rows qk + lane / MLPR with
+  //    qk = (w NINST + q) * MRPI, physical chunk lane % MLPR; the swizzle
+  //    mswz(qk + kr) = mswz(qk) ^ mswz(kr) (MRPI is a power of two above kr)
+  //    splits the same way.
   struct Lane {
     uint32_t base;    // bytes: row part (k-major) / row-in-group + column part (m-major)
     uint32_t c16;     // 16 * (per-lane part of the logical chunk index)
@@ -259,10 +272,9 @@ struct DmaTile {
       L.c16 = (uint32_t)(c * 16);
       L.sub = c;
     } else {
-      constexpr int LPR = R / 8;                       // lanes per k row
-      const int kr = lane / LPR, phys = lane % LPR;
-      const int c = phys ^ ((kr & 3) << 2);
-      L.base = (uint32_t)((int64_t)kr * ld * 2 + (int64_t)row0 * 2);
+      const int kr = lane / MLPR, phys = lane % MLPR;
+      const int c = phys ^ mswz(kr);
+      L.base = (uint32_t)((int64_t)kr * ld * ES + (int64_t)row0 * ES);
       L.c16 = (uint32_t)(c * 16);
       L.sub = kr;
     }
@@ -286,10 +298,9 @@ struct DmaTile {
         off = L.base + (uint32_t)q * (uint32_t)(8 * ld * ES) + (uint32_t)(k0 * ES) + c16;
         if (k_tail) ok = k0 + (int)(c16 >> 4) * (16 / ES) < K;
       } else {
-        constexpr int RPI = 1024 / (2 * R);              // k rows per instruction
-        const int qk = iq * RPI;
-        const uint32_t u16 = (uint32_t)((((qk & 3) << 2) & 12) * 16);
-        off = L.base + (uint32_t)((int64_t)(k0 + qk) * ld * 2) + (L.c16 ^ u16);
+        const int qk = iq * MRPI;
+        const uint32_t u16 = (uint32_t)(mswz(qk) * 16);
+        off = L.base + (uint32_t)((int64_t)(k0 + qk) * ld * ES) + (L.c16 ^ u16);
         if (k_tail) ok = k0 + qk + L.sub < K;
       }
       dma_lds16(rs, (GPT2_LDS void*)(tile + iq * 1024), ok ? off : kOutOfRange);
@@ -304,26 +315,44 @@ struct DmaTile {
     if constexpr (KMAJ) {
       off = L.base + (uint32_t)q * (uint32_t)(8 * ld * ES) + (uint32_t)(k0 * ES) + (L.c16 ^ (uint32_t)((iq & 7) * 16));
     } else {
-      constexpr int RPI = 1024 / (2 * R);
-      const int qk = iq * RPI;
-      off = L.base + (uint32_t)((int64_t)(k0 + qk) * ld * 2) + (L.c16 ^ (uint32_t)((((qk & 3) << 2) & 12) * 16));
+      const int qk = iq * MRPI;
+      off = L.base + (uint32_t)((int64_t)(k0 + qk) * ld * ES) + (L.c16 ^ (uint32_t)(mswz(qk) * 16));
     }
     dma_lds16(rs, (GPT2_LDS void*)(tile + iq * 1024), off);
   }
 
   // fp8 MFMA operand fragment (v_mfma_scale_f32_32x32x64_f8f6f4): rows
-  // [rbase, rbase + 32), k64 step kk (0 or 1 of the 128-byte row); lane l
-  // receives row rbase + l%32, k = 64 kk + 32 (l/32) + 0..31 (32 bytes, two
-  // swizzled 16-byte chunks).
+  // [rbase, rbase + 32), k64 step kk (0 or 1 of the K step); lane l receives
+  // row rbase + l%32, k = 64 kk + 32 (l/32) + 0..31 (32 bytes: two swizzled
+  // 16-byte chunks of a k-major row, or four transposing reads of an m-major
+  // tile).
   __device__ __forceinline__ static i32x8 frag8(const GPT2_LDS char* tile, int rbase, int kk, int lane) {
     static_assert(ES == 1, "fp8 fragments");
-    typedef int i32x4 __attribute__((ext_vector_type(4)));
-    const int row = rbase + (lane & 31), c = kk * 4 + (lane >> 5) * 2;
-    const i32x4 lo = *reinterpret_cast<const GPT2_LDS i32x4*>(tile + row * 128 + swz(row, c) * 16);
-    const i32x4 hi = *reinterpret_cast<const GPT2_LDS i32x4*>(tile + row * 128 + swz(row, c + 1) * 16);
     i32x8 out;
+    if constexpr (KMAJ) {
+      typedef int i32x4 __attribute__((ext_vector_type(4)));
+      const int row = rbase + (lane & 31), c = kk * 4 + (lane >> 5) * 2;
+      const i32x4 lo = *reinterpret_cast<const GPT2_LDS i32x4*>(tile + row * 128 + swz(row, c) * 16);
+      const i32x4 hi = *reinterpret_cast<const GPT2_LDS i32x4*>(tile + row * 128 + swz(row, c + 1) * 16);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { out[e] = lo[e]; out[4 + e] = hi[e]; }
+      for (int e = 0; e < 4; ++e) { out[e] = lo[e]; out[4 + e] = hi[e]; }
+    } else {
+      // lane l = 16 g + j provides the run of k row 8 t + j/2 (of its half of
+      // the k64 step) at columns m .. m + 7 and receives 8 consecutive k of
+      // column rbase + l%32, four times
+      typedef int i32x2 __attribute__((ext_vector_type(2)));
+      const int g = lane >> 4, j = lane & 15;
+      const int m = rbase + 16 * (g & 1) + 8 * (j & 1);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int kr = 64 * kk + 32 * (g >> 1) + 8 * t + (j >> 1);
+        const int c = (m >> 4) ^ mswz(kr);
+        const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            const_cast<GPT2_LDS i32x2*>(reinterpret_cast<const GPT2_LDS i32x2*>(tile + kr * R + c * 16 + (m & 15))));
+        out[2 * t] = v[0];
+        out[2 * t + 1] = v[1];
+      }
+    }
     return out;
   }
 
@@ -405,7 +434,7 @@ void gemm_bf16_dma_kernel(MfmaArgs p) {
   using S = DmaShape<BM, BN, EPI, KGS>;
   constexpr int ES = F8 ? 1 : 2;                          // bytes per operand element
   constexpr int KE = F8 ? kBK8 : kBK;                      // K elements per step
-  static_assert(!F8 || (A_KMAJ && B_KMAJ && !BIAS_GRAD && KGS == 1), "fp8: k-major operands, one K-group");
+  static_assert(!F8 || (!BIAS_GRAD && KGS == 1), "fp8: one K-group, bias gradient taken by the quantisation");
   using TA = DmaTile<BM, A_KMAJ, S::WAVES, ES>;
   using TB = DmaTile<BN, B_KMAJ, S::WAVES, ES>;
   constexpr int NT = S::NT;

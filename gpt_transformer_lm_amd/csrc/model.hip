@@ -212,7 +212,7 @@ struct LayerOffsets {
   size_t g;   // activation of the fc pre-activation (GELU or relu^2)
   size_t qk_rstd;   // QK-Norm: 1 / rms of every q and k head vector [BT, 2H] fp32 (0 if unused)
   // fp8 mode: codes of the fp8 products' inputs, row-major (q) and transposed (qt)
-  size_t ln1_q, ln1_qt, ln2_q, ln2_qt, g_q, g_qt;
+  size_t ln1_q, ln2_q, g_q;
 };
 
 // fp8 mode: the weight tensors of the fp8 products (token table, W_qkv, W_fc,
@@ -243,10 +243,12 @@ struct Layout {
   size_t sorted_keys;                    // encoder-backward key sort (computed during the forward)
   size_t rope_cs;                        // rotary embedding cos / sin table [maxT][hd/2] (0 if unused)
   // fp8 mode (0 otherwise): weight codes per parameter tensor (row-major and
-  // transposed, all layers), lnf codes, the current output gradient's codes,
+  // transposed, all layers), lnf codes, the current output gradient's codes
+  // (row-major only: the weight-gradient products read activation and
+  // gradient codes m-major),
   // per-tensor scales, absmax partials, the maxima producer kernels leave
   // (kAmaxWays slots, kAmaxStride floats apart, per scale slot)
-  size_t wq[16], wqt[16], lnf_q, lnf_qt, dq, dqt, fp8_scales, fp8_amax, fp8_colsum, fp8_slot_max;
+  size_t wq[16], wqt[16], lnf_q, dq, fp8_scales, fp8_amax, fp8_colsum, fp8_slot_max;
   size_t scratch_bytes;
   size_t total;
 };
@@ -320,11 +322,8 @@ void make_layout(const gpt2_config& c, Layout* lo) {
     o.qk_rstd = (c.arch_flags & GPT2_ARCH_QK_NORM) ? p.alloc((size_t)BT * 2 * c.num_heads * 4) : 0;
     const bool f8 = c.dtype == GPT2_BF16_FP8;
     o.ln1_q = f8 ? p.alloc(BT * C) : 0;
-    o.ln1_qt = f8 ? p.alloc(BT * C) : 0;
     o.ln2_q = f8 ? p.alloc(BT * C) : 0;
-    o.ln2_qt = f8 ? p.alloc(BT * C) : 0;
     o.g_q = f8 ? p.alloc(BT * 4 * C) : 0;
-    o.g_qt = f8 ? p.alloc(BT * 4 * C) : 0;
   }
   lo->lnf = p.alloc(BT * C * es);
   lo->lnf_mean = p.alloc(BT * 4);
@@ -344,7 +343,7 @@ void make_layout(const gpt2_config& c, Layout* lo) {
                     ? p.alloc((size_t)c.max_seq_len * (c.channels / c.num_heads / 2) * sizeof(float2))
                     : 0;
   for (int i = 0; i < 16; ++i) lo->wq[i] = lo->wqt[i] = 0;
-  lo->lnf_q = lo->lnf_qt = lo->dq = lo->dqt = lo->fp8_scales = lo->fp8_amax = lo->fp8_colsum = lo->fp8_slot_max = 0;
+  lo->lnf_q = lo->dq = lo->fp8_scales = lo->fp8_amax = lo->fp8_colsum = lo->fp8_slot_max = 0;
   if (c.dtype == GPT2_BF16_FP8) {
     for (int i : kFp8Weights) {
       const int64_t* sh = lo->pt.shape[i];
@@ -352,10 +351,8 @@ void make_layout(const gpt2_config& c, Layout* lo) {
       lo->wqt[i] = p.alloc((size_t)sh[0] * sh[1] * sh[2]);
     }
     lo->lnf_q = p.alloc(BT * C);
-    lo->lnf_qt = p.alloc(BT * C);
     const size_t big = BT * std::max<size_t>((size_t)c.padded_vocab_size, 4 * C);   // the largest output gradient
     lo->dq = p.alloc(big);
-    lo->dqt = p.alloc(big);
     lo->fp8_scales = p.alloc((size_t)fp8_slots((int)L) * sizeof(Fp8Scale));
     lo->fp8_amax = p.alloc(fp8_scale_workspace_bytes());
     lo->fp8_colsum = p.alloc(fp8_colsum_bytes((int)BT, 4 * C));
@@ -608,14 +605,15 @@ GemmDesc fp8_dx(gpt2_model* m, int M, int N, int K, const uint8_t* dq, int ds, c
   return d;
 }
 
-// dW [N, K] (+)= dY^T X from the transposed codes dqt [N, M] (slot ds) and
-// xqt [K, M] (slot xs); the bias gradient is taken separately.
-GemmDesc fp8_dw(gpt2_model* m, int M, int N, int K, const uint8_t* dqt, int ds, const uint8_t* xqt, int xs, float* dW,
+// dW [N, K] (+)= dY^T X from the row-major codes dq [M, N] (slot ds) and
+// xq [M, K] (slot xs), read m-major (no transposed copies); the bias
+// gradient is taken separately.
+GemmDesc fp8_dw(gpt2_model* m, int M, int N, int K, const uint8_t* dq, int ds, const uint8_t* xq, int xs, float* dW,
                 bool acc) {
   GemmDesc d = gdesc(GPT2_BF16);
-  d.a_kmajor = d.b_kmajor = true;
+  d.a_kmajor = d.b_kmajor = false;
   d.M = N; d.N = K; d.K = M;
-  d.A = dqt; d.lda = M; d.B = xqt; d.ldb = M;
+  d.A = dq; d.lda = N; d.B = xq; d.ldb = K;
   d.epi = EPI_WGRAD; d.out32 = dW; d.accumulate = acc;
   d.workspace = m->scratch(); d.workspace_bytes = m->lo.scratch_bytes;
   d.fp8 = 2;
@@ -680,7 +678,7 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets, f
                             m->lparam(5, l), nullptr, nullptr);
       if (m->fp8()) {
         RC(fp8_quant(m, GPT2_BF16, m->at<char>(o.ln1), BT, C, 0, fp8_slot(L, Q_ACT, 0, l), m->at<uint8_t>(o.ln1_q),
-                     m->at<uint8_t>(o.ln1_qt), false, true));
+                     nullptr, false, true));
         d = fp8_fwd(m, d, m->at<uint8_t>(o.ln1_q), fp8_slot(L, Q_ACT, 0, l), m->wq(4, l), fp8_slot(L, Q_WEIGHT, 1, l));
       }
       RC(run_gemm(m, S_QKV, d));
@@ -707,7 +705,7 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets, f
                             nullptr, m->at<char>(o.u));
       if (m->fp8()) {
         RC(fp8_quant(m, GPT2_BF16, m->at<char>(o.ln2), BT, C, 0, fp8_slot(L, Q_ACT, 1, l), m->at<uint8_t>(o.ln2_q),
-                     m->at<uint8_t>(o.ln2_qt), false, true));
+                     nullptr, false, true));
         d = fp8_fwd(m, d, m->at<uint8_t>(o.ln2_q), fp8_slot(L, Q_ACT, 1, l), m->wq(10, l),
                     fp8_slot(L, Q_WEIGHT, 2, l));
         d.amax = m->slot_max(fp8_slot(L, Q_ACT, 2, l));   // g's maximum, for its quantisation below
@@ -719,7 +717,7 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets, f
                             m->at<char>(lo.resid[l + 1]), m->lparam(13, l), m->at<char>(o.h), nullptr);
       if (m->fp8()) {
         RC(fp8_quant(m, GPT2_BF16, m->at<char>(o.g), BT, 4 * C, 0, fp8_slot(L, Q_ACT, 2, l), m->at<uint8_t>(o.g_q),
-                     m->at<uint8_t>(o.g_qt), false, true));
+                     nullptr, false, true));
         d = fp8_fwd(m, d, m->at<uint8_t>(o.g_q), fp8_slot(L, Q_ACT, 2, l), m->wq(12, l),
                     fp8_slot(L, Q_WEIGHT, 3, l));
       }
@@ -736,7 +734,7 @@ int forward_impl(gpt2_model* m, const int32_t* tokens, const int32_t* targets, f
                           nullptr, nullptr);
     if (m->fp8()) {
       RC(fp8_quant(m, GPT2_BF16, m->at<char>(lo.lnf), BT, C, 0, fp8_slot(L, Q_ACT, 3, 0), m->at<uint8_t>(lo.lnf_q),
-                   m->at<uint8_t>(lo.lnf_qt), false, true));
+                   nullptr, false, true));
       d = fp8_fwd(m, d, m->at<uint8_t>(lo.lnf_q), fp8_slot(L, Q_ACT, 3, 0), m->wq(0, 0), fp8_slot(L, Q_WEIGHT, 0, 0));
     }
     RC(run_gemm(m, S_LOGITS, d));
@@ -778,14 +776,13 @@ int backward_impl(gpt2_model* m, bool acc) {
   };
 
   uint8_t* dq = m->at<uint8_t>(lo.dq);
-  uint8_t* dqt = m->at<uint8_t>(lo.dqt);
   // classifier: d_lnf = dz wte;  d_wte = dz^T lnf (overwrite; padded rows get exactly 0)
   if (m->fp8()) {
     const int gs = fp8_slot(L, Q_GRAD, 3, 0);
-    RC(fp8_quant(m, GPT2_BF16, logits, BT, Vp, 1, gs, dq, dqt, false, softmax_xent_has_amax(dt, c.vocab_size, Vp)));
+    RC(fp8_quant(m, GPT2_BF16, logits, BT, Vp, 1, gs, dq, nullptr, false, softmax_xent_has_amax(dt, c.vocab_size, Vp)));
     RC(run_gemm(m, S_CLS_DX, fp8_dx(m, BT, Vp, C, dq, gs, m->wqt(0, 0), fp8_slot(L, Q_WEIGHT, 0, 0), d_ln, EPI_STORE,
                                     nullptr)));
-    RC(run_gemm(m, S_CLS_DW, fp8_dw(m, BT, Vp, C, dqt, gs, m->at<uint8_t>(lo.lnf_qt), fp8_slot(L, Q_ACT, 3, 0),
+    RC(run_gemm(m, S_CLS_DW, fp8_dw(m, BT, Vp, C, dq, gs, m->at<uint8_t>(lo.lnf_q), fp8_slot(L, Q_ACT, 3, 0),
                                     m->lgrad(0, 0), acc)));
   } else {
     RC(run_gemm(m, S_CLS_DX, dx_desc(m, BT, Vp, C, logits, m->param(0), m->wt(0, 0), d_ln, EPI_STORE, nullptr)));
@@ -801,8 +798,8 @@ int backward_impl(gpt2_model* m, bool acc) {
     if (m->fp8()) {
       // x_{l+1} = h + g Wp^T + bp: dY = the residual gradient (bf16 copy)
       const int gp = fp8_slot(L, Q_GRAD, 0, l), gf = fp8_slot(L, Q_GRAD, 1, l);
-      RC(fp8_quant(m, GPT2_BF16, dres_t, BT, C, 1, gp, dq, dqt, true, true));
-      RC(run_gemm(m, S_FCPROJ_DW, fp8_dw(m, BT, C, 4 * C, dqt, gp, m->at<uint8_t>(o.g_qt), fp8_slot(L, Q_ACT, 2, l),
+      RC(fp8_quant(m, GPT2_BF16, dres_t, BT, C, 1, gp, dq, nullptr, true, true));
+      RC(run_gemm(m, S_FCPROJ_DW, fp8_dw(m, BT, C, 4 * C, dq, gp, m->at<uint8_t>(o.g_q), fp8_slot(L, Q_ACT, 2, l),
                                          m->lgrad(12, l), acc)));
       RC(fp8_bias_grad(m, BT, C, m->lgrad(13, l), acc));
       // du = (dy W_p) * GELU'(u), the derivative saved by the forward
@@ -811,8 +808,8 @@ int backward_impl(gpt2_model* m, bool acc) {
       ddx.amax = m->slot_max(gf);   // du's maximum, for its quantisation below
       RC(run_gemm(m, S_FCPROJ_DX, ddx));
       // u = ln2 Wfc^T + bfc   (d_big now holds du)
-      RC(fp8_quant(m, GPT2_BF16, d_big, BT, 4 * C, 1, gf, dq, dqt, true, true));
-      RC(run_gemm(m, S_FC_DW, fp8_dw(m, BT, 4 * C, C, dqt, gf, m->at<uint8_t>(o.ln2_qt), fp8_slot(L, Q_ACT, 1, l),
+      RC(fp8_quant(m, GPT2_BF16, d_big, BT, 4 * C, 1, gf, dq, nullptr, true, true));
+      RC(run_gemm(m, S_FC_DW, fp8_dw(m, BT, 4 * C, C, dq, gf, m->at<uint8_t>(o.ln2_q), fp8_slot(L, Q_ACT, 1, l),
                                      m->lgrad(10, l), acc)));
       RC(fp8_bias_grad(m, BT, 4 * C, m->lgrad(11, l), acc));
       RC(run_gemm(m, S_FC_DX, fp8_dx(m, BT, 4 * C, C, dq, gf, m->wqt(10, l), fp8_slot(L, Q_WEIGHT, 2, l), d_ln,
@@ -870,8 +867,8 @@ int backward_impl(gpt2_model* m, bool acc) {
     // qkv = ln1 Wqkv^T + bqkv
     if (m->fp8()) {
       const int gq = fp8_slot(L, Q_GRAD, 2, l);
-      RC(fp8_quant(m, GPT2_BF16, d_qkv, BT, 3 * C, 1, gq, dq, dqt, true, qkv_max));
-      RC(run_gemm(m, S_QKV_DW, fp8_dw(m, BT, 3 * C, C, dqt, gq, m->at<uint8_t>(o.ln1_qt), fp8_slot(L, Q_ACT, 0, l),
+      RC(fp8_quant(m, GPT2_BF16, d_qkv, BT, 3 * C, 1, gq, dq, nullptr, true, qkv_max));
+      RC(run_gemm(m, S_QKV_DW, fp8_dw(m, BT, 3 * C, C, dq, gq, m->at<uint8_t>(o.ln1_q), fp8_slot(L, Q_ACT, 0, l),
                                       m->lgrad(4, l), acc)));
       RC(fp8_bias_grad(m, BT, 3 * C, m->lgrad(5, l), acc));
       RC(run_gemm(m, S_QKV_DX, fp8_dx(m, BT, 3 * C, C, dq, gq, m->wqt(4, l), fp8_slot(L, Q_WEIGHT, 1, l), d_ln,
@@ -1567,10 +1564,11 @@ int gpt2_op_fp8_quantize(int in_dtype, int fmt, int R, int C, const void* x, flo
 
 namespace {
 // Workspace of the op-level fp8 linear layer: 4 scales, absmax partials, the
-// codes of x, W (row-major and transposed) and dY (row-major and
-// transposed), then the products' split-K / bias-gradient scratch.
+// codes of x, W (row-major and transposed) and dY (row-major: the weight
+// gradient reads it and x's codes m-major), then the products' split-K /
+// bias-gradient scratch.
 struct OpFp8Ws {
-  size_t scales, amax, xq, xqt, wq, wqt, dq, dqt, colsum, scratch, scratch_bytes, total;
+  size_t scales, amax, xq, wq, wqt, dq, colsum, scratch, scratch_bytes, total;
 };
 OpFp8Ws op_fp8_ws(int M, int N, int K) {
   Plan p;
@@ -1578,13 +1576,11 @@ OpFp8Ws op_fp8_ws(int M, int N, int K) {
   w.scales = p.alloc(4 * sizeof(Fp8Scale));
   w.amax = p.alloc(fp8_scale_workspace_bytes());
   w.xq = p.alloc((size_t)M * K);
-  w.xqt = p.alloc((size_t)M * K);
   w.wq = p.alloc((size_t)N * K);
   w.wqt = p.alloc((size_t)N * K);
   w.dq = p.alloc((size_t)M * N);
-  w.dqt = p.alloc((size_t)M * N);
   w.colsum = p.alloc(fp8_colsum_bytes(M, N));
-  w.scratch_bytes = std::max({gemm_workspace_bytes(GPT2_BF16, EPI_WGRAD, N, K, M, true, true, 2),
+  w.scratch_bytes = std::max({gemm_workspace_bytes(GPT2_BF16, EPI_WGRAD, N, K, M, false, false, 2),
                               gemm_workspace_bytes(GPT2_BF16, EPI_STORE, M, K, N, true, true, 2),
                               gemm_workspace_bytes(GPT2_BF16, EPI_STORE, M, N, K, true, true, 1)});
   w.scratch = p.alloc(w.scratch_bytes);
@@ -1646,18 +1642,17 @@ int gpt2_op_linear_fp8_backward(int M, int N, int K, const void* dy, const void*
   Fp8Scale* sc = reinterpret_cast<Fp8Scale*>(ws + w.scales);
   float* amax = reinterpret_cast<float*>(ws + w.amax);
   uint8_t* dq = reinterpret_cast<uint8_t*>(ws + w.dq);
-  uint8_t* dqt = reinterpret_cast<uint8_t*>(ws + w.dqt);
   RC(fp8_amax(GPT2_BF16, (int64_t)M * N, dy, amax, s));
   float* colsum = db ? reinterpret_cast<float*>(ws + w.colsum) : nullptr;
-  RC(fp8_quantize(GPT2_BF16, 1, M, N, dy, N, amax, &sc[2], dq, dqt, s, colsum));
-  if (dW) {
-    uint8_t* xqt = reinterpret_cast<uint8_t*>(ws + w.xqt);
+  RC(fp8_quantize(GPT2_BF16, 1, M, N, dy, N, amax, &sc[2], dq, nullptr, s, colsum));
+  if (dW) {   // as the training step: both operands' row-major codes, read m-major
+    uint8_t* xq = reinterpret_cast<uint8_t*>(ws + w.xq);
     RC(fp8_amax(GPT2_BF16, (int64_t)M * K, x, amax, s));
-    RC(fp8_quantize(GPT2_BF16, 0, M, K, x, K, amax, &sc[0], nullptr, xqt, s));
+    RC(fp8_quantize(GPT2_BF16, 0, M, K, x, K, amax, &sc[0], xq, nullptr, s));
     GemmDesc d = gdesc(GPT2_BF16);
-    d.a_kmajor = d.b_kmajor = true;
+    d.a_kmajor = d.b_kmajor = false;
     d.M = N; d.N = K; d.K = M;
-    d.A = dqt; d.lda = M; d.B = xqt; d.ldb = M;
+    d.A = dq; d.lda = N; d.B = xq; d.ldb = K;
     d.epi = EPI_WGRAD; d.out32 = dW; d.accumulate = accumulate != 0;
     d.workspace = ws + w.scratch; d.workspace_bytes = w.scratch_bytes;
     d.fp8 = 2; d.scale_a = &sc[2].s; d.scale_b = &sc[0].s;
