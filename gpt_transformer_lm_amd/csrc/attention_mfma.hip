@@ -154,6 +154,9 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
   asm volatile("" : "+v"(x));
   return x;
 }
+// An empty asm that rewrites x: x's producers stay before this point, in
+// this block, instead of sinking towards a later use.
+__device__ __forceinline__ void pin(bf16x8& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ bf16x8 frag_at(const GPT2_LDS char* t, uint32_t off) {
   return *reinterpret_cast<const GPT2_LDS bf16x8*>(t + off);
 }
@@ -185,6 +188,21 @@ __device__ __forceinline__ void frags_global(const bf16* G, size_t ld, int row, 
 }
 
 // Index (0..31) inside a 32-slice of the row that accumulator register r holds.
+// The block's (tile, batch·head) pair, with whole heads on one XCD: the
+// dispatcher hands consecutive linear block ids to the 8 XCDs in turn, so
+// linear id n runs on XCD n % 8; renumbering n -> (n % 8) q + n / 8 (q =
+// blocks / 8, the tail of a grid that is not a multiple of 8 left as it is)
+// gives each XCD a run of consecutive ids, taken head-major, and the tiles of
+// one head re-read its K / V (or Q / dO) rows from that XCD's L2 instead of
+// from memory.  Within a head, tile 0 comes first.
+__device__ __forceinline__ void head_major_block(int& tile, int& bh) {
+  const int X = (int)gridDim.x, n = (int)(blockIdx.x + gridDim.x * blockIdx.y);
+  const int q = (int)(gridDim.x * gridDim.y) / 8;
+  const int id = n < 8 * q ? (n % 8) * q + n / 8 : n;
+  bh = id / X;
+  tile = id % X;
+}
+
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
 // Writes 64 values of row `row` held as two 32 x 32 accumulators (d on registers).
@@ -216,8 +234,10 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_mfma_kernel(int T, int H, con
   __shared__ __attribute__((aligned(1024))) char ring[NS][2 * TILE];   // K tile, V tile
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), hi = lane >> 5;
   const int nqt = (T + ROWS - 1) / ROWS;
-  const int qt = nqt - 1 - (int)blockIdx.x;
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  int tile, bh;
+  head_major_block(tile, bh);
+  const int qt = nqt - 1 - tile;   // longer rows first
+  const int b = bh / H, h = bh % H;
   const int C = H * HD;
   const int ld = 3 * C;
   const bf16* Bg = qkv + (size_t)b * T * ld;                 // row 0 of this sequence
@@ -393,8 +413,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
   constexpr int NS = NS_DKDV;
   __shared__ __attribute__((aligned(1024))) char ring[NS][KV_STAGE_BYTES];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ktile = (int)blockIdx.x;           // lower key tiles see more queries: launch them first
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  int ktile, bh;
+  head_major_block(ktile, bh);   // lower key tiles see more queries: launched first
+  const int b = bh / H, h = bh % H;
   const int C = H * HD;
   const int ld = 3 * C;
   const bf16* Bg = qkv + (size_t)b * T * ld;
@@ -469,7 +490,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
     if (s < nst) issue(s, s);
   // unrolled by the ring depth: LDS addresses are fixed offsets + immediates
   for (int st0 = 0; st0 < nst; st0 += NS) {
-#pragma unroll 1
+#pragma unroll
     for (int sl = 0; sl < NS; ++sl) {
       const int st = st0 + sl;
       if (st >= nst) break;
@@ -484,68 +505,130 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
       const GPT2_LDS char* Ls = Qs + 2 * TILE;
       const GPT2_LDS char* Ds = Qs + 2 * TILE + 1024;
       const int q0 = qbeg + st * STAGE;
-      // Both 32-query slices' score products first, then each slice's
-      // softmax-gradient work and its dV / dK products: the second slice's
-      // S and dP run on the matrix cores while the first slice's exponentials
-      // run on the vector units, and the first slice's dV / dK products while
-      // the second slice's do.
+      // Issue order: slice 0's score products; slice 1's score products, each
+      // followed by two rows of slice 0's vector work; slice 0's dV / dK
+      // products, each followed by two rows of slice 1's vector work; slice
+      // 1's dV / dK products.  Each product's fragments are read one product
+      // ahead, and scheduling barriers keep the order (in-order issue would
+      // otherwise leave the matrix cores idle during the exponentials and the
+      // vector units idle during the products).  Masked entries (key after
+      // query, query past the end) get S = -inf, so P = 0 and dS = 0 exactly
+      // (zero-filled rows past the end have dP = D = 0); a slice no query of
+      // which sees a key of the wave only adds zeros.
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
       floatx16 s[2], dp[2];
-      bool ok[2];
-#pragma unroll
-      for (int u2 = 0; u2 < 2; ++u2) {
+      bf16x8 pb[2][2], db[2][2];
+      float lv[16];
+      auto mask = [&](int u2) {   // only on slices that cross the diagonal or the end
         const int qb = q0 + 32 * u2;
-        ok[u2] = qb + 31 >= kw0 && qb < T && kw0 < T;
-        if (ok[u2]) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) { s[u2][r] = 0.f; dp[u2][r] = 0.f; }
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            s[u2] = mfma(frag_at(Qs, noffs[u2][k]), kf[k], s[u2]);
-            dp[u2] = mfma(frag_at(Os, noffs[u2][k]), vf[k], dp[u2]);
-          }
-        }
-      }
-#pragma unroll
-      for (int u2 = 0; u2 < 2; ++u2) {
-        const int qs = 32 * u2, qb = q0 + qs;
-        if (ok[u2]) {
-          // s[r]: query qb + acc_row(r), key mykey.  The lane's 16 query rows are
-          // qs + 4 hi + 8 g + 0..3 (g = 0..3): four 16-byte reads each of L2 and D.
-          typedef float f32x4 __attribute__((ext_vector_type(4)));
-          float lv[16], dv_[16];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 l4 = *reinterpret_cast<const GPT2_LDS f32x4*>(Ls + ldoff + 4 * (qs + 8 * g));
-            const f32x4 d4 = *reinterpret_cast<const GPT2_LDS f32x4*>(Ds + ldoff + 4 * (qs + 8 * g));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { lv[4 * g + e] = l4[e]; dv_[4 * g + e] = d4[e]; }
-          }
-          float p[16];
-          // the causal / end-of-sequence mask only touches slices on the diagonal
-          if ((qb < kw0 + 31) || (qb + 32 > T)) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int q = qb + acc_row(r, lane);
-              p[r] = (mykey > q || q >= T) ? 0.f : ex2(fmaf(s[u2][r], sl2, -lv[r]));
-            }
-          } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) p[r] = ex2(fmaf(s[u2][r], sl2, -lv[r]));
-          }
-          bf16x8 pb[2], db[2];
+        if (qb < kw0 + 31 || qb + 32 > T) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            pb[r >> 3][r & 7] = (bf16)p[r];
-            db[r >> 3][r & 7] = (bf16)(p[r] * (dp[u2][r] - dv_[r]));
+            const int q = qb + acc_row(r, lane);
+            if (mykey > q || q >= T) s[u2][r] = -__builtin_inff();
           }
+        }
+      };
+      // s[r] is query q0 + 32 u2 + acc_row(r), key mykey; the lane's 16 query
+      // rows are 32 u2 + 4 hi + 8 g + 0..3 (g = 0..3): four 16-byte reads each
+      // of lse·log2e (into lv) and of -D (dP's initial accumulator, so the
+      // products leave dP - D)
+      auto load_l = [&](int u2) {
 #pragma unroll
-          for (int u = 0; u < 2; ++u)
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 l4 = *reinterpret_cast<const GPT2_LDS f32x4*>(Ls + ldoff + 4 * (32 * u2 + 8 * g));
 #pragma unroll
-            for (int dt = 0; dt < 2; ++dt) {
-              const uint32_t o0 = toffs[dt][2 * u2 + u][0], o1 = toffs[dt][2 * u2 + u][1];
-              dv[dt] = mfma(frag_tr_at(Os, o0, o1), pb[u], dv[dt]);
-              dk[dt] = mfma(frag_tr_at(Qs, o0, o1), db[u], dk[dt]);
-            }
+          for (int e = 0; e < 4; ++e) lv[4 * g + e] = l4[e];
+        }
+      };
+      auto load_nd = [&](int u2) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 d4 = *reinterpret_cast<const GPT2_LDS f32x4*>(Ds + ldoff + 4 * (32 * u2 + 8 * g));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dp[u2][4 * g + e] = d4[e];
+        }
+      };
+      // P and dS of rows r, r + 1 of slice u2
+      auto softgrad2 = [&](int u2, int r) {
+#pragma unroll
+        for (int e = r; e < r + 2; ++e) {
+          const float p = ex2(fmaf(s[u2][e], sl2, -lv[e]));
+          pb[u2][e >> 3][e & 7] = (bf16)p;
+          db[u2][e >> 3][e & 7] = (bf16)(p * dp[u2][e]);
+        }
+      };
+      // score product i of slice u2: k16 step i / 2 of S (i even) or dP (odd)
+      auto score_frag = [&](int u2, int i) { return frag_at((i & 1) ? Os : Qs, noffs[u2][i >> 1]); };
+      auto score_mfma = [&](int u2, int i, const bf16x8& a) {
+        if (i & 1) dp[u2] = mfma(a, vf[i >> 1], dp[u2]);
+        else s[u2] = mfma(a, kf[i >> 1], s[u2]);
+      };
+      // update product i of slice u2: u = i / 4, dt = (i / 2) % 2, dV (i even) or dK (odd)
+      auto upd_frag = [&](int u2, int i) {
+        const int u = i >> 2, dt = (i >> 1) & 1;
+        return frag_tr_at((i & 1) ? Qs : Os, toffs[dt][2 * u2 + u][0], toffs[dt][2 * u2 + u][1]);
+      };
+      auto upd_mfma = [&](int u2, int i, const bf16x8& a) {
+        const int u = i >> 2, dt = (i >> 1) & 1;
+        if (i & 1) dk[dt] = mfma(a, db[u2][u], dk[dt]);
+        else dv[dt] = mfma(a, pb[u2][u], dv[dt]);
+      };
+#pragma unroll
+      for (int u2 = 0; u2 < 2; ++u2) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[u2][r] = 0.f;
+        load_nd(u2);
+      }
+      // slice 0's score products
+      {
+        bf16x8 nx = score_frag(0, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const bf16x8 a = nx;
+          if (i < 7) nx = score_frag(0, i + 1);
+          score_mfma(0, i, a);
+        }
+      }
+      mask(0);
+      // slice 1's score products with slice 0's vector work
+      load_l(0);
+      {
+        bf16x8 nx = score_frag(1, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const bf16x8 a = nx;
+          if (i < 7) nx = score_frag(1, i + 1);
+          score_mfma(1, i, a);
+          softgrad2(0, 2 * i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // slice 0's P and dS are produced above: they would otherwise sink past
+      // the next branch to their use and the interleaving would be lost
+      pin(pb[0][0]); pin(pb[0][1]); pin(db[0][0]); pin(db[0][1]);
+      mask(1);
+      // slice 0's dV / dK products with slice 1's vector work
+      load_l(1);
+      {
+        bf16x8 nx = upd_frag(0, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const bf16x8 a = nx;
+          if (i < 7) nx = upd_frag(0, i + 1);
+          upd_mfma(0, i, a);
+          softgrad2(1, 2 * i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // slice 1's dV / dK products
+      {
+        bf16x8 nx = upd_frag(1, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const bf16x8 a = nx;
+          if (i < 7) nx = upd_frag(1, i + 1);
+          upd_mfma(1, i, a);
         }
       }
     }
@@ -582,8 +665,10 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dq_mfma_kernel(int T, int H, 
   __shared__ __attribute__((aligned(1024))) char ring[NS][2 * TILE];   // K tile, V tile
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nqt = (T + ROWS - 1) / ROWS;
-  const int qt = nqt - 1 - (int)blockIdx.x;
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  int tile, bh;
+  head_major_block(tile, bh);
+  const int qt = nqt - 1 - tile;   // longer rows first
+  const int b = bh / H, h = bh % H;
   const int C = H * HD;
   const int ld = 3 * C;
   const bf16* Bg = qkv + (size_t)b * T * ld;
@@ -608,7 +693,7 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dq_mfma_kernel(int T, int H, 
     Dq = half_sum(d);
     lq = myq < T ? lse[(size_t)bh * T + myq] * kLog2e : 0.f;
     if (myq < T && lane < 32) {
-      Dv[(size_t)bh * T + myq] = Dq;
+      Dv[(size_t)bh * T + myq] = -Dq;   // the dK / dV kernel starts dP's sums from -D
       lse2[(size_t)bh * T + myq] = lq;
     }
   }
