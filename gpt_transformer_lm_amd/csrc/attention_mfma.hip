@@ -51,6 +51,11 @@ constexpr int STAGE = 64;            // rows streamed per LDS stage
 // occupancy the kernel's registers permit (forward: 4 blocks of 2 x 16 KiB per
 // compute unit; dQ: 3 blocks of 3 x 16 KiB; dK/dV: 2 blocks of 4 x 18 KiB).
 constexpr int NS_FWD = 2, NS_DQ = 3, NS_DKDV = 4;
+// Products whose LDS fragments the dK/dV kernel has in flight ahead of the
+// matrix instruction that uses them (LDS latency is several products long;
+// measured at 124M: 1 -> 1.75, 2 -> 1.65, 3 -> 1.63, 4 -> 1.64, 6 -> 1.66 ms
+// per step).
+constexpr int DKDV_PREFETCH = 3;
 constexpr int TILE = STAGE * HD * 2; // bytes of one 64 x 64 bf16 tile
 constexpr uint32_t kOut = 0xFFFFFFF0u;   // offset past every buffer range
 constexpr float kLog2e = 1.4426950408889634f;
@@ -508,8 +513,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
       // Issue order: slice 0's score products; slice 1's score products, each
       // followed by two rows of slice 0's vector work; slice 0's dV / dK
       // products, each followed by two rows of slice 1's vector work; slice
-      // 1's dV / dK products.  Each product's fragments are read one product
-      // ahead, and scheduling barriers keep the order (in-order issue would
+      // 1's dV / dK products.  Each product's fragments are read a few
+      // products ahead, and scheduling barriers keep the order (in-order issue would
       // otherwise leave the matrix cores idle during the exponentials and the
       // vector units idle during the products).  Masked entries (key after
       // query, query past the end) get S = -inf, so P = 0 and dS = 0 exactly
@@ -580,29 +585,39 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
         for (int r = 0; r < 16; ++r) s[u2][r] = 0.f;
         load_nd(u2);
       }
-      // slice 0's score products
-      {
-        bf16x8 nx = score_frag(0, 0);
+      // The stage's 32 products in issue order: op 0..7 slice 0's S / dP,
+      // 8..15 slice 1's, 16..23 slice 0's dV / dK, 24..31 slice 1's; the
+      // fragments of op o + PD are read right after op o is issued.
+      constexpr int PD = DKDV_PREFETCH;
+      auto frag_of = [&](int o) {
+        return o < 16 ? score_frag(o >> 3, o & 7) : upd_frag((o >> 3) & 1, o & 7);
+      };
+      auto mfma_of = [&](int o, const bf16x8& a) {
+        if (o < 16) score_mfma(o >> 3, o & 7, a);
+        else upd_mfma((o >> 3) & 1, o & 7, a);
+      };
+      bf16x8 fq[PD];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const bf16x8 a = nx;
-          if (i < 7) nx = score_frag(0, i + 1);
-          score_mfma(0, i, a);
-        }
+      for (int o = 0; o < PD; ++o) fq[o] = frag_of(o);
+      auto op = [&](int o) {
+        const bf16x8 a = fq[o % PD];
+        if (o + PD < 32) fq[o % PD] = frag_of(o + PD);
+        mfma_of(o, a);
+      };
+      // slice 0's score products
+#pragma unroll
+      for (int o = 0; o < 8; ++o) {
+        op(o);
+        __builtin_amdgcn_sched_barrier(0);
       }
       mask(0);
       // slice 1's score products with slice 0's vector work
       load_l(0);
-      {
-        bf16x8 nx = score_frag(1, 0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const bf16x8 a = nx;
-          if (i < 7) nx = score_frag(1, i + 1);
-          score_mfma(1, i, a);
-          softgrad2(0, 2 * i);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+      for (int o = 8; o < 16; ++o) {
+        op(o);
+        softgrad2(0, 2 * (o - 8));
+        __builtin_amdgcn_sched_barrier(0);
       }
       // slice 0's P and dS are produced above: they would otherwise sink past
       // the next branch to their use and the interleaving would be lost
@@ -610,26 +625,17 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
       mask(1);
       // slice 0's dV / dK products with slice 1's vector work
       load_l(1);
-      {
-        bf16x8 nx = upd_frag(0, 0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const bf16x8 a = nx;
-          if (i < 7) nx = upd_frag(0, i + 1);
-          upd_mfma(0, i, a);
-          softgrad2(1, 2 * i);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+      for (int o = 16; o < 24; ++o) {
+        op(o);
+        softgrad2(1, 2 * (o - 16));
+        __builtin_amdgcn_sched_barrier(0);
       }
       // slice 1's dV / dK products
-      {
-        bf16x8 nx = upd_frag(1, 0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const bf16x8 a = nx;
-          if (i < 7) nx = upd_frag(1, i + 1);
-          upd_mfma(1, i, a);
-        }
+      for (int o = 24; o < 32; ++o) {
+        op(o);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
