@@ -514,12 +514,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(int T, int H
       // followed by two rows of slice 0's vector work; slice 0's dV / dK
       // products, each followed by two rows of slice 1's vector work; slice
       // 1's dV / dK products.  Each product's fragments are read a few
-      // products ahead, and scheduling barriers keep the order (in-order issue would
-      // otherwise leave the matrix cores idle during the exponentials and the
-      // vector units idle during the products).  Masked entries (key after
-      // query, query past the end) get S = -inf, so P = 0 and dS = 0 exactly
-      // (zero-filled rows past the end have dP = D = 0); a slice no query of
-      // which sees a key of the wave only adds zeros.
+      // products ahead, and scheduling barriers keep the order (in-order
+      // issue would otherwise leave the matrix cores idle during the
+      // exponentials and the vector units idle during the products).  Masked
+      // entries (key after query, query past the end) get S = -inf, so P = 0
+      // and dS = 0 exactly (zero-filled rows past the end have dP = D = 0); a
+      // slice no query of which sees a key of the wave only adds zeros.
       typedef float f32x4 __attribute__((ext_vector_type(4)));
       floatx16 s[2], dp[2];
       bf16x8 pb[2][2], db[2][2];
