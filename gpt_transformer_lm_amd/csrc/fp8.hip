@@ -108,13 +108,23 @@ constexpr int kQT = 128;
 // per-block maxima, or a producer's slots): every block takes their maximum
 // (exact, so all agree) and forms inv and s as above; block (0, 0) stores
 // (amax, inv, s) for the products.  The tile's loads are issued first: they
-// do not depend on the scale.
+// do not depend on the scale.  blockIdx.z selects one of several tensors of
+// the same shape (x, slots, scale and codes advanced by their layer strides).
 template <typename T, int FMT, bool CS>
 __global__ __launch_bounds__(256) void quantize_kernel(int R, int Cc, const T* __restrict__ x, int64_t ldx,
                                                        const float* __restrict__ amax_part, int np, int pstride,
                                                        float fmax,
                                                        Fp8Scale* __restrict__ sc, uint8_t* __restrict__ qrow,
-                                                       uint8_t* __restrict__ qt, float* __restrict__ colsum) {
+                                                       uint8_t* __restrict__ qt, float* __restrict__ colsum,
+                                                       int64_t amax_lstride) {
+  {
+    const int64_t z = blockIdx.z;
+    x += z * R * ldx;
+    amax_part += z * amax_lstride;
+    sc += z;
+    if (qrow) qrow += z * R * Cc;
+    if (qt) qt += z * R * Cc;
+  }
   constexpr int kPitch = kQT / 4 + 2;   // dwords per LDS row: the two half-waves' rows 16 apart differ by 32 banks
   __shared__ uint32_t tile[kQT][kPitch];
   __shared__ float smax[4];
@@ -256,22 +266,27 @@ int fp8_amax(int dtype_in, int64_t n, const void* x, float* workspace, hipStream
 
 template <typename T, int FMT>
 void launch_quantize(dim3 grid, int R, int Cc, const void* x, int64_t ldx, const float* amax_part, int np,
-                     int pstride, Fp8Scale* sc, uint8_t* qrow, uint8_t* qt, float* colsum, hipStream_t stream) {
+                     int pstride, Fp8Scale* sc, uint8_t* qrow, uint8_t* qt, float* colsum, int64_t als,
+                     hipStream_t stream) {
   const float fmax = FMT == 0 ? 448.0f : 57344.0f;
   if (colsum)
     hipLaunchKernelGGL((quantize_kernel<T, FMT, true>), grid, dim3(256), 0, stream, R, Cc, (const T*)x, ldx, amax_part,
-                       np, pstride, fmax, sc, qrow, qt, colsum);
+                       np, pstride, fmax, sc, qrow, qt, colsum, als);
   else
     hipLaunchKernelGGL((quantize_kernel<T, FMT, false>), grid, dim3(256), 0, stream, R, Cc, (const T*)x, ldx,
-                       amax_part, np, pstride, fmax, sc, qrow, qt, colsum);
+                       amax_part, np, pstride, fmax, sc, qrow, qt, colsum, als);
 }
 
 int fp8_quantize(int dtype_in, int fmt, int R, int Cc, const void* x, int64_t ldx, const float* amax_part,
-                 Fp8Scale* sc, uint8_t* qrow, uint8_t* qt, hipStream_t stream, float* colsum, int amax_np) {
+                 Fp8Scale* sc, uint8_t* qrow, uint8_t* qt, hipStream_t stream, float* colsum, int amax_np,
+                 int layers) {
   if (R < 0 || Cc < 0 || !x || !amax_part || !sc || (!qrow && !qt) || Cc % 8 || ldx % 8 || (qt && R % 16) ||
       (uintptr_t)x % 16 || (fmt != 0 && fmt != 1))
     return gpt2_internal_fail(1, "fp8_quantize: bad arguments (R=%d, C=%d)", R, Cc);
   if (amax_np < 0 || amax_np > kAmaxWays) return gpt2_internal_fail(1, "fp8_quantize: amax_np=%d", amax_np);
+  if (layers < 1 || layers > 65535 || (layers > 1 && (!amax_np || colsum || R == 0 || Cc == 0)))
+    return gpt2_internal_fail(1, "fp8_quantize: %d layers need producer slots, no column sums, a non-empty shape",
+                              layers);
   const int np = amax_np ? amax_np : amax_blocks((int64_t)R * Cc);
   const int ps = amax_np ? kAmaxStride : 1;
   if (R == 0 || Cc == 0) {   // no tile to store the scale: the one-block form
@@ -280,14 +295,15 @@ int fp8_quantize(int dtype_in, int fmt, int R, int Cc, const void* x, int64_t ld
     GPT2_LAUNCH_CHECK();
     return 0;
   }
-  dim3 grid((unsigned)ceil_div64(Cc, kQT), (unsigned)ceil_div64(R, kQT));
+  dim3 grid((unsigned)ceil_div64(Cc, kQT), (unsigned)ceil_div64(R, kQT), (unsigned)layers);
+  const int64_t als = (int64_t)kAmaxWays * kAmaxStride;   // slots of consecutive layers
   mark_begin(0, stream);
   if (dtype_in == BF16) {
-    if (fmt == 0) launch_quantize<bf16, 0>(grid, R, Cc, x, ldx, amax_part, np, ps, sc, qrow, qt, colsum, stream);
-    else launch_quantize<bf16, 1>(grid, R, Cc, x, ldx, amax_part, np, ps, sc, qrow, qt, colsum, stream);
+    if (fmt == 0) launch_quantize<bf16, 0>(grid, R, Cc, x, ldx, amax_part, np, ps, sc, qrow, qt, colsum, als, stream);
+    else launch_quantize<bf16, 1>(grid, R, Cc, x, ldx, amax_part, np, ps, sc, qrow, qt, colsum, als, stream);
   } else {
-    if (fmt == 0) launch_quantize<float, 0>(grid, R, Cc, x, ldx, amax_part, np, ps, sc, qrow, qt, colsum, stream);
-    else launch_quantize<float, 1>(grid, R, Cc, x, ldx, amax_part, np, ps, sc, qrow, qt, colsum, stream);
+    if (fmt == 0) launch_quantize<float, 0>(grid, R, Cc, x, ldx, amax_part, np, ps, sc, qrow, qt, colsum, als, stream);
+    else launch_quantize<float, 1>(grid, R, Cc, x, ldx, amax_part, np, ps, sc, qrow, qt, colsum, als, stream);
   }
   GPT2_LAUNCH_CHECK();
   mark_end(0, stream);

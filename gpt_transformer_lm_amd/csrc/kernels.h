@@ -149,9 +149,12 @@ int fp8_amax(int dtype_in, int64_t n, const void* x, float* workspace, hipStream
 // x that colsum_reduce turns into a bias gradient.  amax_np > 0 (at most
 // kAmaxWays): amax_part holds that many slots, kAmaxStride floats apart, left
 // by a producer kernel (amax_atomic_bf16), instead of fp8_amax's maxima.
+// layers > 1 (producer slots, no colsum): that many tensors of the same shape
+// in one launch, tensor l at x + l R ldx with slots amax_part + l kAmaxWays
+// kAmaxStride, scale sc[l] and codes qrow / qt + l R Cc.
 int fp8_quantize(int dtype_in, int fmt, int R, int Cc, const void* x, int64_t ldx, const float* amax_part,
                  Fp8Scale* sc, uint8_t* qrow, uint8_t* qt, hipStream_t stream, float* colsum = nullptr,
-                 int amax_np = 0);
+                 int amax_np = 0, int layers = 1);
 size_t fp8_colsum_bytes(int R, int N);
 // db[n] (+)= sum of the column sums left by fp8_quantize for R rows, in a
 // fixed order.

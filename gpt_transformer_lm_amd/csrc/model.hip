@@ -573,16 +573,19 @@ GemmDesc dw_desc(gpt2_model* m, int M, int N, int K, const void* dy, const void*
 // arena's column-sum buffer.  produced: the kernel that wrote x also left its
 // maximum in slot_max(slot) (zeroed at the start of the forward), so no pass
 // of its own takes it.
+// (layers > 1: that many consecutive tensors of the same shape, with
+// consecutive slots, from the producers' maxima, in one launch.)
 int fp8_quant(gpt2_model* m, int dtype_in, const void* x, int R, int Cc, int fmt, int slot, uint8_t* q, uint8_t* qt,
-              bool colsum = false, bool produced = false) {
+              bool colsum = false, bool produced = false, int layers = 1) {
   if (m->dry()) return 0;
   Fp8Scale* sc = m->fscale(slot);
   float* amax = produced ? m->slot_max(slot) : m->at<float>(m->lo.fp8_amax);
   if (!produced) RC(fp8_amax(dtype_in, (int64_t)R * Cc, x, amax, m->stream));
-  const double in_b = (double)R * Cc * (dtype_in == GPT2_BF16 ? 2 : 4);
-  return timed(m, S_FP8_QUANT, 0.0, in_b + (double)R * Cc * ((q ? 1 : 0) + (qt ? 1 : 0)), [&] {
+  const double n = (double)layers * R * Cc;
+  const double in_b = n * (dtype_in == GPT2_BF16 ? 2 : 4);
+  return timed(m, S_FP8_QUANT, 0.0, in_b + n * ((q ? 1 : 0) + (qt ? 1 : 0)), [&] {
     return fp8_quantize(dtype_in, fmt, R, Cc, x, Cc, amax, sc, q, qt, m->stream,
-                        colsum ? m->at<float>(m->lo.fp8_colsum) : nullptr, produced ? kAmaxWays : 0);
+                        colsum ? m->at<float>(m->lo.fp8_colsum) : nullptr, produced ? kAmaxWays : 0, layers);
   });
 }
 
@@ -955,6 +958,11 @@ int refresh_fp8_weights(gpt2_model* m, bool produced = false) {
     const int64_t* sh = m->lo.pt.shape[i];
     const bool layered = m->lo.pt.ndim[i] == 3;
     const int R = (int)(layered ? sh[1] : sh[0]), Cc = (int)(layered ? sh[2] : sh[1]);
+    if (produced && layered) {   // every layer's matrix in one launch (their slots are consecutive)
+      RC(fp8_quant(m, GPT2_FP32, m->master() + m->lo.pt.off[i], R, Cc, 0, fp8_slot(L, Q_WEIGHT, w, 0), m->wq(i, 0),
+                   m->wqt(i, 0), false, true, L));
+      continue;
+    }
     for (int l = 0; l < (layered ? L : 1); ++l) {
       const float* src = m->master() + m->lo.pt.off[i] + (int64_t)l * R * Cc;
       RC(fp8_quant(m, GPT2_FP32, src, R, Cc, 0, fp8_slot(L, Q_WEIGHT, w, l), m->wq(i, l), m->wqt(i, l), false,
