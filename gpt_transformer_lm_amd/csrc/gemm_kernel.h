@@ -1034,12 +1034,16 @@ Plan plan_bf16(int epi, int M, int N, int K, bool a_kmajor, bool b_kmajor) {
     best = Plan{256, 256, 1, kt * kBK};
     return best;
   }
-  // Other short-K products with an epilogue (residual add, GELU' multiply,
-  // which read an input tile): the epilogue is a large share of each tile, and
-  // 128x128 tiles at two blocks per compute unit overlap it with the other
-  // block's main loop (measured 15-25% faster than one-block tiles at
-  // M = 24576, K = 768).
-  if (!may_split && epi != EPI_STORE && a_kmajor && b_kmajor && M >= 2048 && K <= 1024) {
+  // Other short-K products with an epilogue that reads an input tile (the
+  // GELU' multiply; a residual add whose N is not a multiple of 192): the
+  // epilogue is a large share of each tile, and 128x128 tiles at two blocks
+  // per compute unit overlap it with the other block's main loop (measured
+  // 15-25% faster than the 4-wave one-block tiles at M = 24576, K = 768).  A
+  // residual add with N a multiple of 192 takes the 384x192 tile below (its
+  // residual loaded to registers after the main loop; attn-proj forward,
+  // N = 768: 256 tiles, one round, 0.62 -> 0.54 ms per step).
+  if (!may_split && epi != EPI_STORE && !(epi == EPI_BIAS_RES && N % 192 == 0 && M >= 8192) && a_kmajor && b_kmajor &&
+      M >= 2048 && K <= 1024) {
     best = Plan{128, 128, 1, 0};
     best.k_per_split = kt * kBK;
     return best;
